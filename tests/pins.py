@@ -1,0 +1,474 @@
+"""Checks that pin the CPU oracle to facts fixed outside itself.
+
+Each check raises AssertionError on failure.  They are collected as tests in
+test_oracle_pins.py and re-run against deliberately broken copies of the oracle
+in test_oracle_mutations.py, which shows that a plausible mistake anywhere in
+the oracle fails at least one of them.
+
+Sources of truth used here, none of which is the oracle's own arithmetic:
+  * hand-worked fixtures in tests/golden/ (each cites the page section);
+  * independent library routines: torch's bfloat16 rounding, numpy.linalg.eigh
+    of the covariance (the oracle uses an SVD of the data), exact rational
+    arithmetic (fractions) for dot products;
+  * closed forms: Parseval for an orthonormal basis, the uniform quantizer's
+    half-step bound, exact reconstruction on a dyadic grid with an exactly
+    orthonormal Hadamard basis;
+  * brute force over every width vector for a few groups;
+  * the KV size the page states for Llama 3.1 8B (128 MiB per 1K tokens).
+"""
+from __future__ import annotations
+
+import fractions
+import itertools
+import json
+import os
+import struct
+
+import numpy as np
+
+import oracle.kvtc_oracle as O
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------- helpers ---
+
+def small_params(F=64, G=16, bpv=4.0, s=4, w=8, dtype=O.DTYPE_F32, max_bits=8):
+    return O.Params(1, 1, F, s, w, G, max_bits, bpv, dtype)
+
+
+def hadamard(n):
+    h = np.array([[1.0]])
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def injected_slot(V32, widths, mu32, G):
+    F = V32.shape[0]
+    return O.Slot(0, 0, F, G, np.asarray(widths, np.uint8), np.asarray(mu32, np.float32),
+                  np.zeros(F), np.asarray(V32, np.float32))
+
+
+def family_b_small(seed=7, n=4096):
+    """A small family-B-like tensor: 2 heads x 32 dims sharing a rank-12 latent."""
+    rng = np.random.default_rng(seed)
+    d, r, H = 32, 12, 2
+    U, _ = np.linalg.qr(rng.standard_normal((d, r)))
+    M = np.concatenate([np.linalg.qr(rng.standard_normal((d, d)))[0] @ U for _ in range(H)])
+    sig = np.arange(1, r + 1) ** -1.2 * 4.0
+    mean = rng.standard_normal(d * H)
+    x = (rng.standard_normal((n, r)) * sig) @ M.T + mean + 1e-3 * rng.standard_normal((n, d * H))
+    return x.astype(np.float32), M
+
+
+def brute_force_widths(D, G, budget):
+    """Enumerate every width vector and order them by (objective, bits,
+    lexicographically largest widths).  D must hold exact binary fractions
+    small enough that every sum is exact in fp64, so no summation order
+    matters."""
+    n_g, nb = D.shape
+    ws = np.array(list(itertools.product(range(nb), repeat=n_g)), np.int64)
+    cost = np.sum(G * ws + 64 * (ws > 0), axis=1)
+    obj = np.sum(D[np.arange(n_g), ws], axis=1)
+    ok = cost <= budget
+    ws, cost, obj = ws[ok], cost[ok], obj[ok]
+    # lexsort: last key is primary
+    keys = [-ws[:, g] for g in range(n_g - 1, -1, -1)] + [cost, obj]
+    i = np.lexsort(keys)[0]
+    return ws[i].astype(np.uint8), obj[i]
+
+
+# ------------------------------------------------------------------- pins ---
+
+def check_bf16_vs_torch():
+    import torch
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * 10.0 ** rng.integers(-6, 6, 20000),
+        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -130, 0.0, -0.0,
+                  3.0e38, 1.0 - 2 ** -24], np.float32)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    got = O.bf16_rne(x)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), "bf16 rounding differs from torch"
+
+
+def check_fnv_vectors():
+    # Published FNV-1a 64-bit test vectors.
+    assert O.fnv1a64(b"") == 0xCBF29CE484222325
+    assert O.fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert O.fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+def check_pack_golden():
+    for case in golden("pack_examples.json")["cases"]:
+        q = np.array([case["codes"]], np.uint8)
+        got = O.pack_codes(q, case["b"]).tobytes().hex()
+        assert got == case["bytes_hex"], (case["b"], got, case["bytes_hex"])
+        back = O.unpack_codes(np.frombuffer(bytes.fromhex(case["bytes_hex"]), np.uint8)[None, :],
+                              16, case["b"])
+        assert np.array_equal(back, q), case["b"]
+
+
+def check_pack_roundtrip():
+    rng = np.random.default_rng(1)
+    for G in (16, 32):
+        for b in range(1, 9):
+            q = rng.integers(0, 2 ** b, (37, G)).astype(np.uint8)
+            p = O.pack_codes(q, b)
+            assert p.shape == (37, G * b // 8)
+            assert np.array_equal(O.unpack_codes(p, G, b), q)
+
+
+def check_quantizer_golden():
+    for case in golden("quantizer_examples.json")["cases"]:
+        c = np.array([case["c"]], np.float32)
+        q, shift, scale = O.quantize_fp32(c, case["b"])
+        assert q.tolist()[0] == case["q"], (case, q)
+        assert float(shift[0]) == case["shift"] and float(scale[0]) == case["scale"]
+
+
+def check_quantizer_bound():
+    rng = np.random.default_rng(2)
+    for b in range(1, 9):
+        c = (rng.standard_normal((500, 16)) * 10.0 ** rng.uniform(-3, 3, (500, 1))).astype(np.float32)
+        q, shift, scale = O.quantize_fp32(c, b)
+        k = 2 ** b - 1
+        assert q.max() <= k
+        assert np.all(q.min(axis=1) == 0) and np.all(q.max(axis=1) == k)
+        chat = O.dequantize(q, shift, scale, b)
+        step = scale.astype(np.float64) / k
+        err = np.abs(chat - c.astype(np.float64))
+        assert np.all(err <= step[:, None] * (0.5 + 1e-5) + 1e-6 * np.abs(c)), b
+
+
+def check_pca_invariants():
+    x, M = family_b_small()
+    p = O.Params(1, 2, 32, 4, 8, 16, 8, 2.0, O.DTYPE_F32)
+    sl = O.calibrate(x, p, 0, 0)
+    V, lam = sl.V64, sl.lam
+    F = V.shape[0]
+    assert np.allclose(V.T @ V, np.eye(F), atol=1e-10), "basis not orthonormal"
+    rows = x[4:-8].astype(np.float64)
+    xc = rows - rows.mean(axis=0)
+    cov = xc.T @ xc / xc.shape[0]
+    proj = V.T @ cov @ V
+    off = proj - np.diag(np.diag(proj))
+    assert np.abs(off).max() <= 1e-9 * np.abs(proj).max(), "projected covariance not diagonal"
+    assert np.allclose(np.diag(proj), lam, rtol=1e-9, atol=1e-12)
+    ev = np.linalg.eigh(cov)[0][::-1]                    # independent route
+    assert np.allclose(lam, ev, rtol=1e-8, atol=1e-12 * ev[0]), "eigenvalues disagree with eigh"
+    assert np.all(np.diff(lam) <= 0), "components not sorted by variance"
+    for j in range(F):
+        i = int(np.argmax(np.abs(V[:, j])))
+        assert V[i, j] > 0, "sign rule"
+    # the planted rank-12 subspace is recovered (principal angles ~ 0)
+    Q = np.linalg.qr(M)[0]
+    s = np.linalg.svd(Q.T @ V[:, :12], compute_uv=False)
+    assert s.min() > 0.999, s.min()
+    # mean is the mean of the rows [s, n - w)
+    assert np.allclose(sl.mu64, rows.mean(axis=0), rtol=0, atol=1e-12)
+
+
+def check_parseval():
+    x, _ = family_b_small(seed=3, n=2048)
+    p = O.Params(1, 2, 32, 4, 8, 16, 8, 2.0, O.DTYPE_F32)
+    sl = O.calibrate(x, p, 0, 0)
+    rows = x[4:-8].astype(np.float64)
+    xc = rows - rows.mean(axis=0)
+    feat = np.mean(np.sum(xc * xc, axis=1))
+    assert np.isclose(np.sum(sl.D[:, 0]), feat, rtol=1e-10), "Parseval"
+    # the retained error in feature space equals the table's prediction
+    C = xc @ sl.V64
+    xhat = np.zeros_like(xc)
+    for g in range(sl.D.shape[0]):
+        b = int(sl.widths[g])
+        cols = slice(16 * g, 16 * g + 16)
+        if b:
+            xhat += O.quant_dequant_fp64(C[:, cols], b) @ sl.V64[:, cols].T
+    err = np.mean(np.sum((xc - xhat) ** 2, axis=1))
+    pred = sum(sl.D[g, int(sl.widths[g])] for g in range(sl.D.shape[0]))
+    assert np.isclose(err, pred, rtol=1e-9), "distortion table does not predict the error"
+
+
+def check_distortion_bound():
+    x, _ = family_b_small(seed=4, n=1024)
+    p = O.Params(1, 2, 32, 4, 8, 16, 8, 2.0, O.DTYPE_F32)
+    sl = O.calibrate(x, p, 0, 0)
+    rows = x[4:-8].astype(np.float64)
+    C = (rows - rows.mean(axis=0)) @ sl.V64
+    for g in range(sl.D.shape[0]):
+        cg = C[:, 16 * g:16 * g + 16]
+        rng_ = cg.max(axis=1) - cg.min(axis=1)
+        for b in range(1, 9):
+            bound = np.mean(16 * (rng_ / (2 ** b - 1) / 2) ** 2)
+            assert sl.D[g, b] <= bound * (1 + 1e-9)
+        assert np.isclose(sl.D[g, 0], np.mean(np.sum(cg * cg, axis=1)))
+
+
+def check_dp_golden():
+    gd = golden("dp_examples.json")
+    D = np.array(gd["D"])
+    for case in gd["cases"]:
+        w = O.dp_allocate(D, gd["G"], case["budget"])
+        assert w.tolist() == case["widths"], (case, w)
+        assert sum(D[g, b] for g, b in enumerate(w)) == case["objective"]
+
+
+def check_dp_bruteforce():
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        n_g = int(rng.integers(1, 5))
+        G = int(rng.choice([16, 32]))
+        e = np.sort(rng.uniform(0, 100, n_g))[::-1]
+        # realistic tables: decreasing in b, exact small dyadic values so ties are real
+        D = np.array([[np.round(e[g] * 4.0 ** -b * 64) / 64 for b in range(9)] for g in range(n_g)])
+        if trial % 5 == 0:
+            D[-1] = 0.0
+        for budget in (0, 63, 80, 100, 150, 300, 500, 900):
+            w = O.dp_allocate(D, G, budget)
+            bw, bobj = brute_force_widths(D, G, budget)
+            assert np.array_equal(w, bw), (D, G, budget, w, bw)
+    # optimum non-increasing in the budget
+    D = np.array([[50 * 3.0 ** -b for b in range(9)], [20 * 3.0 ** -b for b in range(9)],
+                  [5 * 3.0 ** -b for b in range(9)]])
+    prev = np.inf
+    for budget in range(0, 700, 16):
+        w = O.dp_allocate(D, 16, budget)
+        obj = sum(D[g, b] for g, b in enumerate(w))
+        assert obj <= prev + 1e-12
+        assert sum(16 * int(b) + (64 if b else 0) for b in w) <= budget
+        prev = obj
+
+
+def check_projection_exact():
+    """c = fp32 of the exact dot product of bf16 operands (section 2B)."""
+    rng = np.random.default_rng(6)
+    F, r = 64, 32
+    V32 = np.linalg.qr(rng.standard_normal((F, F)))[0][:, :r].astype(np.float32)
+    mu = rng.standard_normal(F).astype(np.float32)
+    sl = injected_slot(V32, [1, 1, 0, 0], mu, 16)
+    x = (rng.standard_normal((5, F)) * 3 + mu).astype(np.float32)
+    c = O.project(x, sl)
+    import torch
+    xc = (torch.from_numpy(x) - torch.from_numpy(mu)).to(torch.bfloat16).double().numpy()
+    Vb = torch.from_numpy(V32).to(torch.bfloat16).double().numpy()
+    for t in range(5):
+        for j in range(r):
+            exact = sum(fractions.Fraction(float(xc[t, f])) * fractions.Fraction(float(Vb[f, j]))
+                        for f in range(F))
+            assert c[t, j] == np.float32(float(exact)), (t, j)
+
+
+def check_exact_roundtrip_identity():
+    """mu = 0, V = I, all groups at 8 bits, values on each group's 8-bit grid:
+    decode returns the input bit for bit."""
+    rng = np.random.default_rng(8)
+    F, G, T = 64, 16, 40
+    p = small_params(F=F, G=G, bpv=12.0)
+    sl = injected_slot(np.eye(F), [8, 8, 8, 8], np.zeros(F), G)
+    x = np.zeros((T, F), np.float32)
+    for g in range(F // G):
+        e = rng.integers(-6, 3, T).astype(np.float64)
+        m = rng.integers(-255, 1, T)               # |m + q| <= 255 is exact in bf16
+        q = rng.integers(0, 256, (T, G))
+        q[:, 0], q[:, 1] = 0, 255
+        x[:, g * G:(g + 1) * G] = (m[:, None] + q) * 2.0 ** e[:, None]
+    assert np.array_equal(O.bf16_rne(x), x)
+    er = O.encode(x, p, sl, 0, 0)
+    full, out = O.decode(er.stream, p, sl, 0, 0, T)
+    assert np.array_equal(out.view(np.uint32), x.view(np.uint32)), "identity round trip not exact"
+
+
+def check_hadamard_roundtrip_bound():
+    """Exactly orthonormal bf16 basis (Hadamard / 8): ||x_hat - mu - x'|| <=
+    sqrt(sum (step/2)^2), by Parseval and the half-step bound."""
+    rng = np.random.default_rng(9)
+    F, G, T = 64, 16, 300
+    H = hadamard(F) / 8.0
+    assert np.allclose(H.T @ H, np.eye(F))
+    mu = rng.standard_normal(F).astype(np.float32)
+    for widths in ([8, 8, 8, 8], [6, 4, 2, 1], [3, 0, 5, 0]):
+        p = small_params(F=F, G=G, bpv=12.0, s=2, w=3)
+        cols = [j for g in range(4) if widths[g] for j in range(g * G, (g + 1) * G)]
+        sl = injected_slot(H[:, cols], widths, mu, G)
+        x = (rng.standard_normal((T, F)) * 2 + mu).astype(np.float32)
+        er = O.encode(x, p, sl, 0, 0)
+        full, _ = O.decode(er.stream, p, sl, 0, 0, T)
+        xs = x[2:T - 3]
+        xprime = O.bf16_rne((xs - mu).astype(np.float32)).astype(np.float64)
+        err = full[2:T - 3] - mu.astype(np.float64) - xprime
+        bound2 = np.zeros(T - 5)
+        act = [g for g in range(4) if widths[g]]
+        for a, g in enumerate(act):
+            step = er.scale[:, a].astype(np.float64) / (2 ** widths[g] - 1)
+            bound2 += G * (step / 2) ** 2
+        for g in range(4):
+            if not widths[g]:
+                bound2 += np.sum((xprime @ H[:, g * G:(g + 1) * G]) ** 2, axis=1)
+        assert np.all(np.sum(err ** 2, axis=1) <= bound2 * (1 + 1e-3) + 1e-12), widths
+
+
+def check_zero_bit_decodes_to_mean():
+    rng = np.random.default_rng(10)
+    F, T = 64, 50
+    for dtype in (O.DTYPE_F32, O.DTYPE_BF16):
+        p = small_params(F=F, dtype=dtype, s=3, w=5)
+        mu = rng.standard_normal(F).astype(np.float32)
+        sl = injected_slot(np.zeros((F, 0)), [0, 0, 0, 0], mu, 16)
+        x = rng.standard_normal((T, F)).astype(np.float32)
+        store = O.f32_to_bf16_bits(x) if dtype == O.DTYPE_BF16 else x
+        er = O.encode(store, p, sl, 0, 0)
+        assert sl.record_bytes == 0
+        for od in (O.DTYPE_F32, O.DTYPE_BF16):
+            full, out = O.decode(er.stream, p, sl, 0, 0, T, od)
+            want = O.f32_to_bf16_bits(mu) if od == O.DTYPE_BF16 else mu
+            assert np.array_equal(out[3:T - 5], np.broadcast_to(want, (T - 8, F)))
+            if od == dtype:
+                assert np.array_equal(out[:3], store[:3]) and np.array_equal(out[T - 5:], store[T - 5:])
+
+
+def check_sink_window_layout():
+    rng = np.random.default_rng(11)
+    F = 64
+    mu = np.zeros(F, np.float32)
+    sl = injected_slot(np.eye(F)[:, :16], [4, 0, 0, 0], mu, 16)
+    for T, s, w in ((100, 4, 8), (12, 4, 8), (10, 4, 8), (3, 4, 8), (0, 4, 8), (30, 0, 0)):
+        p = small_params(F=F, s=s, w=w, dtype=O.DTYPE_BF16)
+        x = O.f32_to_bf16_bits(rng.standard_normal((T, F)).astype(np.float32))
+        er = O.encode(x, p, sl, 0, 0)
+        h = O.parse_header(er.stream)
+        s1 = min(s, T)
+        w1 = min(w, T - s1)
+        assert (h.s, h.w, h.tc) == (s1, w1, T - s1 - w1)
+        pt = np.frombuffer(er.stream, np.uint16, (s1 + w1) * F, 64).reshape(-1, F)
+        assert np.array_equal(pt[:s1], x[:s1]) and np.array_equal(pt[s1:], x[T - w1:])
+        assert len(er.stream) == 64 + (s1 + w1) * F * 2 + (T - s1 - w1) * sl.record_bytes
+        full, out = O.decode(er.stream, p, sl, 0, 0, T, O.DTYPE_BF16)
+        assert np.array_equal(out[:s1], x[:s1]) and np.array_equal(out[T - w1:], x[T - w1:])
+
+
+def check_header_golden():
+    gd = golden("header_example.json")
+    f = gd["fields"]
+
+    class FakeSlot:
+        G = f["G"]
+        n_act = len(f["widths_active"])
+        record_bytes = 8 * n_act + f["G"] * sum(f["widths_active"]) // 8
+        slot_id = int(f["slot_id"], 16)
+
+    p = O.Params(8, 8, 128, f["sink"], f["window"], f["G"], 8, 1.0, f["dtype"])
+    h = O.make_header(p, FakeSlot, f["layer"], f["kind"], f["T"])
+    assert h.hex() == gd["hex"].replace(" ", ""), h.hex()
+    assert FakeSlot.record_bytes == gd["derived"]["record_bytes"]
+
+
+def check_header_validation():
+    rng = np.random.default_rng(12)
+    F, T = 64, 40
+    p = small_params(F=F)
+    sl = injected_slot(np.eye(F)[:, :16], [4, 0, 0, 0], np.zeros(F, np.float32), 16)
+    er = O.encode(rng.standard_normal((T, F)).astype(np.float32), p, sl, 2, 1)
+    O.decode(er.stream, p, sl, 2, 1, T)
+    bad = []
+    for off in (0, 4, 6, 7, 8, 12, 16, 20, 24, 28, 32, 34, 36, 40, 47):
+        s = bytearray(er.stream)
+        s[off] ^= 0x5A
+        bad.append(bytes(s))
+    for s in bad:
+        try:
+            O.decode(s, p, sl, 2, 1, T)
+        except O.OracleError:
+            continue
+        raise AssertionError("corrupt header accepted")
+    for args in ((3, 1, T), (2, 0, T), (2, 1, T + 1)):
+        try:
+            O.decode(er.stream, p, sl, *args)
+        except O.OracleError:
+            continue
+        raise AssertionError("mismatched job accepted")
+    try:
+        O.decode(er.stream[:-1], p, sl, 2, 1, T)
+    except O.OracleError:
+        pass
+    else:
+        raise AssertionError("truncated stream accepted")
+
+
+def check_artifact_roundtrip():
+    x, _ = family_b_small(seed=13, n=1024)
+    p = O.Params(1, 2, 32, 4, 8, 16, 8, 2.0, O.DTYPE_F32)
+    sl = O.calibrate(x, p, 0, 1)
+    art = O.Artifact(p, {(0, 1): sl})
+    buf = art.serialize()
+    back = O.parse_artifact(buf)
+    s2 = back.slots[(0, 1)]
+    assert np.array_equal(s2.widths, sl.widths) and np.array_equal(s2.V32, sl.V32)
+    assert np.array_equal(s2.mu32, sl.mu32) and np.array_equal(s2.lam, sl.lam)
+    assert s2.slot_id == sl.slot_id
+    raw = bytearray(buf)
+    raw[-20] ^= 1
+    try:
+        O.parse_artifact(bytes(raw))
+    except O.OracleError:
+        pass
+    else:
+        raise AssertionError("corrupt artifact accepted")
+    # layout: slot header and widths at the documented offsets
+    assert buf[48:52] == b"KVTS"
+    assert struct.unpack_from("<7i", buf, 52)[:6] == (0, 1, 64, 16, sl.n_act, sl.r_eff)
+
+
+def check_decode_exact_sum():
+    """x_hat = mu32 + sum_j c_hat_j V'_j, checked element-wise in exact rationals."""
+    rng = np.random.default_rng(14)
+    F, T = 64, 30
+    V32 = np.linalg.qr(rng.standard_normal((F, F)))[0][:, :32].astype(np.float32)
+    mu = rng.standard_normal(F).astype(np.float32)
+    p = small_params(F=F, s=1, w=1)
+    sl = injected_slot(V32, [3, 0, 6, 0], mu, 16)
+    x = (rng.standard_normal((T, F)) + mu).astype(np.float32)
+    er = O.encode(x, p, sl, 0, 0)
+    full, _ = O.decode(er.stream, p, sl, 0, 0, T)
+    import torch
+    Vb = torch.from_numpy(sl.V32).to(torch.bfloat16).double().numpy()
+    Fr = fractions.Fraction
+    for t in (0, 7, 27):
+        for f in (0, 13, 63):
+            acc = Fr(float(mu[f]))
+            for a, b in ((0, 3), (1, 6)):
+                step = np.float32(er.scale[t, a]) / np.float32(2 ** b - 1)
+                for j in range(16):
+                    chat = Fr(float(er.shift[t, a])) + int(er.codes[t, 16 * a + j]) * Fr(float(step))
+                    acc += chat * Fr(float(Vb[f, 16 * a + j]))
+            assert abs(float(acc) - full[t + 1, f]) <= 1e-12 * max(1.0, abs(float(acc)))
+
+
+def check_shapes_vs_page():
+    w = synth.workload("llama31_8b")
+    per_1k = w.n_layers * len(w.kinds) * w.features * 2 * 1024
+    assert per_1k == 128 * 2 ** 20, "Llama 3.1 8B KV at 1K tokens must be 128 MiB"
+
+
+def check_generators():
+    w = synth.workload("tiny")
+    a = synth.gen_kv(w, 0, 0, 1, 300)
+    b = synth.gen_kv(w, 0, 0, 1, 300)
+    c = synth.gen_kv(w, 0, 0, 2, 300)
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+    x = synth.gen_kv(w, 0, 0, 1, 4000).astype(np.float64)
+    ev = np.linalg.eigvalsh(np.cov(x.T))[::-1]
+    assert ev[15] > 50 * ev[16], "family A must have rank 16 above the noise"
+    wb = synth.workload("llama31_8b")
+    y = synth.gen_kv(wb, 0, 0, 1, 64)
+    assert np.array_equal(O.bf16_rne(y), y)
+
+
+ALL = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

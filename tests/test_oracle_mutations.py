@@ -1,0 +1,165 @@
+"""Plant plausible mistakes in the CPU oracle and show that the pins catch them.
+
+Every mutation here is applied to the oracle module only, on the CPU, for the
+duration of one test.  Each must make at least one of the listed pin checks
+fail; that is what makes the pins a real check of the oracle rather than a
+restatement of it.
+"""
+import numpy as np
+import pytest
+
+import oracle.kvtc_oracle as O
+import pins
+
+_orig = {name: getattr(O, name) for name in dir(O) if callable(getattr(O, name))}
+
+
+def _project_no_centering(x_vals, slot):
+    xc = O.bf16_rne(x_vals.astype(np.float32))
+    return (xc.astype(np.float64) @ slot.basis_bf16().astype(np.float64)).astype(np.float32)
+
+
+def _project_fp32_basis(x_vals, slot):
+    xc = O.bf16_rne((x_vals.astype(np.float32) - slot.mu32).astype(np.float32))
+    return (xc.astype(np.float64) @ slot.V32.astype(np.float64)).astype(np.float32)
+
+
+def _dequant_wrong_levels(q, shift, scale, b):
+    step = (np.asarray(scale, np.float32) / np.float32(2 ** b)).astype(np.float32)
+    return shift.astype(np.float64)[:, None] + q * step.astype(np.float64)[:, None]
+
+
+def _dequant_wrong_sign(q, shift, scale, b):
+    return -_orig["dequantize"](q, -shift, scale, b) + 0.0 * q
+
+
+def _pack_msb_first(q, b):
+    T, G = q.shape
+    bits = ((q.astype(np.uint16)[:, :, None] >> np.arange(b - 1, -1, -1, dtype=np.uint16)) & 1)
+    return np.packbits(bits.astype(np.uint8).reshape(T, G * b), axis=1, bitorder="little")
+
+
+def _split_swapped(T, s, w):
+    return _orig["split_rows"](T, w, s)
+
+
+def _pca_unsorted(xc):
+    V, lam = _orig["pca_basis"](xc)
+    return V[:, ::-1].copy(), lam[::-1].copy()
+
+
+def _pca_no_sign(xc):
+    n, F = xc.shape
+    _, s, vt = np.linalg.svd(xc, full_matrices=n < F)
+    V = -vt.T
+    return V, s ** 2 / n
+
+
+def _dp_small_lex(D, G, budget):
+    """Ties resolved toward the smallest widths instead of the largest."""
+    n_g, nb = D.shape
+    f = np.full((n_g + 1, budget + 1), np.inf)
+    f[n_g, 0] = 0.0
+    for g in range(n_g - 1, -1, -1):
+        for u in range(budget + 1):
+            for b in range(nb):
+                c = O.group_cost(b, G)
+                if c <= u:
+                    f[g, u] = min(f[g, u], D[g, b] + f[g + 1, u - c])
+    u = int(np.argmin(f[0]))
+    w = np.zeros(n_g, np.uint8)
+    for g in range(n_g):
+        for b in range(nb):
+            c = O.group_cost(b, G)
+            if c <= u and D[g, b] + f[g + 1, u - c] == f[g, u]:
+                w[g] = b
+                u -= c
+                break
+    return w
+
+
+def _dp_no_scale_cost(D, G, budget):
+    old = O.group_cost
+    try:
+        O.group_cost = lambda b, G: G * b
+        return _orig["dp_allocate"](D, G, budget)
+    finally:
+        O.group_cost = old
+
+
+def _quant_floor(c, b):
+    c = np.asarray(c, np.float32)
+    k = np.float32(2 ** b - 1)
+    shift = c.min(axis=1)
+    scale = (c.max(axis=1) - shift).astype(np.float32)
+    nz = scale > 0
+    inv = np.zeros_like(scale)
+    inv[nz] = k / scale[nz]
+    u = ((c - shift[:, None]).astype(np.float32) * inv[:, None]).astype(np.float32)
+    q = np.clip(np.floor(u), 0, k)
+    q[~nz] = 0
+    return q.astype(np.uint8), shift, scale
+
+
+def _reconstruct_no_mean(codes, shift, scale, slot):
+    return _orig["reconstruct"](codes, shift, scale, slot) - slot.mu32.astype(np.float64)
+
+
+def _distortion_dropped_term(C, G, max_bits):
+    D = _orig["distortion_table"](C, G, max_bits)
+    D[:, 0] = 0.0
+    return D
+
+
+def _calibrate_all_rows(x_cal, params, layer, kind):
+    p2 = O.Params(**{**params.__dict__, "sink": 0, "window": 0})
+    return _orig["calibrate"](x_cal, p2, layer, kind)
+
+
+def _bf16_truncate(x):
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((b >> 16) << 16).view(np.float32).reshape(np.shape(x))
+
+
+def _header_swapped(params, slot, layer, kind, T):
+    p2 = O.Params(**{**params.__dict__, "sink": params.window, "window": params.sink})
+    return _orig["make_header"](p2, slot, layer, kind, T)
+
+
+def _quant_no_clamp(c, b):
+    q, shift, scale = _orig["quantize_fp32"](c, b)
+    return np.where(q == 2 ** b - 1, 0, q).astype(np.uint8), shift, scale
+
+
+MUTATIONS = {
+    "no_centering": ("project", _project_no_centering),
+    "fp32_basis_in_projection": ("project", _project_fp32_basis),
+    "dequant_wrong_levels": ("dequantize", _dequant_wrong_levels),
+    "dequant_wrong_sign": ("dequantize", _dequant_wrong_sign),
+    "pack_msb_first": ("pack_codes", _pack_msb_first),
+    "sink_window_swapped": ("split_rows", _split_swapped),
+    "pca_unsorted": ("pca_basis", _pca_unsorted),
+    "pca_no_sign_rule": ("pca_basis", _pca_no_sign),
+    "dp_no_scale_cost": ("dp_allocate", _dp_no_scale_cost),
+    "dp_ties_smallest": ("dp_allocate", _dp_small_lex),
+    "quant_floor": ("quantize_fp32", _quant_floor),
+    "quant_top_code_lost": ("quantize_fp32", _quant_no_clamp),
+    "reconstruct_no_mean": ("reconstruct", _reconstruct_no_mean),
+    "distortion_dropped_term": ("distortion_table", _distortion_dropped_term),
+    "calibrate_all_rows": ("calibrate", _calibrate_all_rows),
+    "bf16_truncate": ("bf16_rne", _bf16_truncate),
+    "header_fields_swapped": ("make_header", _header_swapped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fake = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fake)
+    failed = []
+    for check in pins.ALL:
+        try:
+            check()
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            failed.append(check.__name__)
+    assert failed, f"mutation {name} was not caught by any pin"
