@@ -1,0 +1,234 @@
+/*
+ * kvtc.h - C ABI of libkvtc, KV-cache transform coding on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method is the one on the page "KV Cache Transform Coding for Compact
+ * Storage in LLM Inference" (gist.science, paper 2511.01815), section 2:
+ *   2A calibration   : PCA basis by SVD, shared across heads and computed once;
+ *                      s sink tokens and w window tokens stay uncompressed;
+ *                      dynamic-programming bit widths under a bit budget;
+ *                      a group of components shares a scale and a shift.
+ *   2B compression   : subtract the mean, multiply by V, quantize, pack
+ *                      (the DEFLATE stage is on the host and only reports the
+ *                      lossless ratio, see kvtc_deflate).
+ *   2C decompression : dequantize, multiply by V^T, add the mean, layer by
+ *                      layer.
+ * The page fixes no formats or arithmetic; the byte formats and rounding rules
+ * implemented here are:
+ *   widths       one width b in 0..max_bits (<= 8) per group of G consecutive
+ *                components (G = group, 16 or 32 in practice, a multiple of 8);
+ *                cost per compressed token: G*b bits + 64 bits (fp32 shift and
+ *                fp32 scale) for every group with b > 0; budget
+ *                floor(bits_per_value * F) bits; ties go to fewer bits, then to
+ *                the lexicographically larger widths.
+ *   quantizer    per (token, active group): shift = min c, scale = max c - min c
+ *                (fp32), q = clamp(rint_even(fp32(c - shift) * fp32(k/scale)),
+ *                0, k) with k = 2^b - 1 and q = 0 when scale == 0.
+ *   projection   x' = bf16_rne(fp32(x) - mu32), c = sum_f x'_f V'_fj with
+ *                V' = bf16_rne(V32); products are exact, accumulation in fp32
+ *                MFMA steps, so a code may differ by one step from an exact sum
+ *                near a rounding boundary.
+ *   dequantize   c_hat = shift + q * fp32(scale / k); dropped groups give 0;
+ *                x_hat = mu32 + sum_j c_hat_j V'_j.
+ *   stream       64-byte header ("KVTC", u16 version=1, u8 dtype, u8 kind,
+ *                u32 layer, T, F, s', w', T_c, u16 G, u16 n_act,
+ *                u32 record_bytes, u64 slot_id, zeros), then the raw rows
+ *                [0, s') and [T - w', T), then T_c records of record_bytes;
+ *                s' = min(s, T), w' = min(w, T - s'), T_c = T - s' - w'.
+ *   record       n_act x (f32 shift, f32 scale), then per active group its G
+ *                codes, code j in bits [j*b, j*b + b) of the group's G*b/8-byte
+ *                chunk, least significant bit first.
+ *   artifact     see kvtc_save.
+ * All multi-byte fields are little-endian.
+ *
+ * Memory and ownership: the caller owns every device buffer (KV tensors,
+ * streams, device state, workspace, staging, block tables) and every stream.
+ * The library owns only the host-side codec. It never allocates device memory;
+ * it enqueues work only on the stream it is given and never synchronises it,
+ * except kvtc_upload and kvtc_read_device_status, which say so.
+ *
+ * Errors: every call returns kvtc_status. Argument, shape, capacity and
+ * calibration errors are found on the host; the call then enqueues nothing
+ * and kvtc_last_error() describes the problem. Stream-content errors (magic,
+ * version, slot id, shape fields) are found on the device: the failing job's
+ * status word in the workspace is set and none of its output rows are written.
+ *
+ * Threads: a codec may be used from several host threads and streams at once
+ * for encode and decode if each concurrent call has its own workspace.
+ * kvtc_calibrate may run concurrently on distinct (layer, kind) slots.
+ */
+#ifndef KVTC_H
+#define KVTC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVTC_OK = 0,
+  KVTC_E_INVALID = -1,         /* bad argument, shape or parameter            */
+  KVTC_E_CAPACITY = -2,        /* an output or workspace buffer is too small  */
+  KVTC_E_CORRUPT = -3,         /* malformed artifact or stream                */
+  KVTC_E_MISMATCH = -4,        /* stream does not belong to this job/codec    */
+  KVTC_E_NOT_CALIBRATED = -5,  /* (layer, kind) has no calibration            */
+  KVTC_E_HIP = -6,             /* a HIP runtime call failed                   */
+  KVTC_E_UNSUPPORTED = -7      /* valid but outside this build's limits       */
+} kvtc_status;
+
+typedef enum { KVTC_F32 = 0, KVTC_BF16 = 1 } kvtc_dtype;
+typedef enum { KVTC_K = 0, KVTC_V = 1 } kvtc_kind;
+
+/* Codec parameters. F = kv_heads * head_dim; feature h*head_dim + i is element
+ * i of head h (heads concatenated, the basis is shared across heads). */
+typedef struct {
+  int32_t n_layers;
+  int32_t kv_heads;
+  int32_t head_dim;
+  int32_t sink;            /* s: oldest tokens kept verbatim                 */
+  int32_t window;          /* w: newest tokens kept verbatim                 */
+  int32_t group;           /* G: components per microscale group             */
+  int32_t max_bits;        /* largest width, 0..8                            */
+  float bits_per_value;    /* budget per compressed value, e.g. 16/ratio     */
+  int32_t dtype;           /* kvtc_dtype of the KV tensors                   */
+} kvtc_params;
+
+typedef struct kvtc_codec kvtc_codec;
+
+/* One tensor of work: the K or V cache of one layer, [n_tokens, F] rows.
+ *   encode:  src = KV rows (device, params.dtype), dst = stream (device).
+ *   decode:  src = stream (device), dst = KV rows (device, out dtype).
+ * block_table (device, int32, decode only): when non-NULL, token t is written
+ * to physical row block_table[t / block_size] * block_size + t % block_size
+ * of dst (a paged cache of [n_blocks, block_size, F]); dst_capacity bounds the
+ * physical rows. */
+typedef struct {
+  int32_t layer;
+  int32_t kind;
+  int64_t n_tokens;
+  const void* src;
+  void* dst;
+  size_t dst_capacity;     /* bytes available at dst                         */
+  const int32_t* block_table;
+  int32_t block_size;
+  int32_t n_blocks;        /* physical blocks in dst when paged              */
+} kvtc_job;
+
+/* Per-slot calibration summary. */
+typedef struct {
+  int32_t calibrated;
+  int32_t n_act;           /* groups with b > 0                              */
+  int32_t r_eff;           /* n_act * G active components                    */
+  int32_t record_bytes;    /* bytes per compressed token                     */
+  uint64_t slot_id;        /* FNV-1a 64 of the slot's serialized bytes       */
+  uint8_t widths[512];     /* width per group (F/G entries)                  */
+} kvtc_slot_info;
+
+/* Largest active component count the kernels accept. */
+#define KVTC_MAX_REFF 256
+/* Largest number of jobs per call. */
+#define KVTC_MAX_JOBS 4096
+
+const char* kvtc_version(void);
+/* Last error message of the calling thread ("" if none). */
+const char* kvtc_last_error(void);
+
+/* Create a codec (host memory only). Fails with KVTC_E_INVALID unless
+ * F % G == 0, G % 8 == 0, 0 <= max_bits <= 8, bits_per_value >= 0,
+ * F / G <= 512 and dtype is KVTC_F32 or KVTC_BF16. */
+kvtc_status kvtc_create(const kvtc_params* params, kvtc_codec** out);
+void kvtc_destroy(kvtc_codec* codec);
+
+/* Calibrate one (layer, kind) on the host (section 2A): rows [s, n - w) of
+ * host_kv ([n_tokens, F], params.dtype storage, host memory, read only) give
+ * the fp64 mean, the covariance, its eigenvectors (a Householder
+ * tridiagonalisation and implicit QL iteration; the eigenvectors of the
+ * covariance are the right singular vectors of the centred rows) sorted by
+ * descending eigenvalue with the largest-magnitude entry of each made
+ * positive, the empirical distortion D_g(b) of the quantizer on the
+ * calibration coefficients, and the DP widths. n_tokens - s - w must be >= 1.
+ * Returns KVTC_E_UNSUPPORTED if the widths need more than KVTC_MAX_REFF active
+ * components. Uses up to `threads` host threads (0 = hardware concurrency). */
+kvtc_status kvtc_calibrate(kvtc_codec* codec, int32_t layer, int32_t kind,
+                           const void* host_kv, int64_t n_tokens, int32_t threads);
+
+kvtc_status kvtc_slot_info_get(const kvtc_codec* codec, int32_t layer, int32_t kind,
+                               kvtc_slot_info* info);
+
+/* Serialize every calibrated slot. With buf == NULL, only *written (the size
+ * needed) is set. Format (little-endian): "KVTA", u32 version=1, i32 n_layers,
+ * kv_heads, head_dim, sink, window, group, max_bits, f32 bits_per_value,
+ * i32 dtype, i32 n_slots, then per slot in (layer, kind) order: "KVTS",
+ * i32 layer, kind, F, G, n_act, r_eff, 0, u8 widths[F/G] zero-padded to a
+ * multiple of 8, f32 mu32[F], f64 lambda[F], f32 V32[F][r_eff] (active columns
+ * in component order), u64 slot_id = FNV-1a 64 of the slot's preceding bytes. */
+kvtc_status kvtc_save(const kvtc_codec* codec, void* buf, size_t cap, size_t* written);
+/* Create a codec from artifact bytes (host memory); checks every slot id. */
+kvtc_status kvtc_load(const void* buf, size_t n, kvtc_codec** out);
+
+/* Device state: the operational basis in the layouts the kernels read, the
+ * means and the per-slot descriptors. kvtc_upload copies it into the caller's
+ * device buffer d_state (>= kvtc_device_state_bytes bytes, 256-byte aligned)
+ * on `stream` and synchronises that stream before returning. Encode and decode
+ * use the buffer of the last upload; re-upload after any new calibration. */
+size_t kvtc_device_state_bytes(const kvtc_codec* codec);
+kvtc_status kvtc_upload(kvtc_codec* codec, void* d_state, size_t bytes, hipStream_t stream);
+
+/* Exact stream size for a tensor of n_tokens rows (0 if not calibrated). */
+size_t kvtc_encoded_bytes(const kvtc_codec* codec, int32_t layer, int32_t kind,
+                          int64_t n_tokens);
+/* Workspace (device) for a call with up to max_jobs jobs: one int32 status
+ * word per job, 256-byte aligned. */
+size_t kvtc_workspace_bytes(int32_t max_jobs);
+
+/* Encode n_jobs tensors in one launch (section 2B). Each job's dst must hold
+ * kvtc_encoded_bytes. d_ws: workspace for n_jobs jobs. */
+kvtc_status kvtc_encode(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
+                        void* d_ws, hipStream_t stream);
+
+/* Decode n_jobs streams in one launch (section 2C), writing out_dtype rows.
+ * Passthrough rows are copied bit for bit when out_dtype equals the codec
+ * dtype (converted with round-to-nearest-even otherwise). */
+kvtc_status kvtc_decode(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
+                        int32_t out_dtype, void* d_ws, hipStream_t stream);
+
+/* Two-stage decode for layer-by-layer pipelines (section 2C: decompression
+ * can proceed layer by layer). Stage 1 validates headers, copies passthrough
+ * rows to dst and unpacks records into d_staging; stage 2 dequantizes,
+ * applies V^T, adds the mean and writes the compressed rows to dst. Both
+ * stages must see the same jobs, staging and workspace. Staging layout per job
+ * (consecutive, each 256-byte aligned): u8 codes[T_c][r_eff], then
+ * f32 shift_scale[T_c][n_act][2]. */
+size_t kvtc_staging_bytes(const kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs);
+kvtc_status kvtc_decode_unpack(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
+                               int32_t out_dtype, void* d_staging, size_t staging_bytes,
+                               void* d_ws, hipStream_t stream);
+kvtc_status kvtc_decode_restore(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
+                                int32_t out_dtype, const void* d_staging,
+                                size_t staging_bytes, void* d_ws, hipStream_t stream);
+
+/* Test hook: build the whole stream of one job from given codes
+ * (u8 [T_c][r_eff], device) and shift/scale pairs (f32 [T_c][n_act][2],
+ * device) with the encoder's own record packing; job.src supplies the
+ * passthrough rows. */
+kvtc_status kvtc_pack(kvtc_codec* codec, const kvtc_job* job, const void* d_codes,
+                      const void* d_shift_scale, void* d_ws, hipStream_t stream);
+
+/* Copy n_jobs status words from the workspace to host memory. This
+ * synchronises `stream` first. Each word is KVTC_OK or a kvtc_status. */
+kvtc_status kvtc_read_device_status(const void* d_ws, int32_t n_jobs, int32_t* status,
+                                    hipStream_t stream);
+
+/* Host DEFLATE (zlib, the given level) of n bytes of host memory, for the
+ * lossless ratio of section 2B. With out == NULL only *out_len (an upper
+ * bound) is set. */
+kvtc_status kvtc_deflate(const void* in, size_t n, void* out, size_t cap, size_t* out_len,
+                         int32_t level);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVTC_H */

@@ -1,0 +1,797 @@
+// Host core of libkvtc: codec state, calibration (page "KV Cache Transform
+// Coding for Compact Storage in LLM Inference", section 2A), artifact and
+// stream sizes, device-state upload, job validation and kernel launches.
+#include <zlib.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <limits>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "kvtc_internal.h"
+#include "kvtc_linalg.h"
+
+using namespace kvtc;
+
+namespace {
+
+thread_local std::string g_err;
+
+kvtc_status fail(kvtc_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+struct Slot {
+  bool calibrated = false;
+  std::vector<uint8_t> widths;   // [F/G]
+  std::vector<float> mu32;       // [F]
+  std::vector<double> lam;       // [F]
+  std::vector<float> V32;        // [F][r_eff]
+  int n_act = 0, r_eff = 0, record_bytes = 0;
+  uint64_t slot_id = 0;
+  std::vector<uint8_t> bytes;    // serialized slot (including the id)
+};
+
+uint64_t fnv1a64(const uint8_t* p, size_t n) {
+  uint64_t h = 0xCBF29CE484222325ull;
+  for (size_t i = 0; i < n; ++i) {
+    h ^= p[i];
+    h *= 0x100000001B3ull;
+  }
+  return h;
+}
+
+template <class T>
+void put(std::vector<uint8_t>& b, const T& v) {
+  const uint8_t* p = reinterpret_cast<const uint8_t*>(&v);
+  b.insert(b.end(), p, p + sizeof(T));
+}
+
+uint16_t f32_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+float bf16_to_f32(uint16_t b) {
+  const uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// fp32 -> fp16 bits, round to nearest even, with subnormals.
+uint16_t f32_to_f16(float f) {
+  uint32_t x;
+  std::memcpy(&x, &f, 4);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7FFFFFFFu;
+  if (ax >= 0x7F800000u) return (uint16_t)(sign | (ax > 0x7F800000u ? 0x7E00u : 0x7C00u));
+  if (ax >= 0x47800000u) return (uint16_t)(sign | 0x7C00u);  // >= 65536
+  if (ax < 0x38800000u) {                                    // below 2^-14
+    float a;
+    std::memcpy(&a, &ax, 4);
+    const uint32_t m = (uint32_t)std::nearbyint(a * 16777216.0f);  // units of 2^-24
+    return (uint16_t)(sign | m);
+  }
+  const uint32_t mant = ax & 0x7FFFFFu;
+  uint32_t h = ((((ax >> 23) - 112u)) << 10) | (mant >> 13);
+  const uint32_t rem = mant & 0x1FFFu;
+  if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) ++h;
+  return (uint16_t)(sign | h);
+}
+
+}  // namespace
+
+struct kvtc_codec {
+  kvtc_params p;
+  int F = 0, n_g = 0;
+  std::vector<Slot> slots;                // n_layers * 2
+  std::mutex mu;                          // guards the version counters
+  uint64_t calib_version = 0;
+  uint64_t uploaded_version = ~0ull;
+  const uint8_t* d_state = nullptr;
+  size_t d_state_bytes = 0;
+};
+
+namespace {
+
+kvtc_status check_params(const kvtc_params* p) {
+  if (!p) return fail(KVTC_E_INVALID, "null params");
+  if (p->n_layers <= 0 || p->kv_heads <= 0 || p->head_dim <= 0)
+    return fail(KVTC_E_INVALID, "n_layers, kv_heads and head_dim must be positive");
+  const long F = (long)p->kv_heads * p->head_dim;
+  if (F > 65536) return fail(KVTC_E_INVALID, "F too large");
+  if (p->group <= 0 || p->group % 8 || F % p->group)
+    return fail(KVTC_E_INVALID, "group must be a positive multiple of 8 dividing F");
+  if (F / p->group > 512) return fail(KVTC_E_INVALID, "more than 512 groups");
+  if (p->max_bits < 0 || p->max_bits > 8) return fail(KVTC_E_INVALID, "max_bits must be in 0..8");
+  if (!(p->bits_per_value >= 0.f) || !std::isfinite(p->bits_per_value))
+    return fail(KVTC_E_INVALID, "bits_per_value must be finite and >= 0");
+  if (p->sink < 0 || p->window < 0) return fail(KVTC_E_INVALID, "negative sink or window");
+  if (p->dtype != KVTC_F32 && p->dtype != KVTC_BF16) return fail(KVTC_E_INVALID, "bad dtype");
+  return KVTC_OK;
+}
+
+long budget_bits(const kvtc_params& p) {
+  return (long)std::floor((double)p.bits_per_value * (double)(p.kv_heads * p.head_dim));
+}
+
+int group_cost(int b, int G) { return G * b + (b > 0 ? kScaleBits : 0); }
+
+// DP bit allocation (section 2A): minimise sum_g D[g][b_g] subject to
+// sum_g cost(b_g) <= budget. f[g][u] is the least distortion of groups g..
+// spending exactly u bits, f[g][u] = min_b D[g][b] + f[g+1][u - cost(b)],
+// evaluated from the last group so that every objective is the nested sum
+// D[0] + (D[1] + (... + 0)). Ties: fewest bits, then the lexicographically
+// largest widths (largest b first when walking forward).
+std::vector<uint8_t> dp_allocate(const std::vector<double>& D, int n_g, int nb, int G, long budget) {
+  const double INF = std::numeric_limits<double>::infinity();
+  const long U = budget + 1;
+  std::vector<double> f((size_t)(n_g + 1) * U, INF);
+  f[(size_t)n_g * U + 0] = 0.0;
+  for (int g = n_g - 1; g >= 0; --g) {
+    const double* nxt = f.data() + (size_t)(g + 1) * U;
+    double* cur = f.data() + (size_t)g * U;
+    for (long u = 0; u < U; ++u) {
+      double best = INF;
+      for (int b = 0; b < nb; ++b) {
+        const long c = group_cost(b, G);
+        if (c <= u && nxt[u - c] < INF) {
+          const double v = D[(size_t)g * nb + b] + nxt[u - c];
+          if (v < best) best = v;
+        }
+      }
+      cur[u] = best;
+    }
+  }
+  long u = 0;
+  for (long v = 1; v < U; ++v)
+    if (f[v] < f[u]) u = v;
+  std::vector<uint8_t> w(n_g, 0);
+  for (int g = 0; g < n_g; ++g) {
+    for (int b = nb - 1; b >= 0; --b) {
+      const long c = group_cost(b, G);
+      if (c <= u && D[(size_t)g * nb + b] + f[(size_t)(g + 1) * U + u - c] == f[(size_t)g * U + u]) {
+        w[g] = (uint8_t)b;
+        u -= c;
+        break;
+      }
+    }
+  }
+  return w;
+}
+
+void finish_slot(const kvtc_params& p, int layer, int kind, Slot& s) {
+  const int F = p.kv_heads * p.head_dim, G = p.group, n_g = F / G;
+  s.n_act = 0;
+  int sum_b = 0;
+  for (int g = 0; g < n_g; ++g)
+    if (s.widths[g]) {
+      ++s.n_act;
+      sum_b += s.widths[g];
+    }
+  s.r_eff = s.n_act * G;
+  s.record_bytes = 8 * s.n_act + G * sum_b / 8;
+  std::vector<uint8_t> b;
+  b.insert(b.end(), {'K', 'V', 'T', 'S'});
+  const int32_t hdr[7] = {layer, kind, F, G, s.n_act, s.r_eff, 0};
+  for (int32_t v : hdr) put(b, v);
+  const size_t wpad = (size_t)(n_g + 7) / 8 * 8;
+  for (size_t i = 0; i < wpad; ++i) b.push_back(i < (size_t)n_g ? s.widths[i] : 0);
+  for (float v : s.mu32) put(b, v);
+  for (double v : s.lam) put(b, v);
+  for (float v : s.V32) put(b, v);
+  s.slot_id = fnv1a64(b.data(), b.size());
+  put(b, s.slot_id);
+  s.bytes.swap(b);
+  s.calibrated = true;
+}
+
+bool slot_index(const kvtc_codec* c, int layer, int kind, int* idx) {
+  if (!c || layer < 0 || layer >= c->p.n_layers || (kind != KVTC_K && kind != KVTC_V)) return false;
+  *idx = layer * 2 + kind;
+  return true;
+}
+
+void split_rows(long T, const kvtc_params& p, uint32_t* s1, uint32_t* w1, uint32_t* tc) {
+  const long s = std::min<long>(p.sink, T);
+  const long w = std::min<long>(p.window, T - s);
+  *s1 = (uint32_t)s;
+  *w1 = (uint32_t)w;
+  *tc = (uint32_t)(T - s - w);
+}
+
+size_t elem_bytes(int dtype) { return dtype == KVTC_F32 ? 4 : 2; }
+
+size_t stream_bytes(const kvtc_codec* c, const Slot& s, long T) {
+  uint32_t s1, w1, tc;
+  split_rows(T, c->p, &s1, &w1, &tc);
+  return kHeaderBytes + (size_t)(s1 + w1) * c->F * elem_bytes(c->p.dtype) + (size_t)tc * s.record_bytes;
+}
+
+size_t job_staging_bytes(const Slot& s, uint32_t tc) {
+  return align_up((size_t)tc * s.r_eff, kAlign) + align_up((size_t)tc * s.n_act * 8, kAlign);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvtc_version(void) { return "kvtc 0.1 gfx950"; }
+
+const char* kvtc_last_error(void) { return g_err.c_str(); }
+
+kvtc_status kvtc_create(const kvtc_params* params, kvtc_codec** out) {
+  if (!out) return fail(KVTC_E_INVALID, "null output pointer");
+  *out = nullptr;
+  const kvtc_status st = check_params(params);
+  if (st != KVTC_OK) return st;
+  auto c = std::make_unique<kvtc_codec>();
+  c->p = *params;
+  c->F = params->kv_heads * params->head_dim;
+  c->n_g = c->F / params->group;
+  c->slots.resize((size_t)params->n_layers * 2);
+  *out = c.release();
+  return KVTC_OK;
+}
+
+void kvtc_destroy(kvtc_codec* codec) { delete codec; }
+
+kvtc_status kvtc_calibrate(kvtc_codec* c, int32_t layer, int32_t kind, const void* host_kv,
+                           int64_t n_tokens, int32_t threads) {
+  int idx;
+  if (!slot_index(c, layer, kind, &idx)) return fail(KVTC_E_INVALID, "bad codec, layer or kind");
+  if (!host_kv) return fail(KVTC_E_INVALID, "null calibration data");
+  const kvtc_params& p = c->p;
+  const int F = c->F, G = p.group, n_g = c->n_g, nb = p.max_bits + 1;
+  const long n_r = (long)n_tokens - p.sink - p.window;
+  if (n_tokens < 0 || n_r < 1) return fail(KVTC_E_INVALID, "need at least one row after sink and window");
+  if (threads <= 0) threads = std::max(1u, std::thread::hardware_concurrency());
+
+  // Rows [s, n - w) in fp64.
+  std::vector<double> X((size_t)n_r * F);
+  parallel_for((int)std::min<long>(n_r, 1L << 30), threads, [&](int t) {
+    const size_t src_row = (size_t)(t + p.sink) * F;
+    double* xr = X.data() + (size_t)t * F;
+    if (p.dtype == KVTC_BF16) {
+      const uint16_t* s = (const uint16_t*)host_kv + src_row;
+      for (int f = 0; f < F; ++f) xr[f] = bf16_to_f32(s[f]);
+    } else {
+      const float* s = (const float*)host_kv + src_row;
+      for (int f = 0; f < F; ++f) xr[f] = s[f];
+    }
+  });
+  // Mean (section 2B subtracts it before the transform).
+  std::vector<double> mu(F, 0.0);
+  for (long t = 0; t < n_r; ++t) {
+    const double* xr = X.data() + (size_t)t * F;
+    for (int f = 0; f < F; ++f) mu[f] += xr[f];
+  }
+  for (int f = 0; f < F; ++f) mu[f] /= (double)n_r;
+  parallel_for((int)n_r, threads, [&](int t) {
+    double* xr = X.data() + (size_t)t * F;
+    for (int f = 0; f < F; ++f) xr[f] -= mu[f];
+  });
+  // Covariance; its eigenvectors are the right singular vectors of the
+  // centred rows (the SVD of section 2A) and its eigenvalues are sigma^2/n.
+  std::vector<double> cov((size_t)F * F);
+  gemm_f64(F, F, (int)n_r, X.data(), 1, F, X.data(), F, cov.data(), F, true, threads);
+  for (int i = 0; i < F; ++i)
+    for (int j = 0; j < i; ++j) cov[(size_t)i * F + j] = cov[(size_t)j * F + i];
+  for (auto& v : cov) v /= (double)n_r;
+  std::vector<double> evals, zt;
+  if (sym_eigen(F, cov, evals, zt) != 0) return fail(KVTC_E_INVALID, "eigensolver did not converge");
+  std::vector<int> order(F);
+  for (int j = 0; j < F; ++j) order[j] = j;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return evals[a] > evals[b]; });
+  std::vector<double> V((size_t)F * F);  // V[f][j], column j = component j
+  std::vector<double> lam(F);
+  for (int j = 0; j < F; ++j) {
+    const double* z = zt.data() + (size_t)order[j] * F;
+    lam[j] = evals[order[j]];
+    int imax = 0;
+    for (int f = 1; f < F; ++f)
+      if (std::fabs(z[f]) > std::fabs(z[imax])) imax = f;
+    const double sgn = z[imax] < 0 ? -1.0 : 1.0;
+    for (int f = 0; f < F; ++f) V[(size_t)f * F + j] = sgn * z[f];
+  }
+  // Calibration coefficients and the empirical distortion table.
+  std::vector<double> C((size_t)n_r * F);
+  gemm_f64((int)n_r, F, F, X.data(), F, 1, V.data(), F, C.data(), F, false, threads);
+  X.clear();
+  X.shrink_to_fit();
+  std::vector<double> D((size_t)n_g * nb, 0.0);
+  parallel_for(n_g, threads, [&](int g) {
+    std::vector<double> acc(nb, 0.0);
+    for (long t = 0; t < n_r; ++t) {
+      const double* cg = C.data() + (size_t)t * F + (size_t)g * G;
+      double mn = cg[0], mx = cg[0], e0 = 0.0;
+      for (int i = 0; i < G; ++i) {
+        mn = std::min(mn, cg[i]);
+        mx = std::max(mx, cg[i]);
+        e0 += cg[i] * cg[i];
+      }
+      acc[0] += e0;
+      const double scale = mx - mn;
+      for (int b = 1; b < nb; ++b) {
+        if (!(scale > 0)) continue;  // every value equals the shift: no error
+        const double k = (double)((1 << b) - 1);
+        const double inv = k / scale, step = scale / k;
+        double e = 0.0;
+        for (int i = 0; i < G; ++i) {
+          double q = std::nearbyint((cg[i] - mn) * inv);
+          q = std::min(std::max(q, 0.0), k);
+          const double d = cg[i] - (mn + q * step);
+          e += d * d;
+        }
+        acc[b] += e;
+      }
+    }
+    for (int b = 0; b < nb; ++b) D[(size_t)g * nb + b] = acc[b] / (double)n_r;
+  });
+  C.clear();
+  C.shrink_to_fit();
+  Slot s;
+  s.widths = dp_allocate(D, n_g, nb, G, budget_bits(p));
+  int n_act = 0;
+  for (int g = 0; g < n_g; ++g) n_act += s.widths[g] ? 1 : 0;
+  if (n_act * G > KVTC_MAX_REFF)
+    return fail(KVTC_E_UNSUPPORTED, "allocation needs more than KVTC_MAX_REFF active components");
+  s.mu32.resize(F);
+  for (int f = 0; f < F; ++f) s.mu32[f] = (float)mu[f];
+  s.lam = lam;
+  s.V32.resize((size_t)F * n_act * G);
+  int a = 0;
+  for (int g = 0; g < n_g; ++g) {
+    if (!s.widths[g]) continue;
+    for (int i = 0; i < G; ++i)
+      for (int f = 0; f < F; ++f)
+        s.V32[(size_t)f * n_act * G + a * G + i] = (float)V[(size_t)f * F + g * G + i];
+    ++a;
+  }
+  finish_slot(p, layer, kind, s);
+  c->slots[idx] = std::move(s);
+  std::lock_guard<std::mutex> lk(c->mu);
+  ++c->calib_version;
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_slot_info_get(const kvtc_codec* c, int32_t layer, int32_t kind, kvtc_slot_info* info) {
+  int idx;
+  if (!slot_index(c, layer, kind, &idx) || !info) return fail(KVTC_E_INVALID, "bad arguments");
+  std::memset(info, 0, sizeof(*info));
+  const Slot& s = c->slots[idx];
+  info->calibrated = s.calibrated;
+  if (!s.calibrated) return KVTC_OK;
+  info->n_act = s.n_act;
+  info->r_eff = s.r_eff;
+  info->record_bytes = s.record_bytes;
+  info->slot_id = s.slot_id;
+  for (int g = 0; g < c->n_g && g < 512; ++g) info->widths[g] = s.widths[g];
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_save(const kvtc_codec* c, void* buf, size_t cap, size_t* written) {
+  if (!c || !written) return fail(KVTC_E_INVALID, "bad arguments");
+  std::vector<uint8_t> b;
+  b.insert(b.end(), {'K', 'V', 'T', 'A'});
+  put(b, (uint32_t)kFormatVersion);
+  const int32_t hdr[7] = {c->p.n_layers, c->p.kv_heads, c->p.head_dim, c->p.sink,
+                          c->p.window, c->p.group, c->p.max_bits};
+  for (int32_t v : hdr) put(b, v);
+  put(b, c->p.bits_per_value);
+  put(b, (int32_t)c->p.dtype);
+  int32_t n = 0;
+  for (const Slot& s : c->slots) n += s.calibrated;
+  put(b, n);
+  for (const Slot& s : c->slots)
+    if (s.calibrated) b.insert(b.end(), s.bytes.begin(), s.bytes.end());
+  *written = b.size();
+  if (!buf) return KVTC_OK;
+  if (cap < b.size()) return fail(KVTC_E_CAPACITY, "artifact buffer too small");
+  std::memcpy(buf, b.data(), b.size());
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_load(const void* buf, size_t n, kvtc_codec** out) {
+  if (!buf || !out) return fail(KVTC_E_INVALID, "bad arguments");
+  *out = nullptr;
+  const uint8_t* b = (const uint8_t*)buf;
+  size_t off = 0;
+  auto need = [&](size_t k) { return off + k <= n; };
+  auto rd32 = [&](int32_t* v) {
+    std::memcpy(v, b + off, 4);
+    off += 4;
+  };
+  if (!need(48) || std::memcmp(b, "KVTA", 4) != 0) return fail(KVTC_E_CORRUPT, "bad artifact magic");
+  off = 4;
+  int32_t ver;
+  rd32(&ver);
+  if (ver != kFormatVersion) return fail(KVTC_E_CORRUPT, "bad artifact version");
+  kvtc_params p;
+  rd32(&p.n_layers);
+  rd32(&p.kv_heads);
+  rd32(&p.head_dim);
+  rd32(&p.sink);
+  rd32(&p.window);
+  rd32(&p.group);
+  rd32(&p.max_bits);
+  std::memcpy(&p.bits_per_value, b + off, 4);
+  off += 4;
+  rd32(&p.dtype);
+  int32_t n_slots;
+  rd32(&n_slots);
+  kvtc_codec* c = nullptr;
+  kvtc_status st = kvtc_create(&p, &c);
+  if (st != KVTC_OK) return fail(KVTC_E_CORRUPT, std::string("artifact parameters: ") + g_err);
+  std::unique_ptr<kvtc_codec> guard(c);
+  const int F = c->F, G = p.group, n_g = c->n_g;
+  for (int i = 0; i < n_slots; ++i) {
+    const size_t start = off;
+    if (!need(32) || std::memcmp(b + off, "KVTS", 4) != 0) return fail(KVTC_E_CORRUPT, "bad slot magic");
+    off += 4;
+    int32_t layer, kind, sF, sG, n_act, r_eff, zero;
+    rd32(&layer);
+    rd32(&kind);
+    rd32(&sF);
+    rd32(&sG);
+    rd32(&n_act);
+    rd32(&r_eff);
+    rd32(&zero);
+    int idx;
+    if (!slot_index(c, layer, kind, &idx) || sF != F || sG != G || r_eff != n_act * G ||
+        n_act < 0 || n_act > n_g)
+      return fail(KVTC_E_CORRUPT, "inconsistent slot header");
+    if (r_eff > KVTC_MAX_REFF) return fail(KVTC_E_UNSUPPORTED, "slot exceeds KVTC_MAX_REFF");
+    const size_t wpad = (size_t)(n_g + 7) / 8 * 8;
+    const size_t body = wpad + 4 * (size_t)F + 8 * (size_t)F + 4 * (size_t)F * r_eff + 8;
+    if (!need(body)) return fail(KVTC_E_CORRUPT, "truncated slot");
+    Slot s;
+    s.widths.assign(b + off, b + off + n_g);
+    off += wpad;
+    int cnt = 0;
+    for (uint8_t w : s.widths) {
+      if (w > p.max_bits) return fail(KVTC_E_CORRUPT, "width above max_bits");
+      cnt += w ? 1 : 0;
+    }
+    if (cnt != n_act) return fail(KVTC_E_CORRUPT, "n_act does not match widths");
+    s.mu32.resize(F);
+    std::memcpy(s.mu32.data(), b + off, 4 * (size_t)F);
+    off += 4 * (size_t)F;
+    s.lam.resize(F);
+    std::memcpy(s.lam.data(), b + off, 8 * (size_t)F);
+    off += 8 * (size_t)F;
+    s.V32.resize((size_t)F * r_eff);
+    std::memcpy(s.V32.data(), b + off, 4 * (size_t)F * r_eff);
+    off += 4 * (size_t)F * r_eff;
+    uint64_t id;
+    std::memcpy(&id, b + off, 8);
+    if (fnv1a64(b + start, off - start) != id) return fail(KVTC_E_CORRUPT, "slot id mismatch");
+    off += 8;
+    finish_slot(p, layer, kind, s);
+    c->slots[idx] = std::move(s);
+  }
+  c->calib_version = 1;
+  *out = guard.release();
+  return KVTC_OK;
+}
+
+size_t kvtc_device_state_bytes(const kvtc_codec* c) {
+  if (!c) return 0;
+  size_t n = align_up(c->slots.size() * sizeof(DevSlot), kAlign);
+  for (const Slot& s : c->slots) {
+    if (!s.calibrated) continue;
+    const size_t r_enc = align_up((size_t)s.r_eff, 32), r_dec = align_up((size_t)s.r_eff, 16);
+    n += align_up(4 * (size_t)c->F, kAlign) + align_up(2 * r_enc * c->F, kAlign) +
+         align_up(2 * (size_t)c->F * r_dec, kAlign);
+  }
+  return n;
+}
+
+kvtc_status kvtc_upload(kvtc_codec* c, void* d_state, size_t bytes, hipStream_t stream) {
+  if (!c || !d_state) return fail(KVTC_E_INVALID, "bad arguments");
+  if ((uintptr_t)d_state % kAlign) return fail(KVTC_E_INVALID, "device state must be 256-byte aligned");
+  const size_t need = kvtc_device_state_bytes(c);
+  if (bytes < need) return fail(KVTC_E_CAPACITY, "device state buffer too small");
+  if (c->p.group != 16 && c->p.group != 32)
+    return fail(KVTC_E_UNSUPPORTED, "the kernels support group sizes 16 and 32");
+  if (c->F % 64) return fail(KVTC_E_UNSUPPORTED, "the kernels need F to be a multiple of 64");
+  std::vector<uint8_t> h(need, 0);
+  std::vector<DevSlot> table(c->slots.size());
+  std::memset(table.data(), 0, table.size() * sizeof(DevSlot));
+  size_t off = align_up(c->slots.size() * sizeof(DevSlot), kAlign);
+  const int F = c->F, G = c->p.group;
+  for (size_t i = 0; i < c->slots.size(); ++i) {
+    const Slot& s = c->slots[i];
+    DevSlot& d = table[i];
+    if (!s.calibrated) continue;
+    const int r = s.r_eff;
+    const int r_enc = (int)align_up(r, 32), r_dec = (int)align_up(r, 16);
+    d.calibrated = 1;
+    d.n_act = s.n_act;
+    d.r_eff = r;
+    d.record_bytes = s.record_bytes;
+    d.r_enc = r_enc;
+    d.r_dec = r_dec;
+    d.G = G;
+    d.F = F;
+    d.slot_id = s.slot_id;
+    int a = 0, chunk = 8 * s.n_act;
+    for (int g = 0; g < c->n_g; ++g) {
+      if (!s.widths[g]) continue;
+      d.width[a] = s.widths[g];
+      d.chunk_off[a] = (uint16_t)chunk;
+      chunk += G * s.widths[g] / 8;
+      ++a;
+    }
+    d.mu_off = off;
+    std::memcpy(h.data() + off, s.mu32.data(), 4 * (size_t)F);
+    off += align_up(4 * (size_t)F, kAlign);
+    d.venc_off = off;
+    uint16_t* venc = (uint16_t*)(h.data() + off);  // V'^T [r_enc][F] bf16
+    for (int j = 0; j < r; ++j)
+      for (int f = 0; f < F; ++f) venc[(size_t)j * F + f] = f32_to_bf16(s.V32[(size_t)f * r + j]);
+    off += align_up(2 * (size_t)r_enc * F, kAlign);
+    d.vdec_off = off;
+    uint16_t* vdec = (uint16_t*)(h.data() + off);  // V' [F][r_dec] fp16
+    for (int f = 0; f < F; ++f)
+      for (int j = 0; j < r; ++j)
+        vdec[(size_t)f * r_dec + j] = f32_to_f16(bf16_to_f32(f32_to_bf16(s.V32[(size_t)f * r + j])));
+    off += align_up(2 * (size_t)F * r_dec, kAlign);
+  }
+  std::memcpy(h.data(), table.data(), table.size() * sizeof(DevSlot));
+  hipError_t e = hipMemcpyAsync(d_state, h.data(), need, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(KVTC_E_HIP, std::string("upload: ") + hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(c->mu);
+  c->d_state = (const uint8_t*)d_state;
+  c->d_state_bytes = need;
+  c->uploaded_version = c->calib_version;
+  return KVTC_OK;
+}
+
+size_t kvtc_encoded_bytes(const kvtc_codec* c, int32_t layer, int32_t kind, int64_t n_tokens) {
+  int idx;
+  if (!slot_index(c, layer, kind, &idx) || n_tokens < 0 || !c->slots[idx].calibrated) return 0;
+  return stream_bytes(c, c->slots[idx], n_tokens);
+}
+
+size_t kvtc_workspace_bytes(int32_t max_jobs) {
+  return align_up((size_t)std::max(max_jobs, 1) * sizeof(int32_t), kAlign);
+}
+
+size_t kvtc_staging_bytes(const kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs) {
+  if (!c || !jobs || n_jobs <= 0) return 0;
+  size_t n = 0;
+  for (int i = 0; i < n_jobs; ++i) {
+    int idx;
+    if (!slot_index(c, jobs[i].layer, jobs[i].kind, &idx) || !c->slots[idx].calibrated) return 0;
+    uint32_t s1, w1, tc;
+    split_rows(jobs[i].n_tokens, c->p, &s1, &w1, &tc);
+    n += job_staging_bytes(c->slots[idx], tc);
+  }
+  return n;
+}
+
+}  // extern "C"
+
+namespace {
+
+enum class Mode { Encode, Decode, Unpack, Restore, Pack };
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validate jobs [0, n) on the host and fill LaunchArgs batches.
+kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_dtype, void* d_ws,
+                 uint8_t* d_staging, size_t staging_bytes, std::vector<LaunchArgs>& batches,
+                 std::vector<int>& kmax, std::vector<size_t>& lds) {
+  if (!c || !jobs || n <= 0 || n > KVTC_MAX_JOBS) return fail(KVTC_E_INVALID, "bad codec, jobs or job count");
+  if (!d_ws || !aligned16(d_ws)) return fail(KVTC_E_INVALID, "workspace must be non-null and aligned");
+  if (!c->d_state || c->uploaded_version != c->calib_version)
+    return fail(KVTC_E_INVALID, "device state is missing or stale: call kvtc_upload");
+  if (mode != Mode::Encode && mode != Mode::Pack && out_dtype != KVTC_F32 && out_dtype != KVTC_BF16)
+    return fail(KVTC_E_INVALID, "bad output dtype");
+  const int F = c->F;
+  const size_t in_esz = elem_bytes(c->p.dtype);
+  const size_t out_esz = elem_bytes(out_dtype);
+  size_t st_off = 0;
+  for (int b0 = 0; b0 < n; b0 += kMaxLaunchJobs) {
+    LaunchArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.n_jobs = std::min(kMaxLaunchJobs, n - b0);
+    a.dtype = c->p.dtype;
+    a.out_dtype = out_dtype;
+    a.F = F;
+    a.state = c->d_state;
+    a.status = (int32_t*)d_ws + b0;
+    uint32_t tiles = 0;
+    int km = 0;
+    size_t rb_max = 0, r_enc_max = 0;
+    for (int i = 0; i < a.n_jobs; ++i) {
+      const kvtc_job& j = jobs[b0 + i];
+      int idx;
+      if (!slot_index(c, j.layer, j.kind, &idx)) return fail(KVTC_E_INVALID, "job: bad layer or kind");
+      const Slot& s = c->slots[idx];
+      if (!s.calibrated) return fail(KVTC_E_NOT_CALIBRATED, "job: (layer, kind) is not calibrated");
+      if (j.n_tokens < 0 || j.n_tokens > (int64_t)INT32_MAX) return fail(KVTC_E_INVALID, "job: bad n_tokens");
+      if (!j.dst || !aligned16(j.dst)) return fail(KVTC_E_INVALID, "job: dst must be non-null and 16-byte aligned");
+      if (!j.src || !aligned16(j.src)) return fail(KVTC_E_INVALID, "job: src must be non-null and 16-byte aligned");
+      JobDesc& d = a.jobs[i];
+      d.src = j.src;
+      d.dst = j.dst;
+      d.T = (uint32_t)j.n_tokens;
+      split_rows(j.n_tokens, c->p, &d.s1, &d.w1, &d.tc);
+      d.slot = idx;
+      d.layer = j.layer;
+      d.kind = j.kind;
+      const uint32_t ptiles = (d.s1 + d.w1 + kPassRows - 1) / kPassRows;
+      if (mode == Mode::Encode || mode == Mode::Pack) {
+        if (j.dst_capacity < stream_bytes(c, s, j.n_tokens))
+          return fail(KVTC_E_CAPACITY, "job: dst_capacity below kvtc_encoded_bytes");
+        d.n_ctiles = (d.tc + kEncTile - 1) / kEncTile;
+        d.tile_begin = tiles;
+        tiles += std::max<uint32_t>(1, d.n_ctiles + ptiles);
+      } else {
+        if (j.block_table) {
+          if (j.block_size <= 0 || j.n_blocks <= 0) return fail(KVTC_E_INVALID, "job: bad paging");
+          if ((size_t)j.n_blocks * j.block_size * F * out_esz > j.dst_capacity)
+            return fail(KVTC_E_CAPACITY, "job: paged dst smaller than n_blocks * block_size rows");
+          d.block_table = j.block_table;
+          d.block_size = j.block_size;
+          d.n_blocks = j.n_blocks;
+        } else if ((size_t)j.n_tokens * F * out_esz > j.dst_capacity) {
+          return fail(KVTC_E_CAPACITY, "job: dst smaller than n_tokens rows");
+        }
+        if (mode == Mode::Unpack || mode == Mode::Restore) {
+          d.staging = d_staging + st_off;
+          st_off += job_staging_bytes(s, d.tc);
+          if (!d_staging || st_off > staging_bytes) return fail(KVTC_E_CAPACITY, "staging buffer too small");
+        }
+        const int tile = mode == Mode::Unpack ? kUnpackTile : kDecTile;
+        d.n_ctiles = (d.tc + tile - 1) / tile;
+        d.tile_begin = tiles;
+        if (mode == Mode::Restore)
+          tiles += d.n_ctiles;
+        else
+          tiles += std::max<uint32_t>(1, d.n_ctiles + ptiles);
+      }
+      rb_max = std::max(rb_max, (size_t)s.record_bytes);
+      r_enc_max = std::max(r_enc_max, align_up((size_t)s.r_eff, 32));
+      km = std::max(km, (int)(align_up((size_t)s.r_eff, 16) / 16));
+    }
+    (void)in_esz;
+    a.total_tiles = tiles;
+    size_t l = 16;
+    if (mode == Mode::Encode)
+      l = std::max({l, r_enc_max * kEncRowPad * 2, (size_t)kEncTile * rb_max});
+    else if (mode == Mode::Pack)
+      l = std::max(l, (size_t)kEncTile * rb_max);
+    else if (mode == Mode::Decode)
+      l = std::max(l, (size_t)kDecTile * rb_max);
+    else if (mode == Mode::Unpack)
+      l = std::max(l, (size_t)kUnpackTile * rb_max);
+    if (l > 65536) return fail(KVTC_E_UNSUPPORTED, "records too large for one tile's LDS");
+    batches.push_back(a);
+    kmax.push_back(mode == Mode::Encode ? (int)(r_enc_max / 32) : km);
+    lds.push_back(l);
+  }
+  return KVTC_OK;
+}
+
+kvtc_status hip_status(int e, const char* what) {
+  if (e == 0) return KVTC_OK;
+  return fail(KVTC_E_HIP, std::string(what) + ": " + hipGetErrorString((hipError_t)e));
+}
+
+}  // namespace
+
+extern "C" {
+
+kvtc_status kvtc_encode(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, void* d_ws,
+                        hipStream_t stream) {
+  std::vector<LaunchArgs> b;
+  std::vector<int> k;
+  std::vector<size_t> l;
+  kvtc_status st = plan(c, Mode::Encode, jobs, n_jobs, c ? c->p.dtype : 0, d_ws, nullptr, 0, b, k, l);
+  if (st != KVTC_OK) return st;
+  for (size_t i = 0; i < b.size(); ++i) {
+    if (b[i].total_tiles == 0) continue;
+    st = hip_status(launch_encode(b[i], std::max(k[i], 1), c->p.group, l[i], stream), "encode launch");
+    if (st != KVTC_OK) return st;
+  }
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_decode(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, int32_t out_dtype,
+                        void* d_ws, hipStream_t stream) {
+  std::vector<LaunchArgs> b;
+  std::vector<int> k;
+  std::vector<size_t> l;
+  kvtc_status st = plan(c, Mode::Decode, jobs, n_jobs, out_dtype, d_ws, nullptr, 0, b, k, l);
+  if (st != KVTC_OK) return st;
+  for (size_t i = 0; i < b.size(); ++i) {
+    if (b[i].total_tiles == 0) continue;
+    st = hip_status(launch_decode(b[i], std::max(k[i], 1), c->p.group, l[i], stream), "decode launch");
+    if (st != KVTC_OK) return st;
+  }
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_decode_unpack(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, int32_t out_dtype,
+                               void* d_staging, size_t staging_bytes, void* d_ws, hipStream_t stream) {
+  std::vector<LaunchArgs> b;
+  std::vector<int> k;
+  std::vector<size_t> l;
+  kvtc_status st = plan(c, Mode::Unpack, jobs, n_jobs, out_dtype, d_ws, (uint8_t*)d_staging,
+                        staging_bytes, b, k, l);
+  if (st != KVTC_OK) return st;
+  for (size_t i = 0; i < b.size(); ++i) {
+    if (b[i].total_tiles == 0) continue;
+    st = hip_status(launch_unpack(b[i], c->p.group, l[i], stream), "unpack launch");
+    if (st != KVTC_OK) return st;
+  }
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_decode_restore(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, int32_t out_dtype,
+                                const void* d_staging, size_t staging_bytes, void* d_ws,
+                                hipStream_t stream) {
+  std::vector<LaunchArgs> b;
+  std::vector<int> k;
+  std::vector<size_t> l;
+  kvtc_status st = plan(c, Mode::Restore, jobs, n_jobs, out_dtype, d_ws, (uint8_t*)d_staging,
+                        staging_bytes, b, k, l);
+  if (st != KVTC_OK) return st;
+  for (size_t i = 0; i < b.size(); ++i) {
+    if (b[i].total_tiles == 0) continue;
+    st = hip_status(launch_restore(b[i], std::max(k[i], 1), c->p.group, stream), "restore launch");
+    if (st != KVTC_OK) return st;
+  }
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_pack(kvtc_codec* c, const kvtc_job* job, const void* d_codes, const void* d_shift_scale,
+                      void* d_ws, hipStream_t stream) {
+  std::vector<LaunchArgs> b;
+  std::vector<int> k;
+  std::vector<size_t> l;
+  kvtc_status st = plan(c, Mode::Pack, job, 1, c ? c->p.dtype : 0, d_ws, nullptr, 0, b, k, l);
+  if (st != KVTC_OK) return st;
+  int idx = job->layer * 2 + job->kind;
+  if (c->slots[idx].r_eff > 0 && (!d_codes || !d_shift_scale))
+    return fail(KVTC_E_INVALID, "null codes or shift/scale");
+  return hip_status(launch_pack(b[0], c->p.group, l[0], d_codes, d_shift_scale, stream), "pack launch");
+}
+
+kvtc_status kvtc_read_device_status(const void* d_ws, int32_t n_jobs, int32_t* status, hipStream_t stream) {
+  if (!d_ws || !status || n_jobs <= 0) return fail(KVTC_E_INVALID, "bad arguments");
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e == hipSuccess) e = hipMemcpy(status, d_ws, sizeof(int32_t) * n_jobs, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(KVTC_E_HIP, std::string("status read: ") + hipGetErrorString(e));
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_deflate(const void* in, size_t n, void* out, size_t cap, size_t* out_len, int32_t level) {
+  if ((!in && n) || !out_len) return fail(KVTC_E_INVALID, "bad arguments");
+  const uLong bound = compressBound((uLong)n);
+  if (!out) {
+    *out_len = bound;
+    return KVTC_OK;
+  }
+  uLongf len = (uLongf)cap;
+  const int z = compress2((Bytef*)out, &len, (const Bytef*)in, (uLong)n, level);
+  if (z == Z_BUF_ERROR) return fail(KVTC_E_CAPACITY, "deflate output buffer too small");
+  if (z != Z_OK) return fail(KVTC_E_INVALID, "zlib error");
+  *out_len = len;
+  return KVTC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Internal declarations shared by the host core (kvtc_host.cpp) and the HIP
+// kernels and launchers (kvtc_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "kvtc.h"
+
+namespace kvtc {
+
+constexpr int kHeaderBytes = 64;
+constexpr uint16_t kFormatVersion = 1;
+constexpr int kScaleBits = 64;         // fp32 shift + fp32 scale per active group
+constexpr int kMaxActGroups = 32;      // KVTC_MAX_REFF / smallest supported G (8)
+constexpr int kMaxLaunchJobs = 32;     // jobs passed by value in one launch
+constexpr size_t kAlign = 256;
+
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Descriptor of one calibrated (layer, kind) inside the device state buffer.
+// Offsets are bytes from the start of the device state.
+struct alignas(16) DevSlot {
+  uint64_t mu_off;        // f32 mu32[F]
+  uint64_t venc_off;      // bf16 V'^T [r_enc][F]   (rows >= r_eff are zero)
+  uint64_t vdec_off;      // f16  V'   [F][r_dec]   (cols >= r_eff are zero)
+  uint64_t slot_id;
+  int32_t calibrated;
+  int32_t n_act;
+  int32_t r_eff;
+  int32_t record_bytes;
+  int32_t r_enc;          // r_eff rounded up to 32 (encode MFMA blocks)
+  int32_t r_dec;          // r_eff rounded up to 16 (decode MFMA K steps)
+  int32_t G;
+  int32_t F;
+  uint8_t width[kMaxActGroups];        // width of active group a
+  uint16_t chunk_off[kMaxActGroups];   // byte offset of its chunk in a record
+};
+
+// Per-job launch descriptor, passed by value in the kernel arguments.
+struct JobDesc {
+  const void* src;
+  void* dst;
+  const int32_t* block_table;
+  const void* staging;     // decode stage 2 / stage-1 output
+  uint32_t T;
+  uint32_t s1;             // effective sink rows
+  uint32_t w1;             // effective window rows
+  uint32_t tc;             // compressed rows
+  uint32_t tile_begin;     // first logical tile of this job
+  uint32_t n_ctiles;       // compressed-row tiles
+  int32_t slot;            // layer * 2 + kind
+  int32_t layer;
+  int32_t kind;
+  int32_t block_size;      // paged output when block_table != nullptr
+  int32_t n_blocks;
+  int32_t pad;
+};
+
+struct LaunchArgs {
+  JobDesc jobs[kMaxLaunchJobs];
+  int32_t n_jobs;
+  uint32_t total_tiles;
+  int32_t dtype;           // stream / input element type
+  int32_t out_dtype;       // decode output element type
+  int32_t F;
+  int32_t pad;
+  const uint8_t* state;    // device state base
+  int32_t* status;         // per-launch slice of the workspace status words
+};
+
+// Tile sizes (tokens per workgroup tile).
+constexpr int kEncTile = 128;
+constexpr int kDecTile = 128;
+constexpr int kUnpackTile = 256;
+constexpr int kPassRows = 16;
+constexpr int kEncKS = 64;                 // features per LDS basis slice (encode)
+constexpr int kEncRowPad = kEncKS + 8;     // bf16 elements per LDS basis row
+
+// Host-side launchers implemented in kvtc_kernels.hip (G = group size, lds =
+// dynamic LDS bytes). They return a hipError_t value cast to int.
+int launch_encode(const LaunchArgs& a, int nb_max, int G, size_t lds, hipStream_t s);
+int launch_decode(const LaunchArgs& a, int kmax, int G, size_t lds, hipStream_t s);
+int launch_unpack(const LaunchArgs& a, int G, size_t lds, hipStream_t s);
+int launch_restore(const LaunchArgs& a, int kmax, int G, hipStream_t s);
+int launch_pack(const LaunchArgs& a, int G, size_t lds, const void* codes, const void* ss,
+                hipStream_t s);
+
+}  // namespace kvtc

@@ -1,0 +1,753 @@
+// HIP kernels of KV-cache transform coding for gfx950 (MI355X).
+//
+// Method: "KV Cache Transform Coding for Compact Storage in LLM Inference"
+// (gist.science, 2511.01815), section 2B (compression: subtract the mean,
+// multiply by V, quantize with the DP widths, pack) and section 2C
+// (decompression: dequantize, multiply by V^T, add the mean, layer by layer).
+//
+// Every launch covers a batch of jobs (tensors). The grid is a flat list of
+// logical tiles; tiles of one job are consecutive and the blockIdx -> tile map
+// sends consecutive tiles to the same XCD, so one tensor's basis stays in one
+// XCD's L2.
+//
+// Encode tile (256 threads, 128 tokens): the four waves each own 32 tokens.
+// The projection runs on v_mfma_f32_32x32x16_bf16 in transposed form,
+// D[component][token] = sum_f V'^T[component][f] * x'[token][f]: the basis
+// K-slice is staged in LDS and shared by the waves, the centred tokens
+// x' = bf16_rne(fp32(x) - mu) are formed in registers straight from global
+// memory. In the accumulator layout a lane owns one token and half of every
+// group's components, so the per-(token, group) min/max needs one cross-lane
+// exchange (lane ^ 32), quantization is lane-local, and a second exchange
+// gives each lane G/2 consecutive codes that it packs into one or two 64-bit
+// words. Records are assembled in LDS and leave in 16-byte stores.
+//
+// Decode tile (256 threads, 128 tokens): records are staged into LDS with
+// 16-byte loads; each lane rebuilds its token's dequantized coefficients
+// c_hat = shift + q * fp32(scale / k) for the 8 components it feeds to the
+// MFMA, scaled by a per-token power of two into fp16 (the fp16 operand keeps
+// 11 significant bits; the scale makes the range irrelevant), then runs
+// D[feature][token] = sum_j V'[feature][j] * c_hat[token][j] on
+// v_mfma_f32_32x32x16_f16 per 32-feature block and writes S_t * D + mu.
+#include <hip/hip_runtime.h>
+
+#include "kvtc_internal.h"
+
+namespace kvtc {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+
+// ------------------------------------------------------------- helpers ---
+
+__device__ __forceinline__ uint32_t logical_tile() {
+  const uint32_t n8 = gridDim.x >> 3;      // grid is a multiple of 8
+  return (blockIdx.x & 7u) * n8 + (blockIdx.x >> 3);
+}
+
+__device__ __forceinline__ int find_job(const LaunchArgs& a, uint32_t tile) {
+  int j = 0;
+  for (int i = 1; i < a.n_jobs; ++i)
+    if (a.jobs[i].tile_begin <= tile) j = i;
+  return j;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ size_t record_base(const JobDesc& jd, int F, int esz) {
+  return (size_t)kHeaderBytes + (size_t)(jd.s1 + jd.w1) * F * esz;
+}
+
+__device__ void write_header(const LaunchArgs& a, const JobDesc& jd, const DevSlot& sl) {
+  uint32_t h[16];
+  h[0] = 0x4354564Bu;  // "KVTC"
+  h[1] = (uint32_t)kFormatVersion | ((uint32_t)a.dtype << 16) | ((uint32_t)jd.kind << 24);
+  h[2] = (uint32_t)jd.layer;
+  h[3] = jd.T;
+  h[4] = (uint32_t)a.F;
+  h[5] = jd.s1;
+  h[6] = jd.w1;
+  h[7] = jd.tc;
+  h[8] = (uint32_t)sl.G | ((uint32_t)sl.n_act << 16);
+  h[9] = (uint32_t)sl.record_bytes;
+  h[10] = (uint32_t)sl.slot_id;
+  h[11] = (uint32_t)(sl.slot_id >> 32);
+  h[12] = h[13] = h[14] = h[15] = 0;
+  uint4* d = (uint4*)jd.dst;
+  for (int i = 0; i < 4; ++i) d[i] = make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
+}
+
+// Returns KVTC_OK or the status a stream with this header earns.
+__device__ int check_header(const LaunchArgs& a, const JobDesc& jd, const DevSlot& sl) {
+  const uint32_t* h = (const uint32_t*)jd.src;
+  if (h[0] != 0x4354564Bu || (h[1] & 0xFFFFu) != kFormatVersion) return KVTC_E_CORRUPT;
+  const uint32_t want1 = (uint32_t)kFormatVersion | ((uint32_t)a.dtype << 16) | ((uint32_t)jd.kind << 24);
+  if (h[1] != want1 || h[2] != (uint32_t)jd.layer || h[3] != jd.T || h[4] != (uint32_t)a.F ||
+      h[5] != jd.s1 || h[6] != jd.w1 || h[7] != jd.tc ||
+      h[8] != ((uint32_t)sl.G | ((uint32_t)sl.n_act << 16)) || h[9] != (uint32_t)sl.record_bytes ||
+      h[10] != (uint32_t)sl.slot_id || h[11] != (uint32_t)(sl.slot_id >> 32))
+    return KVTC_E_MISMATCH;
+  return KVTC_OK;
+}
+
+// Physical output row of token t (contiguous or through the block table);
+// -1 if the block table entry is out of range.
+__device__ __forceinline__ long out_row(const JobDesc& jd, uint32_t t) {
+  if (!jd.block_table) return (long)t;
+  const int blk = jd.block_table[t / (uint32_t)jd.block_size];
+  if (blk < 0 || blk >= jd.n_blocks) return -1;
+  return (long)blk * jd.block_size + (long)(t % (uint32_t)jd.block_size);
+}
+
+// Encode: copy passthrough rows [p*kPassRows, ...) of the stream's row list
+// (rows [0, s') then [T - w', T)) from the KV tensor into the stream.
+__device__ void encode_passthrough(const JobDesc& jd, uint32_t p, size_t row_bytes) {
+  const uint32_t n_rows = jd.s1 + jd.w1;
+  const uint32_t r0 = p * kPassRows;
+  const uint32_t r1 = min(n_rows, r0 + kPassRows);
+  const size_t vec_per_row = row_bytes / 16;
+  const size_t total = (size_t)(r1 - r0) * vec_per_row;
+  for (size_t i = threadIdx.x; i < total; i += kThreads) {
+    const uint32_t r = r0 + (uint32_t)(i / vec_per_row);
+    const size_t c = i % vec_per_row;
+    const uint32_t src_row = r < jd.s1 ? r : jd.T - jd.w1 + (r - jd.s1);
+    const uint4 v = ((const uint4*)((const uint8_t*)jd.src + (size_t)src_row * row_bytes))[c];
+    ((uint4*)((uint8_t*)jd.dst + kHeaderBytes + (size_t)r * row_bytes))[c] = v;
+  }
+}
+
+// Decode: copy passthrough rows from the stream to the output, converting
+// the element type if needed. Returns false if a block table entry was bad.
+__device__ bool decode_passthrough(const LaunchArgs& a, const JobDesc& jd, uint32_t p) {
+  const int F = a.F;
+  const uint32_t n_rows = jd.s1 + jd.w1;
+  const uint32_t r0 = p * kPassRows;
+  const uint32_t r1 = min(n_rows, r0 + kPassRows);
+  const int in_esz = a.dtype == KVTC_F32 ? 4 : 2;
+  const int out_esz = a.out_dtype == KVTC_F32 ? 4 : 2;
+  const uint8_t* src = (const uint8_t*)jd.src + kHeaderBytes;
+  bool ok = true;
+  if (a.dtype == a.out_dtype) {
+    const size_t vec_per_row = (size_t)F * in_esz / 16;
+    const size_t total = (size_t)(r1 - r0) * vec_per_row;
+    for (size_t i = threadIdx.x; i < total; i += kThreads) {
+      const uint32_t r = r0 + (uint32_t)(i / vec_per_row);
+      const size_t c = i % vec_per_row;
+      const uint32_t t = r < jd.s1 ? r : jd.T - jd.w1 + (r - jd.s1);
+      const long orow = out_row(jd, t);
+      if (orow < 0) { ok = false; continue; }
+      const uint4 v = ((const uint4*)(src + (size_t)r * F * in_esz))[c];
+      ((uint4*)((uint8_t*)jd.dst + (size_t)orow * F * out_esz))[c] = v;
+    }
+  } else {
+    const size_t total = (size_t)(r1 - r0) * F;
+    for (size_t i = threadIdx.x; i < total; i += kThreads) {
+      const uint32_t r = r0 + (uint32_t)(i / F);
+      const int c = (int)(i % F);
+      const uint32_t t = r < jd.s1 ? r : jd.T - jd.w1 + (r - jd.s1);
+      const long orow = out_row(jd, t);
+      if (orow < 0) { ok = false; continue; }
+      if (a.dtype == KVTC_BF16) {  // bf16 -> f32, exact
+        const uint16_t b = ((const uint16_t*)(src + (size_t)r * F * 2))[c];
+        ((float*)jd.dst)[(size_t)orow * F + c] = bf16_to_f32(b);
+      } else {                     // f32 -> bf16, nearest even
+        const float f = ((const float*)(src + (size_t)r * F * 4))[c];
+        ((uint16_t*)jd.dst)[(size_t)orow * F + c] = (uint16_t)bf16_bits_rne(f);
+      }
+    }
+  }
+  return ok;
+}
+
+// Copy n bytes from 16-byte aligned global memory into LDS (cooperative).
+__device__ void stage_to_lds(uint8_t* lds, const uint8_t* g, size_t n) {
+  const size_t nv = n / 16;
+  for (size_t i = threadIdx.x; i < nv; i += kThreads) ((uint4*)lds)[i] = ((const uint4*)g)[i];
+  for (size_t i = nv * 16 + threadIdx.x; i < n; i += kThreads) lds[i] = g[i];
+}
+
+// Copy n bytes from LDS to 16-byte aligned global memory (cooperative).
+__device__ void lds_to_global(uint8_t* g, const uint8_t* lds, size_t n) {
+  const size_t nv = n / 16;
+  for (size_t i = threadIdx.x; i < nv; i += kThreads) ((uint4*)g)[i] = ((const uint4*)lds)[i];
+  for (size_t i = nv * 16 + threadIdx.x; i < n; i += kThreads) g[i] = lds[i];
+}
+
+// Pack n codes of width w (LSB first) into a 64-bit word (n * w <= 64).
+__device__ __forceinline__ uint64_t pack_codes(const uint32_t* q, int n, int w) {
+  uint64_t bits = 0;
+  for (int j = 0; j < n; ++j) bits |= (uint64_t)q[j] << (j * w);
+  return bits;
+}
+
+// Store the low n bytes of v at an arbitrary LDS byte address.
+__device__ __forceinline__ void lds_store_bytes(uint8_t* p, uint64_t v, int n) {
+  for (int i = 0; i < n; ++i) p[i] = (uint8_t)(v >> (8 * i));
+}
+
+// Load n (<= 8) bytes from an arbitrary LDS/global byte address.
+__device__ __forceinline__ uint64_t load_bytes(const uint8_t* p, int n) {
+  uint64_t v = 0;
+  for (int i = 0; i < n; ++i) v |= (uint64_t)p[i] << (8 * i);
+  return v;
+}
+
+// Write the G/2 codes a lane holds for active group `a` (half h) and, for
+// h == 0, the group's (shift, scale), into the token's record.
+template <int G>
+__device__ __forceinline__ void put_group(uint8_t* rec, const DevSlot& sl, int a, int h,
+                                          const uint32_t* codes, float shift, float scale) {
+  const int w = sl.width[a];
+  const int half_bytes = (G / 2) * w / 8;
+  uint8_t* p = rec + sl.chunk_off[a] + h * half_bytes;
+  if (G == 16) {
+    lds_store_bytes(p, pack_codes(codes, 8, w), w);
+  } else {
+    lds_store_bytes(p, pack_codes(codes, 8, w), w);
+    lds_store_bytes(p + w, pack_codes(codes + 8, 8, w), w);
+  }
+  if (h == 0) {
+    const uint32_t s = __float_as_uint(shift), c = __float_as_uint(scale);
+    lds_store_bytes(rec + 8 * a, (uint64_t)s | ((uint64_t)c << 32), 8);
+  }
+}
+
+// The 8 codes of components [o, o + 8) of active group a from a record:
+// one byte per code in a 64-bit word.
+__device__ __forceinline__ uint64_t get_codes8(const uint8_t* rec, const DevSlot& sl, int a, int o) {
+  const int w = sl.width[a];
+  const uint64_t bits = load_bytes(rec + sl.chunk_off[a] + (o * w) / 8, w);
+  const uint64_t mask = (1ull << w) - 1ull;
+  uint64_t out = 0;
+  for (int j = 0; j < 8; ++j) out |= ((bits >> (j * w)) & mask) << (8 * j);
+  return out;
+}
+
+// --------------------------------------------------------------- encode ---
+
+template <int NB, int G>
+__global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t tile = logical_tile();
+  if (tile >= a.total_tiles) return;
+  const int j = find_job(a, tile);
+  const JobDesc& jd = a.jobs[j];
+  const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
+  const uint32_t lt = tile - jd.tile_begin;
+  const int F = a.F;
+  const int esz = a.dtype == KVTC_F32 ? 4 : 2;
+  const size_t row_bytes = (size_t)F * esz;
+  if (lt == 0 && threadIdx.x == 0) {
+    write_header(a, jd, sl);
+    a.status[j] = KVTC_OK;
+  }
+  if (lt >= jd.n_ctiles) {
+    encode_passthrough(jd, lt - jd.n_ctiles, row_bytes);
+    return;
+  }
+  const uint32_t t0 = lt * kEncTile;
+  const uint32_t n = min((uint32_t)kEncTile, jd.tc - t0);
+  const int rb = sl.record_bytes;
+  if (sl.r_eff == 0) return;  // zero-width records: nothing to write
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5;
+  const int tl = wave * 32 + (lane & 31);            // token within the tile
+  const bool tok_ok = (uint32_t)tl < n;
+  const uint8_t* xrow = (const uint8_t*)jd.src + (size_t)(jd.s1 + t0 + (tok_ok ? tl : 0)) * row_bytes;
+  const float* mu = (const float*)(a.state + sl.mu_off);
+  const uint16_t* venc = (const uint16_t*)(a.state + sl.venc_off);
+  const int nb = sl.r_enc / 32;
+  uint16_t* vs = (uint16_t*)smem;
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
+
+  for (int k0 = 0; k0 < F; k0 += kEncKS) {
+    __syncthreads();
+    const int nvec = sl.r_enc * (kEncKS / 8);
+    for (int idx = threadIdx.x; idx < nvec; idx += kThreads) {
+      const int r = idx / (kEncKS / 8), c8 = idx % (kEncKS / 8);
+      const uint4 v = *(const uint4*)(venc + (size_t)r * F + k0 + c8 * 8);
+      *(uint4*)(vs + r * kEncRowPad + c8 * 8) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kEncKS / 16; ++s) {
+      const int f = k0 + 16 * s + 8 * h;
+      // Centred token operand: x' = bf16_rne(fp32(x) - mu).
+      float xv[8];
+      if (a.dtype == KVTC_BF16) {
+        const uint4 raw = *(const uint4*)(xrow + (size_t)f * 2);
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[2 * e] = bf16_to_f32(w4[e] & 0xFFFFu);
+          xv[2 * e + 1] = bf16_to_f32(w4[e] >> 16);
+        }
+      } else {
+        const float4 lo = *(const float4*)(xrow + (size_t)f * 4);
+        const float4 hi = *(const float4*)(xrow + (size_t)f * 4 + 16);
+        xv[0] = lo.x; xv[1] = lo.y; xv[2] = lo.z; xv[3] = lo.w;
+        xv[4] = hi.x; xv[5] = hi.y; xv[6] = hi.z; xv[7] = hi.w;
+      }
+      const float4 m0 = *(const float4*)(mu + f);
+      const float4 m1 = *(const float4*)(mu + f + 4);
+      const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pk[e] = bf16_bits_rne(xv[2 * e] - mv[2 * e]) | (bf16_bits_rne(xv[2 * e + 1] - mv[2 * e + 1]) << 16);
+      const bf16x8 bx = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (b < nb) {
+          const uint4 av = *(const uint4*)(vs + (b * 32 + (lane & 31)) * kEncRowPad + 16 * s + 8 * h);
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bx,
+                                                           acc[b], 0, 0, 0);
+        }
+      }
+    }
+  }
+  __syncthreads();  // the basis slice region becomes the record staging area
+
+  // Quantize and pack. acc[b][i] holds component 32b + 8(i/4) + 4h + i%4 of
+  // token tl; a group of G components is the item range
+  // [(G/2) * sg, (G/2) * (sg + 1)) of block b with sg = a % (32/G).
+  uint8_t* rec = smem + (size_t)tl * rb;
+  constexpr int SUB = 32 / G;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int sg = 0; sg < SUB; ++sg) {
+      const int ag = b * SUB + sg;
+      if (b < nb && ag < sl.n_act) {
+        float v[G / 2];
+#pragma unroll
+        for (int i = 0; i < G / 2; ++i) v[i] = acc[b][(G / 2) * sg + i];
+        float mn = v[0], mx = v[0];
+#pragma unroll
+        for (int i = 1; i < G / 2; ++i) {
+          mn = fminf(mn, v[i]);
+          mx = fmaxf(mx, v[i]);
+        }
+        mn = fminf(mn, __shfl_xor(mn, 32));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const int w = sl.width[ag];
+        const float k = (float)((1 << w) - 1);
+        const float scale = mx - mn;
+        const float inv = scale > 0.f ? k / scale : 0.f;
+        uint32_t quad[G / 8];
+#pragma unroll
+        for (int m = 0; m < G / 8; ++m) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float d = v[4 * m + e] - mn;
+            const float u = d * inv;
+            const float r = fminf(fmaxf(__builtin_rintf(u), 0.f), k);
+            word |= (uint32_t)r << (8 * e);
+          }
+          quad[m] = word;
+        }
+        // Lane h holds the group's component quads 2m + h; gather quads
+        // [h * G/8, (h + 1) * G/8) so each lane packs G/2 consecutive codes.
+        uint32_t recv[G / 8];
+#pragma unroll
+        for (int m = 0; m < G / 8; ++m) recv[m] = __shfl_xor(quad[m], 32);
+        uint32_t codes[G / 2];
+#pragma unroll
+        for (int m = 0; m < G / 8; ++m) {
+          const int q0 = m, q1 = G / 8 + m;  // target quad for h = 0 / h = 1
+          const uint32_t c0 = (q0 % 2 == 0) ? quad[q0 / 2] : recv[q0 / 2];
+          const uint32_t c1 = (q1 % 2 == 1) ? quad[q1 / 2] : recv[q1 / 2];
+          const uint32_t word = h ? c1 : c0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) codes[4 * m + e] = (word >> (8 * e)) & 0xFFu;
+        }
+        if (tok_ok) put_group<G>(rec, sl, ag, h, codes, mn, scale);
+      }
+    }
+  }
+  __syncthreads();
+  uint8_t* dst = (uint8_t*)jd.dst + record_base(jd, F, esz) + (size_t)t0 * rb;
+  lds_to_global(dst, smem, (size_t)n * rb);
+}
+
+// --------------------------------------------------------------- decode ---
+
+// Per-token power-of-two scale: S = 2^(e - 14) where 2^e <= max |c_hat| over
+// the token's groups < 2^(e+1), so the fp16 operand peaks in [2^14, 2^15).
+__device__ __forceinline__ void token_scale(float m, float& S, float& Sinv) {
+  int e = (int)((__float_as_uint(m) >> 23) & 0xFF) - 127;
+  if (m == 0.f) e = 14;
+  e = max(min(e, 100), -100);
+  S = __uint_as_float((uint32_t)(127 + e - 14) << 23);
+  Sinv = __uint_as_float((uint32_t)(127 + 14 - e) << 23);
+}
+
+// Build the fp16 B fragment of K step s (components [16s + 8h, +8)).
+__device__ __forceinline__ f16x8 make_frag(uint64_t codes8, float shift, float scale, int w,
+                                           float Sinv) {
+  const float k = (float)((1 << w) - 1);
+  const float step = scale / k;
+  f16x8 f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float q = (float)((codes8 >> (8 * j)) & 0xFFu);
+    const float c = __builtin_fmaf(q, step, shift);
+    f[j] = (_Float16)(c * Sinv);
+  }
+  return f;
+}
+
+// Restore the compressed rows of one tile. FROM_STAGING selects the code
+// source: LDS-staged records (fused decode) or the stage-1 staging buffer.
+template <int KMAX, int G, bool FROM_STAGING>
+__device__ void restore_tile(const LaunchArgs& a, const JobDesc& jd, const DevSlot& sl,
+                             const uint8_t* lds_rec, uint32_t t0, uint32_t n, int* bad) {
+  const int F = a.F;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5;
+  const int tl = wave * 32 + (lane & 31);
+  const bool tok_ok = (uint32_t)tl < n;
+  const int tt = tok_ok ? tl : 0;
+  const float* mu = (const float*)(a.state + sl.mu_off);
+  const uint16_t* vdec = (const uint16_t*)(a.state + sl.vdec_off);
+  const int ks = sl.r_dec / 16;
+
+  // Code source for this token.
+  const uint8_t* rec = nullptr;
+  const uint8_t* scodes = nullptr;
+  const float2* ssp;
+  if (FROM_STAGING) {
+    const uint8_t* st = (const uint8_t*)jd.staging;
+    scodes = st + (size_t)(t0 + tt) * sl.r_eff;
+    const size_t ss_off = align_up((size_t)jd.tc * sl.r_eff, kAlign);
+    ssp = (const float2*)(st + ss_off) + (size_t)(t0 + tt) * sl.n_act;
+  } else {
+    rec = lds_rec + (size_t)tt * sl.record_bytes;
+    ssp = (const float2*)rec;  // 8-byte pairs at the record start (LDS)
+  }
+  auto ss_of = [&](int g) -> float2 {
+    if (FROM_STAGING) return ssp[g];
+    const uint64_t raw = load_bytes(rec + 8 * g, 8);
+    return make_float2(__uint_as_float((uint32_t)raw), __uint_as_float((uint32_t)(raw >> 32)));
+  };
+  float S, Sinv;
+  {
+    float m = 0.f;
+    for (int g = 0; g < sl.n_act; ++g) {
+      const float2 p = ss_of(g);
+      m = fmaxf(m, fmaxf(fabsf(p.x), fabsf(p.x + p.y)));
+    }
+    token_scale(m, S, Sinv);
+  }
+
+  f16x8 bfr[KMAX];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    f16x8 z;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = (_Float16)0.f;
+    bfr[s] = z;
+    const int c = 16 * s + 8 * h;
+    if (s < ks && c < sl.r_eff) {
+      const int ag = c / G, o = c % G;
+      uint64_t codes8;
+      if (FROM_STAGING)
+        codes8 = *(const uint64_t*)(scodes + c);
+      else
+        codes8 = get_codes8(rec, sl, ag, o);
+      const float2 p = ss_of(ag);
+      bfr[s] = make_frag(codes8, p.x, p.y, sl.width[ag], Sinv);
+    }
+  }
+
+  const uint32_t t = jd.s1 + t0 + tt;
+  const long orow = tok_ok ? out_row(jd, t) : -1;
+  if (tok_ok && orow < 0) *bad = 1;
+  const bool store = orow >= 0;
+  for (int fb = 0; fb < F / 32; ++fb) {
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    const uint16_t* vrow = vdec + (size_t)(fb * 32 + (lane & 31)) * sl.r_dec + 8 * h;
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+      if (s < ks) {
+        const uint4 av = *(const uint4*)(vrow + 16 * s);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av), bfr[s], acc,
+                                                     0, 0, 0);
+      }
+    }
+    if (store) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int f = fb * 32 + 8 * qd + 4 * h;
+        const float4 m4 = *(const float4*)(mu + f);
+        const float o0 = __builtin_fmaf(acc[4 * qd + 0], S, m4.x);
+        const float o1 = __builtin_fmaf(acc[4 * qd + 1], S, m4.y);
+        const float o2 = __builtin_fmaf(acc[4 * qd + 2], S, m4.z);
+        const float o3 = __builtin_fmaf(acc[4 * qd + 3], S, m4.w);
+        if (a.out_dtype == KVTC_F32) {
+          *(float4*)((float*)jd.dst + (size_t)orow * F + f) = make_float4(o0, o1, o2, o3);
+        } else {
+          const uint32_t p0 = bf16_bits_rne(o0) | (bf16_bits_rne(o1) << 16);
+          const uint32_t p1 = bf16_bits_rne(o2) | (bf16_bits_rne(o3) << 16);
+          *(uint2*)((uint16_t*)jd.dst + (size_t)orow * F + f) = make_uint2(p0, p1);
+        }
+      }
+    }
+  }
+}
+
+template <int KMAX, int G>
+__global__ __launch_bounds__(kThreads) void decode_kernel(const LaunchArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int flag;
+  const uint32_t tile = logical_tile();
+  if (tile >= a.total_tiles) return;
+  const int j = find_job(a, tile);
+  const JobDesc& jd = a.jobs[j];
+  const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
+  const uint32_t lt = tile - jd.tile_begin;
+  if (threadIdx.x == 0) flag = check_header(a, jd, sl);
+  __syncthreads();
+  const int st = flag;
+  if (lt == 0 && threadIdx.x == 0 && st != KVTC_OK) a.status[j] = st;
+  if (st != KVTC_OK) return;
+  __syncthreads();
+  if (threadIdx.x == 0) flag = 0;
+  __syncthreads();
+  int bad = 0;
+  if (lt >= jd.n_ctiles) {
+    bad = !decode_passthrough(a, jd, lt - jd.n_ctiles);
+  } else {
+    const uint32_t t0 = lt * kDecTile;
+    const uint32_t n = min((uint32_t)kDecTile, jd.tc - t0);
+    const int esz = a.dtype == KVTC_F32 ? 4 : 2;
+    const uint8_t* recs = (const uint8_t*)jd.src + record_base(jd, a.F, esz) +
+                          (size_t)t0 * sl.record_bytes;
+    stage_to_lds(smem, recs, (size_t)n * sl.record_bytes);
+    __syncthreads();
+    restore_tile<KMAX, G, false>(a, jd, sl, smem, t0, n, &bad);
+  }
+  if (bad) atomicExch(&flag, 1);
+  __syncthreads();
+  if (threadIdx.x == 0 && flag) atomicExch(&a.status[j], KVTC_E_INVALID);
+}
+
+// Stage 1: header check, passthrough rows, records -> staging codes/scales.
+template <int G>
+__global__ __launch_bounds__(kThreads) void unpack_kernel(const LaunchArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int flag;
+  const uint32_t tile = logical_tile();
+  if (tile >= a.total_tiles) return;
+  const int j = find_job(a, tile);
+  const JobDesc& jd = a.jobs[j];
+  const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
+  const uint32_t lt = tile - jd.tile_begin;
+  if (threadIdx.x == 0) flag = check_header(a, jd, sl);
+  __syncthreads();
+  const int st = flag;
+  if (lt == 0 && threadIdx.x == 0 && st != KVTC_OK) a.status[j] = st;
+  if (st != KVTC_OK) return;
+  __syncthreads();
+  if (threadIdx.x == 0) flag = 0;
+  __syncthreads();
+  int bad = 0;
+  if (lt >= jd.n_ctiles) {
+    bad = !decode_passthrough(a, jd, lt - jd.n_ctiles);
+  } else if (sl.r_eff > 0) {
+    const uint32_t t0 = lt * kUnpackTile;
+    const uint32_t n = min((uint32_t)kUnpackTile, jd.tc - t0);
+    const int esz = a.dtype == KVTC_F32 ? 4 : 2;
+    const int rb = sl.record_bytes;
+    const uint8_t* recs = (const uint8_t*)jd.src + record_base(jd, a.F, esz) + (size_t)t0 * rb;
+    stage_to_lds(smem, recs, (size_t)n * rb);
+    __syncthreads();
+    uint8_t* st8 = (uint8_t*)jd.staging;
+    float2* ssg = (float2*)(st8 + align_up((size_t)jd.tc * sl.r_eff, kAlign));
+    // One thread per (token, 8-component chunk).
+    const int chunks = sl.r_eff / 8;
+    for (int idx = threadIdx.x; idx < (int)n * chunks; idx += kThreads) {
+      const int tl = idx / chunks, c = (idx % chunks) * 8;
+      const uint8_t* rec = smem + (size_t)tl * rb;
+      const int ag = c / G, o = c % G;
+      *(uint64_t*)(st8 + (size_t)(t0 + tl) * sl.r_eff + c) = get_codes8(rec, sl, ag, o);
+      if (o == 0) {
+        const uint64_t raw = load_bytes(rec + 8 * ag, 8);
+        ssg[(size_t)(t0 + tl) * sl.n_act + ag] =
+            make_float2(__uint_as_float((uint32_t)raw), __uint_as_float((uint32_t)(raw >> 32)));
+      }
+    }
+  }
+  if (bad) atomicExch(&flag, 1);
+  __syncthreads();
+  if (threadIdx.x == 0 && flag) atomicExch(&a.status[j], KVTC_E_INVALID);
+}
+
+// Stage 2: staging -> compressed output rows.
+template <int KMAX, int G>
+__global__ __launch_bounds__(kThreads) void restore_kernel(const LaunchArgs a) {
+  __shared__ int flag;
+  const uint32_t tile = logical_tile();
+  if (tile >= a.total_tiles) return;
+  const int j = find_job(a, tile);
+  const JobDesc& jd = a.jobs[j];
+  const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
+  const uint32_t lt = tile - jd.tile_begin;
+  if (a.status[j] != KVTC_OK || lt >= jd.n_ctiles) return;
+  if (threadIdx.x == 0) flag = 0;
+  __syncthreads();
+  int bad = 0;
+  const uint32_t t0 = lt * kDecTile;
+  const uint32_t n = min((uint32_t)kDecTile, jd.tc - t0);
+  restore_tile<KMAX, G, true>(a, jd, sl, nullptr, t0, n, &bad);
+  if (bad) atomicExch(&flag, 1);
+  __syncthreads();
+  if (threadIdx.x == 0 && flag) atomicExch(&a.status[j], KVTC_E_INVALID);
+}
+
+// Test hook: stream from given codes and (shift, scale) pairs, through the
+// encoder's record packing (put_group) and header/passthrough writers.
+template <int G>
+__global__ __launch_bounds__(kThreads) void pack_kernel(const LaunchArgs a, const uint8_t* codes,
+                                                        const float2* ss) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t tile = logical_tile();
+  if (tile >= a.total_tiles) return;
+  const JobDesc& jd = a.jobs[0];
+  const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
+  const uint32_t lt = tile - jd.tile_begin;
+  const int esz = a.dtype == KVTC_F32 ? 4 : 2;
+  const size_t row_bytes = (size_t)a.F * esz;
+  if (lt == 0 && threadIdx.x == 0) {
+    write_header(a, jd, sl);
+    a.status[0] = KVTC_OK;
+  }
+  if (lt >= jd.n_ctiles) {
+    encode_passthrough(jd, lt - jd.n_ctiles, row_bytes);
+    return;
+  }
+  if (sl.r_eff == 0) return;
+  const uint32_t t0 = lt * kEncTile;
+  const uint32_t n = min((uint32_t)kEncTile, jd.tc - t0);
+  const int rb = sl.record_bytes;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5;
+  const int tl = wave * 32 + (lane & 31);
+  if ((uint32_t)tl < n) {
+    const uint32_t t = t0 + tl;
+    for (int ag = 0; ag < sl.n_act; ++ag) {
+      uint32_t cv[G / 2];
+      for (int i = 0; i < G / 2; ++i) cv[i] = codes[(size_t)t * sl.r_eff + ag * G + h * (G / 2) + i];
+      const float2 p = ss[(size_t)t * sl.n_act + ag];
+      put_group<G>(smem + (size_t)tl * rb, sl, ag, h, cv, p.x, p.y);
+    }
+  }
+  __syncthreads();
+  lds_to_global((uint8_t*)jd.dst + record_base(jd, a.F, esz) + (size_t)t0 * rb, smem, (size_t)n * rb);
+}
+
+// Status words start at KVTC_OK; tiles only ever write errors into them.
+__global__ void reset_status(int32_t* status, int n) {
+  if ((int)threadIdx.x < n) status[threadIdx.x] = KVTC_OK;
+}
+
+// ------------------------------------------------------------- launchers ---
+
+static dim3 grid_for(uint32_t tiles) { return dim3((tiles + 7u) / 8u * 8u); }
+
+template <int G>
+static int launch_encode_g(const LaunchArgs& a, int nb, size_t lds, hipStream_t s) {
+  const dim3 g = grid_for(a.total_tiles);
+#define KVTC_ENC(NBV)                                                                  \
+  case NBV:                                                                            \
+    hipLaunchKernelGGL((encode_kernel<NBV, G>), g, dim3(kThreads), lds, s, a); \
+    break;
+  switch (nb) {
+    KVTC_ENC(1) KVTC_ENC(2) KVTC_ENC(3) KVTC_ENC(4) KVTC_ENC(5) KVTC_ENC(6) KVTC_ENC(7) KVTC_ENC(8)
+    default:
+      return (int)hipErrorInvalidValue;
+  }
+#undef KVTC_ENC
+  return (int)hipGetLastError();
+}
+
+int launch_encode(const LaunchArgs& a, int nb_max, int G, size_t lds, hipStream_t s) {
+  if (G == 16) return launch_encode_g<16>(a, nb_max, lds, s);
+  if (G == 32) return launch_encode_g<32>(a, nb_max, lds, s);
+  return (int)hipErrorInvalidValue;
+}
+
+template <int G>
+static int launch_decode_g(const LaunchArgs& a, int kmax, size_t lds, bool staged, hipStream_t s) {
+  const dim3 g = grid_for(a.total_tiles);
+  if (!staged) hipLaunchKernelGGL(reset_status, dim3(1), dim3(kMaxLaunchJobs), 0, s, a.status, a.n_jobs);
+#define KVTC_DEC(KV)                                                                            \
+  if (kmax <= KV) {                                                                             \
+    if (staged)                                                                                 \
+      hipLaunchKernelGGL((restore_kernel<KV, G>), g, dim3(kThreads), 0, s, a);                 \
+    else                                                                                        \
+      hipLaunchKernelGGL((decode_kernel<KV, G>), g, dim3(kThreads), lds, s, a);                \
+    return (int)hipGetLastError();                                                             \
+  }
+  KVTC_DEC(2) KVTC_DEC(4) KVTC_DEC(6) KVTC_DEC(8) KVTC_DEC(12) KVTC_DEC(16)
+#undef KVTC_DEC
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_decode(const LaunchArgs& a, int kmax, int G, size_t lds, hipStream_t s) {
+  if (G == 16) return launch_decode_g<16>(a, kmax, lds, false, s);
+  if (G == 32) return launch_decode_g<32>(a, kmax, lds, false, s);
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_restore(const LaunchArgs& a, int kmax, int G, hipStream_t s) {
+  if (G == 16) return launch_decode_g<16>(a, kmax, 0, true, s);
+  if (G == 32) return launch_decode_g<32>(a, kmax, 0, true, s);
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_unpack(const LaunchArgs& a, int G, size_t lds, hipStream_t s) {
+  const dim3 g = grid_for(a.total_tiles);
+  hipLaunchKernelGGL(reset_status, dim3(1), dim3(kMaxLaunchJobs), 0, s, a.status, a.n_jobs);
+  if (G == 16)
+    hipLaunchKernelGGL((unpack_kernel<16>), g, dim3(kThreads), lds, s, a);
+  else if (G == 32)
+    hipLaunchKernelGGL((unpack_kernel<32>), g, dim3(kThreads), lds, s, a);
+  else
+    return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+int launch_pack(const LaunchArgs& a, int G, size_t lds, const void* codes, const void* ss,
+                hipStream_t s) {
+  const dim3 g = grid_for(a.total_tiles);
+  if (G == 16)
+    hipLaunchKernelGGL((pack_kernel<16>), g, dim3(kThreads), lds, s, a, (const uint8_t*)codes,
+                       (const float2*)ss);
+  else if (G == 32)
+    hipLaunchKernelGGL((pack_kernel<32>), g, dim3(kThreads), lds, s, a, (const uint8_t*)codes,
+                       (const float2*)ss);
+  else
+    return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+}  // namespace kvtc

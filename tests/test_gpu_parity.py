@@ -1,0 +1,352 @@
+"""GPU parity of libkvtc against the CPU oracle (cuda:0, through the C ABI).
+
+Contract (oracle = oracle/kvtc_oracle.py; every input is seeded and
+synthetic, every artifact is written by the oracle and loaded by the library):
+  T1  kvtc_pack of the oracle's codes and (shift, scale) reproduces the
+      oracle's stream byte for byte; kvtc_decode_unpack of the oracle's stream
+      returns its codes and fp32 bits exactly.
+  T2  GPU encode codes differ from the oracle's in at most 1e-4 of positions
+      (pooled per workload), each by at most one step.
+  T3  GPU decode of the oracle's stream: max |x_gpu - x_orc| / max |x_orc|
+      <= 1e-3 for fp32 output; bf16 output within 1e-3 * max|x| plus the bf16
+      rounding of the value (2^-8 relative).
+  T4  header and passthrough bytes are bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_transform_amd as K
+import oracle.kvtc_oracle as O
+import synth
+from gpu_util import (DEV, DevCodec, bf16_out_to_f64, code_stats, oracle_artifact,
+                      oracle_params, storage_to_dev, to_dev_bytes)
+
+pytestmark = pytest.mark.gpu
+
+CODE_RATE = 1e-4
+DEC_TOL = 1e-3
+
+# name: (workload, slots, T, requests, calibration tokens or None for the workload's)
+CASES = {
+    "tiny": ("tiny", [(0, 0)], 512, 1, None),
+    "llama31_8b": ("llama31_8b", [(0, 0), (0, 1), (1, 0), (1, 1)], 8192, 1, None),
+    "nemo12b": ("nemo12b", [(0, 0), (0, 1)], 32768, 1, 4096),
+    "llama33_70b_16x": ("llama33_70b_16x", [(0, 0), (0, 1)], 16384, 1, 4096),
+    "llama33_70b_64x": ("llama33_70b_64x", [(0, 0), (0, 1)], 16384, 1, 4096),
+    "qwen25_7b_paged": ("qwen25_7b_paged", [(0, 0), (0, 1)], 8192, 2, 4096),
+}
+
+
+def _setup(case):
+    wname, slots, T, reqs, calib = CASES[case]
+    w = synth.workload(wname)
+    art = oracle_artifact(wname, slots, calib)
+    op = art.params
+    items = []
+    for (l, k) in slots:
+        for r in range(reqs):
+            store = synth.storage(w, synth.gen_kv(w, l, k, synth.ROLE_EVAL, T, r))
+            items.append((l, k, store, O.encode(store, op, art.slots[(l, k)], l, k)))
+    return w, art, op, items
+
+
+def _decode_check(w, op, slot, ref_stream, T, out, out_dtype, layer, kind, rows=None):
+    full, ref_out = O.decode(ref_stream, op, slot, layer, kind, T, out_dtype)
+    got = out[:T] if rows is None else out[rows]
+    s1, w1, tc = O.split_rows(T, op.sink, op.window)
+    if out_dtype == K.KVTC_F32:
+        g = got.cpu().numpy().astype(np.float64)
+    else:
+        g = bf16_out_to_f64(got)
+    M = max(np.abs(full).max(initial=0.0), 1e-30)
+    err = np.abs(g - full)
+    if out_dtype == K.KVTC_F32:
+        rel = err.max(initial=0.0) / M
+        assert rel <= DEC_TOL, rel
+    else:
+        assert np.all(err <= DEC_TOL * M + 2.0 ** -8 * np.abs(full)), err.max()
+        rel = err.max(initial=0.0) / M
+    if out_dtype == op.dtype:  # passthrough rows come back bit for bit
+        raw = got.cpu().numpy()
+        ref = ref_out.view(np.int16) if ref_out.dtype == np.uint16 else ref_out
+        pt = np.r_[0:s1, T - w1:T]
+        assert np.array_equal(raw[pt].view(np.uint8), np.ascontiguousarray(ref[pt]).view(np.uint8))
+    return rel
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_encode_parity(case):
+    w, art, op, items = _setup(case)
+    dc = DevCodec(art.serialize())
+    devs = [storage_to_dev(store) for _, _, store, _ in items]
+    streams = dc.encode([(l, k, x) for (l, k, _, _), x in zip(items, devs)])
+    bad = total = worst = 0
+    for (l, k, store, ref), sb in zip(items, streams):
+        slot = art.slots[(l, k)]
+        T = store.shape[0]
+        assert len(sb) == len(ref.stream)
+        s1, w1, tc = O.split_rows(T, op.sink, op.window)
+        rec0 = O.HEADER_BYTES + (s1 + w1) * op.F * op.elem_bytes
+        assert sb[:rec0] == ref.stream[:rec0], "header or passthrough differs"
+        nb, nt, mx, shift, scale = code_stats(sb, ref, op, slot, T)
+        bad, total, worst = bad + nb, total + nt, max(worst, mx)
+        if slot.n_act:
+            assert np.allclose(shift, ref.shift, rtol=1e-5, atol=1e-6 * np.abs(ref.shift).max())
+            assert np.allclose(scale, ref.scale, rtol=1e-4, atol=1e-6 * np.abs(ref.scale).max())
+    rate = bad / max(total, 1)
+    print(f"{case}: code mismatches {bad}/{total} = {rate:.2e}, max step {worst}")
+    assert worst <= 1
+    assert rate <= CODE_RATE
+
+
+@pytest.mark.parametrize("out_dtype", [K.KVTC_F32, K.KVTC_BF16])
+@pytest.mark.parametrize("case", list(CASES))
+def test_decode_parity(case, out_dtype):
+    w, art, op, items = _setup(case)
+    dc = DevCodec(art.serialize())
+    T = items[0][2].shape[0]
+    paging = None
+    if synth.workload(CASES[case][0]).paged:
+        rng = np.random.default_rng(3)
+        bs = w.block_size
+        nblk = (T + bs - 1) // bs + 37
+        paging, tables = [], []
+        for _ in items:
+            table = rng.permutation(nblk)[: (T + bs - 1) // bs].astype(np.int32)
+            tables.append(table)
+            paging.append((torch.from_numpy(table).to(DEV), bs, nblk))
+    outs, st = dc.decode([(l, k, T, ref.stream) for l, k, _, ref in items], out_dtype, op.F, paging)
+    assert np.all(st == 0), st
+    worst = 0.0
+    for i, (l, k, store, ref) in enumerate(items):
+        rows = None
+        if paging is not None:
+            t = np.arange(T)
+            rows = torch.from_numpy(tables[i][t // w.block_size] * w.block_size + t % w.block_size).to(DEV)
+        worst = max(worst, _decode_check(w, op, art.slots[(l, k)], ref.stream, T, outs[i],
+                                         out_dtype, l, k, rows))
+    print(f"{case} out={out_dtype}: max rel err {worst:.3e}")
+    # the two-stage (unpack + restore) path computes exactly what the fused one does
+    outs2, st2 = dc.decode([(l, k, T, ref.stream) for l, k, _, ref in items], out_dtype, op.F,
+                           paging, two_stage=True)
+    assert np.all(st2 == 0), st2
+    for a, b in zip(outs, outs2):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("case", ["tiny", "llama31_8b", "nemo12b"])
+def test_pack_unpack_bit_exact(case):
+    w, art, op, items = _setup(case)
+    dc = DevCodec(art.serialize())
+    l, k, store, ref = items[0]
+    slot = art.slots[(l, k)]
+    T = store.shape[0]
+    x = storage_to_dev(store)
+    n = dc.codec.encoded_bytes(l, k, T)
+    buf = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    codes = torch.from_numpy(np.ascontiguousarray(ref.codes)).to(DEV)
+    ss = torch.from_numpy(np.ascontiguousarray(np.stack([ref.shift, ref.scale], axis=2))).to(DEV)
+    job = K.make_job(l, k, T, x, buf, n)
+    dc.codec.pack(job, codes, ss, dc.ws, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert bytes(buf.cpu().numpy().tobytes()) == ref.stream          # T1 pack
+    src = to_dev_bytes(ref.stream, 16)
+    out = torch.zeros((T, op.F), dtype=torch.int16 if op.dtype == O.DTYPE_BF16 else torch.float32,
+                      device=DEV)
+    djob = K.make_job(l, k, T, src, out, out.numel() * out.element_size())
+    nst = dc.codec.staging_bytes([djob])
+    stg = torch.zeros(nst, dtype=torch.uint8, device=DEV)
+    dc.codec.decode_unpack([djob], op.dtype, stg, nst, dc.ws, torch.cuda.current_stream())
+    assert np.all(dc.status(1) == 0)
+    h = stg.cpu().numpy()
+    tc = ref.codes.shape[0]
+    got_codes = h[: tc * slot.r_eff].reshape(tc, slot.r_eff)
+    off = (tc * slot.r_eff + 255) // 256 * 256
+    got_ss = h[off: off + tc * slot.n_act * 8].view(np.float32).reshape(tc, slot.n_act, 2)
+    assert np.array_equal(got_codes, ref.codes)                      # T1 unpack
+    assert np.array_equal(got_ss[:, :, 0].view(np.uint32), ref.shift.view(np.uint32))
+    assert np.array_equal(got_ss[:, :, 1].view(np.uint32), ref.scale.view(np.uint32))
+
+
+def test_edge_lengths_in_one_launch():
+    """Empty, all-passthrough, one-row and ragged tensors share one launch."""
+    wname, slots, _, _, calib = CASES["tiny"]
+    w = synth.workload(wname)
+    art = oracle_artifact(wname, slots, calib)
+    op = art.params
+    slot = art.slots[(0, 0)]
+    dc = DevCodec(art.serialize())
+    lens = [0, 1, 4, 60, 68, 69, 70, 131, 132, 133, 200, 1000]
+    stores = [synth.storage(w, synth.gen_kv(w, 0, 0, synth.ROLE_EVAL, T, 7 + i))
+              for i, T in enumerate(lens)]
+    refs = [O.encode(s, op, slot, 0, 0) for s in stores]
+    devs = [storage_to_dev(s) if s.shape[0] else torch.zeros((1, op.F), dtype=torch.float32, device=DEV)
+            for s in stores]
+    jobs, bufs = [], []
+    for x, T in zip(devs, lens):
+        n = dc.codec.encoded_bytes(0, 0, T)
+        b = torch.full((n,), 0xEE, dtype=torch.uint8, device=DEV)
+        bufs.append(b)
+        jobs.append(K.make_job(0, 0, T, x, b, n))
+    dc.codec.encode(jobs, dc.ws, torch.cuda.current_stream())
+    assert np.all(dc.status(len(jobs)) == 0)
+    for T, b, ref in zip(lens, bufs, refs):
+        sb = bytes(b.cpu().numpy().tobytes())
+        s1, w1, tc = O.split_rows(T, op.sink, op.window)
+        rec0 = 64 + (s1 + w1) * op.F * op.elem_bytes
+        assert sb[:rec0] == ref.stream[:rec0], T
+        nbad, ntot, mx, _, _ = code_stats(sb, ref, op, slot, T)
+        assert mx <= 1 and nbad <= max(1, ntot // 1000), (T, nbad)
+    for od in (K.KVTC_F32, K.KVTC_BF16):
+        outs, st = dc.decode([(0, 0, T, ref.stream) for T, ref in zip(lens, refs)], od, op.F)
+        assert np.all(st == 0), st
+        for T, out, ref in zip(lens, outs, refs):
+            _decode_check(w, op, slot, ref.stream, T, out, od, 0, 0)
+
+
+def _injected(F, G, widths, dtype, seed, s=4, w=16, mu_scale=1.0):
+    rng = np.random.default_rng(seed)
+    widths = np.asarray(widths, np.uint8)
+    r = int(np.count_nonzero(widths)) * G
+    V = np.linalg.qr(rng.standard_normal((F, F)))[0][:, :r] if r else np.zeros((F, 0))
+    p = O.Params(1, 1, F, s, w, G, 8, 16.0, dtype)
+    sl = O.Slot(0, 0, F, G, widths, (mu_scale * rng.standard_normal(F)).astype(np.float32),
+                np.zeros(F), V.astype(np.float32))
+    return p, sl
+
+
+@pytest.mark.parametrize("variant", ["zero_bits", "reff256_g16", "reff256_g32", "odd_groups"])
+def test_injected_artifacts(variant):
+    F = 1024
+    if variant == "zero_bits":
+        p, sl = _injected(F, 16, np.zeros(64), O.DTYPE_BF16, 1)
+    elif variant == "reff256_g16":
+        wd = np.zeros(64, np.uint8)
+        wd[:16] = [8, 1, 7, 2, 6, 3, 5, 4, 8, 8, 1, 1, 3, 3, 6, 2]
+        p, sl = _injected(F, 16, wd, O.DTYPE_BF16, 2)
+    elif variant == "reff256_g32":
+        wd = np.zeros(32, np.uint8)
+        wd[:8] = [8, 7, 6, 5, 4, 3, 2, 1]
+        p, sl = _injected(F, 32, wd, O.DTYPE_BF16, 3)
+    else:
+        wd = np.zeros(64, np.uint8)
+        wd[[0, 3, 9, 40, 63]] = [5, 8, 1, 2, 3]    # odd n_act, scattered groups
+        p, sl = _injected(F, 16, wd, O.DTYPE_BF16, 4)
+    art = O.Artifact(p, {(0, 0): sl})
+    dc = DevCodec(art.serialize())
+    rng = np.random.default_rng(9)
+    T = 777
+    x = (rng.standard_normal((T, F)) * 3).astype(np.float32)
+    store = O.f32_to_bf16_bits(x)
+    ref = O.encode(store, p, sl, 0, 0)
+    sb = dc.encode([(0, 0, storage_to_dev(store))])[0]
+    s1, w1, tc = O.split_rows(T, p.sink, p.window)
+    rec0 = 64 + (s1 + w1) * F * 2
+    assert sb[:rec0] == ref.stream[:rec0]
+    nbad, ntot, mx, _, _ = code_stats(sb, ref, p, sl, T)
+    assert mx <= 1 and nbad <= max(2, ntot * CODE_RATE), (nbad, ntot)
+    for od in (K.KVTC_F32, K.KVTC_BF16):
+        outs, st = dc.decode([(0, 0, T, ref.stream)], od, F)
+        assert np.all(st == 0)
+        _decode_check(None, p, sl, ref.stream, T, outs[0], od, 0, 0)
+
+
+def test_identity_basis_is_exact():
+    """mu = 0, V = I, 8-bit groups, inputs on each group's 8-bit grid: the GPU
+    stream equals the oracle's byte for byte and decode returns the input."""
+    F, G, T = 64, 16, 300
+    rng = np.random.default_rng(8)
+    p = O.Params(1, 1, F, 2, 3, G, 8, 12.0, O.DTYPE_BF16)
+    sl = O.Slot(0, 0, F, G, np.full(4, 8, np.uint8), np.zeros(F, np.float32), np.zeros(F),
+                np.eye(F, dtype=np.float32))
+    x = np.zeros((T, F), np.float32)
+    for g in range(4):
+        e = rng.integers(-6, 3, T).astype(np.float64)
+        m = rng.integers(-255, 1, T)
+        q = rng.integers(0, 256, (T, G))
+        q[:, 0], q[:, 1] = 0, 255
+        x[:, g * G:(g + 1) * G] = (m[:, None] + q) * 2.0 ** e[:, None]
+    store = O.f32_to_bf16_bits(x)
+    ref = O.encode(store, p, sl, 0, 0)
+    dc = DevCodec(O.Artifact(p, {(0, 0): sl}).serialize())
+    sb = dc.encode([(0, 0, storage_to_dev(store))])[0]
+    assert sb == ref.stream
+    for od in (K.KVTC_F32, K.KVTC_BF16):
+        outs, st = dc.decode([(0, 0, T, ref.stream)], od, F)
+        assert np.all(st == 0)
+        got = outs[0].cpu().numpy()
+        want = x if od == K.KVTC_F32 else store.view(np.int16)
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+
+
+def test_corrupt_stream_is_rejected_without_writes():
+    wname, slots, T, _, calib = CASES["tiny"]
+    w = synth.workload(wname)
+    art = oracle_artifact(wname, slots, calib)
+    op = art.params
+    slot = art.slots[(0, 0)]
+    dc = DevCodec(art.serialize())
+    store = synth.storage(w, synth.gen_kv(w, 0, 0, synth.ROLE_EVAL, T))
+    ref = O.encode(store, op, slot, 0, 0)
+    for off, want in ((0, K.KVTC_E_CORRUPT), (4, K.KVTC_E_CORRUPT), (12, K.KVTC_E_MISMATCH),
+                      (34, K.KVTC_E_MISMATCH), (41, K.KVTC_E_MISMATCH)):
+        bad = bytearray(ref.stream)
+        bad[off] ^= 0x21
+        for two in (False, True):
+            outs, st = dc.decode([(0, 0, T, bytes(bad))], K.KVTC_F32, op.F, two_stage=two)
+            assert st[0] == want, (off, st)
+            assert torch.all(outs[0] == -7.0), "a rejected stream wrote output rows"
+
+
+def test_bad_block_table_entry_is_reported():
+    wname, slots, T, _, calib = CASES["tiny"]
+    w = synth.workload(wname)
+    art = oracle_artifact(wname, slots, calib)
+    op = art.params
+    dc = DevCodec(art.serialize())
+    store = synth.storage(w, synth.gen_kv(w, 0, 0, synth.ROLE_EVAL, T))
+    ref = O.encode(store, op, art.slots[(0, 0)], 0, 0)
+    nblk = T // 16
+    table = np.arange(nblk, dtype=np.int32)
+    table[5] = nblk + 3                            # out of range
+    bt = torch.from_numpy(table).to(DEV)
+    outs, st = dc.decode([(0, 0, T, ref.stream)], K.KVTC_F32, op.F, [(bt, 16, nblk)])
+    assert st[0] == K.KVTC_E_INVALID
+    got = outs[0].cpu().numpy()
+    full, _ = O.decode(ref.stream, op, art.slots[(0, 0)], 0, 0, T)
+    ok_rows = np.r_[0:80, 96:T]                    # block 5 = tokens 80..95 is skipped
+    M = np.abs(full).max()
+    assert np.abs(got[ok_rows] - full[ok_rows]).max() / M <= DEC_TOL
+
+
+def test_full_size_launch_llama8b():
+    """The benchmark's launch shape: 64 tensors of 8192 tokens in one call
+    (jobs over 4 calibrated slots, 16 tensors each); every output compared."""
+    wname, slots, T, _, calib = CASES["llama31_8b"]
+    w = synth.workload(wname)
+    art = oracle_artifact(wname, slots, calib)
+    op = art.params
+    dc = DevCodec(art.serialize())
+    srcs = {}
+    for (l, k) in slots:
+        store = synth.storage(w, synth.gen_kv(w, l, k, synth.ROLE_EVAL, T, 5))
+        srcs[(l, k)] = (store, storage_to_dev(store), O.encode(store, op, art.slots[(l, k)], l, k))
+    order = [slots[i % 4] for i in range(64)]
+    streams = dc.encode([(l, k, srcs[(l, k)][1]) for l, k in order])
+    bad = total = worst = 0
+    for (l, k), sb in zip(order, streams):
+        ref = srcs[(l, k)][2]
+        nb, nt, mx, _, _ = code_stats(sb, ref, op, art.slots[(l, k)], T)
+        assert sb[:64] == ref.stream[:64]
+        bad, total, worst = bad + nb, total + nt, max(worst, mx)
+    assert worst <= 1 and bad / total <= CODE_RATE, (bad, total)
+    outs, st = dc.decode([(l, k, T, srcs[(l, k)][2].stream) for l, k in order], K.KVTC_BF16, op.F)
+    assert np.all(st == 0)
+    refs = {key: O.decode(v[2].stream, op, art.slots[key], key[0], key[1], T)[0]
+            for key, v in srcs.items()}
+    for (l, k), out in zip(order, outs):
+        full = refs[(l, k)]
+        g = bf16_out_to_f64(out[:T])
+        M = np.abs(full).max()
+        assert np.all(np.abs(g - full) <= DEC_TOL * M + 2.0 ** -8 * np.abs(full))

@@ -1,0 +1,175 @@
+"""Host-side checks of libkvtc that need no GPU: the C ABI loads and exports
+every declared symbol, artifacts interoperate byte for byte with the oracle's
+format, sizes match, errors are reported, and the library's calibration
+agrees with the oracle's (eigenvalues, group projectors, DP widths)."""
+import os
+import re
+import zlib
+
+import numpy as np
+import pytest
+
+import kv_cache_transform_amd as K
+import oracle.kvtc_oracle as O
+import pins
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _params_pair(w, max_bits=8):
+    dt = O.DTYPE_F32 if w.dtype == "f32" else O.DTYPE_BF16
+    op = O.Params(w.n_layers, w.kv_heads, w.head_dim, w.sink, w.window, w.group, max_bits,
+                  w.bits_per_value, dt)
+    kp = K.params(w.n_layers, w.kv_heads, w.head_dim, w.sink, w.window, w.group, max_bits,
+                  w.bits_per_value, dt)
+    return op, kp
+
+
+def test_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "kvtc.h")).read()
+    declared = set(re.findall(r"\b(kvtc_[a-z_]+)\s*\(", header))
+    L = K.lib()
+    missing = [s for s in sorted(declared) if not hasattr(L, s)]
+    assert not missing, missing
+    assert len(declared) >= 20
+    assert K.kvtc_version().startswith("kvtc")
+
+
+def test_calibration_matches_oracle_tiny():
+    w = synth.workload("tiny")
+    op, kp = _params_pair(w)
+    x = synth.gen_kv(w, 0, 0, 1, w.calib_tokens)
+    c = K.Codec(kp)
+    c.calibrate(0, 0, synth.storage(w, x), threads=4)
+    so = O.calibrate(x, op, 0, 0)
+    sl = O.parse_artifact(c.save()).slots[(0, 0)]
+    _compare_slots(sl, so)
+
+
+def _compare_slots(sl, so):
+    assert np.array_equal(sl.mu32, so.mu32)
+    lam_ok = so.lam > so.lam[0] * 1e-12
+    assert np.allclose(sl.lam[lam_ok], so.lam[lam_ok], rtol=1e-6)
+    if np.array_equal(sl.widths, so.widths):
+        G = so.G
+        for a, g in enumerate(so.active_groups):
+            Vl = sl.V32[:, a * G:(a + 1) * G].astype(np.float64)
+            Vo = so.V64[:, g * G:(g + 1) * G]
+            assert np.abs(Vl @ Vl.T - Vo @ Vo.T).max() <= 1e-5
+    else:  # a near-tie may flip: the objective must still agree
+        obj = lambda wv: sum(so.D[g, b] for g, b in enumerate(wv))
+        assert abs(obj(sl.widths) - obj(so.widths)) <= 1e-9 * obj(so.widths)
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_calibration_matches_oracle_llama8b_tensor(kind):
+    w = synth.workload("llama31_8b")
+    op, kp = _params_pair(w)
+    x = synth.gen_kv(w, 3, kind, 1, w.calib_tokens)
+    c = K.Codec(kp)
+    c.calibrate(3, kind, synth.storage(w, x), threads=8)
+    so = O.calibrate(x, op, 3, kind)
+    sl = O.parse_artifact(c.save()).slots[(3, kind)]
+    _compare_slots(sl, so)
+    assert np.array_equal(sl.widths, so.widths)
+
+
+def test_calibration_matches_oracle_group32_small():
+    x, _ = pins.family_b_small(seed=21, n=3000)
+    op = O.Params(2, 2, 32, 4, 8, 32, 8, 1.5, O.DTYPE_F32)
+    kp = K.params(2, 2, 32, 4, 8, 32, 8, 1.5, K.KVTC_F32)
+    c = K.Codec(kp)
+    c.calibrate(1, 1, x, threads=2)
+    so = O.calibrate(x, op, 1, 1)
+    _compare_slots(O.parse_artifact(c.save()).slots[(1, 1)], so)
+
+
+def test_artifact_bytes_interoperate():
+    w = synth.workload("tiny")
+    op, kp = _params_pair(w)
+    x = synth.gen_kv(w, 0, 0, 1, w.calib_tokens)
+    so = O.calibrate(x, op, 0, 0)
+    art = O.Artifact(op, {(0, 0): so}).serialize()
+    c = K.Codec.load(art)
+    assert c.save() == art                       # oracle -> library -> bytes
+    info = c.slot(0, 0)
+    assert info.slot_id == so.slot_id and info.record_bytes == so.record_bytes
+    assert list(info.widths[: op.n_groups]) == so.widths.tolist()
+    c2 = K.Codec(kp)
+    c2.calibrate(0, 0, synth.storage(w, x))
+    back = O.parse_artifact(c2.save())         # library -> oracle parser
+    assert back.slots[(0, 0)].slot_id == c2.slot(0, 0).slot_id
+
+
+def test_artifact_corruption_is_rejected():
+    w = synth.workload("tiny")
+    op, _ = _params_pair(w)
+    so = O.calibrate(synth.gen_kv(w, 0, 0, 1, 600), op, 0, 0)
+    art = bytearray(O.Artifact(op, {(0, 0): so}).serialize())
+    for off in (0, 4, 60, len(art) - 30, len(art) - 1):
+        bad = bytearray(art)
+        bad[off] ^= 0x40
+        with pytest.raises(K.KvtcError) as e:
+            K.Codec.load(bytes(bad))
+        assert e.value.status in (K.KVTC_E_CORRUPT, K.KVTC_E_INVALID)
+    with pytest.raises(K.KvtcError):
+        K.Codec.load(bytes(art[:-9]))
+
+
+def test_encoded_bytes_match_oracle():
+    w = synth.workload("tiny")
+    op, _ = _params_pair(w)
+    so = O.calibrate(synth.gen_kv(w, 0, 0, 1, 800), op, 0, 0)
+    c = K.Codec.load(O.Artifact(op, {(0, 0): so}).serialize())
+    for T in (0, 1, 4, 5, 67, 68, 69, 512, 1000):
+        assert c.encoded_bytes(0, 0, T) == O.stream_bytes(op, so, T)
+    assert c.encoded_bytes(0, 1, 100) == 0          # V never calibrated
+
+
+def test_bad_params_rejected():
+    good = dict(n_layers=1, kv_heads=2, head_dim=64, sink=4, window=8, group=16, max_bits=8,
+                bits_per_value=1.0, dtype=K.KVTC_BF16)
+    for key, val in (("group", 12), ("group", 24), ("head_dim", 60), ("max_bits", 9),
+                     ("bits_per_value", -1.0), ("dtype", 5), ("n_layers", 0), ("sink", -1)):
+        p = dict(good, **{key: val})
+        with pytest.raises(K.KvtcError) as e:
+            K.kvtc_create(K.params(**p))
+        assert e.value.status == K.KVTC_E_INVALID, (key, val)
+
+
+def test_calibrate_errors():
+    c = K.Codec(K.params(2, 1, 64, 4, 8, 16, 8, 2.0, K.KVTC_F32))
+    with pytest.raises(K.KvtcError):
+        c.calibrate(0, 0, np.zeros((12, 64), np.float32))       # no row after s + w
+    with pytest.raises(K.KvtcError):
+        c.calibrate(2, 0, np.zeros((100, 64), np.float32))      # bad layer
+    with pytest.raises(K.KvtcError):
+        c.calibrate(0, 2, np.zeros((100, 64), np.float32))      # bad kind
+
+
+def test_encode_requires_upload_and_calibration():
+    w = synth.workload("tiny")
+    op, kp = _params_pair(w)
+    c = K.Codec(kp)
+    job = K.make_job(0, 0, 100, 4096, 8192, 1 << 20)
+    with pytest.raises(K.KvtcError) as e:
+        c.encode([job], 256)
+    assert e.value.status == K.KVTC_E_INVALID           # never uploaded
+    with pytest.raises(K.KvtcError) as e:
+        c.encode([job], 0)
+    assert e.value.status == K.KVTC_E_INVALID           # no workspace
+
+
+def test_zero_allocation_when_budget_too_small():
+    x, _ = pins.family_b_small(seed=5, n=500)
+    c = K.Codec(K.params(1, 2, 32, 4, 8, 16, 8, 79.0 / 64, K.KVTC_F32))   # 79 bits < 80
+    c.calibrate(0, 0, x)
+    info = c.slot(0, 0)
+    assert info.n_act == 0 and info.record_bytes == 0
+
+
+def test_deflate_roundtrip():
+    data = bytes(np.random.default_rng(0).integers(0, 4, 50000, dtype=np.uint8))
+    z = K.kvtc_deflate(data, 6)
+    assert zlib.decompress(z) == data and len(z) < len(data)
