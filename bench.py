@@ -1,16 +1,19 @@
 """Benchmark of KV-cache transform coding on one MI355X.
 
-Workload: Llama-3.1-8B-shaped cache, 32 layers x {K, V}, 8 kv heads x 128 =
-1024 features, 8192 tokens, bf16, sink 4, window 128, 16x budget (1 bit per
-value), microscale group 16; seeded synthetic KV (shared 96-dim latent per
-layer, per-head rotations, power-law spectrum, 4 outlier key channels per
-head), calibrated on 16384 synthetic tokens per tensor by the library on the
-host.
+Default workload (llama31_8b): Llama-3.1-8B-shaped cache, 32 layers x {K, V},
+8 kv heads x 128 = 1024 features, 8192 tokens, bf16, sink 4, window 128, 16x
+budget (1 bit per value), microscale group 16; seeded synthetic KV (shared
+96-dim latent per layer, per-head rotations, power-law spectrum, 4 outlier key
+channels per head), calibrated on 16384 synthetic tokens per tensor by the
+library on the host.
 
-One step = kvtc_encode of all 64 tensors followed by kvtc_decode of all 64
-streams back to bf16 (each call is one launch per 32 tensors), with inputs,
-streams and outputs resident in HBM. value = bf16 KV bytes per step / step
-time. The DEFLATE ratio (host zlib) is reported outside the timed region.
+One step = kvtc_encode of every tensor followed by kvtc_decode of every
+stream back to bf16 (one launch per 32 tensors), with inputs, streams and
+outputs resident in HBM. value = bf16 KV bytes per step / step time. For a
+paged workload (qwen25_7b_paged) the decode is the layer-by-layer two-stream
+pipeline: stage 1 (unpack) of layer l+1 runs on one stream while stage 2
+(restore into the paged cache) of layer l runs on another. The DEFLATE ratio
+(host zlib) is reported outside the timed region.
 """
 from __future__ import annotations
 
@@ -42,6 +45,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=16, help="most tensors in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-tokens", type=int, default=0, help="override (0 = workload's)")
+    ap.add_argument("--distinct-requests", type=int, default=2,
+                    help="distinct synthetic requests per (layer, kind); the rest are copies")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -82,39 +87,89 @@ def main():
     n_state = codec.state_bytes()
     state = torch.empty(n_state, dtype=torch.uint8, device=dev)
     codec.upload(state, n_state, stream)
-    ws = torch.zeros(K.kvtc_workspace_bytes(len(slots)) // 4, dtype=torch.int32, device=dev)
 
-    # --- resident inputs, streams and outputs
+    # --- jobs: every (layer, kind, request); inputs, streams, outputs resident
     T, F = w.n_tokens, w.features
     esz = w.elem_bytes
+    R = w.n_requests
+    jobs = [(l, k, r) for l in range(w.n_layers) for k in w.kinds for r in range(R)]
+    n_jobs = len(jobs)
     tdt = torch.int16 if dt == K.KVTC_BF16 else torch.float32
-    xs = torch.empty((len(slots), T, F), dtype=tdt, device=dev)
-    for i, (l, k) in enumerate(slots):
-        st = synth.storage(w, synth.gen_kv(w, l, k, synth.ROLE_EVAL, T))
-        xs[i].copy_(torch.from_numpy(st.view(np.int16) if dt == K.KVTC_BF16 else st))
-    sizes = [codec.encoded_bytes(l, k, T) for l, k in slots]
+    xs = torch.empty((n_jobs, T, F), dtype=tdt, device=dev)
+    n_distinct = max(1, min(R, args.distinct_requests))
+    for i, (l, k, r) in enumerate(jobs):
+        if r < n_distinct:
+            st = synth.storage(w, synth.gen_kv(w, l, k, synth.ROLE_EVAL, T, r))
+            xs[i].copy_(torch.from_numpy(st.view(np.int16) if dt == K.KVTC_BF16 else st))
+        else:
+            xs[i].copy_(xs[i - r + r % n_distinct])
+    sizes = [codec.encoded_bytes(l, k, T) for l, k, _ in jobs]
     offs = np.cumsum([0] + [(n + 255) // 256 * 256 for n in sizes])
     sbuf = torch.zeros(int(offs[-1]), dtype=torch.uint8, device=dev)
-    out = torch.empty((len(slots), T, F), dtype=torch.int16, device=dev)
+    ws = torch.zeros(K.kvtc_workspace_bytes(n_jobs) // 4, dtype=torch.int32, device=dev)
     enc_jobs = [K.make_job(l, k, T, xs[i], sbuf.data_ptr() + int(offs[i]), sizes[i])
-                for i, (l, k) in enumerate(slots)]
-    dec_jobs = [K.make_job(l, k, T, sbuf.data_ptr() + int(offs[i]), out[i],
-                           out[i].numel() * 2) for i, (l, k) in enumerate(slots)]
-    log(f"calibration {calib_s:.1f}s; state {n_state / 2**20:.1f} MiB; streams {offs[-1] / 2**20:.1f} MiB")
+                for i, (l, k, _) in enumerate(jobs)]
+    if w.paged:
+        # Each (layer, kind) owns a pool of R * ceil(T / bs) blocks; every
+        # request gets a random disjoint subset of it as its block table.
+        bs = w.block_size
+        per_req = (T + bs - 1) // bs
+        rng = np.random.default_rng(11)
+        tables = torch.empty((n_jobs, per_req), dtype=torch.int32)
+        pools = {}
+        for i, (l, k, r) in enumerate(jobs):
+            if (l, k) not in pools:
+                pools[(l, k)] = rng.permutation(R * per_req).astype(np.int32)
+            tables[i] = torch.from_numpy(pools[(l, k)][r * per_req:(r + 1) * per_req])
+        tables = tables.to(dev)
+        out = torch.empty((len(slots), R * per_req * bs, F), dtype=torch.int16, device=dev)
+        pool_of = {s: i for i, s in enumerate(slots)}
+        dec_jobs = [K.make_job(l, k, T, sbuf.data_ptr() + int(offs[i]), out[pool_of[(l, k)]],
+                               out[pool_of[(l, k)]].numel() * 2, tables[i], bs, R * per_req)
+                    for i, (l, k, _) in enumerate(jobs)]
+    else:
+        out = torch.empty((n_jobs, T, F), dtype=torch.int16, device=dev)
+        dec_jobs = [K.make_job(l, k, T, sbuf.data_ptr() + int(offs[i]), out[i], out[i].numel() * 2)
+                    for i, (l, k, _) in enumerate(jobs)]
+    log(f"calibration {calib_s:.1f}s; state {n_state / 2**20:.1f} MiB; "
+        f"streams {offs[-1] / 2**20:.1f} MiB; {n_jobs} tensors")
 
     def encode():
         codec.encode(enc_jobs, ws, stream)
 
+    pipe = Pipeline(K, codec, w, jobs, dec_jobs, dev) if w.paged else None
+
     def decode():
-        codec.decode(dec_jobs, K.KVTC_BF16, ws, stream)
+        if pipe is not None:
+            pipe.run(stream)
+        else:
+            codec.decode(dec_jobs, K.KVTC_BF16, ws, stream)
+
+    # Plain device copy of a known size: the practical HBM ceiling and the
+    # reference that scales the FETCH_SIZE / WRITE_SIZE counters.
+    copy_bytes = 1 << 30
+    csrc = torch.empty(copy_bytes // 2, dtype=torch.int16, device=dev)
+    cdst = torch.empty_like(csrc)
+    for _ in range(2):
+        cdst.copy_(csrc)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        cdst.copy_(csrc)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * copy_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del csrc, cdst
 
     for _ in range(args.warmup):
         encode()
         decode()
     torch.cuda.synchronize()
-    st = K.kvtc_read_device_status(ws, len(slots), stream)
+    st = K.kvtc_read_device_status(ws, n_jobs, stream)
     if np.any(st != 0):
         raise SystemExit(f"device status errors: {st}")
+    if pipe is not None:
+        pipe.check()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -132,31 +187,31 @@ def main():
     dec_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
     ms_per_step = wall * 1e3 / args.steps
 
-    kv_bytes = len(slots) * T * F * esz
+    kv_bytes = n_jobs * T * F * esz
     r_eff = {s: infos[s].r_eff for s in slots}
-    # Algorithmic HBM bytes per tensor: raw KV, the stream, the operational
-    # basis (bf16 for encode, fp16 for decode) and the fp32 mean.
-    basis = sum(r_eff[s] * F * 2 + F * 4 for s in slots)
+    # Algorithmic HBM bytes of one call: raw KV, the streams, and per tensor
+    # the operational basis (bf16 for encode, fp16 for decode) and fp32 mean.
+    basis = sum(r_eff[(l, k)] * F * 2 + F * 4 for l, k, _ in jobs)
     stream_total = int(sum(sizes))
     enc_alg = kv_bytes + stream_total + basis
     dec_alg = kv_bytes + stream_total + basis
-    n_launch = (len(slots) + 31) // 32
-    enc_gbps = kv_bytes / (np.median(enc_ms) * 1e-3) / 1e9
-    dec_gbps = kv_bytes / (np.median(dec_ms) * 1e-3) / 1e9
-    enc_ach = enc_alg / (np.median(enc_ms) * 1e-3) / 1e9
-    dec_ach = dec_alg / (np.median(dec_ms) * 1e-3) / 1e9
-    dominant = "decode" if np.median(dec_ms) >= np.median(enc_ms) else "encode"
-    ach = dec_ach if dominant == "decode" else enc_ach
+    n_launch = (n_jobs + 31) // 32
+    enc_t = float(np.median(enc_ms)) * 1e-3
+    dec_t = float(np.median(dec_ms)) * 1e-3
+    dominant = "decode" if dec_t >= enc_t else "encode"
+    ach = (dec_alg / dec_t if dominant == "decode" else enc_alg / enc_t) / 1e9
+    other = (enc_alg / enc_t if dominant == "decode" else dec_alg / dec_t) / 1e9
     alg = dec_alg if dominant == "decode" else enc_alg
-    flops = sum(2 * F * r_eff[s] * (T - w.sink - w.window) for s in slots)
+    flops = sum(2 * F * r_eff[(l, k)] * (T - w.sink - w.window) for l, k, _ in jobs)
 
     # --- compression ratio (host zlib on a sample of streams; not timed)
     host_streams = sbuf.cpu().numpy()
-    samp = list(range(0, len(slots), max(1, len(slots) // 8)))
-    raw_s = sum(T * F * esz for _ in samp)
+    samp = list(range(0, n_jobs, max(1, n_jobs // 8)))
+    raw_s = len(samp) * T * F * esz
     st_s = sum(sizes[i] for i in samp)
     z_s = sum(len(K.kvtc_deflate(host_streams[offs[i]:offs[i] + sizes[i]].tobytes(), 6)) for i in samp)
 
+    dec_kernel = "unpack_kernel + restore_kernel (two streams)" if w.paged else "decode_kernel"
     result = {
         "metric": "KV encode/decode GB/s (bf16 KV) and % of roofline, Llama-3.1-8B shape 8K tok",
         "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
@@ -170,31 +225,111 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {len(slots)} tensors x {T} tokens x {F} "
-                               f"features bf16, s={w.sink} w={w.window} G={w.group} "
-                               f"{w.bits_per_value} bit/value, encode+decode per step",
-                   "layers": w.n_layers, "tokens": T, "features": F},
-        "encode_GBps": round(enc_gbps, 2),
-        "decode_GBps": round(dec_gbps, 2),
-        "encode_ms": round(float(np.median(enc_ms)), 4),
-        "decode_ms": round(float(np.median(dec_ms)), 4),
-        "roofline": {"bound": "hbm", "kernel": f"{dominant}_kernel",
+        "config": {"workload": f"{args.workload}: {n_jobs} tensors x {T} tokens x {F} "
+                               f"features {w.dtype}, s={w.sink} w={w.window} G={w.group} "
+                               f"{w.bits_per_value} bit/value, encode+decode per step"
+                               + (", paged 16-token blocks, two-stream decode" if w.paged else ""),
+                   "layers": w.n_layers, "requests": R, "tokens": T, "features": F},
+        "encode_GBps": round(kv_bytes / enc_t / 1e9, 2),
+        "decode_GBps": round(kv_bytes / dec_t / 1e9, 2),
+        "encode_ms": round(enc_t * 1e3, 4),
+        "decode_ms": round(dec_t * 1e3, 4),
+        "roofline": {"bound": "hbm",
+                     "kernel": dec_kernel if dominant == "decode" else "encode_kernel",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
                      "alg_bytes_per_launch": int(alg / n_launch), "launches_per_call": n_launch},
-        "roofline_other": {"kernel": ("encode" if dominant == "decode" else "decode") + "_kernel",
-                           "achieved": round(enc_ach if dominant == "decode" else dec_ach, 1),
-                           "frac": round((enc_ach if dominant == "decode" else dec_ach) / HBM_PEAK_GBPS, 4)},
+        "roofline_other": {"kernel": "encode_kernel" if dominant == "decode" else dec_kernel,
+                           "achieved": round(other, 1), "frac": round(other / HBM_PEAK_GBPS, 4)},
         "mfma_flops_per_call": flops,
+        "copy_GBps": round(copy_gbps, 1),
         "compression": {"raw_over_stream": round(raw_s / st_s, 3),
                         "raw_over_deflate": round(raw_s / z_s, 3),
                         "r_eff": sorted(set(r_eff.values()))},
         "calibration_s": round(calib_s, 1),
     }
-
+    if pipe is not None:
+        result["pipeline"] = pipe.overlap(stream)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(codec, w, slots[: args.cpu_sample], xs, K)
+        result["cpu_baseline"] = cpu_baseline(codec, w, jobs[: args.cpu_sample], xs, K)
     print(json.dumps(result), flush=True)
+
+
+class Pipeline:
+    """Layer-by-layer decode on two streams: stage 1 (unpack, stream U) of
+    layer l+1 overlaps stage 2 (restore, stream R) of layer l; two staging
+    buffers and workspaces alternate between layers."""
+
+    def __init__(self, K, codec, w, jobs, dec_jobs, dev):
+        import torch
+        self.K, self.codec, self.torch = K, codec, torch
+        self.layers = []
+        for l in range(w.n_layers):
+            self.layers.append([dj for (jl, _, _), dj in zip(jobs, dec_jobs) if jl == l])
+        self.nst = max(codec.staging_bytes(js) for js in self.layers)
+        self.staging = [torch.empty(self.nst, dtype=torch.uint8, device=dev) for _ in range(2)]
+        self.nj = max(len(js) for js in self.layers)
+        self.ws = [torch.zeros(K.kvtc_workspace_bytes(self.nj) // 4, dtype=torch.int32, device=dev)
+                   for _ in range(2)]
+        self.su, self.sr = torch.cuda.Stream(), torch.cuda.Stream()
+        L = len(self.layers)
+        self.ev_u = [torch.cuda.Event() for _ in range(L)]
+        self.ev_r = [torch.cuda.Event() for _ in range(L)]
+
+    def run(self, stream):
+        torch, K = self.torch, self.K
+        start = torch.cuda.Event()
+        start.record(stream)
+        self.su.wait_event(start)
+        self.sr.wait_event(start)
+        for l, js in enumerate(self.layers):
+            b = l % 2
+            if l >= 2:
+                self.su.wait_event(self.ev_r[l - 2])        # staging buffer b is free again
+            self.codec.decode_unpack(js, K.KVTC_BF16, self.staging[b], self.nst, self.ws[b], self.su)
+            self.ev_u[l].record(self.su)
+            self.sr.wait_event(self.ev_u[l])
+            self.codec.decode_restore(js, K.KVTC_BF16, self.staging[b], self.nst, self.ws[b], self.sr)
+            self.ev_r[l].record(self.sr)
+        stream.wait_event(self.ev_r[-1])
+        stream.wait_stream(self.su)
+
+    def check(self):
+        for b in range(2):
+            st = self.K.kvtc_read_device_status(self.ws[b], self.nj, None)
+            if np.any(st != 0):
+                raise SystemExit(f"pipeline status errors: {st}")
+
+    def overlap(self, stream, reps=3):
+        """overlap = (unpack time + restore time, back to back on one stream)
+        / (two-stream pipelined time)."""
+        torch, K = self.torch, self.K
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        seq = []
+        for _ in range(reps):
+            e[0].record(stream)
+            for js in self.layers:
+                self.codec.decode_unpack(js, K.KVTC_BF16, self.staging[0], self.nst, self.ws[0], stream)
+            e[1].record(stream)
+            for js in self.layers:
+                self.codec.decode_unpack(js, K.KVTC_BF16, self.staging[0], self.nst, self.ws[0], stream)
+                self.codec.decode_restore(js, K.KVTC_BF16, self.staging[0], self.nst, self.ws[0], stream)
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            t_u = e[0].elapsed_time(e[1])
+            seq.append((t_u, e[1].elapsed_time(e[2]) - t_u))
+        t_u, t_r = np.median(np.array(seq), axis=0)
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(reps):
+            p0.record(stream)
+            self.run(stream)
+            p1.record(stream)
+            torch.cuda.synchronize()
+            times.append(p0.elapsed_time(p1))
+        t_p = float(np.median(times))
+        return {"unpack_ms": round(float(t_u), 4), "restore_ms": round(float(t_r), 4),
+                "pipelined_ms": round(t_p, 4), "overlap": round(float(t_u + t_r) / t_p, 3)}
 
 
 def cpu_baseline(codec, w, sample, xs, K, budget_s=12.0):
@@ -208,10 +343,11 @@ def cpu_baseline(codec, w, sample, xs, K, budget_s=12.0):
     T, F = w.n_tokens, w.features
     t_enc = t_dec = 0.0
     done = []
-    for i, (l, k) in enumerate(sample):
+    for i, (l, k, _) in enumerate(sample):
         if t_enc + t_dec > budget_s:
             break
-        store = xs[i].cpu().numpy().view(np.uint16)
+        store = xs[i].cpu().numpy()
+        store = store.view(np.uint16) if store.dtype == np.int16 else store
         t = time.perf_counter()
         er = O.encode(store, p, art.slots[(l, k)], l, k)
         t_enc += time.perf_counter() - t
@@ -219,14 +355,13 @@ def cpu_baseline(codec, w, sample, xs, K, budget_s=12.0):
         O.decode(er.stream, p, art.slots[(l, k)], l, k, T, O.DTYPE_BF16)
         t_dec += time.perf_counter() - t
         done.append((l, k))
-    sample = done
-    kv = len(sample) * T * F * w.elem_bytes
+    kv = len(done) * T * F * w.elem_bytes
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     return {"value": round(kv / (t_enc + t_dec) / 1e9, 4), "unit": "GB/s",
             "cores": int(threads), "kind": "oracle",
             "encode_GBps": round(kv / t_enc / 1e9, 4), "decode_GBps": round(kv / t_dec / 1e9, 4),
-            "sample": f"{len(sample)} of {w.n_layers * len(w.kinds)} tensors "
-                      f"({len(sample)} x {T} x {F} bf16), encode + decode, same artifact"}
+            "sample": f"{len(done)} of {w.n_tensors} tensors ({len(done)} x {T} x {F} "
+                      f"{w.dtype}), encode + decode, same artifact, about {budget_s:.0f} s"}
 
 
 if __name__ == "__main__":

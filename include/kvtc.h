@@ -180,8 +180,10 @@ kvtc_status kvtc_upload(kvtc_codec* codec, void* d_state, size_t bytes, hipStrea
 /* Exact stream size for a tensor of n_tokens rows (0 if not calibrated). */
 size_t kvtc_encoded_bytes(const kvtc_codec* codec, int32_t layer, int32_t kind,
                           int64_t n_tokens);
-/* Workspace (device) for a call with up to max_jobs jobs: one int32 status
- * word per job, 256-byte aligned. */
+/* Workspace (device) for a call with up to max_jobs jobs: one 64-bit status
+ * word per job, 256-byte aligned. Each launch stamps the words it writes, so
+ * the workspace needs no clearing between calls; kvtc_decode_restore reads
+ * the words kvtc_decode_unpack left. */
 size_t kvtc_workspace_bytes(int32_t max_jobs);
 
 /* Encode n_jobs tensors in one launch (section 2B). Each job's dst must hold

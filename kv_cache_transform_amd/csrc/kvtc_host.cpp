@@ -4,6 +4,7 @@
 #include <zlib.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <limits>
@@ -565,7 +566,7 @@ size_t kvtc_encoded_bytes(const kvtc_codec* c, int32_t layer, int32_t kind, int6
 }
 
 size_t kvtc_workspace_bytes(int32_t max_jobs) {
-  return align_up((size_t)std::max(max_jobs, 1) * sizeof(int32_t), kAlign);
+  return align_up((size_t)std::max(max_jobs, 1) * sizeof(uint64_t), kAlign);
 }
 
 size_t kvtc_staging_bytes(const kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs) {
@@ -586,6 +587,14 @@ size_t kvtc_staging_bytes(const kvtc_codec* c, const kvtc_job* jobs, int32_t n_j
 namespace {
 
 enum class Mode { Encode, Decode, Unpack, Restore, Pack };
+
+// Launch stamps for the workspace status words (0 is never issued).
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t e = ++counter;
+  if (e == 0) e = ++counter;
+  return e;
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -611,7 +620,8 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
     a.out_dtype = out_dtype;
     a.F = F;
     a.state = c->d_state;
-    a.status = (int32_t*)d_ws + b0;
+    a.status = (unsigned long long*)d_ws + b0;
+    a.epoch = next_epoch();
     uint32_t tiles = 0;
     int km = 0;
     size_t rb_max = 0, r_enc_max = 0;
@@ -671,14 +681,15 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
     a.total_tiles = tiles;
     size_t l = 16;
     if (mode == Mode::Encode)
-      l = std::max({l, r_enc_max * kEncRowPad * 2, (size_t)kEncTile * rb_max});
+      l = std::max({l, 2 * std::max<size_t>(r_enc_max, 32) * kEncRowPad * 2 + (size_t)F * 4,
+                    (size_t)kEncTile * rb_max});
     else if (mode == Mode::Pack)
       l = std::max(l, (size_t)kEncTile * rb_max);
     else if (mode == Mode::Decode)
-      l = std::max(l, (size_t)kDecTile * rb_max);
+      l = std::max(align_up((size_t)kDecTile * rb_max + 16, 16), (size_t)4 * 32 * kOutRow) + (size_t)F * 4;
     else if (mode == Mode::Unpack)
-      l = std::max(l, (size_t)kUnpackTile * rb_max);
-    if (l > 65536) return fail(KVTC_E_UNSUPPORTED, "records too large for one tile's LDS");
+      l = std::max(l, (size_t)kUnpackTile * rb_max + 16);
+    if (l > 160 * 1024) return fail(KVTC_E_UNSUPPORTED, "records too large for one tile's LDS");
     batches.push_back(a);
     kmax.push_back(mode == Mode::Encode ? (int)(r_enc_max / 32) : km);
     lds.push_back(l);
@@ -773,9 +784,11 @@ kvtc_status kvtc_pack(kvtc_codec* c, const kvtc_job* job, const void* d_codes, c
 
 kvtc_status kvtc_read_device_status(const void* d_ws, int32_t n_jobs, int32_t* status, hipStream_t stream) {
   if (!d_ws || !status || n_jobs <= 0) return fail(KVTC_E_INVALID, "bad arguments");
+  std::vector<uint64_t> words(n_jobs);
   hipError_t e = hipStreamSynchronize(stream);
-  if (e == hipSuccess) e = hipMemcpy(status, d_ws, sizeof(int32_t) * n_jobs, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(words.data(), d_ws, sizeof(uint64_t) * n_jobs, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(KVTC_E_HIP, std::string("status read: ") + hipGetErrorString(e));
+  for (int i = 0; i < n_jobs; ++i) status[i] = rank_status((int)(words[i] & 0xFF));
   return KVTC_OK;
 }
 

@@ -70,8 +70,21 @@ struct LaunchArgs {
   int32_t F;
   int32_t pad;
   const uint8_t* state;    // device state base
-  int32_t* status;         // per-launch slice of the workspace status words
+  unsigned long long* status;  // per-launch slice of the workspace status words
+  uint32_t epoch;          // stamp of this launch (see status_word)
+  uint32_t pad2;
 };
+
+// Workspace status words: (epoch << 32) | rank, combined with atomicMax so
+// that every launch overrides older contents without a reset and the most
+// severe result of a launch wins. Ranks: 0 OK, 1 INVALID (bad block table
+// entry), 2 MISMATCH, 3 CORRUPT.
+__host__ __device__ inline int status_rank(int st) {
+  return st == KVTC_OK ? 0 : st == KVTC_E_INVALID ? 1 : st == KVTC_E_MISMATCH ? 2 : 3;
+}
+__host__ __device__ inline int rank_status(int rank) {
+  return rank == 0 ? KVTC_OK : rank == 1 ? KVTC_E_INVALID : rank == 2 ? KVTC_E_MISMATCH : KVTC_E_CORRUPT;
+}
 
 // Tile sizes (tokens per workgroup tile).
 constexpr int kEncTile = 128;
@@ -80,6 +93,7 @@ constexpr int kUnpackTile = 256;
 constexpr int kPassRows = 16;
 constexpr int kEncKS = 64;                 // features per LDS basis slice (encode)
 constexpr int kEncRowPad = kEncKS + 8;     // bf16 elements per LDS basis row
+constexpr int kOutRow = 128 + 16;          // bytes per LDS output-staging row (decode)
 
 // Host-side launchers implemented in kvtc_kernels.hip (G = group size, lds =
 // dynamic LDS bytes). They return a hipError_t value cast to int.

@@ -37,6 +37,9 @@ namespace kvtc {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 
@@ -62,6 +65,28 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Two fp32 -> packed bf16 / fp16, round to nearest even (v_cvt_pk_*_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// 8 bytes from any LDS byte address: three aligned dword reads and two
+// byte-aligns (the buffer is padded so the last read stays inside it).
+__device__ __forceinline__ uint64_t lds_u64(const uint8_t* p) {
+  const uintptr_t a = (uintptr_t)p;
+  const uint32_t* b = (const uint32_t*)(a & ~(uintptr_t)3);
+  const uint32_t sh = (uint32_t)(a & 3u);
+  const uint32_t w0 = b[0], w1 = b[1], w2 = b[2];
+  const uint32_t lo = __builtin_amdgcn_alignbyte(w1, w0, sh);
+  const uint32_t hi = __builtin_amdgcn_alignbyte(w2, w1, sh);
+  return (uint64_t)lo | ((uint64_t)hi << 32);
+}
 
 __device__ __forceinline__ size_t record_base(const JobDesc& jd, int F, int esz) {
   return (size_t)kHeaderBytes + (size_t)(jd.s1 + jd.w1) * F * esz;
@@ -97,6 +122,17 @@ __device__ int check_header(const LaunchArgs& a, const JobDesc& jd, const DevSlo
       h[10] != (uint32_t)sl.slot_id || h[11] != (uint32_t)(sl.slot_id >> 32))
     return KVTC_E_MISMATCH;
   return KVTC_OK;
+}
+
+__device__ __forceinline__ void set_status(const LaunchArgs& a, int j, int st) {
+  atomicMax(&a.status[j], ((unsigned long long)a.epoch << 32) | (unsigned long long)status_rank(st));
+}
+
+// Rank an earlier launch on this workspace (stage 1) recorded for job j;
+// results this launch wrote itself do not count.
+__device__ __forceinline__ int prior_rank(const LaunchArgs& a, int j) {
+  const unsigned long long w = a.status[j];
+  return (uint32_t)(w >> 32) == a.epoch ? 0 : (int)(w & 0xFFull);
 }
 
 // Physical output row of token t (contiguous or through the block table);
@@ -225,7 +261,7 @@ __device__ __forceinline__ void put_group(uint8_t* rec, const DevSlot& sl, int a
 // one byte per code in a 64-bit word.
 __device__ __forceinline__ uint64_t get_codes8(const uint8_t* rec, const DevSlot& sl, int a, int o) {
   const int w = sl.width[a];
-  const uint64_t bits = load_bytes(rec + sl.chunk_off[a] + (o * w) / 8, w);
+  const uint64_t bits = lds_u64(rec + sl.chunk_off[a] + (o * w) / 8);
   const uint64_t mask = (1ull << w) - 1ull;
   uint64_t out = 0;
   for (int j = 0; j < 8; ++j) out |= ((bits >> (j * w)) & mask) << (8 * j);
@@ -234,7 +270,7 @@ __device__ __forceinline__ uint64_t get_codes8(const uint8_t* rec, const DevSlot
 
 // --------------------------------------------------------------- encode ---
 
-template <int NB, int G>
+template <int NB, int G, bool F32IN>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const uint32_t tile = logical_tile();
@@ -244,11 +280,11 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
   const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
   const uint32_t lt = tile - jd.tile_begin;
   const int F = a.F;
-  const int esz = a.dtype == KVTC_F32 ? 4 : 2;
+  constexpr int esz = F32IN ? 4 : 2;
   const size_t row_bytes = (size_t)F * esz;
   if (lt == 0 && threadIdx.x == 0) {
     write_header(a, jd, sl);
-    a.status[j] = KVTC_OK;
+    set_status(a, j, KVTC_OK);
   }
   if (lt >= jd.n_ctiles) {
     encode_passthrough(jd, lt - jd.n_ctiles, row_bytes);
@@ -264,10 +300,50 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
   const int tl = wave * 32 + (lane & 31);            // token within the tile
   const bool tok_ok = (uint32_t)tl < n;
   const uint8_t* xrow = (const uint8_t*)jd.src + (size_t)(jd.s1 + t0 + (tok_ok ? tl : 0)) * row_bytes;
-  const float* mu = (const float*)(a.state + sl.mu_off);
   const uint16_t* venc = (const uint16_t*)(a.state + sl.venc_off);
   const int nb = sl.r_enc / 32;
-  uint16_t* vs = (uint16_t*)smem;
+
+  // LDS: two basis K-slices [32 * NB][kEncRowPad] bf16, then the mean (F fp32).
+  constexpr int slice_elems = 32 * NB * kEncRowPad;
+  uint16_t* const vbase = (uint16_t*)smem;
+  float* mu_l = (float*)(smem + (size_t)4 * slice_elems);
+  {
+    const float4* mu = (const float4*)(a.state + sl.mu_off);
+    for (int i = threadIdx.x; i < F / 4; i += kThreads) ((float4*)mu_l)[i] = mu[i];
+  }
+  // Slice copy: a slice holds 32 * NB rows of kEncKS features, 32 * NB * 8
+  // vectors of 16 bytes, so thread t moves vectors t + q * kThreads, q < NB,
+  // with no predicate. Rows >= r_enc (zero in the device state when r_enc
+  // < 32 * NB, clamped re-reads otherwise) are never read by the MFMA loop.
+  typedef uint32_t vregs_t __attribute__((ext_vector_type(4 * NB)));
+  vregs_t vreg;
+  const int vlast = sl.r_enc * (kEncKS / 8) - 1;
+#define KVTC_LOAD_SLICE(K0)                                                          \
+  _Pragma("unroll") for (int q = 0; q < NB; ++q) {                                   \
+    const int idx = min((int)threadIdx.x + q * kThreads, vlast);                     \
+    const uint4 v = *(const uint4*)(venc + (size_t)(idx / (kEncKS / 8)) * F + (K0) + \
+                                    (idx % (kEncKS / 8)) * 8);                       \
+    vreg[4 * q] = v.x;                                                               \
+    vreg[4 * q + 1] = v.y;                                                           \
+    vreg[4 * q + 2] = v.z;                                                           \
+    vreg[4 * q + 3] = v.w;                                                           \
+  }
+#define KVTC_STORE_SLICE(BUF)                                                        \
+  _Pragma("unroll") for (int q = 0; q < NB; ++q) {                                   \
+    const int idx = (int)threadIdx.x + q * kThreads;                                 \
+    *(uint4*)((BUF) + (idx / (kEncKS / 8)) * kEncRowPad + (idx % (kEncKS / 8)) * 8) = \
+        make_uint4(vreg[4 * q], vreg[4 * q + 1], vreg[4 * q + 2], vreg[4 * q + 3]);  \
+  }
+  // Token fragments of one slice: K step s reads features k0 + 16s + 8h .. +8.
+  constexpr int XV = F32IN ? 2 : 1;                  // 16-byte vectors per K step
+  uint4 xr[4 * XV], xn[4 * XV];
+  auto load_x = [&](int k0, uint4* dst) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int v = 0; v < XV; ++v)
+        dst[s * XV + v] = *(const uint4*)(xrow + (size_t)(k0 + 16 * s + 8 * h) * esz + 16 * v);
+  };
 
   f32x16 acc[NB];
 #pragma unroll
@@ -275,22 +351,25 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
 
-  for (int k0 = 0; k0 < F; k0 += kEncKS) {
-    __syncthreads();
-    const int nvec = sl.r_enc * (kEncKS / 8);
-    for (int idx = threadIdx.x; idx < nvec; idx += kThreads) {
-      const int r = idx / (kEncKS / 8), c8 = idx % (kEncKS / 8);
-      const uint4 v = *(const uint4*)(venc + (size_t)r * F + k0 + c8 * 8);
-      *(uint4*)(vs + r * kEncRowPad + c8 * 8) = v;
+  KVTC_LOAD_SLICE(0)
+  load_x(0, xr);
+  KVTC_STORE_SLICE(vbase)
+  __syncthreads();
+  int it = 0;
+  for (int k0 = 0; k0 < F; k0 += kEncKS, ++it) {
+    const bool more = k0 + kEncKS < F;
+    if (more) {
+      KVTC_LOAD_SLICE(k0 + kEncKS)
+      load_x(k0 + kEncKS, xn);
     }
-    __syncthreads();
+    const uint16_t* vs = vbase + (it & 1) * slice_elems;
 #pragma unroll
     for (int s = 0; s < kEncKS / 16; ++s) {
       const int f = k0 + 16 * s + 8 * h;
       // Centred token operand: x' = bf16_rne(fp32(x) - mu).
       float xv[8];
-      if (a.dtype == KVTC_BF16) {
-        const uint4 raw = *(const uint4*)(xrow + (size_t)f * 2);
+      if (!F32IN) {
+        const uint4 raw = xr[s];
         const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -298,18 +377,18 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
           xv[2 * e + 1] = bf16_to_f32(w4[e] >> 16);
         }
       } else {
-        const float4 lo = *(const float4*)(xrow + (size_t)f * 4);
-        const float4 hi = *(const float4*)(xrow + (size_t)f * 4 + 16);
-        xv[0] = lo.x; xv[1] = lo.y; xv[2] = lo.z; xv[3] = lo.w;
-        xv[4] = hi.x; xv[5] = hi.y; xv[6] = hi.z; xv[7] = hi.w;
+        const uint4 lo = xr[2 * s], hi = xr[2 * s + 1];
+        xv[0] = __uint_as_float(lo.x); xv[1] = __uint_as_float(lo.y);
+        xv[2] = __uint_as_float(lo.z); xv[3] = __uint_as_float(lo.w);
+        xv[4] = __uint_as_float(hi.x); xv[5] = __uint_as_float(hi.y);
+        xv[6] = __uint_as_float(hi.z); xv[7] = __uint_as_float(hi.w);
       }
-      const float4 m0 = *(const float4*)(mu + f);
-      const float4 m1 = *(const float4*)(mu + f + 4);
+      const float4 m0 = *(const float4*)(mu_l + f);
+      const float4 m1 = *(const float4*)(mu_l + f + 4);
       const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
       uint32_t pk[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pk[e] = bf16_bits_rne(xv[2 * e] - mv[2 * e]) | (bf16_bits_rne(xv[2 * e + 1] - mv[2 * e + 1]) << 16);
+      for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(xv[2 * e] - mv[2 * e], xv[2 * e + 1] - mv[2 * e + 1]);
       const bf16x8 bx = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
@@ -320,8 +399,15 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
         }
       }
     }
+    if (more) {
+      KVTC_STORE_SLICE(vbase + ((it + 1) & 1) * slice_elems)
+#pragma unroll
+      for (int v = 0; v < 4 * XV; ++v) xr[v] = xn[v];
+    }
+    __syncthreads();
   }
-  __syncthreads();  // the basis slice region becomes the record staging area
+#undef KVTC_LOAD_SLICE
+#undef KVTC_STORE_SLICE
 
   // Quantize and pack. acc[b][i] holds component 32b + 8(i/4) + 4h + i%4 of
   // token tl; a group of G components is the item range
@@ -403,35 +489,39 @@ __device__ __forceinline__ f16x8 make_frag(uint64_t codes8, float shift, float s
                                            float Sinv) {
   const float k = (float)((1 << w) - 1);
   const float step = scale / k;
-  f16x8 f;
+  uint32_t pk[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float q = (float)((codes8 >> (8 * j)) & 0xFFu);
-    const float c = __builtin_fmaf(q, step, shift);
-    f[j] = (_Float16)(c * Sinv);
+  for (int j = 0; j < 4; ++j) {
+    const float q0 = (float)((codes8 >> (16 * j)) & 0xFFu);
+    const float q1 = (float)((codes8 >> (16 * j + 8)) & 0xFFu);
+    pk[j] = pack_f16x2(__builtin_fmaf(q0, step, shift) * Sinv, __builtin_fmaf(q1, step, shift) * Sinv);
   }
-  return f;
+  return __builtin_bit_cast(f16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
 }
 
 // Restore the compressed rows of one tile. FROM_STAGING selects the code
 // source: LDS-staged records (fused decode) or the stage-1 staging buffer.
+// Each wave owns 32 tokens. The basis fragments of the next 32-feature block
+// are loaded while the current block runs on the MFMA; the result (lane =
+// token, 16 features) goes through a wave-private LDS area so that the global
+// stores are 16-byte lanes over whole 128-byte row segments.
+// LDS: lds_out = 4 waves x 32 rows x kOutRow bytes, mu_l = F floats.
 template <int KMAX, int G, bool FROM_STAGING>
 __device__ void restore_tile(const LaunchArgs& a, const JobDesc& jd, const DevSlot& sl,
-                             const uint8_t* lds_rec, uint32_t t0, uint32_t n, int* bad) {
+                             const uint8_t* lds_rec, uint8_t* lds_out, const float* mu_l,
+                             uint32_t t0, uint32_t n, int* bad) {
   const int F = a.F;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5;
   const int tl = wave * 32 + (lane & 31);
   const bool tok_ok = (uint32_t)tl < n;
   const int tt = tok_ok ? tl : 0;
-  const float* mu = (const float*)(a.state + sl.mu_off);
   const uint16_t* vdec = (const uint16_t*)(a.state + sl.vdec_off);
   const int ks = sl.r_dec / 16;
 
-  // Code source for this token.
   const uint8_t* rec = nullptr;
   const uint8_t* scodes = nullptr;
-  const float2* ssp;
+  const float2* ssp = nullptr;
   if (FROM_STAGING) {
     const uint8_t* st = (const uint8_t*)jd.staging;
     scodes = st + (size_t)(t0 + tt) * sl.r_eff;
@@ -439,11 +529,10 @@ __device__ void restore_tile(const LaunchArgs& a, const JobDesc& jd, const DevSl
     ssp = (const float2*)(st + ss_off) + (size_t)(t0 + tt) * sl.n_act;
   } else {
     rec = lds_rec + (size_t)tt * sl.record_bytes;
-    ssp = (const float2*)rec;  // 8-byte pairs at the record start (LDS)
   }
   auto ss_of = [&](int g) -> float2 {
     if (FROM_STAGING) return ssp[g];
-    const uint64_t raw = load_bytes(rec + 8 * g, 8);
+    const uint64_t raw = lds_u64(rec + 8 * g);
     return make_float2(__uint_as_float((uint32_t)raw), __uint_as_float((uint32_t)(raw >> 32)));
   };
   float S, Sinv;
@@ -459,10 +548,7 @@ __device__ void restore_tile(const LaunchArgs& a, const JobDesc& jd, const DevSl
   f16x8 bfr[KMAX];
 #pragma unroll
   for (int s = 0; s < KMAX; ++s) {
-    f16x8 z;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) z[e] = (_Float16)0.f;
-    bfr[s] = z;
+    bfr[s] = __builtin_bit_cast(f16x8, make_uint4(0u, 0u, 0u, 0u));
     const int c = 16 * s + 8 * h;
     if (s < ks && c < sl.r_eff) {
       const int ag = c / G, o = c % G;
@@ -475,44 +561,85 @@ __device__ void restore_tile(const LaunchArgs& a, const JobDesc& jd, const DevSl
       bfr[s] = make_frag(codes8, p.x, p.y, sl.width[ag], Sinv);
     }
   }
+  // The record area may be reused by the output staging from here on.
+  __syncthreads();
 
-  const uint32_t t = jd.s1 + t0 + tt;
-  const long orow = tok_ok ? out_row(jd, t) : -1;
-  if (tok_ok && orow < 0) *bad = 1;
-  const bool store = orow >= 0;
-  for (int fb = 0; fb < F / 32; ++fb) {
-    f32x16 acc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  const int osz = a.out_dtype == KVTC_F32 ? 4 : 2;
+  const int fpg = 128 / (32 * osz);                   // feature blocks per 128-byte group
+  uint8_t* wout = lds_out + (size_t)wave * 32 * kOutRow;
+  const uint32_t tok0 = jd.s1 + t0 + wave * 32;       // first token of this wave
+  const int nfb_all = F / 32;
+
+  uint4 cur[KMAX], nxt[KMAX];
+  auto load_a = [&](int fb, uint4* dst) {
     const uint16_t* vrow = vdec + (size_t)(fb * 32 + (lane & 31)) * sl.r_dec + 8 * h;
 #pragma unroll
-    for (int s = 0; s < KMAX; ++s) {
-      if (s < ks) {
-        const uint4 av = *(const uint4*)(vrow + 16 * s);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av), bfr[s], acc,
-                                                     0, 0, 0);
+    for (int s = 0; s < KMAX; ++s)
+      if (s < ks) dst[s] = *(const uint4*)(vrow + 16 * s);
+  };
+  load_a(0, cur);
+  for (int fg = 0; fg < nfb_all; fg += fpg) {
+    const int nfb = min(fpg, nfb_all - fg);
+    for (int u = 0; u < nfb; ++u) {
+      const int fb = fg + u;
+      if (fb + 1 < nfb_all) load_a(fb + 1, nxt);
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < KMAX; ++s) {
+        if (s < ks)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, cur[s]), bfr[s], acc,
+                                                       0, 0, 0);
       }
-    }
-    if (store) {
+      // D[feature][token]: this lane holds token (lane & 31) and features
+      // fb*32 + 8*qd + 4*h + {0..3} in acc[4*qd .. 4*qd+3].
+      uint8_t* orow_l = wout + (size_t)(lane & 31) * kOutRow + (size_t)u * 32 * osz;
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         const int f = fb * 32 + 8 * qd + 4 * h;
-        const float4 m4 = *(const float4*)(mu + f);
+        const float4 m4 = *(const float4*)(mu_l + f);
         const float o0 = __builtin_fmaf(acc[4 * qd + 0], S, m4.x);
         const float o1 = __builtin_fmaf(acc[4 * qd + 1], S, m4.y);
         const float o2 = __builtin_fmaf(acc[4 * qd + 2], S, m4.z);
         const float o3 = __builtin_fmaf(acc[4 * qd + 3], S, m4.w);
-        if (a.out_dtype == KVTC_F32) {
-          *(float4*)((float*)jd.dst + (size_t)orow * F + f) = make_float4(o0, o1, o2, o3);
+        const int col = (8 * qd + 4 * h) * osz;
+        if (osz == 4)
+          *(float4*)(orow_l + col) = make_float4(o0, o1, o2, o3);
+        else
+          *(uint2*)(orow_l + col) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+      }
+#pragma unroll
+      for (int s = 0; s < KMAX; ++s) cur[s] = nxt[s];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // 32 rows x (nfb * 32 * osz) bytes, 16 bytes per lane.
+    const int row_bytes = nfb * 32 * osz;
+    const int lpr = row_bytes / 16;                  // lanes per row
+    const int rows_per_it = 64 / lpr;
+    for (int r0 = 0; r0 < 32; r0 += rows_per_it) {
+      const int r = r0 + lane / lpr;
+      const int c16 = lane % lpr;
+      if (r < 32 && (uint32_t)(wave * 32 + r) < n) {
+        const long orow = out_row(jd, tok0 + r);
+        if (orow >= 0) {
+          const uint4 v = *(const uint4*)(wout + (size_t)r * kOutRow + c16 * 16);
+          *(uint4*)((uint8_t*)jd.dst + ((size_t)orow * F + (size_t)fg * 32) * osz + c16 * 16) = v;
         } else {
-          const uint32_t p0 = bf16_bits_rne(o0) | (bf16_bits_rne(o1) << 16);
-          const uint32_t p1 = bf16_bits_rne(o2) | (bf16_bits_rne(o3) << 16);
-          *(uint2*)((uint16_t*)jd.dst + (size_t)orow * F + f) = make_uint2(p0, p1);
+          *bad = 1;
         }
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
+
+// LDS layout of a decode tile: [records (fused only) | output staging | mean].
+__host__ __device__ inline size_t dec_out_off(size_t rec_bytes) { return align_up(rec_bytes + 16, 16); }
 
 template <int KMAX, int G>
 __global__ __launch_bounds__(kThreads) void decode_kernel(const LaunchArgs a) {
@@ -527,7 +654,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const LaunchArgs a) {
   if (threadIdx.x == 0) flag = check_header(a, jd, sl);
   __syncthreads();
   const int st = flag;
-  if (lt == 0 && threadIdx.x == 0 && st != KVTC_OK) a.status[j] = st;
+  if (lt == 0 && threadIdx.x == 0) set_status(a, j, st);
   if (st != KVTC_OK) return;
   __syncthreads();
   if (threadIdx.x == 0) flag = 0;
@@ -541,13 +668,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const LaunchArgs a) {
     const int esz = a.dtype == KVTC_F32 ? 4 : 2;
     const uint8_t* recs = (const uint8_t*)jd.src + record_base(jd, a.F, esz) +
                           (size_t)t0 * sl.record_bytes;
+    // Records and output staging share one region (records are consumed
+    // before the first output row is staged); the mean follows it.
+    const size_t region = max(align_up((size_t)kDecTile * sl.record_bytes + 16, 16),
+                              (size_t)4 * 32 * kOutRow);
+    float* mu_l = (float*)(smem + region);
+    {
+      const float4* mu = (const float4*)(a.state + sl.mu_off);
+      for (int i = threadIdx.x; i < a.F / 4; i += kThreads) ((float4*)mu_l)[i] = mu[i];
+    }
     stage_to_lds(smem, recs, (size_t)n * sl.record_bytes);
     __syncthreads();
-    restore_tile<KMAX, G, false>(a, jd, sl, smem, t0, n, &bad);
+    restore_tile<KMAX, G, false>(a, jd, sl, smem, smem, mu_l, t0, n, &bad);
   }
   if (bad) atomicExch(&flag, 1);
   __syncthreads();
-  if (threadIdx.x == 0 && flag) atomicExch(&a.status[j], KVTC_E_INVALID);
+  if (threadIdx.x == 0 && flag) set_status(a, j, KVTC_E_INVALID);
 }
 
 // Stage 1: header check, passthrough rows, records -> staging codes/scales.
@@ -564,7 +700,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const LaunchArgs a) {
   if (threadIdx.x == 0) flag = check_header(a, jd, sl);
   __syncthreads();
   const int st = flag;
-  if (lt == 0 && threadIdx.x == 0 && st != KVTC_OK) a.status[j] = st;
+  if (lt == 0 && threadIdx.x == 0) set_status(a, j, st);
   if (st != KVTC_OK) return;
   __syncthreads();
   if (threadIdx.x == 0) flag = 0;
@@ -590,7 +726,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const LaunchArgs a) {
       const int ag = c / G, o = c % G;
       *(uint64_t*)(st8 + (size_t)(t0 + tl) * sl.r_eff + c) = get_codes8(rec, sl, ag, o);
       if (o == 0) {
-        const uint64_t raw = load_bytes(rec + 8 * ag, 8);
+        const uint64_t raw = lds_u64(rec + 8 * ag);
         ssg[(size_t)(t0 + tl) * sl.n_act + ag] =
             make_float2(__uint_as_float((uint32_t)raw), __uint_as_float((uint32_t)(raw >> 32)));
       }
@@ -598,12 +734,13 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const LaunchArgs a) {
   }
   if (bad) atomicExch(&flag, 1);
   __syncthreads();
-  if (threadIdx.x == 0 && flag) atomicExch(&a.status[j], KVTC_E_INVALID);
+  if (threadIdx.x == 0 && flag) set_status(a, j, KVTC_E_INVALID);
 }
 
 // Stage 2: staging -> compressed output rows.
 template <int KMAX, int G>
 __global__ __launch_bounds__(kThreads) void restore_kernel(const LaunchArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int flag;
   const uint32_t tile = logical_tile();
   if (tile >= a.total_tiles) return;
@@ -611,16 +748,22 @@ __global__ __launch_bounds__(kThreads) void restore_kernel(const LaunchArgs a) {
   const JobDesc& jd = a.jobs[j];
   const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
   const uint32_t lt = tile - jd.tile_begin;
-  if (a.status[j] != KVTC_OK || lt >= jd.n_ctiles) return;
+  if (prior_rank(a, j) != 0 || lt >= jd.n_ctiles) return;  // stage 1 rejected the stream
   if (threadIdx.x == 0) flag = 0;
   __syncthreads();
   int bad = 0;
   const uint32_t t0 = lt * kDecTile;
   const uint32_t n = min((uint32_t)kDecTile, jd.tc - t0);
-  restore_tile<KMAX, G, true>(a, jd, sl, nullptr, t0, n, &bad);
+  float* mu_l = (float*)(smem + (size_t)4 * 32 * kOutRow);
+  {
+    const float4* mu = (const float4*)(a.state + sl.mu_off);
+    for (int i = threadIdx.x; i < a.F / 4; i += kThreads) ((float4*)mu_l)[i] = mu[i];
+  }
+  __syncthreads();
+  restore_tile<KMAX, G, true>(a, jd, sl, nullptr, smem, mu_l, t0, n, &bad);
   if (bad) atomicExch(&flag, 1);
   __syncthreads();
-  if (threadIdx.x == 0 && flag) atomicExch(&a.status[j], KVTC_E_INVALID);
+  if (threadIdx.x == 0 && flag) set_status(a, j, KVTC_E_INVALID);
 }
 
 // Test hook: stream from given codes and (shift, scale) pairs, through the
@@ -638,7 +781,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const LaunchArgs a, cons
   const size_t row_bytes = (size_t)a.F * esz;
   if (lt == 0 && threadIdx.x == 0) {
     write_header(a, jd, sl);
-    a.status[0] = KVTC_OK;
+    set_status(a, 0, KVTC_OK);
   }
   if (lt >= jd.n_ctiles) {
     encode_passthrough(jd, lt - jd.n_ctiles, row_bytes);
@@ -664,21 +807,24 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const LaunchArgs a, cons
   lds_to_global((uint8_t*)jd.dst + record_base(jd, a.F, esz) + (size_t)t0 * rb, smem, (size_t)n * rb);
 }
 
-// Status words start at KVTC_OK; tiles only ever write errors into them.
-__global__ void reset_status(int32_t* status, int n) {
-  if ((int)threadIdx.x < n) status[threadIdx.x] = KVTC_OK;
-}
-
 // ------------------------------------------------------------- launchers ---
 
 static dim3 grid_for(uint32_t tiles) { return dim3((tiles + 7u) / 8u * 8u); }
 
-template <int G>
+// Dynamic LDS above the 64 KiB default needs an explicit opt-in (gfx950 has
+// 160 KiB per CU).
+template <class K>
+static void allow_lds(K kernel, size_t lds) {
+  if (lds > 65536) hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+template <int G, bool F32IN>
 static int launch_encode_g(const LaunchArgs& a, int nb, size_t lds, hipStream_t s) {
   const dim3 g = grid_for(a.total_tiles);
 #define KVTC_ENC(NBV)                                                                  \
   case NBV:                                                                            \
-    hipLaunchKernelGGL((encode_kernel<NBV, G>), g, dim3(kThreads), lds, s, a); \
+    allow_lds(encode_kernel<NBV, G, F32IN>, lds);                                      \
+    hipLaunchKernelGGL((encode_kernel<NBV, G, F32IN>), g, dim3(kThreads), lds, s, a);  \
     break;
   switch (nb) {
     KVTC_ENC(1) KVTC_ENC(2) KVTC_ENC(3) KVTC_ENC(4) KVTC_ENC(5) KVTC_ENC(6) KVTC_ENC(7) KVTC_ENC(8)
@@ -690,21 +836,24 @@ static int launch_encode_g(const LaunchArgs& a, int nb, size_t lds, hipStream_t 
 }
 
 int launch_encode(const LaunchArgs& a, int nb_max, int G, size_t lds, hipStream_t s) {
-  if (G == 16) return launch_encode_g<16>(a, nb_max, lds, s);
-  if (G == 32) return launch_encode_g<32>(a, nb_max, lds, s);
+  const bool f32 = a.dtype == KVTC_F32;
+  if (G == 16) return f32 ? launch_encode_g<16, true>(a, nb_max, lds, s) : launch_encode_g<16, false>(a, nb_max, lds, s);
+  if (G == 32) return f32 ? launch_encode_g<32, true>(a, nb_max, lds, s) : launch_encode_g<32, false>(a, nb_max, lds, s);
   return (int)hipErrorInvalidValue;
 }
 
 template <int G>
 static int launch_decode_g(const LaunchArgs& a, int kmax, size_t lds, bool staged, hipStream_t s) {
   const dim3 g = grid_for(a.total_tiles);
-  if (!staged) hipLaunchKernelGGL(reset_status, dim3(1), dim3(kMaxLaunchJobs), 0, s, a.status, a.n_jobs);
 #define KVTC_DEC(KV)                                                                            \
   if (kmax <= KV) {                                                                             \
-    if (staged)                                                                                 \
-      hipLaunchKernelGGL((restore_kernel<KV, G>), g, dim3(kThreads), 0, s, a);                 \
-    else                                                                                        \
+    if (staged) {                                                                               \
+      allow_lds(restore_kernel<KV, G>, lds);                                                    \
+      hipLaunchKernelGGL((restore_kernel<KV, G>), g, dim3(kThreads), lds, s, a);               \
+    } else {                                                                                    \
+      allow_lds(decode_kernel<KV, G>, lds);                                                     \
       hipLaunchKernelGGL((decode_kernel<KV, G>), g, dim3(kThreads), lds, s, a);                \
+    }                                                                                           \
     return (int)hipGetLastError();                                                             \
   }
   KVTC_DEC(2) KVTC_DEC(4) KVTC_DEC(6) KVTC_DEC(8) KVTC_DEC(12) KVTC_DEC(16)
@@ -719,18 +868,21 @@ int launch_decode(const LaunchArgs& a, int kmax, int G, size_t lds, hipStream_t 
 }
 
 int launch_restore(const LaunchArgs& a, int kmax, int G, hipStream_t s) {
-  if (G == 16) return launch_decode_g<16>(a, kmax, 0, true, s);
-  if (G == 32) return launch_decode_g<32>(a, kmax, 0, true, s);
+  const size_t lds = (size_t)4 * 32 * kOutRow + (size_t)a.F * 4;
+  if (G == 16) return launch_decode_g<16>(a, kmax, lds, true, s);
+  if (G == 32) return launch_decode_g<32>(a, kmax, lds, true, s);
   return (int)hipErrorInvalidValue;
 }
 
 int launch_unpack(const LaunchArgs& a, int G, size_t lds, hipStream_t s) {
   const dim3 g = grid_for(a.total_tiles);
-  hipLaunchKernelGGL(reset_status, dim3(1), dim3(kMaxLaunchJobs), 0, s, a.status, a.n_jobs);
-  if (G == 16)
+  if (G == 16) {
+    allow_lds(unpack_kernel<16>, lds);
     hipLaunchKernelGGL((unpack_kernel<16>), g, dim3(kThreads), lds, s, a);
-  else if (G == 32)
+  } else if (G == 32) {
+    allow_lds(unpack_kernel<32>, lds);
     hipLaunchKernelGGL((unpack_kernel<32>), g, dim3(kThreads), lds, s, a);
+  }
   else
     return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();

@@ -350,3 +350,58 @@ def test_full_size_launch_llama8b():
         g = bf16_out_to_f64(out[:T])
         M = np.abs(full).max()
         assert np.all(np.abs(g - full) <= DEC_TOL * M + 2.0 ** -8 * np.abs(full))
+
+
+def test_two_stream_layer_pipeline_matches_fused():
+    """Layer-by-layer decode on two streams (stage 1 of layer l+1 overlapping
+    stage 2 of layer l, two alternating staging buffers and workspaces) gives
+    exactly the fused decode's paged output."""
+    w, art, op, items = _setup("qwen25_7b_paged")
+    dc = DevCodec(art.serialize())
+    T = items[0][2].shape[0]
+    bs = w.block_size
+    per_req = (T + bs - 1) // bs
+    rng = np.random.default_rng(5)
+    layers = sorted({l for l, _, _, _ in items})
+    pool_blocks = per_req * len(items)
+    srcs, jobs_by_layer, outs_f, outs_p = [], {l: [] for l in layers}, [], []
+    perm = rng.permutation(pool_blocks).astype(np.int32)
+    tables = []
+    for i, (l, k, store, ref) in enumerate(items):
+        src = to_dev_bytes(ref.stream, 16)
+        srcs.append(src)
+        tables.append(torch.from_numpy(perm[i * per_req:(i + 1) * per_req].copy()).to(DEV))
+    pool_f = torch.full((pool_blocks * bs, op.F), -7, dtype=torch.int16, device=DEV)
+    pool_p = torch.full_like(pool_f, -7)
+    nbytes = pool_f.numel() * 2
+    fused_jobs, pipe_jobs = [], {l: [] for l in layers}
+    for i, (l, k, store, ref) in enumerate(items):
+        fused_jobs.append(K.make_job(l, k, T, srcs[i], pool_f, nbytes, tables[i], bs, pool_blocks))
+        pipe_jobs[l].append(K.make_job(l, k, T, srcs[i], pool_p, nbytes, tables[i], bs, pool_blocks))
+    s = torch.cuda.current_stream()
+    dc.codec.decode(fused_jobs, K.KVTC_BF16, dc.ws, s)
+    assert np.all(dc.status(len(fused_jobs)) == 0)
+    nst = max(dc.codec.staging_bytes(js) for js in pipe_jobs.values())
+    stg = [torch.zeros(nst, dtype=torch.uint8, device=DEV) for _ in range(2)]
+    wss = [torch.zeros(64, dtype=torch.int32, device=DEV) for _ in range(2)]
+    su, sr = torch.cuda.Stream(), torch.cuda.Stream()
+    ev_u = [torch.cuda.Event() for _ in layers]
+    ev_r = [torch.cuda.Event() for _ in layers]
+    start = torch.cuda.Event()
+    start.record(s)
+    su.wait_event(start)
+    sr.wait_event(start)
+    for idx, l in enumerate(layers):
+        b = idx % 2
+        if idx >= 2:
+            su.wait_event(ev_r[idx - 2])
+        dc.codec.decode_unpack(pipe_jobs[l], K.KVTC_BF16, stg[b], nst, wss[b], su)
+        ev_u[idx].record(su)
+        sr.wait_event(ev_u[idx])
+        dc.codec.decode_restore(pipe_jobs[l], K.KVTC_BF16, stg[b], nst, wss[b], sr)
+        ev_r[idx].record(sr)
+    torch.cuda.synchronize()
+    for b in range(2):
+        assert np.all(K.kvtc_read_device_status(wss[b], len(pipe_jobs[layers[0]]), s) == 0)
+    assert torch.equal(pool_f, pool_p)
+    assert not torch.any(pool_f == -7)   # every block of the pool was written
