@@ -598,10 +598,13 @@ uint32_t next_epoch() {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Validate jobs [0, n) on the host and fill LaunchArgs batches.
+// Validate jobs [0, n) on the host and fill LaunchArgs batches. Jobs are
+// grouped (stably) by the kernel shape they need (encode: r_enc / 32,
+// decode and restore: r_dec / 16) and cut into batches of at most
+// kMaxLaunchJobs; each job keeps its own status word (its index in `jobs`).
 kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_dtype, void* d_ws,
                  uint8_t* d_staging, size_t staging_bytes, std::vector<LaunchArgs>& batches,
-                 std::vector<int>& kmax, std::vector<size_t>& lds) {
+                 std::vector<int>& shape, std::vector<size_t>& lds) {
   if (!c || !jobs || n <= 0 || n > KVTC_MAX_JOBS) return fail(KVTC_E_INVALID, "bad codec, jobs or job count");
   if (!d_ws || !aligned16(d_ws)) return fail(KVTC_E_INVALID, "workspace must be non-null and aligned");
   if (!c->d_state || c->uploaded_version != c->calib_version)
@@ -609,90 +612,101 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
   if (mode != Mode::Encode && mode != Mode::Pack && out_dtype != KVTC_F32 && out_dtype != KVTC_BF16)
     return fail(KVTC_E_INVALID, "bad output dtype");
   const int F = c->F;
-  const size_t in_esz = elem_bytes(c->p.dtype);
   const size_t out_esz = elem_bytes(out_dtype);
-  size_t st_off = 0;
-  for (int b0 = 0; b0 < n; b0 += kMaxLaunchJobs) {
+  // Per-job validation and the fields that do not depend on the batch.
+  std::vector<JobDesc> desc(n);
+  std::vector<int> key(n);
+  std::vector<size_t> st_off(n, 0);
+  size_t st_total = 0;
+  for (int i = 0; i < n; ++i) {
+    const kvtc_job& j = jobs[i];
+    int idx;
+    if (!slot_index(c, j.layer, j.kind, &idx)) return fail(KVTC_E_INVALID, "job: bad layer or kind");
+    const Slot& s = c->slots[idx];
+    if (!s.calibrated) return fail(KVTC_E_NOT_CALIBRATED, "job: (layer, kind) is not calibrated");
+    if (j.n_tokens < 0 || j.n_tokens > (int64_t)INT32_MAX) return fail(KVTC_E_INVALID, "job: bad n_tokens");
+    if (!j.dst || !aligned16(j.dst)) return fail(KVTC_E_INVALID, "job: dst must be non-null and 16-byte aligned");
+    if (!j.src || !aligned16(j.src)) return fail(KVTC_E_INVALID, "job: src must be non-null and 16-byte aligned");
+    JobDesc& d = desc[i];
+    std::memset(&d, 0, sizeof(d));
+    d.src = j.src;
+    d.dst = j.dst;
+    d.T = (uint32_t)j.n_tokens;
+    split_rows(j.n_tokens, c->p, &d.s1, &d.w1, &d.tc);
+    d.slot = idx;
+    d.layer = j.layer;
+    d.kind = j.kind;
+    d.status_idx = i;
+    if (mode == Mode::Encode || mode == Mode::Pack) {
+      if (j.dst_capacity < stream_bytes(c, s, j.n_tokens))
+        return fail(KVTC_E_CAPACITY, "job: dst_capacity below kvtc_encoded_bytes");
+      key[i] = std::max<int>(1, (int)(align_up((size_t)s.r_eff, 32) / 32));
+    } else {
+      if (j.block_table) {
+        if (j.block_size <= 0 || j.n_blocks <= 0) return fail(KVTC_E_INVALID, "job: bad paging");
+        if ((size_t)j.n_blocks * j.block_size * F * out_esz > j.dst_capacity)
+          return fail(KVTC_E_CAPACITY, "job: paged dst smaller than n_blocks * block_size rows");
+        d.block_table = j.block_table;
+        d.block_size = j.block_size;
+        d.n_blocks = j.n_blocks;
+      } else if ((size_t)j.n_tokens * F * out_esz > j.dst_capacity) {
+        return fail(KVTC_E_CAPACITY, "job: dst smaller than n_tokens rows");
+      }
+      if (mode == Mode::Unpack || mode == Mode::Restore) {
+        st_off[i] = st_total;
+        st_total += job_staging_bytes(s, d.tc);
+        if (!d_staging || st_total > staging_bytes) return fail(KVTC_E_CAPACITY, "staging buffer too small");
+        d.staging = d_staging + st_off[i];
+      }
+      key[i] = mode == Mode::Unpack ? 0 : (int)(align_up((size_t)s.r_eff, 16) / 16);
+    }
+  }
+  std::vector<int> order(n);
+  for (int i = 0; i < n; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return key[x] < key[y]; });
+  for (int p = 0; p < n;) {
+    int q = p;
+    while (q < n && q - p < kMaxLaunchJobs && key[order[q]] == key[order[p]]) ++q;
     LaunchArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.n_jobs = std::min(kMaxLaunchJobs, n - b0);
+    a.n_jobs = q - p;
     a.dtype = c->p.dtype;
     a.out_dtype = out_dtype;
     a.F = F;
     a.state = c->d_state;
-    a.status = (unsigned long long*)d_ws + b0;
+    a.status = (unsigned long long*)d_ws;
     a.epoch = next_epoch();
     uint32_t tiles = 0;
-    int km = 0;
-    size_t rb_max = 0, r_enc_max = 0;
-    for (int i = 0; i < a.n_jobs; ++i) {
-      const kvtc_job& j = jobs[b0 + i];
-      int idx;
-      if (!slot_index(c, j.layer, j.kind, &idx)) return fail(KVTC_E_INVALID, "job: bad layer or kind");
-      const Slot& s = c->slots[idx];
-      if (!s.calibrated) return fail(KVTC_E_NOT_CALIBRATED, "job: (layer, kind) is not calibrated");
-      if (j.n_tokens < 0 || j.n_tokens > (int64_t)INT32_MAX) return fail(KVTC_E_INVALID, "job: bad n_tokens");
-      if (!j.dst || !aligned16(j.dst)) return fail(KVTC_E_INVALID, "job: dst must be non-null and 16-byte aligned");
-      if (!j.src || !aligned16(j.src)) return fail(KVTC_E_INVALID, "job: src must be non-null and 16-byte aligned");
-      JobDesc& d = a.jobs[i];
-      d.src = j.src;
-      d.dst = j.dst;
-      d.T = (uint32_t)j.n_tokens;
-      split_rows(j.n_tokens, c->p, &d.s1, &d.w1, &d.tc);
-      d.slot = idx;
-      d.layer = j.layer;
-      d.kind = j.kind;
+    size_t rb_max = 0;
+    for (int b = 0; b < a.n_jobs; ++b) {
+      JobDesc d = desc[order[p + b]];
+      const Slot& s = c->slots[d.slot];
       const uint32_t ptiles = (d.s1 + d.w1 + kPassRows - 1) / kPassRows;
-      if (mode == Mode::Encode || mode == Mode::Pack) {
-        if (j.dst_capacity < stream_bytes(c, s, j.n_tokens))
-          return fail(KVTC_E_CAPACITY, "job: dst_capacity below kvtc_encoded_bytes");
-        d.n_ctiles = (d.tc + kEncTile - 1) / kEncTile;
-        d.tile_begin = tiles;
-        tiles += std::max<uint32_t>(1, d.n_ctiles + ptiles);
-      } else {
-        if (j.block_table) {
-          if (j.block_size <= 0 || j.n_blocks <= 0) return fail(KVTC_E_INVALID, "job: bad paging");
-          if ((size_t)j.n_blocks * j.block_size * F * out_esz > j.dst_capacity)
-            return fail(KVTC_E_CAPACITY, "job: paged dst smaller than n_blocks * block_size rows");
-          d.block_table = j.block_table;
-          d.block_size = j.block_size;
-          d.n_blocks = j.n_blocks;
-        } else if ((size_t)j.n_tokens * F * out_esz > j.dst_capacity) {
-          return fail(KVTC_E_CAPACITY, "job: dst smaller than n_tokens rows");
-        }
-        if (mode == Mode::Unpack || mode == Mode::Restore) {
-          d.staging = d_staging + st_off;
-          st_off += job_staging_bytes(s, d.tc);
-          if (!d_staging || st_off > staging_bytes) return fail(KVTC_E_CAPACITY, "staging buffer too small");
-        }
-        const int tile = mode == Mode::Unpack ? kUnpackTile : kDecTile;
-        d.n_ctiles = (d.tc + tile - 1) / tile;
-        d.tile_begin = tiles;
-        if (mode == Mode::Restore)
-          tiles += d.n_ctiles;
-        else
-          tiles += std::max<uint32_t>(1, d.n_ctiles + ptiles);
-      }
+      const int tile = mode == Mode::Encode || mode == Mode::Pack ? kEncTile
+                       : mode == Mode::Unpack                     ? kUnpackTile
+                                                                  : kDecTile;
+      d.n_ctiles = (d.tc + tile - 1) / tile;
+      d.tile_begin = tiles;
+      tiles += mode == Mode::Restore ? d.n_ctiles : std::max<uint32_t>(1, d.n_ctiles + ptiles);
+      a.jobs[b] = d;
       rb_max = std::max(rb_max, (size_t)s.record_bytes);
-      r_enc_max = std::max(r_enc_max, align_up((size_t)s.r_eff, 32));
-      km = std::max(km, (int)(align_up((size_t)s.r_eff, 16) / 16));
     }
-    (void)in_esz;
     a.total_tiles = tiles;
+    const int k = key[order[p]];
     size_t l = 16;
     if (mode == Mode::Encode)
-      l = std::max({l, 2 * std::max<size_t>(r_enc_max, 32) * kEncRowPad * 2 + (size_t)F * 4,
-                    (size_t)kEncTile * rb_max});
+      l = std::max({l, 2 * (size_t)32 * k * kEncRowPad * 2 + (size_t)F * 4, (size_t)kEncTile * rb_max});
     else if (mode == Mode::Pack)
       l = std::max(l, (size_t)kEncTile * rb_max);
-    else if (mode == Mode::Decode)
-      l = std::max(align_up((size_t)kDecTile * rb_max + 16, 16), (size_t)4 * 32 * kOutRow) + (size_t)F * 4;
     else if (mode == Mode::Unpack)
       l = std::max(l, (size_t)kUnpackTile * rb_max + 16);
-    if (l > 160 * 1024) return fail(KVTC_E_UNSUPPORTED, "records too large for one tile's LDS");
+    else
+      l = decode_lds_bytes(16 * k, F);
+    if (l > 160 * 1024) return fail(KVTC_E_UNSUPPORTED, "tile does not fit in LDS");
     batches.push_back(a);
-    kmax.push_back(mode == Mode::Encode ? (int)(r_enc_max / 32) : km);
+    shape.push_back(k);
     lds.push_back(l);
+    p = q;
   }
   return KVTC_OK;
 }
@@ -715,7 +729,7 @@ kvtc_status kvtc_encode(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, voi
   if (st != KVTC_OK) return st;
   for (size_t i = 0; i < b.size(); ++i) {
     if (b[i].total_tiles == 0) continue;
-    st = hip_status(launch_encode(b[i], std::max(k[i], 1), c->p.group, l[i], stream), "encode launch");
+    st = hip_status(launch_encode(b[i], k[i], c->p.group, l[i], stream), "encode launch");
     if (st != KVTC_OK) return st;
   }
   return KVTC_OK;
@@ -730,7 +744,7 @@ kvtc_status kvtc_decode(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, int
   if (st != KVTC_OK) return st;
   for (size_t i = 0; i < b.size(); ++i) {
     if (b[i].total_tiles == 0) continue;
-    st = hip_status(launch_decode(b[i], std::max(k[i], 1), c->p.group, l[i], stream), "decode launch");
+    st = hip_status(launch_decode(b[i], k[i], l[i], stream), "decode launch");
     if (st != KVTC_OK) return st;
   }
   return KVTC_OK;
@@ -763,7 +777,7 @@ kvtc_status kvtc_decode_restore(kvtc_codec* c, const kvtc_job* jobs, int32_t n_j
   if (st != KVTC_OK) return st;
   for (size_t i = 0; i < b.size(); ++i) {
     if (b[i].total_tiles == 0) continue;
-    st = hip_status(launch_restore(b[i], std::max(k[i], 1), c->p.group, stream), "restore launch");
+    st = hip_status(launch_restore(b[i], k[i], l[i], stream), "restore launch");
     if (st != KVTC_OK) return st;
   }
   return KVTC_OK;

@@ -58,7 +58,7 @@ struct JobDesc {
   int32_t kind;
   int32_t block_size;      // paged output when block_table != nullptr
   int32_t n_blocks;
-  int32_t pad;
+  int32_t status_idx;      // this job's word in LaunchArgs::status
 };
 
 struct LaunchArgs {
@@ -96,12 +96,15 @@ constexpr int kEncRowPad = kEncKS + 8;     // bf16 elements per LDS basis row
 constexpr int kOutRow = 128 + 16;          // bytes per LDS output-staging row (decode)
 
 // Host-side launchers implemented in kvtc_kernels.hip (G = group size, lds =
-// dynamic LDS bytes). They return a hipError_t value cast to int.
-int launch_encode(const LaunchArgs& a, int nb_max, int G, size_t lds, hipStream_t s);
-int launch_decode(const LaunchArgs& a, int kmax, int G, size_t lds, hipStream_t s);
+// dynamic LDS bytes). Every job of one launch has the same shape parameter:
+// nb = r_enc / 32 for encode, ks = r_dec / 16 for decode and restore. They
+// return a hipError_t value cast to int.
+int launch_encode(const LaunchArgs& a, int nb, int G, size_t lds, hipStream_t s);
+int launch_decode(const LaunchArgs& a, int ks, size_t lds, hipStream_t s);
 int launch_unpack(const LaunchArgs& a, int G, size_t lds, hipStream_t s);
-int launch_restore(const LaunchArgs& a, int kmax, int G, hipStream_t s);
+int launch_restore(const LaunchArgs& a, int ks, size_t lds, hipStream_t s);
 int launch_pack(const LaunchArgs& a, int G, size_t lds, const void* codes, const void* ss,
                 hipStream_t s);
+size_t decode_lds_bytes(int r_dec, int F);
 
 }  // namespace kvtc

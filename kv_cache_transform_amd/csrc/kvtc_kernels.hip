@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
   const size_t row_bytes = (size_t)F * esz;
   if (lt == 0 && threadIdx.x == 0) {
     write_header(a, jd, sl);
-    set_status(a, j, KVTC_OK);
+    set_status(a, jd.status_idx, KVTC_OK);
   }
   if (lt >= jd.n_ctiles) {
     encode_passthrough(jd, lt - jd.n_ctiles, row_bytes);
@@ -301,7 +301,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
   const bool tok_ok = (uint32_t)tl < n;
   const uint8_t* xrow = (const uint8_t*)jd.src + (size_t)(jd.s1 + t0 + (tok_ok ? tl : 0)) * row_bytes;
   const uint16_t* venc = (const uint16_t*)(a.state + sl.venc_off);
-  const int nb = sl.r_enc / 32;
 
   // LDS: two basis K-slices [32 * NB][kEncRowPad] bf16, then the mean (F fp32).
   constexpr int slice_elems = 32 * NB * kEncRowPad;
@@ -392,11 +391,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
       const bf16x8 bx = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        if (b < nb) {
-          const uint4 av = *(const uint4*)(vs + (b * 32 + (lane & 31)) * kEncRowPad + 16 * s + 8 * h);
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bx,
-                                                           acc[b], 0, 0, 0);
-        }
+        const uint4 av = *(const uint4*)(vs + (b * 32 + (lane & 31)) * kEncRowPad + 16 * s + 8 * h);
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bx,
+                                                         acc[b], 0, 0, 0);
       }
     }
     if (more) {
@@ -419,7 +416,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
 #pragma unroll
     for (int sg = 0; sg < SUB; ++sg) {
       const int ag = b * SUB + sg;
-      if (b < nb && ag < sl.n_act) {
+      if (ag < sl.n_act) {
         float v[G / 2];
 #pragma unroll
         for (int i = 0; i < G / 2; ++i) v[i] = acc[b][(G / 2) * sg + i];
@@ -484,8 +481,9 @@ __device__ __forceinline__ void token_scale(float m, float& S, float& Sinv) {
   Sinv = __uint_as_float((uint32_t)(127 + 14 - e) << 23);
 }
 
-// Build the fp16 B fragment of K step s (components [16s + 8h, +8)).
-__device__ __forceinline__ f16x8 make_frag(uint64_t codes8, float shift, float scale, int w,
+// Dequantize 8 codes (one byte each in codes8) of a group of width w and
+// scale them by Sinv into packed fp16: c_hat = fma(q, fp32(scale / k), shift).
+__device__ __forceinline__ uint4 make_frag(uint64_t codes8, float shift, float scale, int w,
                                            float Sinv) {
   const float k = (float)((1 << w) - 1);
   const float step = scale / k;
@@ -496,152 +494,219 @@ __device__ __forceinline__ f16x8 make_frag(uint64_t codes8, float shift, float s
     const float q1 = (float)((codes8 >> (16 * j + 8)) & 0xFFu);
     pk[j] = pack_f16x2(__builtin_fmaf(q0, step, shift) * Sinv, __builtin_fmaf(q1, step, shift) * Sinv);
   }
-  return __builtin_bit_cast(f16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+  return make_uint4(pk[0], pk[1], pk[2], pk[3]);
 }
 
-// Restore the compressed rows of one tile. FROM_STAGING selects the code
-// source: LDS-staged records (fused decode) or the stage-1 staging buffer.
-// Each wave owns 32 tokens. The basis fragments of the next 32-feature block
-// are loaded while the current block runs on the MFMA; the result (lane =
-// token, 16 features) goes through a wave-private LDS area so that the global
-// stores are 16-byte lanes over whole 128-byte row segments.
-// LDS: lds_out = 4 waves x 32 rows x kOutRow bytes, mu_l = F floats.
-template <int KMAX, int G, bool FROM_STAGING>
+// 8 bytes from global memory at any byte address p inside [., end): three
+// aligned dword loads and two byte-aligns, or byte loads near the end so that
+// nothing past `end` is touched.
+__device__ __forceinline__ uint64_t gl_u64(const uint8_t* p, const uint8_t* end) {
+  const uintptr_t a = (uintptr_t)p;
+  if (p + 12 <= end) {
+    const uint32_t* b = (const uint32_t*)(a & ~(uintptr_t)3);
+    const uint32_t sh = (uint32_t)(a & 3u);
+    const uint32_t w0 = b[0], w1 = b[1], w2 = b[2];
+    return (uint64_t)__builtin_amdgcn_alignbyte(w1, w0, sh) |
+           ((uint64_t)__builtin_amdgcn_alignbyte(w2, w1, sh) << 32);
+  }
+  uint64_t v = 0;
+  for (int i = 0; i < 8 && p + i < end; ++i) v |= (uint64_t)p[i] << (8 * i);
+  return v;
+}
+
+// Unpack the 8 codes of components [o, o + 8) of active group a from packed
+// bits (LSB first), one byte per code.
+__device__ __forceinline__ uint64_t spread_codes8(uint64_t bits, int w) {
+  const uint64_t mask = (1ull << w) - 1ull;
+  uint64_t out = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) out |= ((bits >> (j * w)) & mask) << (8 * j);
+  return out;
+}
+
+constexpr int kChatPad = 16;  // bytes of padding per LDS c_hat row
+
+// LDS bytes of a decode tile: the c_hat rows (reused for output staging),
+// the per-token scale words and the mean.
+__host__ __device__ inline size_t dec_lds_bytes(int r_dec, int F) {
+  const size_t chat = (size_t)kDecTile * (2 * r_dec + kChatPad);
+  const size_t outs = (size_t)4 * 32 * kOutRow;
+  return align_up(chat > outs ? chat : outs, 16) + 4 * kDecTile + 4 * (size_t)F;
+}
+
+// Compressed rows of one tile (128 tokens; wave w owns tokens 32w..32w+31).
+//  1. the mean goes to LDS; per token the scale S_t is the power of two
+//     above max |c_hat| (LDS atomicMax over its groups);
+//  2. cooperative dequantization: one thread per (token, 8 components)
+//     writes c_hat / S_t as fp16 into LDS; codes come straight from the
+//     stream's records (fused) or the staging buffer (two-stage);
+//  3. each lane loads its token's KS B fragments from LDS;
+//  4. per 32-feature block, KS MFMAs D[feature][token] = V' c_hat^T with the
+//     basis fragments of the next block already in flight (two register
+//     sets, no copies), then S_t * D + mu, staged through LDS so that stores
+//     are 16-byte lanes over 128-byte row segments.
+template <int KS, bool OUT32, bool STAGED>
 __device__ void restore_tile(const LaunchArgs& a, const JobDesc& jd, const DevSlot& sl,
-                             const uint8_t* lds_rec, uint8_t* lds_out, const float* mu_l,
-                             uint32_t t0, uint32_t n, int* bad) {
+                             uint8_t* smem, uint32_t t0, uint32_t n, int* bad) {
   const int F = a.F;
+  const int r_eff = sl.r_eff, r_dec = sl.r_dec, n_act = sl.n_act, G = sl.G;
+  const int rb = sl.record_bytes;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5;
   const int tl = wave * 32 + (lane & 31);
-  const bool tok_ok = (uint32_t)tl < n;
-  const int tt = tok_ok ? tl : 0;
-  const uint16_t* vdec = (const uint16_t*)(a.state + sl.vdec_off);
-  const int ks = sl.r_dec / 16;
+  const size_t chat_stride = 2 * (size_t)r_dec + kChatPad;
+  const size_t chat_bytes = align_up(max((size_t)kDecTile * chat_stride, (size_t)4 * 32 * kOutRow), 16);
+  uint8_t* chat = smem;
+  uint32_t* sbits = (uint32_t*)(smem + chat_bytes);
+  float* mu_l = (float*)(sbits + kDecTile);
+  const float4* mu_g = (const float4*)(a.state + sl.mu_off);
+  for (int i = threadIdx.x; i < F / 4; i += kThreads) ((float4*)mu_l)[i] = mu_g[i];
+  if (threadIdx.x < kDecTile) sbits[threadIdx.x] = 0u;
 
-  const uint8_t* rec = nullptr;
+  // Code sources.
+  const int esz = a.dtype == KVTC_F32 ? 4 : 2;
+  const uint8_t* recs = nullptr;
+  const uint8_t* rec_end = nullptr;
   const uint8_t* scodes = nullptr;
-  const float2* ssp = nullptr;
-  if (FROM_STAGING) {
+  const float2* sss = nullptr;
+  if (STAGED) {
     const uint8_t* st = (const uint8_t*)jd.staging;
-    scodes = st + (size_t)(t0 + tt) * sl.r_eff;
-    const size_t ss_off = align_up((size_t)jd.tc * sl.r_eff, kAlign);
-    ssp = (const float2*)(st + ss_off) + (size_t)(t0 + tt) * sl.n_act;
+    scodes = st + (size_t)t0 * r_eff;
+    sss = (const float2*)(st + align_up((size_t)jd.tc * r_eff, kAlign)) + (size_t)t0 * n_act;
   } else {
-    rec = lds_rec + (size_t)tt * sl.record_bytes;
+    const uint8_t* base = (const uint8_t*)jd.src + record_base(jd, F, esz);
+    recs = base + (size_t)t0 * rb;
+    rec_end = base + (size_t)jd.tc * rb;
   }
-  auto ss_of = [&](int g) -> float2 {
-    if (FROM_STAGING) return ssp[g];
-    const uint64_t raw = lds_u64(rec + 8 * g);
+  auto ss_of = [&](int t, int g) -> float2 {
+    if (STAGED) return sss[(size_t)t * n_act + g];
+    const uint64_t raw = gl_u64(recs + (size_t)t * rb + 8 * g, rec_end);
     return make_float2(__uint_as_float((uint32_t)raw), __uint_as_float((uint32_t)(raw >> 32)));
   };
-  float S, Sinv;
-  {
-    float m = 0.f;
-    for (int g = 0; g < sl.n_act; ++g) {
-      const float2 p = ss_of(g);
-      m = fmaxf(m, fmaxf(fabsf(p.x), fabsf(p.x + p.y)));
-    }
-    token_scale(m, S, Sinv);
-  }
-
-  f16x8 bfr[KMAX];
-#pragma unroll
-  for (int s = 0; s < KMAX; ++s) {
-    bfr[s] = __builtin_bit_cast(f16x8, make_uint4(0u, 0u, 0u, 0u));
-    const int c = 16 * s + 8 * h;
-    if (s < ks && c < sl.r_eff) {
-      const int ag = c / G, o = c % G;
-      uint64_t codes8;
-      if (FROM_STAGING)
-        codes8 = *(const uint64_t*)(scodes + c);
-      else
-        codes8 = get_codes8(rec, sl, ag, o);
-      const float2 p = ss_of(ag);
-      bfr[s] = make_frag(codes8, p.x, p.y, sl.width[ag], Sinv);
-    }
-  }
-  // The record area may be reused by the output staging from here on.
   __syncthreads();
-
-  const int osz = a.out_dtype == KVTC_F32 ? 4 : 2;
-  const int fpg = 128 / (32 * osz);                   // feature blocks per 128-byte group
-  uint8_t* wout = lds_out + (size_t)wave * 32 * kOutRow;
-  const uint32_t tok0 = jd.s1 + t0 + wave * 32;       // first token of this wave
-  const int nfb_all = F / 32;
-
-  uint4 cur[KMAX], nxt[KMAX];
-  auto load_a = [&](int fb, uint4* dst) {
-    const uint16_t* vrow = vdec + (size_t)(fb * 32 + (lane & 31)) * sl.r_dec + 8 * h;
+  // 1. per-token scales (max over groups; non-negative floats order as ints)
+  for (int i = threadIdx.x; i < (int)n * n_act; i += kThreads) {
+    const int t = i / n_act, g = i - t * n_act;
+    const float2 p = ss_of(t, g);
+    const float m = fmaxf(fabsf(p.x), fabsf(p.x + p.y));
+    atomicMax(&sbits[t], __float_as_uint(m));
+  }
+  __syncthreads();
+  // 2. c_hat / S_t in fp16, 8 components per item
+  const int c8n = r_dec / 8;
+  for (int i = threadIdx.x; i < (int)n * c8n; i += kThreads) {
+    const int t = i / c8n, c = (i - t * c8n) * 8;
+    uint4 frag = make_uint4(0u, 0u, 0u, 0u);
+    if (c < r_eff) {
+      float S, Sinv;
+      token_scale(__uint_as_float(sbits[t]), S, Sinv);
+      const int ag = c / G, o = c - ag * G;
+      const int w = sl.width[ag];
+      uint64_t codes8;
+      if (STAGED)
+        codes8 = *(const uint64_t*)(scodes + (size_t)t * r_eff + c);
+      else
+        codes8 = spread_codes8(gl_u64(recs + (size_t)t * rb + sl.chunk_off[ag] + (o * w) / 8, rec_end), w);
+      const float2 p = ss_of(t, ag);
+      frag = make_frag(codes8, p.x, p.y, w, Sinv);
+    }
+    *(uint4*)(chat + (size_t)t * chat_stride + 2 * c) = frag;
+  }
+  __syncthreads();
+  // 3. this lane's B fragments and token scale
+  uint4 bfr[KS > 0 ? KS : 1];
 #pragma unroll
-    for (int s = 0; s < KMAX; ++s)
-      if (s < ks) dst[s] = *(const uint4*)(vrow + 16 * s);
+  for (int s = 0; s < KS; ++s) bfr[s] = *(const uint4*)(chat + (size_t)tl * chat_stride + 2 * (16 * s + 8 * h));
+  float S, Sinv;
+  token_scale(__uint_as_float(sbits[tl]), S, Sinv);
+  __syncthreads();  // the c_hat region becomes the output staging area
+
+  // Store rows of this lane: row r = 8 * it + lane / 8 of the wave's 32
+  // tokens, 16 bytes at column (lane % 8) * 16 of a 128-byte segment.
+  constexpr int OSZ = OUT32 ? 4 : 2;
+  constexpr int FPG = 128 / (32 * OSZ);               // feature blocks per 128-byte segment
+  const int c16 = lane & 7;
+  long orow_off[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int r = 8 * it + (lane >> 3);
+    orow_off[it] = -1;
+    if ((uint32_t)(wave * 32 + r) < n) {
+      const long orow = out_row(jd, jd.s1 + t0 + wave * 32 + r);
+      if (orow < 0)
+        *bad = 1;
+      else
+        orow_off[it] = orow * (long)F * OSZ + c16 * 16;
+    }
+  }
+  uint8_t* wout = smem + (size_t)wave * 32 * kOutRow;
+  uint8_t* dst = (uint8_t*)jd.dst;
+  const uint16_t* vrow = (const uint16_t*)(a.state + sl.vdec_off) + (size_t)(lane & 31) * r_dec + 8 * h;
+  const size_t fb_stride = (size_t)32 * r_dec;        // elements per 32-feature block
+
+  uint4 A0[KS > 0 ? KS : 1], A1[KS > 0 ? KS : 1];
+  auto load_a = [&](int fb, uint4* A) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) A[s] = *(const uint4*)(vrow + fb * fb_stride + 16 * s);
   };
-  load_a(0, cur);
-  for (int fg = 0; fg < nfb_all; fg += fpg) {
-    const int nfb = min(fpg, nfb_all - fg);
-    for (int u = 0; u < nfb; ++u) {
-      const int fb = fg + u;
-      if (fb + 1 < nfb_all) load_a(fb + 1, nxt);
-      f32x16 acc;
+  auto block = [&](int fb, const uint4* A, int u) {
+    f32x16 acc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-      for (int s = 0; s < KMAX; ++s) {
-        if (s < ks)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, cur[s]), bfr[s], acc,
-                                                       0, 0, 0);
-      }
-      // D[feature][token]: this lane holds token (lane & 31) and features
-      // fb*32 + 8*qd + 4*h + {0..3} in acc[4*qd .. 4*qd+3].
-      uint8_t* orow_l = wout + (size_t)(lane & 31) * kOutRow + (size_t)u * 32 * osz;
+    for (int s = 0; s < KS; ++s)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, A[s]),
+                                                   __builtin_bit_cast(f16x8, bfr[s]), acc, 0, 0, 0);
+    // D[feature][token]: lane holds token (lane & 31), features
+    // fb*32 + 8*qd + 4*h + {0..3} in acc[4*qd .. 4*qd+3].
+    uint8_t* orow_l = wout + (size_t)(lane & 31) * kOutRow + u * 32 * OSZ;
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int f = fb * 32 + 8 * qd + 4 * h;
-        const float4 m4 = *(const float4*)(mu_l + f);
-        const float o0 = __builtin_fmaf(acc[4 * qd + 0], S, m4.x);
-        const float o1 = __builtin_fmaf(acc[4 * qd + 1], S, m4.y);
-        const float o2 = __builtin_fmaf(acc[4 * qd + 2], S, m4.z);
-        const float o3 = __builtin_fmaf(acc[4 * qd + 3], S, m4.w);
-        const int col = (8 * qd + 4 * h) * osz;
-        if (osz == 4)
-          *(float4*)(orow_l + col) = make_float4(o0, o1, o2, o3);
-        else
-          *(uint2*)(orow_l + col) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-      }
-#pragma unroll
-      for (int s = 0; s < KMAX; ++s) cur[s] = nxt[s];
+    for (int qd = 0; qd < 4; ++qd) {
+      const int f = fb * 32 + 8 * qd + 4 * h;
+      const float4 m4 = *(const float4*)(mu_l + f);
+      const float o0 = __builtin_fmaf(acc[4 * qd + 0], S, m4.x);
+      const float o1 = __builtin_fmaf(acc[4 * qd + 1], S, m4.y);
+      const float o2 = __builtin_fmaf(acc[4 * qd + 2], S, m4.z);
+      const float o3 = __builtin_fmaf(acc[4 * qd + 3], S, m4.w);
+      const int col = (8 * qd + 4 * h) * OSZ;
+      if (OUT32)
+        *(float4*)(orow_l + col) = make_float4(o0, o1, o2, o3);
+      else
+        *(uint2*)(orow_l + col) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
     }
+  };
+  auto store_segment = [&](int fb0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // 32 rows x (nfb * 32 * osz) bytes, 16 bytes per lane.
-    const int row_bytes = nfb * 32 * osz;
-    const int lpr = row_bytes / 16;                  // lanes per row
-    const int rows_per_it = 64 / lpr;
-    for (int r0 = 0; r0 < 32; r0 += rows_per_it) {
-      const int r = r0 + lane / lpr;
-      const int c16 = lane % lpr;
-      if (r < 32 && (uint32_t)(wave * 32 + r) < n) {
-        const long orow = out_row(jd, tok0 + r);
-        if (orow >= 0) {
-          const uint4 v = *(const uint4*)(wout + (size_t)r * kOutRow + c16 * 16);
-          *(uint4*)((uint8_t*)jd.dst + ((size_t)orow * F + (size_t)fg * 32) * osz + c16 * 16) = v;
-        } else {
-          *bad = 1;
-        }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      if (orow_off[it] >= 0) {
+        const uint4 v = *(const uint4*)(wout + (size_t)(8 * it + (lane >> 3)) * kOutRow + c16 * 16);
+        *(uint4*)(dst + orow_off[it] + (size_t)fb0 * 32 * OSZ) = v;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // F/32 is even (F is a multiple of 64): feature blocks go in pairs with
+  // ping-pong basis registers.
+  const int nfb = F / 32;
+  load_a(0, A0);
+  for (int fb = 0; fb < nfb; fb += 2) {
+    load_a(fb + 1, A1);
+    block(fb, A0, OUT32 ? 0 : 0);
+    if (OUT32) store_segment(fb);
+    if (fb + 2 < nfb) load_a(fb + 2, A0);
+    block(fb + 1, A1, OUT32 ? 0 : 1);
+    store_segment(OUT32 ? fb + 1 : fb);
   }
 }
 
-// LDS layout of a decode tile: [records (fused only) | output staging | mean].
-__host__ __device__ inline size_t dec_out_off(size_t rec_bytes) { return align_up(rec_bytes + 16, 16); }
-
-template <int KMAX, int G>
+// Fused decode: header check, passthrough tiles and compressed tiles.
+template <int KS, bool OUT32>
 __global__ __launch_bounds__(kThreads) void decode_kernel(const LaunchArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int flag;
@@ -654,7 +719,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const LaunchArgs a) {
   if (threadIdx.x == 0) flag = check_header(a, jd, sl);
   __syncthreads();
   const int st = flag;
-  if (lt == 0 && threadIdx.x == 0) set_status(a, j, st);
+  if (lt == 0 && threadIdx.x == 0) set_status(a, jd.status_idx, st);
   if (st != KVTC_OK) return;
   __syncthreads();
   if (threadIdx.x == 0) flag = 0;
@@ -665,25 +730,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const LaunchArgs a) {
   } else {
     const uint32_t t0 = lt * kDecTile;
     const uint32_t n = min((uint32_t)kDecTile, jd.tc - t0);
-    const int esz = a.dtype == KVTC_F32 ? 4 : 2;
-    const uint8_t* recs = (const uint8_t*)jd.src + record_base(jd, a.F, esz) +
-                          (size_t)t0 * sl.record_bytes;
-    // Records and output staging share one region (records are consumed
-    // before the first output row is staged); the mean follows it.
-    const size_t region = max(align_up((size_t)kDecTile * sl.record_bytes + 16, 16),
-                              (size_t)4 * 32 * kOutRow);
-    float* mu_l = (float*)(smem + region);
-    {
-      const float4* mu = (const float4*)(a.state + sl.mu_off);
-      for (int i = threadIdx.x; i < a.F / 4; i += kThreads) ((float4*)mu_l)[i] = mu[i];
-    }
-    stage_to_lds(smem, recs, (size_t)n * sl.record_bytes);
-    __syncthreads();
-    restore_tile<KMAX, G, false>(a, jd, sl, smem, smem, mu_l, t0, n, &bad);
+    restore_tile<KS, OUT32, false>(a, jd, sl, smem, t0, n, &bad);
   }
   if (bad) atomicExch(&flag, 1);
   __syncthreads();
-  if (threadIdx.x == 0 && flag) set_status(a, j, KVTC_E_INVALID);
+  if (threadIdx.x == 0 && flag) set_status(a, jd.status_idx, KVTC_E_INVALID);
 }
 
 // Stage 1: header check, passthrough rows, records -> staging codes/scales.
@@ -700,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const LaunchArgs a) {
   if (threadIdx.x == 0) flag = check_header(a, jd, sl);
   __syncthreads();
   const int st = flag;
-  if (lt == 0 && threadIdx.x == 0) set_status(a, j, st);
+  if (lt == 0 && threadIdx.x == 0) set_status(a, jd.status_idx, st);
   if (st != KVTC_OK) return;
   __syncthreads();
   if (threadIdx.x == 0) flag = 0;
@@ -734,11 +785,11 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const LaunchArgs a) {
   }
   if (bad) atomicExch(&flag, 1);
   __syncthreads();
-  if (threadIdx.x == 0 && flag) set_status(a, j, KVTC_E_INVALID);
+  if (threadIdx.x == 0 && flag) set_status(a, jd.status_idx, KVTC_E_INVALID);
 }
 
 // Stage 2: staging -> compressed output rows.
-template <int KMAX, int G>
+template <int KS, bool OUT32>
 __global__ __launch_bounds__(kThreads) void restore_kernel(const LaunchArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int flag;
@@ -748,22 +799,16 @@ __global__ __launch_bounds__(kThreads) void restore_kernel(const LaunchArgs a) {
   const JobDesc& jd = a.jobs[j];
   const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
   const uint32_t lt = tile - jd.tile_begin;
-  if (prior_rank(a, j) != 0 || lt >= jd.n_ctiles) return;  // stage 1 rejected the stream
+  if (prior_rank(a, jd.status_idx) != 0 || lt >= jd.n_ctiles) return;  // stage 1 rejected it
   if (threadIdx.x == 0) flag = 0;
   __syncthreads();
   int bad = 0;
   const uint32_t t0 = lt * kDecTile;
   const uint32_t n = min((uint32_t)kDecTile, jd.tc - t0);
-  float* mu_l = (float*)(smem + (size_t)4 * 32 * kOutRow);
-  {
-    const float4* mu = (const float4*)(a.state + sl.mu_off);
-    for (int i = threadIdx.x; i < a.F / 4; i += kThreads) ((float4*)mu_l)[i] = mu[i];
-  }
-  __syncthreads();
-  restore_tile<KMAX, G, true>(a, jd, sl, nullptr, smem, mu_l, t0, n, &bad);
+  restore_tile<KS, OUT32, true>(a, jd, sl, smem, t0, n, &bad);
   if (bad) atomicExch(&flag, 1);
   __syncthreads();
-  if (threadIdx.x == 0 && flag) set_status(a, j, KVTC_E_INVALID);
+  if (threadIdx.x == 0 && flag) set_status(a, jd.status_idx, KVTC_E_INVALID);
 }
 
 // Test hook: stream from given codes and (shift, scale) pairs, through the
@@ -781,7 +826,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const LaunchArgs a, cons
   const size_t row_bytes = (size_t)a.F * esz;
   if (lt == 0 && threadIdx.x == 0) {
     write_header(a, jd, sl);
-    set_status(a, 0, KVTC_OK);
+    set_status(a, jd.status_idx, KVTC_OK);
   }
   if (lt >= jd.n_ctiles) {
     encode_passthrough(jd, lt - jd.n_ctiles, row_bytes);
@@ -835,43 +880,49 @@ static int launch_encode_g(const LaunchArgs& a, int nb, size_t lds, hipStream_t 
   return (int)hipGetLastError();
 }
 
-int launch_encode(const LaunchArgs& a, int nb_max, int G, size_t lds, hipStream_t s) {
+int launch_encode(const LaunchArgs& a, int nb, int G, size_t lds, hipStream_t s) {
   const bool f32 = a.dtype == KVTC_F32;
-  if (G == 16) return f32 ? launch_encode_g<16, true>(a, nb_max, lds, s) : launch_encode_g<16, false>(a, nb_max, lds, s);
-  if (G == 32) return f32 ? launch_encode_g<32, true>(a, nb_max, lds, s) : launch_encode_g<32, false>(a, nb_max, lds, s);
+  if (G == 16) return f32 ? launch_encode_g<16, true>(a, nb, lds, s) : launch_encode_g<16, false>(a, nb, lds, s);
+  if (G == 32) return f32 ? launch_encode_g<32, true>(a, nb, lds, s) : launch_encode_g<32, false>(a, nb, lds, s);
   return (int)hipErrorInvalidValue;
 }
 
-template <int G>
-static int launch_decode_g(const LaunchArgs& a, int kmax, size_t lds, bool staged, hipStream_t s) {
+size_t decode_lds_bytes(int r_dec, int F) { return dec_lds_bytes(r_dec, F); }
+
+// Decode launches take the exact K-step count ks = r_dec / 16 of every job
+// in the batch (the host groups jobs by it).
+template <bool OUT32>
+static int launch_decode_o(const LaunchArgs& a, int ks, size_t lds, bool staged, hipStream_t s) {
   const dim3 g = grid_for(a.total_tiles);
-#define KVTC_DEC(KV)                                                                            \
-  if (kmax <= KV) {                                                                             \
-    if (staged) {                                                                               \
-      allow_lds(restore_kernel<KV, G>, lds);                                                    \
-      hipLaunchKernelGGL((restore_kernel<KV, G>), g, dim3(kThreads), lds, s, a);               \
-    } else {                                                                                    \
-      allow_lds(decode_kernel<KV, G>, lds);                                                     \
-      hipLaunchKernelGGL((decode_kernel<KV, G>), g, dim3(kThreads), lds, s, a);                \
-    }                                                                                           \
-    return (int)hipGetLastError();                                                             \
+#define KVTC_DEC(KV)                                                                 \
+  case KV:                                                                           \
+    if (staged) {                                                                    \
+      allow_lds(restore_kernel<KV, OUT32>, lds);                                     \
+      hipLaunchKernelGGL((restore_kernel<KV, OUT32>), g, dim3(kThreads), lds, s, a); \
+    } else {                                                                         \
+      allow_lds(decode_kernel<KV, OUT32>, lds);                                      \
+      hipLaunchKernelGGL((decode_kernel<KV, OUT32>), g, dim3(kThreads), lds, s, a);  \
+    }                                                                                \
+    break;
+  switch (ks) {
+    KVTC_DEC(0) KVTC_DEC(1) KVTC_DEC(2) KVTC_DEC(3) KVTC_DEC(4) KVTC_DEC(5) KVTC_DEC(6)
+    KVTC_DEC(7) KVTC_DEC(8) KVTC_DEC(9) KVTC_DEC(10) KVTC_DEC(11) KVTC_DEC(12) KVTC_DEC(13)
+    KVTC_DEC(14) KVTC_DEC(15) KVTC_DEC(16)
+    default:
+      return (int)hipErrorInvalidValue;
   }
-  KVTC_DEC(2) KVTC_DEC(4) KVTC_DEC(6) KVTC_DEC(8) KVTC_DEC(12) KVTC_DEC(16)
 #undef KVTC_DEC
-  return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
 }
 
-int launch_decode(const LaunchArgs& a, int kmax, int G, size_t lds, hipStream_t s) {
-  if (G == 16) return launch_decode_g<16>(a, kmax, lds, false, s);
-  if (G == 32) return launch_decode_g<32>(a, kmax, lds, false, s);
-  return (int)hipErrorInvalidValue;
+int launch_decode(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
+  return a.out_dtype == KVTC_F32 ? launch_decode_o<true>(a, ks, lds, false, s)
+                                 : launch_decode_o<false>(a, ks, lds, false, s);
 }
 
-int launch_restore(const LaunchArgs& a, int kmax, int G, hipStream_t s) {
-  const size_t lds = (size_t)4 * 32 * kOutRow + (size_t)a.F * 4;
-  if (G == 16) return launch_decode_g<16>(a, kmax, lds, true, s);
-  if (G == 32) return launch_decode_g<32>(a, kmax, lds, true, s);
-  return (int)hipErrorInvalidValue;
+int launch_restore(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
+  return a.out_dtype == KVTC_F32 ? launch_decode_o<true>(a, ks, lds, true, s)
+                                 : launch_decode_o<false>(a, ks, lds, true, s);
 }
 
 int launch_unpack(const LaunchArgs& a, int G, size_t lds, hipStream_t s) {
