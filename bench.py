@@ -139,11 +139,14 @@ def main():
 
     pipe = Pipeline(K, codec, w, jobs, dec_jobs, dev) if w.paged else None
 
+    n_dws = codec.decode_workspace_bytes(dec_jobs)
+    dws = torch.zeros((n_dws + 3) // 4, dtype=torch.int32, device=dev)
+
     def decode():
         if pipe is not None:
             pipe.run(stream)
         else:
-            codec.decode(dec_jobs, K.KVTC_BF16, ws, stream)
+            codec.decode(dec_jobs, K.KVTC_BF16, dws, n_dws, stream)
 
     # Plain device copy of a known size: the practical HBM ceiling and the
     # reference that scales the FETCH_SIZE / WRITE_SIZE counters.
@@ -166,6 +169,8 @@ def main():
         decode()
     torch.cuda.synchronize()
     st = K.kvtc_read_device_status(ws, n_jobs, stream)
+    if pipe is None:
+        st = np.concatenate([st, K.kvtc_read_device_status(dws, n_jobs, stream)])
     if np.any(st != 0):
         raise SystemExit(f"device status errors: {st}")
     if pipe is not None:

@@ -181,9 +181,10 @@ kvtc_status kvtc_upload(kvtc_codec* codec, void* d_state, size_t bytes, hipStrea
 size_t kvtc_encoded_bytes(const kvtc_codec* codec, int32_t layer, int32_t kind,
                           int64_t n_tokens);
 /* Workspace (device) for a call with up to max_jobs jobs: one 64-bit status
- * word per job, 256-byte aligned. Each launch stamps the words it writes, so
- * the workspace needs no clearing between calls; kvtc_decode_restore reads
- * the words kvtc_decode_unpack left. */
+ * word per job (256-byte aligned), then a 256-byte sink that absorbs the
+ * kernels' stores that have no destination row. Each launch stamps the words
+ * it writes, so the workspace needs no clearing between calls;
+ * kvtc_decode_restore reads the words kvtc_decode_unpack left. */
 size_t kvtc_workspace_bytes(int32_t max_jobs);
 
 /* Encode n_jobs tensors in one launch (section 2B). Each job's dst must hold
@@ -191,19 +192,30 @@ size_t kvtc_workspace_bytes(int32_t max_jobs);
 kvtc_status kvtc_encode(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
                         void* d_ws, hipStream_t stream);
 
-/* Decode n_jobs streams in one launch (section 2C), writing out_dtype rows.
- * Passthrough rows are copied bit for bit when out_dtype equals the codec
- * dtype (converted with round-to-nearest-even otherwise). */
+/* Decode n_jobs streams (section 2C), writing out_dtype rows: stage 1 and
+ * stage 2 below back to back on `stream`, with the staging buffer inside
+ * d_ws. d_ws must hold ws_bytes >= kvtc_decode_workspace_bytes(jobs)
+ * (kvtc_workspace_bytes(n_jobs) followed by kvtc_staging_bytes(jobs));
+ * KVTC_E_CAPACITY otherwise. Passthrough rows are copied bit for bit when
+ * out_dtype equals the codec dtype (converted with round-to-nearest-even
+ * otherwise). */
+size_t kvtc_decode_workspace_bytes(const kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs);
 kvtc_status kvtc_decode(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
-                        int32_t out_dtype, void* d_ws, hipStream_t stream);
+                        int32_t out_dtype, void* d_ws, size_t ws_bytes, hipStream_t stream);
 
 /* Two-stage decode for layer-by-layer pipelines (section 2C: decompression
  * can proceed layer by layer). Stage 1 validates headers, copies passthrough
- * rows to dst and unpacks records into d_staging; stage 2 dequantizes,
- * applies V^T, adds the mean and writes the compressed rows to dst. Both
- * stages must see the same jobs, staging and workspace. Staging layout per job
- * (consecutive, each 256-byte aligned): u8 codes[T_c][r_eff], then
- * f32 shift_scale[T_c][n_act][2]. */
+ * rows to dst and turns every record into the operands of the
+ * reconstruction: for each token the dequantized coefficients
+ * c_hat = shift + q * fp32(scale / (2^b - 1)) divided by a power of two S_t
+ * (chosen per token so the largest |c_hat| / S_t lies in [2^14, 2^15)) as
+ * fp16, and S_t. Stage 2 forms S_t * (V' c) + mu for every compressed row and
+ * writes it to dst. Both stages must see the same jobs, staging and
+ * workspace. Staging layout per job (consecutive, each 256-byte aligned):
+ * for each block of 32 compressed tokens, ks = ceil(r_eff / 16) x 64
+ * fragments of 8 fp16 (fragment (s, l) holds components 16 s + 8 (l / 32)
+ * .. + 8 of token l % 32 of the block; zero past r_eff and past the last
+ * token), then 32 f32 S_t. */
 size_t kvtc_staging_bytes(const kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs);
 kvtc_status kvtc_decode_unpack(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
                                int32_t out_dtype, void* d_staging, size_t staging_bytes,
@@ -218,6 +230,13 @@ kvtc_status kvtc_decode_restore(kvtc_codec* codec, const kvtc_job* jobs, int32_t
  * passthrough rows. */
 kvtc_status kvtc_pack(kvtc_codec* codec, const kvtc_job* job, const void* d_codes,
                       const void* d_shift_scale, void* d_ws, hipStream_t stream);
+
+/* Test hook: the inverse of kvtc_pack's record packing. Reads the records of
+ * one job's stream (job.src; the header is not checked) into codes
+ * (u8 [T_c][r_eff], device) and shift/scale pairs (f32 [T_c][n_act][2],
+ * device); job.dst is not written. */
+kvtc_status kvtc_unpack(kvtc_codec* codec, const kvtc_job* job, void* d_codes, void* d_shift_scale,
+                        void* d_ws, hipStream_t stream);
 
 /* Copy n_jobs status words from the workspace to host memory. This
  * synchronises `stream` first. Each word is KVTC_OK or a kvtc_status. */

@@ -74,7 +74,9 @@ def lib():
         "kvtc_encoded_bytes": (sz, [vp, i32, i32, i64]),
         "kvtc_workspace_bytes": (sz, [i32]),
         "kvtc_encode": (st, [vp, C.POINTER(kvtc_job), i32, vp, vp]),
-        "kvtc_decode": (st, [vp, C.POINTER(kvtc_job), i32, i32, vp, vp]),
+        "kvtc_decode": (st, [vp, C.POINTER(kvtc_job), i32, i32, vp, sz, vp]),
+        "kvtc_decode_workspace_bytes": (sz, [vp, C.POINTER(kvtc_job), i32]),
+        "kvtc_unpack": (st, [vp, C.POINTER(kvtc_job), vp, vp, vp, vp]),
         "kvtc_staging_bytes": (sz, [vp, C.POINTER(kvtc_job), i32]),
         "kvtc_decode_unpack": (st, [vp, C.POINTER(kvtc_job), i32, i32, vp, sz, vp, vp]),
         "kvtc_decode_restore": (st, [vp, C.POINTER(kvtc_job), i32, i32, vp, sz, vp, vp]),
@@ -190,8 +192,13 @@ def kvtc_encode(codec: int, jobs, d_ws, stream=None) -> None:
     _check(lib().kvtc_encode(codec, _jobs(jobs), len(jobs), _ptr(d_ws), _stream(stream)))
 
 
-def kvtc_decode(codec: int, jobs, out_dtype: int, d_ws, stream=None) -> None:
-    _check(lib().kvtc_decode(codec, _jobs(jobs), len(jobs), out_dtype, _ptr(d_ws), _stream(stream)))
+def kvtc_decode(codec: int, jobs, out_dtype: int, d_ws, ws_bytes: int, stream=None) -> None:
+    _check(lib().kvtc_decode(codec, _jobs(jobs), len(jobs), out_dtype, _ptr(d_ws), ws_bytes,
+                             _stream(stream)))
+
+
+def kvtc_decode_workspace_bytes(codec: int, jobs) -> int:
+    return lib().kvtc_decode_workspace_bytes(codec, _jobs(jobs), len(jobs))
 
 
 def kvtc_staging_bytes(codec: int, jobs) -> int:
@@ -213,6 +220,11 @@ def kvtc_decode_restore(codec: int, jobs, out_dtype: int, d_staging, staging_byt
 def kvtc_pack(codec: int, job: kvtc_job, d_codes, d_shift_scale, d_ws, stream=None) -> None:
     _check(lib().kvtc_pack(codec, C.byref(job), _ptr(d_codes), _ptr(d_shift_scale), _ptr(d_ws),
                            _stream(stream)))
+
+
+def kvtc_unpack(codec: int, job: kvtc_job, d_codes, d_shift_scale, d_ws, stream=None) -> None:
+    _check(lib().kvtc_unpack(codec, C.byref(job), _ptr(d_codes), _ptr(d_shift_scale), _ptr(d_ws),
+                             _stream(stream)))
 
 
 def kvtc_read_device_status(d_ws, n_jobs: int, stream=None) -> np.ndarray:
@@ -274,8 +286,11 @@ class Codec:
     def encode(self, jobs, d_ws, stream=None):
         kvtc_encode(self.h, jobs, d_ws, stream)
 
-    def decode(self, jobs, out_dtype, d_ws, stream=None):
-        kvtc_decode(self.h, jobs, out_dtype, d_ws, stream)
+    def decode(self, jobs, out_dtype, d_ws, ws_bytes, stream=None):
+        kvtc_decode(self.h, jobs, out_dtype, d_ws, ws_bytes, stream)
+
+    def decode_workspace_bytes(self, jobs) -> int:
+        return kvtc_decode_workspace_bytes(self.h, jobs)
 
     def staging_bytes(self, jobs) -> int:
         return kvtc_staging_bytes(self.h, jobs)
@@ -288,6 +303,9 @@ class Codec:
 
     def pack(self, job, d_codes, d_shift_scale, d_ws, stream=None):
         kvtc_pack(self.h, job, d_codes, d_shift_scale, d_ws, stream)
+
+    def unpack(self, job, d_codes, d_shift_scale, d_ws, stream=None):
+        kvtc_unpack(self.h, job, d_codes, d_shift_scale, d_ws, stream)
 
 
 def params(n_layers, kv_heads, head_dim, sink, window, group, max_bits, bits_per_value,

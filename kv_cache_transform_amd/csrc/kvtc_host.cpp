@@ -100,6 +100,7 @@ struct kvtc_codec {
   uint64_t uploaded_version = ~0ull;
   const uint8_t* d_state = nullptr;
   size_t d_state_bytes = 0;
+  const int32_t* d_zero = nullptr;        // a zero word in the device state
 };
 
 namespace {
@@ -218,9 +219,15 @@ size_t stream_bytes(const kvtc_codec* c, const Slot& s, long T) {
   return kHeaderBytes + (size_t)(s1 + w1) * c->F * elem_bytes(c->p.dtype) + (size_t)tc * s.record_bytes;
 }
 
+// Decode staging of one job: stg_block_bytes(ks) per block of kDecTok
+// compressed tokens.
 size_t job_staging_bytes(const Slot& s, uint32_t tc) {
-  return align_up((size_t)tc * s.r_eff, kAlign) + align_up((size_t)tc * s.n_act * 8, kAlign);
+  const int ks = (int)(align_up((size_t)s.r_eff, 16) / 16);
+  return align_up((size_t)((tc + kDecTok - 1) / kDecTok) * stg_block_bytes(ks), kAlign);
 }
+
+// Byte offset of the workspace sink behind the status words of n jobs.
+size_t sink_offset(int32_t n) { return align_up((size_t)std::max(n, 1) * sizeof(uint64_t), kAlign); }
 
 }  // namespace
 
@@ -487,7 +494,7 @@ kvtc_status kvtc_load(const void* buf, size_t n, kvtc_codec** out) {
 
 size_t kvtc_device_state_bytes(const kvtc_codec* c) {
   if (!c) return 0;
-  size_t n = align_up(c->slots.size() * sizeof(DevSlot), kAlign);
+  size_t n = align_up(c->slots.size() * sizeof(DevSlot), kAlign) + kAlign;   // table, zero block
   for (const Slot& s : c->slots) {
     if (!s.calibrated) continue;
     const size_t r_enc = align_up((size_t)s.r_eff, 32), r_dec = align_up((size_t)s.r_eff, 16);
@@ -508,7 +515,8 @@ kvtc_status kvtc_upload(kvtc_codec* c, void* d_state, size_t bytes, hipStream_t 
   std::vector<uint8_t> h(need, 0);
   std::vector<DevSlot> table(c->slots.size());
   std::memset(table.data(), 0, table.size() * sizeof(DevSlot));
-  size_t off = align_up(c->slots.size() * sizeof(DevSlot), kAlign);
+  const size_t zero_off = align_up(c->slots.size() * sizeof(DevSlot), kAlign);
+  size_t off = zero_off + kAlign;
   const int F = c->F, G = c->p.group;
   for (size_t i = 0; i < c->slots.size(); ++i) {
     const Slot& s = c->slots[i];
@@ -555,6 +563,7 @@ kvtc_status kvtc_upload(kvtc_codec* c, void* d_state, size_t bytes, hipStream_t 
   std::lock_guard<std::mutex> lk(c->mu);
   c->d_state = (const uint8_t*)d_state;
   c->d_state_bytes = need;
+  c->d_zero = (const int32_t*)((const uint8_t*)d_state + zero_off);
   c->uploaded_version = c->calib_version;
   return KVTC_OK;
 }
@@ -565,9 +574,7 @@ size_t kvtc_encoded_bytes(const kvtc_codec* c, int32_t layer, int32_t kind, int6
   return stream_bytes(c, c->slots[idx], n_tokens);
 }
 
-size_t kvtc_workspace_bytes(int32_t max_jobs) {
-  return align_up((size_t)std::max(max_jobs, 1) * sizeof(uint64_t), kAlign);
-}
+size_t kvtc_workspace_bytes(int32_t max_jobs) { return sink_offset(max_jobs) + kSinkBytes; }
 
 size_t kvtc_staging_bytes(const kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs) {
   if (!c || !jobs || n_jobs <= 0) return 0;
@@ -582,11 +589,16 @@ size_t kvtc_staging_bytes(const kvtc_codec* c, const kvtc_job* jobs, int32_t n_j
   return n;
 }
 
+size_t kvtc_decode_workspace_bytes(const kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs) {
+  const size_t st = kvtc_staging_bytes(c, jobs, n_jobs);
+  return st ? kvtc_workspace_bytes(n_jobs) + st : 0;
+}
+
 }  // extern "C"
 
 namespace {
 
-enum class Mode { Encode, Decode, Unpack, Restore, Pack };
+enum class Mode { Encode, Unpack, Restore, Pack, UnpackCodes };
 
 // Launch stamps for the workspace status words (0 is never issued).
 uint32_t next_epoch() {
@@ -609,8 +621,8 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
   if (!d_ws || !aligned16(d_ws)) return fail(KVTC_E_INVALID, "workspace must be non-null and aligned");
   if (!c->d_state || c->uploaded_version != c->calib_version)
     return fail(KVTC_E_INVALID, "device state is missing or stale: call kvtc_upload");
-  if (mode != Mode::Encode && mode != Mode::Pack && out_dtype != KVTC_F32 && out_dtype != KVTC_BF16)
-    return fail(KVTC_E_INVALID, "bad output dtype");
+  const bool dec = mode == Mode::Unpack || mode == Mode::Restore;
+  if (dec && out_dtype != KVTC_F32 && out_dtype != KVTC_BF16) return fail(KVTC_E_INVALID, "bad output dtype");
   const int F = c->F;
   const size_t out_esz = elem_bytes(out_dtype);
   // Per-job validation and the fields that do not depend on the batch.
@@ -641,6 +653,8 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
       if (j.dst_capacity < stream_bytes(c, s, j.n_tokens))
         return fail(KVTC_E_CAPACITY, "job: dst_capacity below kvtc_encoded_bytes");
       key[i] = std::max<int>(1, (int)(align_up((size_t)s.r_eff, 32) / 32));
+    } else if (mode == Mode::UnpackCodes) {
+      key[i] = 0;
     } else {
       if (j.block_table) {
         if (j.block_size <= 0 || j.n_blocks <= 0) return fail(KVTC_E_INVALID, "job: bad paging");
@@ -651,14 +665,18 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
         d.n_blocks = j.n_blocks;
       } else if ((size_t)j.n_tokens * F * out_esz > j.dst_capacity) {
         return fail(KVTC_E_CAPACITY, "job: dst smaller than n_tokens rows");
+      } else {
+        // Contiguous output as one block of 2^30 rows through a zero entry,
+        // so the kernels have a single (paged) row mapping.
+        d.block_table = c->d_zero;
+        d.block_size = 1 << 30;
+        d.n_blocks = 1;
       }
-      if (mode == Mode::Unpack || mode == Mode::Restore) {
-        st_off[i] = st_total;
-        st_total += job_staging_bytes(s, d.tc);
-        if (!d_staging || st_total > staging_bytes) return fail(KVTC_E_CAPACITY, "staging buffer too small");
-        d.staging = d_staging + st_off[i];
-      }
-      key[i] = mode == Mode::Unpack ? 0 : (int)(align_up((size_t)s.r_eff, 16) / 16);
+      st_off[i] = st_total;
+      st_total += job_staging_bytes(s, d.tc);
+      if (!d_staging || st_total > staging_bytes) return fail(KVTC_E_CAPACITY, "staging buffer too small");
+      d.staging = d_staging + st_off[i];
+      key[i] = (int)(align_up((size_t)s.r_eff, 16) / 16);
     }
   }
   std::vector<int> order(n);
@@ -675,6 +693,7 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
     a.F = F;
     a.state = c->d_state;
     a.status = (unsigned long long*)d_ws;
+    a.sink = (uint8_t*)d_ws + sink_offset(n);
     a.epoch = next_epoch();
     uint32_t tiles = 0;
     size_t rb_max = 0;
@@ -682,26 +701,36 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
       JobDesc d = desc[order[p + b]];
       const Slot& s = c->slots[d.slot];
       const uint32_t ptiles = (d.s1 + d.w1 + kPassRows - 1) / kPassRows;
-      const int tile = mode == Mode::Encode || mode == Mode::Pack ? kEncTile
-                       : mode == Mode::Unpack                     ? kUnpackTile
-                                                                  : kDecTile;
-      d.n_ctiles = (d.tc + tile - 1) / tile;
+      if (mode == Mode::Restore) {
+        // feature slabs x token ranges of kGemmTok
+        const int fs = gemm_features(key[order[p]]);
+        d.n_ctiles = (uint32_t)((F + fs - 1) / fs) * ((d.tc + kGemmTok - 1) / kGemmTok);
+      } else {
+        const int tile = mode == Mode::Unpack ? kPrepTok : mode == Mode::UnpackCodes ? kUnpackTile : kEncTile;
+        d.n_ctiles = (d.tc + tile - 1) / tile;
+      }
       d.tile_begin = tiles;
-      tiles += mode == Mode::Restore ? d.n_ctiles : std::max<uint32_t>(1, d.n_ctiles + ptiles);
+      if (mode == Mode::Restore || mode == Mode::UnpackCodes)
+        tiles += d.n_ctiles;
+      else
+        tiles += std::max<uint32_t>(1, d.n_ctiles + ptiles);
       a.jobs[b] = d;
       rb_max = std::max(rb_max, (size_t)s.record_bytes);
     }
     a.total_tiles = tiles;
     const int k = key[order[p]];
     size_t l = 16;
+    const size_t rbp = (size_t)padded_stride((int)rb_max);
     if (mode == Mode::Encode)
-      l = std::max({l, 2 * (size_t)32 * k * kEncRowPad * 2 + (size_t)F * 4, (size_t)kEncTile * rb_max});
+      l = std::max({l, 2 * (size_t)32 * k * kEncRowPad * 2 + (size_t)F * 4, (size_t)kEncTile * rbp});
     else if (mode == Mode::Pack)
-      l = std::max(l, (size_t)kEncTile * rb_max);
-    else if (mode == Mode::Unpack)
+      l = std::max(l, (size_t)kEncTile * rbp);
+    else if (mode == Mode::UnpackCodes)
       l = std::max(l, (size_t)kUnpackTile * rb_max + 16);
+    else if (mode == Mode::Unpack)
+      l = std::max(l, (size_t)kPrepTok * rbp + 16);
     else
-      l = decode_lds_bytes(16 * k, F);
+      l = gemm_lds_bytes(k);
     if (l > 160 * 1024) return fail(KVTC_E_UNSUPPORTED, "tile does not fit in LDS");
     batches.push_back(a);
     shape.push_back(k);
@@ -735,21 +764,6 @@ kvtc_status kvtc_encode(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, voi
   return KVTC_OK;
 }
 
-kvtc_status kvtc_decode(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, int32_t out_dtype,
-                        void* d_ws, hipStream_t stream) {
-  std::vector<LaunchArgs> b;
-  std::vector<int> k;
-  std::vector<size_t> l;
-  kvtc_status st = plan(c, Mode::Decode, jobs, n_jobs, out_dtype, d_ws, nullptr, 0, b, k, l);
-  if (st != KVTC_OK) return st;
-  for (size_t i = 0; i < b.size(); ++i) {
-    if (b[i].total_tiles == 0) continue;
-    st = hip_status(launch_decode(b[i], k[i], l[i], stream), "decode launch");
-    if (st != KVTC_OK) return st;
-  }
-  return KVTC_OK;
-}
-
 kvtc_status kvtc_decode_unpack(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, int32_t out_dtype,
                                void* d_staging, size_t staging_bytes, void* d_ws, hipStream_t stream) {
   std::vector<LaunchArgs> b;
@@ -760,7 +774,7 @@ kvtc_status kvtc_decode_unpack(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jo
   if (st != KVTC_OK) return st;
   for (size_t i = 0; i < b.size(); ++i) {
     if (b[i].total_tiles == 0) continue;
-    st = hip_status(launch_unpack(b[i], c->p.group, l[i], stream), "unpack launch");
+    st = hip_status(launch_prep(b[i], k[i], l[i], stream), "decode stage 1 launch");
     if (st != KVTC_OK) return st;
   }
   return KVTC_OK;
@@ -777,7 +791,38 @@ kvtc_status kvtc_decode_restore(kvtc_codec* c, const kvtc_job* jobs, int32_t n_j
   if (st != KVTC_OK) return st;
   for (size_t i = 0; i < b.size(); ++i) {
     if (b[i].total_tiles == 0) continue;
-    st = hip_status(launch_restore(b[i], k[i], l[i], stream), "restore launch");
+    st = hip_status(launch_gemm(b[i], k[i], l[i], stream), "decode stage 2 launch");
+    if (st != KVTC_OK) return st;
+  }
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_decode(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, int32_t out_dtype,
+                        void* d_ws, size_t ws_bytes, hipStream_t stream) {
+  if (!c || !jobs || n_jobs <= 0 || n_jobs > KVTC_MAX_JOBS) return fail(KVTC_E_INVALID, "bad codec, jobs or job count");
+  const size_t need = kvtc_decode_workspace_bytes(c, jobs, n_jobs);
+  if (need == 0) return fail(KVTC_E_INVALID, "job: bad layer or kind, or not calibrated");
+  if (!d_ws || ws_bytes < need) return fail(KVTC_E_CAPACITY, "workspace below kvtc_decode_workspace_bytes");
+  uint8_t* stg = (uint8_t*)d_ws + kvtc_workspace_bytes(n_jobs);
+  const size_t stg_bytes = ws_bytes - kvtc_workspace_bytes(n_jobs);
+  kvtc_status st = kvtc_decode_unpack(c, jobs, n_jobs, out_dtype, stg, stg_bytes, d_ws, stream);
+  if (st != KVTC_OK) return st;
+  return kvtc_decode_restore(c, jobs, n_jobs, out_dtype, stg, stg_bytes, d_ws, stream);
+}
+
+kvtc_status kvtc_unpack(kvtc_codec* c, const kvtc_job* job, void* d_codes, void* d_shift_scale, void* d_ws,
+                        hipStream_t stream) {
+  std::vector<LaunchArgs> b;
+  std::vector<int> k;
+  std::vector<size_t> l;
+  kvtc_status st = plan(c, Mode::UnpackCodes, job, 1, c ? c->p.dtype : 0, d_ws, nullptr, 0, b, k, l);
+  if (st != KVTC_OK) return st;
+  const int idx = job->layer * 2 + job->kind;
+  if (c->slots[idx].r_eff > 0 && (!d_codes || !d_shift_scale))
+    return fail(KVTC_E_INVALID, "null codes or shift/scale");
+  for (size_t i = 0; i < b.size(); ++i) {
+    if (b[i].total_tiles == 0) continue;
+    st = hip_status(launch_unpack(b[i], c->p.group, l[i], d_codes, d_shift_scale, stream), "unpack launch");
     if (st != KVTC_OK) return st;
   }
   return KVTC_OK;

@@ -71,6 +71,7 @@ struct LaunchArgs {
   int32_t pad;
   const uint8_t* state;    // device state base
   unsigned long long* status;  // per-launch slice of the workspace status words
+  uint8_t* sink;           // kSinkBytes of workspace that absorb stores without a row
   uint32_t epoch;          // stamp of this launch (see status_word)
   uint32_t pad2;
 };
@@ -88,23 +89,46 @@ __host__ __device__ inline int rank_status(int rank) {
 
 // Tile sizes (tokens per workgroup tile).
 constexpr int kEncTile = 128;
-constexpr int kDecTile = 128;
 constexpr int kUnpackTile = 256;
 constexpr int kPassRows = 16;
 constexpr int kEncKS = 64;                 // features per LDS basis slice (encode)
 constexpr int kEncRowPad = kEncKS + 8;     // bf16 elements per LDS basis row
 constexpr int kOutRow = 128 + 16;          // bytes per LDS output-staging row (decode)
 
+// LDS row stride for records under assembly (encode, pack): a multiple of 4
+// bytes with an odd dword count, so lanes of consecutive tokens write to
+// different banks.
+__host__ __device__ inline int padded_stride(int rb) {
+  int p = (rb + 3) & ~3;
+  if (((p >> 2) & 1) == 0) p += 4;
+  return p;
+}
+
+// Decode. Stage 1 handles kPrepTok compressed tokens per tile and writes,
+// per block of kDecTok tokens, ks * 64 B-operand fragments of 16 bytes (fp16,
+// MFMA lane order) and kDecTok f32 token scales: stg_block_bytes(ks) bytes.
+// Stage 2 tiles are gemm_features(ks) features x kGemmTok tokens; the slab of
+// V' (rows padded by 16 bytes), mu and four waves' output staging rows take
+// gemm_lds_bytes(ks) of LDS.
+constexpr int kDecTok = 32;
+constexpr int kPrepTok = 128;
+constexpr int kGemmTok = 1024;
+constexpr size_t kSinkBytes = 256;         // workspace target of stores that have no row
+__host__ __device__ constexpr size_t stg_block_bytes(int ks) { return (size_t)ks * 1024 + kDecTok * 4; }
+__host__ __device__ constexpr int gemm_features(int ks) { return ks <= 8 ? 128 : 64; }
+__host__ __device__ constexpr size_t gemm_lds_bytes(int ks) {
+  return (size_t)gemm_features(ks) * (ks * 32 + 16) + (size_t)gemm_features(ks) * 4 + 4 * kDecTok * kOutRow;
+}
+
 // Host-side launchers implemented in kvtc_kernels.hip (G = group size, lds =
 // dynamic LDS bytes). Every job of one launch has the same shape parameter:
-// nb = r_enc / 32 for encode, ks = r_dec / 16 for decode and restore. They
+// nb = r_enc / 32 for encode, ks = r_dec / 16 for the decode stages. They
 // return a hipError_t value cast to int.
 int launch_encode(const LaunchArgs& a, int nb, int G, size_t lds, hipStream_t s);
-int launch_decode(const LaunchArgs& a, int ks, size_t lds, hipStream_t s);
-int launch_unpack(const LaunchArgs& a, int G, size_t lds, hipStream_t s);
-int launch_restore(const LaunchArgs& a, int ks, size_t lds, hipStream_t s);
+int launch_prep(const LaunchArgs& a, int ks, size_t lds, hipStream_t s);
+int launch_gemm(const LaunchArgs& a, int ks, size_t lds, hipStream_t s);
+int launch_unpack(const LaunchArgs& a, int G, size_t lds, void* codes, void* ss, hipStream_t s);
 int launch_pack(const LaunchArgs& a, int G, size_t lds, const void* codes, const void* ss,
                 hipStream_t s);
-size_t decode_lds_bytes(int r_dec, int F);
 
 }  // namespace kvtc

@@ -38,10 +38,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 
 // ------------------------------------------------------------- helpers ---
 
@@ -78,10 +80,12 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
 
 // 8 bytes from any LDS byte address: three aligned dword reads and two
 // byte-aligns (the buffer is padded so the last read stays inside it).
+// The aligned address is formed as p minus its misalignment (not through an
+// integer round trip) so the compiler still sees an LDS pointer and emits
+// ds_read rather than a flat load, which would also wait for pending stores.
 __device__ __forceinline__ uint64_t lds_u64(const uint8_t* p) {
-  const uintptr_t a = (uintptr_t)p;
-  const uint32_t* b = (const uint32_t*)(a & ~(uintptr_t)3);
-  const uint32_t sh = (uint32_t)(a & 3u);
+  const uint32_t sh = (uint32_t)(uintptr_t)p & 3u;
+  const uint32_t* b = (const uint32_t*)(p - sh);
   const uint32_t w0 = b[0], w1 = b[1], w2 = b[2];
   const uint32_t lo = __builtin_amdgcn_alignbyte(w1, w0, sh);
   const uint32_t hi = __builtin_amdgcn_alignbyte(w2, w1, sh);
@@ -251,9 +255,54 @@ __device__ __forceinline__ void put_group(uint8_t* rec, const DevSlot& sl, int a
     lds_store_bytes(p, pack_codes(codes, 8, w), w);
     lds_store_bytes(p + w, pack_codes(codes + 8, 8, w), w);
   }
-  if (h == 0) {
-    const uint32_t s = __float_as_uint(shift), c = __float_as_uint(scale);
-    lds_store_bytes(rec + 8 * a, (uint64_t)s | ((uint64_t)c << 32), 8);
+  if (h == 0) {  // rec is 4-byte aligned (padded_stride)
+    ((uint32_t*)(rec + 8 * a))[0] = __float_as_uint(shift);
+    ((uint32_t*)(rec + 8 * a))[1] = __float_as_uint(scale);
+  }
+}
+
+// Copy n records of rb bytes from LDS rows of stride rbp into the contiguous
+// stream at dst (16-byte aligned): 16-byte stores gathered from 4-byte (rb %
+// 4 == 0) or 2-byte pieces, then a byte tail.
+__device__ void records_to_global(uint8_t* dst, const uint8_t* lds, uint32_t n, int rb, int rbp) {
+  const uint32_t total = n * (uint32_t)rb;
+  const uint32_t nv = total / 16;
+  const float inv = 1.0f / (float)rb;
+  auto locate = [&](uint32_t j, uint32_t& row, uint32_t& col) {
+    row = (uint32_t)((float)j * inv);
+    while (row * (uint32_t)rb > j) --row;
+    while ((row + 1) * (uint32_t)rb <= j) ++row;
+    col = j - row * (uint32_t)rb;
+  };
+  for (uint32_t v = threadIdx.x; v < nv; v += kThreads) {
+    uint32_t row, col;
+    locate(v * 16, row, col);
+    uint32_t w[4];
+    if ((rb & 3) == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w[i] = *(const uint32_t*)(lds + row * rbp + col);
+        col += 4;
+        if (col >= (uint32_t)rb) { col = 0; ++row; }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t lo = *(const uint16_t*)(lds + row * rbp + col);
+        col += 2;
+        if (col >= (uint32_t)rb) { col = 0; ++row; }
+        uint32_t hi = *(const uint16_t*)(lds + row * rbp + col);
+        col += 2;
+        if (col >= (uint32_t)rb) { col = 0; ++row; }
+        w[i] = lo | (hi << 16);
+      }
+    }
+    *(uint4*)(dst + (size_t)v * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  for (uint32_t j = nv * 16 + threadIdx.x; j < total; j += kThreads) {
+    uint32_t row, col;
+    locate(j, row, col);
+    dst[j] = lds[row * rbp + col];
   }
 }
 
@@ -409,7 +458,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
   // Quantize and pack. acc[b][i] holds component 32b + 8(i/4) + 4h + i%4 of
   // token tl; a group of G components is the item range
   // [(G/2) * sg, (G/2) * (sg + 1)) of block b with sg = a % (32/G).
-  uint8_t* rec = smem + (size_t)tl * rb;
+  const int rbp = padded_stride(rb);
+  uint8_t* rec = smem + (size_t)tl * rbp;
   constexpr int SUB = 32 / G;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -466,10 +516,18 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
   }
   __syncthreads();
   uint8_t* dst = (uint8_t*)jd.dst + record_base(jd, F, esz) + (size_t)t0 * rb;
-  lds_to_global(dst, smem, (size_t)n * rb);
+  records_to_global(dst, smem, n, rb, rbp);
 }
 
 // --------------------------------------------------------------- decode ---
+//
+// Decode runs in two kernels. Stage 1 (prep) turns each token's record into
+// the MFMA B operands of the reconstruction: the dequantized coefficients
+// c_hat / S_t as fp16, in MFMA lane order, with S_t a per-token power of two,
+// written to a staging buffer. Stage 2 (gemm) computes x_hat = S_t * (V' B) +
+// mu for every compressed row, a tall-skinny product whose cost is writing
+// the output. Dequantizing once per token in stage 1 keeps that work out of
+// stage 2, whose tiles each cover a slab of features.
 
 // Per-token power-of-two scale: S = 2^(e - 14) where 2^e <= max |c_hat| over
 // the token's groups < 2^(e+1), so the fp16 operand peaks in [2^14, 2^15).
@@ -481,306 +539,156 @@ __device__ __forceinline__ void token_scale(float m, float& S, float& Sinv) {
   Sinv = __uint_as_float((uint32_t)(127 + 14 - e) << 23);
 }
 
-// Dequantize 8 codes (one byte each in codes8) of a group of width w and
-// scale them by Sinv into packed fp16: c_hat = fma(q, fp32(scale / k), shift).
-__device__ __forceinline__ uint4 make_frag(uint64_t codes8, float shift, float scale, int w,
-                                           float Sinv) {
-  const float k = (float)((1 << w) - 1);
-  const float step = scale / k;
+// B fragment of 8 components of a group of width w from packed record bits
+// (code j at bits [j w, j w + w), LSB first): c_hat = shift + q * fp32(scale
+// / k), times the power of two Sinv, as packed fp16. Sinv is folded into the
+// fma operands; scaling by a power of two is exact, so the rounded results
+// are those of the unscaled fma times Sinv.
+__device__ __forceinline__ uint4 frag_from_bits(uint64_t bits, float shift, float scale, int w,
+                                                float Sinv) {
+  const float step = scale / (float)((1 << w) - 1) * Sinv;
+  const float sh = shift * Sinv;
+  const uint32_t mask = (1u << w) - 1u;
   uint32_t pk[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float q0 = (float)((codes8 >> (16 * j)) & 0xFFu);
-    const float q1 = (float)((codes8 >> (16 * j + 8)) & 0xFFu);
-    pk[j] = pack_f16x2(__builtin_fmaf(q0, step, shift) * Sinv, __builtin_fmaf(q1, step, shift) * Sinv);
+    const float q0 = (float)((uint32_t)(bits >> (2 * j * w)) & mask);
+    const float q1 = (float)((uint32_t)(bits >> ((2 * j + 1) * w)) & mask);
+    pk[j] = pack_f16x2(__builtin_fmaf(q0, step, sh), __builtin_fmaf(q1, step, sh));
   }
   return make_uint4(pk[0], pk[1], pk[2], pk[3]);
 }
 
-// 8 bytes from global memory at any byte address p inside [., end): three
-// aligned dword loads and two byte-aligns, or byte loads near the end so that
-// nothing past `end` is touched.
-__device__ __forceinline__ uint64_t gl_u64(const uint8_t* p, const uint8_t* end) {
-  const uintptr_t a = (uintptr_t)p;
-  if (p + 12 <= end) {
-    const uint32_t* b = (const uint32_t*)(a & ~(uintptr_t)3);
-    const uint32_t sh = (uint32_t)(a & 3u);
-    const uint32_t w0 = b[0], w1 = b[1], w2 = b[2];
-    return (uint64_t)__builtin_amdgcn_alignbyte(w1, w0, sh) |
-           ((uint64_t)__builtin_amdgcn_alignbyte(w2, w1, sh) << 32);
-  }
-  uint64_t v = 0;
-  for (int i = 0; i < 8 && p + i < end; ++i) v |= (uint64_t)p[i] << (8 * i);
-  return v;
+// Make this wave's LDS writes visible to its own lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Unpack the 8 codes of components [o, o + 8) of active group a from packed
-// bits (LSB first), one byte per code.
-__device__ __forceinline__ uint64_t spread_codes8(uint64_t bits, int w) {
-  const uint64_t mask = (1ull << w) - 1ull;
-  uint64_t out = 0;
+// Scatter 16-byte vector v (bytes [16v, 16v+16) of a contiguous run of
+// records of rb bytes) into LDS rows of stride rbp.
+__device__ __forceinline__ void scatter_vec(uint8_t* lds, uint32_t v, u32x4 x, int rb, int rbp,
+                                            float inv) {
+  uint32_t j = v * 16;
+  uint32_t row = (uint32_t)((float)j * inv);
+  while (row * (uint32_t)rb > j) --row;
+  while ((row + 1) * (uint32_t)rb <= j) ++row;
+  uint32_t col = j - row * (uint32_t)rb;
+  const uint32_t w[4] = {x[0], x[1], x[2], x[3]};
+  if ((rb & 3) == 0) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) out |= ((bits >> (j * w)) & mask) << (8 * j);
-  return out;
-}
-
-constexpr int kChatPad = 16;  // bytes of padding per LDS c_hat row
-
-// LDS bytes of a decode tile: the c_hat rows (reused for output staging),
-// the per-token scale words and the mean.
-__host__ __device__ inline size_t dec_lds_bytes(int r_dec, int F) {
-  const size_t chat = (size_t)kDecTile * (2 * r_dec + kChatPad);
-  const size_t outs = (size_t)4 * 32 * kOutRow;
-  return align_up(chat > outs ? chat : outs, 16) + 4 * kDecTile + 4 * (size_t)F;
-}
-
-// Compressed rows of one tile (128 tokens; wave w owns tokens 32w..32w+31).
-//  1. the mean goes to LDS; per token the scale S_t is the power of two
-//     above max |c_hat| (LDS atomicMax over its groups);
-//  2. cooperative dequantization: one thread per (token, 8 components)
-//     writes c_hat / S_t as fp16 into LDS; codes come straight from the
-//     stream's records (fused) or the staging buffer (two-stage);
-//  3. each lane loads its token's KS B fragments from LDS;
-//  4. per 32-feature block, KS MFMAs D[feature][token] = V' c_hat^T with the
-//     basis fragments of the next block already in flight (two register
-//     sets, no copies), then S_t * D + mu, staged through LDS so that stores
-//     are 16-byte lanes over 128-byte row segments.
-template <int KS, bool OUT32, bool STAGED>
-__device__ void restore_tile(const LaunchArgs& a, const JobDesc& jd, const DevSlot& sl,
-                             uint8_t* smem, uint32_t t0, uint32_t n, int* bad) {
-  const int F = a.F;
-  const int r_eff = sl.r_eff, r_dec = sl.r_dec, n_act = sl.n_act, G = sl.G;
-  const int rb = sl.record_bytes;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = lane >> 5;
-  const int tl = wave * 32 + (lane & 31);
-  const size_t chat_stride = 2 * (size_t)r_dec + kChatPad;
-  const size_t chat_bytes = align_up(max((size_t)kDecTile * chat_stride, (size_t)4 * 32 * kOutRow), 16);
-  uint8_t* chat = smem;
-  uint32_t* sbits = (uint32_t*)(smem + chat_bytes);
-  float* mu_l = (float*)(sbits + kDecTile);
-  const float4* mu_g = (const float4*)(a.state + sl.mu_off);
-  for (int i = threadIdx.x; i < F / 4; i += kThreads) ((float4*)mu_l)[i] = mu_g[i];
-  if (threadIdx.x < kDecTile) sbits[threadIdx.x] = 0u;
-
-  // Code sources.
-  const int esz = a.dtype == KVTC_F32 ? 4 : 2;
-  const uint8_t* recs = nullptr;
-  const uint8_t* rec_end = nullptr;
-  const uint8_t* scodes = nullptr;
-  const float2* sss = nullptr;
-  if (STAGED) {
-    const uint8_t* st = (const uint8_t*)jd.staging;
-    scodes = st + (size_t)t0 * r_eff;
-    sss = (const float2*)(st + align_up((size_t)jd.tc * r_eff, kAlign)) + (size_t)t0 * n_act;
+    for (int i = 0; i < 4; ++i) {
+      *(uint32_t*)(lds + row * rbp + col) = w[i];
+      col += 4;
+      if (col >= (uint32_t)rb) { col = 0; ++row; }
+    }
   } else {
-    const uint8_t* base = (const uint8_t*)jd.src + record_base(jd, F, esz);
-    recs = base + (size_t)t0 * rb;
-    rec_end = base + (size_t)jd.tc * rb;
-  }
-  auto ss_of = [&](int t, int g) -> float2 {
-    if (STAGED) return sss[(size_t)t * n_act + g];
-    const uint64_t raw = gl_u64(recs + (size_t)t * rb + 8 * g, rec_end);
-    return make_float2(__uint_as_float((uint32_t)raw), __uint_as_float((uint32_t)(raw >> 32)));
-  };
-  __syncthreads();
-  // 1. per-token scales (max over groups; non-negative floats order as ints)
-  for (int i = threadIdx.x; i < (int)n * n_act; i += kThreads) {
-    const int t = i / n_act, g = i - t * n_act;
-    const float2 p = ss_of(t, g);
-    const float m = fmaxf(fabsf(p.x), fabsf(p.x + p.y));
-    atomicMax(&sbits[t], __float_as_uint(m));
-  }
-  __syncthreads();
-  // 2. c_hat / S_t in fp16, 8 components per item
-  const int c8n = r_dec / 8;
-  for (int i = threadIdx.x; i < (int)n * c8n; i += kThreads) {
-    const int t = i / c8n, c = (i - t * c8n) * 8;
-    uint4 frag = make_uint4(0u, 0u, 0u, 0u);
-    if (c < r_eff) {
-      float S, Sinv;
-      token_scale(__uint_as_float(sbits[t]), S, Sinv);
-      const int ag = c / G, o = c - ag * G;
-      const int w = sl.width[ag];
-      uint64_t codes8;
-      if (STAGED)
-        codes8 = *(const uint64_t*)(scodes + (size_t)t * r_eff + c);
-      else
-        codes8 = spread_codes8(gl_u64(recs + (size_t)t * rb + sl.chunk_off[ag] + (o * w) / 8, rec_end), w);
-      const float2 p = ss_of(t, ag);
-      frag = make_frag(codes8, p.x, p.y, w, Sinv);
-    }
-    *(uint4*)(chat + (size_t)t * chat_stride + 2 * c) = frag;
-  }
-  __syncthreads();
-  // 3. this lane's B fragments and token scale
-  uint4 bfr[KS > 0 ? KS : 1];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) bfr[s] = *(const uint4*)(chat + (size_t)tl * chat_stride + 2 * (16 * s + 8 * h));
-  float S, Sinv;
-  token_scale(__uint_as_float(sbits[tl]), S, Sinv);
-  __syncthreads();  // the c_hat region becomes the output staging area
+    for (int i = 0; i < 4; ++i) {
+      *(uint16_t*)(lds + row * rbp + col) = (uint16_t)w[i];
+      col += 2;
+      if (col >= (uint32_t)rb) { col = 0; ++row; }
+      *(uint16_t*)(lds + row * rbp + col) = (uint16_t)(w[i] >> 16);
+      col += 2;
+      if (col >= (uint32_t)rb) { col = 0; ++row; }
+    }
+  }
+}
 
-  // Store rows of this lane: row r = 8 * it + lane / 8 of the wave's 32
-  // tokens, 16 bytes at column (lane % 8) * 16 of a 128-byte segment.
-  constexpr int OSZ = OUT32 ? 4 : 2;
-  constexpr int FPG = 128 / (32 * OSZ);               // feature blocks per 128-byte segment
-  const int c16 = lane & 7;
-  long orow_off[4];
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int r = 8 * it + (lane >> 3);
-    orow_off[it] = -1;
-    if ((uint32_t)(wave * 32 + r) < n) {
-      const long orow = out_row(jd, jd.s1 + t0 + wave * 32 + r);
-      if (orow < 0)
-        *bad = 1;
-      else
-        orow_off[it] = orow * (long)F * OSZ + c16 * 16;
-    }
-  }
-  uint8_t* wout = smem + (size_t)wave * 32 * kOutRow;
-  uint8_t* dst = (uint8_t*)jd.dst;
-  const uint16_t* vrow = (const uint16_t*)(a.state + sl.vdec_off) + (size_t)(lane & 31) * r_dec + 8 * h;
-  const size_t fb_stride = (size_t)32 * r_dec;        // elements per 32-feature block
-
-  uint4 A0[KS > 0 ? KS : 1], A1[KS > 0 ? KS : 1];
-  auto load_a = [&](int fb, uint4* A) {
-#pragma unroll
-    for (int s = 0; s < KS; ++s) A[s] = *(const uint4*)(vrow + fb * fb_stride + 16 * s);
-  };
-  auto block = [&](int fb, const uint4* A, int u) {
-    f32x16 acc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, A[s]),
-                                                   __builtin_bit_cast(f16x8, bfr[s]), acc, 0, 0, 0);
-    // D[feature][token]: lane holds token (lane & 31), features
-    // fb*32 + 8*qd + 4*h + {0..3} in acc[4*qd .. 4*qd+3].
-    uint8_t* orow_l = wout + (size_t)(lane & 31) * kOutRow + u * 32 * OSZ;
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const int f = fb * 32 + 8 * qd + 4 * h;
-      const float4 m4 = *(const float4*)(mu_l + f);
-      const float o0 = __builtin_fmaf(acc[4 * qd + 0], S, m4.x);
-      const float o1 = __builtin_fmaf(acc[4 * qd + 1], S, m4.y);
-      const float o2 = __builtin_fmaf(acc[4 * qd + 2], S, m4.z);
-      const float o3 = __builtin_fmaf(acc[4 * qd + 3], S, m4.w);
-      const int col = (8 * qd + 4 * h) * OSZ;
-      if (OUT32)
-        *(float4*)(orow_l + col) = make_float4(o0, o1, o2, o3);
-      else
-        *(uint2*)(orow_l + col) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-    }
-  };
-  auto store_segment = [&](int fb0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      if (orow_off[it] >= 0) {
-        const uint4 v = *(const uint4*)(wout + (size_t)(8 * it + (lane >> 3)) * kOutRow + c16 * 16);
-        *(uint4*)(dst + orow_off[it] + (size_t)fb0 * 32 * OSZ) = v;
+// Stage 1: header check, passthrough rows, and for kPrepTok compressed
+// tokens per tile: records -> LDS rows (stride padded_stride(rb)) -> one wave
+// per block of kDecTok tokens builds the B operands and token scales of its
+// block and writes them to the staging buffer (stg_block_bytes(KS) per block).
+template <int KS>
+__global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int flag;
+  const uint32_t tile = logical_tile();
+  if (tile >= a.total_tiles) return;
+  const int j = find_job(a, tile);
+  const JobDesc& jd = a.jobs[j];
+  const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
+  const uint32_t lt = tile - jd.tile_begin;
+  if (threadIdx.x == 0) flag = check_header(a, jd, sl);
+  __syncthreads();
+  const int st = flag;
+  if (lt == 0 && threadIdx.x == 0) set_status(a, jd.status_idx, st);
+  if (st != KVTC_OK) return;
+  __syncthreads();
+  if (threadIdx.x == 0) flag = 0;
+  __syncthreads();
+  int bad = 0;
+  if (lt >= jd.n_ctiles) {
+    bad = !decode_passthrough(a, jd, lt - jd.n_ctiles);
+  } else {
+    constexpr int KA = KS > 0 ? KS : 1;
+    const uint32_t t0 = lt * kPrepTok;
+    const uint32_t n = min((uint32_t)kPrepTok, jd.tc - t0);
+    const int r_eff = sl.r_eff, G = sl.G;
+    const int rb = sl.record_bytes, rbp = padded_stride(rb);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = lane & 31, h = lane >> 5;
+    if (KS > 0) {
+      const int esz = a.dtype == KVTC_F32 ? 4 : 2;
+      const uint8_t* src = (const uint8_t*)jd.src + record_base(jd, a.F, esz) + (size_t)t0 * rb;
+      const uint32_t total = n * rb, nvv = total / 16;
+      const float inv_rb = 1.0f / (float)rb;
+      for (uint32_t v = threadIdx.x; v < nvv; v += kThreads)
+        scatter_vec(smem, v, *(const u32x4*)(src + (size_t)v * 16), rb, rbp, inv_rb);
+      for (uint32_t q = nvv * 16 + threadIdx.x; q < total; q += kThreads) {   // ragged end
+        const uint32_t row = q / (uint32_t)rb;
+        smem[row * rbp + (q - row * (uint32_t)rb)] = src[q];
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  };
-
-  // F/32 is even (F is a multiple of 64): feature blocks go in pairs with
-  // ping-pong basis registers.
-  const int nfb = F / 32;
-  load_a(0, A0);
-  for (int fb = 0; fb < nfb; fb += 2) {
-    load_a(fb + 1, A1);
-    block(fb, A0, OUT32 ? 0 : 0);
-    if (OUT32) store_segment(fb);
-    if (fb + 2 < nfb) load_a(fb + 2, A0);
-    block(fb + 1, A1, OUT32 ? 0 : 1);
-    store_segment(OUT32 ? fb + 1 : fb);
-  }
-}
-
-// Fused decode: header check, passthrough tiles and compressed tiles.
-template <int KS, bool OUT32>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const LaunchArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int flag;
-  const uint32_t tile = logical_tile();
-  if (tile >= a.total_tiles) return;
-  const int j = find_job(a, tile);
-  const JobDesc& jd = a.jobs[j];
-  const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
-  const uint32_t lt = tile - jd.tile_begin;
-  if (threadIdx.x == 0) flag = check_header(a, jd, sl);
-  __syncthreads();
-  const int st = flag;
-  if (lt == 0 && threadIdx.x == 0) set_status(a, jd.status_idx, st);
-  if (st != KVTC_OK) return;
-  __syncthreads();
-  if (threadIdx.x == 0) flag = 0;
-  __syncthreads();
-  int bad = 0;
-  if (lt >= jd.n_ctiles) {
-    bad = !decode_passthrough(a, jd, lt - jd.n_ctiles);
-  } else {
-    const uint32_t t0 = lt * kDecTile;
-    const uint32_t n = min((uint32_t)kDecTile, jd.tc - t0);
-    restore_tile<KS, OUT32, false>(a, jd, sl, smem, t0, n, &bad);
-  }
-  if (bad) atomicExch(&flag, 1);
-  __syncthreads();
-  if (threadIdx.x == 0 && flag) set_status(a, jd.status_idx, KVTC_E_INVALID);
-}
-
-// Stage 1: header check, passthrough rows, records -> staging codes/scales.
-template <int G>
-__global__ __launch_bounds__(kThreads) void unpack_kernel(const LaunchArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int flag;
-  const uint32_t tile = logical_tile();
-  if (tile >= a.total_tiles) return;
-  const int j = find_job(a, tile);
-  const JobDesc& jd = a.jobs[j];
-  const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
-  const uint32_t lt = tile - jd.tile_begin;
-  if (threadIdx.x == 0) flag = check_header(a, jd, sl);
-  __syncthreads();
-  const int st = flag;
-  if (lt == 0 && threadIdx.x == 0) set_status(a, jd.status_idx, st);
-  if (st != KVTC_OK) return;
-  __syncthreads();
-  if (threadIdx.x == 0) flag = 0;
-  __syncthreads();
-  int bad = 0;
-  if (lt >= jd.n_ctiles) {
-    bad = !decode_passthrough(a, jd, lt - jd.n_ctiles);
-  } else if (sl.r_eff > 0) {
-    const uint32_t t0 = lt * kUnpackTile;
-    const uint32_t n = min((uint32_t)kUnpackTile, jd.tc - t0);
-    const int esz = a.dtype == KVTC_F32 ? 4 : 2;
-    const int rb = sl.record_bytes;
-    const uint8_t* recs = (const uint8_t*)jd.src + record_base(jd, a.F, esz) + (size_t)t0 * rb;
-    stage_to_lds(smem, recs, (size_t)n * rb);
     __syncthreads();
-    uint8_t* st8 = (uint8_t*)jd.staging;
-    float2* ssg = (float2*)(st8 + align_up((size_t)jd.tc * sl.r_eff, kAlign));
-    // One thread per (token, 8-component chunk).
-    const int chunks = sl.r_eff / 8;
-    for (int idx = threadIdx.x; idx < (int)n * chunks; idx += kThreads) {
-      const int tl = idx / chunks, c = (idx % chunks) * 8;
-      const uint8_t* rec = smem + (size_t)tl * rb;
-      const int ag = c / G, o = c % G;
-      *(uint64_t*)(st8 + (size_t)(t0 + tl) * sl.r_eff + c) = get_codes8(rec, sl, ag, o);
-      if (o == 0) {
-        const uint64_t raw = lds_u64(rec + 8 * ag);
-        ssg[(size_t)(t0 + tl) * sl.n_act + ag] =
-            make_float2(__uint_as_float((uint32_t)raw), __uint_as_float((uint32_t)(raw >> 32)));
+    const uint32_t tb = t0 / kDecTok + wave;               // this wave's token block
+    if ((uint32_t)wave * kDecTok < n) {
+      const uint32_t nt = min((uint32_t)kDecTok, n - wave * kDecTok);
+      const bool tok_ok = (uint32_t)t < nt;
+      const uint8_t* r = smem + (wave * kDecTok + (tok_ok ? t : 0)) * rbp;
+      // K-step s: components c = 16 s + 8 h of active group ag, w-bit codes
+      // at byte off of the record; (shift, scale) at byte 8 ag.
+      int w_s[KA], off_s[KA], ag_s[KA];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int c = 16 * s + 8 * h;
+        w_s[s] = 0;
+        off_s[s] = 0;
+        ag_s[s] = 0;
+        if (c < r_eff) {
+          const int ag = c / G, o = c - ag * G;
+          ag_s[s] = ag;
+          w_s[s] = sl.width[ag];
+          off_s[s] = sl.chunk_off[ag] + (o * w_s[s]) / 8;
+        }
       }
+      auto shift_scale = [&](int s) -> float2 {
+        const uint32_t* q = (const uint32_t*)(r + 8 * ag_s[s]);   // rows are 4-byte aligned
+        return make_float2(__uint_as_float(q[0]), __uint_as_float(q[1]));
+      };
+      // Every active group has a component among this lane's K-steps, so
+      // both lanes of a token see the same maximum.
+      float m = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (w_s[s]) {
+          const float2 p = shift_scale(s);
+          m = fmaxf(m, fmaxf(fabsf(p.x), fabsf(p.x + p.y)));
+        }
+      }
+      float S, Sinv;
+      token_scale(m, S, Sinv);
+      uint8_t* blk = (uint8_t*)jd.staging + (size_t)tb * stg_block_bytes(KS);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        uint4 f = make_uint4(0u, 0u, 0u, 0u);
+        if (tok_ok && w_s[s]) {
+          const float2 p = shift_scale(s);
+          f = frag_from_bits(lds_u64(r + off_s[s]), p.x, p.y, w_s[s], Sinv);
+        }
+        *(uint4*)(blk + s * 1024 + lane * 16) = f;
+      }
+      if (h == 0) *(float*)(blk + KS * 1024 + t * 4) = tok_ok ? S : 1.f;
     }
   }
   if (bad) atomicExch(&flag, 1);
@@ -788,9 +696,24 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const LaunchArgs a) {
   if (threadIdx.x == 0 && flag) set_status(a, jd.status_idx, KVTC_E_INVALID);
 }
 
-// Stage 2: staging -> compressed output rows.
+// Stage 2: one tile is features [f0, f0 + FS) x compressed tokens
+// [t0, t0 + kGemmTok) of one job. The slab of V' (fp16, FS rows of r_dec,
+// padded by 16 bytes per row) and mu stay in LDS; each wave then runs on its
+// own over blocks of kDecTok tokens: it loads the block's B operands and
+// scales (the next block's are in flight meanwhile), runs FS / 32 x KS
+// MFMAs D[feature][token], forms S_t * D + mu and stores it through its LDS
+// staging rows as 128-byte segments. Every store is issued (rows past the
+// tile, or with a bad block table entry, go to the workspace sink), so the
+// number of memory operations per block is fixed and the wait for the next
+// block's operands never covers this block's stores.
 template <int KS, bool OUT32>
-__global__ __launch_bounds__(kThreads) void restore_kernel(const LaunchArgs a) {
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const LaunchArgs a) {
+  constexpr int FS = gemm_features(KS);
+  constexpr int NFB = FS / 32;
+  constexpr int OSZ = OUT32 ? 4 : 2;
+  constexpr int BPS = 128 / (32 * OSZ);           // feature blocks per 128-byte segment
+  constexpr int KA = KS > 0 ? KS : 1;
+  constexpr int AST = KS * 32 + 16;               // LDS bytes per V' row
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int flag;
   const uint32_t tile = logical_tile();
@@ -800,15 +723,157 @@ __global__ __launch_bounds__(kThreads) void restore_kernel(const LaunchArgs a) {
   const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
   const uint32_t lt = tile - jd.tile_begin;
   if (prior_rank(a, jd.status_idx) != 0 || lt >= jd.n_ctiles) return;  // stage 1 rejected it
-  if (threadIdx.x == 0) flag = 0;
+  const int F = a.F;
+  const uint32_t n_slab = (uint32_t)(F + FS - 1) / FS;
+  const int f0 = (int)(lt % n_slab) * FS;
+  const uint32_t t0 = (lt / n_slab) * kGemmTok;
+  const uint32_t n_ch = (min((uint32_t)kGemmTok, jd.tc - t0) + kDecTok - 1) / kDecTok;
+  const int lane = threadIdx.x & 63, h = lane >> 5, c16 = lane & 7;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+
+  uint8_t* As = smem;
+  float* mu_s = (float*)(smem + FS * AST);
+  uint8_t* stg = smem + FS * AST + FS * 4 + wave * kDecTok * kOutRow;
+  {
+    const int r_dec = sl.r_dec;
+    const uint8_t* vdec = a.state + sl.vdec_off;
+    for (int i = threadIdx.x; i < FS * 2 * KS; i += kThreads) {
+      const int row = i / (2 * KS), c = i - row * (2 * KS);
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (f0 + row < F) v = *(const uint4*)(vdec + ((size_t)(f0 + row) * r_dec + 8 * c) * 2);
+      *(uint4*)(As + row * AST + 16 * c) = v;
+    }
+    const float* mu = (const float*)(a.state + sl.mu_off);
+    for (int i = threadIdx.x; i < FS; i += kThreads) mu_s[i] = f0 + i < F ? mu[f0 + i] : 0.f;
+    if (threadIdx.x == 0) flag = 0;
+  }
   __syncthreads();
+
+  const uint8_t* stg_job = (const uint8_t*)jd.staging;
+  constexpr size_t BB = stg_block_bytes(KS);
+  const uint32_t tb0 = t0 / kDecTok;
+  uint8_t* dst = (uint8_t*)jd.dst;
+  uint8_t* sink = a.sink + c16 * 16;
   int bad = 0;
-  const uint32_t t0 = lt * kDecTile;
-  const uint32_t n = min((uint32_t)kDecTile, jd.tc - t0);
-  restore_tile<KS, OUT32, true>(a, jd, sl, smem, t0, n, &bad);
+
+  // Operands of block c: B fragments, the lane's token scale and the block
+  // table entries of the rows this lane stores (r = 8 it + lane / 8).
+  uint4 Bn[KA];
+  float Sn;
+  int btn[4];
+  auto fetch = [&](uint32_t c) {
+    const uint8_t* blk = stg_job + (size_t)(tb0 + c) * BB;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) Bn[s] = *(const uint4*)(blk + s * 1024 + lane * 16);
+    Sn = *(const float*)(blk + KS * 1024 + (lane & 31) * 4);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const uint32_t tok = min(t0 + c * kDecTok + 8 * it + (lane >> 3), jd.tc - 1);
+      btn[it] = jd.block_table[(jd.s1 + tok) / (uint32_t)jd.block_size];
+    }
+  };
+  // Operands in use: B fragments, token scale and the store addresses of
+  // the lane's rows; taken over from the fetched ones only after the
+  // block's stores were issued, so every wait covers loads alone.
+  uint4 B[KA];
+  float S;
+  uint8_t* dp[4];
+  auto take = [&](uint32_t c) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) B[s] = Bn[s];
+    S = Sn;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const uint32_t tok = t0 + c * kDecTok + 8 * it + (lane >> 3);
+      const uint32_t tt = jd.s1 + tok;
+      const int bt = btn[it];
+      const bool blk_ok = bt >= 0 && bt < jd.n_blocks;
+      bad |= (int)(tok < jd.tc && !blk_ok);
+      const long row = (long)bt * jd.block_size + (long)(tt % (uint32_t)jd.block_size);
+      dp[it] = tok < jd.tc && blk_ok ? dst + (row * F + f0) * OSZ + c16 * 16 : sink;
+    }
+  };
+  if ((uint32_t)wave < n_ch) {
+    fetch(wave);
+    take(wave);
+  }
+  for (uint32_t c = wave; c < n_ch; c += kWaves) {
+    fetch(min(c + kWaves, n_ch - 1));   // unconditional: a fixed count of loads per block
+#pragma unroll
+    for (int fb = 0; fb < NFB; ++fb) {
+      const uint8_t* arow = As + (fb * 32 + (lane & 31)) * AST + 16 * h;
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, *(const uint4*)(arow + 32 * s)),
+                                                     __builtin_bit_cast(f16x8, B[s]), acc, 0, 0, 0);
+      // D[feature][token]: token lane % 32, features 8 qd + 4 h + {0..3}
+      uint8_t* srow = stg + (lane & 31) * kOutRow + (fb % BPS) * 32 * OSZ;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int fl = 8 * qd + 4 * h;
+        const float4 m4 = *(const float4*)(mu_s + 32 * fb + fl);
+        const float o0 = __builtin_fmaf(acc[4 * qd + 0], S, m4.x);
+        const float o1 = __builtin_fmaf(acc[4 * qd + 1], S, m4.y);
+        const float o2 = __builtin_fmaf(acc[4 * qd + 2], S, m4.z);
+        const float o3 = __builtin_fmaf(acc[4 * qd + 3], S, m4.w);
+        if (OUT32)
+          *(float4*)(srow + fl * 4) = make_float4(o0, o1, o2, o3);
+        else
+          *(uint2*)(srow + fl * 2) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+      }
+      if (fb % BPS == BPS - 1) {
+        const int fs = 32 * (fb - BPS + 1);            // segment's first feature in the slab
+        const bool in_f = f0 + fs < F;                 // F % 64 == 0: whole segments
+        wave_lds_sync();
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const uint4 v = *(const uint4*)(stg + (8 * it + (lane >> 3)) * kOutRow + c16 * 16);
+          *(uint4*)(dp[it] == sink || !in_f ? sink : dp[it] + fs * OSZ) = v;
+        }
+        wave_lds_sync();
+      }
+    }
+    take(min(c + kWaves, n_ch - 1));
+  }
   if (bad) atomicExch(&flag, 1);
   __syncthreads();
   if (threadIdx.x == 0 && flag) set_status(a, jd.status_idx, KVTC_E_INVALID);
+}
+
+// Test hook: records -> codes (u8, one per component) and (shift, scale)
+// pairs, the unpacking half of stage 1 on its own.
+template <int G>
+__global__ __launch_bounds__(kThreads) void unpack_kernel(const LaunchArgs a, uint8_t* codes, float2* ssg) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t tile = logical_tile();
+  if (tile >= a.total_tiles) return;
+  const JobDesc& jd = a.jobs[0];
+  const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
+  const uint32_t lt = tile - jd.tile_begin;
+  if (lt >= jd.n_ctiles || sl.r_eff == 0) return;
+  const uint32_t t0 = lt * kUnpackTile;
+  const uint32_t n = min((uint32_t)kUnpackTile, jd.tc - t0);
+  const int esz = a.dtype == KVTC_F32 ? 4 : 2;
+  const int rb = sl.record_bytes;
+  const uint8_t* recs = (const uint8_t*)jd.src + record_base(jd, a.F, esz) + (size_t)t0 * rb;
+  stage_to_lds(smem, recs, (size_t)n * rb);
+  __syncthreads();
+  // One thread per (token, 8-component chunk).
+  const int chunks = sl.r_eff / 8;
+  for (int idx = threadIdx.x; idx < (int)n * chunks; idx += kThreads) {
+    const int tl = idx / chunks, c = (idx % chunks) * 8;
+    const uint8_t* rec = smem + (size_t)tl * rb;
+    const int ag = c / G, o = c % G;
+    *(uint64_t*)(codes + (size_t)(t0 + tl) * sl.r_eff + c) = get_codes8(rec, sl, ag, o);
+    if (o == 0) {
+      const uint64_t raw = lds_u64(rec + 8 * ag);
+      ssg[(size_t)(t0 + tl) * sl.n_act + ag] =
+          make_float2(__uint_as_float((uint32_t)raw), __uint_as_float((uint32_t)(raw >> 32)));
+    }
+  }
 }
 
 // Test hook: stream from given codes and (shift, scale) pairs, through the
@@ -839,17 +904,18 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const LaunchArgs a, cons
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5;
   const int tl = wave * 32 + (lane & 31);
+  const int rbp = padded_stride(rb);
   if ((uint32_t)tl < n) {
     const uint32_t t = t0 + tl;
     for (int ag = 0; ag < sl.n_act; ++ag) {
       uint32_t cv[G / 2];
       for (int i = 0; i < G / 2; ++i) cv[i] = codes[(size_t)t * sl.r_eff + ag * G + h * (G / 2) + i];
       const float2 p = ss[(size_t)t * sl.n_act + ag];
-      put_group<G>(smem + (size_t)tl * rb, sl, ag, h, cv, p.x, p.y);
+      put_group<G>(smem + (size_t)tl * rbp, sl, ag, h, cv, p.x, p.y);
     }
   }
   __syncthreads();
-  lds_to_global((uint8_t*)jd.dst + record_base(jd, a.F, esz) + (size_t)t0 * rb, smem, (size_t)n * rb);
+  records_to_global((uint8_t*)jd.dst + record_base(jd, a.F, esz) + (size_t)t0 * rb, smem, n, rb, rbp);
 }
 
 // ------------------------------------------------------------- launchers ---
@@ -887,55 +953,60 @@ int launch_encode(const LaunchArgs& a, int nb, int G, size_t lds, hipStream_t s)
   return (int)hipErrorInvalidValue;
 }
 
-size_t decode_lds_bytes(int r_dec, int F) { return dec_lds_bytes(r_dec, F); }
-
 // Decode launches take the exact K-step count ks = r_dec / 16 of every job
 // in the batch (the host groups jobs by it).
-template <bool OUT32>
-static int launch_decode_o(const LaunchArgs& a, int ks, size_t lds, bool staged, hipStream_t s) {
+#define KVTC_KS_CASES(X)                                                          \
+  X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) \
+  X(15) X(16)
+
+int launch_prep(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
   const dim3 g = grid_for(a.total_tiles);
-#define KVTC_DEC(KV)                                                                 \
-  case KV:                                                                           \
-    if (staged) {                                                                    \
-      allow_lds(restore_kernel<KV, OUT32>, lds);                                     \
-      hipLaunchKernelGGL((restore_kernel<KV, OUT32>), g, dim3(kThreads), lds, s, a); \
-    } else {                                                                         \
-      allow_lds(decode_kernel<KV, OUT32>, lds);                                      \
-      hipLaunchKernelGGL((decode_kernel<KV, OUT32>), g, dim3(kThreads), lds, s, a);  \
-    }                                                                                \
+#define KVTC_PREP(KV)                                                       \
+  case KV:                                                                  \
+    allow_lds(prep_kernel<KV>, lds);                                        \
+    hipLaunchKernelGGL((prep_kernel<KV>), g, dim3(kThreads), lds, s, a);    \
     break;
   switch (ks) {
-    KVTC_DEC(0) KVTC_DEC(1) KVTC_DEC(2) KVTC_DEC(3) KVTC_DEC(4) KVTC_DEC(5) KVTC_DEC(6)
-    KVTC_DEC(7) KVTC_DEC(8) KVTC_DEC(9) KVTC_DEC(10) KVTC_DEC(11) KVTC_DEC(12) KVTC_DEC(13)
-    KVTC_DEC(14) KVTC_DEC(15) KVTC_DEC(16)
+    KVTC_KS_CASES(KVTC_PREP)
     default:
       return (int)hipErrorInvalidValue;
   }
-#undef KVTC_DEC
+#undef KVTC_PREP
   return (int)hipGetLastError();
 }
 
-int launch_decode(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
-  return a.out_dtype == KVTC_F32 ? launch_decode_o<true>(a, ks, lds, false, s)
-                                 : launch_decode_o<false>(a, ks, lds, false, s);
+template <bool OUT32>
+static int launch_gemm_o(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
+  const dim3 g = grid_for(a.total_tiles);
+#define KVTC_GEMM(KV)                                                            \
+  case KV:                                                                       \
+    allow_lds(gemm_kernel<KV, OUT32>, lds);                                      \
+    hipLaunchKernelGGL((gemm_kernel<KV, OUT32>), g, dim3(kThreads), lds, s, a);  \
+    break;
+  switch (ks) {
+    KVTC_KS_CASES(KVTC_GEMM)
+    default:
+      return (int)hipErrorInvalidValue;
+  }
+#undef KVTC_GEMM
+  return (int)hipGetLastError();
 }
 
-int launch_restore(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
-  return a.out_dtype == KVTC_F32 ? launch_decode_o<true>(a, ks, lds, true, s)
-                                 : launch_decode_o<false>(a, ks, lds, true, s);
+int launch_gemm(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
+  return a.out_dtype == KVTC_F32 ? launch_gemm_o<true>(a, ks, lds, s) : launch_gemm_o<false>(a, ks, lds, s);
 }
 
-int launch_unpack(const LaunchArgs& a, int G, size_t lds, hipStream_t s) {
+int launch_unpack(const LaunchArgs& a, int G, size_t lds, void* codes, void* ss, hipStream_t s) {
   const dim3 g = grid_for(a.total_tiles);
   if (G == 16) {
     allow_lds(unpack_kernel<16>, lds);
-    hipLaunchKernelGGL((unpack_kernel<16>), g, dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((unpack_kernel<16>), g, dim3(kThreads), lds, s, a, (uint8_t*)codes, (float2*)ss);
   } else if (G == 32) {
     allow_lds(unpack_kernel<32>, lds);
-    hipLaunchKernelGGL((unpack_kernel<32>), g, dim3(kThreads), lds, s, a);
-  }
-  else
+    hipLaunchKernelGGL((unpack_kernel<32>), g, dim3(kThreads), lds, s, a, (uint8_t*)codes, (float2*)ss);
+  } else {
     return (int)hipErrorInvalidValue;
+  }
   return (int)hipGetLastError();
 }
 

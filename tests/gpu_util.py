@@ -102,11 +102,19 @@ class DevCodec:
             stg = torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV)
             self.codec.decode_unpack(jobs, out_dtype, stg, stg.numel(), self.ws, s)
             self.codec.decode_restore(jobs, out_dtype, stg, stg.numel(), self.ws, s)
+            st = self.status(len(jobs))
         else:
-            self.codec.decode(jobs, out_dtype, self.ws, s)
-        st = self.status(len(jobs))
+            st = self.decode_jobs(jobs, out_dtype)
         torch.cuda.synchronize()
         return outs, st
+
+    def decode_jobs(self, jobs, out_dtype):
+        """Fused decode of prepared jobs with a workspace of its own; returns the status."""
+        s = torch.cuda.current_stream()
+        n = self.codec.decode_workspace_bytes(jobs)
+        dws = torch.zeros((n + 3) // 4, dtype=torch.int32, device=DEV)
+        self.codec.decode(jobs, out_dtype, dws, n, s)
+        return K.kvtc_read_device_status(dws, len(jobs), s)
 
 
 def bf16_out_to_f64(t: torch.Tensor) -> np.ndarray:

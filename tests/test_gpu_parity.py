@@ -155,15 +155,13 @@ def test_pack_unpack_bit_exact(case):
     out = torch.zeros((T, op.F), dtype=torch.int16 if op.dtype == O.DTYPE_BF16 else torch.float32,
                       device=DEV)
     djob = K.make_job(l, k, T, src, out, out.numel() * out.element_size())
-    nst = dc.codec.staging_bytes([djob])
-    stg = torch.zeros(nst, dtype=torch.uint8, device=DEV)
-    dc.codec.decode_unpack([djob], op.dtype, stg, nst, dc.ws, torch.cuda.current_stream())
-    assert np.all(dc.status(1) == 0)
-    h = stg.cpu().numpy()
     tc = ref.codes.shape[0]
-    got_codes = h[: tc * slot.r_eff].reshape(tc, slot.r_eff)
-    off = (tc * slot.r_eff + 255) // 256 * 256
-    got_ss = h[off: off + tc * slot.n_act * 8].view(np.float32).reshape(tc, slot.n_act, 2)
+    gc = torch.full((max(tc * slot.r_eff, 1),), 0xEE, dtype=torch.uint8, device=DEV)
+    gs = torch.full((max(tc * slot.n_act * 2, 1),), -1.0, dtype=torch.float32, device=DEV)
+    dc.codec.unpack(djob, gc, gs, dc.ws, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    got_codes = gc.cpu().numpy()[: tc * slot.r_eff].reshape(tc, slot.r_eff)
+    got_ss = gs.cpu().numpy()[: tc * slot.n_act * 2].reshape(tc, slot.n_act, 2)
     assert np.array_equal(got_codes, ref.codes)                      # T1 unpack
     assert np.array_equal(got_ss[:, :, 0].view(np.uint32), ref.shift.view(np.uint32))
     assert np.array_equal(got_ss[:, :, 1].view(np.uint32), ref.scale.view(np.uint32))
@@ -379,11 +377,11 @@ def test_two_stream_layer_pipeline_matches_fused():
         fused_jobs.append(K.make_job(l, k, T, srcs[i], pool_f, nbytes, tables[i], bs, pool_blocks))
         pipe_jobs[l].append(K.make_job(l, k, T, srcs[i], pool_p, nbytes, tables[i], bs, pool_blocks))
     s = torch.cuda.current_stream()
-    dc.codec.decode(fused_jobs, K.KVTC_BF16, dc.ws, s)
-    assert np.all(dc.status(len(fused_jobs)) == 0)
+    assert np.all(dc.decode_jobs(fused_jobs, K.KVTC_BF16) == 0)
     nst = max(dc.codec.staging_bytes(js) for js in pipe_jobs.values())
     stg = [torch.zeros(nst, dtype=torch.uint8, device=DEV) for _ in range(2)]
-    wss = [torch.zeros(64, dtype=torch.int32, device=DEV) for _ in range(2)]
+    nws = max(K.kvtc_workspace_bytes(len(js)) for js in pipe_jobs.values())
+    wss = [torch.zeros(nws // 4, dtype=torch.int32, device=DEV) for _ in range(2)]
     su, sr = torch.cuda.Stream(), torch.cuda.Stream()
     ev_u = [torch.cuda.Event() for _ in layers]
     ev_r = [torch.cuda.Event() for _ in layers]
