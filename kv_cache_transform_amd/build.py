@@ -18,6 +18,8 @@ HIP_FLAGS = [
     # IEEE fp32 division and square root (the quantizer divides)
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-ffp-contract=on",
+    # MFMA results in VGPRs (no AGPR round trips in the epilogues)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -649,6 +649,7 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
     d.layer = j.layer;
     d.kind = j.kind;
     d.status_idx = i;
+    d.bs_shift = -1;
     if (mode == Mode::Encode || mode == Mode::Pack) {
       if (j.dst_capacity < stream_bytes(c, s, j.n_tokens))
         return fail(KVTC_E_CAPACITY, "job: dst_capacity below kvtc_encoded_bytes");
@@ -672,6 +673,9 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
         d.block_size = 1 << 30;
         d.n_blocks = 1;
       }
+      if ((d.block_size & (d.block_size - 1)) == 0)
+        for (int b = 0; b < 31; ++b)
+          if ((1 << b) == d.block_size) d.bs_shift = b;
       st_off[i] = st_total;
       st_total += job_staging_bytes(s, d.tc);
       if (!d_staging || st_total > staging_bytes) return fail(KVTC_E_CAPACITY, "staging buffer too small");
@@ -702,9 +706,9 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
       const Slot& s = c->slots[d.slot];
       const uint32_t ptiles = (d.s1 + d.w1 + kPassRows - 1) / kPassRows;
       if (mode == Mode::Restore) {
-        // feature slabs x token ranges of kGemmTok
+        // units: feature slabs x blocks of kDecTok tokens
         const int fs = gemm_features(key[order[p]]);
-        d.n_ctiles = (uint32_t)((F + fs - 1) / fs) * ((d.tc + kGemmTok - 1) / kGemmTok);
+        d.n_ctiles = (uint32_t)((F + fs - 1) / fs) * ((d.tc + kDecTok - 1) / kDecTok);
       } else {
         const int tile = mode == Mode::Unpack ? kPrepTok : mode == Mode::UnpackCodes ? kUnpackTile : kEncTile;
         d.n_ctiles = (d.tc + tile - 1) / tile;

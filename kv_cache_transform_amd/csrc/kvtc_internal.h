@@ -59,6 +59,7 @@ struct JobDesc {
   int32_t block_size;      // paged output when block_table != nullptr
   int32_t n_blocks;
   int32_t status_idx;      // this job's word in LaunchArgs::status
+  int32_t bs_shift;        // log2(block_size) if a power of two, else -1
 };
 
 struct LaunchArgs {
@@ -107,17 +108,21 @@ __host__ __device__ inline int padded_stride(int rb) {
 // Decode. Stage 1 handles kPrepTok compressed tokens per tile and writes,
 // per block of kDecTok tokens, ks * 64 B-operand fragments of 16 bytes (fp16,
 // MFMA lane order) and kDecTok f32 token scales: stg_block_bytes(ks) bytes.
-// Stage 2 tiles are gemm_features(ks) features x kGemmTok tokens; the slab of
-// V' (rows padded by 16 bytes), mu and four waves' output staging rows take
-// gemm_lds_bytes(ks) of LDS.
+// Stage 2 works in units of one block of kDecTok tokens of one slab of
+// gemm_features(ks) features; the slab of V' (rows padded by 16 bytes), mu
+// and kGemmWaves waves' output staging rows take gemm_lds_bytes(ks) of LDS.
+// Its workgroups get at least kGemmMinUnits units each.
 constexpr int kDecTok = 32;
 constexpr int kPrepTok = 128;
-constexpr int kGemmTok = 1024;
+constexpr uint32_t kGemmMinUnits = 16;
+constexpr int kGemmWaves = 8;              // waves sharing one slab of V'
+constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr size_t kSinkBytes = 256;         // workspace target of stores that have no row
 __host__ __device__ constexpr size_t stg_block_bytes(int ks) { return (size_t)ks * 1024 + kDecTok * 4; }
 __host__ __device__ constexpr int gemm_features(int ks) { return ks <= 8 ? 128 : 64; }
 __host__ __device__ constexpr size_t gemm_lds_bytes(int ks) {
-  return (size_t)gemm_features(ks) * (ks * 32 + 16) + (size_t)gemm_features(ks) * 4 + 4 * kDecTok * kOutRow;
+  return (size_t)gemm_features(ks) * (ks * 32 + 16) + (size_t)gemm_features(ks) * 4 +
+         (size_t)kGemmWaves * kDecTok * kOutRow;
 }
 
 // Host-side launchers implemented in kvtc_kernels.hip (G = group size, lds =

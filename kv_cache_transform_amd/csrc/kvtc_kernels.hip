@@ -30,6 +30,8 @@
 // v_mfma_f32_32x32x16_f16 per 32-feature block and writes S_t * D + mu.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "kvtc_internal.h"
 
 namespace kvtc {
@@ -696,10 +698,10 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
   if (threadIdx.x == 0 && flag) set_status(a, jd.status_idx, KVTC_E_INVALID);
 }
 
-// Stage 2: one tile is features [f0, f0 + FS) x compressed tokens
-// [t0, t0 + kGemmTok) of one job. The slab of V' (fp16, FS rows of r_dec,
+// Stage 2 segment: features [f0, f0 + FS) x blocks [c_lo, c_hi) of kDecTok
+// compressed tokens of one job. The slab of V' (fp16, FS rows of r_dec,
 // padded by 16 bytes per row) and mu stay in LDS; each wave then runs on its
-// own over blocks of kDecTok tokens: it loads the block's B operands and
+// own over every fourth block: it loads the block's B operands and
 // scales (the next block's are in flight meanwhile), runs FS / 32 x KS
 // MFMAs D[feature][token], forms S_t * D + mu and stores it through its LDS
 // staging rows as 128-byte segments. Every store is issued (rows past the
@@ -707,27 +709,20 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
 // number of memory operations per block is fixed and the wait for the next
 // block's operands never covers this block's stores.
 template <int KS, bool OUT32>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const LaunchArgs a) {
+__device__ void gemm_segment(const LaunchArgs& a, int j, uint32_t slab, uint32_t c_lo, uint32_t c_hi,
+                             uint8_t* smem) {
   constexpr int FS = gemm_features(KS);
   constexpr int NFB = FS / 32;
   constexpr int OSZ = OUT32 ? 4 : 2;
   constexpr int BPS = 128 / (32 * OSZ);           // feature blocks per 128-byte segment
   constexpr int KA = KS > 0 ? KS : 1;
   constexpr int AST = KS * 32 + 16;               // LDS bytes per V' row
-  extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int flag;
-  const uint32_t tile = logical_tile();
-  if (tile >= a.total_tiles) return;
-  const int j = find_job(a, tile);
   const JobDesc& jd = a.jobs[j];
   const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
-  const uint32_t lt = tile - jd.tile_begin;
-  if (prior_rank(a, jd.status_idx) != 0 || lt >= jd.n_ctiles) return;  // stage 1 rejected it
+  if (prior_rank(a, jd.status_idx) != 0) return;  // stage 1 rejected it
   const int F = a.F;
-  const uint32_t n_slab = (uint32_t)(F + FS - 1) / FS;
-  const int f0 = (int)(lt % n_slab) * FS;
-  const uint32_t t0 = (lt / n_slab) * kGemmTok;
-  const uint32_t n_ch = (min((uint32_t)kGemmTok, jd.tc - t0) + kDecTok - 1) / kDecTok;
+  const int f0 = (int)slab * FS;
+  const uint32_t t0 = 0;
   const int lane = threadIdx.x & 63, h = lane >> 5, c16 = lane & 7;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 
@@ -737,15 +732,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const LaunchArgs a) {
   {
     const int r_dec = sl.r_dec;
     const uint8_t* vdec = a.state + sl.vdec_off;
-    for (int i = threadIdx.x; i < FS * 2 * KS; i += kThreads) {
+    for (int i = threadIdx.x; i < FS * 2 * KS; i += kGemmThreads) {
       const int row = i / (2 * KS), c = i - row * (2 * KS);
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (f0 + row < F) v = *(const uint4*)(vdec + ((size_t)(f0 + row) * r_dec + 8 * c) * 2);
       *(uint4*)(As + row * AST + 16 * c) = v;
     }
     const float* mu = (const float*)(a.state + sl.mu_off);
-    for (int i = threadIdx.x; i < FS; i += kThreads) mu_s[i] = f0 + i < F ? mu[f0 + i] : 0.f;
-    if (threadIdx.x == 0) flag = 0;
+    for (int i = threadIdx.x; i < FS; i += kGemmThreads) mu_s[i] = f0 + i < F ? mu[f0 + i] : 0.f;
   }
   __syncthreads();
 
@@ -755,6 +749,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const LaunchArgs a) {
   uint8_t* dst = (uint8_t*)jd.dst;
   uint8_t* sink = a.sink + c16 * 16;
   int bad = 0;
+  // Job fields used per block, held in registers.
+  const uint32_t tc = jd.tc, s1 = jd.s1;
+  const int32_t* btab = jd.block_table;
+  const int bsz = jd.block_size, bsh = jd.bs_shift, nblk = jd.n_blocks;
 
   // Operands of block c: B fragments, the lane's token scale and the block
   // table entries of the rows this lane stores (r = 8 it + lane / 8).
@@ -768,8 +766,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const LaunchArgs a) {
     Sn = *(const float*)(blk + KS * 1024 + (lane & 31) * 4);
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const uint32_t tok = min(t0 + c * kDecTok + 8 * it + (lane >> 3), jd.tc - 1);
-      btn[it] = jd.block_table[(jd.s1 + tok) / (uint32_t)jd.block_size];
+      const uint32_t tt = s1 + min(t0 + c * kDecTok + 8 * it + (lane >> 3), tc - 1);
+      btn[it] = btab[bsh >= 0 ? tt >> bsh : tt / (uint32_t)bsz];
     }
   };
   // Operands in use: B fragments, token scale and the store addresses of
@@ -785,20 +783,24 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const LaunchArgs a) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const uint32_t tok = t0 + c * kDecTok + 8 * it + (lane >> 3);
-      const uint32_t tt = jd.s1 + tok;
+      const uint32_t tt = s1 + tok;
       const int bt = btn[it];
-      const bool blk_ok = bt >= 0 && bt < jd.n_blocks;
-      bad |= (int)(tok < jd.tc && !blk_ok);
-      const long row = (long)bt * jd.block_size + (long)(tt % (uint32_t)jd.block_size);
-      dp[it] = tok < jd.tc && blk_ok ? dst + (row * F + f0) * OSZ + c16 * 16 : sink;
+      const bool blk_ok = bt >= 0 && bt < nblk;
+      bad |= (int)(tok < tc && !blk_ok);
+      const uint32_t in_blk = bsh >= 0 ? tt & ((1u << bsh) - 1u) : tt % (uint32_t)bsz;
+      const long row = (long)bt * bsz + (long)in_blk;
+      dp[it] = tok < tc && blk_ok ? dst + (row * F + f0) * OSZ + c16 * 16 : sink;
     }
   };
-  if ((uint32_t)wave < n_ch) {
-    fetch(wave);
-    take(wave);
+  if (c_lo + wave < c_hi) {
+    fetch(c_lo + wave);
+    take(c_lo + wave);
   }
-  for (uint32_t c = wave; c < n_ch; c += kWaves) {
-    fetch(min(c + kWaves, n_ch - 1));   // unconditional: a fixed count of loads per block
+  for (uint32_t c = c_lo + wave; c < c_hi; c += kGemmWaves) {
+    fetch(min(c + kGemmWaves, c_hi - 1));   // unconditional: a fixed count of loads per block
+    // Keep the scheduler from pulling the next block's takeover (which waits
+    // for these loads) into this block's work.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int fb = 0; fb < NFB; ++fb) {
       const uint8_t* arow = As + (fb * 32 + (lane & 31)) * AST + 16 * h;
@@ -831,16 +833,44 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const LaunchArgs a) {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
           const uint4 v = *(const uint4*)(stg + (8 * it + (lane >> 3)) * kOutRow + c16 * 16);
-          *(uint4*)(dp[it] == sink || !in_f ? sink : dp[it] + fs * OSZ) = v;
+          // streaming (non-temporal) stores: the output is not read back here
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
+                                      (u32x4*)(dp[it] == sink || !in_f ? sink : dp[it] + fs * OSZ));
         }
         wave_lds_sync();
       }
     }
-    take(min(c + kWaves, n_ch - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    take(min(c + kGemmWaves, c_hi - 1));
   }
-  if (bad) atomicExch(&flag, 1);
-  __syncthreads();
-  if (threadIdx.x == 0 && flag) set_status(a, jd.status_idx, KVTC_E_INVALID);
+  if (bad) set_status(a, jd.status_idx, KVTC_E_INVALID);
+  __syncthreads();  // the slab and staging rows are free for the next tile
+}
+
+// Stage 2 work is counted in units of one block of kDecTok tokens of one
+// feature slab of one job, ordered (job, slab, block); job j's units start
+// at tile_begin and number n_ctiles = slabs * blocks. The host launches at
+// most as many workgroups as fit on the device at once and each takes an
+// equal contiguous range of units, so all finish together; a range crosses
+// few (job, slab) boundaries (the slab of V' is loaded once per segment),
+// and the ranges in flight on one XCD cover the slabs of the same tokens.
+template <int KS, bool OUT32>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4))) void gemm_kernel(const LaunchArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint64_t U = a.total_tiles;
+  const uint32_t g = logical_tile();
+  uint32_t u = (uint32_t)(U * g / gridDim.x);
+  const uint32_t u_end = (uint32_t)(U * (g + 1) / gridDim.x);
+  while (u < u_end) {
+    const int j = find_job(a, u);
+    const JobDesc& jd = a.jobs[j];
+    const uint32_t n_ch = (jd.tc + kDecTok - 1) / kDecTok;
+    const uint32_t lu = u - jd.tile_begin;
+    const uint32_t slab = lu / n_ch, c = lu - slab * n_ch;
+    const uint32_t seg_end = min(u_end, jd.tile_begin + (slab + 1) * n_ch);
+    gemm_segment<KS, OUT32>(a, j, slab, c, c + (seg_end - u), smem);
+    u = seg_end;
+  }
 }
 
 // Test hook: records -> codes (u8, one per component) and (shift, scale)
@@ -975,14 +1005,29 @@ int launch_prep(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
   return (int)hipGetLastError();
 }
 
+// Workgroups of `kernel` (threads, lds bytes) resident on the current
+// device at once, a multiple of 8, at least 8.
+template <class K>
+static uint32_t resident_grid(K kernel, int threads, size_t lds) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kernel, threads, lds) != hipSuccess)
+    return 8;
+  const uint32_t n = (uint32_t)std::max(1, per_cu) * (uint32_t)std::max(1, cus);
+  return std::max(8u, n / 8u * 8u);
+}
+
 template <bool OUT32>
 static int launch_gemm_o(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
-  const dim3 g = grid_for(a.total_tiles);
-#define KVTC_GEMM(KV)                                                            \
-  case KV:                                                                       \
-    allow_lds(gemm_kernel<KV, OUT32>, lds);                                      \
-    hipLaunchKernelGGL((gemm_kernel<KV, OUT32>), g, dim3(kThreads), lds, s, a);  \
-    break;
+#define KVTC_GEMM(KV)                                                                        \
+  case KV: {                                                                                 \
+    allow_lds(gemm_kernel<KV, OUT32>, lds);                                                  \
+    const dim3 g(std::min(std::max(8u, a.total_tiles / (8 * kGemmMinUnits) * 8),          \
+                          resident_grid(gemm_kernel<KV, OUT32>, kGemmThreads, lds)));                     \
+    hipLaunchKernelGGL((gemm_kernel<KV, OUT32>), g, dim3(kGemmThreads), lds, s, a);              \
+    break;                                                                                   \
+  }
   switch (ks) {
     KVTC_KS_CASES(KVTC_GEMM)
     default:
