@@ -726,13 +726,13 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
     size_t l = 16;
     const size_t rbp = (size_t)padded_stride((int)rb_max);
     if (mode == Mode::Encode)
-      l = std::max({l, 2 * (size_t)32 * k * kEncRowPad * 2 + (size_t)F * 4, (size_t)kEncTile * rbp});
+      l = std::max({l, 3 * (size_t)32 * k * kEncRowPad * 2 + (size_t)F * 4, (size_t)kEncTile * rbp});
     else if (mode == Mode::Pack)
       l = std::max(l, (size_t)kEncTile * rbp);
     else if (mode == Mode::UnpackCodes)
       l = std::max(l, (size_t)kUnpackTile * rb_max + 16);
     else if (mode == Mode::Unpack)
-      l = std::max(l, (size_t)kPrepTok * rbp + 16);
+      l = std::max({l, (size_t)kPrepTok * rbp + 16, (size_t)kPassRows * sizeof(long)});
     else
       l = gemm_lds_bytes(k);
     if (l > 160 * 1024) return fail(KVTC_E_UNSUPPORTED, "tile does not fit in LDS");

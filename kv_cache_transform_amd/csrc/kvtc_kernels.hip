@@ -151,58 +151,89 @@ __device__ __forceinline__ long out_row(const JobDesc& jd, uint32_t t) {
 }
 
 // Encode: copy passthrough rows [p*kPassRows, ...) of the stream's row list
-// (rows [0, s') then [T - w', T)) from the KV tensor into the stream.
+// (rows [0, s') then [T - w', T)) from the KV tensor into the stream, with
+// four 16-byte loads in flight per thread.
 __device__ void encode_passthrough(const JobDesc& jd, uint32_t p, size_t row_bytes) {
   const uint32_t n_rows = jd.s1 + jd.w1;
   const uint32_t r0 = p * kPassRows;
   const uint32_t r1 = min(n_rows, r0 + kPassRows);
-  const size_t vec_per_row = row_bytes / 16;
-  const size_t total = (size_t)(r1 - r0) * vec_per_row;
-  for (size_t i = threadIdx.x; i < total; i += kThreads) {
-    const uint32_t r = r0 + (uint32_t)(i / vec_per_row);
-    const size_t c = i % vec_per_row;
-    const uint32_t src_row = r < jd.s1 ? r : jd.T - jd.w1 + (r - jd.s1);
-    const uint4 v = ((const uint4*)((const uint8_t*)jd.src + (size_t)src_row * row_bytes))[c];
-    ((uint4*)((uint8_t*)jd.dst + kHeaderBytes + (size_t)r * row_bytes))[c] = v;
+  const uint32_t vpr = (uint32_t)(row_bytes / 16);
+  const uint32_t total = (r1 - r0) * vpr;
+  uint8_t* dst = (uint8_t*)jd.dst + kHeaderBytes + (size_t)r0 * row_bytes;
+  for (uint32_t i0 = threadIdx.x; i0 < total; i0 += 4 * kThreads) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t i = i0 + u * kThreads;
+      if (i < total) {
+        const uint32_t r = r0 + i / vpr;
+        const uint32_t src_row = r < jd.s1 ? r : jd.T - jd.w1 + (r - jd.s1);
+        v[u] = ((const u32x4*)((const uint8_t*)jd.src + (size_t)src_row * row_bytes))[i % vpr];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t i = i0 + u * kThreads;
+      if (i < total) ((u32x4*)dst)[i] = v[u];
+    }
   }
 }
 
-// Decode: copy passthrough rows from the stream to the output, converting
-// the element type if needed. Returns false if a block table entry was bad.
-__device__ bool decode_passthrough(const LaunchArgs& a, const JobDesc& jd, uint32_t p) {
+// Decode: copy passthrough rows [p*kPassRows, ...) of the stream's row list
+// to the output, converting the element type if needed; every thread of the
+// workgroup calls it (rows_lds: kPassRows longs of LDS). The output row of
+// each stream row is looked up once; the copy keeps four 16-byte loads in
+// flight per thread. Returns false if a block table entry was bad.
+__device__ bool decode_passthrough(const LaunchArgs& a, const JobDesc& jd, uint32_t p, long* rows_lds) {
   const int F = a.F;
   const uint32_t n_rows = jd.s1 + jd.w1;
   const uint32_t r0 = p * kPassRows;
-  const uint32_t r1 = min(n_rows, r0 + kPassRows);
+  const uint32_t nr = min(n_rows, r0 + kPassRows) - r0;
   const int in_esz = a.dtype == KVTC_F32 ? 4 : 2;
   const int out_esz = a.out_dtype == KVTC_F32 ? 4 : 2;
-  const uint8_t* src = (const uint8_t*)jd.src + kHeaderBytes;
+  const uint8_t* src = (const uint8_t*)jd.src + kHeaderBytes + (size_t)r0 * F * in_esz;
+  if (threadIdx.x < nr) {
+    const uint32_t r = r0 + threadIdx.x;
+    rows_lds[threadIdx.x] = out_row(jd, r < jd.s1 ? r : jd.T - jd.w1 + (r - jd.s1));
+  }
+  __syncthreads();
   bool ok = true;
   if (a.dtype == a.out_dtype) {
-    const size_t vec_per_row = (size_t)F * in_esz / 16;
-    const size_t total = (size_t)(r1 - r0) * vec_per_row;
-    for (size_t i = threadIdx.x; i < total; i += kThreads) {
-      const uint32_t r = r0 + (uint32_t)(i / vec_per_row);
-      const size_t c = i % vec_per_row;
-      const uint32_t t = r < jd.s1 ? r : jd.T - jd.w1 + (r - jd.s1);
-      const long orow = out_row(jd, t);
-      if (orow < 0) { ok = false; continue; }
-      const uint4 v = ((const uint4*)(src + (size_t)r * F * in_esz))[c];
-      ((uint4*)((uint8_t*)jd.dst + (size_t)orow * F * out_esz))[c] = v;
+    const uint32_t vpr = (uint32_t)F * in_esz / 16;          // 16-byte vectors per row
+    const uint32_t total = nr * vpr;
+    for (uint32_t i0 = threadIdx.x; i0 < total; i0 += 4 * kThreads) {
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t i = i0 + u * kThreads;
+        if (i < total) v[u] = ((const u32x4*)src)[i];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t i = i0 + u * kThreads;
+        if (i < total) {
+          const uint32_t rr = i / vpr;
+          const long orow = rows_lds[rr];
+          if (orow < 0) {
+            ok = false;
+          } else {
+            ((u32x4*)((uint8_t*)jd.dst + (size_t)orow * F * out_esz))[i - rr * vpr] = v[u];
+          }
+        }
+      }
     }
   } else {
-    const size_t total = (size_t)(r1 - r0) * F;
-    for (size_t i = threadIdx.x; i < total; i += kThreads) {
-      const uint32_t r = r0 + (uint32_t)(i / F);
-      const int c = (int)(i % F);
-      const uint32_t t = r < jd.s1 ? r : jd.T - jd.w1 + (r - jd.s1);
-      const long orow = out_row(jd, t);
+    const uint32_t total = nr * (uint32_t)F;
+    for (uint32_t i = threadIdx.x; i < total; i += kThreads) {
+      const uint32_t rr = i / (uint32_t)F;
+      const int c = (int)(i - rr * (uint32_t)F);
+      const long orow = rows_lds[rr];
       if (orow < 0) { ok = false; continue; }
       if (a.dtype == KVTC_BF16) {  // bf16 -> f32, exact
-        const uint16_t b = ((const uint16_t*)(src + (size_t)r * F * 2))[c];
+        const uint16_t b = ((const uint16_t*)src)[i];
         ((float*)jd.dst)[(size_t)orow * F + c] = bf16_to_f32(b);
       } else {                     // f32 -> bf16, nearest even
-        const float f = ((const float*)(src + (size_t)r * F * 4))[c];
+        const float f = ((const float*)src)[i];
         ((uint16_t*)jd.dst)[(size_t)orow * F + c] = (uint16_t)bf16_bits_rne(f);
       }
     }
@@ -353,10 +384,15 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
   const uint8_t* xrow = (const uint8_t*)jd.src + (size_t)(jd.s1 + t0 + (tok_ok ? tl : 0)) * row_bytes;
   const uint16_t* venc = (const uint16_t*)(a.state + sl.venc_off);
 
-  // LDS: two basis K-slices [32 * NB][kEncRowPad] bf16, then the mean (F fp32).
+  // LDS: three basis K-slices [32 * NB][kEncRowPad] bf16, then the mean (F fp32).
+  // Slices and token fragments are loaded two slices ahead of their use: the
+  // loads for slice i + 2 are issued while slice i is computed, the basis
+  // slice i + 1 (loaded during slice i - 1) goes to LDS at the end of slice
+  // i. Loads past the last slice re-read it, so every slice issues the same
+  // loads and the waits count exactly.
   constexpr int slice_elems = 32 * NB * kEncRowPad;
   uint16_t* const vbase = (uint16_t*)smem;
-  float* mu_l = (float*)(smem + (size_t)4 * slice_elems);
+  float* mu_l = (float*)(smem + (size_t)6 * slice_elems);
   {
     const float4* mu = (const float4*)(a.state + sl.mu_off);
     for (int i = threadIdx.x; i < F / 4; i += kThreads) ((float4*)mu_l)[i] = mu[i];
@@ -366,34 +402,30 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
   // with no predicate. Rows >= r_enc (zero in the device state when r_enc
   // < 32 * NB, clamped re-reads otherwise) are never read by the MFMA loop.
   typedef uint32_t vregs_t __attribute__((ext_vector_type(4 * NB)));
-  vregs_t vreg;
   const int vlast = sl.r_enc * (kEncKS / 8) - 1;
-#define KVTC_LOAD_SLICE(K0)                                                          \
+#define KVTC_LOAD_SLICE(V, K0)                                                       \
   _Pragma("unroll") for (int q = 0; q < NB; ++q) {                                   \
     const int idx = min((int)threadIdx.x + q * kThreads, vlast);                     \
     const uint4 v = *(const uint4*)(venc + (size_t)(idx / (kEncKS / 8)) * F + (K0) + \
                                     (idx % (kEncKS / 8)) * 8);                       \
-    vreg[4 * q] = v.x;                                                               \
-    vreg[4 * q + 1] = v.y;                                                           \
-    vreg[4 * q + 2] = v.z;                                                           \
-    vreg[4 * q + 3] = v.w;                                                           \
+    V[4 * q] = v.x;                                                                  \
+    V[4 * q + 1] = v.y;                                                              \
+    V[4 * q + 2] = v.z;                                                              \
+    V[4 * q + 3] = v.w;                                                              \
   }
-#define KVTC_STORE_SLICE(BUF)                                                        \
+#define KVTC_STORE_SLICE(V, BUF)                                                     \
   _Pragma("unroll") for (int q = 0; q < NB; ++q) {                                   \
     const int idx = (int)threadIdx.x + q * kThreads;                                 \
     *(uint4*)((BUF) + (idx / (kEncKS / 8)) * kEncRowPad + (idx % (kEncKS / 8)) * 8) = \
-        make_uint4(vreg[4 * q], vreg[4 * q + 1], vreg[4 * q + 2], vreg[4 * q + 3]);  \
+        make_uint4(V[4 * q], V[4 * q + 1], V[4 * q + 2], V[4 * q + 3]);              \
   }
   // Token fragments of one slice: K step s reads features k0 + 16s + 8h .. +8.
   constexpr int XV = F32IN ? 2 : 1;                  // 16-byte vectors per K step
-  uint4 xr[4 * XV], xn[4 * XV];
-  auto load_x = [&](int k0, uint4* dst) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int v = 0; v < XV; ++v)
-        dst[s * XV + v] = *(const uint4*)(xrow + (size_t)(k0 + 16 * s + 8 * h) * esz + 16 * v);
-  };
+  // (ext-vector registers, which stay in registers when passed around)
+#define KVTC_LOAD_X(K0, DST)                                                           \
+  _Pragma("unroll") for (int s = 0; s < 4; ++s)                                        \
+    _Pragma("unroll") for (int v = 0; v < XV; ++v)                                     \
+      DST[s * XV + v] = *(const u32x4*)(xrow + (size_t)((K0) + 16 * s + 8 * h) * esz + 16 * v);
 
   f32x16 acc[NB];
 #pragma unroll
@@ -401,37 +433,38 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
 
-  KVTC_LOAD_SLICE(0)
-  load_x(0, xr);
-  KVTC_STORE_SLICE(vbase)
-  __syncthreads();
-  int it = 0;
-  for (int k0 = 0; k0 < F; k0 += kEncKS, ++it) {
-    const bool more = k0 + kEncKS < F;
-    if (more) {
-      KVTC_LOAD_SLICE(k0 + kEncKS)
-      load_x(k0 + kEncKS, xn);
-    }
-    const uint16_t* vs = vbase + (it & 1) * slice_elems;
+  const int n_sl = F / kEncKS;
+  auto slice_k = [&](int i) { return min(i, n_sl - 1) * kEncKS; };
+  // One slice: issue the loads of slice it + 2 (basis into vl, tokens into
+  // xl), run the K steps of slice it (tokens xc, basis LDS buffer it % 3),
+  // then move basis slice it + 1 (vs, loaded one slice earlier) into LDS. The
+  // caller rotates the buffers (x with period 3, basis registers with period
+  // 2), so no register is copied and every wait is for loads two slices old.
+  auto step = [&](int it, u32x4 (&xc)[4 * XV], u32x4 (&xl)[4 * XV], vregs_t& vl, vregs_t& vs)
+      __attribute__((always_inline)) {
+    const int k0 = it * kEncKS;
+    KVTC_LOAD_SLICE(vl, slice_k(it + 2))
+    KVTC_LOAD_X(slice_k(it + 2), xl)
+    const uint16_t* vsl = vbase + (it % 3) * slice_elems;
 #pragma unroll
     for (int s = 0; s < kEncKS / 16; ++s) {
       const int f = k0 + 16 * s + 8 * h;
       // Centred token operand: x' = bf16_rne(fp32(x) - mu).
       float xv[8];
       if (!F32IN) {
-        const uint4 raw = xr[s];
-        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+        const u32x4 raw = xc[s];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          xv[2 * e] = bf16_to_f32(w4[e] & 0xFFFFu);
-          xv[2 * e + 1] = bf16_to_f32(w4[e] >> 16);
+          xv[2 * e] = bf16_to_f32(raw[e] & 0xFFFFu);
+          xv[2 * e + 1] = bf16_to_f32(raw[e] >> 16);
         }
       } else {
-        const uint4 lo = xr[2 * s], hi = xr[2 * s + 1];
-        xv[0] = __uint_as_float(lo.x); xv[1] = __uint_as_float(lo.y);
-        xv[2] = __uint_as_float(lo.z); xv[3] = __uint_as_float(lo.w);
-        xv[4] = __uint_as_float(hi.x); xv[5] = __uint_as_float(hi.y);
-        xv[6] = __uint_as_float(hi.z); xv[7] = __uint_as_float(hi.w);
+        const u32x4 lo = xc[2 * s], hi = xc[2 * s + 1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[e] = __uint_as_float(lo[e]);
+          xv[4 + e] = __uint_as_float(hi[e]);
+        }
       }
       const float4 m0 = *(const float4*)(mu_l + f);
       const float4 m1 = *(const float4*)(mu_l + f + 4);
@@ -442,20 +475,34 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
       const bf16x8 bx = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const uint4 av = *(const uint4*)(vs + (b * 32 + (lane & 31)) * kEncRowPad + 16 * s + 8 * h);
+        const uint4 av = *(const uint4*)(vsl + (b * 32 + (lane & 31)) * kEncRowPad + 16 * s + 8 * h);
         acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bx,
                                                          acc[b], 0, 0, 0);
       }
     }
-    if (more) {
-      KVTC_STORE_SLICE(vbase + ((it + 1) & 1) * slice_elems)
-#pragma unroll
-      for (int v = 0; v < 4 * XV; ++v) xr[v] = xn[v];
-    }
+    // Slice it + 1 to LDS (its buffer was last read in slice it - 2).
+    KVTC_STORE_SLICE(vs, vbase + ((it + 1) % 3) * slice_elems)
     __syncthreads();
+  };
+  u32x4 x0[4 * XV], x1[4 * XV], x2[4 * XV];
+  vregs_t v0, v1;
+  KVTC_LOAD_SLICE(v0, 0)
+  KVTC_LOAD_X(0, x0)
+  KVTC_LOAD_SLICE(v1, slice_k(1))
+  KVTC_LOAD_X(slice_k(1), x1)
+  KVTC_STORE_SLICE(v0, vbase)
+  __syncthreads();
+  for (int it = 0; it < n_sl; it += 6) {
+    step(it, x0, x2, v0, v1);
+    if (it + 1 < n_sl) step(it + 1, x1, x0, v1, v0);
+    if (it + 2 < n_sl) step(it + 2, x2, x1, v0, v1);
+    if (it + 3 < n_sl) step(it + 3, x0, x2, v1, v0);
+    if (it + 4 < n_sl) step(it + 4, x1, x0, v0, v1);
+    if (it + 5 < n_sl) step(it + 5, x2, x1, v1, v0);
   }
 #undef KVTC_LOAD_SLICE
 #undef KVTC_STORE_SLICE
+#undef KVTC_LOAD_X
 
   // Quantize and pack. acc[b][i] holds component 32b + 8(i/4) + 4h + i%4 of
   // token tl; a group of G components is the item range
@@ -622,7 +669,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
   __syncthreads();
   int bad = 0;
   if (lt >= jd.n_ctiles) {
-    bad = !decode_passthrough(a, jd, lt - jd.n_ctiles);
+    bad = !decode_passthrough(a, jd, lt - jd.n_ctiles, (long*)smem);
   } else {
     constexpr int KA = KS > 0 ? KS : 1;
     const uint32_t t0 = lt * kPrepTok;
