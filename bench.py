@@ -7,9 +7,12 @@ budget (1 bit per value), microscale group 16; seeded synthetic KV (shared
 channels per head), calibrated on 16384 synthetic tokens per tensor by the
 library on the host.
 
-One step = kvtc_encode of every tensor followed by kvtc_decode of every
-stream back to bf16 (one launch per 32 tensors), with inputs, streams and
-outputs resident in HBM. value = bf16 KV bytes per step / step time. For a
+One step = kvtc_encode of every tensor followed by the decode of every
+stream back to bf16 (one launch per 32 tensors per kernel), with inputs,
+streams and outputs resident in HBM. The decode is issued as its two stages
+(kvtc_decode_unpack, kvtc_decode_restore: exactly what kvtc_decode runs) so
+that HIP events on the launch stream time each kernel inside the timed
+region. value = bf16 KV bytes per step / step time. For a
 paged workload (qwen25_7b_paged) the decode is the layer-by-layer two-stream
 pipeline: stage 1 (unpack) of layer l+1 runs on one stream while stage 2
 (restore into the paged cache) of layer l runs on another. The DEFLATE ratio
@@ -47,6 +50,10 @@ def main():
     ap.add_argument("--calib-tokens", type=int, default=0, help="override (0 = workload's)")
     ap.add_argument("--distinct-requests", type=int, default=2,
                     help="distinct synthetic requests per (layer, kind); the rest are copies")
+    ap.add_argument("--save-artifact", default="", help="write the calibrated artifact here")
+    ap.add_argument("--load-artifact", default="",
+                    help="use this artifact (written by --save-artifact for the same workload) "
+                         "instead of calibrating")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -61,7 +68,11 @@ def main():
     cores = len(os.sched_getaffinity(0))
     kp = K.params(w.n_layers, w.kv_heads, w.head_dim, w.sink, w.window, w.group, 8,
                   w.bits_per_value, dt)
-    codec = K.Codec(kp)
+    if args.load_artifact:
+        with open(args.load_artifact, "rb") as f:
+            codec = K.Codec.load(f.read())
+    else:
+        codec = K.Codec(kp)
     slots = [(l, k) for l in range(w.n_layers) for k in w.kinds]
     calib_n = args.calib_tokens or w.calib_tokens
 
@@ -75,10 +86,14 @@ def main():
         x = synth.storage(w, synth.gen_kv(w, l, k, synth.ROLE_CALIB, calib_n))
         codec.calibrate(l, k, x, threads=per)
 
-    with cf.ThreadPoolExecutor(workers) as ex:
-        for i, _ in enumerate(ex.map(calib, slots)):
-            if (i + 1) % 16 == 0:
-                log(f"calibrated {i + 1}/{len(slots)} slots ({time.time() - t0:.1f}s)")
+    if not args.load_artifact:
+        with cf.ThreadPoolExecutor(workers) as ex:
+            for i, _ in enumerate(ex.map(calib, slots)):
+                if (i + 1) % 16 == 0:
+                    log(f"calibrated {i + 1}/{len(slots)} slots ({time.time() - t0:.1f}s)")
+        if args.save_artifact:
+            with open(args.save_artifact, "wb") as f:
+                f.write(codec.save())
     calib_s = time.time() - t0
     infos = {s: codec.slot(*s) for s in slots}
 
@@ -141,12 +156,20 @@ def main():
 
     n_dws = codec.decode_workspace_bytes(dec_jobs)
     dws = torch.zeros((n_dws + 3) // 4, dtype=torch.int32, device=dev)
+    n_wsb = K.kvtc_workspace_bytes(n_jobs)
+    stg = dws.view(torch.uint8)[n_wsb:]
+    n_stg = n_dws - n_wsb
 
-    def decode():
+    def decode(mid=None):
         if pipe is not None:
             pipe.run(stream)
+            if mid is not None:
+                mid.record(stream)
         else:
-            codec.decode(dec_jobs, K.KVTC_BF16, dws, n_dws, stream)
+            codec.decode_unpack(dec_jobs, K.KVTC_BF16, stg, n_stg, dws, stream)
+            if mid is not None:
+                mid.record(stream)
+            codec.decode_restore(dec_jobs, K.KVTC_BF16, stg, n_stg, dws, stream)
 
     # Plain device copy of a known size: the practical HBM ceiling and the
     # reference that scales the FETCH_SIZE / WRITE_SIZE counters.
@@ -176,38 +199,61 @@ def main():
     if pipe is not None:
         pipe.check()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for e0, e1, e2 in ev:
+    for e0, e1, e2, e3 in ev:
         e0.record(stream)
         encode()
         e1.record(stream)
-        decode()
-        e2.record(stream)
+        decode(e2)
+        e3.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    enc_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
-    dec_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    enc_ms = np.array([a.elapsed_time(b) for a, b, _, _ in ev])
+    prep_ms = np.array([b.elapsed_time(c) for _, b, c, _ in ev])
+    gemm_ms = np.array([c.elapsed_time(d) for _, _, c, d in ev])
+    dec_ms = prep_ms + gemm_ms
     ms_per_step = wall * 1e3 / args.steps
 
     kv_bytes = n_jobs * T * F * esz
     r_eff = {s: infos[s].r_eff for s in slots}
-    # Algorithmic HBM bytes of one call: raw KV, the streams, and per tensor
-    # the operational basis (bf16 for encode, fp16 for decode) and fp32 mean.
-    basis = sum(r_eff[(l, k)] * F * 2 + F * 4 for l, k, _ in jobs)
-    stream_total = int(sum(sizes))
-    enc_alg = kv_bytes + stream_total + basis
-    dec_alg = kv_bytes + stream_total + basis
     n_launch = (n_jobs + 31) // 32
-    enc_t = float(np.median(enc_ms)) * 1e-3
-    dec_t = float(np.median(dec_ms)) * 1e-3
-    dominant = "decode" if dec_t >= enc_t else "encode"
-    ach = (dec_alg / dec_t if dominant == "decode" else enc_alg / enc_t) / 1e9
-    other = (enc_alg / enc_t if dominant == "decode" else dec_alg / dec_t) / 1e9
-    alg = dec_alg if dominant == "decode" else enc_alg
-    flops = sum(2 * F * r_eff[(l, k)] * (T - w.sink - w.window) for l, k, _ in jobs)
+    stream_total = int(sum(sizes))
+    tc = T - min(w.sink, T) - min(w.window, T - min(w.sink, T))
+    pass_rows = T - tc
+    # Algorithmic HBM bytes of one call of each kernel, per launch: what the
+    # kernel must read and write at least.
+    #  encode: the KV rows, the streams, the bf16 basis and fp32 mean per tensor
+    #  decode stage 1: the streams, the staging it writes, passthrough rows out
+    #  decode stage 2: the staging, the compressed rows out, fp16 basis + mean
+    staging = n_stg
+    enc_alg = kv_bytes + stream_total + sum(((r_eff[(l, k)] + 31) // 32 * 32) * F * 2 + F * 4
+                                            for l, k, _ in jobs)
+    prep_alg = stream_total + staging + n_jobs * pass_rows * F * esz
+    gemm_alg = staging + n_jobs * tc * F * esz + sum(((r_eff[(l, k)] + 15) // 16 * 16) * F * 2 + F * 4
+                                                     for l, k, _ in jobs)
+    dec_alg = stream_total + kv_bytes + sum(((r_eff[(l, k)] + 15) // 16 * 16) * F * 2 + F * 4
+                                            for l, k, _ in jobs)
+    med = lambda v: float(np.median(v)) * 1e-3
+    kern = {"encode_kernel": (enc_alg, med(enc_ms)), "prep_kernel": (prep_alg, med(prep_ms)),
+            "gemm_kernel": (gemm_alg, med(gemm_ms))}
+    if pipe is not None:   # two streams: stage times overlap; report the pipeline as one
+        kern = {"encode_kernel": kern["encode_kernel"],
+                "prep_kernel + gemm_kernel (two streams)": (dec_alg, med(dec_ms))}
+    dominant = max(kern, key=lambda k: kern[k][1])
+    enc_t, dec_t = med(enc_ms), med(dec_ms)
+
+    def roof(name):
+        alg, t = kern[name]
+        per_launch_t = t / n_launch
+        ach = alg / n_launch / per_launch_t / 1e9
+        return {"kernel": name, "achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBPS, 4),
+                "alg_bytes_per_launch": int(alg / n_launch), "us_per_launch": round(per_launch_t * 1e6, 2),
+                "launches_per_call": n_launch}
+
+    flops = sum(2 * F * r_eff[(l, k)] * tc for l, k, _ in jobs)
+    traffic = measured_traffic(dominant, args.workload)
 
     # --- compression ratio (host zlib on a sample of streams; not timed)
     host_streams = sbuf.cpu().numpy()
@@ -216,7 +262,6 @@ def main():
     st_s = sum(sizes[i] for i in samp)
     z_s = sum(len(K.kvtc_deflate(host_streams[offs[i]:offs[i] + sizes[i]].tobytes(), 6)) for i in samp)
 
-    dec_kernel = "unpack_kernel + restore_kernel (two streams)" if w.paged else "decode_kernel"
     result = {
         "metric": "KV encode/decode GB/s (bf16 KV) and % of roofline, Llama-3.1-8B shape 8K tok",
         "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
@@ -239,19 +284,16 @@ def main():
         "decode_GBps": round(kv_bytes / dec_t / 1e9, 2),
         "encode_ms": round(enc_t * 1e3, 4),
         "decode_ms": round(dec_t * 1e3, 4),
-        "roofline": {"bound": "hbm",
-                     "kernel": dec_kernel if dominant == "decode" else "encode_kernel",
-                     "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "alg_bytes_per_launch": int(alg / n_launch), "launches_per_call": n_launch},
-        "roofline_other": {"kernel": "encode_kernel" if dominant == "decode" else dec_kernel,
-                           "achieved": round(other, 1), "frac": round(other / HBM_PEAK_GBPS, 4)},
+        "decode_path": {"achieved": round(dec_alg / dec_t / 1e9, 1),
+                        "frac": round(dec_alg / dec_t / 1e9 / HBM_PEAK_GBPS, 4)},
+        "roofline": dict(bound="hbm", peak=HBM_PEAK_GBPS, unit="GB/s", traffic=traffic, **roof(dominant)),
+        "roofline_other": [roof(k) for k in kern if k != dominant],
         "mfma_flops_per_call": flops,
         "copy_GBps": round(copy_gbps, 1),
         "compression": {"raw_over_stream": round(raw_s / st_s, 3),
                         "raw_over_deflate": round(raw_s / z_s, 3),
                         "r_eff": sorted(set(r_eff.values()))},
-        "calibration_s": round(calib_s, 1),
+        "calibration_s": None if args.load_artifact else round(calib_s, 1),
     }
     if pipe is not None:
         result["pipeline"] = pipe.overlap(stream)
@@ -335,6 +377,26 @@ class Pipeline:
         t_p = float(np.median(times))
         return {"unpack_ms": round(float(t_u), 4), "restore_ms": round(float(t_r), 4),
                 "pipelined_ms": round(t_p, 4), "overlap": round(float(t_u + t_r) / t_p, 3)}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs recorded in profiles/traffic.json, if they were taken on
+    this workload with the kernel source as it is now (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "kv_cache_transform_amd", "csrc", "kvtc_kernels.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernels_sha256") != digest or rec.get("workload") != workload:
+        return None
+    k = rec.get("per_launch_bytes", {}).get(kernel)
+    return int(k) if k is not None else None
 
 
 def cpu_baseline(codec, w, sample, xs, K, budget_s=12.0):
