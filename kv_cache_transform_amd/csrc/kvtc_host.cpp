@@ -726,7 +726,7 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
     size_t l = 16;
     const size_t rbp = (size_t)padded_stride((int)rb_max);
     if (mode == Mode::Encode)
-      l = std::max({l, 3 * (size_t)32 * k * kEncRowPad * 2 + (size_t)F * 4, (size_t)kEncTile * rbp});
+      l = std::max({l, enc_lds_bytes(k, F), (size_t)kEncTile * rbp});
     else if (mode == Mode::Pack)
       l = std::max(l, (size_t)kEncTile * rbp);
     else if (mode == Mode::UnpackCodes)

@@ -95,6 +95,15 @@ constexpr int kPassRows = 16;
 constexpr int kEncKS = 64;                 // features per LDS basis slice (encode)
 constexpr int kEncRowPad = kEncKS + 8;     // bf16 elements per LDS basis row
 constexpr int kOutRow = 128 + 16;          // bytes per LDS output-staging row (decode)
+constexpr int kEncWaves = kEncTile / 32;   // encode waves, 32 tokens each
+
+// Encode LDS: two basis slices [32 nb][kEncRowPad] bf16, one token tile
+// [32][kEncRowPad] bf16 per wave, then the mean (F fp32).
+__host__ __device__ constexpr size_t enc_basis_bytes(int nb) { return (size_t)32 * nb * kEncRowPad * 2; }
+__host__ __device__ constexpr size_t enc_xtile_bytes() { return (size_t)32 * kEncRowPad * 2; }
+__host__ __device__ constexpr size_t enc_lds_bytes(int nb, int F) {
+  return 2 * enc_basis_bytes(nb) + kEncWaves * enc_xtile_bytes() + (size_t)F * 4;
+}
 
 // LDS row stride for records under assembly (encode, pack): a multiple of 4
 // bytes with an odd dword count, so lanes of consecutive tokens write to

@@ -350,6 +350,13 @@ __device__ __forceinline__ uint64_t get_codes8(const uint8_t* rec, const DevSlot
   return out;
 }
 
+// Make this wave's LDS writes visible to its own lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // --------------------------------------------------------------- encode ---
 
 template <int NB, int G, bool F32IN>
@@ -381,22 +388,27 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
   const int h = lane >> 5;
   const int tl = wave * 32 + (lane & 31);            // token within the tile
   const bool tok_ok = (uint32_t)tl < n;
-  const uint8_t* xrow = (const uint8_t*)jd.src + (size_t)(jd.s1 + t0 + (tok_ok ? tl : 0)) * row_bytes;
   const uint16_t* venc = (const uint16_t*)(a.state + sl.venc_off);
+  static_assert(kEncWaves * 64 == kThreads, "one wave per 32 tokens of a tile");
 
-  // LDS: three basis K-slices [32 * NB][kEncRowPad] bf16, then the mean (F fp32).
-  // Slices and token fragments are loaded two slices ahead of their use: the
-  // loads for slice i + 2 are issued while slice i is computed, the basis
-  // slice i + 1 (loaded during slice i - 1) goes to LDS at the end of slice
-  // i. Loads past the last slice re-read it, so every slice issues the same
-  // loads and the waits count exactly.
+  // LDS: two basis K-slices [32 * NB][kEncRowPad] bf16, a token tile
+  // [32][kEncRowPad] bf16 per wave, then the mean (F fp32). Basis slices and
+  // token rows are loaded from memory two slices ahead of their use: during
+  // slice i the loads of slice i + 2 are issued, and at the end of slice i
+  // the token rows of slice i + 1 are centred into the wave's token tile and
+  // basis slice i + 1 goes to the other basis buffer (last read in slice
+  // i - 1, before the barrier that ended it). Loads past the last slice
+  // re-read it, so every slice issues the same loads and the waits count
+  // exactly.
   constexpr int slice_elems = 32 * NB * kEncRowPad;
   uint16_t* const vbase = (uint16_t*)smem;
-  float* mu_l = (float*)(smem + (size_t)6 * slice_elems);
+  uint16_t* const xs = (uint16_t*)(smem + 2 * enc_basis_bytes(NB) + wave * enc_xtile_bytes());
+  float* mu_l = (float*)(smem + 2 * enc_basis_bytes(NB) + kEncWaves * enc_xtile_bytes());
   {
     const float4* mu = (const float4*)(a.state + sl.mu_off);
     for (int i = threadIdx.x; i < F / 4; i += kThreads) ((float4*)mu_l)[i] = mu[i];
   }
+  __syncthreads();  // every wave centres with all of the mean
   // Slice copy: a slice holds 32 * NB rows of kEncKS features, 32 * NB * 8
   // vectors of 16 bytes, so thread t moves vectors t + q * kThreads, q < NB,
   // with no predicate. Rows >= r_enc (zero in the device state when r_enc
@@ -419,13 +431,54 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
     *(uint4*)((BUF) + (idx / (kEncKS / 8)) * kEncRowPad + (idx % (kEncKS / 8)) * 8) = \
         make_uint4(V[4 * q], V[4 * q + 1], V[4 * q + 2], V[4 * q + 3]);              \
   }
-  // Token fragments of one slice: K step s reads features k0 + 16s + 8h .. +8.
-  constexpr int XV = F32IN ? 2 : 1;                  // 16-byte vectors per K step
-  // (ext-vector registers, which stay in registers when passed around)
-#define KVTC_LOAD_X(K0, DST)                                                           \
-  _Pragma("unroll") for (int s = 0; s < 4; ++s)                                        \
-    _Pragma("unroll") for (int v = 0; v < XV; ++v)                                     \
-      DST[s * XV + v] = *(const u32x4*)(xrow + (size_t)((K0) + 16 * s + 8 * h) * esz + 16 * v);
+  // Token rows of one slice, row-contiguous: CH lanes cover the kEncKS
+  // features of a row (16 bytes each), so one load instruction reads RPI
+  // whole row segments and a slice takes NI instructions per wave. Rows past
+  // the tile's last token re-read its first row; their results are dropped.
+  constexpr int CH = kEncKS * esz / 16;   // 16-byte chunks per row segment
+  constexpr int RPI = 64 / CH;            // rows per load instruction
+  constexpr int NI = 32 / RPI;            // load instructions per slice
+  constexpr int EPC = 16 / esz;           // features per chunk
+  const int cx = lane % CH;
+  const uint8_t* const xtile = (const uint8_t*)jd.src + (size_t)(jd.s1 + t0) * row_bytes;
+  uint32_t xoff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t r = (uint32_t)(wave * 32 + i * RPI + lane / CH);
+    xoff[i] = (r < n ? r : 0u) * (uint32_t)row_bytes + (uint32_t)cx * 16u;
+  }
+#define KVTC_LOAD_X(K0, DST) \
+  _Pragma("unroll") for (int i = 0; i < NI; ++i) DST[i] = *(const u32x4*)(xtile + xoff[i] + (size_t)(K0) * esz);
+  // Centre the rows of one slice (x' = bf16_rne(fp32(x) - mu)) into the
+  // wave's token tile: row i * RPI + lane / CH, features cx * EPC .. + EPC.
+  auto stage_x = [&](int k0, const u32x4 (&xr)[NI]) __attribute__((always_inline)) {
+    float mv[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; e += 4) {
+      const float4 m = *(const float4*)(mu_l + k0 + cx * EPC + e);
+      mv[e] = m.x;
+      mv[e + 1] = m.y;
+      mv[e + 2] = m.z;
+      mv[e + 3] = m.w;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      uint16_t* dst = xs + (i * RPI + lane / CH) * kEncRowPad + cx * EPC;
+      if (!F32IN) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pk[e] = pack_bf16x2(bf16_to_f32(xr[i][e] & 0xFFFFu) - mv[2 * e],
+                              bf16_to_f32(xr[i][e] >> 16) - mv[2 * e + 1]);
+        *(uint4*)dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      } else {
+        *(uint2*)dst = make_uint2(pack_bf16x2(__uint_as_float(xr[i][0]) - mv[0],
+                                              __uint_as_float(xr[i][1]) - mv[1]),
+                                  pack_bf16x2(__uint_as_float(xr[i][2]) - mv[2],
+                                              __uint_as_float(xr[i][3]) - mv[3]));
+      }
+    }
+  };
 
   f32x16 acc[NB];
 #pragma unroll
@@ -436,43 +489,20 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
   const int n_sl = F / kEncKS;
   auto slice_k = [&](int i) { return min(i, n_sl - 1) * kEncKS; };
   // One slice: issue the loads of slice it + 2 (basis into vl, tokens into
-  // xl), run the K steps of slice it (tokens xc, basis LDS buffer it % 3),
-  // then move basis slice it + 1 (vs, loaded one slice earlier) into LDS. The
-  // caller rotates the buffers (x with period 3, basis registers with period
-  // 2), so no register is copied and every wait is for loads two slices old.
-  auto step = [&](int it, u32x4 (&xc)[4 * XV], u32x4 (&xl)[4 * XV], vregs_t& vl, vregs_t& vs)
+  // xl, both free since the end of slice it - 1), run the K steps of slice it
+  // (token tile, basis buffer it % 2; K step s takes features 16s + 8h .. +8
+  // of the slice), then stage slice it + 1 (tokens xn, basis vs). The caller
+  // alternates the register sets, so no register is copied and every wait is
+  // for loads issued one slice earlier.
+  auto step = [&](int it, const u32x4 (&xn)[NI], u32x4 (&xl)[NI], vregs_t& vl, vregs_t& vs)
       __attribute__((always_inline)) {
-    const int k0 = it * kEncKS;
     KVTC_LOAD_SLICE(vl, slice_k(it + 2))
     KVTC_LOAD_X(slice_k(it + 2), xl)
-    const uint16_t* vsl = vbase + (it % 3) * slice_elems;
+    const uint16_t* vsl = vbase + (it & 1) * slice_elems;
 #pragma unroll
     for (int s = 0; s < kEncKS / 16; ++s) {
-      const int f = k0 + 16 * s + 8 * h;
-      // Centred token operand: x' = bf16_rne(fp32(x) - mu).
-      float xv[8];
-      if (!F32IN) {
-        const u32x4 raw = xc[s];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          xv[2 * e] = bf16_to_f32(raw[e] & 0xFFFFu);
-          xv[2 * e + 1] = bf16_to_f32(raw[e] >> 16);
-        }
-      } else {
-        const u32x4 lo = xc[2 * s], hi = xc[2 * s + 1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          xv[e] = __uint_as_float(lo[e]);
-          xv[4 + e] = __uint_as_float(hi[e]);
-        }
-      }
-      const float4 m0 = *(const float4*)(mu_l + f);
-      const float4 m1 = *(const float4*)(mu_l + f + 4);
-      const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-      uint32_t pk[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(xv[2 * e] - mv[2 * e], xv[2 * e + 1] - mv[2 * e + 1]);
-      const bf16x8 bx = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+      const uint4 xv = *(const uint4*)(xs + (lane & 31) * kEncRowPad + 16 * s + 8 * h);
+      const bf16x8 bx = __builtin_bit_cast(bf16x8, xv);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const uint4 av = *(const uint4*)(vsl + (b * 32 + (lane & 31)) * kEncRowPad + 16 * s + 8 * h);
@@ -480,25 +510,25 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
                                                          acc[b], 0, 0, 0);
       }
     }
-    // Slice it + 1 to LDS (its buffer was last read in slice it - 2).
-    KVTC_STORE_SLICE(vs, vbase + ((it + 1) % 3) * slice_elems)
+    // The token tile is private to the wave: its reads above come before the
+    // writes below in the wave's LDS order.
+    wave_lds_sync();
+    stage_x(slice_k(it + 1), xn);
+    KVTC_STORE_SLICE(vs, vbase + ((it + 1) & 1) * slice_elems)
     __syncthreads();
   };
-  u32x4 x0[4 * XV], x1[4 * XV], x2[4 * XV];
+  u32x4 x0[NI], x1[NI];
   vregs_t v0, v1;
   KVTC_LOAD_SLICE(v0, 0)
   KVTC_LOAD_X(0, x0)
   KVTC_LOAD_SLICE(v1, slice_k(1))
   KVTC_LOAD_X(slice_k(1), x1)
   KVTC_STORE_SLICE(v0, vbase)
+  stage_x(0, x0);
   __syncthreads();
-  for (int it = 0; it < n_sl; it += 6) {
-    step(it, x0, x2, v0, v1);
-    if (it + 1 < n_sl) step(it + 1, x1, x0, v1, v0);
-    if (it + 2 < n_sl) step(it + 2, x2, x1, v0, v1);
-    if (it + 3 < n_sl) step(it + 3, x0, x2, v1, v0);
-    if (it + 4 < n_sl) step(it + 4, x1, x0, v0, v1);
-    if (it + 5 < n_sl) step(it + 5, x2, x1, v1, v0);
+  for (int it = 0; it < n_sl; it += 2) {
+    step(it, x1, x0, v0, v1);
+    if (it + 1 < n_sl) step(it + 1, x0, x1, v1, v0);
   }
 #undef KVTC_LOAD_SLICE
 #undef KVTC_STORE_SLICE
@@ -606,13 +636,6 @@ __device__ __forceinline__ uint4 frag_from_bits(uint64_t bits, float shift, floa
     pk[j] = pack_f16x2(__builtin_fmaf(q0, step, sh), __builtin_fmaf(q1, step, sh));
   }
   return make_uint4(pk[0], pk[1], pk[2], pk[3]);
-}
-
-// Make this wave's LDS writes visible to its own lanes.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Scatter 16-byte vector v (bytes [16v, 16v+16) of a contiguous run of
