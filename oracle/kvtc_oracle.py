@@ -39,8 +39,9 @@ choice below is marked READING and is the plainest one the text supports:
   Q6  budget B = floor(bits_per_value * F) bits per compressed token, shift and
       scale included, sink and window excluded.
   Q7  DP ties: fewest total bits, then the lexicographically largest widths.
-  N1  A operand x' = bf16_rne(fp32(x) - mu32); operational basis
-      V' = bf16_rne(fp32(V)) restricted to active groups.
+  N1  projection c = fp32 of sum_f (x_f - mu32_f) V'_fj, the centred values
+      and the sum taken exactly (fp64 here: x - mu32 is exact in fp64);
+      operational basis V' = bf16_rne(fp32(V)) restricted to active groups.
   N2  round half to even; clamp to [0, 2^b - 1]; a zero range gives code 0;
       IEEE fp32 division; no fused multiply-add in the quantizer.
   Z0  a dropped (0-bit) component decodes to 0, so it adds nothing to the mean.
@@ -450,9 +451,9 @@ class EncodeResult:
 
 
 def project(x_vals: np.ndarray, slot: Slot) -> np.ndarray:
-    """Centre and project (section 2B): c = fp32(sum_f x'_f V'_fj), fp64 sums."""
-    xc = bf16_rne((x_vals.astype(np.float32) - slot.mu32).astype(np.float32))   # N1
-    return (xc.astype(np.float64) @ slot.basis_bf16().astype(np.float64)).astype(np.float32)
+    """Centre and project (section 2B): c = fp32(sum_f (x_f - mu32_f) V'_fj), fp64 (N1)."""
+    xc = x_vals.astype(np.float64) - slot.mu32.astype(np.float64)
+    return (xc @ slot.basis_bf16().astype(np.float64)).astype(np.float32)
 
 
 def build_records(codes, shift, scale, slot: Slot) -> np.ndarray:

@@ -248,7 +248,7 @@ def check_dp_bruteforce():
 
 
 def check_projection_exact():
-    """c = fp32 of the exact dot product of bf16 operands (section 2B)."""
+    """c = fp32 of the exact sum of (x - mu32) times bf16 V' (section 2B)."""
     rng = np.random.default_rng(6)
     F, r = 64, 32
     V32 = np.linalg.qr(rng.standard_normal((F, F)))[0][:, :r].astype(np.float32)
@@ -257,12 +257,11 @@ def check_projection_exact():
     x = (rng.standard_normal((5, F)) * 3 + mu).astype(np.float32)
     c = O.project(x, sl)
     import torch
-    xc = (torch.from_numpy(x) - torch.from_numpy(mu)).to(torch.bfloat16).double().numpy()
     Vb = torch.from_numpy(V32).to(torch.bfloat16).double().numpy()
     for t in range(5):
         for j in range(r):
-            exact = sum(fractions.Fraction(float(xc[t, f])) * fractions.Fraction(float(Vb[f, j]))
-                        for f in range(F))
+            exact = sum((fractions.Fraction(float(x[t, f])) - fractions.Fraction(float(mu[f]))) *
+                        fractions.Fraction(float(Vb[f, j])) for f in range(F))
             assert c[t, j] == np.float32(float(exact)), (t, j)
 
 
@@ -302,7 +301,7 @@ def check_hadamard_roundtrip_bound():
         er = O.encode(x, p, sl, 0, 0)
         full, _ = O.decode(er.stream, p, sl, 0, 0, T)
         xs = x[2:T - 3]
-        xprime = O.bf16_rne((xs - mu).astype(np.float32)).astype(np.float64)
+        xprime = xs.astype(np.float64) - mu.astype(np.float64)
         err = full[2:T - 3] - mu.astype(np.float64) - xprime
         bound2 = np.zeros(T - 5)
         act = [g for g in range(4) if widths[g]]

@@ -15,13 +15,18 @@ _orig = {name: getattr(O, name) for name in dir(O) if callable(getattr(O, name))
 
 
 def _project_no_centering(x_vals, slot):
-    xc = O.bf16_rne(x_vals.astype(np.float32))
-    return (xc.astype(np.float64) @ slot.basis_bf16().astype(np.float64)).astype(np.float32)
+    xc = x_vals.astype(np.float64)
+    return (xc @ slot.basis_bf16().astype(np.float64)).astype(np.float32)
 
 
 def _project_fp32_basis(x_vals, slot):
+    xc = x_vals.astype(np.float64) - slot.mu32.astype(np.float64)
+    return (xc @ slot.V32.astype(np.float64)).astype(np.float32)
+
+
+def _project_bf16_centred(x_vals, slot):
     xc = O.bf16_rne((x_vals.astype(np.float32) - slot.mu32).astype(np.float32))
-    return (xc.astype(np.float64) @ slot.V32.astype(np.float64)).astype(np.float32)
+    return (xc.astype(np.float64) @ slot.basis_bf16().astype(np.float64)).astype(np.float32)
 
 
 def _dequant_wrong_levels(q, shift, scale, b):
@@ -134,6 +139,7 @@ def _quant_no_clamp(c, b):
 MUTATIONS = {
     "no_centering": ("project", _project_no_centering),
     "fp32_basis_in_projection": ("project", _project_fp32_basis),
+    "bf16_centred_operand": ("project", _project_bf16_centred),
     "dequant_wrong_levels": ("dequantize", _dequant_wrong_levels),
     "dequant_wrong_sign": ("dequantize", _dequant_wrong_sign),
     "pack_msb_first": ("pack_codes", _pack_msb_first),
