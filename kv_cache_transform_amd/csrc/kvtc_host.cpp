@@ -499,7 +499,7 @@ size_t kvtc_device_state_bytes(const kvtc_codec* c) {
     if (!s.calibrated) continue;
     const size_t r_enc = align_up((size_t)s.r_eff, 32), r_dec = align_up((size_t)s.r_eff, 16);
     n += align_up(4 * (size_t)c->F, kAlign) + align_up(2 * r_enc * c->F, kAlign) +
-         align_up(2 * (size_t)c->F * r_dec, kAlign);
+         align_up(2 * (size_t)c->F * r_dec, kAlign) + align_up(4 * r_enc, kAlign);
   }
   return n;
 }
@@ -555,6 +555,18 @@ kvtc_status kvtc_upload(kvtc_codec* c, void* d_state, size_t bytes, hipStream_t 
       for (int j = 0; j < r; ++j)
         vdec[(size_t)f * r_dec + j] = f32_to_f16(bf16_to_f32(f32_to_bf16(s.V32[(size_t)f * r + j])));
     off += align_up(2 * (size_t)F * r_dec, kAlign);
+    // The projection of the mean onto the bf16 basis, V'^T mu32, in fp64
+    // rounded once: the encode multiplies bf16 tokens as they are (exact
+    // operands) and subtracts this per component.
+    d.cmu_off = off;
+    float* cmu = (float*)(h.data() + off);
+    for (int j = 0; j < r; ++j) {
+      double acc = 0.0;
+      for (int f = 0; f < F; ++f)
+        acc += (double)s.mu32[f] * (double)bf16_to_f32(f32_to_bf16(s.V32[(size_t)f * r + j]));
+      cmu[j] = (float)acc;
+    }
+    off += align_up(4 * (size_t)r_enc, kAlign);
   }
   std::memcpy(h.data(), table.data(), table.size() * sizeof(DevSlot));
   hipError_t e = hipMemcpyAsync(d_state, h.data(), need, hipMemcpyHostToDevice, stream);
@@ -699,7 +711,7 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
     a.status = (unsigned long long*)d_ws;
     a.sink = (uint8_t*)d_ws + sink_offset(n);
     a.epoch = next_epoch();
-    uint32_t tiles = 0;
+    uint32_t tiles = 0, ctiles = 0;
     size_t rb_max = 0;
     for (int b = 0; b < a.n_jobs; ++b) {
       JobDesc d = desc[order[p + b]];
@@ -714,6 +726,8 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
         d.n_ctiles = (d.tc + tile - 1) / tile;
       }
       d.tile_begin = tiles;
+      d.ctile_begin = ctiles;
+      if (s.r_eff > 0) ctiles += d.n_ctiles;
       if (mode == Mode::Restore || mode == Mode::UnpackCodes)
         tiles += d.n_ctiles;
       else
@@ -722,11 +736,12 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
       rb_max = std::max(rb_max, (size_t)s.record_bytes);
     }
     a.total_tiles = tiles;
+    a.total_ctiles = ctiles;
     const int k = key[order[p]];
     size_t l = 16;
     const size_t rbp = (size_t)padded_stride((int)rb_max);
     if (mode == Mode::Encode)
-      l = std::max({l, enc_lds_bytes(k, F), (size_t)kEncTile * rbp});
+      l = std::max({l, enc_lds_bytes(k, F, c->p.dtype == KVTC_F32), (size_t)kEncTile * rbp});
     else if (mode == Mode::Pack)
       l = std::max(l, (size_t)kEncTile * rbp);
     else if (mode == Mode::UnpackCodes)

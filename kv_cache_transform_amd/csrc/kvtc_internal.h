@@ -28,6 +28,7 @@ struct alignas(16) DevSlot {
   uint64_t mu_off;        // f32 mu32[F]
   uint64_t venc_off;      // bf16 V'^T [r_enc][F]   (rows >= r_eff are zero)
   uint64_t vdec_off;      // f16  V'   [F][r_dec]   (cols >= r_eff are zero)
+  uint64_t cmu_off;       // f32  V'^T mu32 [r_enc]  (rows >= r_eff are zero)
   uint64_t slot_id;
   int32_t calibrated;
   int32_t n_act;
@@ -53,6 +54,7 @@ struct JobDesc {
   uint32_t tc;             // compressed rows
   uint32_t tile_begin;     // first logical tile of this job
   uint32_t n_ctiles;       // compressed-row tiles
+  uint32_t ctile_begin;    // encode: first compressed tile with records (jobs in order)
   int32_t slot;            // layer * 2 + kind
   int32_t layer;
   int32_t kind;
@@ -69,7 +71,7 @@ struct LaunchArgs {
   int32_t dtype;           // stream / input element type
   int32_t out_dtype;       // decode output element type
   int32_t F;
-  int32_t pad;
+  uint32_t total_ctiles;   // encode: compressed tiles with records
   const uint8_t* state;    // device state base
   unsigned long long* status;  // per-launch slice of the workspace status words
   uint8_t* sink;           // kSinkBytes of workspace that absorb stores without a row
@@ -97,12 +99,15 @@ constexpr int kEncRowPad = kEncKS + 8;     // bf16 elements per LDS basis row
 constexpr int kOutRow = 128 + 16;          // bytes per LDS output-staging row (decode)
 constexpr int kEncWaves = kEncTile / 32;   // encode waves, 32 tokens each
 
-// Encode LDS: two basis slices [32 nb][kEncRowPad] bf16, one token tile
-// [32][kEncRowPad] bf16 per wave, then the mean (F fp32).
+// Encode LDS: two basis slices [32 nb][kEncRowPad] bf16, then per wave its
+// token tiles [32][kEncRowPad] bf16 (one for bf16 input; two, the high and
+// low bf16 parts, for f32 input), then for f32 input the mean (F fp32).
 __host__ __device__ constexpr size_t enc_basis_bytes(int nb) { return (size_t)32 * nb * kEncRowPad * 2; }
-__host__ __device__ constexpr size_t enc_xtile_bytes() { return (size_t)32 * kEncRowPad * 2; }
-__host__ __device__ constexpr size_t enc_lds_bytes(int nb, int F) {
-  return 2 * enc_basis_bytes(nb) + kEncWaves * enc_xtile_bytes() + (size_t)F * 4;
+__host__ __device__ constexpr size_t enc_xtile_bytes(bool f32in) {
+  return (size_t)(f32in ? 2 : 1) * 32 * kEncRowPad * 2;
+}
+__host__ __device__ constexpr size_t enc_lds_bytes(int nb, int F, bool f32in) {
+  return 2 * enc_basis_bytes(nb) + kEncWaves * enc_xtile_bytes(f32in) + (f32in ? (size_t)F * 4 : 0);
 }
 
 // LDS row stride for records under assembly (encode, pack): a multiple of 4

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 
 #include "kvtc_internal.h"
 
@@ -94,11 +95,29 @@ __device__ __forceinline__ uint64_t lds_u64(const uint8_t* p) {
   return (uint64_t)lo | ((uint64_t)hi << 32);
 }
 
+// Device-state slots are read through the constant address space: the
+// state is never written by a kernel, so uniform reads become scalar loads.
+// Vector loads of it would be counted with the token and record traffic, and
+// their waits would drain every load in flight. Sub-dword fields are read
+// as whole dwords (scalar loads are dword-granular).
+typedef const __attribute__((address_space(4))) DevSlot CSlot;
+typedef const __attribute__((address_space(4))) uint32_t CU32;
+__device__ __forceinline__ CSlot& slot_of(const LaunchArgs& a, int s) { return ((CSlot*)a.state)[s]; }
+__device__ __forceinline__ int slot_width(CSlot& sl, int g) {
+  return (int)((((CU32*)sl.width)[g >> 2] >> (8 * (g & 3))) & 0xFFu);
+}
+__device__ __forceinline__ int slot_chunk(CSlot& sl, int g) {
+  return (int)((((CU32*)sl.chunk_off)[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
+}
+static_assert(offsetof(DevSlot, width) % 4 == 0 && offsetof(DevSlot, chunk_off) % 4 == 0,
+              "packed slot arrays are read as dwords");
+static_assert(kMaxActGroups % 4 == 0, "packed slot arrays are read as dwords");
+
 __device__ __forceinline__ size_t record_base(const JobDesc& jd, int F, int esz) {
   return (size_t)kHeaderBytes + (size_t)(jd.s1 + jd.w1) * F * esz;
 }
 
-__device__ void write_header(const LaunchArgs& a, const JobDesc& jd, const DevSlot& sl) {
+__device__ void write_header(const LaunchArgs& a, const JobDesc& jd, CSlot& sl) {
   uint32_t h[16];
   h[0] = 0x4354564Bu;  // "KVTC"
   h[1] = (uint32_t)kFormatVersion | ((uint32_t)a.dtype << 16) | ((uint32_t)jd.kind << 24);
@@ -118,7 +137,7 @@ __device__ void write_header(const LaunchArgs& a, const JobDesc& jd, const DevSl
 }
 
 // Returns KVTC_OK or the status a stream with this header earns.
-__device__ int check_header(const LaunchArgs& a, const JobDesc& jd, const DevSlot& sl) {
+__device__ int check_header(const LaunchArgs& a, const JobDesc& jd, CSlot& sl) {
   const uint32_t* h = (const uint32_t*)jd.src;
   if (h[0] != 0x4354564Bu || (h[1] & 0xFFFFu) != kFormatVersion) return KVTC_E_CORRUPT;
   const uint32_t want1 = (uint32_t)kFormatVersion | ((uint32_t)a.dtype << 16) | ((uint32_t)jd.kind << 24);
@@ -277,11 +296,11 @@ __device__ __forceinline__ uint64_t load_bytes(const uint8_t* p, int n) {
 // Write the G/2 codes a lane holds for active group `a` (half h) and, for
 // h == 0, the group's (shift, scale), into the token's record.
 template <int G>
-__device__ __forceinline__ void put_group(uint8_t* rec, const DevSlot& sl, int a, int h,
+__device__ __forceinline__ void put_group(uint8_t* rec, CSlot& sl, int a, int h,
                                           const uint32_t* codes, float shift, float scale) {
-  const int w = sl.width[a];
+  const int w = slot_width(sl, a);
   const int half_bytes = (G / 2) * w / 8;
-  uint8_t* p = rec + sl.chunk_off[a] + h * half_bytes;
+  uint8_t* p = rec + slot_chunk(sl, a) + h * half_bytes;
   if (G == 16) {
     lds_store_bytes(p, pack_codes(codes, 8, w), w);
   } else {
@@ -341,9 +360,9 @@ __device__ void records_to_global(uint8_t* dst, const uint8_t* lds, uint32_t n, 
 
 // The 8 codes of components [o, o + 8) of active group a from a record:
 // one byte per code in a 64-bit word.
-__device__ __forceinline__ uint64_t get_codes8(const uint8_t* rec, const DevSlot& sl, int a, int o) {
-  const int w = sl.width[a];
-  const uint64_t bits = lds_u64(rec + sl.chunk_off[a] + (o * w) / 8);
+__device__ __forceinline__ uint64_t get_codes8(const uint8_t* rec, CSlot& sl, int a, int o) {
+  const int w = slot_width(sl, a);
+  const uint64_t bits = lds_u64(rec + slot_chunk(sl, a) + (o * w) / 8);
   const uint64_t mask = (1ull << w) - 1ull;
   uint64_t out = 0;
   for (int j = 0; j < 8; ++j) out |= ((bits >> (j * w)) & mask) << (8 * j);
@@ -359,187 +378,38 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // --------------------------------------------------------------- encode ---
 
-template <int NB, int G, bool F32IN>
-__global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  const uint32_t tile = logical_tile();
-  if (tile >= a.total_tiles) return;
-  const int j = find_job(a, tile);
-  const JobDesc& jd = a.jobs[j];
-  const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
-  const uint32_t lt = tile - jd.tile_begin;
-  const int F = a.F;
-  constexpr int esz = F32IN ? 4 : 2;
-  const size_t row_bytes = (size_t)F * esz;
-  if (lt == 0 && threadIdx.x == 0) {
-    write_header(a, jd, sl);
-    set_status(a, jd.status_idx, KVTC_OK);
-  }
-  if (lt >= jd.n_ctiles) {
-    encode_passthrough(jd, lt - jd.n_ctiles, row_bytes);
-    return;
-  }
-  const uint32_t t0 = lt * kEncTile;
-  const uint32_t n = min((uint32_t)kEncTile, jd.tc - t0);
-  const int rb = sl.record_bytes;
-  if (sl.r_eff == 0) return;  // zero-width records: nothing to write
+// Compressed tiles carry their own index space (JobDesc::ctile_begin): the
+// kEncTile-token tiles of every job with records, job after job.
+__device__ __forceinline__ int find_ctile_job(const LaunchArgs& a, uint32_t c) {
+  int j = 0;
+  for (int i = 1; i < a.n_jobs; ++i)
+    if (a.jobs[i].ctile_begin <= c) j = i;
+  return j;
+}
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = lane >> 5;
-  const int tl = wave * 32 + (lane & 31);            // token within the tile
-  const bool tok_ok = (uint32_t)tl < n;
-  const uint16_t* venc = (const uint16_t*)(a.state + sl.venc_off);
-  static_assert(kEncWaves * 64 == kThreads, "one wave per 32 tokens of a tile");
+// The value of lane l ^ 32 (the other half-wave), through
+// v_permlane32_swap: with x in both operands the first result holds the low
+// half in both halves, the second the high half in both.
+__device__ __forceinline__ float xor32(float x, int h) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(h ? r[0] : r[1]);
+}
 
-  // LDS: two basis K-slices [32 * NB][kEncRowPad] bf16, a token tile
-  // [32][kEncRowPad] bf16 per wave, then the mean (F fp32). Basis slices and
-  // token rows are loaded from memory two slices ahead of their use: during
-  // slice i the loads of slice i + 2 are issued, and at the end of slice i
-  // the token rows of slice i + 1 are centred into the wave's token tile and
-  // basis slice i + 1 goes to the other basis buffer (last read in slice
-  // i - 1, before the barrier that ended it). Loads past the last slice
-  // re-read it, so every slice issues the same loads and the waits count
-  // exactly.
-  constexpr int slice_elems = 32 * NB * kEncRowPad;
-  uint16_t* const vbase = (uint16_t*)smem;
-  uint16_t* const xs = (uint16_t*)(smem + 2 * enc_basis_bytes(NB) + wave * enc_xtile_bytes());
-  float* mu_l = (float*)(smem + 2 * enc_basis_bytes(NB) + kEncWaves * enc_xtile_bytes());
-  {
-    const float4* mu = (const float4*)(a.state + sl.mu_off);
-    for (int i = threadIdx.x; i < F / 4; i += kThreads) ((float4*)mu_l)[i] = mu[i];
-  }
-  __syncthreads();  // every wave centres with all of the mean
-  // Slice copy: a slice holds 32 * NB rows of kEncKS features, 32 * NB * 8
-  // vectors of 16 bytes, so thread t moves vectors t + q * kThreads, q < NB,
-  // with no predicate. Rows >= r_enc (zero in the device state when r_enc
-  // < 32 * NB, clamped re-reads otherwise) are never read by the MFMA loop.
-  typedef uint32_t vregs_t __attribute__((ext_vector_type(4 * NB)));
-  const int vlast = sl.r_enc * (kEncKS / 8) - 1;
-#define KVTC_LOAD_SLICE(V, K0)                                                       \
-  _Pragma("unroll") for (int q = 0; q < NB; ++q) {                                   \
-    const int idx = min((int)threadIdx.x + q * kThreads, vlast);                     \
-    const uint4 v = *(const uint4*)(venc + (size_t)(idx / (kEncKS / 8)) * F + (K0) + \
-                                    (idx % (kEncKS / 8)) * 8);                       \
-    V[4 * q] = v.x;                                                                  \
-    V[4 * q + 1] = v.y;                                                              \
-    V[4 * q + 2] = v.z;                                                              \
-    V[4 * q + 3] = v.w;                                                              \
-  }
-#define KVTC_STORE_SLICE(V, BUF)                                                     \
-  _Pragma("unroll") for (int q = 0; q < NB; ++q) {                                   \
-    const int idx = (int)threadIdx.x + q * kThreads;                                 \
-    *(uint4*)((BUF) + (idx / (kEncKS / 8)) * kEncRowPad + (idx % (kEncKS / 8)) * 8) = \
-        make_uint4(V[4 * q], V[4 * q + 1], V[4 * q + 2], V[4 * q + 3]);              \
-  }
-  // Token rows of one slice, row-contiguous: CH lanes cover the kEncKS
-  // features of a row (16 bytes each), so one load instruction reads RPI
-  // whole row segments and a slice takes NI instructions per wave. Rows past
-  // the tile's last token re-read its first row; their results are dropped.
-  constexpr int CH = kEncKS * esz / 16;   // 16-byte chunks per row segment
-  constexpr int RPI = 64 / CH;            // rows per load instruction
-  constexpr int NI = 32 / RPI;            // load instructions per slice
-  constexpr int EPC = 16 / esz;           // features per chunk
-  const int cx = lane % CH;
-  const uint8_t* const xtile = (const uint8_t*)jd.src + (size_t)(jd.s1 + t0) * row_bytes;
-  uint32_t xoff[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const uint32_t r = (uint32_t)(wave * 32 + i * RPI + lane / CH);
-    xoff[i] = (r < n ? r : 0u) * (uint32_t)row_bytes + (uint32_t)cx * 16u;
-  }
-#define KVTC_LOAD_X(K0, DST) \
-  _Pragma("unroll") for (int i = 0; i < NI; ++i) DST[i] = *(const u32x4*)(xtile + xoff[i] + (size_t)(K0) * esz);
-  // Centre the rows of one slice (x' = bf16_rne(fp32(x) - mu)) into the
-  // wave's token tile: row i * RPI + lane / CH, features cx * EPC .. + EPC.
-  auto stage_x = [&](int k0, const u32x4 (&xr)[NI]) __attribute__((always_inline)) {
-    float mv[EPC];
-#pragma unroll
-    for (int e = 0; e < EPC; e += 4) {
-      const float4 m = *(const float4*)(mu_l + k0 + cx * EPC + e);
-      mv[e] = m.x;
-      mv[e + 1] = m.y;
-      mv[e + 2] = m.z;
-      mv[e + 3] = m.w;
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      uint16_t* dst = xs + (i * RPI + lane / CH) * kEncRowPad + cx * EPC;
-      if (!F32IN) {
-        uint32_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pk[e] = pack_bf16x2(bf16_to_f32(xr[i][e] & 0xFFFFu) - mv[2 * e],
-                              bf16_to_f32(xr[i][e] >> 16) - mv[2 * e + 1]);
-        *(uint4*)dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      } else {
-        *(uint2*)dst = make_uint2(pack_bf16x2(__uint_as_float(xr[i][0]) - mv[0],
-                                              __uint_as_float(xr[i][1]) - mv[1]),
-                                  pack_bf16x2(__uint_as_float(xr[i][2]) - mv[2],
-                                              __uint_as_float(xr[i][3]) - mv[3]));
-      }
-    }
-  };
-
-  f32x16 acc[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
-
-  const int n_sl = F / kEncKS;
-  auto slice_k = [&](int i) { return min(i, n_sl - 1) * kEncKS; };
-  // One slice: issue the loads of slice it + 2 (basis into vl, tokens into
-  // xl, both free since the end of slice it - 1), run the K steps of slice it
-  // (token tile, basis buffer it % 2; K step s takes features 16s + 8h .. +8
-  // of the slice), then stage slice it + 1 (tokens xn, basis vs). The caller
-  // alternates the register sets, so no register is copied and every wait is
-  // for loads issued one slice earlier.
-  auto step = [&](int it, const u32x4 (&xn)[NI], u32x4 (&xl)[NI], vregs_t& vl, vregs_t& vs)
-      __attribute__((always_inline)) {
-    KVTC_LOAD_SLICE(vl, slice_k(it + 2))
-    KVTC_LOAD_X(slice_k(it + 2), xl)
-    const uint16_t* vsl = vbase + (it & 1) * slice_elems;
-#pragma unroll
-    for (int s = 0; s < kEncKS / 16; ++s) {
-      const uint4 xv = *(const uint4*)(xs + (lane & 31) * kEncRowPad + 16 * s + 8 * h);
-      const bf16x8 bx = __builtin_bit_cast(bf16x8, xv);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const uint4 av = *(const uint4*)(vsl + (b * 32 + (lane & 31)) * kEncRowPad + 16 * s + 8 * h);
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bx,
-                                                         acc[b], 0, 0, 0);
-      }
-    }
-    // The token tile is private to the wave: its reads above come before the
-    // writes below in the wave's LDS order.
-    wave_lds_sync();
-    stage_x(slice_k(it + 1), xn);
-    KVTC_STORE_SLICE(vs, vbase + ((it + 1) & 1) * slice_elems)
-    __syncthreads();
-  };
-  u32x4 x0[NI], x1[NI];
-  vregs_t v0, v1;
-  KVTC_LOAD_SLICE(v0, 0)
-  KVTC_LOAD_X(0, x0)
-  KVTC_LOAD_SLICE(v1, slice_k(1))
-  KVTC_LOAD_X(slice_k(1), x1)
-  KVTC_STORE_SLICE(v0, vbase)
-  stage_x(0, x0);
-  __syncthreads();
-  for (int it = 0; it < n_sl; it += 2) {
-    step(it, x1, x0, v0, v1);
-    if (it + 1 < n_sl) step(it + 1, x0, x1, v1, v0);
-  }
-#undef KVTC_LOAD_SLICE
-#undef KVTC_STORE_SLICE
-#undef KVTC_LOAD_X
-
-  // Quantize and pack. acc[b][i] holds component 32b + 8(i/4) + 4h + i%4 of
-  // token tl; a group of G components is the item range
-  // [(G/2) * sg, (G/2) * (sg + 1)) of block b with sg = a % (32/G).
-  const int rbp = padded_stride(rb);
-  uint8_t* rec = smem + (size_t)tl * rbp;
+// Quantize the projected tile held in acc (acc[b][i]: component
+// 32b + 8(i/4) + 4h + i%4 of token tl) into the token's LDS record row rec,
+// which the caller has zeroed. Lane h holds, of each group, the runs of four
+// components 8m + 4h .. + 3 (m < G/8): their codes occupy bits
+// [(8m + 4h) w, (8m + 4h + 4) w) of the group's chunk and are merged into
+// the record with at most two 32-bit ORs per run (runs of the two lanes can
+// share a word).
+template <int NB, int G>
+__device__ __forceinline__ void quantize_tile(const f32x16 (&acc)[NB], CSlot& sl, uint8_t* rec,
+                                              int h, bool tok_ok) {
+  // A group of G components is the item range [(G/2) * sg, (G/2) * (sg + 1))
+  // of block b with sg = a % (32/G).
   constexpr int SUB = 32 / G;
+  uint32_t* const rw = (uint32_t*)rec;   // rec is 4-byte aligned (padded_stride)
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
 #pragma unroll
@@ -555,47 +425,333 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const LaunchArgs a) {
           mn = fminf(mn, v[i]);
           mx = fmaxf(mx, v[i]);
         }
-        mn = fminf(mn, __shfl_xor(mn, 32));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const int w = sl.width[ag];
+        mn = fminf(mn, xor32(mn, h));
+        mx = fmaxf(mx, xor32(mx, h));
+        const int w = slot_width(sl, ag);
         const float k = (float)((1 << w) - 1);
         const float scale = mx - mn;
         const float inv = scale > 0.f ? k / scale : 0.f;
-        uint32_t quad[G / 8];
+        const uint32_t base = 8u * slot_chunk(sl, ag);   // chunk bit offset in the record
 #pragma unroll
         for (int m = 0; m < G / 8; ++m) {
-          uint32_t word = 0;
+          uint32_t run = 0;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float d = v[4 * m + e] - mn;
             const float u = d * inv;
             const float r = fminf(fmaxf(__builtin_rintf(u), 0.f), k);
-            word |= (uint32_t)r << (8 * e);
+            run |= (uint32_t)r << (e * w);
           }
-          quad[m] = word;
+          const uint32_t pos = base + (uint32_t)(8 * m + 4 * h) * (uint32_t)w;
+          const uint32_t sh = pos & 31u;
+          if (tok_ok) {
+            atomicOr(rw + (pos >> 5), run << sh);
+            if (sh + 4u * (uint32_t)w > 32u) atomicOr(rw + (pos >> 5) + 1, run >> (32u - sh));
+          }
         }
-        // Lane h holds the group's component quads 2m + h; gather quads
-        // [h * G/8, (h + 1) * G/8) so each lane packs G/2 consecutive codes.
-        uint32_t recv[G / 8];
-#pragma unroll
-        for (int m = 0; m < G / 8; ++m) recv[m] = __shfl_xor(quad[m], 32);
-        uint32_t codes[G / 2];
-#pragma unroll
-        for (int m = 0; m < G / 8; ++m) {
-          const int q0 = m, q1 = G / 8 + m;  // target quad for h = 0 / h = 1
-          const uint32_t c0 = (q0 % 2 == 0) ? quad[q0 / 2] : recv[q0 / 2];
-          const uint32_t c1 = (q1 % 2 == 1) ? quad[q1 / 2] : recv[q1 / 2];
-          const uint32_t word = h ? c1 : c0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) codes[4 * m + e] = (word >> (8 * e)) & 0xFFu;
+        if (tok_ok && h == 0) {
+          rw[2 * ag] = __float_as_uint(mn);
+          rw[2 * ag + 1] = __float_as_uint(scale);
         }
-        if (tok_ok) put_group<G>(rec, sl, ag, h, codes, mn, scale);
+      }
+      // One group at a time: interleaving them only raises register pressure.
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Persistent encode. Each workgroup first writes the headers and passthrough
+// units u = g, g + grid, ... of the launch, then projects, quantizes and
+// packs an equal contiguous range of the compressed tiles. Its four waves
+// take 32 tokens of a tile each; the K loop walks slices of kEncKS features.
+// The slice pipeline runs across tile boundaries: a load cursor two slices
+// ahead of the computation moves on into the next tile of the range, so the
+// loads of a tile's first slices are in flight during the previous tile's
+// quantization, and the pipeline fills once per workgroup.
+template <int NB, int G, bool F32IN, bool ODD>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!F32IN && NB <= 3 ? 3 : 1))) void encode_kernel(const LaunchArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t g = logical_tile();
+  const int F = a.F;
+  constexpr int esz = F32IN ? 4 : 2;
+  const size_t row_bytes = (size_t)F * esz;
+  for (uint32_t u = g; u < a.total_tiles; u += gridDim.x) {
+    const JobDesc& jd = a.jobs[find_job(a, u)];
+    const uint32_t lt = u - jd.tile_begin;
+    if (lt == 0 && threadIdx.x == 0) {
+      write_header(a, jd, slot_of(a, jd.slot));
+      set_status(a, jd.status_idx, KVTC_OK);
+    }
+    if (lt >= jd.n_ctiles) encode_passthrough(jd, lt - jd.n_ctiles, row_bytes);
+  }
+  const uint32_t C = a.total_ctiles;
+  const uint32_t c_begin = (uint32_t)((uint64_t)C * g / gridDim.x);
+  const uint32_t c_end = (uint32_t)((uint64_t)C * (g + 1) / gridDim.x);
+  if (c_begin >= c_end) return;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5;
+  const int tl = wave * 32 + (lane & 31);            // token within the tile
+  static_assert(kEncWaves * 64 == kThreads, "one wave per 32 tokens of a tile");
+
+  // LDS: two basis K-slices [32 * NB][kEncRowPad] bf16, the wave's token
+  // tiles [32][kEncRowPad] bf16 (one; for f32 input two, high and low part),
+  // then for f32 input the mean (F fp32). Basis slices and token rows are
+  // loaded from memory two slices ahead of their use: during slice i the
+  // loads of slice i + 2 are issued, and at the end of slice i the token rows
+  // of slice i + 1 go to the wave's token tiles and basis slice i + 1 to the
+  // other basis buffer (last read in slice i - 1, before the barrier that
+  // ended it). After a tile's last slice the records are assembled in LDS
+  // from offset 0, then slice 0 of the next tile is staged. Loads past the
+  // range's last slice re-read it, so every slice issues the same loads and
+  // the waits count exactly.
+  //
+  // The projection c = (x - mu) V' is taken as x V' - mu V': a bf16 token is
+  // an exact MFMA operand, so only the fp32 sums round, and mu V' (fp64,
+  // rounded once, in the device state) is subtracted per component at the
+  // end. An f32 token is centred in fp32 and split into two bf16 operands
+  // hi = bf16(x - mu), lo = bf16(x - mu - hi), both multiplied.
+  constexpr int slice_elems = 32 * NB * kEncRowPad;
+  constexpr int XT = 32 * kEncRowPad;   // elements per token tile
+  uint16_t* const vbase = (uint16_t*)smem;
+  uint16_t* const xs = (uint16_t*)(smem + 2 * enc_basis_bytes(NB) + wave * enc_xtile_bytes(F32IN));
+  float* const mu_l = (float*)(smem + 2 * enc_basis_bytes(NB) + kEncWaves * enc_xtile_bytes(F32IN));
+  const int n_sl = F / kEncKS;   // odd exactly when ODD (the host picks the kernel)
+
+  // Load cursor: tile lc, slice lk; the tile's basis and token row offsets.
+  // Rows past the tile's last token re-read its first row; their results
+  // are dropped.
+  constexpr int CH = kEncKS * esz / 16;   // 16-byte chunks per row segment
+  constexpr int RPI = 64 / CH;            // rows per load instruction
+  constexpr int NI = 32 / RPI;            // load instructions per slice
+  constexpr int EPC = 16 / esz;           // features per chunk
+  const int cx = lane % CH;
+  uint32_t lc = c_begin;
+  int lk = 0;
+  const uint16_t* l_venc;
+  const uint8_t* l_x;
+  const float* l_mu;
+  uint32_t xoff[NI];
+  auto cursor_tile = [&](uint32_t c) __attribute__((always_inline)) {
+    const JobDesc& jd = a.jobs[find_ctile_job(a, c)];
+    CSlot& sl = slot_of(a, jd.slot);
+    const uint32_t t0 = (c - jd.ctile_begin) * kEncTile;
+    const uint32_t n = min((uint32_t)kEncTile, jd.tc - t0);
+    l_venc = (const uint16_t*)(a.state + sl.venc_off);
+    l_mu = (const float*)(a.state + sl.mu_off);
+    l_x = (const uint8_t*)jd.src + (size_t)(jd.s1 + t0) * row_bytes;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t r = (uint32_t)(wave * 32 + i * RPI + lane / CH);
+      xoff[i] = (r < n ? r : 0u) * (uint32_t)row_bytes + (uint32_t)cx * 16u;
+    }
+  };
+  auto cursor_next = [&]() __attribute__((always_inline)) {
+    if (lk + 1 < n_sl) {
+      ++lk;
+    } else if (lc + 1 < c_end) {
+      ++lc;
+      lk = 0;
+      cursor_tile(lc);
+    }
+  };
+  cursor_tile(lc);
+
+  // Slice copy: a slice holds 32 * NB rows of kEncKS features, 32 * NB * 8
+  // vectors of 16 bytes, so thread t moves vectors t + q * kThreads, q < NB,
+  // with no predicate. Every job of a launch has r_enc = 32 * NB; rows >=
+  // r_eff are zero in the device state.
+  typedef uint32_t vregs_t __attribute__((ext_vector_type(4 * NB)));
+#define KVTC_LOAD_SLICE(V)                                                              \
+  _Pragma("unroll") for (int q = 0; q < NB; ++q) {                                      \
+    const int idx = (int)threadIdx.x + q * kThreads;                                    \
+    const uint4 v = *(const uint4*)(l_venc + (size_t)(idx / (kEncKS / 8)) * F +          \
+                                    lk * kEncKS + (idx % (kEncKS / 8)) * 8);            \
+    V[4 * q] = v.x;                                                                     \
+    V[4 * q + 1] = v.y;                                                                 \
+    V[4 * q + 2] = v.z;                                                                 \
+    V[4 * q + 3] = v.w;                                                                 \
+  }
+#define KVTC_STORE_SLICE(V, BUF)                                                     \
+  _Pragma("unroll") for (int q = 0; q < NB; ++q) {                                   \
+    const int idx = (int)threadIdx.x + q * kThreads;                                 \
+    *(uint4*)((BUF) + (idx / (kEncKS / 8)) * kEncRowPad + (idx % (kEncKS / 8)) * 8) = \
+        make_uint4(V[4 * q], V[4 * q + 1], V[4 * q + 2], V[4 * q + 3]);              \
+  }
+#define KVTC_LOAD_X(DST) \
+  _Pragma("unroll") for (int i = 0; i < NI; ++i) DST[i] = *(const u32x4*)(l_x + xoff[i] + (size_t)lk * kEncKS * esz);
+  // Rows of one slice into the wave's token tiles: row i * RPI + lane / CH,
+  // features cx * EPC .. + EPC. bf16 rows are stored as loaded; f32 rows are
+  // centred with the mean of their tile's job (mu_l, staged with slice 0).
+  auto stage_x = [&](int k0, const u32x4 (&xr)[NI]) __attribute__((always_inline)) {
+    if (!F32IN) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        *(u32x4*)(xs + (i * RPI + lane / CH) * kEncRowPad + cx * EPC) = xr[i];
+    } else {
+      const float4 m = *(const float4*)(mu_l + k0 + cx * EPC);
+      const float mv[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        uint32_t hi[2], lo[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float d0 = __uint_as_float(xr[i][2 * e]) - mv[2 * e];
+          const float d1 = __uint_as_float(xr[i][2 * e + 1]) - mv[2 * e + 1];
+          hi[e] = pack_bf16x2(d0, d1);
+          lo[e] = pack_bf16x2(d0 - bf16_to_f32(hi[e] & 0xFFFFu), d1 - bf16_to_f32(hi[e] >> 16));
+        }
+        uint16_t* dst = xs + (i * RPI + lane / CH) * kEncRowPad + cx * EPC;
+        *(uint2*)dst = make_uint2(hi[0], hi[1]);
+        *(uint2*)(dst + XT) = make_uint2(lo[0], lo[1]);
+      }
+    }
+  };
+  // Slice 0 of a tile: its job's mean (f32 input), basis and token rows.
+  auto stage_first = [&](const float* mu, const u32x4 (&xr)[NI], const vregs_t& v)
+      __attribute__((always_inline)) {
+    if (F32IN) {
+      for (int i = threadIdx.x; i < F / 4; i += kThreads) ((float4*)mu_l)[i] = ((const float4*)mu)[i];
+      __syncthreads();
+    }
+    stage_x(0, xr);
+    KVTC_STORE_SLICE(v, vbase)
+    __syncthreads();
+  };
+
+  // acc[b][i] holds component 32b + 8(i/4) + 4h + i%4 of token tl. It
+  // starts at -mu V' for bf16 input (the x V' - mu V' form), at 0 for f32.
+  f32x16 acc[NB];
+  auto init_acc = [&](uint32_t c) __attribute__((always_inline)) {
+    if (F32IN) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
+    } else {
+      // Scalar loads (constant address space): items 32b + 8q + e of the
+      // low half-wave, + 4 for the high one.
+      CSlot& sl = slot_of(a, a.jobs[find_ctile_job(a, c)].slot);
+      CU32* cmu = (CU32*)(a.state + sl.cmu_off);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float lo = __uint_as_float(cmu[32 * b + 8 * q + e]);
+            const float hi = __uint_as_float(cmu[32 * b + 8 * q + 4 + e]);
+            acc[b][4 * q + e] = -(h ? hi : lo);
+          }
+    }
+  };
+  // One slice: run the K steps of slice it (token tile, basis buffer it % 2;
+  // K step s takes features 16s + 8h .. +8 of the slice), issue the loads at
+  // the load cursor (basis into vl, tokens into xl, both free since the end
+  // of slice it - 1; mul is the mean of the tile they belong to), then,
+  // unless it is the tile's last slice,
+  // stage slice it + 1 (tokens xn, basis vs). The caller alternates the
+  // register sets, so no register is copied and every wait is for loads
+  // issued one slice earlier.
+  auto step = [&](int it, const u32x4 (&xn)[NI], u32x4 (&xl)[NI], vregs_t& vl, vregs_t& vs,
+                  const float*& mul) __attribute__((always_inline)) {
+    const uint16_t* vsl = vbase + (it & 1) * slice_elems;
+#pragma unroll
+    for (int s = 0; s < kEncKS / 16; ++s) {
+      const int xo = (lane & 31) * kEncRowPad + 16 * s + 8 * h;
+      const bf16x8 bx = __builtin_bit_cast(bf16x8, *(const uint4*)(xs + xo));
+      bf16x8 bl;
+      if (F32IN) bl = __builtin_bit_cast(bf16x8, *(const uint4*)(xs + XT + xo));
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const bf16x8 av = __builtin_bit_cast(
+            bf16x8, *(const uint4*)(vsl + (b * 32 + (lane & 31)) * kEncRowPad + 16 * s + 8 * h));
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bx, acc[b], 0, 0, 0);
+        if (F32IN) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl, acc[b], 0, 0, 0);
+      }
+    }
+    // The loads go after the MFMA issue: when the memory pipeline is backed
+    // up, issuing them stalls the wave, and the MFMAs then run meanwhile.
+    __builtin_amdgcn_sched_barrier(0);
+    KVTC_LOAD_SLICE(vl)
+    KVTC_LOAD_X(xl)
+    mul = l_mu;
+    cursor_next();
+    // The token tile is private to the wave: its reads above come before the
+    // writes below in the wave's LDS order. After a tile's last slice this
+    // stages the next tile's slice 0, which the records then overwrite; it
+    // is staged again from the same registers after them.
+    wave_lds_sync();
+    stage_x(((it + 1) % n_sl) * kEncKS, xn);
+    KVTC_STORE_SLICE(vs, vbase + ((it + 1) & 1) * slice_elems)
+    __syncthreads();
+  };
+
+  u32x4 x0[NI], x1[NI];
+  vregs_t v0, v1;
+  const float *mu0 = l_mu, *mu1;   // the mean of the tile in x0 / x1
+  KVTC_LOAD_SLICE(v0)
+  KVTC_LOAD_X(x0)
+  cursor_next();
+  mu1 = l_mu;
+  KVTC_LOAD_SLICE(v1)
+  KVTC_LOAD_X(x1)
+  cursor_next();
+  init_acc(c_begin);
+  stage_first(mu0, x0, v0);
+  for (uint32_t c = c_begin; c < c_end; ++c) {
+    const JobDesc& jd = a.jobs[find_ctile_job(a, c)];
+    CSlot& sl = slot_of(a, jd.slot);
+    const uint32_t t0 = (c - jd.ctile_begin) * kEncTile;
+    const uint32_t n = min((uint32_t)kEncTile, jd.tc - t0);
+    // The loop runs whole pairs of steps and an odd last slice follows it,
+    // so the loop is only re-entered after a pair; with the parity fixed at
+    // compile time every path into the loop has the same loads in flight and
+    // the waits the compiler derives at its head cover just those.
+    int it = 0;
+    for (; it + 1 < n_sl; it += 2) {
+      step(it, x1, x0, v0, v1, mu0);
+      step(it + 1, x0, x1, v1, v0, mu1);
+    }
+    if (ODD) step(it, x1, x0, v0, v1, mu0);
+    __syncthreads();  // every wave is done with the slices in LDS
+    const int rb = sl.record_bytes;
+    const int rbp = padded_stride(rb);
+    {
+      // Zero the wave's 32 record rows (16-byte aligned: rbp % 4 == 0).
+      u32x4* z = (u32x4*)(smem + (size_t)wave * 32 * rbp);
+      const int nz = 32 * rbp / 16;
+      for (int i = lane; i < nz; i += 64) z[i] = (u32x4){0u, 0u, 0u, 0u};
+      wave_lds_sync();
+    }
+    quantize_tile<NB, G>(acc, sl, smem + (size_t)tl * rbp, h, (uint32_t)tl < n);
+    if (c + 1 < c_end) init_acc(c + 1);
+    __syncthreads();
+    records_to_global((uint8_t*)jd.dst + record_base(jd, F, esz) + (size_t)t0 * rb, smem, n, rb, rbp);
+    if (c + 1 < c_end) {
+      __syncthreads();  // the records are out of LDS
+      if (ODD) {
+        // Odd slice count: the next tile's slice 0 is in (x1, v1), slice 1
+        // in (x0, v0); swap so the tile starts like the first one.
+        stage_first(mu1, x1, v1);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const u32x4 t = x0[i];
+          x0[i] = x1[i];
+          x1[i] = t;
+        }
+        const vregs_t t = v0;
+        v0 = v1;
+        v1 = t;
+        mu1 = mu0;
+      } else {
+        stage_first(mu0, x0, v0);
       }
     }
   }
-  __syncthreads();
-  uint8_t* dst = (uint8_t*)jd.dst + record_base(jd, F, esz) + (size_t)t0 * rb;
-  records_to_global(dst, smem, n, rb, rbp);
+#undef KVTC_LOAD_SLICE
+#undef KVTC_STORE_SLICE
+#undef KVTC_LOAD_X
 }
 
 // --------------------------------------------------------------- decode ---
@@ -680,7 +836,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
   if (tile >= a.total_tiles) return;
   const int j = find_job(a, tile);
   const JobDesc& jd = a.jobs[j];
-  const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
+  CSlot& sl = slot_of(a, jd.slot);
   const uint32_t lt = tile - jd.tile_begin;
   if (threadIdx.x == 0) flag = check_header(a, jd, sl);
   __syncthreads();
@@ -730,8 +886,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
         if (c < r_eff) {
           const int ag = c / G, o = c - ag * G;
           ag_s[s] = ag;
-          w_s[s] = sl.width[ag];
-          off_s[s] = sl.chunk_off[ag] + (o * w_s[s]) / 8;
+          w_s[s] = slot_width(sl, ag);
+          off_s[s] = slot_chunk(sl, ag) + (o * w_s[s]) / 8;
         }
       }
       auto shift_scale = [&](int s) -> float2 {
@@ -788,7 +944,7 @@ __device__ void gemm_segment(const LaunchArgs& a, int j, uint32_t slab, uint32_t
   constexpr int KA = KS > 0 ? KS : 1;
   constexpr int AST = KS * 32 + 16;               // LDS bytes per V' row
   const JobDesc& jd = a.jobs[j];
-  const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
+  CSlot& sl = slot_of(a, jd.slot);
   if (prior_rank(a, jd.status_idx) != 0) return;  // stage 1 rejected it
   const int F = a.F;
   const int f0 = (int)slab * FS;
@@ -951,7 +1107,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const LaunchArgs a, ui
   const uint32_t tile = logical_tile();
   if (tile >= a.total_tiles) return;
   const JobDesc& jd = a.jobs[0];
-  const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
+  CSlot& sl = slot_of(a, jd.slot);
   const uint32_t lt = tile - jd.tile_begin;
   if (lt >= jd.n_ctiles || sl.r_eff == 0) return;
   const uint32_t t0 = lt * kUnpackTile;
@@ -985,7 +1141,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const LaunchArgs a, cons
   const uint32_t tile = logical_tile();
   if (tile >= a.total_tiles) return;
   const JobDesc& jd = a.jobs[0];
-  const DevSlot& sl = ((const DevSlot*)a.state)[jd.slot];
+  CSlot& sl = slot_of(a, jd.slot);
   const uint32_t lt = tile - jd.tile_begin;
   const int esz = a.dtype == KVTC_F32 ? 4 : 2;
   const size_t row_bytes = (size_t)a.F * esz;
@@ -1029,14 +1185,44 @@ static void allow_lds(K kernel, size_t lds) {
   if (lds > 65536) hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
-template <int G, bool F32IN>
+// Workgroups of `kernel` (threads, lds bytes) resident on the current
+// device at once, a multiple of 8, at least 8.
+template <class K>
+static uint32_t resident_grid(K kernel, int threads, size_t lds) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kernel, threads, lds) != hipSuccess)
+    return 8;
+  const uint32_t n = (uint32_t)std::max(1, per_cu) * (uint32_t)std::max(1, cus);
+  return std::max(8u, n / 8u * 8u);
+}
+
+// Optional cap on the persistent encode grid (environment variable
+// KVTC_MAX_WORKGROUPS, rounded down to a multiple of 8, at least 8): fewer
+// workgroups each walk more tiles. Unset or invalid: no cap.
+static uint32_t encode_grid_cap() {
+  const char* e = std::getenv("KVTC_MAX_WORKGROUPS");
+  if (!e || !*e) return UINT32_MAX;
+  char* end = nullptr;
+  const long v = std::strtol(e, &end, 10);
+  if (end == e || *end || v <= 0) return UINT32_MAX;
+  return std::max<uint32_t>(8u, (uint32_t)std::min<long>(v, 1L << 20) / 8u * 8u);
+}
+
+template <int G, bool F32IN, bool ODD>
 static int launch_encode_g(const LaunchArgs& a, int nb, size_t lds, hipStream_t s) {
-  const dim3 g = grid_for(a.total_tiles);
-#define KVTC_ENC(NBV)                                                                  \
-  case NBV:                                                                            \
-    allow_lds(encode_kernel<NBV, G, F32IN>, lds);                                      \
-    hipLaunchKernelGGL((encode_kernel<NBV, G, F32IN>), g, dim3(kThreads), lds, s, a);  \
-    break;
+  // Persistent: the resident workgroups, or fewer when there are fewer
+  // compressed tiles (any grid covers the headers and passthrough units).
+#define KVTC_ENC(NBV)                                                                      \
+  case NBV: {                                                                              \
+    allow_lds(encode_kernel<NBV, G, F32IN, ODD>, lds);                                     \
+    const dim3 g(std::min({grid_for(std::max(1u, a.total_ctiles)).x,                       \
+                           resident_grid(encode_kernel<NBV, G, F32IN, ODD>, kThreads, lds), \
+                           encode_grid_cap()}));                                           \
+    hipLaunchKernelGGL((encode_kernel<NBV, G, F32IN, ODD>), g, dim3(kThreads), lds, s, a); \
+    break;                                                                                 \
+  }
   switch (nb) {
     KVTC_ENC(1) KVTC_ENC(2) KVTC_ENC(3) KVTC_ENC(4) KVTC_ENC(5) KVTC_ENC(6) KVTC_ENC(7) KVTC_ENC(8)
     default:
@@ -1048,8 +1234,16 @@ static int launch_encode_g(const LaunchArgs& a, int nb, size_t lds, hipStream_t 
 
 int launch_encode(const LaunchArgs& a, int nb, int G, size_t lds, hipStream_t s) {
   const bool f32 = a.dtype == KVTC_F32;
-  if (G == 16) return f32 ? launch_encode_g<16, true>(a, nb, lds, s) : launch_encode_g<16, false>(a, nb, lds, s);
-  if (G == 32) return f32 ? launch_encode_g<32, true>(a, nb, lds, s) : launch_encode_g<32, false>(a, nb, lds, s);
+  const bool odd = (a.F / kEncKS) & 1;
+#define KVTC_ENC_G(GV)                                                                   \
+  if (G == GV)                                                                           \
+    return f32 ? (odd ? launch_encode_g<GV, true, true>(a, nb, lds, s)                   \
+                      : launch_encode_g<GV, true, false>(a, nb, lds, s))                 \
+               : (odd ? launch_encode_g<GV, false, true>(a, nb, lds, s)                  \
+                      : launch_encode_g<GV, false, false>(a, nb, lds, s));
+  KVTC_ENC_G(16)
+  KVTC_ENC_G(32)
+#undef KVTC_ENC_G
   return (int)hipErrorInvalidValue;
 }
 
@@ -1073,19 +1267,6 @@ int launch_prep(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
   }
 #undef KVTC_PREP
   return (int)hipGetLastError();
-}
-
-// Workgroups of `kernel` (threads, lds bytes) resident on the current
-// device at once, a multiple of 8, at least 8.
-template <class K>
-static uint32_t resident_grid(K kernel, int threads, size_t lds) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kernel, threads, lds) != hipSuccess)
-    return 8;
-  const uint32_t n = (uint32_t)std::max(1, per_cu) * (uint32_t)std::max(1, cus);
-  return std::max(8u, n / 8u * 8u);
 }
 
 template <bool OUT32>

@@ -74,7 +74,9 @@ class Workload:
         return self.n_tensors * self.n_tokens * self.features * self.elem_bytes
 
 
-# The five workloads.  bits_per_value = 16 / ratio for 16-bit KV.
+# The five workloads of the pages, then two small shapes whose feature
+# count is an odd multiple of 64 (parity cases only).  bits_per_value =
+# 16 / ratio for 16-bit KV.
 WORKLOADS = {
     "tiny": Workload("tiny", 0, 1, (K,), 2, 64, 512, 1, 2048, "f32", 4, 64, 16,
                      2.0, "A", 16),
@@ -89,6 +91,10 @@ WORKLOADS = {
     "qwen25_7b_paged": Workload("qwen25_7b_paged", 4, 28, (K, V), 4, 128, 8192,
                                 16, 16384, "bf16", 4, 128, 16, 0.8, "B", 96,
                                 paged=True),
+    "odd3_bf16": Workload("odd3_bf16", 5, 1, (K, V), 3, 64, 1100, 1, 2048,
+                          "bf16", 4, 64, 16, 2.0, "B", 48),
+    "odd1_f32": Workload("odd1_f32", 6, 1, (K,), 1, 64, 2100, 1, 2048, "f32", 4,
+                         32, 16, 3.0, "A", 16),
 }
 
 

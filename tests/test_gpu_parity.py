@@ -35,6 +35,9 @@ CASES = {
     "llama33_70b_16x": ("llama33_70b_16x", [(0, 0), (0, 1)], 16384, 1, 4096),
     "llama33_70b_64x": ("llama33_70b_64x", [(0, 0), (0, 1)], 16384, 1, 4096),
     "qwen25_7b_paged": ("qwen25_7b_paged", [(0, 0), (0, 1)], 8192, 2, 4096),
+    # feature counts 192 and 64: an odd number of 64-feature slices
+    "odd3_bf16": ("odd3_bf16", [(0, 0), (0, 1)], 1100, 1, None),
+    "odd1_f32": ("odd1_f32", [(0, 0)], 2100, 1, None),
 }
 
 
@@ -77,6 +80,20 @@ def _decode_check(w, op, slot, ref_stream, T, out, out_dtype, layer, kind, rows=
 
 @pytest.mark.parametrize("case", list(CASES))
 def test_encode_parity(case):
+    _check_encode(case)
+
+
+# A persistent encode workgroup walks a contiguous range of tiles, with the
+# next tile's first slices in flight during a tile's quantization. Capping
+# the grid at 8 workgroups gives each one many tiles, across job boundaries,
+# with an even (llama31_8b) and an odd (odd3_bf16, odd1_f32) slice count.
+@pytest.mark.parametrize("case", ["llama31_8b", "odd3_bf16", "odd1_f32"])
+def test_encode_parity_few_workgroups(case, monkeypatch):
+    monkeypatch.setenv("KVTC_MAX_WORKGROUPS", "8")
+    _check_encode(case)
+
+
+def _check_encode(case):
     w, art, op, items = _setup(case)
     dc = DevCodec(art.serialize())
     devs = [storage_to_dev(store) for _, _, store, _ in items]
