@@ -224,11 +224,13 @@ def main():
     pass_rows = T - tc
     # Algorithmic HBM bytes of one call of each kernel, per launch: what the
     # kernel must read and write at least.
-    #  encode: the KV rows, the streams, the bf16 basis and fp32 mean per tensor
+    #  encode: the KV rows, the streams, the bf16 basis per tensor, and its
+    #          fp32 mean (f32 input) or the mean's projection mu V' (bf16 input)
     #  decode stage 1: the streams, the staging it writes, passthrough rows out
     #  decode stage 2: the staging, the compressed rows out, fp16 basis + mean
     staging = n_stg
-    enc_alg = kv_bytes + stream_total + sum(((r_eff[(l, k)] + 31) // 32 * 32) * F * 2 + F * 4
+    r_enc = {s: (r + 31) // 32 * 32 for s, r in r_eff.items()}
+    enc_alg = kv_bytes + stream_total + sum(r_enc[(l, k)] * F * 2 + (F * 4 if esz == 4 else r_enc[(l, k)] * 4)
                                             for l, k, _ in jobs)
     prep_alg = stream_total + staging + n_jobs * pass_rows * F * esz
     gemm_alg = staging + n_jobs * tc * F * esz + sum(((r_eff[(l, k)] + 15) // 16 * 16) * F * 2 + F * 4
