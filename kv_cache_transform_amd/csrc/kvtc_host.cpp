@@ -711,7 +711,7 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
     a.status = (unsigned long long*)d_ws;
     a.sink = (uint8_t*)d_ws + sink_offset(n);
     a.epoch = next_epoch();
-    uint32_t tiles = 0, ctiles = 0;
+    uint32_t tiles = 0, cblks = 0;
     size_t rb_max = 0;
     for (int b = 0; b < a.n_jobs; ++b) {
       JobDesc d = desc[order[p + b]];
@@ -726,8 +726,8 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
         d.n_ctiles = (d.tc + tile - 1) / tile;
       }
       d.tile_begin = tiles;
-      d.ctile_begin = ctiles;
-      if (s.r_eff > 0) ctiles += d.n_ctiles;
+      d.cblk_begin = cblks;
+      if (s.r_eff > 0) cblks += (d.tc + kEncBlk - 1) / kEncBlk;
       if (mode == Mode::Restore || mode == Mode::UnpackCodes)
         tiles += d.n_ctiles;
       else
@@ -736,7 +736,7 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
       rb_max = std::max(rb_max, (size_t)s.record_bytes);
     }
     a.total_tiles = tiles;
-    a.total_ctiles = ctiles;
+    a.total_cblks = cblks;
     const int k = key[order[p]];
     size_t l = 16;
     const size_t rbp = (size_t)padded_stride((int)rb_max);

@@ -54,7 +54,7 @@ struct JobDesc {
   uint32_t tc;             // compressed rows
   uint32_t tile_begin;     // first logical tile of this job
   uint32_t n_ctiles;       // compressed-row tiles
-  uint32_t ctile_begin;    // encode: first compressed tile with records (jobs in order)
+  uint32_t cblk_begin;     // encode: first 32-token block with records (jobs in order)
   int32_t slot;            // layer * 2 + kind
   int32_t layer;
   int32_t kind;
@@ -71,7 +71,7 @@ struct LaunchArgs {
   int32_t dtype;           // stream / input element type
   int32_t out_dtype;       // decode output element type
   int32_t F;
-  uint32_t total_ctiles;   // encode: compressed tiles with records
+  uint32_t total_cblks;    // encode: 32-token blocks with records
   const uint8_t* state;    // device state base
   unsigned long long* status;  // per-launch slice of the workspace status words
   uint8_t* sink;           // kSinkBytes of workspace that absorb stores without a row
@@ -97,7 +97,8 @@ constexpr int kPassRows = 16;
 constexpr int kEncKS = 64;                 // features per LDS basis slice (encode)
 constexpr int kEncRowPad = kEncKS + 8;     // bf16 elements per LDS basis row
 constexpr int kOutRow = 128 + 16;          // bytes per LDS output-staging row (decode)
-constexpr int kEncWaves = kEncTile / 32;   // encode waves, 32 tokens each
+constexpr int kEncBlk = 32;                // encode tokens per wave (one block)
+constexpr int kEncWaves = kEncTile / kEncBlk;   // encode waves per tile
 
 // Encode LDS: two basis slices [32 nb][kEncRowPad] bf16, then per wave its
 // token tiles [32][kEncRowPad] bf16 (one for bf16 input; two, the high and

@@ -137,8 +137,10 @@ __device__ void write_header(const LaunchArgs& a, const JobDesc& jd, CSlot& sl) 
 }
 
 // Returns KVTC_OK or the status a stream with this header earns.
+// (Read through the constant address space: uniform scalar loads; the
+// stream is not written while it is decoded.)
 __device__ int check_header(const LaunchArgs& a, const JobDesc& jd, CSlot& sl) {
-  const uint32_t* h = (const uint32_t*)jd.src;
+  CU32* h = (CU32*)jd.src;
   if (h[0] != 0x4354564Bu || (h[1] & 0xFFFFu) != kFormatVersion) return KVTC_E_CORRUPT;
   const uint32_t want1 = (uint32_t)kFormatVersion | ((uint32_t)a.dtype << 16) | ((uint32_t)jd.kind << 24);
   if (h[1] != want1 || h[2] != (uint32_t)jd.layer || h[3] != jd.T || h[4] != (uint32_t)a.F ||
@@ -378,12 +380,18 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // --------------------------------------------------------------- encode ---
 
-// Compressed tiles carry their own index space (JobDesc::ctile_begin): the
-// kEncTile-token tiles of every job with records, job after job.
-__device__ __forceinline__ int find_ctile_job(const LaunchArgs& a, uint32_t c) {
+// Compressed rows carry their own index space of kEncBlk-token blocks
+// (JobDesc::cblk_begin): the blocks of every job with records, job after job.
+__device__ __forceinline__ int find_cblk_job(const LaunchArgs& a, uint32_t b) {
   int j = 0;
   for (int i = 1; i < a.n_jobs; ++i)
-    if (a.jobs[i].ctile_begin <= c) j = i;
+    if (a.jobs[i].cblk_begin <= b) j = i;
+  return j;
+}
+// The job of block b >= the first block of job j: j moved forward (a
+// workgroup's blocks are contiguous, so this is usually zero or one step).
+__device__ __forceinline__ int next_cblk_job(const LaunchArgs& a, int j, uint32_t b) {
+  while (j + 1 < a.n_jobs && a.jobs[j + 1].cblk_begin <= b) ++j;
   return j;
 }
 
@@ -462,8 +470,9 @@ __device__ __forceinline__ void quantize_tile(const f32x16 (&acc)[NB], CSlot& sl
 
 // Persistent encode. Each workgroup first writes the headers and passthrough
 // units u = g, g + grid, ... of the launch, then projects, quantizes and
-// packs an equal contiguous range of the compressed tiles. Its four waves
-// take 32 tokens of a tile each; the K loop walks slices of kEncKS features.
+// packs an equal contiguous range of the compressed 32-token blocks, as
+// tiles of up to four blocks of one job. Its four waves take a block of a
+// tile each; the K loop walks slices of kEncKS features.
 // The slice pipeline runs across tile boundaries: a load cursor two slices
 // ahead of the computation moves on into the next tile of the range, so the
 // loads of a tile's first slices are in flight during the previous tile's
@@ -484,10 +493,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!F32IN
     }
     if (lt >= jd.n_ctiles) encode_passthrough(jd, lt - jd.n_ctiles, row_bytes);
   }
-  const uint32_t C = a.total_ctiles;
-  const uint32_t c_begin = (uint32_t)((uint64_t)C * g / gridDim.x);
-  const uint32_t c_end = (uint32_t)((uint64_t)C * (g + 1) / gridDim.x);
-  if (c_begin >= c_end) return;
+  // This workgroup's blocks [b_begin, b_end), taken as tiles of up to
+  // kEncWaves blocks of one job (tile_end); equal block counts per
+  // workgroup keep them busy until the end of the launch.
+  const uint32_t B = a.total_cblks;
+  const uint32_t b_begin = (uint32_t)((uint64_t)B * g / gridDim.x);
+  const uint32_t b_end = (uint32_t)((uint64_t)B * (g + 1) / gridDim.x);
+  if (b_begin >= b_end) return;
+  auto tile_end = [&](int j, uint32_t b) -> uint32_t {
+    const JobDesc& jd = a.jobs[j];
+    const uint32_t job_end = jd.cblk_begin + (jd.tc + kEncBlk - 1) / kEncBlk;
+    return min(min(b + (uint32_t)kEncWaves, job_end), b_end);
+  };
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5;
@@ -526,17 +543,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!F32IN
   constexpr int NI = 32 / RPI;            // load instructions per slice
   constexpr int EPC = 16 / esz;           // features per chunk
   const int cx = lane % CH;
-  uint32_t lc = c_begin;
+  uint32_t lbe;       // end block of the load cursor's tile
   int lk = 0;
+  const int j_begin = find_cblk_job(a, b_begin);
+  int lj = j_begin;   // the load cursor's job
   const uint16_t* l_venc;
   const uint8_t* l_x;
   const float* l_mu;
   uint32_t xoff[NI];
-  auto cursor_tile = [&](uint32_t c) __attribute__((always_inline)) {
-    const JobDesc& jd = a.jobs[find_ctile_job(a, c)];
+  auto cursor_tile = [&](uint32_t b) __attribute__((always_inline)) {
+    lj = next_cblk_job(a, lj, b);
+    const JobDesc& jd = a.jobs[lj];
     CSlot& sl = slot_of(a, jd.slot);
-    const uint32_t t0 = (c - jd.ctile_begin) * kEncTile;
-    const uint32_t n = min((uint32_t)kEncTile, jd.tc - t0);
+    lbe = tile_end(lj, b);
+    const uint32_t t0 = (b - jd.cblk_begin) * kEncBlk;
+    const uint32_t n = min((lbe - b) * kEncBlk, jd.tc - t0);
     l_venc = (const uint16_t*)(a.state + sl.venc_off);
     l_mu = (const float*)(a.state + sl.mu_off);
     l_x = (const uint8_t*)jd.src + (size_t)(jd.s1 + t0) * row_bytes;
@@ -549,13 +570,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!F32IN
   auto cursor_next = [&]() __attribute__((always_inline)) {
     if (lk + 1 < n_sl) {
       ++lk;
-    } else if (lc + 1 < c_end) {
-      ++lc;
+    } else if (lbe < b_end) {
       lk = 0;
-      cursor_tile(lc);
+      cursor_tile(lbe);
     }
   };
-  cursor_tile(lc);
+  cursor_tile(b_begin);
 
   // Slice copy: a slice holds 32 * NB rows of kEncKS features, 32 * NB * 8
   // vectors of 16 bytes, so thread t moves vectors t + q * kThreads, q < NB,
@@ -622,7 +642,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!F32IN
   // acc[b][i] holds component 32b + 8(i/4) + 4h + i%4 of token tl. It
   // starts at -mu V' for bf16 input (the x V' - mu V' form), at 0 for f32.
   f32x16 acc[NB];
-  auto init_acc = [&](uint32_t c) __attribute__((always_inline)) {
+  auto init_acc = [&](int j) __attribute__((always_inline)) {
     if (F32IN) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
@@ -631,7 +651,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!F32IN
     } else {
       // Scalar loads (constant address space): items 32b + 8q + e of the
       // low half-wave, + 4 for the high one.
-      CSlot& sl = slot_of(a, a.jobs[find_ctile_job(a, c)].slot);
+      CSlot& sl = slot_of(a, a.jobs[j].slot);
       CU32* cmu = (CU32*)(a.state + sl.cmu_off);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
@@ -697,13 +717,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!F32IN
   KVTC_LOAD_SLICE(v1)
   KVTC_LOAD_X(x1)
   cursor_next();
-  init_acc(c_begin);
+  init_acc(j_begin);
   stage_first(mu0, x0, v0);
-  for (uint32_t c = c_begin; c < c_end; ++c) {
-    const JobDesc& jd = a.jobs[find_ctile_job(a, c)];
+  int cj = j_begin;   // the computed tile's job
+  for (uint32_t b = b_begin, te; b < b_end; b = te) {
+    cj = next_cblk_job(a, cj, b);
+    te = tile_end(cj, b);
+    const JobDesc& jd = a.jobs[cj];
     CSlot& sl = slot_of(a, jd.slot);
-    const uint32_t t0 = (c - jd.ctile_begin) * kEncTile;
-    const uint32_t n = min((uint32_t)kEncTile, jd.tc - t0);
+    const uint32_t t0 = (b - jd.cblk_begin) * kEncBlk;
+    const uint32_t n = min((te - b) * kEncBlk, jd.tc - t0);
     // The loop runs whole pairs of steps and an odd last slice follows it,
     // so the loop is only re-entered after a pair; with the parity fixed at
     // compile time every path into the loop has the same loads in flight and
@@ -725,10 +748,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!F32IN
       wave_lds_sync();
     }
     quantize_tile<NB, G>(acc, sl, smem + (size_t)tl * rbp, h, (uint32_t)tl < n);
-    if (c + 1 < c_end) init_acc(c + 1);
+    if (te < b_end) init_acc(next_cblk_job(a, cj, te));
     __syncthreads();
     records_to_global((uint8_t*)jd.dst + record_base(jd, F, esz) + (size_t)t0 * rb, smem, n, rb, rbp);
-    if (c + 1 < c_end) {
+    if (te < b_end) {
       __syncthreads();  // the records are out of LDS
       if (ODD) {
         // Odd slice count: the next tile's slice 0 is in (x1, v1), slice 1
@@ -838,12 +861,9 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
   const JobDesc& jd = a.jobs[j];
   CSlot& sl = slot_of(a, jd.slot);
   const uint32_t lt = tile - jd.tile_begin;
-  if (threadIdx.x == 0) flag = check_header(a, jd, sl);
-  __syncthreads();
-  const int st = flag;
+  const int st = check_header(a, jd, sl);   // uniform
   if (lt == 0 && threadIdx.x == 0) set_status(a, jd.status_idx, st);
   if (st != KVTC_OK) return;
-  __syncthreads();
   if (threadIdx.x == 0) flag = 0;
   __syncthreads();
   int bad = 0;
@@ -861,8 +881,20 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
       const uint8_t* src = (const uint8_t*)jd.src + record_base(jd, a.F, esz) + (size_t)t0 * rb;
       const uint32_t total = n * rb, nvv = total / 16;
       const float inv_rb = 1.0f / (float)rb;
-      for (uint32_t v = threadIdx.x; v < nvv; v += kThreads)
-        scatter_vec(smem, v, *(const u32x4*)(src + (size_t)v * 16), rb, rbp, inv_rb);
+      // Four 16-byte loads in flight per thread, then their scatter.
+      for (uint32_t v0 = threadIdx.x; v0 < nvv; v0 += 4 * kThreads) {
+        u32x4 x[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t v = v0 + k * kThreads;
+          if (v < nvv) x[k] = *(const u32x4*)(src + (size_t)v * 16);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t v = v0 + k * kThreads;
+          if (v < nvv) scatter_vec(smem, v, x[k], rb, rbp, inv_rb);
+        }
+      }
       for (uint32_t q = nvv * 16 + threadIdx.x; q < total; q += kThreads) {   // ragged end
         const uint32_t row = q / (uint32_t)rb;
         smem[row * rbp + (q - row * (uint32_t)rb)] = src[q];
@@ -876,19 +908,24 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
       const uint8_t* r = smem + (wave * kDecTok + (tok_ok ? t : 0)) * rbp;
       // K-step s: components c = 16 s + 8 h of active group ag, w-bit codes
       // at byte off of the record; (shift, scale) at byte 8 ag.
+      // The slot fields are read for both half-waves (uniform indices:
+      // scalar loads) and selected by h.
       int w_s[KA], off_s[KA], ag_s[KA];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const int c = 16 * s + 8 * h;
-        w_s[s] = 0;
-        off_s[s] = 0;
-        ag_s[s] = 0;
-        if (c < r_eff) {
+        int wh[2], oh[2], ah[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int c = 16 * s + 8 * hh;
           const int ag = c / G, o = c - ag * G;
-          ag_s[s] = ag;
-          w_s[s] = slot_width(sl, ag);
-          off_s[s] = slot_chunk(sl, ag) + (o * w_s[s]) / 8;
+          const bool act = c < r_eff;
+          ah[hh] = act ? ag : 0;
+          wh[hh] = act ? slot_width(sl, ag) : 0;
+          oh[hh] = act ? slot_chunk(sl, ag) + (o * wh[hh]) / 8 : 0;
         }
+        w_s[s] = h ? wh[1] : wh[0];
+        off_s[s] = h ? oh[1] : oh[0];
+        ag_s[s] = h ? ah[1] : ah[0];
       }
       auto shift_scale = [&](int s) -> float2 {
         const uint32_t* q = (const uint32_t*)(r + 8 * ag_s[s]);   // rows are 4-byte aligned
@@ -1186,15 +1223,15 @@ static void allow_lds(K kernel, size_t lds) {
 }
 
 // Workgroups of `kernel` (threads, lds bytes) resident on the current
-// device at once, a multiple of 8, at least 8.
+// device at once, at most max_per_cu per CU; a multiple of 8, at least 8.
 template <class K>
-static uint32_t resident_grid(K kernel, int threads, size_t lds) {
+static uint32_t resident_grid(K kernel, int threads, size_t lds, int max_per_cu = 1 << 20) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kernel, threads, lds) != hipSuccess)
     return 8;
-  const uint32_t n = (uint32_t)std::max(1, per_cu) * (uint32_t)std::max(1, cus);
+  const uint32_t n = (uint32_t)std::max(1, std::min(per_cu, max_per_cu)) * (uint32_t)std::max(1, cus);
   return std::max(8u, n / 8u * 8u);
 }
 
@@ -1210,15 +1247,22 @@ static uint32_t encode_grid_cap() {
   return std::max<uint32_t>(8u, (uint32_t)std::min<long>(v, 1L << 20) / 8u * 8u);
 }
 
+// Encode workgroups per CU: the per-CU load throughput saturates at two
+// (measured on llama31_8b, 32 tensors: 174 us per launch at one per CU,
+// 143 at two, 150 at three).
+constexpr int kEncMaxPerCU = 2;
+
 template <int G, bool F32IN, bool ODD>
 static int launch_encode_g(const LaunchArgs& a, int nb, size_t lds, hipStream_t s) {
-  // Persistent: the resident workgroups, or fewer when there are fewer
-  // compressed tiles (any grid covers the headers and passthrough units).
+  // Persistent: the resident workgroups (at most kEncMaxPerCU per CU), or
+  // fewer when there are fewer compressed blocks (any grid covers the
+  // headers and passthrough units).
 #define KVTC_ENC(NBV)                                                                      \
   case NBV: {                                                                              \
     allow_lds(encode_kernel<NBV, G, F32IN, ODD>, lds);                                     \
-    const dim3 g(std::min({grid_for(std::max(1u, a.total_ctiles)).x,                       \
-                           resident_grid(encode_kernel<NBV, G, F32IN, ODD>, kThreads, lds), \
+    const dim3 g(std::min({grid_for(std::max(1u, (a.total_cblks + kEncWaves - 1) / kEncWaves)).x, \
+                           resident_grid(encode_kernel<NBV, G, F32IN, ODD>, kThreads, lds,  \
+                                         kEncMaxPerCU),                                    \
                            encode_grid_cap()}));                                           \
     hipLaunchKernelGGL((encode_kernel<NBV, G, F32IN, ODD>), g, dim3(kThreads), lds, s, a); \
     break;                                                                                 \
