@@ -189,10 +189,10 @@ size_t kvtc_workspace_bytes(int32_t max_jobs);
 
 /* Encode n_jobs tensors in one launch (section 2B). Each job's dst must hold
  * kvtc_encoded_bytes. d_ws: workspace for n_jobs jobs. The kernel is
- * persistent (as many workgroups as fit, each over an equal range of
- * 128-token tiles); the environment variable KVTC_MAX_WORKGROUPS, if set to
- * a positive integer, caps that grid (rounded down to a multiple of 8, at
- * least 8) and changes no result. */
+ * persistent (at most two workgroups per CU, each over an equal range of
+ * 32-token blocks); the environment variable KVTC_MAX_WORKGROUPS, if set to
+ * a positive integer, caps that grid and the decode stage-2 grid (rounded
+ * down to a multiple of 8, at least 8) and changes no result. */
 kvtc_status kvtc_encode(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
                         void* d_ws, hipStream_t stream);
 

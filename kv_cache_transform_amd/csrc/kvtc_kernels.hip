@@ -1235,10 +1235,11 @@ static uint32_t resident_grid(K kernel, int threads, size_t lds, int max_per_cu 
   return std::max(8u, n / 8u * 8u);
 }
 
-// Optional cap on the persistent encode grid (environment variable
-// KVTC_MAX_WORKGROUPS, rounded down to a multiple of 8, at least 8): fewer
-// workgroups each walk more tiles. Unset or invalid: no cap.
-static uint32_t encode_grid_cap() {
+// Optional cap on the persistent grids, encode and decode stage 2
+// (environment variable KVTC_MAX_WORKGROUPS, rounded down to a multiple of
+// 8, at least 8): fewer workgroups each walk more work. Unset or invalid:
+// no cap.
+static uint32_t persistent_grid_cap() {
   const char* e = std::getenv("KVTC_MAX_WORKGROUPS");
   if (!e || !*e) return UINT32_MAX;
   char* end = nullptr;
@@ -1263,7 +1264,7 @@ static int launch_encode_g(const LaunchArgs& a, int nb, size_t lds, hipStream_t 
     const dim3 g(std::min({grid_for(std::max(1u, (a.total_cblks + kEncWaves - 1) / kEncWaves)).x, \
                            resident_grid(encode_kernel<NBV, G, F32IN, ODD>, kThreads, lds,  \
                                          kEncMaxPerCU),                                    \
-                           encode_grid_cap()}));                                           \
+                           persistent_grid_cap()}));                                           \
     hipLaunchKernelGGL((encode_kernel<NBV, G, F32IN, ODD>), g, dim3(kThreads), lds, s, a); \
     break;                                                                                 \
   }
@@ -1318,8 +1319,9 @@ static int launch_gemm_o(const LaunchArgs& a, int ks, size_t lds, hipStream_t s)
 #define KVTC_GEMM(KV)                                                                        \
   case KV: {                                                                                 \
     allow_lds(gemm_kernel<KV, OUT32>, lds);                                                  \
-    const dim3 g(std::min(std::max(8u, a.total_tiles / (8 * kGemmMinUnits) * 8),          \
-                          resident_grid(gemm_kernel<KV, OUT32>, kGemmThreads, lds)));                     \
+    const dim3 g(std::min({std::max(8u, a.total_tiles / (8 * kGemmMinUnits) * 8),         \
+                           resident_grid(gemm_kernel<KV, OUT32>, kGemmThreads, lds),       \
+                           persistent_grid_cap()}));                                       \
     hipLaunchKernelGGL((gemm_kernel<KV, OUT32>), g, dim3(kGemmThreads), lds, s, a);              \
     break;                                                                                   \
   }
