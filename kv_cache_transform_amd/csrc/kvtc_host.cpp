@@ -693,6 +693,7 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
       if (!d_staging || st_total > staging_bytes) return fail(KVTC_E_CAPACITY, "staging buffer too small");
       d.staging = d_staging + st_off[i];
       key[i] = (int)(align_up((size_t)s.r_eff, 16) / 16);
+      if (s.record_bytes > 24 * key[i]) return fail(KVTC_E_UNSUPPORTED, "record wider than the decode tiles");
     }
   }
   std::vector<int> order(n);
@@ -721,14 +722,19 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
         // units: feature slabs x blocks of kDecTok tokens
         const int fs = gemm_features(key[order[p]]);
         d.n_ctiles = (uint32_t)((F + fs - 1) / fs) * ((d.tc + kDecTok - 1) / kDecTok);
+      } else if (mode == Mode::Unpack) {
+        d.n_ctiles = (d.tc + kDecTok - 1) / kDecTok;   // one wave per block
       } else {
-        const int tile = mode == Mode::Unpack ? kPrepTok : mode == Mode::UnpackCodes ? kUnpackTile : kEncTile;
+        const int tile = mode == Mode::UnpackCodes ? kUnpackTile : kEncTile;
         d.n_ctiles = (d.tc + tile - 1) / tile;
       }
       d.tile_begin = tiles;
       d.cblk_begin = cblks;
-      if (s.r_eff > 0) cblks += (d.tc + kEncBlk - 1) / kEncBlk;
-      if (mode == Mode::Restore || mode == Mode::UnpackCodes)
+      if (mode == Mode::Unpack)   // header and passthrough units
+        cblks += std::max<uint32_t>(1, (d.s1 + d.w1 + kPrepPassRows - 1) / kPrepPassRows);
+      else if (s.r_eff > 0)
+        cblks += (d.tc + kEncBlk - 1) / kEncBlk;
+      if (mode == Mode::Restore || mode == Mode::Unpack || mode == Mode::UnpackCodes)
         tiles += d.n_ctiles;
       else
         tiles += std::max<uint32_t>(1, d.n_ctiles + ptiles);
@@ -746,8 +752,11 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
       l = std::max(l, (size_t)kEncTile * rbp);
     else if (mode == Mode::UnpackCodes)
       l = std::max(l, (size_t)kUnpackTile * rb_max + 16);
-    else if (mode == Mode::Unpack)
-      l = std::max({l, (size_t)kPrepTok * rbp + 16, (size_t)kPassRows * sizeof(long)});
+    else if (mode == Mode::Unpack) {
+      // each wave's 32 record rows, plus 16 bytes for the 8-byte reads past a row
+      a.wave_lds = (uint32_t)align_up((size_t)kDecTok * dec_rec_stride((int)rb_max), 16);
+      l = (size_t)kPrepRowsOff + (size_t)kPrepWaves * a.wave_lds + 16;
+    }
     else
       l = gemm_lds_bytes(k);
     if (l > 160 * 1024) return fail(KVTC_E_UNSUPPORTED, "tile does not fit in LDS");

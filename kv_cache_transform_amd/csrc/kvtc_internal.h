@@ -54,7 +54,8 @@ struct JobDesc {
   uint32_t tc;             // compressed rows
   uint32_t tile_begin;     // first logical tile of this job
   uint32_t n_ctiles;       // compressed-row tiles
-  uint32_t cblk_begin;     // encode: first 32-token block with records (jobs in order)
+  uint32_t cblk_begin;     // encode: first 32-token block with records (jobs in order);
+                           // decode stage 1: first header/passthrough unit
   int32_t slot;            // layer * 2 + kind
   int32_t layer;
   int32_t kind;
@@ -71,12 +72,13 @@ struct LaunchArgs {
   int32_t dtype;           // stream / input element type
   int32_t out_dtype;       // decode output element type
   int32_t F;
-  uint32_t total_cblks;    // encode: 32-token blocks with records
+  uint32_t total_cblks;    // encode: 32-token blocks with records; decode stage 1:
+                           // header/passthrough units
   const uint8_t* state;    // device state base
   unsigned long long* status;  // per-launch slice of the workspace status words
   uint8_t* sink;           // kSinkBytes of workspace that absorb stores without a row
   uint32_t epoch;          // stamp of this launch (see status_word)
-  uint32_t pad2;
+  uint32_t wave_lds;       // decode stage 1: LDS bytes of each wave's record rows
 };
 
 // Workspace status words: (epoch << 32) | rank, combined with atomicMax so
@@ -120,15 +122,20 @@ __host__ __device__ inline int padded_stride(int rb) {
   return p;
 }
 
-// Decode. Stage 1 handles kPrepTok compressed tokens per tile and writes,
-// per block of kDecTok tokens, ks * 64 B-operand fragments of 16 bytes (fp16,
-// MFMA lane order) and kDecTok f32 token scales: stg_block_bytes(ks) bytes.
+// Decode. Stage 1 runs one wave per block of kDecTok compressed tokens and
+// writes, per block, ks * 64 B-operand fragments of 16 bytes (fp16, MFMA
+// lane order) and kDecTok f32 token scales: stg_block_bytes(ks) bytes. Its
+// header and passthrough units cover kPrepPassRows rows each; the waves'
+// record rows (stride dec_rec_stride(rb)) start at kPrepRowsOff of LDS.
 // Stage 2 works in units of one block of kDecTok tokens of one slab of
 // gemm_features(ks) features; the slab of V' (rows padded by 16 bytes), mu
 // and kGemmWaves waves' output staging rows take gemm_lds_bytes(ks) of LDS.
 // Its workgroups get at least kGemmMinUnits units each.
 constexpr int kDecTok = 32;
-constexpr int kPrepTok = 128;
+constexpr int kPrepPassRows = 4;
+constexpr int kPrepWaves = 4;              // waves per stage-1 workgroup
+constexpr int kPrepRowsOff = 64;           // after the passthrough row list (kPrepPassRows longs)
+__host__ __device__ constexpr int dec_rec_stride(int rb) { return rb % 16 == 0 ? rb + 16 : rb; }
 constexpr uint32_t kGemmMinUnits = 16;
 constexpr int kGemmWaves = 8;              // waves sharing one slab of V'
 constexpr int kGemmThreads = 64 * kGemmWaves;

@@ -47,6 +47,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+static_assert(kWaves == kPrepWaves, "stage-1 workgroups run kThreads threads");
 
 // ------------------------------------------------------------- helpers ---
 
@@ -200,16 +201,17 @@ __device__ void encode_passthrough(const JobDesc& jd, uint32_t p, size_t row_byt
   }
 }
 
-// Decode: copy passthrough rows [p*kPassRows, ...) of the stream's row list
-// to the output, converting the element type if needed; every thread of the
-// workgroup calls it (rows_lds: kPassRows longs of LDS). The output row of
+// Decode: copy passthrough rows [p*PR, ...) of the stream's row list to the
+// output, converting the element type if needed; every thread of the
+// workgroup (NT threads) calls it (rows_lds: PR longs of LDS). The output row of
 // each stream row is looked up once; the copy keeps four 16-byte loads in
 // flight per thread. Returns false if a block table entry was bad.
+template <int NT, int PR = kPassRows>
 __device__ bool decode_passthrough(const LaunchArgs& a, const JobDesc& jd, uint32_t p, long* rows_lds) {
   const int F = a.F;
   const uint32_t n_rows = jd.s1 + jd.w1;
-  const uint32_t r0 = p * kPassRows;
-  const uint32_t nr = min(n_rows, r0 + kPassRows) - r0;
+  const uint32_t r0 = p * PR;
+  const uint32_t nr = min(n_rows, r0 + PR) - r0;
   const int in_esz = a.dtype == KVTC_F32 ? 4 : 2;
   const int out_esz = a.out_dtype == KVTC_F32 ? 4 : 2;
   const uint8_t* src = (const uint8_t*)jd.src + kHeaderBytes + (size_t)r0 * F * in_esz;
@@ -222,16 +224,16 @@ __device__ bool decode_passthrough(const LaunchArgs& a, const JobDesc& jd, uint3
   if (a.dtype == a.out_dtype) {
     const uint32_t vpr = (uint32_t)F * in_esz / 16;          // 16-byte vectors per row
     const uint32_t total = nr * vpr;
-    for (uint32_t i0 = threadIdx.x; i0 < total; i0 += 4 * kThreads) {
+    for (uint32_t i0 = threadIdx.x; i0 < total; i0 += 4 * NT) {
       u32x4 v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t i = i0 + u * kThreads;
+        const uint32_t i = i0 + u * NT;
         if (i < total) v[u] = ((const u32x4*)src)[i];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t i = i0 + u * kThreads;
+        const uint32_t i = i0 + u * NT;
         if (i < total) {
           const uint32_t rr = i / vpr;
           const long orow = rows_lds[rr];
@@ -245,7 +247,7 @@ __device__ bool decode_passthrough(const LaunchArgs& a, const JobDesc& jd, uint3
     }
   } else {
     const uint32_t total = nr * (uint32_t)F;
-    for (uint32_t i = threadIdx.x; i < total; i += kThreads) {
+    for (uint32_t i = threadIdx.x; i < total; i += NT) {
       const uint32_t rr = i / (uint32_t)F;
       const int c = (int)(i - rr * (uint32_t)F);
       const long orow = rows_lds[rr];
@@ -797,168 +799,173 @@ __device__ __forceinline__ void token_scale(float m, float& S, float& Sinv) {
   Sinv = __uint_as_float((uint32_t)(127 + 14 - e) << 23);
 }
 
-// B fragment of 8 components of a group of width w from packed record bits
-// (code j at bits [j w, j w + w), LSB first): c_hat = shift + q * fp32(scale
-// / k), times the power of two Sinv, as packed fp16. Sinv is folded into the
-// fma operands; scaling by a power of two is exact, so the rounded results
-// are those of the unscaled fma times Sinv.
-__device__ __forceinline__ uint4 frag_from_bits(uint64_t bits, float shift, float scale, int w,
-                                                float Sinv) {
-  const float step = scale / (float)((1 << w) - 1) * Sinv;
-  const float sh = shift * Sinv;
-  const uint32_t mask = (1u << w) - 1u;
+// fp32(scale / k) for k = 2^w - 1 from rk = fp32(1 / k): the product and one
+// fma correction (the residual scale - q k is exact in an fma), which gives
+// the correctly rounded quotient except in rare double-rounding cases, and
+// exactly whenever the quotient is representable (the decode tolerance does
+// not depend on the last bit; both decode routes share this function).
+__device__ __forceinline__ float div_by_levels(float scale, float kf, float rk) {
+  const float q = scale * rk;
+  return __builtin_fmaf(__builtin_fmaf(-q, kf, scale), rk, q);
+}
+
+// B fragment of 8 components of a group of width W from packed record bits
+// (code j at bits [j W, j W + W), LSB first): c_hat = shift + q * step,
+// step = fp32(scale / k), times the power of two Sinv, as packed fp16.
+// Sinv is folded into the fma operands; scaling by a power of two is exact,
+// so the rounded results are those of the unscaled fma times Sinv. The bit
+// offsets are constants, so each code is one field extract (two where it
+// straddles the 32-bit halves).
+template <int W>
+__device__ __forceinline__ uint4 frag_w(uint64_t bits, float step, float sh) {
+  constexpr uint32_t mask = (1u << W) - 1u;
+  const uint32_t lo = (uint32_t)bits, hi = (uint32_t)(bits >> 32);
+  float q[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int p = j * W;
+    uint32_t v;
+    if (p + W <= 32)
+      v = (lo >> p) & mask;
+    else if (p >= 32)
+      v = (hi >> (p - 32)) & mask;
+    else
+      v = __builtin_amdgcn_alignbit(hi, lo, p) & mask;
+    q[j] = (float)v;
+  }
   uint32_t pk[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float q0 = (float)((uint32_t)(bits >> (2 * j * w)) & mask);
-    const float q1 = (float)((uint32_t)(bits >> ((2 * j + 1) * w)) & mask);
-    pk[j] = pack_f16x2(__builtin_fmaf(q0, step, sh), __builtin_fmaf(q1, step, sh));
-  }
+  for (int j = 0; j < 4; ++j)
+    pk[j] = pack_f16x2(__builtin_fmaf(q[2 * j], step, sh), __builtin_fmaf(q[2 * j + 1], step, sh));
   return make_uint4(pk[0], pk[1], pk[2], pk[3]);
 }
 
-// Scatter 16-byte vector v (bytes [16v, 16v+16) of a contiguous run of
-// records of rb bytes) into LDS rows of stride rbp.
-__device__ __forceinline__ void scatter_vec(uint8_t* lds, uint32_t v, u32x4 x, int rb, int rbp,
-                                            float inv) {
-  uint32_t j = v * 16;
-  uint32_t row = (uint32_t)((float)j * inv);
-  while (row * (uint32_t)rb > j) --row;
-  while ((row + 1) * (uint32_t)rb <= j) ++row;
-  uint32_t col = j - row * (uint32_t)rb;
-  const uint32_t w[4] = {x[0], x[1], x[2], x[3]};
-  if ((rb & 3) == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(uint32_t*)(lds + row * rbp + col) = w[i];
-      col += 4;
-      if (col >= (uint32_t)rb) { col = 0; ++row; }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(uint16_t*)(lds + row * rbp + col) = (uint16_t)w[i];
-      col += 2;
-      if (col >= (uint32_t)rb) { col = 0; ++row; }
-      *(uint16_t*)(lds + row * rbp + col) = (uint16_t)(w[i] >> 16);
-      col += 2;
-      if (col >= (uint32_t)rb) { col = 0; ++row; }
-    }
+// The same for a width w in 1..8 known only at run time (uniform across the
+// wave: one branch per fragment); kf = 2^w - 1 and rk = fp32(1 / kf).
+__device__ __forceinline__ uint4 frag_from_bits(uint64_t bits, float shift, float scale, int w,
+                                                float kf, float rk, float Sinv) {
+  const float step = div_by_levels(scale, kf, rk) * Sinv;
+  const float sh = shift * Sinv;
+  switch (w) {
+    case 1: return frag_w<1>(bits, step, sh);
+    case 2: return frag_w<2>(bits, step, sh);
+    case 3: return frag_w<3>(bits, step, sh);
+    case 4: return frag_w<4>(bits, step, sh);
+    case 5: return frag_w<5>(bits, step, sh);
+    case 6: return frag_w<6>(bits, step, sh);
+    case 7: return frag_w<7>(bits, step, sh);
+    default: return frag_w<8>(bits, step, sh);
   }
 }
 
-// Stage 1: header check, passthrough rows, and for kPrepTok compressed
-// tokens per tile: records -> LDS rows (stride padded_stride(rb)) -> one wave
-// per block of kDecTok tokens builds the B operands and token scales of its
-// block and writes them to the staging buffer (stg_block_bytes(KS) per block).
+// Stage 1, one launch over a batch of jobs. First the header and
+// passthrough units (kPrepPassRows rows each; job j owns max(1, units) of
+// them from cblk_begin, and its first one records the header check in the
+// job's status word), split evenly over the workgroups so they add little to
+// any one; then one wave per block of kDecTok compressed tokens (block
+// tile_begin + c of job j is the c-th block of its records): the wave loads
+// the block's records with coalesced 16-byte loads (all in flight at once),
+// stores them into its LDS rows (stride rb + 16 if rb % 16 == 0, which keeps
+// a vector inside one row and spreads the rows over the banks; contiguous
+// otherwise), and builds the B operands and token scales of its 32 tokens,
+// stg_block_bytes(KS) bytes of staging per block. No workgroup barrier
+// follows the passthrough units: the waves run on their own.
 template <int KS>
 __global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int flag;
-  const uint32_t tile = logical_tile();
-  if (tile >= a.total_tiles) return;
-  const int j = find_job(a, tile);
-  const JobDesc& jd = a.jobs[j];
-  CSlot& sl = slot_of(a, jd.slot);
-  const uint32_t lt = tile - jd.tile_begin;
-  const int st = check_header(a, jd, sl);   // uniform
-  if (lt == 0 && threadIdx.x == 0) set_status(a, jd.status_idx, st);
-  if (st != KVTC_OK) return;
-  if (threadIdx.x == 0) flag = 0;
-  __syncthreads();
-  int bad = 0;
-  if (lt >= jd.n_ctiles) {
-    bad = !decode_passthrough(a, jd, lt - jd.n_ctiles, (long*)smem);
-  } else {
-    constexpr int KA = KS > 0 ? KS : 1;
-    const uint32_t t0 = lt * kPrepTok;
-    const uint32_t n = min((uint32_t)kPrepTok, jd.tc - t0);
-    const int r_eff = sl.r_eff, G = sl.G;
-    const int rb = sl.record_bytes, rbp = padded_stride(rb);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = lane & 31, h = lane >> 5;
-    if (KS > 0) {
-      const int esz = a.dtype == KVTC_F32 ? 4 : 2;
-      const uint8_t* src = (const uint8_t*)jd.src + record_base(jd, a.F, esz) + (size_t)t0 * rb;
-      const uint32_t total = n * rb, nvv = total / 16;
-      const float inv_rb = 1.0f / (float)rb;
-      // Four 16-byte loads in flight per thread, then their scatter.
-      for (uint32_t v0 = threadIdx.x; v0 < nvv; v0 += 4 * kThreads) {
-        u32x4 x[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t v = v0 + k * kThreads;
-          if (v < nvv) x[k] = *(const u32x4*)(src + (size_t)v * 16);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t v = v0 + k * kThreads;
-          if (v < nvv) scatter_vec(smem, v, x[k], rb, rbp, inv_rb);
-        }
-      }
-      for (uint32_t q = nvv * 16 + threadIdx.x; q < total; q += kThreads) {   // ragged end
-        const uint32_t row = q / (uint32_t)rb;
-        smem[row * rbp + (q - row * (uint32_t)rb)] = src[q];
-      }
-    }
-    __syncthreads();
-    const uint32_t tb = t0 / kDecTok + wave;               // this wave's token block
-    if ((uint32_t)wave * kDecTok < n) {
-      const uint32_t nt = min((uint32_t)kDecTok, n - wave * kDecTok);
-      const bool tok_ok = (uint32_t)t < nt;
-      const uint8_t* r = smem + (wave * kDecTok + (tok_ok ? t : 0)) * rbp;
-      // K-step s: components c = 16 s + 8 h of active group ag, w-bit codes
-      // at byte off of the record; (shift, scale) at byte 8 ag.
-      // The slot fields are read for both half-waves (uniform indices:
-      // scalar loads) and selected by h.
-      int w_s[KA], off_s[KA], ag_s[KA];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        int wh[2], oh[2], ah[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int c = 16 * s + 8 * hh;
-          const int ag = c / G, o = c - ag * G;
-          const bool act = c < r_eff;
-          ah[hh] = act ? ag : 0;
-          wh[hh] = act ? slot_width(sl, ag) : 0;
-          oh[hh] = act ? slot_chunk(sl, ag) + (o * wh[hh]) / 8 : 0;
-        }
-        w_s[s] = h ? wh[1] : wh[0];
-        off_s[s] = h ? oh[1] : oh[0];
-        ag_s[s] = h ? ah[1] : ah[0];
-      }
-      auto shift_scale = [&](int s) -> float2 {
-        const uint32_t* q = (const uint32_t*)(r + 8 * ag_s[s]);   // rows are 4-byte aligned
-        return make_float2(__uint_as_float(q[0]), __uint_as_float(q[1]));
-      };
-      // Every active group has a component among this lane's K-steps, so
-      // both lanes of a token see the same maximum.
-      float m = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (w_s[s]) {
-          const float2 p = shift_scale(s);
-          m = fmaxf(m, fmaxf(fabsf(p.x), fabsf(p.x + p.y)));
-        }
-      }
-      float S, Sinv;
-      token_scale(m, S, Sinv);
-      uint8_t* blk = (uint8_t*)jd.staging + (size_t)tb * stg_block_bytes(KS);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        uint4 f = make_uint4(0u, 0u, 0u, 0u);
-        if (tok_ok && w_s[s]) {
-          const float2 p = shift_scale(s);
-          f = frag_from_bits(lds_u64(r + off_s[s]), p.x, p.y, w_s[s], Sinv);
-        }
-        *(uint4*)(blk + s * 1024 + lane * 16) = f;
-      }
-      if (h == 0) *(float*)(blk + KS * 1024 + t * 4) = tok_ok ? S : 1.f;
+  constexpr int KA = KS > 0 ? KS : 1;
+  // 16-byte record vectors per lane for a block of the widest record this
+  // K-step count allows (every active group of width <= 8 adds at most
+  // 8 + G bytes per G / 16 K steps: rb <= 24 KS).
+  constexpr int NV = (kDecTok * 24 * KA / 16 + 63) / 64;
+  const uint32_t g = logical_tile(), ng = gridDim.x;
+  {
+    const uint32_t P = a.total_cblks;
+    const uint32_t p_end = (uint32_t)((uint64_t)P * (g + 1) / ng);
+    for (uint32_t p = (uint32_t)((uint64_t)P * g / ng); p < p_end; ++p) {
+      int j = 0;
+      for (int i = 1; i < a.n_jobs; ++i)
+        if (a.jobs[i].cblk_begin <= p) j = i;
+      const JobDesc& jd = a.jobs[j];
+      CSlot& sl = slot_of(a, jd.slot);
+      const uint32_t lp = p - jd.cblk_begin;
+      const int st = check_header(a, jd, sl);   // uniform
+      if (lp == 0 && threadIdx.x == 0) set_status(a, jd.status_idx, st);
+      if (st != KVTC_OK) continue;
+      if (threadIdx.x == 0) flag = 0;
+      __syncthreads();
+      bool ok = true;
+      if (lp * kPrepPassRows < jd.s1 + jd.w1)
+        ok = decode_passthrough<kThreads, kPrepPassRows>(a, jd, lp, (long*)smem);
+      if (!ok) atomicExch(&flag, 1);
+      __syncthreads();
+      if (threadIdx.x == 0 && flag) set_status(a, jd.status_idx, KVTC_E_INVALID);
+      __syncthreads();   // row list and flag are free for the next unit
     }
   }
-  if (bad) atomicExch(&flag, 1);
-  __syncthreads();
-  if (threadIdx.x == 0 && flag) set_status(a, jd.status_idx, KVTC_E_INVALID);
+  const int lane = threadIdx.x & 63, t = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const uint32_t b = g * kWaves + wave;
+  if (b >= a.total_tiles || KS == 0) return;
+  const int j = find_job(a, b);
+  const JobDesc& jd = a.jobs[j];
+  CSlot& sl = slot_of(a, jd.slot);
+  if (check_header(a, jd, sl) != KVTC_OK) return;   // reported by the job's first unit
+  const uint32_t c = b - jd.tile_begin;
+  const uint32_t nrec = min((uint32_t)kDecTok, jd.tc - c * kDecTok);
+  const int rb = sl.record_bytes, rbp = dec_rec_stride(rb);
+  // row of record byte q: (q * mrb) >> 24 = q / rb exactly for q < 2^24 / rb
+  const uint32_t mrb = (0xFFFFFFu + (uint32_t)rb) / (uint32_t)rb;
+  const uint32_t nbytes = nrec * (uint32_t)rb, nvv = nbytes / 16u;
+  const uint8_t* rec = (const uint8_t*)jd.src + record_base(jd, a.F, a.dtype == KVTC_F32 ? 4 : 2) +
+                       (size_t)c * kDecTok * rb;
+  uint8_t* rows = smem + kPrepRowsOff + (size_t)wave * a.wave_lds;
+  u32x4 x[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if ((uint32_t)(64 * i) < nvv)   // uniform
+      x[i] = *(const u32x4*)(rec + (size_t)min((uint32_t)(lane + 64 * i), nvv - 1u) * 16);
+  // Byte q of the block's records goes to LDS byte q + (q / rb) * (rbp - rb).
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const uint32_t q = (uint32_t)(lane + 64 * i) * 16u;
+    if ((uint32_t)(64 * i) < nvv && q < nbytes - 15u)
+      *(u32x4*)(rows + q + ((q * mrb) >> 24) * (uint32_t)(rbp - rb)) = x[i];
+  }
+  for (uint32_t q = nvv * 16u + lane; q < nbytes; q += 64) rows[q] = rec[q];   // ragged end (rbp == rb)
+  wave_lds_sync();
+  // K step s: components 16 s + 8 h .. + 8 of active group ag = 16 s / G
+  // (both halves lie in one group since G >= 16, so the group, its width and
+  // the reciprocal of its level count are uniform); their w-bit codes start at
+  // byte off of the record, the group's (shift, scale) at byte 8 ag.
+  const bool tok_ok = (uint32_t)t < nrec;
+  const uint8_t* r = rows + (tok_ok ? t : 0) * rbp;
+  const int G = sl.G;
+  float2 ps[KA];
+  float m = 0.f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const uint64_t q = lds_u64(r + 8 * (16 * s / G));   // rows are 2-byte aligned
+    ps[s] = make_float2(__uint_as_float((uint32_t)q), __uint_as_float((uint32_t)(q >> 32)));
+    // every active group has a component among the K steps, so both lanes
+    // of a token see the same maximum
+    m = fmaxf(m, fmaxf(fabsf(ps[s].x), fabsf(ps[s].x + ps[s].y)));
+  }
+  float S, Sinv;
+  token_scale(m, S, Sinv);
+  uint8_t* blk = (uint8_t*)jd.staging + (size_t)c * stg_block_bytes(KS);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int ag = 16 * s / G;
+    const int w = slot_width(sl, ag);
+    const float kf = (float)((1 << w) - 1);
+    const int off = slot_chunk(sl, ag) + ((16 * s + 8 * h - ag * G) * w) / 8;
+    const uint4 f = tok_ok ? frag_from_bits(lds_u64(r + off), ps[s].x, ps[s].y, w, kf, 1.0f / kf, Sinv)
+                           : make_uint4(0u, 0u, 0u, 0u);
+    *(uint4*)(blk + s * 1024 + lane * 16) = f;
+  }
+  if (h == 0) *(float*)(blk + KS * 1024 + t * 4) = tok_ok ? S : 1.f;
 }
 
 // Stage 2 segment: features [f0, f0 + FS) x blocks [c_lo, c_hi) of kDecTok
@@ -1299,7 +1306,8 @@ int launch_encode(const LaunchArgs& a, int nb, int G, size_t lds, hipStream_t s)
   X(15) X(16)
 
 int launch_prep(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
-  const dim3 g = grid_for(a.total_tiles);
+  // one wave per compressed block; any grid covers the passthrough units
+  const dim3 g = grid_for(std::max(8u, (a.total_tiles + kWaves - 1) / kWaves));
 #define KVTC_PREP(KV)                                                       \
   case KV:                                                                  \
     allow_lds(prep_kernel<KV>, lds);                                        \
