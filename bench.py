@@ -7,12 +7,13 @@ budget (1 bit per value), microscale group 16; seeded synthetic KV (shared
 channels per head), calibrated on 16384 synthetic tokens per tensor by the
 library on the host.
 
-One step = kvtc_encode of every tensor followed by the decode of every
+One step = kvtc_encode of every tensor followed by kvtc_decode of every
 stream back to bf16 (one launch per 32 tensors per kernel), with inputs,
-streams and outputs resident in HBM. The decode is issued as its two stages
-(kvtc_decode_unpack, kvtc_decode_restore: exactly what kvtc_decode runs) so
-that HIP events on the launch stream time each kernel inside the timed
-region. value = bf16 KV bytes per step / step time. For a
+streams and outputs resident in HBM; HIP events on the launch stream time
+the encode and the decode inside the timed region. value = bf16 KV bytes per
+step / step time. After the timed steps, as many decode calls issued as
+their two stages (kvtc_decode_unpack, kvtc_decode_restore: what kvtc_decode
+runs) with an event between them time each decode kernel on its own. For a
 paged workload (qwen25_7b_paged) the decode is the layer-by-layer two-stream
 pipeline: stage 1 (unpack) of layer l+1 runs on one stream while stage 2
 (restore into the paged cache) of layer l runs on another. The DEFLATE ratio
@@ -160,16 +161,16 @@ def main():
     stg = dws.view(torch.uint8)[n_wsb:]
     n_stg = n_dws - n_wsb
 
-    def decode(mid=None):
+    def decode():
         if pipe is not None:
             pipe.run(stream)
-            if mid is not None:
-                mid.record(stream)
         else:
-            codec.decode_unpack(dec_jobs, K.KVTC_BF16, stg, n_stg, dws, stream)
-            if mid is not None:
-                mid.record(stream)
-            codec.decode_restore(dec_jobs, K.KVTC_BF16, stg, n_stg, dws, stream)
+            codec.decode(dec_jobs, K.KVTC_BF16, dws, n_dws, stream)
+
+    def decode_staged(mid):
+        codec.decode_unpack(dec_jobs, K.KVTC_BF16, stg, n_stg, dws, stream)
+        mid.record(stream)
+        codec.decode_restore(dec_jobs, K.KVTC_BF16, stg, n_stg, dws, stream)
 
     # Plain device copy of a known size: the practical HBM ceiling and the
     # reference that scales the FETCH_SIZE / WRITE_SIZE counters.
@@ -199,22 +200,30 @@ def main():
     if pipe is not None:
         pipe.check()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for e0, e1, e2, e3 in ev:
+    for e0, e1, e2 in ev:
         e0.record(stream)
         encode()
         e1.record(stream)
-        decode(e2)
-        e3.record(stream)
+        decode()
+        e2.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    enc_ms = np.array([a.elapsed_time(b) for a, b, _, _ in ev])
-    prep_ms = np.array([b.elapsed_time(c) for _, b, c, _ in ev])
-    gemm_ms = np.array([c.elapsed_time(d) for _, _, c, d in ev])
-    dec_ms = prep_ms + gemm_ms
+    enc_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    dec_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
     ms_per_step = wall * 1e3 / args.steps
+    if pipe is None:
+        # per-kernel breakdown of the decode (same calls, an event between the stages)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for d0, d1, d2 in evs:
+            d0.record(stream)
+            decode_staged(d1)
+            d2.record(stream)
+        torch.cuda.synchronize()
+        prep_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
+        gemm_ms = np.array([b.elapsed_time(c) for _, b, c in evs])
 
     kv_bytes = n_jobs * T * F * esz
     r_eff = {s: infos[s].r_eff for s in slots}
@@ -238,10 +247,11 @@ def main():
     dec_alg = stream_total + kv_bytes + sum(((r_eff[(l, k)] + 15) // 16 * 16) * F * 2 + F * 4
                                             for l, k, _ in jobs)
     med = lambda v: float(np.median(v)) * 1e-3
-    kern = {"encode_kernel": (enc_alg, med(enc_ms)), "prep_kernel": (prep_alg, med(prep_ms)),
-            "gemm_kernel": (gemm_alg, med(gemm_ms))}
-    if pipe is not None:   # two streams: stage times overlap; report the pipeline as one
-        kern = {"encode_kernel": kern["encode_kernel"],
+    if pipe is None:
+        kern = {"encode_kernel": (enc_alg, med(enc_ms)), "prep_kernel": (prep_alg, med(prep_ms)),
+                "gemm_kernel": (gemm_alg, med(gemm_ms))}
+    else:   # two streams: stage times overlap; report the pipeline as one
+        kern = {"encode_kernel": (enc_alg, med(enc_ms)),
                 "prep_kernel + gemm_kernel (two streams)": (dec_alg, med(dec_ms))}
     dominant = max(kern, key=lambda k: kern[k][1])
     enc_t, dec_t = med(enc_ms), med(dec_ms)
@@ -250,9 +260,12 @@ def main():
         alg, t = kern[name]
         per_launch_t = t / n_launch
         ach = alg / n_launch / per_launch_t / 1e9
-        return {"kernel": name, "achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBPS, 4),
-                "alg_bytes_per_launch": int(alg / n_launch), "us_per_launch": round(per_launch_t * 1e6, 2),
-                "launches_per_call": n_launch}
+        r = {"kernel": name, "achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBPS, 4),
+             "alg_bytes_per_launch": int(alg / n_launch), "us_per_launch": round(per_launch_t * 1e6, 2),
+             "launches_per_call": n_launch}
+        if name in ("prep_kernel", "gemm_kernel"):
+            r["timed_in"] = "decode breakdown loop after the timed steps"
+        return r
 
     flops = sum(2 * F * r_eff[(l, k)] * tc for l, k, _ in jobs)
     traffic = measured_traffic(dominant, args.workload)

@@ -197,10 +197,12 @@ kvtc_status kvtc_encode(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
                         void* d_ws, hipStream_t stream);
 
 /* Decode n_jobs streams (section 2C), writing out_dtype rows: stage 1 and
- * stage 2 below back to back on `stream`, with the staging buffer inside
- * d_ws. d_ws must hold ws_bytes >= kvtc_decode_workspace_bytes(jobs)
- * (kvtc_workspace_bytes(n_jobs) followed by kvtc_staging_bytes(jobs));
- * KVTC_E_CAPACITY otherwise. Passthrough rows are copied bit for bit when
+ * stage 2 below on `stream`, stage 2 of each launch batch (at most 32 jobs
+ * of one K-step count) right after its stage 1, with the staging buffer
+ * inside d_ws. d_ws must hold ws_bytes >= kvtc_decode_workspace_bytes(jobs)
+ * (kvtc_workspace_bytes(n_jobs) followed by kvtc_staging_bytes(jobs); 0 if a
+ * job names an unknown or uncalibrated (layer, kind)); KVTC_E_CAPACITY
+ * otherwise. Passthrough rows are copied bit for bit when
  * out_dtype equals the codec dtype (converted with round-to-nearest-even
  * otherwise). */
 size_t kvtc_decode_workspace_bytes(const kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs);

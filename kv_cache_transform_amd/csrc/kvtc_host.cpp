@@ -602,8 +602,14 @@ size_t kvtc_staging_bytes(const kvtc_codec* c, const kvtc_job* jobs, int32_t n_j
 }
 
 size_t kvtc_decode_workspace_bytes(const kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs) {
-  const size_t st = kvtc_staging_bytes(c, jobs, n_jobs);
-  return st ? kvtc_workspace_bytes(n_jobs) + st : 0;
+  // 0 flags jobs the codec cannot decode; jobs without compressed rows need
+  // no staging but still a workspace.
+  if (!c || !jobs || n_jobs <= 0) return 0;
+  for (int i = 0; i < n_jobs; ++i) {
+    int idx;
+    if (!slot_index(c, jobs[i].layer, jobs[i].kind, &idx) || !c->slots[idx].calibrated) return 0;
+  }
+  return kvtc_workspace_bytes(n_jobs) + kvtc_staging_bytes(c, jobs, n_jobs);
 }
 
 }  // extern "C"
@@ -801,7 +807,7 @@ kvtc_status kvtc_decode_unpack(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jo
                         staging_bytes, b, k, l);
   if (st != KVTC_OK) return st;
   for (size_t i = 0; i < b.size(); ++i) {
-    if (b[i].total_tiles == 0) continue;
+    if (b[i].total_tiles + b[i].total_cblks == 0) continue;   // every job has a header unit
     st = hip_status(launch_prep(b[i], k[i], l[i], stream), "decode stage 1 launch");
     if (st != KVTC_OK) return st;
   }
@@ -833,9 +839,27 @@ kvtc_status kvtc_decode(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, int
   if (!d_ws || ws_bytes < need) return fail(KVTC_E_CAPACITY, "workspace below kvtc_decode_workspace_bytes");
   uint8_t* stg = (uint8_t*)d_ws + kvtc_workspace_bytes(n_jobs);
   const size_t stg_bytes = ws_bytes - kvtc_workspace_bytes(n_jobs);
-  kvtc_status st = kvtc_decode_unpack(c, jobs, n_jobs, out_dtype, stg, stg_bytes, d_ws, stream);
+  // Both stages are planned over the same jobs, so their batches match; each
+  // batch's stage 2 follows its stage 1 at once, while its staging is in cache.
+  std::vector<LaunchArgs> bu, br;
+  std::vector<int> ku, kr;
+  std::vector<size_t> lu, lr;
+  kvtc_status st = plan(c, Mode::Unpack, jobs, n_jobs, out_dtype, d_ws, stg, stg_bytes, bu, ku, lu);
   if (st != KVTC_OK) return st;
-  return kvtc_decode_restore(c, jobs, n_jobs, out_dtype, stg, stg_bytes, d_ws, stream);
+  st = plan(c, Mode::Restore, jobs, n_jobs, out_dtype, d_ws, stg, stg_bytes, br, kr, lr);
+  if (st != KVTC_OK) return st;
+  if (bu.size() != br.size()) return fail(KVTC_E_INVALID, "internal: decode stages planned differently");
+  for (size_t i = 0; i < bu.size(); ++i) {
+    if (bu[i].total_tiles + bu[i].total_cblks > 0) {
+      st = hip_status(launch_prep(bu[i], ku[i], lu[i], stream), "decode stage 1 launch");
+      if (st != KVTC_OK) return st;
+    }
+    if (br[i].total_tiles > 0) {
+      st = hip_status(launch_gemm(br[i], kr[i], lr[i], stream), "decode stage 2 launch");
+      if (st != KVTC_OK) return st;
+    }
+  }
+  return KVTC_OK;
 }
 
 kvtc_status kvtc_unpack(kvtc_codec* c, const kvtc_job* job, void* d_codes, void* d_shift_scale, void* d_ws,

@@ -1033,7 +1033,8 @@ __device__ void gemm_segment(const LaunchArgs& a, int j, uint32_t slab, uint32_t
     const uint8_t* blk = stg_job + (size_t)(tb0 + c) * BB;
 #pragma unroll
     for (int s = 0; s < KS; ++s) Bn[s] = *(const uint4*)(blk + s * 1024 + lane * 16);
-    Sn = *(const float*)(blk + KS * 1024 + (lane & 31) * 4);
+    // stage 1 writes no staging when no component is kept (KS == 0)
+    Sn = KS > 0 ? *(const float*)(blk + KS * 1024 + (lane & 31) * 4) : 1.f;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const uint32_t tt = s1 + min(t0 + c * kDecTok + 8 * it + (lane >> 3), tc - 1);

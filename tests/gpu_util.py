@@ -79,9 +79,11 @@ class DevCodec:
         return torch.full((max(rows, 1), F), -7, dtype=dt, device=DEV) if dt == torch.int16 else \
             torch.full((max(rows, 1), F), -7.0, dtype=dt, device=DEV)
 
-    def decode(self, items, out_dtype, F, paging=None, two_stage=False):
+    def decode(self, items, out_dtype, F, paging=None, two_stage=False, stg_fill=0):
         """items: list of (layer, kind, T, stream bytes). paging: list of
         (block_table dev tensor, block_size, n_blocks) per item or None.
+        stg_fill: byte the staging memory holds before the call (0xFF makes
+        every float read from it that stage 1 did not write a NaN).
         Returns (outputs, status)."""
         jobs, outs, keep = [], [], []
         for i, (layer, kind, T, sb) in enumerate(items):
@@ -99,20 +101,22 @@ class DevCodec:
         s = torch.cuda.current_stream()
         if two_stage:
             n = self.codec.staging_bytes(jobs)
-            stg = torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV)
+            stg = torch.full((max(n, 256),), stg_fill, dtype=torch.uint8, device=DEV)
             self.codec.decode_unpack(jobs, out_dtype, stg, stg.numel(), self.ws, s)
             self.codec.decode_restore(jobs, out_dtype, stg, stg.numel(), self.ws, s)
             st = self.status(len(jobs))
         else:
-            st = self.decode_jobs(jobs, out_dtype)
+            st = self.decode_jobs(jobs, out_dtype, stg_fill)
         torch.cuda.synchronize()
         return outs, st
 
-    def decode_jobs(self, jobs, out_dtype):
-        """Fused decode of prepared jobs with a workspace of its own; returns the status."""
+    def decode_jobs(self, jobs, out_dtype, stg_fill=0):
+        """kvtc_decode of prepared jobs with a workspace of its own (status words
+        zeroed, the staging part filled with stg_fill); returns the status."""
         s = torch.cuda.current_stream()
         n = self.codec.decode_workspace_bytes(jobs)
         dws = torch.zeros((n + 3) // 4, dtype=torch.int32, device=DEV)
+        dws.view(torch.uint8)[K.kvtc_workspace_bytes(len(jobs)):].fill_(stg_fill)
         self.codec.decode(jobs, out_dtype, dws, n, s)
         return K.kvtc_read_device_status(dws, len(jobs), s)
 

@@ -218,6 +218,14 @@ def test_edge_lengths_in_one_launch():
         assert np.all(st == 0), st
         for T, out, ref in zip(lens, outs, refs):
             _decode_check(w, op, slot, ref.stream, T, out, od, 0, 0)
+    # a launch with no compressed row at all still validates and copies
+    short = [i for i, T in enumerate(lens) if T <= op.sink + op.window]
+    for two in (False, True):
+        outs, st = dc.decode([(0, 0, lens[i], refs[i].stream) for i in short], K.KVTC_F32, op.F,
+                             two_stage=two)
+        assert np.all(st == 0), st
+        for i, out in zip(short, outs):
+            _decode_check(w, op, slot, refs[i].stream, lens[i], out, K.KVTC_F32, 0, 0)
 
 
 def _injected(F, G, widths, dtype, seed, s=4, w=16, mu_scale=1.0):
@@ -262,9 +270,11 @@ def test_injected_artifacts(variant):
     nbad, ntot, mx, _, _ = code_stats(sb, ref, p, sl, T)
     assert mx <= 1 and nbad <= max(2, ntot * CODE_RATE), (nbad, ntot)
     for od in (K.KVTC_F32, K.KVTC_BF16):
-        outs, st = dc.decode([(0, 0, T, ref.stream)], od, F)
-        assert np.all(st == 0)
-        _decode_check(None, p, sl, ref.stream, T, outs[0], od, 0, 0)
+        for two in (False, True):
+            # staging that stage 1 leaves unwritten holds NaN bit patterns
+            outs, st = dc.decode([(0, 0, T, ref.stream)], od, F, two_stage=two, stg_fill=0xFF)
+            assert np.all(st == 0)
+            _decode_check(None, p, sl, ref.stream, T, outs[0], od, 0, 0)
 
 
 def test_identity_basis_is_exact():
