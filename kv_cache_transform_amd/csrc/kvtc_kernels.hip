@@ -5,29 +5,32 @@
 // multiply by V, quantize with the DP widths, pack) and section 2C
 // (decompression: dequantize, multiply by V^T, add the mean, layer by layer).
 //
-// Every launch covers a batch of jobs (tensors). The grid is a flat list of
-// logical tiles; tiles of one job are consecutive and the blockIdx -> tile map
-// sends consecutive tiles to the same XCD, so one tensor's basis stays in one
-// XCD's L2.
+// Every launch covers a batch of jobs (tensors) of one shape parameter, with
+// the job descriptors passed by value. Persistent grids take equal contiguous
+// ranges of work units, and the blockIdx -> range map sends consecutive
+// ranges to the same XCD, so one tensor's basis stays in one XCD's L2.
 //
-// Encode tile (256 threads, 128 tokens): the four waves each own 32 tokens.
-// The projection runs on v_mfma_f32_32x32x16_bf16 in transposed form,
-// D[component][token] = sum_f V'^T[component][f] * x'[token][f]: the basis
-// K-slice is staged in LDS and shared by the waves, the centred tokens
-// x' = bf16_rne(fp32(x) - mu) are formed in registers straight from global
-// memory. In the accumulator layout a lane owns one token and half of every
+// Encode (256 threads, persistent, at most two workgroups per CU): each wave
+// owns 32 tokens of a tile. The projection runs on v_mfma_f32_32x32x16_bf16
+// in transposed form, D[component][token] = sum_f V'^T[component][f] *
+// x[token][f], with the accumulators started at -mu V' for bf16 input (the
+// mean folded into the product) and f32 input centred and split into two
+// bf16 operands. Token rows go through a per-wave LDS tile (row-contiguous
+// loads), basis K-slices through two shared LDS buffers, both two slices
+// ahead. In the accumulator layout a lane owns one token and half of every
 // group's components, so the per-(token, group) min/max needs one cross-lane
-// exchange (lane ^ 32), quantization is lane-local, and a second exchange
-// gives each lane G/2 consecutive codes that it packs into one or two 64-bit
-// words. Records are assembled in LDS and leave in 16-byte stores.
+// exchange (lane ^ 32) and quantization is lane-local; codes are OR-ed into
+// LDS record rows and leave in 16-byte stores.
 //
-// Decode tile (256 threads, 128 tokens): records are staged into LDS with
-// 16-byte loads; each lane rebuilds its token's dequantized coefficients
-// c_hat = shift + q * fp32(scale / k) for the 8 components it feeds to the
-// MFMA, scaled by a per-token power of two into fp16 (the fp16 operand keeps
-// 11 significant bits; the scale makes the range irrelevant), then runs
-// D[feature][token] = sum_j V'[feature][j] * c_hat[token][j] on
-// v_mfma_f32_32x32x16_f16 per 32-feature block and writes S_t * D + mu.
+// Decode, stage 1 (256 threads): one wave per block of 32 compressed tokens
+// loads the block's records, stages them in LDS and builds each token's
+// dequantized coefficients c_hat = shift + q * fp32(scale / k) for the 8
+// components per K step it feeds to the MFMA, divided by a per-token power of
+// two into fp16 (the fp16 operand keeps 11 significant bits; the scale makes
+// the range irrelevant), into a staging buffer. Stage 2 (512 threads,
+// persistent): D[feature][token] = sum_j V'[feature][j] * c_hat[token][j] on
+// v_mfma_f32_32x32x16_f16 per 128-feature slab (V' in LDS), written as
+// S_t * D + mu through LDS rows in 128-byte streaming stores.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
