@@ -1230,7 +1230,9 @@ static dim3 grid_for(uint32_t tiles) { return dim3((tiles + 7u) / 8u * 8u); }
 // 160 KiB per CU).
 template <class K>
 static void allow_lds(K kernel, size_t lds) {
-  if (lds > 65536) hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // a refusal surfaces as the launch error that follows
+  if (lds > 65536)
+    (void)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
 // Workgroups of `kernel` (threads, lds bytes) resident on the current
