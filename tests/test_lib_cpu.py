@@ -173,3 +173,26 @@ def test_deflate_roundtrip():
     data = bytes(np.random.default_rng(0).integers(0, 4, 50000, dtype=np.uint8))
     z = K.kvtc_deflate(data, 6)
     assert zlib.decompress(z) == data and len(z) < len(data)
+
+
+def test_decode_workspace_sizes():
+    """kvtc_decode_workspace_bytes: status words plus staging; jobs without
+    compressed rows still get a workspace (0 is reserved for jobs naming an
+    unknown or uncalibrated (layer, kind)); the staging is one block of
+    ks * 1024 + 128 bytes per 32 compressed tokens."""
+    w = synth.workload("tiny")
+    _, kp = _params_pair(w)
+    c = K.Codec(kp)
+    c.calibrate(0, 0, synth.storage(w, synth.gen_kv(w, 0, 0, 1, w.calib_tokens)), threads=2)
+    info = c.slot(0, 0)
+    ks = (info.r_eff + 15) // 16
+    short = [K.make_job(0, 0, T, 16, 16, 1 << 20) for T in (0, 1, w.sink + w.window)]
+    base = K.kvtc_workspace_bytes(len(short))
+    assert c.staging_bytes(short) == 0
+    assert c.decode_workspace_bytes(short) == base
+    T = w.sink + w.window + 33                     # 33 compressed rows: two blocks
+    jobs = short + [K.make_job(0, 0, T, 16, 16, 1 << 20)]
+    blocks = 256 * ((2 * (ks * 1024 + 128) + 255) // 256)
+    assert c.staging_bytes(jobs) == blocks
+    assert c.decode_workspace_bytes(jobs) == K.kvtc_workspace_bytes(len(jobs)) + blocks
+    assert c.decode_workspace_bytes([K.make_job(0, 1, T, 16, 16, 1 << 20)]) == 0   # V never calibrated
