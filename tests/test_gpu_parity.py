@@ -93,6 +93,23 @@ def test_encode_parity_few_workgroups(case, monkeypatch):
     _check_encode(case)
 
 
+# Stage 2 is persistent too: with 8 workgroups each range crosses job and
+# feature-slab boundaries (odd3_bf16 ends in a partial slab); the arithmetic
+# per output element does not depend on the split, so the output is identical.
+@pytest.mark.parametrize("case", ["llama31_8b", "odd3_bf16", "qwen25_7b_paged"])
+def test_decode_few_workgroups_is_identical(case, monkeypatch):
+    w, art, op, items = _setup(case)
+    dc = DevCodec(art.serialize())
+    T = items[0][2].shape[0]
+    jobs = [(l, k, T, ref.stream) for l, k, _, ref in items]
+    outs, st = dc.decode(jobs, K.KVTC_BF16, op.F)
+    monkeypatch.setenv("KVTC_MAX_WORKGROUPS", "8")
+    outs8, st8 = dc.decode(jobs, K.KVTC_BF16, op.F)
+    assert np.all(st == 0) and np.all(st8 == 0), (st, st8)
+    for a, b in zip(outs, outs8):
+        assert torch.equal(a, b)
+
+
 def _check_encode(case):
     w, art, op, items = _setup(case)
     dc = DevCodec(art.serialize())
