@@ -221,7 +221,9 @@ kvtc_status kvtc_decode(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
  * for each block of 32 compressed tokens, ks = ceil(r_eff / 16) x 64
  * fragments of 8 fp16 (fragment (s, l) holds components 16 s + 8 (l / 32)
  * .. + 8 of token l % 32 of the block; zero past r_eff and past the last
- * token), then 32 f32 S_t. */
+ * token), then 32 f32 S_t. kvtc_staging_bytes is 0 when no job has
+ * compressed rows (d_staging may then be NULL) or when a job names an unknown
+ * or uncalibrated (layer, kind). */
 size_t kvtc_staging_bytes(const kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs);
 kvtc_status kvtc_decode_unpack(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
                                int32_t out_dtype, void* d_staging, size_t staging_bytes,

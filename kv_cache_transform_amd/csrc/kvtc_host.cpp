@@ -696,7 +696,8 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
           if ((1 << b) == d.block_size) d.bs_shift = b;
       st_off[i] = st_total;
       st_total += job_staging_bytes(s, d.tc);
-      if (!d_staging || st_total > staging_bytes) return fail(KVTC_E_CAPACITY, "staging buffer too small");
+      if (st_total > 0 && (!d_staging || st_total > staging_bytes))
+        return fail(KVTC_E_CAPACITY, "staging buffer too small");
       d.staging = d_staging + st_off[i];
       key[i] = (int)(align_up((size_t)s.r_eff, 16) / 16);
       if (s.record_bytes > 24 * key[i]) return fail(KVTC_E_UNSUPPORTED, "record wider than the decode tiles");

@@ -243,6 +243,18 @@ def test_edge_lengths_in_one_launch():
         assert np.all(st == 0), st
         for i, out in zip(short, outs):
             _decode_check(w, op, slot, refs[i].stream, lens[i], out, K.KVTC_F32, 0, 0)
+    # without compressed rows the two stages need no staging memory at all
+    srcs = [to_dev_bytes(refs[i].stream, 16) for i in short]
+    outs = [dc.out_buffer(lens[i], op.F, K.KVTC_F32) for i in short]
+    jobs = [K.make_job(0, 0, lens[i], src, out, out.numel() * 4) for i, src, out in zip(short, srcs, outs)]
+    assert dc.codec.staging_bytes(jobs) == 0
+    s = torch.cuda.current_stream()
+    dc.codec.decode_unpack(jobs, K.KVTC_F32, None, 0, dc.ws, s)
+    dc.codec.decode_restore(jobs, K.KVTC_F32, None, 0, dc.ws, s)
+    torch.cuda.synchronize()
+    assert np.all(dc.status(len(jobs)) == 0)
+    for i, out in zip(short, outs):
+        _decode_check(w, op, slot, refs[i].stream, lens[i], out, K.KVTC_F32, 0, 0)
 
 
 def _injected(F, G, widths, dtype, seed, s=4, w=16, mu_scale=1.0):
