@@ -169,36 +169,39 @@ def test_decode_parity(case, out_dtype):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("case", ["tiny", "llama31_8b", "nemo12b"])
+@pytest.mark.parametrize("case", list(CASES))
 def test_pack_unpack_bit_exact(case):
+    """T1 on every workload and every tensor of its sample: kvtc_pack of the
+    oracle's codes and (shift, scale) reproduces the oracle's stream byte for
+    byte, and kvtc_unpack of the oracle's stream returns them bit for bit."""
     w, art, op, items = _setup(case)
     dc = DevCodec(art.serialize())
-    l, k, store, ref = items[0]
-    slot = art.slots[(l, k)]
-    T = store.shape[0]
-    x = storage_to_dev(store)
-    n = dc.codec.encoded_bytes(l, k, T)
-    buf = torch.zeros(n, dtype=torch.uint8, device=DEV)
-    codes = torch.from_numpy(np.ascontiguousarray(ref.codes)).to(DEV)
-    ss = torch.from_numpy(np.ascontiguousarray(np.stack([ref.shift, ref.scale], axis=2))).to(DEV)
-    job = K.make_job(l, k, T, x, buf, n)
-    dc.codec.pack(job, codes, ss, dc.ws, torch.cuda.current_stream())
-    torch.cuda.synchronize()
-    assert bytes(buf.cpu().numpy().tobytes()) == ref.stream          # T1 pack
-    src = to_dev_bytes(ref.stream, 16)
-    out = torch.zeros((T, op.F), dtype=torch.int16 if op.dtype == O.DTYPE_BF16 else torch.float32,
-                      device=DEV)
-    djob = K.make_job(l, k, T, src, out, out.numel() * out.element_size())
-    tc = ref.codes.shape[0]
-    gc = torch.full((max(tc * slot.r_eff, 1),), 0xEE, dtype=torch.uint8, device=DEV)
-    gs = torch.full((max(tc * slot.n_act * 2, 1),), -1.0, dtype=torch.float32, device=DEV)
-    dc.codec.unpack(djob, gc, gs, dc.ws, torch.cuda.current_stream())
-    torch.cuda.synchronize()
-    got_codes = gc.cpu().numpy()[: tc * slot.r_eff].reshape(tc, slot.r_eff)
-    got_ss = gs.cpu().numpy()[: tc * slot.n_act * 2].reshape(tc, slot.n_act, 2)
-    assert np.array_equal(got_codes, ref.codes)                      # T1 unpack
-    assert np.array_equal(got_ss[:, :, 0].view(np.uint32), ref.shift.view(np.uint32))
-    assert np.array_equal(got_ss[:, :, 1].view(np.uint32), ref.scale.view(np.uint32))
+    for l, k, store, ref in items:
+        slot = art.slots[(l, k)]
+        T = store.shape[0]
+        x = storage_to_dev(store)
+        n = dc.codec.encoded_bytes(l, k, T)
+        buf = torch.zeros(n, dtype=torch.uint8, device=DEV)
+        codes = torch.from_numpy(np.ascontiguousarray(ref.codes)).to(DEV)
+        ss = torch.from_numpy(np.ascontiguousarray(np.stack([ref.shift, ref.scale], axis=2))).to(DEV)
+        job = K.make_job(l, k, T, x, buf, n)
+        dc.codec.pack(job, codes, ss, dc.ws, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        assert bytes(buf.cpu().numpy().tobytes()) == ref.stream          # T1 pack
+        src = to_dev_bytes(ref.stream, 16)
+        out = torch.zeros((T, op.F), dtype=torch.int16 if op.dtype == O.DTYPE_BF16 else torch.float32,
+                          device=DEV)
+        djob = K.make_job(l, k, T, src, out, out.numel() * out.element_size())
+        tc = ref.codes.shape[0]
+        gc = torch.full((max(tc * slot.r_eff, 1),), 0xEE, dtype=torch.uint8, device=DEV)
+        gs = torch.full((max(tc * slot.n_act * 2, 1),), -1.0, dtype=torch.float32, device=DEV)
+        dc.codec.unpack(djob, gc, gs, dc.ws, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        got_codes = gc.cpu().numpy()[: tc * slot.r_eff].reshape(tc, slot.r_eff)
+        got_ss = gs.cpu().numpy()[: tc * slot.n_act * 2].reshape(tc, slot.n_act, 2)
+        assert np.array_equal(got_codes, ref.codes)                      # T1 unpack
+        assert np.array_equal(got_ss[:, :, 0].view(np.uint32), ref.shift.view(np.uint32))
+        assert np.array_equal(got_ss[:, :, 1].view(np.uint32), ref.scale.view(np.uint32))
 
 
 def test_edge_lengths_in_one_launch():
@@ -296,6 +299,15 @@ def test_injected_artifacts(variant):
     s1, w1, tc = O.split_rows(T, p.sink, p.window)
     rec0 = 64 + (s1 + w1) * F * 2
     assert sb[:rec0] == ref.stream[:rec0]
+    # T1: the oracle's codes and (shift, scale) pack to the oracle's stream
+    n = dc.codec.encoded_bytes(0, 0, T)
+    buf = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    codes = torch.from_numpy(np.ascontiguousarray(ref.codes)).to(DEV)
+    ss = torch.from_numpy(np.ascontiguousarray(np.stack([ref.shift, ref.scale], axis=2))).to(DEV)
+    dc.codec.pack(K.make_job(0, 0, T, storage_to_dev(store), buf, n), codes, ss, dc.ws,
+                  torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert bytes(buf.cpu().numpy().tobytes()) == ref.stream
     nbad, ntot, mx, _, _ = code_stats(sb, ref, p, sl, T)
     assert mx <= 1 and nbad <= max(2, ntot * CODE_RATE), (nbad, ntot)
     for od in (K.KVTC_F32, K.KVTC_BF16):
