@@ -584,6 +584,8 @@ def decode(stream: bytes, params: Params, slot: Slot, layer: int, kind: int, T: 
 
 
 def deflate_ratio(stream: bytes, raw_bytes: int):
-    """DEFLATE stage (section 2B), here zlib level 6, for the ratio only (Z1)."""
+    """DEFLATE stage (section 2B), here zlib level 6, for the ratio only (Z1).
+
+    Returns (raw / stream bytes, raw / deflated bytes, the deflated bytes)."""
     z = zlib.compress(bytes(stream), 6)
-    return raw_bytes / len(stream), raw_bytes / len(z), len(z)
+    return raw_bytes / len(stream), raw_bytes / len(z), z

@@ -450,6 +450,23 @@ def check_decode_exact_sum():
             assert abs(float(acc) - full[t + 1, f]) <= 1e-12 * max(1.0, abs(float(acc)))
 
 
+def check_deflate_ratio():
+    """Z1: DEFLATE is lossless (inflate gives the stream back), the ratios are
+    raw bytes over stream bytes and over deflated bytes, and the level is 6:
+    a zlib stream (RFC 1950) starts with CMF = 0x78 (deflate, 32 KiB window)
+    and an FLG byte whose top two bits are the level class, 2 ("default")
+    for level 6, which with the check bits gives 0x9C."""
+    import zlib
+    rng = np.random.default_rng(12)
+    stream = bytes(2000) + rng.integers(0, 4, 3000, dtype=np.uint8).tobytes() + b"KVTC" * 250
+    assert len(stream) == 6000
+    r_stream, r_defl, z = O.deflate_ratio(stream, 96000)
+    assert zlib.decompress(z) == stream
+    assert r_stream == 16.0
+    assert r_defl == 96000 / len(z) and len(z) < 3000
+    assert z[0] == 0x78 and z[1] == 0x9C and (z[0] * 256 + z[1]) % 31 == 0
+
+
 def check_shapes_vs_page():
     w = synth.workload("llama31_8b")
     per_1k = w.n_layers * len(w.kinds) * w.features * 2 * 1024

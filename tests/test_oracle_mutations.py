@@ -136,7 +136,20 @@ def _quant_no_clamp(c, b):
     return np.where(q == 2 ** b - 1, 0, q).astype(np.uint8), shift, scale
 
 
+def _deflate_level9(stream, raw_bytes):
+    import zlib
+    z = zlib.compress(bytes(stream), 9)
+    return raw_bytes / len(stream), raw_bytes / len(z), z
+
+
+def _deflate_ratios_swapped(stream, raw_bytes):
+    a, b, z = _orig["deflate_ratio"](stream, raw_bytes)
+    return b, a, z
+
+
 MUTATIONS = {
+    "deflate_level9": ("deflate_ratio", _deflate_level9),
+    "deflate_ratios_swapped": ("deflate_ratio", _deflate_ratios_swapped),
     "no_centering": ("project", _project_no_centering),
     "fp32_basis_in_projection": ("project", _project_fp32_basis),
     "bf16_centred_operand": ("project", _project_bf16_centred),
