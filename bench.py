@@ -34,6 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# device code the traffic counters in profiles/traffic.json were taken on
+KERNEL_SOURCES = ("kvtc_device.h", "kvtc_encode.hip", "kvtc_decode.hip", "kvtc_internal.h")
 
 
 def log(msg):
@@ -400,12 +402,15 @@ def measured_traffic(kernel, workload):
     this workload with the kernel source as it is now (else None)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    src = os.path.join(ROOT, "kv_cache_transform_amd", "csrc", "kvtc_kernels.hip")
+    csrc = os.path.join(ROOT, "kv_cache_transform_amd", "csrc")
     try:
         with open(path) as f:
             rec = json.load(f)
-        with open(src, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
+        h = hashlib.sha256()
+        for name in KERNEL_SOURCES:
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+        digest = h.hexdigest()
     except (OSError, ValueError):
         return None
     if rec.get("kernels_sha256") != digest or rec.get("workload") != workload:

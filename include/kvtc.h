@@ -24,10 +24,15 @@
  *   quantizer    per (token, active group): shift = min c, scale = max c - min c
  *                (fp32), q = clamp(rint_even(fp32(c - shift) * fp32(k/scale)),
  *                0, k) with k = 2^b - 1 and q = 0 when scale == 0.
- *   projection   x' = bf16_rne(fp32(x) - mu32), c = sum_f x'_f V'_fj with
- *                V' = bf16_rne(V32); products are exact, accumulation in fp32
- *                MFMA steps, so a code may differ by one step from an exact sum
- *                near a rounding boundary.
+ *   projection   c_j = sum_f (x_f - mu32_f) V'_fj with V' = bf16_rne(V32),
+ *                the centred token taken exactly. On the device: d = x - mu_hi
+ *                in fp32 with mu_hi = bf16_rne(mu32) (exact for bf16 tokens
+ *                within a factor 2^8 of the mean), split into bf16 terms
+ *                (two for bf16 input, three for f32) that are each multiplied
+ *                on bf16 MFMA with fp32 accumulation started at
+ *                -(mu32 - mu_hi) V'; the rounding error scales with |x - mu|,
+ *                so a code may differ by one step from the exact sum near a
+ *                rounding boundary whatever the size of the mean.
  *   dequantize   c_hat = shift + q * fp32(scale / k); dropped groups give 0;
  *                x_hat = mu32 + sum_j c_hat_j V'_j.
  *   stream       64-byte header ("KVTC", u16 version=1, u8 dtype, u8 kind,

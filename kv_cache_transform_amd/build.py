@@ -1,5 +1,6 @@
 """Build libkvtc.so in-tree: hipcc for the gfx950 kernels and the host core,
 g++ for the fp64 linear algebra, linked with zlib."""
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -32,21 +33,27 @@ def _run(cmd, verbose):
         raise RuntimeError(f"build step failed: {' '.join(cmd[:3])} ...")
 
 
+# gfx950 kernel translation units (compiled in parallel)
+HIP_SOURCES = ["kvtc_encode.hip", "kvtc_decode.hip"]
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     inc = ["-I", INCLUDE, "-I", CSRC]
-    objs = []
-    o = os.path.join(BUILD, "kvtc_kernels.o")
-    _run([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "kvtc_kernels.hip"), "-o", o], verbose)
-    objs.append(o)
+    steps = []
+    for src in HIP_SOURCES:
+        o = os.path.join(BUILD, src.replace(".hip", ".o"))
+        steps.append((o, [HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", o]))
     o = os.path.join(BUILD, "kvtc_host.o")
-    _run([HIPCC, "-O3", "-std=c++17", "-fPIC", *inc, "-c", os.path.join(CSRC, "kvtc_host.cpp"),
-          "-o", o], verbose)
-    objs.append(o)
+    steps.append((o, [HIPCC, "-O3", "-std=c++17", "-fPIC", *inc, "-c",
+                      os.path.join(CSRC, "kvtc_host.cpp"), "-o", o]))
     o = os.path.join(BUILD, "kvtc_linalg.o")
-    _run(["g++", "-O3", "-march=x86-64-v3", "-std=c++17", "-fPIC", *inc, "-c",
-          os.path.join(CSRC, "kvtc_linalg.cpp"), "-o", o], verbose)
-    objs.append(o)
+    steps.append((o, ["g++", "-O3", "-march=x86-64-v3", "-std=c++17", "-fPIC", *inc, "-c",
+                      os.path.join(CSRC, "kvtc_linalg.cpp"), "-o", o]))
+    with concurrent.futures.ThreadPoolExecutor(len(steps)) as ex:
+        for f in [ex.submit(_run, cmd, verbose) for _, cmd in steps]:
+            f.result()
+    objs = [o for o, _ in steps]
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, "-lz", "-lpthread"],
          verbose)

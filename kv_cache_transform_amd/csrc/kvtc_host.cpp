@@ -498,7 +498,7 @@ size_t kvtc_device_state_bytes(const kvtc_codec* c) {
   for (const Slot& s : c->slots) {
     if (!s.calibrated) continue;
     const size_t r_enc = align_up((size_t)s.r_eff, 32), r_dec = align_up((size_t)s.r_eff, 16);
-    n += align_up(4 * (size_t)c->F, kAlign) + align_up(2 * r_enc * c->F, kAlign) +
+    n += 2 * align_up(4 * (size_t)c->F, kAlign) + align_up(2 * r_enc * c->F, kAlign) +
          align_up(2 * (size_t)c->F * r_dec, kAlign) + align_up(4 * r_enc, kAlign);
   }
   return n;
@@ -555,15 +555,23 @@ kvtc_status kvtc_upload(kvtc_codec* c, void* d_state, size_t bytes, hipStream_t 
       for (int j = 0; j < r; ++j)
         vdec[(size_t)f * r_dec + j] = f32_to_f16(bf16_to_f32(f32_to_bf16(s.V32[(size_t)f * r + j])));
     off += align_up(2 * (size_t)F * r_dec, kAlign);
-    // The projection of the mean onto the bf16 basis, V'^T mu32, in fp64
-    // rounded once: the encode multiplies bf16 tokens as they are (exact
-    // operands) and subtracts this per component.
+    // Centring (section 2B subtracts the mean before the transform). The
+    // encode subtracts mu_hi = bf16_rne(mu32) from each token in fp32 (exact
+    // for bf16 tokens whenever token and mean lie within a factor 2^8 of each
+    // other, so the error scales with |x - mu| and not with |x|) and starts
+    // its accumulators at -V'^T (mu32 - mu_hi), this small remainder's
+    // projection in fp64 rounded once.
+    d.mhi_off = off;
+    float* mhi = (float*)(h.data() + off);
+    for (int f = 0; f < F; ++f) mhi[f] = bf16_to_f32(f32_to_bf16(s.mu32[f]));
+    off += align_up(4 * (size_t)F, kAlign);
     d.cmu_off = off;
     float* cmu = (float*)(h.data() + off);
     for (int j = 0; j < r; ++j) {
       double acc = 0.0;
       for (int f = 0; f < F; ++f)
-        acc += (double)s.mu32[f] * (double)bf16_to_f32(f32_to_bf16(s.V32[(size_t)f * r + j]));
+        acc += ((double)s.mu32[f] - (double)mhi[f]) *
+               (double)bf16_to_f32(f32_to_bf16(s.V32[(size_t)f * r + j]));
       cmu[j] = (float)acc;
     }
     off += align_up(4 * (size_t)r_enc, kAlign);

@@ -1,5 +1,5 @@
 // Internal declarations shared by the host core (kvtc_host.cpp) and the HIP
-// kernels and launchers (kvtc_kernels.hip). Not part of the public ABI.
+// kernels and launchers (kvtc_encode.hip, kvtc_decode.hip). Not part of the public ABI.
 #pragma once
 
 #include <cstddef>
@@ -28,7 +28,8 @@ struct alignas(16) DevSlot {
   uint64_t mu_off;        // f32 mu32[F]
   uint64_t venc_off;      // bf16 V'^T [r_enc][F]   (rows >= r_eff are zero)
   uint64_t vdec_off;      // f16  V'   [F][r_dec]   (cols >= r_eff are zero)
-  uint64_t cmu_off;       // f32  V'^T mu32 [r_enc]  (rows >= r_eff are zero)
+  uint64_t mhi_off;       // f32  mu_hi[F] = bf16_rne(mu32), the encode's centring vector
+  uint64_t cmu_off;       // f32  V'^T (mu32 - mu_hi) [r_enc]  (rows >= r_eff are zero)
   uint64_t slot_id;
   int32_t calibrated;
   int32_t n_act;
@@ -103,14 +104,15 @@ constexpr int kEncBlk = 32;                // encode tokens per wave (one block)
 constexpr int kEncWaves = kEncTile / kEncBlk;   // encode waves per tile
 
 // Encode LDS: two basis slices [32 nb][kEncRowPad] bf16, then per wave its
-// token tiles [32][kEncRowPad] bf16 (one for bf16 input; two, the high and
-// low bf16 parts, for f32 input), then for f32 input the mean (F fp32).
+// token tile of 32 rows of kEncKS raw input elements (padded by 16 bytes),
+// then the centring vector mu_hi (F fp32). The centred token is split into
+// enc_terms bf16 MFMA operands (two for bf16 input, three for f32).
+__host__ __device__ constexpr int enc_terms(bool f32in) { return f32in ? 3 : 2; }
 __host__ __device__ constexpr size_t enc_basis_bytes(int nb) { return (size_t)32 * nb * kEncRowPad * 2; }
-__host__ __device__ constexpr size_t enc_xtile_bytes(bool f32in) {
-  return (size_t)(f32in ? 2 : 1) * 32 * kEncRowPad * 2;
-}
+__host__ __device__ constexpr int enc_xrow_bytes(bool f32in) { return kEncKS * (f32in ? 4 : 2) + 16; }
+__host__ __device__ constexpr size_t enc_xtile_bytes(bool f32in) { return (size_t)32 * enc_xrow_bytes(f32in); }
 __host__ __device__ constexpr size_t enc_lds_bytes(int nb, int F, bool f32in) {
-  return 2 * enc_basis_bytes(nb) + kEncWaves * enc_xtile_bytes(f32in) + (f32in ? (size_t)F * 4 : 0);
+  return 2 * enc_basis_bytes(nb) + kEncWaves * enc_xtile_bytes(f32in) + (size_t)F * 4;
 }
 
 // LDS row stride for records under assembly (encode, pack): a multiple of 4
@@ -147,7 +149,7 @@ __host__ __device__ constexpr size_t gemm_lds_bytes(int ks) {
          (size_t)kGemmWaves * kDecTok * kOutRow;
 }
 
-// Host-side launchers implemented in kvtc_kernels.hip (G = group size, lds =
+// Host-side launchers implemented in kvtc_encode.hip and kvtc_decode.hip (G = group size, lds =
 // dynamic LDS bytes). Every job of one launch has the same shape parameter:
 // nb = r_enc / 32 for encode, ks = r_dec / 16 for the decode stages. They
 // return a hipError_t value cast to int.

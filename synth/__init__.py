@@ -55,6 +55,7 @@ class Workload:
     noise: float = 0.01
     paged: bool = False
     block_size: int = 16
+    mean_scale: float = 0.5    # family B: std of the per-feature mean offset
 
     @property
     def features(self) -> int:
@@ -95,6 +96,11 @@ WORKLOADS = {
                           "bf16", 4, 64, 16, 2.0, "B", 48),
     "odd1_f32": Workload("odd1_f32", 6, 1, (K,), 1, 64, 2100, 1, 2048, "f32", 4,
                          32, 16, 3.0, "A", 16),
+    # Llama-3.1-8B-shaped layer whose features carry large mean offsets
+    # (std 50 against a unit spread; x10 on the key outlier channels): the
+    # centring must not lose precision when |mean| >> spread.
+    "offsets_bf16": Workload("offsets_bf16", 7, 1, (K, V), 8, 128, 4096, 1, 4096,
+                             "bf16", 4, 128, 16, 1.0, "B", 96, mean_scale=50.0),
 }
 
 
@@ -155,7 +161,7 @@ def structure(w: Workload, layer: int, kind: int) -> _Structure:
     M = np.concatenate(blocks, axis=0)                      # [F, r]
     sigma = np.arange(1, r + 1, dtype=np.float64) ** (-w.alpha)
     amp = np.sqrt(d / np.sum(sigma ** 2))                   # unit per-channel std
-    mean = 0.5 * rng.standard_normal(F)
+    mean = w.mean_scale * rng.standard_normal(F)
     scale = np.ones(F)
     if kind == K:
         for h in range(w.kv_heads):

@@ -38,6 +38,8 @@ CASES = {
     # feature counts 192 and 64: an odd number of 64-feature slices
     "odd3_bf16": ("odd3_bf16", [(0, 0), (0, 1)], 1100, 1, None),
     "odd1_f32": ("odd1_f32", [(0, 0)], 2100, 1, None),
+    # per-feature mean offsets about 40 times the spread
+    "offsets_bf16": ("offsets_bf16", [(0, 0), (0, 1)], 4096, 1, None),
 }
 
 
@@ -125,6 +127,10 @@ def _check_encode(case):
         assert sb[:rec0] == ref.stream[:rec0], "header or passthrough differs"
         nb, nt, mx, shift, scale = code_stats(sb, ref, op, slot, T)
         bad, total, worst = bad + nb, total + nt, max(worst, mx)
+        # the records hold nothing but those codes and (shift, scale) pairs,
+        # laid out as the oracle lays them out (no stray or misplaced bits)
+        gcodes, gshift, gscale = O.read_records(sb, op, slot, T)
+        assert O.build_records(gcodes, gshift, gscale, slot).tobytes() == sb[rec0:]
         if slot.n_act:
             assert np.allclose(shift, ref.shift, rtol=1e-5, atol=1e-6 * np.abs(ref.shift).max())
             assert np.allclose(scale, ref.scale, rtol=1e-4, atol=1e-6 * np.abs(ref.scale).max())
@@ -271,10 +277,22 @@ def _injected(F, G, widths, dtype, seed, s=4, w=16, mu_scale=1.0):
     return p, sl
 
 
-@pytest.mark.parametrize("variant", ["zero_bits", "reff256_g16", "reff256_g32", "odd_groups"])
+# Tokens x = mu + 3 z (z ~ N(0, 1)) around a mean of mu_ratio * 3 * N(0, 1)
+# per feature, i.e. |mu| / spread = mu_ratio: the projection is of the
+# centred token, so the code mismatches must stay within the bar however
+# large the mean is.
+MEAN_RATIOS = {"mean10": 10.0, "mean100": 100.0}
+
+
+@pytest.mark.parametrize("variant", ["zero_bits", "reff256_g16", "reff256_g32", "odd_groups",
+                                     "mean10", "mean100"])
 def test_injected_artifacts(variant):
     F = 1024
-    if variant == "zero_bits":
+    if variant in MEAN_RATIOS:
+        wd = np.zeros(64, np.uint8)
+        wd[:6] = [8, 8, 7, 7, 6, 4]
+        p, sl = _injected(F, 16, wd, O.DTYPE_BF16, 5, mu_scale=3.0 * MEAN_RATIOS[variant])
+    elif variant == "zero_bits":
         p, sl = _injected(F, 16, np.zeros(64), O.DTYPE_BF16, 1)
     elif variant == "reff256_g16":
         wd = np.zeros(64, np.uint8)
@@ -293,6 +311,8 @@ def test_injected_artifacts(variant):
     rng = np.random.default_rng(9)
     T = 777
     x = (rng.standard_normal((T, F)) * 3).astype(np.float32)
+    if variant in MEAN_RATIOS:
+        x = (x + sl.mu32).astype(np.float32)
     store = O.f32_to_bf16_bits(x)
     ref = O.encode(store, p, sl, 0, 0)
     sb = dc.encode([(0, 0, storage_to_dev(store))])[0]
@@ -309,6 +329,7 @@ def test_injected_artifacts(variant):
     torch.cuda.synchronize()
     assert bytes(buf.cpu().numpy().tobytes()) == ref.stream
     nbad, ntot, mx, _, _ = code_stats(sb, ref, p, sl, T)
+    print(f"{variant}: code mismatches {nbad}/{ntot}, max step {mx}")
     assert mx <= 1 and nbad <= max(2, ntot * CODE_RATE), (nbad, ntot)
     for od in (K.KVTC_F32, K.KVTC_BF16):
         for two in (False, True):
@@ -318,32 +339,59 @@ def test_injected_artifacts(variant):
             _decode_check(None, p, sl, ref.stream, T, outs[0], od, 0, 0)
 
 
-def test_identity_basis_is_exact():
-    """mu = 0, V = I, 8-bit groups, inputs on each group's 8-bit grid: the GPU
-    stream equals the oracle's byte for byte and decode returns the input."""
-    F, G, T = 64, 16, 300
-    rng = np.random.default_rng(8)
-    p = O.Params(1, 1, F, 2, 3, G, 8, 12.0, O.DTYPE_BF16)
-    sl = O.Slot(0, 0, F, G, np.full(4, 8, np.uint8), np.zeros(F, np.float32), np.zeros(F),
-                np.eye(F, dtype=np.float32))
+# (F, G, widths per group): every width 1..8 with both group sizes, and
+# scattered active groups of mixed widths (odd n_act, dropped groups between).
+IDENTITY_CASES = {f"w{b}_g{G}": (4 * G, G, [b] * 4) for b in range(1, 9) for G in (16, 32)}
+IDENTITY_CASES["mixed_g16"] = (512, 16, [5, 0, 0, 8, 0, 1, 2, 0, 0, 3, 7] + [0] * 20 + [4])
+IDENTITY_CASES["mixed_g32"] = (512, 32, [0, 6, 0, 1, 8, 0, 3, 0, 0, 0, 2, 0, 0, 0, 0, 5])
+
+
+def _grid_tokens(widths, G, T, rng):
+    """Tokens whose every active group lies on its own width's grid:
+    (m + q) 2^e with q in [0, 2^b - 1] (0 and 2^b - 1 both present), |m + q|
+    <= 255 (bfloat16-exact), e in [-6, 2] per (token, group); zero elsewhere."""
+    F = G * len(widths)
     x = np.zeros((T, F), np.float32)
-    for g in range(4):
+    for g, b in enumerate(int(v) for v in widths):
+        if not b:
+            continue
+        k = 2 ** b - 1
         e = rng.integers(-6, 3, T).astype(np.float64)
-        m = rng.integers(-255, 1, T)
-        q = rng.integers(0, 256, (T, G))
-        q[:, 0], q[:, 1] = 0, 255
+        m = rng.integers(-k, 256 - k, T)
+        q = rng.integers(0, k + 1, (T, G))
+        q[:, 0], q[:, G // 2 + 1] = 0, k
         x[:, g * G:(g + 1) * G] = (m[:, None] + q) * 2.0 ** e[:, None]
-    store = O.f32_to_bf16_bits(x)
+    return x
+
+
+@pytest.mark.parametrize("dtype", [O.DTYPE_BF16, O.DTYPE_F32])
+@pytest.mark.parametrize("case", list(IDENTITY_CASES))
+def test_identity_basis_is_exact(case, dtype):
+    """mu = 0, V = identity on the active groups, tokens on each group's grid:
+    the production encode's stream equals the oracle's byte for byte (every
+    code, shift, scale and record bit), and the production decode (both
+    routes) returns the input exactly, in both output types."""
+    F, G, widths = IDENTITY_CASES[case]
+    T = 300
+    rng = np.random.default_rng(8)
+    widths = np.asarray(widths, np.uint8)
+    act = np.concatenate([np.arange(g * G, (g + 1) * G) for g in np.nonzero(widths)[0]])
+    p = O.Params(1, 1, F, 2, 3, G, 8, 12.0, dtype)
+    sl = O.Slot(0, 0, F, G, widths, np.zeros(F, np.float32), np.zeros(F),
+                np.eye(F, dtype=np.float32)[:, act])
+    x = _grid_tokens(widths, G, T, rng)
+    store = O.f32_to_bf16_bits(x) if dtype == O.DTYPE_BF16 else x
     ref = O.encode(store, p, sl, 0, 0)
     dc = DevCodec(O.Artifact(p, {(0, 0): sl}).serialize())
     sb = dc.encode([(0, 0, storage_to_dev(store))])[0]
     assert sb == ref.stream
     for od in (K.KVTC_F32, K.KVTC_BF16):
-        outs, st = dc.decode([(0, 0, T, ref.stream)], od, F)
-        assert np.all(st == 0)
-        got = outs[0].cpu().numpy()
-        want = x if od == K.KVTC_F32 else store.view(np.int16)
-        assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+        for two in (False, True):
+            outs, st = dc.decode([(0, 0, T, ref.stream)], od, F, two_stage=two)
+            assert np.all(st == 0)
+            got = outs[0].cpu().numpy()
+            want = x if od == K.KVTC_F32 else O.f32_to_bf16_bits(x).view(np.int16)
+            assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), (od, two)
 
 
 def test_corrupt_stream_is_rejected_without_writes():
@@ -419,35 +467,46 @@ def test_full_size_launch_llama8b():
 
 
 def test_two_stream_layer_pipeline_matches_fused():
-    """Layer-by-layer decode on two streams (stage 1 of layer l+1 overlapping
-    stage 2 of layer l, two alternating staging buffers and workspaces) gives
-    exactly the fused decode's paged output."""
-    w, art, op, items = _setup("qwen25_7b_paged")
+    """Layer-by-layer decode on two streams over 4 layers x {K, V} x 2
+    requests of the Qwen2.5-7B shape: stage 1 of layer l+1 overlaps stage 2
+    of layer l, two staging buffers and workspaces alternate, and from layer 2
+    on stage 1 waits until stage 2 of layer l-2 has released its buffer. The
+    paged pool equals the fused decode's bit for bit and the oracle's within
+    the decode tolerance."""
+    wname = "qwen25_7b_paged"
+    w = synth.workload(wname)
+    T, reqs = 8192, 2
+    slots = [(l, k) for l in range(4) for k in (0, 1)]
+    art = oracle_artifact(wname, slots, 4096)
+    op = art.params
+    items = []
+    for (l, k) in slots:
+        for r in range(reqs):
+            store = synth.storage(w, synth.gen_kv(w, l, k, synth.ROLE_EVAL, T, r))
+            items.append((l, k, O.encode(store, op, art.slots[(l, k)], l, k)))
     dc = DevCodec(art.serialize())
-    T = items[0][2].shape[0]
     bs = w.block_size
     per_req = (T + bs - 1) // bs
     rng = np.random.default_rng(5)
-    layers = sorted({l for l, _, _, _ in items})
+    layers = sorted({l for l, _, _ in items})
     pool_blocks = per_req * len(items)
-    srcs, jobs_by_layer, outs_f, outs_p = [], {l: [] for l in layers}, [], []
     perm = rng.permutation(pool_blocks).astype(np.int32)
-    tables = []
-    for i, (l, k, store, ref) in enumerate(items):
-        src = to_dev_bytes(ref.stream, 16)
-        srcs.append(src)
-        tables.append(torch.from_numpy(perm[i * per_req:(i + 1) * per_req].copy()).to(DEV))
+    srcs, tables = [], []
+    for i, (l, k, ref) in enumerate(items):
+        srcs.append(to_dev_bytes(ref.stream, 16))
+        tables.append(perm[i * per_req:(i + 1) * per_req].copy())
+    dtables = [torch.from_numpy(t).to(DEV) for t in tables]
     pool_f = torch.full((pool_blocks * bs, op.F), -7, dtype=torch.int16, device=DEV)
     pool_p = torch.full_like(pool_f, -7)
     nbytes = pool_f.numel() * 2
     fused_jobs, pipe_jobs = [], {l: [] for l in layers}
-    for i, (l, k, store, ref) in enumerate(items):
-        fused_jobs.append(K.make_job(l, k, T, srcs[i], pool_f, nbytes, tables[i], bs, pool_blocks))
-        pipe_jobs[l].append(K.make_job(l, k, T, srcs[i], pool_p, nbytes, tables[i], bs, pool_blocks))
+    for i, (l, k, ref) in enumerate(items):
+        fused_jobs.append(K.make_job(l, k, T, srcs[i], pool_f, nbytes, dtables[i], bs, pool_blocks))
+        pipe_jobs[l].append(K.make_job(l, k, T, srcs[i], pool_p, nbytes, dtables[i], bs, pool_blocks))
     s = torch.cuda.current_stream()
     assert np.all(dc.decode_jobs(fused_jobs, K.KVTC_BF16) == 0)
     nst = max(dc.codec.staging_bytes(js) for js in pipe_jobs.values())
-    stg = [torch.zeros(nst, dtype=torch.uint8, device=DEV) for _ in range(2)]
+    stg = [torch.full((nst,), 0xFF, dtype=torch.uint8, device=DEV) for _ in range(2)]
     nws = max(K.kvtc_workspace_bytes(len(js)) for js in pipe_jobs.values())
     wss = [torch.zeros(nws // 4, dtype=torch.int32, device=DEV) for _ in range(2)]
     su, sr = torch.cuda.Stream(), torch.cuda.Stream()
@@ -457,17 +516,24 @@ def test_two_stream_layer_pipeline_matches_fused():
     start.record(s)
     su.wait_event(start)
     sr.wait_event(start)
+    status = []
     for idx, l in enumerate(layers):
         b = idx % 2
         if idx >= 2:
-            su.wait_event(ev_r[idx - 2])
+            su.wait_event(ev_r[idx - 2])      # buffer b is free once layer idx-2 is restored
         dc.codec.decode_unpack(pipe_jobs[l], K.KVTC_BF16, stg[b], nst, wss[b], su)
         ev_u[idx].record(su)
         sr.wait_event(ev_u[idx])
         dc.codec.decode_restore(pipe_jobs[l], K.KVTC_BF16, stg[b], nst, wss[b], sr)
         ev_r[idx].record(sr)
+        if idx >= len(layers) - 2:            # the last use of each workspace
+            status.append((b, len(pipe_jobs[l])))
     torch.cuda.synchronize()
-    for b in range(2):
-        assert np.all(K.kvtc_read_device_status(wss[b], len(pipe_jobs[layers[0]]), s) == 0)
+    for b, n in status:
+        assert np.all(K.kvtc_read_device_status(wss[b], n, s) == 0)
     assert torch.equal(pool_f, pool_p)
     assert not torch.any(pool_f == -7)   # every block of the pool was written
+    t = np.arange(T)
+    for i, (l, k, ref) in enumerate(items):
+        rows = torch.from_numpy(tables[i][t // bs] * bs + t % bs).to(DEV)
+        _decode_check(w, op, art.slots[(l, k)], ref.stream, T, pool_p, K.KVTC_BF16, l, k, rows)
