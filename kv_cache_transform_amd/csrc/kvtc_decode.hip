@@ -207,179 +207,510 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
   if (h == 0) *(float*)(blk + KS * 1024 + t * 4) = tok_ok ? S : 1.f;
 }
 
-// Stage 2 segment: features [f0, f0 + FS) x blocks [c_lo, c_hi) of kDecTok
-// compressed tokens of one job. The slab of V' (fp16, FS rows of r_dec,
-// padded by 16 bytes per row) and mu stay in LDS; each wave then runs on its
-// own over every fourth block: it loads the block's B operands and
-// scales (the next block's are in flight meanwhile), runs FS / 32 x KS
-// MFMAs D[feature][token], forms S_t * D + mu and stores it through its LDS
-// staging rows as 128-byte segments. Every store is issued (rows past the
-// tile, or with a bad block table entry, go to the workspace sink), so the
-// number of memory operations per block is fixed and the wait for the next
-// block's operands never covers this block's stores.
-template <int KS, bool OUT32>
-__device__ void gemm_segment(const LaunchArgs& a, int j, uint32_t slab, uint32_t c_lo, uint32_t c_hi,
-                             uint8_t* smem) {
-  constexpr int FS = gemm_features(KS);
-  constexpr int NFB = FS / 32;
-  constexpr int OSZ = OUT32 ? 4 : 2;
-  constexpr int BPS = 128 / (32 * OSZ);           // feature blocks per 128-byte segment
-  constexpr int KA = KS > 0 ? KS : 1;
-  constexpr int AST = KS * 32 + 16;               // LDS bytes per V' row
+// ------------------------------------------------------- restore kernel ---
+//
+// Restore: x_hat = S_t * (V' B) + mu for every compressed row, where B holds
+// the token's dequantized coefficients c_hat / S_t as fp16 MFMA operands.
+// It is decode stage 2 (B from the staging stage 1 wrote) and, FUSED, the
+// whole decode (headers, passthrough rows, and B built here from the
+// records, with the arithmetic of stage 1).
+//
+// 512 threads (8 waves), one workgroup per CU, persistent over an equal
+// contiguous range of units; a unit is one block of kDecTok compressed tokens
+// of one slab of rest_slab(NFB) features of one job, units ordered (job,
+// slab, block). Wave w owns features [f0 + 32 NFB w, + 32 NFB) of the slab
+// and holds their V' fragments (NFB x KS of them, fp16) in registers while
+// its units share (job, slab), so a workgroup writes whole output rows (at
+// F = 1024 and NFB = 4, 2 KB per row, 64 KB per block) and each token is
+// dequantized once.
+//
+// Per unit u the workgroup runs one barrier-separated step of a pipeline
+// over LDS buffers indexed by unit parity:
+//   FUSED: the records of unit u + 2 are loaded into registers (16-byte
+//     loads), every wave computes unit u from frag[u % 2] and, half-way
+//     through its stores, waves 0 .. KS - 1 build the B fragments and token
+//     scales of unit u + 1 (one K step each) from rec[(u + 1) % 2] into
+//     frag[(u + 1) % 2] while the stores drain; the loaded records then go
+//     to rec[u % 2];
+//   not FUSED: the staging block of unit u + 1 is loaded, unit u computed
+//     from frag[u % 2], and the loaded block goes to frag[(u + 1) % 2].
+// Compute: B fragments from LDS, NFB x KS MFMAs D[feature][token]
+// (v_mfma_f32_32x32x16_f16, K-step-outer so consecutive MFMAs go to
+// different accumulators), S_t * D + mu through the wave's LDS staging rows,
+// then coalesced streaming 16-byte stores of 256-byte row pieces. Every wave
+// issues the same loads and stores for every unit (addresses are clamped to
+// valid ones, rows without a destination go to the workspace sink), so the
+// wait for the next unit's loads, issued before this unit's stores, never
+// covers those stores.
+
+struct RUnit {
+  int j;              // job, -1 past the workgroup's range
+  uint32_t slab, c;   // feature slab, block of the job's compressed rows
+  uint32_t nrec;      // compressed tokens in the block
+  uint32_t n_ch;      // blocks of the job
+  uint32_t left;      // units of the range from this one on (0: past it)
+};
+
+// Unit u of the launch (a search over the jobs and a division: once per
+// workgroup); rest_next steps to the following unit without either.
+__device__ __forceinline__ RUnit rest_unit_at(const LaunchArgs& a, uint32_t u, uint32_t u_hi) {
+  RUnit r;
+  r.left = u < u_hi ? u_hi - u : 0u;
+  if (!r.left) {
+    r.j = -1;
+    r.slab = r.c = r.nrec = r.n_ch = 0;
+    return r;
+  }
+  int j = 0;
+  while (j + 1 < a.n_jobs && a.jobs[j + 1].tile_begin <= u) ++j;
   const JobDesc& jd = a.jobs[j];
-  CSlot& sl = slot_of(a, jd.slot);
-  if (prior_rank(a, jd.status_idx) != 0) return;  // stage 1 rejected it
-  const int F = a.F;
-  const int f0 = (int)slab * FS;
-  const uint32_t t0 = 0;
-  const int lane = threadIdx.x & 63, h = lane >> 5, c16 = lane & 7;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-
-  uint8_t* As = smem;
-  float* mu_s = (float*)(smem + FS * AST);
-  uint8_t* stg = smem + FS * AST + FS * 4 + wave * kDecTok * kOutRow;
-  {
-    const int r_dec = sl.r_dec;
-    const uint8_t* vdec = a.state + sl.vdec_off;
-    for (int i = threadIdx.x; i < FS * 2 * KS; i += kGemmThreads) {
-      const int row = i / (2 * KS), c = i - row * (2 * KS);
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (f0 + row < F) v = *(const uint4*)(vdec + ((size_t)(f0 + row) * r_dec + 8 * c) * 2);
-      *(uint4*)(As + row * AST + 16 * c) = v;
-    }
-    const float* mu = (const float*)(a.state + sl.mu_off);
-    for (int i = threadIdx.x; i < FS; i += kGemmThreads) mu_s[i] = f0 + i < F ? mu[f0 + i] : 0.f;
+  r.j = j;
+  r.n_ch = (jd.tc + kDecTok - 1) / kDecTok;
+  const uint32_t lu = u - jd.tile_begin;
+  r.slab = lu / r.n_ch;
+  r.c = lu - r.slab * r.n_ch;
+  r.nrec = min((uint32_t)kDecTok, jd.tc - r.c * kDecTok);
+  return r;
+}
+__device__ __forceinline__ RUnit rest_next(const LaunchArgs& a, RUnit r, uint32_t n_slabs) {
+  if (r.left <= 1) {
+    r.left = 0;
+    r.j = -1;
+    return r;
   }
-  __syncthreads();
-
-  const uint8_t* stg_job = (const uint8_t*)jd.staging;
-  constexpr size_t BB = stg_block_bytes(KS);
-  const uint32_t tb0 = t0 / kDecTok;
-  uint8_t* dst = (uint8_t*)jd.dst;
-  uint8_t* sink = a.sink + c16 * 16;
-  int bad = 0;
-  // Job fields used per block, held in registers.
-  const uint32_t tc = jd.tc, s1 = jd.s1;
-  const int32_t* btab = jd.block_table;
-  const int bsz = jd.block_size, bsh = jd.bs_shift, nblk = jd.n_blocks;
-
-  // Operands of block c: B fragments, the lane's token scale and the block
-  // table entries of the rows this lane stores (r = 8 it + lane / 8).
-  uint4 Bn[KA];
-  float Sn;
-  int btn[4];
-  auto fetch = [&](uint32_t c) {
-    const uint8_t* blk = stg_job + (size_t)(tb0 + c) * BB;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) Bn[s] = *(const uint4*)(blk + s * 1024 + lane * 16);
-    // stage 1 writes no staging when no component is kept (KS == 0)
-    Sn = KS > 0 ? *(const float*)(blk + KS * 1024 + (lane & 31) * 4) : 1.f;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const uint32_t tt = s1 + min(t0 + c * kDecTok + 8 * it + (lane >> 3), tc - 1);
-      btn[it] = btab[bsh >= 0 ? tt >> bsh : tt / (uint32_t)bsz];
+  --r.left;
+  if (++r.c == r.n_ch) {
+    r.c = 0;
+    if (++r.slab == n_slabs) {
+      r.slab = 0;
+      do {   // the range still has units, so a job with rows follows
+        ++r.j;
+      } while (a.jobs[r.j].n_ctiles == 0);
+      r.n_ch = (a.jobs[r.j].tc + kDecTok - 1) / kDecTok;
     }
-  };
-  // Operands in use: B fragments, token scale and the store addresses of
-  // the lane's rows; taken over from the fetched ones only after the
-  // block's stores were issued, so every wait covers loads alone.
-  uint4 B[KA];
-  float S;
-  uint8_t* dp[4];
-  auto take = [&](uint32_t c) {
-#pragma unroll
-    for (int s = 0; s < KS; ++s) B[s] = Bn[s];
-    S = Sn;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const uint32_t tok = t0 + c * kDecTok + 8 * it + (lane >> 3);
-      const uint32_t tt = s1 + tok;
-      const int bt = btn[it];
-      const bool blk_ok = bt >= 0 && bt < nblk;
-      bad |= (int)(tok < tc && !blk_ok);
-      const uint32_t in_blk = bsh >= 0 ? tt & ((1u << bsh) - 1u) : tt % (uint32_t)bsz;
-      const long row = (long)bt * bsz + (long)in_blk;
-      dp[it] = tok < tc && blk_ok ? dst + (row * F + f0) * OSZ + c16 * 16 : sink;
-    }
-  };
-  if (c_lo + wave < c_hi) {
-    fetch(c_lo + wave);
-    take(c_lo + wave);
   }
-  for (uint32_t c = c_lo + wave; c < c_hi; c += kGemmWaves) {
-    fetch(min(c + kGemmWaves, c_hi - 1));   // unconditional: a fixed count of loads per block
-    // Keep the scheduler from pulling the next block's takeover (which waits
-    // for these loads) into this block's work.
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) {
-      const uint8_t* arow = As + (fb * 32 + (lane & 31)) * AST + 16 * h;
-      f32x16 acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, *(const uint4*)(arow + 32 * s)),
-                                                     __builtin_bit_cast(f16x8, B[s]), acc, 0, 0, 0);
-      // D[feature][token]: token lane % 32, features 8 qd + 4 h + {0..3}
-      uint8_t* srow = stg + (lane & 31) * kOutRow + (fb % BPS) * 32 * OSZ;
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int fl = 8 * qd + 4 * h;
-        const float4 m4 = *(const float4*)(mu_s + 32 * fb + fl);
-        const float o0 = __builtin_fmaf(acc[4 * qd + 0], S, m4.x);
-        const float o1 = __builtin_fmaf(acc[4 * qd + 1], S, m4.y);
-        const float o2 = __builtin_fmaf(acc[4 * qd + 2], S, m4.z);
-        const float o3 = __builtin_fmaf(acc[4 * qd + 3], S, m4.w);
-        if (OUT32)
-          *(float4*)(srow + fl * 4) = make_float4(o0, o1, o2, o3);
-        else
-          *(uint2*)(srow + fl * 2) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-      }
-      if (fb % BPS == BPS - 1) {
-        const int fs = 32 * (fb - BPS + 1);            // segment's first feature in the slab
-        const bool in_f = f0 + fs < F;                 // F % 64 == 0: whole segments
-        wave_lds_sync();
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const uint4 v = *(const uint4*)(stg + (8 * it + (lane >> 3)) * kOutRow + c16 * 16);
-          // streaming (non-temporal) stores: the output is not read back here
-          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
-                                      (u32x4*)(dp[it] == sink || !in_f ? sink : dp[it] + fs * OSZ));
-        }
-        wave_lds_sync();
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    take(min(c + kGemmWaves, c_hi - 1));
-  }
-  if (bad) set_status(a, jd.status_idx, KVTC_E_INVALID);
-  __syncthreads();  // the slab and staging rows are free for the next tile
+  r.nrec = min((uint32_t)kDecTok, a.jobs[r.j].tc - r.c * kDecTok);
+  return r;
 }
 
-// Stage 2 work is counted in units of one block of kDecTok tokens of one
-// feature slab of one job, ordered (job, slab, block); job j's units start
-// at tile_begin and number n_ctiles = slabs * blocks. The host launches at
-// most as many workgroups as fit on the device at once and each takes an
-// equal contiguous range of units, so all finish together; a range crosses
-// few (job, slab) boundaries (the slab of V' is loaded once per segment),
-// and the ranges in flight on one XCD cover the slabs of the same tokens.
-template <int KS, bool OUT32>
-__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4))) void gemm_kernel(const LaunchArgs a) {
+// Output row of the block's token i (lanes < 32), for the unit's job: >= 0
+// a row of dst, -1 past the job's compressed rows, -2 a bad block table
+// entry. The block table is read for every thread (index 0 where there is no
+// token), so all threads issue the same load.
+__device__ __forceinline__ int rest_row_entry(const JobDesc& jd, uint32_t c, int i, int& ent) {
+  const uint32_t tok = c * kDecTok + (uint32_t)i;
+  const bool in = i < kDecTok && tok < jd.tc;
+  const uint32_t tt = jd.s1 + tok;
+  const uint32_t bi = in ? (jd.bs_shift >= 0 ? tt >> jd.bs_shift : tt / (uint32_t)jd.block_size) : 0u;
+  ent = jd.block_table[bi];
+  return in ? 1 : 0;
+}
+__device__ __forceinline__ int rest_row(const JobDesc& jd, uint32_t c, int i, int in, int ent) {
+  if (!in) return -1;
+  if (ent < 0 || ent >= jd.n_blocks) return -2;
+  const uint32_t tt = jd.s1 + c * kDecTok + (uint32_t)i;
+  const uint32_t in_blk = jd.bs_shift >= 0 ? tt & ((1u << jd.bs_shift) - 1u) : tt % (uint32_t)jd.block_size;
+  return ent * jd.block_size + (int)in_blk;
+}
+
+// Rows of dst a store may address: n_blocks * block_size (the host checks
+// them against dst_capacity), or T for a contiguous job (one block of 2^30
+// rows through a zero entry).
+__device__ __forceinline__ uint32_t rest_row_limit(const JobDesc& jd) {
+  return jd.n_blocks == 1 && jd.block_size == (1 << 30) ? jd.T : (uint32_t)jd.n_blocks * (uint32_t)jd.block_size;
+}
+
+// Epilogue of one round of FBR feature blocks (32 features each, starting at
+// block fb0) into the wave's staging rows and out to memory: RB = FBR * 32 *
+// OSZ bytes per row. fill() runs between the round's stores (once, after the
+// first half of them). Returns whether a bad block table entry was met.
+template <int OSZ, int FBR, int NFB, class Fill>
+__device__ __forceinline__ bool rest_epilogue(const f32x16 (&acc)[NFB], int fb0, float S, const float* mu_w,
+                                              uint8_t* stg, const int* rows, uint8_t* dst_w, uint8_t* sink,
+                                              bool store_ok, int F, uint32_t row_lim, Fill&& fill) {
+  constexpr int RB = FBR * 32 * OSZ;          // bytes per row piece (128 or 256)
+  constexpr int LPR = RB / 16;                // lanes per row piece
+  constexpr int RPI = 64 / LPR;               // rows per store instruction
+  constexpr int NST = kDecTok / RPI;          // store instructions
+  const int lane = threadIdx.x & 63, t = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int f = 0; f < FBR; ++f) {
+    // D[feature][token]: token t, features 8 qd + 4 h + {0..3} of block fb0 + f
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const int fl = 32 * f + 8 * qd + 4 * h;
+      const float4 m4 = *(const float4*)(mu_w + 32 * fb0 + fl);
+      const float o0 = __builtin_fmaf(acc[fb0 + f][4 * qd + 0], S, m4.x);
+      const float o1 = __builtin_fmaf(acc[fb0 + f][4 * qd + 1], S, m4.y);
+      const float o2 = __builtin_fmaf(acc[fb0 + f][4 * qd + 2], S, m4.z);
+      const float o3 = __builtin_fmaf(acc[fb0 + f][4 * qd + 3], S, m4.w);
+      if (OSZ == 4)
+        *(float4*)(stg + t * kRestStgRow + fl * 4) = make_float4(o0, o1, o2, o3);
+      else
+        *(uint2*)(stg + t * kRestStgRow + fl * 2) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+    }
+  }
+  wave_lds_sync();
+  bool bad = false;
+  const int col = (lane % LPR) * 16;
+#pragma unroll
+  for (int k = 0; k < NST; ++k) {
+    const int r = k * RPI + lane / LPR;
+    const uint4 v = *(const uint4*)(stg + r * kRestStgRow + col);
+    const int row = rows[r];
+    bad |= row == -2;
+    uint8_t* p = store_ok && row >= 0 && (uint32_t)row < row_lim ? dst_w + ((size_t)row * F + 32 * fb0) * OSZ + col
+                                                                 : sink + (lane & 15) * 16;
+    // streaming (non-temporal) stores: the output is not read back here
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), (u32x4*)p);
+    if (k == NST / 2 - 1) {
+      __builtin_amdgcn_sched_barrier(0);
+      fill();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wave_lds_sync();
+  return bad;
+}
+
+template <int KS, int NFB, bool FUSED, bool OUT32>
+__global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2))) void restore_kernel(const LaunchArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const uint64_t U = a.total_tiles;
-  const uint32_t g = logical_tile();
-  uint32_t u = (uint32_t)(U * g / gridDim.x);
-  const uint32_t u_end = (uint32_t)(U * (g + 1) / gridDim.x);
-  while (u < u_end) {
-    const int j = find_job(a, u);
-    const JobDesc& jd = a.jobs[j];
-    const uint32_t n_ch = (jd.tc + kDecTok - 1) / kDecTok;
-    const uint32_t lu = u - jd.tile_begin;
-    const uint32_t slab = lu / n_ch, c = lu - slab * n_ch;
-    const uint32_t seg_end = min(u_end, jd.tile_begin + (slab + 1) * n_ch);
-    gemm_segment<KS, OUT32>(a, j, slab, c, c + (seg_end - u), smem);
-    u = seg_end;
+  __shared__ int pflag;
+  constexpr int FPW = 32 * NFB;                 // features per wave
+  constexpr int SLAB = rest_slab(NFB);
+  constexpr int KA = KS > 0 ? KS : 1;
+  constexpr size_t FB = rest_frag_bytes(KS);
+  constexpr int OSZ = OUT32 ? 4 : 2;
+  // 16-byte vectors per thread: a block's records (rb <= 24 KS) or staging
+  constexpr int NVR = FUSED ? (kDecTok * 24 * KS / 16 + kRestThreads - 1) / kRestThreads : 0;
+  constexpr int NVS = FUSED ? 0 : (KS > 0 ? ((int)stg_block_bytes(KS) / 16 + kRestThreads - 1) / kRestThreads : 0);
+  constexpr int NXV = NVR > NVS ? NVR : (NVS > 0 ? NVS : 1);
+  constexpr int NMU = (SLAB + kRestThreads - 1) / kRestThreads;   // mu values per thread
+  const int F = a.F;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, t = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t g = logical_tile(), ng = gridDim.x;
+  const int in_esz = a.dtype == KVTC_F32 ? 4 : 2;
+  const uint32_t n_slabs = (uint32_t)((F + SLAB - 1) / SLAB);
+
+  float* const mu_s = (float*)(smem + kRestMuOff);
+  uint8_t* const stg = smem + kRestStgOff + (size_t)wave * kDecTok * kRestStgRow;
+  uint8_t* const frag0 = smem + kRestFragOff;
+  uint8_t* const rec0 = smem + kRestFragOff + 2 * FB;
+  const uint32_t rec_lds = a.wave_lds;
+  const size_t rec_rows_off = rec_lds - kDecTok * 4;
+  auto fragb = [&](uint32_t u) { return frag0 + (u & 1u) * FB; };
+  auto recb = [&](uint32_t u) { return rec0 + (u & 1u) * rec_lds; };
+
+  const uint32_t U = a.total_tiles;
+  const uint32_t u_lo = (uint32_t)((uint64_t)U * g / ng), u_hi = (uint32_t)((uint64_t)U * (g + 1) / ng);
+
+  if (u_lo < u_hi) {   // uniform: the workgroup has units
+    // ---- loads of a unit into registers, and their commit to LDS. The
+    // per-job fields are kept while consecutive units share the job.
+    struct Src {
+      int j;
+      const uint8_t* base;   // FUSED: the job's records; else: its staging
+      const uint8_t* hdr;    // the stream (its header is always readable)
+      uint32_t rb, rbp, mrb;
+    };
+    auto src_of = [&](int j) __attribute__((always_inline)) {
+      Src q;
+      const JobDesc& jd = a.jobs[j];
+      q.j = j;
+      q.hdr = (const uint8_t*)jd.src;
+      if (FUSED) {
+        CSlot& sl = slot_of(a, jd.slot);
+        q.rb = (uint32_t)sl.record_bytes;
+        q.rbp = (uint32_t)dec_rec_stride((int)q.rb);
+        // row of record byte x: (x * mrb) >> 24 = x / rb exactly for x < 2^24 / rb
+        q.mrb = q.rb ? (0xFFFFFFu + q.rb) / q.rb : 0u;
+        q.base = q.hdr + record_base(jd, F, in_esz);
+      } else {
+        q.rb = q.rbp = q.mrb = 0;
+        q.base = (const uint8_t*)jd.staging;
+      }
+      return q;
+    };
+    auto fetch = [&](const RUnit& r, const Src& q, u32x4 (&xv)[NXV], int& ent, int& in) __attribute__((always_inline)) {
+      const JobDesc& jd = a.jobs[r.j];
+      if (FUSED) {
+        const uint8_t* src = q.base + (size_t)r.c * kDecTok * q.rb;
+        const uint32_t nbytes = r.nrec * q.rb, nvv = nbytes / 16u;
+#pragma unroll
+        for (int i = 0; i < NVR; ++i) {
+          const uint32_t v = (uint32_t)(tid + kRestThreads * i);
+          // vector nvv (a ragged end): the 16 bytes that end at the block's
+          // last byte (at least 48 bytes into the stream, so in bounds); past
+          // the block: the stream header
+          const uint8_t* pv = v < nvv ? src + (size_t)v * 16
+                            : v == nvv && nbytes > nvv * 16u ? src + nbytes - 16 : q.hdr;
+          xv[i] = *(const u32x4*)pv;
+        }
+      } else {
+        const uint8_t* blk = q.base + (size_t)r.c * stg_block_bytes(KS);
+        constexpr uint32_t nv = (uint32_t)stg_block_bytes(KS) / 16u;
+#pragma unroll
+        for (int i = 0; i < NVS; ++i) {
+          const uint32_t v = (uint32_t)(tid + kRestThreads * i);
+          xv[i] = *(const u32x4*)(blk + (size_t)(v < nv ? v : 0u) * 16);
+        }
+      }
+      in = rest_row_entry(jd, r.c, tid, ent);
+    };
+    auto commit = [&](const RUnit& r, const Src& q, const u32x4 (&xv)[NXV], int ent, int in, uint8_t* dstb,
+                      int* rows) __attribute__((always_inline)) {
+      const JobDesc& jd = a.jobs[r.j];
+      if (FUSED) {
+        const uint32_t nbytes = r.nrec * q.rb, nvv = nbytes / 16u;
+#pragma unroll
+        for (int i = 0; i < NVR; ++i) {
+          const uint32_t v = (uint32_t)(tid + kRestThreads * i);
+          const uint32_t x = v * 16u;
+          // byte x goes to x + (x / rb) (rbp - rb); a vector never straddles rows
+          if (v < nvv) {
+            *(u32x4*)(dstb + x + ((x * q.mrb) >> 24) * (q.rbp - q.rb)) = xv[i];
+          } else if (v == nvv && nbytes > x) {
+            // the ragged end (then rb % 16 != 0 and rbp == rb): bytes
+            // [x, nbytes) are the last nbytes - x of the vector
+            const uint32_t o = 16u - (nbytes - x);
+#pragma unroll
+            for (uint32_t b = 0; b < 16; ++b)
+              if (b >= o) dstb[nbytes - 16u + b] = (uint8_t)(xv[i][b / 4] >> (8 * (b % 4)));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NVS; ++i) {
+          const uint32_t v = (uint32_t)(tid + kRestThreads * i);
+          if (v < (uint32_t)stg_block_bytes(KS) / 16u) *(u32x4*)(dstb + (size_t)v * 16) = xv[i];
+        }
+      }
+      if (tid < kDecTok) rows[tid] = rest_row(jd, r.c, tid, in, ent);
+    };
+
+    // ---- FUSED: B fragments and token scales of a unit from its records
+    // (the arithmetic of stage 1), one K step per wave.
+    auto build = [&](const RUnit& r, const uint8_t* recs, uint8_t* fr) __attribute__((always_inline)) {
+      const JobDesc& jd = a.jobs[r.j];
+      CSlot& sl = slot_of(a, jd.slot);
+      const int rbp = dec_rec_stride(sl.record_bytes), G = sl.G;
+      const bool tok_ok = (uint32_t)t < r.nrec;
+      const uint8_t* rr = recs + (tok_ok ? t : 0) * rbp;
+#pragma unroll
+      for (int s0 = 0; s0 < KS; s0 += kRestWaves) {
+        const int s = s0 + wave;
+        if (s < KS) {   // uniform per wave
+          // S_t from every active group of the token (each has a component
+          // among the K steps)
+          float m = 0.f;
+#pragma unroll
+          for (int s2 = 0; s2 < KS; ++s2) {
+            const float2 ps = get_scales(rr, 16 * s2 / G);
+            m = fmaxf(m, fmaxf(fabsf(ps.x), fabsf(ps.x + ps.y)));
+          }
+          float S, Sinv;
+          token_scale(m, S, Sinv);
+          const int ag = 16 * s / G;
+          const int w = slot_width(sl, ag);
+          const float kf = (float)((1 << w) - 1);
+          const float2 ps = get_scales(rr, ag);
+          const uint4 f = tok_ok ? frag_from_bits(code_bits8(rr, sl, ag, 16 * s + 8 * h - ag * G, w), ps.x, ps.y,
+                                                  w, kf, 1.0f / kf, Sinv)
+                                 : make_uint4(0u, 0u, 0u, 0u);
+          *(uint4*)(fr + s * 1024 + lane * 16) = f;
+          if (s == 0 && h == 0) *(float*)(fr + KS * 1024 + t * 4) = tok_ok ? S : 1.f;
+        }
+      }
+      if (wave == kRestWaves - 1 && lane < kDecTok)   // the block's output rows
+        ((int*)(fr + stg_block_bytes(KS)))[lane] = ((const int*)(recs + rec_rows_off))[lane];
+    };
+
+    // ---- the (job, slab) segment whose V' fragments and mu are loaded:
+    // seg_issue issues the loads, seg_finish consumes them.
+    int seg_j = -1;
+    uint32_t seg_slab = 0;
+    bool job_ok = false;
+    uint4 A[NFB][KA];
+    float mreg[NMU];
+    int f_w = 0;          // first feature of this wave
+    bool active = false;  // the wave has features (f_w < F)
+    // A bad block table entry met in the segment's units. It is reported when
+    // the segment ends, followed by a full wait: a status atomic among the
+    // loop's loads and stores would make the compiler treat the memory counter
+    // as out of order and drain every store before each wait for a load.
+    bool bad_seen = false;
+    auto report_bad = [&]() __attribute__((always_inline)) {
+      if (bad_seen && seg_j >= 0 && job_ok) set_status(a, a.jobs[seg_j].status_idx, KVTC_E_INVALID);
+      bad_seen = false;
+      __builtin_amdgcn_s_waitcnt(0);
+    };
+    auto seg_issue = [&](const RUnit& r) __attribute__((always_inline)) {
+      seg_j = r.j;
+      seg_slab = r.slab;
+      const JobDesc& jd = a.jobs[r.j];
+      CSlot& sl = slot_of(a, jd.slot);
+      const int f0 = (int)r.slab * SLAB;
+      const float* mu = (const float*)(a.state + sl.mu_off);
+#pragma unroll
+      for (int i = 0; i < NMU; ++i) {
+        const int fi = f0 + tid + kRestThreads * i;
+        mreg[i] = mu[fi < F ? fi : 0];
+      }
+      f_w = f0 + wave * FPW;
+      active = f_w < F;
+      if (active) {
+        const uint8_t* vdec = a.state + sl.vdec_off;
+        const int r_dec = sl.r_dec;
+#pragma unroll
+        for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+          for (int s = 0; s < KS; ++s)
+            A[fb][s] = *(const uint4*)(vdec + ((size_t)(f_w + 32 * fb + t) * r_dec + 16 * s + 8 * h) * 2);
+      }
+      job_ok = FUSED ? check_header(a, jd, sl) == KVTC_OK : prior_rank(a, jd.status_idx) == 0;
+    };
+    auto seg_finish = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NMU; ++i) {
+        const int li = tid + kRestThreads * i;
+        if (li < SLAB) mu_s[li] = seg_slab * SLAB + li < (uint32_t)F ? mreg[i] : 0.f;
+      }
+    };
+
+    // ---- compute one unit from its fragment buffer and store it; fill()
+    // runs while the stores drain
+    auto compute = [&](const RUnit& r, const uint8_t* fr, auto&& fill) __attribute__((always_inline)) {
+      const JobDesc& jd = a.jobs[r.j];
+      f32x16 acc[NFB];
+#pragma unroll
+      for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[fb][i] = 0.f;
+      if (active) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const f16x8 b = __builtin_bit_cast(f16x8, *(const uint4*)(fr + s * 1024 + lane * 16));
+#pragma unroll
+          for (int fb = 0; fb < NFB; ++fb)
+            acc[fb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, A[fb][s]), b, acc[fb], 0, 0, 0);
+        }
+      }
+      const float S = KS > 0 ? *(const float*)(fr + KS * 1024 + t * 4) : 1.f;
+      const int* rows = (const int*)(fr + stg_block_bytes(KS));
+      const float* mu_w = mu_s + wave * FPW;
+      uint8_t* dst_w = (uint8_t*)jd.dst + (size_t)f_w * OSZ;
+      const bool store_ok = job_ok && active;
+      const uint32_t row_lim = rest_row_limit(jd);
+      // (the output type is a template parameter: with a run-time branch the
+      // compiler could not count the stores on every path and would drain
+      // them before the next wait for a load)
+      if (OUT32) {
+        bad_seen |= rest_epilogue<4, 2, NFB>(acc, 0, S, mu_w, stg, rows, dst_w, a.sink, store_ok, F, row_lim, fill);
+        if (NFB > 2)
+          bad_seen |= rest_epilogue<4, 2, NFB>(acc, 2, S, mu_w, stg, rows, dst_w, a.sink, store_ok, F, row_lim,
+                                               [] {});
+      } else {
+        bad_seen |= rest_epilogue<2, NFB, NFB>(acc, 0, S, mu_w, stg, rows, dst_w, a.sink, store_ok, F, row_lim, fill);
+      }
+    };
+
+    // ---- prologue: the first units' loads and the first segment's loads
+    // are all issued before any is waited for
+    RUnit cur = rest_unit_at(a, u_lo, u_hi);
+    RUnit nx = rest_next(a, cur, n_slabs);
+    Src sq = src_of(cur.j);                 // the job of the unit last fetched
+    u32x4 xv[NXV], xv2[NXV];
+    int ent, in, ent2 = 0, in2 = 0;
+    fetch(cur, sq, xv, ent, in);
+    const Src sq2 = FUSED && nx.j >= 0 ? src_of(nx.j) : sq;
+    if (FUSED) fetch(nx.j >= 0 ? nx : cur, sq2, xv2, ent2, in2);
+    seg_issue(cur);
+    if (FUSED) {
+      commit(cur, sq, xv, ent, in, recb(u_lo), (int*)(recb(u_lo) + rec_rows_off));
+      commit(nx.j >= 0 ? nx : cur, sq2, xv2, ent2, in2, recb(u_lo + 1), (int*)(recb(u_lo + 1) + rec_rows_off));
+    } else {
+      commit(cur, sq, xv, ent, in, fragb(u_lo), (int*)(fragb(u_lo) + stg_block_bytes(KS)));
+    }
+    seg_finish();
+    __syncthreads();
+    if (FUSED) {
+      sq = sq2;
+      build(cur, recb(u_lo), fragb(u_lo));
+      __syncthreads();
+    }
+
+    for (uint32_t u = u_lo; u < u_hi; ++u) {
+      if (cur.j != seg_j || cur.slab != seg_slab) {   // uniform: a new segment
+        report_bad();
+        seg_issue(cur);
+        seg_finish();
+        __syncthreads();
+      }
+      // Every iteration issues the same loads and commits them (past the
+      // range the current unit is loaded again into a buffer nothing reads),
+      // so the compiler can count this unit's stores between the loads and
+      // the wait for them.
+      if (FUSED) {
+        const RUnit nx2 = rest_next(a, nx, n_slabs);
+        const RUnit fu = nx2.j >= 0 ? nx2 : cur;
+        if (fu.j != sq.j) sq = src_of(fu.j);
+        fetch(fu, sq, xv, ent, in);
+        __builtin_amdgcn_sched_barrier(0);
+        // unit u + 1 is dequantized while unit u's stores drain
+        compute(cur, fragb(u), [&] {
+          if (nx.j >= 0) build(nx, recb(u + 1), fragb(u + 1));
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        commit(fu, sq, xv, ent, in, recb(u), (int*)(recb(u) + rec_rows_off));
+        __syncthreads();
+        cur = nx;
+        nx = nx2;
+      } else {
+        const RUnit fu = nx.j >= 0 ? nx : cur;
+        if (fu.j != sq.j) sq = src_of(fu.j);
+        fetch(fu, sq, xv, ent, in);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(cur, fragb(u), [] {});
+        __builtin_amdgcn_sched_barrier(0);
+        commit(fu, sq, xv, ent, in, fragb(u + 1), (int*)(fragb(u + 1) + stg_block_bytes(KS)));
+        __syncthreads();
+        cur = nx;
+        nx = rest_next(a, nx, n_slabs);
+      }
+    }
+    report_bad();
+  }
+
+  if (FUSED) {
+    // Header and passthrough units (kRestPassRows rows each; job j owns
+    // max(1, units) of them from cblk_begin, its first one records the header
+    // check in the job's status word), split evenly over the workgroups; run
+    // last, while the last unit's stores drain. (The compressed rows check
+    // the header themselves.)
+    const uint32_t P = a.total_cblks;
+    const uint32_t p_end = (uint32_t)((uint64_t)P * (g + 1) / ng);
+    int j = 0;
+    __syncthreads();   // the passthrough row list reuses LDS
+    for (uint32_t p = (uint32_t)((uint64_t)P * g / ng); p < p_end; ++p) {
+      while (j + 1 < a.n_jobs && a.jobs[j + 1].cblk_begin <= p) ++j;
+      const JobDesc& jd = a.jobs[j];
+      const uint32_t lp = p - jd.cblk_begin;
+      const int st = check_header(a, jd, slot_of(a, jd.slot));   // uniform
+      if (lp == 0 && tid == 0) set_status(a, jd.status_idx, st);
+      if (st != KVTC_OK) continue;
+      if (tid == 0) pflag = 0;
+      __syncthreads();
+      bool ok = true;
+      if (lp * kRestPassRows < jd.s1 + jd.w1)
+        ok = decode_passthrough<kRestThreads, kRestPassRows>(a, jd, lp, (long*)smem);
+      if (!ok) atomicExch(&pflag, 1);
+      __syncthreads();
+      if (tid == 0 && pflag) set_status(a, jd.status_idx, KVTC_E_INVALID);
+      __syncthreads();   // row list and flag are free for the next unit
+    }
   }
 }
 
@@ -443,28 +774,35 @@ int launch_prep(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
   return (int)hipGetLastError();
 }
 
-template <bool OUT32>
-static int launch_gemm_o(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
-#define KVTC_GEMM(KV)                                                                        \
-  case KV: {                                                                                 \
-    allow_lds(gemm_kernel<KV, OUT32>, lds);                                                  \
-    const dim3 g(std::min({std::max(8u, a.total_tiles / (8 * kGemmMinUnits) * 8),         \
-                           resident_grid(gemm_kernel<KV, OUT32>, kGemmThreads, lds),       \
-                           persistent_grid_cap()}));                                       \
-    hipLaunchKernelGGL((gemm_kernel<KV, OUT32>), g, dim3(kGemmThreads), lds, s, a);              \
-    break;                                                                                   \
+// Restore launch: nfb from the K-step count and F; at most 8 / kRestWaves
+// workgroups per CU (the occupancy query), fewer when there are few units.
+template <bool FU, bool O32>
+static int launch_restore_t(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
+  const int nfb = rest_nfb(ks, a.F);
+#define KVTC_REST(KV, NFBV)                                                                      \
+  if (ks == KV && nfb == NFBV) {                                                                 \
+    allow_lds(restore_kernel<KV, NFBV, FU, O32>, lds);                                           \
+    const dim3 g(std::min({std::max(8u, (a.total_tiles + 7u) / 8u * 8u),                         \
+                           resident_grid(restore_kernel<KV, NFBV, FU, O32>, kRestThreads, lds,  \
+                                         8 / kRestWaves),                                        \
+                           persistent_grid_cap()}));                                             \
+    hipLaunchKernelGGL((restore_kernel<KV, NFBV, FU, O32>), g, dim3(kRestThreads), lds, s, a);  \
+    return (int)hipGetLastError();                                                               \
   }
-  switch (ks) {
-    KVTC_KS_CASES(KVTC_GEMM)
-    default:
-      return (int)hipErrorInvalidValue;
-  }
-#undef KVTC_GEMM
-  return (int)hipGetLastError();
+#define KVTC_REST4(KV) KVTC_REST(KV, 4)
+#define KVTC_REST2(KV) KVTC_REST(KV, 2)
+  KVTC_REST4(0) KVTC_REST4(1) KVTC_REST4(2) KVTC_REST4(3) KVTC_REST4(4) KVTC_REST4(5) KVTC_REST4(6)
+  KVTC_KS_CASES(KVTC_REST2)
+#undef KVTC_REST2
+#undef KVTC_REST4
+#undef KVTC_REST
+  return (int)hipErrorInvalidValue;
 }
 
-int launch_gemm(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
-  return a.out_dtype == KVTC_F32 ? launch_gemm_o<true>(a, ks, lds, s) : launch_gemm_o<false>(a, ks, lds, s);
+int launch_restore(const LaunchArgs& a, int ks, bool fused, size_t lds, hipStream_t s) {
+  const bool o32 = a.out_dtype == KVTC_F32;
+  return fused ? (o32 ? launch_restore_t<true, true>(a, ks, lds, s) : launch_restore_t<true, false>(a, ks, lds, s))
+               : (o32 ? launch_restore_t<false, true>(a, ks, lds, s) : launch_restore_t<false, false>(a, ks, lds, s));
 }
 
 int launch_unpack(const LaunchArgs& a, int G, size_t lds, void* codes, void* ss, hipStream_t s) {

@@ -610,21 +610,21 @@ size_t kvtc_staging_bytes(const kvtc_codec* c, const kvtc_job* jobs, int32_t n_j
 }
 
 size_t kvtc_decode_workspace_bytes(const kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs) {
-  // 0 flags jobs the codec cannot decode; jobs without compressed rows need
-  // no staging but still a workspace.
+  // 0 flags jobs the codec cannot decode; the fused decode needs only the
+  // status words and the sink.
   if (!c || !jobs || n_jobs <= 0) return 0;
   for (int i = 0; i < n_jobs; ++i) {
     int idx;
     if (!slot_index(c, jobs[i].layer, jobs[i].kind, &idx) || !c->slots[idx].calibrated) return 0;
   }
-  return kvtc_workspace_bytes(n_jobs) + kvtc_staging_bytes(c, jobs, n_jobs);
+  return kvtc_workspace_bytes(n_jobs);
 }
 
 }  // extern "C"
 
 namespace {
 
-enum class Mode { Encode, Unpack, Restore, Pack, UnpackCodes };
+enum class Mode { Encode, Unpack, Restore, Decode, Pack, UnpackCodes };
 
 // Launch stamps for the workspace status words (0 is never issued).
 uint32_t next_epoch() {
@@ -647,7 +647,7 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
   if (!d_ws || !aligned16(d_ws)) return fail(KVTC_E_INVALID, "workspace must be non-null and aligned");
   if (!c->d_state || c->uploaded_version != c->calib_version)
     return fail(KVTC_E_INVALID, "device state is missing or stale: call kvtc_upload");
-  const bool dec = mode == Mode::Unpack || mode == Mode::Restore;
+  const bool dec = mode == Mode::Unpack || mode == Mode::Restore || mode == Mode::Decode;
   if (dec && out_dtype != KVTC_F32 && out_dtype != KVTC_BF16) return fail(KVTC_E_INVALID, "bad output dtype");
   const int F = c->F;
   const size_t out_esz = elem_bytes(out_dtype);
@@ -699,14 +699,18 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
         d.block_size = 1 << 30;
         d.n_blocks = 1;
       }
+      if (j.block_table && (int64_t)j.n_blocks * j.block_size > (int64_t)INT32_MAX)
+        return fail(KVTC_E_UNSUPPORTED, "job: paged dst has 2^31 rows or more");
       if ((d.block_size & (d.block_size - 1)) == 0)
         for (int b = 0; b < 31; ++b)
           if ((1 << b) == d.block_size) d.bs_shift = b;
-      st_off[i] = st_total;
-      st_total += job_staging_bytes(s, d.tc);
-      if (st_total > 0 && (!d_staging || st_total > staging_bytes))
-        return fail(KVTC_E_CAPACITY, "staging buffer too small");
-      d.staging = d_staging + st_off[i];
+      if (mode != Mode::Decode) {   // the fused decode needs no staging
+        st_off[i] = st_total;
+        st_total += job_staging_bytes(s, d.tc);
+        if (st_total > 0 && (!d_staging || st_total > staging_bytes))
+          return fail(KVTC_E_CAPACITY, "staging buffer too small");
+        d.staging = d_staging + st_off[i];
+      }
       key[i] = (int)(align_up((size_t)s.r_eff, 16) / 16);
       if (s.record_bytes > 24 * key[i]) return fail(KVTC_E_UNSUPPORTED, "record wider than the decode tiles");
     }
@@ -733,9 +737,9 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
       JobDesc d = desc[order[p + b]];
       const Slot& s = c->slots[d.slot];
       const uint32_t ptiles = (d.s1 + d.w1 + kPassRows - 1) / kPassRows;
-      if (mode == Mode::Restore) {
+      if (mode == Mode::Restore || mode == Mode::Decode) {
         // units: feature slabs x blocks of kDecTok tokens
-        const int fs = gemm_features(key[order[p]]);
+        const int fs = rest_slab(rest_nfb(key[order[p]], F));
         d.n_ctiles = (uint32_t)((F + fs - 1) / fs) * ((d.tc + kDecTok - 1) / kDecTok);
       } else if (mode == Mode::Unpack) {
         d.n_ctiles = (d.tc + kDecTok - 1) / kDecTok;   // one wave per block
@@ -747,9 +751,11 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
       d.cblk_begin = cblks;
       if (mode == Mode::Unpack)   // header and passthrough units
         cblks += std::max<uint32_t>(1, (d.s1 + d.w1 + kPrepPassRows - 1) / kPrepPassRows);
+      else if (mode == Mode::Decode)
+        cblks += std::max<uint32_t>(1, (d.s1 + d.w1 + kRestPassRows - 1) / kRestPassRows);
       else if (s.r_eff > 0)
         cblks += (d.tc + kEncBlk - 1) / kEncBlk;
-      if (mode == Mode::Restore || mode == Mode::Unpack || mode == Mode::UnpackCodes)
+      if (mode == Mode::Restore || mode == Mode::Decode || mode == Mode::Unpack || mode == Mode::UnpackCodes)
         tiles += d.n_ctiles;
       else
         tiles += std::max<uint32_t>(1, d.n_ctiles + ptiles);
@@ -769,11 +775,15 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
       l = std::max(l, (size_t)kUnpackTile * rb_max + 16);
     else if (mode == Mode::Unpack) {
       // each wave's 32 record rows, plus 16 bytes for the 8-byte reads past a row
-      a.wave_lds = (uint32_t)align_up((size_t)kDecTok * dec_rec_stride((int)rb_max), 16);
+      a.wave_lds = (uint32_t)align_up(rec_rows_bytes((int)rb_max), 16);
       l = (size_t)kPrepRowsOff + (size_t)kPrepWaves * a.wave_lds + 16;
     }
-    else
-      l = gemm_lds_bytes(k);
+    else if (mode == Mode::Decode) {
+      a.wave_lds = (uint32_t)rest_rec_bytes((int)rb_max);
+      l = rest_lds_bytes(k, true, a.wave_lds);
+    } else {
+      l = rest_lds_bytes(k, false, 0);
+    }
     if (l > 160 * 1024) return fail(KVTC_E_UNSUPPORTED, "tile does not fit in LDS");
     batches.push_back(a);
     shape.push_back(k);
@@ -834,7 +844,7 @@ kvtc_status kvtc_decode_restore(kvtc_codec* c, const kvtc_job* jobs, int32_t n_j
   if (st != KVTC_OK) return st;
   for (size_t i = 0; i < b.size(); ++i) {
     if (b[i].total_tiles == 0) continue;
-    st = hip_status(launch_gemm(b[i], k[i], l[i], stream), "decode stage 2 launch");
+    st = hip_status(launch_restore(b[i], k[i], false, l[i], stream), "decode stage 2 launch");
     if (st != KVTC_OK) return st;
   }
   return KVTC_OK;
@@ -846,27 +856,17 @@ kvtc_status kvtc_decode(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, int
   const size_t need = kvtc_decode_workspace_bytes(c, jobs, n_jobs);
   if (need == 0) return fail(KVTC_E_INVALID, "job: bad layer or kind, or not calibrated");
   if (!d_ws || ws_bytes < need) return fail(KVTC_E_CAPACITY, "workspace below kvtc_decode_workspace_bytes");
-  uint8_t* stg = (uint8_t*)d_ws + kvtc_workspace_bytes(n_jobs);
-  const size_t stg_bytes = ws_bytes - kvtc_workspace_bytes(n_jobs);
-  // Both stages are planned over the same jobs, so their batches match; each
-  // batch's stage 2 follows its stage 1 at once, while its staging is in cache.
-  std::vector<LaunchArgs> bu, br;
-  std::vector<int> ku, kr;
-  std::vector<size_t> lu, lr;
-  kvtc_status st = plan(c, Mode::Unpack, jobs, n_jobs, out_dtype, d_ws, stg, stg_bytes, bu, ku, lu);
+  // One fused launch per batch: headers, passthrough rows, dequantization
+  // and the restore, with no staging buffer.
+  std::vector<LaunchArgs> b;
+  std::vector<int> k;
+  std::vector<size_t> l;
+  kvtc_status st = plan(c, Mode::Decode, jobs, n_jobs, out_dtype, d_ws, nullptr, 0, b, k, l);
   if (st != KVTC_OK) return st;
-  st = plan(c, Mode::Restore, jobs, n_jobs, out_dtype, d_ws, stg, stg_bytes, br, kr, lr);
-  if (st != KVTC_OK) return st;
-  if (bu.size() != br.size()) return fail(KVTC_E_INVALID, "internal: decode stages planned differently");
-  for (size_t i = 0; i < bu.size(); ++i) {
-    if (bu[i].total_tiles + bu[i].total_cblks > 0) {
-      st = hip_status(launch_prep(bu[i], ku[i], lu[i], stream), "decode stage 1 launch");
-      if (st != KVTC_OK) return st;
-    }
-    if (br[i].total_tiles > 0) {
-      st = hip_status(launch_gemm(br[i], kr[i], lr[i], stream), "decode stage 2 launch");
-      if (st != KVTC_OK) return st;
-    }
+  for (size_t i = 0; i < b.size(); ++i) {
+    if (b[i].total_tiles + b[i].total_cblks == 0) continue;   // every job has a header unit
+    st = hip_status(launch_restore(b[i], k[i], true, l[i], stream), "decode launch");
+    if (st != KVTC_OK) return st;
   }
   return KVTC_OK;
 }

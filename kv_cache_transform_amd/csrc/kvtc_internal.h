@@ -79,7 +79,8 @@ struct LaunchArgs {
   unsigned long long* status;  // per-launch slice of the workspace status words
   uint8_t* sink;           // kSinkBytes of workspace that absorb stores without a row
   uint32_t epoch;          // stamp of this launch (see status_word)
-  uint32_t wave_lds;       // decode stage 1: LDS bytes of each wave's record rows
+  uint32_t wave_lds;       // decode stage 1: LDS bytes of each wave's record rows;
+                           // fused decode: LDS bytes of each record buffer
 };
 
 // Workspace status words: (epoch << 32) | rank, combined with atomicMax so
@@ -99,7 +100,6 @@ constexpr int kUnpackTile = 256;
 constexpr int kPassRows = 16;
 constexpr int kEncKS = 64;                 // features per LDS basis slice (encode)
 constexpr int kEncRowPad = kEncKS + 8;     // bf16 elements per LDS basis row
-constexpr int kOutRow = 128 + 16;          // bytes per LDS output-staging row (decode)
 constexpr int kEncBlk = 32;                // encode tokens per wave (one block)
 constexpr int kEncWaves = kEncTile / kEncBlk;   // encode waves per tile
 
@@ -129,24 +129,44 @@ __host__ __device__ inline int padded_stride(int rb) {
 // lane order) and kDecTok f32 token scales: stg_block_bytes(ks) bytes. Its
 // header and passthrough units cover kPrepPassRows rows each; the waves'
 // record rows (stride dec_rec_stride(rb)) start at kPrepRowsOff of LDS.
-// Stage 2 works in units of one block of kDecTok tokens of one slab of
-// gemm_features(ks) features; the slab of V' (rows padded by 16 bytes), mu
-// and kGemmWaves waves' output staging rows take gemm_lds_bytes(ks) of LDS.
-// Its workgroups get at least kGemmMinUnits units each.
 constexpr int kDecTok = 32;
 constexpr int kPrepPassRows = 4;
 constexpr int kPrepWaves = 4;              // waves per stage-1 workgroup
 constexpr int kPrepRowsOff = 64;           // after the passthrough row list (kPrepPassRows longs)
 __host__ __device__ constexpr int dec_rec_stride(int rb) { return rb % 16 == 0 ? rb + 16 : rb; }
-constexpr uint32_t kGemmMinUnits = 16;
-constexpr int kGemmWaves = 8;              // waves sharing one slab of V'
-constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr size_t kSinkBytes = 256;         // workspace target of stores that have no row
 __host__ __device__ constexpr size_t stg_block_bytes(int ks) { return (size_t)ks * 1024 + kDecTok * 4; }
-__host__ __device__ constexpr int gemm_features(int ks) { return ks <= 8 ? 128 : 64; }
-__host__ __device__ constexpr size_t gemm_lds_bytes(int ks) {
-  return (size_t)gemm_features(ks) * (ks * 32 + 16) + (size_t)gemm_features(ks) * 4 +
-         (size_t)kGemmWaves * kDecTok * kOutRow;
+
+// Restore kernel (decode stage 2, and the whole decode when fused): units
+// of one block of kDecTok compressed tokens of one slab of rest_slab(nfb)
+// features of one job. kRestWaves waves, wave w owns 32 * nfb features of
+// the slab with their V' fragments in registers; nfb = 4 needs ks <= 6 (the
+// fragments and four accumulators then fit in 256 VGPRs) and F a multiple of
+// 1024 (one slab covers 1024 features), else nfb = 2.
+// LDS (bytes): the passthrough row list, the slab's mu (fp32), the waves'
+// output staging rows (kRestStgRow each), two fragment buffers
+// (rest_frag_bytes: the B fragments and token scales of a block, then its 32
+// output rows as int32), and for the fused decode two record buffers of
+// rec_lds bytes (32 record rows of stride dec_rec_stride(rb), 16 bytes of
+// padding for 8-byte reads, then 32 int32 output rows).
+constexpr int kRestWaves = 8;
+constexpr int kRestThreads = 64 * kRestWaves;
+constexpr int kRestPassRows = 8;
+constexpr int kRestStgRow = 256 + 16;
+__host__ __device__ constexpr int rest_nfb(int ks, int F) { return ks <= 6 && F % 1024 == 0 ? 4 : 2; }
+__host__ __device__ constexpr int rest_slab(int nfb) { return kRestWaves * 32 * nfb; }
+__host__ __device__ constexpr size_t rest_frag_bytes(int ks) { return stg_block_bytes(ks) + kDecTok * 4; }
+// A batch's jobs share ks but not record_bytes; dec_rec_stride(rb) <= rb + 16
+// <= rb_max + 16 bounds every job's row stride.
+__host__ __device__ constexpr size_t rec_rows_bytes(int rb_max) { return (size_t)kDecTok * (rb_max + 16); }
+__host__ __device__ constexpr size_t rest_rec_bytes(int rb_max) {
+  return (rec_rows_bytes(rb_max) + 16 + 15) / 16 * 16 + kDecTok * 4;
+}
+constexpr size_t kRestMuOff = 64;
+constexpr size_t kRestStgOff = kRestMuOff + 4 * 1024;
+constexpr size_t kRestFragOff = kRestStgOff + (size_t)kRestWaves * kDecTok * kRestStgRow;
+__host__ __device__ constexpr size_t rest_lds_bytes(int ks, bool fused, size_t rec_lds) {
+  return kRestFragOff + 2 * rest_frag_bytes(ks) + (fused ? 2 * rec_lds : 0);
 }
 
 // Host-side launchers implemented in kvtc_encode.hip and kvtc_decode.hip (G = group size, lds =
@@ -155,7 +175,7 @@ __host__ __device__ constexpr size_t gemm_lds_bytes(int ks) {
 // return a hipError_t value cast to int.
 int launch_encode(const LaunchArgs& a, int nb, int G, size_t lds, hipStream_t s);
 int launch_prep(const LaunchArgs& a, int ks, size_t lds, hipStream_t s);
-int launch_gemm(const LaunchArgs& a, int ks, size_t lds, hipStream_t s);
+int launch_restore(const LaunchArgs& a, int ks, bool fused, size_t lds, hipStream_t s);
 int launch_unpack(const LaunchArgs& a, int G, size_t lds, void* codes, void* ss, hipStream_t s);
 int launch_pack(const LaunchArgs& a, int G, size_t lds, const void* codes, const void* ss,
                 hipStream_t s);

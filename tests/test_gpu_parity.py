@@ -364,6 +364,36 @@ def _grid_tokens(widths, G, T, rng):
     return x
 
 
+def test_mixed_record_sizes_in_one_launch():
+    """Two slots with the same K-step count (six 16-component groups) but
+    record sizes 128 bytes (a multiple of 16: LDS rows padded to 144) and
+    142 bytes decoded in one launch, through both decode routes: every job's
+    record rows must fit the batch's LDS rows."""
+    F, G, T = 1024, 16, 901
+    rng = np.random.default_rng(21)
+    V = np.linalg.qr(rng.standard_normal((F, F)))[0]
+    slots = {}
+    for kind, wd6 in ((0, [8, 8, 8, 8, 4, 4]), (1, [8, 8, 8, 8, 8, 7])):
+        wd = np.zeros(F // G, np.uint8)
+        wd[:6] = wd6
+        slots[(0, kind)] = O.Slot(0, kind, F, G, wd, rng.standard_normal(F).astype(np.float32),
+                                  np.zeros(F), V[:, :96].astype(np.float32))
+    assert [sl.record_bytes for sl in slots.values()] == [128, 142]
+    p = O.Params(1, 1, F, 4, 16, G, 8, 16.0, O.DTYPE_BF16)
+    dc = DevCodec(O.Artifact(p, slots).serialize())
+    items = []
+    for rep in range(3):
+        for kind in (0, 1):
+            x = (rng.standard_normal((T, F)) * 2).astype(np.float32)
+            ref = O.encode(O.f32_to_bf16_bits(x), p, slots[(0, kind)], 0, kind)
+            items.append((kind, ref))
+    for two in (False, True):
+        outs, st = dc.decode([(0, kind, T, ref.stream) for kind, ref in items], K.KVTC_F32, F, two_stage=two)
+        assert np.all(st == 0), st
+        for (kind, ref), out in zip(items, outs):
+            _decode_check(None, p, slots[(0, kind)], ref.stream, T, out, K.KVTC_F32, 0, kind)
+
+
 @pytest.mark.parametrize("dtype", [O.DTYPE_BF16, O.DTYPE_F32])
 @pytest.mark.parametrize("case", list(IDENTITY_CASES))
 def test_identity_basis_is_exact(case, dtype):
