@@ -124,10 +124,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
     const uint32_t P = a.total_cblks;
     const uint32_t p_end = (uint32_t)((uint64_t)P * (g + 1) / ng);
     for (uint32_t p = (uint32_t)((uint64_t)P * g / ng); p < p_end; ++p) {
-      int j = 0;
-      for (int i = 1; i < a.n_jobs; ++i)
-        if (a.jobs[i].cblk_begin <= p) j = i;
-      const JobDesc& jd = a.jobs[j];
+      const JobDesc& jd = a.jobs[job_at<&JobDesc::cblk_begin>(a, p)];
       CSlot& sl = slot_of(a, jd.slot);
       const uint32_t lp = p - jd.cblk_begin;
       const int st = check_header(a, jd, sl);   // uniform
@@ -261,8 +258,7 @@ __device__ __forceinline__ RUnit rest_unit_at(const LaunchArgs& a, uint32_t u, u
     r.slab = r.c = r.nrec = r.n_ch = 0;
     return r;
   }
-  int j = 0;
-  while (j + 1 < a.n_jobs && a.jobs[j + 1].tile_begin <= u) ++j;
+  const int j = job_at<&JobDesc::tile_begin>(a, u);
   const JobDesc& jd = a.jobs[j];
   r.j = j;
   r.n_ch = (jd.tc + kDecTok - 1) / kDecTok;
@@ -322,16 +318,19 @@ __device__ __forceinline__ uint32_t rest_row_limit(const JobDesc& jd) {
 
 // Epilogue of one round of FBR feature blocks (32 features each, starting at
 // block fb0) into the wave's staging rows and out to memory: RB = FBR * 32 *
-// OSZ bytes per row. fill() runs between the round's stores (once, after the
-// first half of them). Returns whether a bad block table entry was met.
+// OSZ bytes per row. fill() runs once between the round's stores: after a
+// quarter of them in an early wave, after three quarters in a late one.
+// Returns whether a bad block table entry was met.
 template <int OSZ, int FBR, int NFB, class Fill>
 __device__ __forceinline__ bool rest_epilogue(const f32x16 (&acc)[NFB], int fb0, float S, const float* mu_w,
                                               uint8_t* stg, const int* rows, uint8_t* dst_w, uint8_t* sink,
-                                              bool store_ok, int F, uint32_t row_lim, Fill&& fill) {
+                                              bool store_ok, int F, uint32_t row_lim, bool early, Fill&& fill) {
   constexpr int RB = FBR * 32 * OSZ;          // bytes per row piece (128 or 256)
   constexpr int LPR = RB / 16;                // lanes per row piece
   constexpr int RPI = 64 / LPR;               // rows per store instruction
   constexpr int NST = kDecTok / RPI;          // store instructions
+  constexpr int K1 = NST / 4 - 1, K2 = 3 * NST / 4 - 1;
+  static_assert(K1 >= 0 && K1 < K2, "a round has at least four stores");
   const int lane = threadIdx.x & 63, t = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int f = 0; f < FBR; ++f) {
@@ -363,10 +362,12 @@ __device__ __forceinline__ bool rest_epilogue(const f32x16 (&acc)[NFB], int fb0,
                                                                  : sink + (lane & 15) * 16;
     // streaming (non-temporal) stores: the output is not read back here
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), (u32x4*)p);
-    if (k == NST / 2 - 1) {
-      __builtin_amdgcn_sched_barrier(0);
-      fill();
-      __builtin_amdgcn_sched_barrier(0);
+    if (k == K1 || k == K2) {
+      if (early == (k == K1)) {   // uniform
+        __builtin_amdgcn_sched_barrier(0);
+        fill();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   wave_lds_sync();
@@ -387,6 +388,9 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
   constexpr int NVS = FUSED ? 0 : (KS > 0 ? ((int)stg_block_bytes(KS) / 16 + kRestThreads - 1) / kRestThreads : 0);
   constexpr int NXV = NVR > NVS ? NVR : (NVS > 0 ? NVS : 1);
   constexpr int NMU = (SLAB + kRestThreads - 1) / kRestThreads;   // mu values per thread
+  // stores per unit and wave: rounds of row pieces of 256 (or 128) bytes,
+  // 1 KB per store instruction
+  constexpr int NSTORES = OUT32 ? 8 * (NFB / 2) : (NFB == 4 ? 8 : 4);
   const int F = a.F;
   const int tid = threadIdx.x;
   const int lane = tid & 63, t = lane & 31, h = lane >> 5;
@@ -562,13 +566,15 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
       f_w = f0 + wave * FPW;
       active = f_w < F;
       if (active) {
+        // one coalesced 1 KB load per operand (the state stores V' in
+        // operand order)
         const uint8_t* vdec = a.state + sl.vdec_off;
-        const int r_dec = sl.r_dec;
+        const int nks = sl.r_dec >> 4;
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
           for (int s = 0; s < KS; ++s)
-            A[fb][s] = *(const uint4*)(vdec + ((size_t)(f_w + 32 * fb + t) * r_dec + 16 * s + 8 * h) * 2);
+            A[fb][s] = *(const uint4*)(vdec + (((size_t)((f_w >> 5) + fb) * nks + s) * 64 + lane) * 16);
       }
       job_ok = FUSED ? check_header(a, jd, sl) == KVTC_OK : prior_rank(a, jd.status_idx) == 0;
     };
@@ -578,6 +584,9 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
         const int li = tid + kRestThreads * i;
         if (li < SLAB) mu_s[li] = seg_slab * SLAB + li < (uint32_t)F ? mreg[i] : 0.f;
       }
+      // the segment's loads (the V' fragments too) complete here, on every
+      // path: no register enters the unit loop awaiting a load
+      wait_vmcnt<0>();
     };
 
     // ---- compute one unit from its fragment buffer and store it; fill()
@@ -604,16 +613,21 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
       uint8_t* dst_w = (uint8_t*)jd.dst + (size_t)f_w * OSZ;
       const bool store_ok = job_ok && active;
       const uint32_t row_lim = rest_row_limit(jd);
+      // the waves that fill in early are one per SIMD (waves go to the SIMDs
+      // round robin), so every SIMD keeps a wave issuing stores
+      const bool early = wave < 4;
       // (the output type is a template parameter: with a run-time branch the
       // compiler could not count the stores on every path and would drain
       // them before the next wait for a load)
       if (OUT32) {
-        bad_seen |= rest_epilogue<4, 2, NFB>(acc, 0, S, mu_w, stg, rows, dst_w, a.sink, store_ok, F, row_lim, fill);
+        bad_seen |=
+            rest_epilogue<4, 2, NFB>(acc, 0, S, mu_w, stg, rows, dst_w, a.sink, store_ok, F, row_lim, early, fill);
         if (NFB > 2)
           bad_seen |= rest_epilogue<4, 2, NFB>(acc, 2, S, mu_w, stg, rows, dst_w, a.sink, store_ok, F, row_lim,
-                                               [] {});
+                                               early, [] {});
       } else {
-        bad_seen |= rest_epilogue<2, NFB, NFB>(acc, 0, S, mu_w, stg, rows, dst_w, a.sink, store_ok, F, row_lim, fill);
+        bad_seen |=
+            rest_epilogue<2, NFB, NFB>(acc, 0, S, mu_w, stg, rows, dst_w, a.sink, store_ok, F, row_lim, early, fill);
       }
     };
 
@@ -641,6 +655,10 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
       build(cur, recb(u_lo), fragb(u_lo));
       __syncthreads();
     }
+    // Every load of the prologue has completed, also in lanes that had no use
+    // for theirs: the loop starts with no register awaiting a load, so the
+    // compiler needs no wait for the loop's stores before reusing registers.
+    wait_vmcnt<0>();
 
     for (uint32_t u = u_lo; u < u_hi; ++u) {
       if (cur.j != seg_j || cur.slab != seg_slab) {   // uniform: a new segment
@@ -665,6 +683,9 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
         });
         __builtin_amdgcn_sched_barrier(0);
         commit(fu, sq, xv, ent, in, recb(u), (int*)(recb(u) + rec_rows_off));
+        // the loads of this iteration have completed (only its stores may be
+        // outstanding), on every path through commit
+        wait_vmcnt<NSTORES>();
         __syncthreads();
         cur = nx;
         nx = nx2;
@@ -676,6 +697,7 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
         compute(cur, fragb(u), [] {});
         __builtin_amdgcn_sched_barrier(0);
         commit(fu, sq, xv, ent, in, fragb(u + 1), (int*)(fragb(u + 1) + stg_block_bytes(KS)));
+        wait_vmcnt<NSTORES>();
         __syncthreads();
         cur = nx;
         nx = rest_next(a, nx, n_slabs);
@@ -692,10 +714,11 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
     // the header themselves.)
     const uint32_t P = a.total_cblks;
     const uint32_t p_end = (uint32_t)((uint64_t)P * (g + 1) / ng);
-    int j = 0;
+    const uint32_t p_lo = (uint32_t)((uint64_t)P * g / ng);
+    int j = p_lo < p_end ? job_at<&JobDesc::cblk_begin>(a, p_lo) : 0;
     __syncthreads();   // the passthrough row list reuses LDS
-    for (uint32_t p = (uint32_t)((uint64_t)P * g / ng); p < p_end; ++p) {
-      while (j + 1 < a.n_jobs && a.jobs[j + 1].cblk_begin <= p) ++j;
+    for (uint32_t p = p_lo; p < p_end; ++p) {
+      while (j + 1 < a.n_jobs && a.jobs[j + 1].cblk_begin <= p) ++j;   // usually no step
       const JobDesc& jd = a.jobs[j];
       const uint32_t lp = p - jd.cblk_begin;
       const int st = check_header(a, jd, slot_of(a, jd.slot));   // uniform

@@ -33,11 +33,22 @@ __device__ __forceinline__ uint32_t logical_tile() {
   return (blockIdx.x & 7u) * n8 + (blockIdx.x >> 3);
 }
 
+// The last job whose first unit (JobDesc::tile_begin, or ::cblk_begin) is
+// <= x: a binary search over the non-decreasing firsts, a chain of at most
+// log2(kMaxLaunchJobs) + 1 uniform loads. A job with no units shares its first
+// unit with the next job, so the search lands on the job that owns unit x.
+template <uint32_t JobDesc::*M>
+__device__ __forceinline__ int job_at(const LaunchArgs& a, uint32_t x) {
+  int lo = 0, hi = a.n_jobs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.jobs[mid].*M <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
 __device__ __forceinline__ int find_job(const LaunchArgs& a, uint32_t tile) {
-  int j = 0;
-  for (int i = 1; i < a.n_jobs; ++i)
-    if (a.jobs[i].tile_begin <= tile) j = i;
-  return j;
+  return job_at<&JobDesc::tile_begin>(a, tile);
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
@@ -365,6 +376,16 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Wait until at most N vector memory operations of this wave are
+// outstanding (s_waitcnt vmcnt(N); the other counters untouched). Memory
+// operations complete in issue order for this count, so after it every one
+// issued before the last N has completed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // ------------------------------------------------------ launch helpers ---

@@ -25,10 +25,7 @@ namespace kvtc {
 // Compressed rows carry their own index space of kEncBlk-token blocks
 // (JobDesc::cblk_begin): the blocks of every job with records, job after job.
 __device__ __forceinline__ int find_cblk_job(const LaunchArgs& a, uint32_t b) {
-  int j = 0;
-  for (int i = 1; i < a.n_jobs; ++i)
-    if (a.jobs[i].cblk_begin <= b) j = i;
-  return j;
+  return job_at<&JobDesc::cblk_begin>(a, b);
 }
 // The job of block b >= the first block of job j: j moved forward (a
 // workgroup's blocks are contiguous, so this is usually zero or one step).

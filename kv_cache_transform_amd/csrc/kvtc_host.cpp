@@ -550,10 +550,20 @@ kvtc_status kvtc_upload(kvtc_codec* c, void* d_state, size_t bytes, hipStream_t 
       for (int f = 0; f < F; ++f) venc[(size_t)j * F + f] = f32_to_bf16(s.V32[(size_t)f * r + j]);
     off += align_up(2 * (size_t)r_enc * F, kAlign);
     d.vdec_off = off;
-    uint16_t* vdec = (uint16_t*)(h.data() + off);  // V' [F][r_dec] fp16
+    // V' (F x r_dec, fp16, zero past r_eff) in the order the decode loads
+    // its MFMA A operands: for feature block b (32 features) and K step k (16
+    // components), 64 lanes x 8 values, lane 32 h + t holding
+    // V'[32 b + t][16 k + 8 h + i], i = 0..7; one wave's operand is 1 KB of
+    // contiguous memory.
+    uint16_t* vdec = (uint16_t*)(h.data() + off);
+    const int nks = r_dec / 16;
     for (int f = 0; f < F; ++f)
-      for (int j = 0; j < r; ++j)
-        vdec[(size_t)f * r_dec + j] = f32_to_f16(bf16_to_f32(f32_to_bf16(s.V32[(size_t)f * r + j])));
+      for (int j = 0; j < r; ++j) {
+        const size_t lane = 32 * (size_t)((j % 16) / 8) + (size_t)(f % 32);
+        const size_t frag = (size_t)(f / 32) * nks + (size_t)(j / 16);
+        vdec[(frag * 64 + lane) * 8 + (size_t)(j % 8)] =
+            f32_to_f16(bf16_to_f32(f32_to_bf16(s.V32[(size_t)f * r + j])));
+      }
     off += align_up(2 * (size_t)F * r_dec, kAlign);
     // Centring (section 2B subtracts the mean before the transform). The
     // encode subtracts mu_hi = bf16_rne(mu32) from each token in fp32 (exact

@@ -27,7 +27,7 @@ __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a -
 struct alignas(16) DevSlot {
   uint64_t mu_off;        // f32 mu32[F]
   uint64_t venc_off;      // bf16 V'^T [r_enc][F]   (rows >= r_eff are zero)
-  uint64_t vdec_off;      // f16  V'   [F][r_dec]   (cols >= r_eff are zero)
+  uint64_t vdec_off;      // f16  V'   F x r_dec in MFMA A-operand order (cols >= r_eff are zero)
   uint64_t mhi_off;       // f32  mu_hi[F] = bf16_rne(mu32), the encode's centring vector
   uint64_t cmu_off;       // f32  V'^T (mu32 - mu_hi) [r_enc]  (rows >= r_eff are zero)
   uint64_t slot_id;
