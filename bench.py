@@ -8,12 +8,14 @@ channels per head), calibrated on 16384 synthetic tokens per tensor by the
 library on the host.
 
 One step = kvtc_encode of every tensor followed by kvtc_decode of every
-stream back to bf16 (one launch per 32 tensors per kernel; kvtc_decode is a
-single fused kernel), with inputs, streams and outputs resident in HBM; HIP
-events on the launch stream time the encode and the decode inside the timed
-region. value = bf16 KV bytes per step / step time. After the timed steps,
-the two-stage decode (kvtc_decode_unpack, kvtc_decode_restore, the calls a
-layer-by-layer pipeline uses) is timed per stage with an event between them.
+stream back to bf16 (one launch per 32 tensors per kernel), with inputs,
+streams and outputs resident in HBM; kvtc_decode gets its full workspace and
+so runs the two-stage schedule (stage 1 unpacks records into MFMA operands in
+a staging buffer, stage 2 restores). HIP events on the launch stream time the
+encode and the decode inside the timed region. value = bf16 KV bytes per
+step / step time. After the timed steps the same two stages are timed with
+an event between them (the per-kernel breakdown), and kvtc_decode with only
+the status words (the single-launch fused schedule) is timed on its own.
 For a paged workload (qwen25_7b_paged) the decode is the layer-by-layer
 two-stream pipeline: stage 1 (unpack) of layer l+1 runs on one stream while
 stage 2 (restore into the paged cache) of layer l runs on another. The
@@ -50,6 +52,9 @@ def main():
     ap.add_argument("--workload", default="llama31_8b")
     ap.add_argument("--cpu-sample", type=int, default=16, help="most tensors in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-schedule", choices=("staged", "fused"), default="staged",
+                    help="kvtc_decode's workspace in the timed step: with the staging (the "
+                         "two-stage schedule) or only the status words (the fused schedule)")
     ap.add_argument("--calib-tokens", type=int, default=0, help="override (0 = workload's)")
     ap.add_argument("--distinct-requests", type=int, default=2,
                     help="distinct synthetic requests per (layer, kind); the rest are copies")
@@ -157,17 +162,25 @@ def main():
 
     pipe = Pipeline(K, codec, w, jobs, dec_jobs, dev) if w.paged else None
 
+    # kvtc_decode's full workspace (status words, sink, staging) selects the
+    # two-stage schedule; the status words alone, the fused one
     n_dws = codec.decode_workspace_bytes(dec_jobs)
+    n_ws0 = K.kvtc_workspace_bytes(n_jobs)
     dws = torch.zeros((n_dws + 3) // 4, dtype=torch.int32, device=dev)
-    # staging of the two-stage decode (timed after the steps, per kernel)
+    # staging for the explicit stage calls of the per-kernel breakdown
     n_stg = codec.staging_bytes(dec_jobs)
     stg = torch.empty(max(n_stg, 256), dtype=torch.uint8, device=dev)
+
+    n_step_ws = n_dws if args.decode_schedule == "staged" else n_ws0
 
     def decode():
         if pipe is not None:
             pipe.run(stream)
         else:
-            codec.decode(dec_jobs, K.KVTC_BF16, dws, n_dws, stream)
+            codec.decode(dec_jobs, K.KVTC_BF16, dws, n_step_ws, stream)
+
+    def decode_fused():
+        codec.decode(dec_jobs, K.KVTC_BF16, dws, n_ws0, stream)
 
     def decode_staged(mid):
         codec.decode_unpack(dec_jobs, K.KVTC_BF16, stg, n_stg, dws, stream)
@@ -226,6 +239,15 @@ def main():
         torch.cuda.synchronize()
         prep_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
         gemm_ms = np.array([b.elapsed_time(c) for _, b, c in evs])
+        evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for f0, f1 in evf:
+            f0.record(stream)
+            decode_fused()
+            f1.record(stream)
+        torch.cuda.synchronize()
+        fused_ms = np.array([a.elapsed_time(b) for a, b in evf])
+        if np.any(K.kvtc_read_device_status(dws, n_jobs, stream) != 0):
+            raise SystemExit("device status errors in the fused decode")
 
     kv_bytes = n_jobs * T * F * esz
     r_eff = {s: infos[s].r_eff for s in slots}
@@ -251,17 +273,23 @@ def main():
                                             for l, k, _ in jobs)
     med = lambda v: float(np.median(v)) * 1e-3
     STAGE1, STAGE2 = "prep_kernel (decode stage 1)", "restore_kernel (decode stage 2)"
+    FUSED = "restore_kernel (fused decode)"
     if pipe is None:
+        # the step's kernels: encode and the decode's two stages (timed per
+        # stage after the steps); the fused schedule is reported beside them
         kern = {"encode_kernel": (enc_alg, med(enc_ms)),
-                "restore_kernel (fused decode)": (dec_alg, med(dec_ms))}
-        breakdown = {STAGE1: (prep_alg, med(prep_ms)), STAGE2: (gemm_alg, med(gemm_ms))}
+                STAGE1: (prep_alg, med(prep_ms)), STAGE2: (gemm_alg, med(gemm_ms))}
+        extra = {FUSED: (dec_alg, med(fused_ms))}
+        timed_in = {STAGE1: "two-stage decode loop after the timed steps",
+                    STAGE2: "two-stage decode loop after the timed steps",
+                    FUSED: "fused-schedule decode loop after the timed steps"}
     else:   # two streams: stage times overlap; report the pipeline as one
         kern = {"encode_kernel": (enc_alg, med(enc_ms)),
                 "prep_kernel + restore_kernel (two streams)": (dec_alg, med(dec_ms))}
-        breakdown = {}
-    # the dominant kernel of the timed step; the two-stage breakdown is extra
+        extra, timed_in = {}, {}
+    # the dominant kernel of the timed step (longest per launch)
     dominant = max(kern, key=lambda k: kern[k][1])
-    kern.update(breakdown)
+    kern.update(extra)
     enc_t, dec_t = med(enc_ms), med(dec_ms)
 
     def roof(name):
@@ -271,8 +299,8 @@ def main():
         r = {"kernel": name, "achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBPS, 4),
              "alg_bytes_per_launch": int(alg / n_launch), "us_per_launch": round(per_launch_t * 1e6, 2),
              "launches_per_call": n_launch}
-        if name in breakdown:
-            r["timed_in"] = "two-stage decode loop after the timed steps"
+        if name in timed_in:
+            r["timed_in"] = timed_in[name]
         return r
 
     flops = sum(2 * F * r_eff[(l, k)] * tc for l, k, _ in jobs)
@@ -307,7 +335,8 @@ def main():
         "decode_GBps": round(kv_bytes / dec_t / 1e9, 2),
         "encode_ms": round(enc_t * 1e3, 4),
         "decode_ms": round(dec_t * 1e3, 4),
-        "decode_path": {"achieved": round(dec_alg / dec_t / 1e9, 1),
+        "decode_path": {"schedule": "two-stage pipeline" if pipe is not None else "two-stage",
+                        "achieved": round(dec_alg / dec_t / 1e9, 1),
                         "frac": round(dec_alg / dec_t / 1e9 / HBM_PEAK_GBPS, 4)},
         "roofline": dict(bound="hbm", peak=HBM_PEAK_GBPS, unit="GB/s", traffic=traffic, **roof(dominant)),
         "roofline_other": [roof(k) for k in kern if k != dominant],

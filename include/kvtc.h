@@ -201,15 +201,20 @@ size_t kvtc_workspace_bytes(int32_t max_jobs);
 kvtc_status kvtc_encode(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
                         void* d_ws, hipStream_t stream);
 
-/* Decode n_jobs streams (section 2C), writing out_dtype rows: stage 1 and
- * stage 2 below on `stream`, stage 2 of each launch batch (at most 32 jobs
- * of one K-step count) right after its stage 1, with the staging buffer
- * inside d_ws. d_ws must hold ws_bytes >= kvtc_decode_workspace_bytes(jobs)
- * (kvtc_workspace_bytes(n_jobs) followed by kvtc_staging_bytes(jobs); 0 if a
- * job names an unknown or uncalibrated (layer, kind)); KVTC_E_CAPACITY
- * otherwise. Passthrough rows are copied bit for bit when
- * out_dtype equals the codec dtype (converted with round-to-nearest-even
- * otherwise). */
+/* Decode n_jobs streams (section 2C), writing out_dtype rows, in one of two
+ * schedules that produce identical results, chosen by the workspace given:
+ *  - ws_bytes >= kvtc_decode_workspace_bytes(jobs) (kvtc_workspace_bytes
+ *    (n_jobs) followed by kvtc_staging_bytes(jobs)): the two-stage schedule
+ *    below (kvtc_decode_unpack, then kvtc_decode_restore) with the staging
+ *    inside d_ws; measured faster, at the cost of the staging memory;
+ *  - kvtc_workspace_bytes(n_jobs) <= ws_bytes < that: the fused schedule, one
+ *    launch per batch (at most 32 jobs of one K-step count) that dequantizes
+ *    each block of 32 records into MFMA operands in LDS and restores it, with
+ *    no staging.
+ * kvtc_decode_workspace_bytes is 0 if a job names an unknown or uncalibrated
+ * (layer, kind); a smaller workspace gives KVTC_E_CAPACITY. Passthrough rows
+ * are copied bit for bit when out_dtype equals the codec dtype (converted
+ * with round-to-nearest-even otherwise). */
 size_t kvtc_decode_workspace_bytes(const kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs);
 kvtc_status kvtc_decode(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
                         int32_t out_dtype, void* d_ws, size_t ws_bytes, hipStream_t stream);

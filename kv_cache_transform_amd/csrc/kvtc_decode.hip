@@ -13,7 +13,7 @@
 // irrelevant), into a staging buffer. Stage 2 (512 threads, persistent):
 // D[feature][token] = sum_j V'[feature][j] * c_hat[token][j] on
 // v_mfma_f32_32x32x16_f16 per 128-feature slab (V' in LDS), written as
-// S_t * D + mu through LDS rows in 128-byte streaming stores.
+// S_t * D + mu through LDS rows in coalesced row-piece stores.
 #include "kvtc_device.h"
 
 namespace kvtc {
@@ -222,23 +222,27 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
 // dequantized once.
 //
 // Per unit u the workgroup runs one barrier-separated step of a pipeline
-// over LDS buffers indexed by unit parity:
+// over LDS buffers (three fragment buffers in rotation, two record buffers
+// by unit parity):
 //   FUSED: the records of unit u + 2 are loaded into registers (16-byte
-//     loads), every wave computes unit u from frag[u % 2] and, half-way
-//     through its stores, waves 0 .. KS - 1 build the B fragments and token
-//     scales of unit u + 1 (one K step each) from rec[(u + 1) % 2] into
-//     frag[(u + 1) % 2] while the stores drain; the loaded records then go
-//     to rec[u % 2];
-//   not FUSED: the staging block of unit u + 1 is loaded, unit u computed
-//     from frag[u % 2], and the loaded block goes to frag[(u + 1) % 2].
+//     loads); unit u - 1, whose product is still in the accumulators, is
+//     staged and stored while unit u's MFMAs run between its stores, and
+//     waves 0 .. KS - 1 build the B fragments and token scales of unit u + 1
+//     (one K step each) from its records between the stores too; the loaded
+//     records then go to the record buffer unit u + 1 does not use;
+//   not FUSED: the staging block of unit u + 1 is loaded into the next
+//     fragment buffer, with the same stores and MFMAs.
+// Deferring each unit's stores to the next step keeps every wave issuing
+// stores from the start of a step, with this step's other work between them,
+// instead of computing first and storing last.
 // Compute: B fragments from LDS, NFB x KS MFMAs D[feature][token]
 // (v_mfma_f32_32x32x16_f16, K-step-outer so consecutive MFMAs go to
 // different accumulators), S_t * D + mu through the wave's LDS staging rows,
-// then coalesced streaming 16-byte stores of 256-byte row pieces. Every wave
+// then coalesced 16-byte stores of 256-byte row pieces. Every wave
 // issues the same loads and stores for every unit (addresses are clamped to
 // valid ones, rows without a destination go to the workspace sink), so the
-// wait for the next unit's loads, issued before this unit's stores, never
-// covers those stores.
+// wait for the next unit's loads, issued before these stores, never covers
+// them.
 
 struct RUnit {
   int j;              // job, -1 past the workgroup's range
@@ -316,63 +320,103 @@ __device__ __forceinline__ uint32_t rest_row_limit(const JobDesc& jd) {
   return jd.n_blocks == 1 && jd.block_size == (1 << 30) ? jd.T : (uint32_t)jd.n_blocks * (uint32_t)jd.block_size;
 }
 
-// Epilogue of one round of FBR feature blocks (32 features each, starting at
-// block fb0) into the wave's staging rows and out to memory: RB = FBR * 32 *
-// OSZ bytes per row. fill() runs once between the round's stores: after a
-// quarter of them in an early wave, after three quarters in a late one.
-// Returns whether a bad block table entry was met.
-template <int OSZ, int FBR, int NFB, class Fill>
-__device__ __forceinline__ bool rest_epilogue(const f32x16 (&acc)[NFB], int fb0, float S, const float* mu_w,
-                                              uint8_t* stg, const int* rows, uint8_t* dst_w, uint8_t* sink,
-                                              bool store_ok, int F, uint32_t row_lim, bool early, Fill&& fill) {
-  constexpr int RB = FBR * 32 * OSZ;          // bytes per row piece (128 or 256)
-  constexpr int LPR = RB / 16;                // lanes per row piece
-  constexpr int RPI = 64 / LPR;               // rows per store instruction
-  constexpr int NST = kDecTok / RPI;          // store instructions
-  constexpr int K1 = NST / 4 - 1, K2 = 3 * NST / 4 - 1;
-  static_assert(K1 >= 0 && K1 < K2, "a round has at least four stores");
+// Epilogue staging of one round of FBR feature blocks (32 features each,
+// starting at block fb0): S_t * D + mu into the wave's staging rows, RB =
+// FBR * 32 * OSZ bytes per row, as 16-byte chunks: logical chunk q of row t
+// at chunk q ^ (t & 7). Every lane writes whole chunks (ds_write_b128), and
+// the swizzle sends the 8 lanes an LDS cycle serves (8 rows, one logical
+// chunk) to 8 different bank groups; the stores read each row's chunks back
+// in 16-lane groups, which the swizzle only permutes.
+// MFMA D[feature][token] leaves lane (t, h) with features 8 qd + 4 h + 0..3
+// of token t per qd. For f32 output that is one chunk. For bf16 the lane
+// halves trade packed values (v_permlane32_swap) so that lane (t, 0) holds
+// features 16 p + 0..7 and lane (t, 1) features 16 p + 8..15 of qd pair p.
+template <int OSZ, int FBR, int NFB>
+__device__ __forceinline__ void rest_stage(const f32x16 (&acc)[NFB], int fb0, float S, const float* mu_w,
+                                           uint8_t* stg) {
+  constexpr int RB = FBR * 32 * OSZ;
   const int lane = threadIdx.x & 63, t = lane & 31, h = lane >> 5;
+  uint8_t* row = stg + t * RB;
+  const int sw = t & 7;
 #pragma unroll
   for (int f = 0; f < FBR; ++f) {
-    // D[feature][token]: token t, features 8 qd + 4 h + {0..3} of block fb0 + f
+    const f32x16& a = acc[fb0 + f];
+    const float* mu_f = mu_w + 32 * (fb0 + f);
+    if (OSZ == 4) {
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const int fl = 32 * f + 8 * qd + 4 * h;
-      const float4 m4 = *(const float4*)(mu_w + 32 * fb0 + fl);
-      const float o0 = __builtin_fmaf(acc[fb0 + f][4 * qd + 0], S, m4.x);
-      const float o1 = __builtin_fmaf(acc[fb0 + f][4 * qd + 1], S, m4.y);
-      const float o2 = __builtin_fmaf(acc[fb0 + f][4 * qd + 2], S, m4.z);
-      const float o3 = __builtin_fmaf(acc[fb0 + f][4 * qd + 3], S, m4.w);
-      if (OSZ == 4)
-        *(float4*)(stg + t * kRestStgRow + fl * 4) = make_float4(o0, o1, o2, o3);
-      else
-        *(uint2*)(stg + t * kRestStgRow + fl * 2) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-    }
-  }
-  wave_lds_sync();
-  bool bad = false;
-  const int col = (lane % LPR) * 16;
+      for (int qd = 0; qd < 4; ++qd) {
+        const float4 m4 = *(const float4*)(mu_f + 8 * qd + 4 * h);
+        const float4 o = make_float4(__builtin_fmaf(a[4 * qd + 0], S, m4.x), __builtin_fmaf(a[4 * qd + 1], S, m4.y),
+                                     __builtin_fmaf(a[4 * qd + 2], S, m4.z), __builtin_fmaf(a[4 * qd + 3], S, m4.w));
+        const int q = 8 * f + 2 * qd + h;
+        *(float4*)(row + (q ^ sw) * 16) = o;
+      }
+    } else {
 #pragma unroll
-  for (int k = 0; k < NST; ++k) {
-    const int r = k * RPI + lane / LPR;
-    const uint4 v = *(const uint4*)(stg + r * kRestStgRow + col);
-    const int row = rows[r];
-    bad |= row == -2;
-    uint8_t* p = store_ok && row >= 0 && (uint32_t)row < row_lim ? dst_w + ((size_t)row * F + 32 * fb0) * OSZ + col
-                                                                 : sink + (lane & 15) * 16;
-    // streaming (non-temporal) stores: the output is not read back here
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), (u32x4*)p);
-    if (k == K1 || k == K2) {
-      if (early == (k == K1)) {   // uniform
-        __builtin_amdgcn_sched_barrier(0);
-        fill();
-        __builtin_amdgcn_sched_barrier(0);
+      for (int p = 0; p < 2; ++p) {
+        // qd 2p in acc[8p .. 8p+3], qd 2p+1 in acc[8p+4 .. 8p+7]
+        const float4 ma = *(const float4*)(mu_f + 16 * p + 4 * h);
+        const float4 mb = *(const float4*)(mu_f + 16 * p + 8 + 4 * h);
+        const uint32_t p0 = pack_bf16x2(__builtin_fmaf(a[8 * p + 0], S, ma.x), __builtin_fmaf(a[8 * p + 1], S, ma.y));
+        const uint32_t p1 = pack_bf16x2(__builtin_fmaf(a[8 * p + 2], S, ma.z), __builtin_fmaf(a[8 * p + 3], S, ma.w));
+        const uint32_t q0 = pack_bf16x2(__builtin_fmaf(a[8 * p + 4], S, mb.x), __builtin_fmaf(a[8 * p + 5], S, mb.y));
+        const uint32_t q1 = pack_bf16x2(__builtin_fmaf(a[8 * p + 6], S, mb.z), __builtin_fmaf(a[8 * p + 7], S, mb.w));
+        // lanes 0-31 keep p* and take the upper lanes' p*; lanes 32-63
+        // take the lower lanes' q* and keep q*
+        const auto x = __builtin_amdgcn_permlane32_swap(p0, q0, false, false);
+        const auto y = __builtin_amdgcn_permlane32_swap(p1, q1, false, false);
+        const int q = 4 * f + 2 * p + h;
+        *(uint4*)(row + (q ^ sw) * 16) = make_uint4(x[0], y[0], x[1], y[1]);
       }
     }
   }
   wave_lds_sync();
-  return bad;
 }
+
+// Row pieces of one staged round (RB bytes per row, 16 bytes per lane): store
+// k covers rows RPI k .. RPI k + RPI - 1.
+template <int OSZ, int FBR>
+struct RestRound {
+  static constexpr int RB = FBR * 32 * OSZ;   // bytes per row piece (128 or 256)
+  static constexpr int LPR = RB / 16;         // lanes per row piece
+  static constexpr int RPI = 64 / LPR;        // rows per store instruction
+  static constexpr int NST = kDecTok / RPI;   // store instructions
+  static constexpr int K1 = NST / 4 - 1, K2 = 3 * NST / 4 - 1;   // fill points
+  static_assert(K1 >= 0 && K1 < K2, "a round has at least four stores");
+  static_assert(RB <= kRestStgRow && LPR >= 8, "a staged row fits and holds 8 swizzled chunks");
+};
+
+// Store k of a staged round, in two parts: rest_load reads the lane's 16
+// bytes and output row from LDS (issued ahead of the store, so the store does
+// not wait on LDS behind other waves' traffic), rest_put issues the 16-byte
+// store to the row piece's output row, or to the sink when the row has no
+// destination, and returns whether the row's block table entry was bad.
+template <int OSZ, int FBR>
+__device__ __forceinline__ void rest_load(int k, const uint8_t* stg, const int* rows, uint4& v, int& row) {
+  using R = RestRound<OSZ, FBR>;
+  const int lane = threadIdx.x & 63;
+  const int c = lane % R::LPR;
+  const int r = k * R::RPI + lane / R::LPR;
+  v = *(const uint4*)(stg + r * R::RB + ((c ^ (r & 7)) * 16));
+  row = rows[r];
+}
+template <int OSZ, int FBR>
+__device__ __forceinline__ bool rest_put(const uint4& v, int row, uint8_t* dst_w, uint8_t* sink, bool store_ok,
+                                         int F, int fb0, uint32_t row_lim) {
+  using R = RestRound<OSZ, FBR>;
+  const int lane = threadIdx.x & 63;
+  const int col = (lane % R::LPR) * 16;
+  uint8_t* p = store_ok && row >= 0 && (uint32_t)row < row_lim ? dst_w + ((size_t)row * F + 32 * fb0) * OSZ + col
+                                                               : sink + (lane & 15) * 16;
+  // non-temporal stores: the output streams to memory without leaving dirty
+  // lines in the caches (plain stores measured faster for this kernel alone,
+  // but the next kernel then pays for writing those lines back)
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), (u32x4*)p);
+  return row == -2;
+}
+
+// Stores whose LDS reads are in flight ahead of the store being issued.
+constexpr int kRestPrefetch = 8;
 
 template <int KS, int NFB, bool FUSED, bool OUT32>
 __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2))) void restore_kernel(const LaunchArgs a) {
@@ -383,14 +427,16 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
   constexpr int KA = KS > 0 ? KS : 1;
   constexpr size_t FB = rest_frag_bytes(KS);
   constexpr int OSZ = OUT32 ? 4 : 2;
+  constexpr int FBR = OUT32 ? 2 : NFB;          // feature blocks per staged round
+  constexpr int NRD = NFB / FBR;                // rounds per unit (1, or 2 for f32 at nfb 4)
+  using R = RestRound<OSZ, FBR>;
   // 16-byte vectors per thread: a block's records (rb <= 24 KS) or staging
   constexpr int NVR = FUSED ? (kDecTok * 24 * KS / 16 + kRestThreads - 1) / kRestThreads : 0;
   constexpr int NVS = FUSED ? 0 : (KS > 0 ? ((int)stg_block_bytes(KS) / 16 + kRestThreads - 1) / kRestThreads : 0);
   constexpr int NXV = NVR > NVS ? NVR : (NVS > 0 ? NVS : 1);
   constexpr int NMU = (SLAB + kRestThreads - 1) / kRestThreads;   // mu values per thread
-  // stores per unit and wave: rounds of row pieces of 256 (or 128) bytes,
-  // 1 KB per store instruction
-  constexpr int NSTORES = OUT32 ? 8 * (NFB / 2) : (NFB == 4 ? 8 : 4);
+  constexpr int NSTORES = NRD * R::NST;         // store instructions per unit and wave
+  static_assert(SLAB * 4 <= (int)kRestMuBytes, "a slab's mu fits its LDS buffer");
   const int F = a.F;
   const int tid = threadIdx.x;
   const int lane = tid & 63, t = lane & 31, h = lane >> 5;
@@ -399,13 +445,11 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int in_esz = a.dtype == KVTC_F32 ? 4 : 2;
   const uint32_t n_slabs = (uint32_t)((F + SLAB - 1) / SLAB);
 
-  float* const mu_s = (float*)(smem + kRestMuOff);
   uint8_t* const stg = smem + kRestStgOff + (size_t)wave * kDecTok * kRestStgRow;
   uint8_t* const frag0 = smem + kRestFragOff;
-  uint8_t* const rec0 = smem + kRestFragOff + 2 * FB;
+  uint8_t* const rec0 = smem + kRestFragOff + 3 * FB;
   const uint32_t rec_lds = a.wave_lds;
   const size_t rec_rows_off = rec_lds - kDecTok * 4;
-  auto fragb = [&](uint32_t u) { return frag0 + (u & 1u) * FB; };
   auto recb = [&](uint32_t u) { return rec0 + (u & 1u) * rec_lds; };
 
   const uint32_t U = a.total_tiles;
@@ -496,33 +540,61 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
     };
 
     // ---- FUSED: B fragments and token scales of a unit from its records
-    // (the arithmetic of stage 1), one K step per wave.
-    auto build = [&](const RUnit& r, const uint8_t* recs, uint8_t* fr) __attribute__((always_inline)) {
-      const JobDesc& jd = a.jobs[r.j];
+    // (the arithmetic of stage 1), one K step per wave. The job's record
+    // layout and this wave's group widths are kept in scalars while
+    // consecutive units share the job, so a build issues no dependent loads
+    // of them.
+    constexpr int NSW = (KS + kRestWaves - 1) / kRestWaves;   // K steps per wave
+    struct BuildJob {
+      int j, rbp, G, n_g;
+      int w[NSW > 0 ? NSW : 1], chunk[NSW > 0 ? NSW : 1];
+    };
+    auto build_job = [&](int j) __attribute__((always_inline)) {
+      BuildJob bj;
+      const JobDesc& jd = a.jobs[j];
       CSlot& sl = slot_of(a, jd.slot);
-      const int rbp = dec_rec_stride(sl.record_bytes), G = sl.G;
+      bj.j = j;
+      bj.rbp = dec_rec_stride(sl.record_bytes);
+      bj.G = sl.G;
+      bj.n_g = 16 * KS / bj.G;
+#pragma unroll
+      for (int i = 0; i < NSW; ++i) {
+        const int s = wave + kRestWaves * i;
+        const int ag = s < KS ? 16 * s / bj.G : 0;
+        bj.w[i] = slot_width(sl, ag);
+        bj.chunk[i] = slot_chunk(sl, ag);
+      }
+      return bj;
+    };
+    auto build = [&](const RUnit& r, const BuildJob& bj, const uint8_t* recs, uint8_t* fr)
+        __attribute__((always_inline)) {
       const bool tok_ok = (uint32_t)t < r.nrec;
-      const uint8_t* rr = recs + (tok_ok ? t : 0) * rbp;
+      const uint8_t* rr = recs + (tok_ok ? t : 0) * bj.rbp;
 #pragma unroll
-      for (int s0 = 0; s0 < KS; s0 += kRestWaves) {
-        const int s = s0 + wave;
+      for (int i = 0; i < NSW; ++i) {
+        const int s = wave + kRestWaves * i;
         if (s < KS) {   // uniform per wave
-          // S_t from every active group of the token (each has a component
-          // among the K steps)
+          // S_t from every active group of the token (the K steps cover
+          // 16 KS / G of them): lane half h takes groups h, h + 2, ..., and
+          // the halves combine (permlane32 swap: each lane sees both)
           float m = 0.f;
-#pragma unroll
-          for (int s2 = 0; s2 < KS; ++s2) {
-            const float2 ps = get_scales(rr, 16 * s2 / G);
+#pragma unroll 4
+          for (int a2 = h; a2 < bj.n_g; a2 += 2) {
+            const float2 ps = get_scales(rr, a2);
             m = fmaxf(m, fmaxf(fabsf(ps.x), fabsf(ps.x + ps.y)));
+          }
+          {
+            const auto mm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+            m = fmaxf(__uint_as_float(mm[0]), __uint_as_float(mm[1]));
           }
           float S, Sinv;
           token_scale(m, S, Sinv);
-          const int ag = 16 * s / G;
-          const int w = slot_width(sl, ag);
+          const int ag = 16 * s / bj.G;
+          const int w = bj.w[i];
           const float kf = (float)((1 << w) - 1);
           const float2 ps = get_scales(rr, ag);
-          const uint4 f = tok_ok ? frag_from_bits(code_bits8(rr, sl, ag, 16 * s + 8 * h - ag * G, w), ps.x, ps.y,
-                                                  w, kf, 1.0f / kf, Sinv)
+          const uint64_t bits = lds_u64(rr + bj.chunk[i] + ((16 * s + 8 * h - ag * bj.G) * w) / 8);
+          const uint4 f = tok_ok ? frag_from_bits(bits, ps.x, ps.y, w, kf, 1.0f / kf, Sinv)
                                  : make_uint4(0u, 0u, 0u, 0u);
           *(uint4*)(fr + s * 1024 + lane * 16) = f;
           if (s == 0 && h == 0) *(float*)(fr + KS * 1024 + t * 4) = tok_ok ? S : 1.f;
@@ -533,27 +605,21 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
     };
 
     // ---- the (job, slab) segment whose V' fragments and mu are loaded:
-    // seg_issue issues the loads, seg_finish consumes them.
+    // seg_issue issues the loads, seg_finish consumes them. The mu of two
+    // segments is kept (by parity), since a unit is stored during the next
+    // unit's iteration, which may start a segment.
     int seg_j = -1;
-    uint32_t seg_slab = 0;
+    uint32_t seg_slab = 0, seg_par = 1;
     bool job_ok = false;
     uint4 A[NFB][KA];
     float mreg[NMU];
     int f_w = 0;          // first feature of this wave
     bool active = false;  // the wave has features (f_w < F)
-    // A bad block table entry met in the segment's units. It is reported when
-    // the segment ends, followed by a full wait: a status atomic among the
-    // loop's loads and stores would make the compiler treat the memory counter
-    // as out of order and drain every store before each wait for a load.
-    bool bad_seen = false;
-    auto report_bad = [&]() __attribute__((always_inline)) {
-      if (bad_seen && seg_j >= 0 && job_ok) set_status(a, a.jobs[seg_j].status_idx, KVTC_E_INVALID);
-      bad_seen = false;
-      __builtin_amdgcn_s_waitcnt(0);
-    };
+    auto mu_buf = [&](uint32_t par) { return (float*)(smem + kRestMuOff + par * kRestMuBytes); };
     auto seg_issue = [&](const RUnit& r) __attribute__((always_inline)) {
       seg_j = r.j;
       seg_slab = r.slab;
+      seg_par ^= 1u;
       const JobDesc& jd = a.jobs[r.j];
       CSlot& sl = slot_of(a, jd.slot);
       const int f0 = (int)r.slab * SLAB;
@@ -579,6 +645,7 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
       job_ok = FUSED ? check_header(a, jd, sl) == KVTC_OK : prior_rank(a, jd.status_idx) == 0;
     };
     auto seg_finish = [&]() __attribute__((always_inline)) {
+      float* mu_s = mu_buf(seg_par);
 #pragma unroll
       for (int i = 0; i < NMU; ++i) {
         const int li = tid + kRestThreads * i;
@@ -589,46 +656,85 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
       wait_vmcnt<0>();
     };
 
-    // ---- compute one unit from its fragment buffer and store it; fill()
-    // runs while the stores drain
-    auto compute = [&](const RUnit& r, const uint8_t* fr, auto&& fill) __attribute__((always_inline)) {
-      const JobDesc& jd = a.jobs[r.j];
-      f32x16 acc[NFB];
+    // ---- the unit whose product is in acc and is stored during the next
+    // iteration (p_real false before the first unit: its stores go to the
+    // sink)
+    f32x16 acc[NFB];
 #pragma unroll
-      for (int fb = 0; fb < NFB; ++fb)
+    for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[fb][i] = 0.f;
-      if (active) {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const f16x8 b = __builtin_bit_cast(f16x8, *(const uint4*)(fr + s * 1024 + lane * 16));
-#pragma unroll
-          for (int fb = 0; fb < NFB; ++fb)
-            acc[fb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, A[fb][s]), b, acc[fb], 0, 0, 0);
-        }
-      }
-      const float S = KS > 0 ? *(const float*)(fr + KS * 1024 + t * 4) : 1.f;
-      const int* rows = (const int*)(fr + stg_block_bytes(KS));
-      const float* mu_w = mu_s + wave * FPW;
-      uint8_t* dst_w = (uint8_t*)jd.dst + (size_t)f_w * OSZ;
-      const bool store_ok = job_ok && active;
+      for (int i = 0; i < 16; ++i) acc[fb][i] = 0.f;
+    bool p_real = false, p_ok = false;
+    int p_j = 0, p_fw = 0;
+    uint32_t p_par = 0, p_fi = 0;
+    // Jobs (bit j) with a bad block table entry among the stored rows,
+    // reported after the loop: a status atomic among the loop's loads and
+    // stores would make the compiler treat the memory counter as out of
+    // order and drain every store before each wait for a load.
+    uint32_t bad_jobs = 0;
+
+    auto fragb = [&](uint32_t fi) { return frag0 + fi * FB; };
+    // The stores of the pending unit, with mfma(i) (K step i of this unit)
+    // and fill() (the next unit's fragments) spread between them. Every wave
+    // issues the same stores on every path (addresses are clamped or sent to
+    // the sink), so the compiler can count them.
+    auto store_pending = [&](auto&& mfma, auto&& fill) __attribute__((always_inline)) {
+      const uint8_t* pf = fragb(p_fi);
+      const float S = KS > 0 ? *(const float*)(pf + KS * 1024 + t * 4) : 1.f;
+      const int* rows = (const int*)(pf + stg_block_bytes(KS));
+      const float* mu_w = mu_buf(p_par) + (p_fw - (p_fw / SLAB) * SLAB);
+      const JobDesc& jd = a.jobs[p_j];
+      uint8_t* dst_w = (uint8_t*)jd.dst + (size_t)p_fw * OSZ;
+      const bool store_ok = p_real && p_ok && p_fw < F;
       const uint32_t row_lim = rest_row_limit(jd);
       // the waves that fill in early are one per SIMD (waves go to the SIMDs
       // round robin), so every SIMD keeps a wave issuing stores
       const bool early = wave < 4;
-      // (the output type is a template parameter: with a run-time branch the
-      // compiler could not count the stores on every path and would drain
-      // them before the next wait for a load)
-      if (OUT32) {
-        bad_seen |=
-            rest_epilogue<4, 2, NFB>(acc, 0, S, mu_w, stg, rows, dst_w, a.sink, store_ok, F, row_lim, early, fill);
-        if (NFB > 2)
-          bad_seen |= rest_epilogue<4, 2, NFB>(acc, 2, S, mu_w, stg, rows, dst_w, a.sink, store_ok, F, row_lim,
-                                               early, [] {});
-      } else {
-        bad_seen |=
-            rest_epilogue<2, NFB, NFB>(acc, 0, S, mu_w, stg, rows, dst_w, a.sink, store_ok, F, row_lim, early, fill);
-      }
+      bool bad = false;
+      static_for<NRD>([&](auto rdc) __attribute__((always_inline)) {
+        constexpr int rd = decltype(rdc)::value;
+        rest_stage<OSZ, FBR, NFB>(acc, rd * FBR, S, mu_w, stg);
+        if constexpr (rd == NRD - 1) {
+          // acc is free: this unit's product starts from zero
+#pragma unroll
+          for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[fb][i] = 0.f;
+        }
+        // slot i: the stores k with k KA / NST == i (spread over the K
+        // steps), then, in the last round, K step i of this unit. The LDS
+        // reads of store k are issued PFD stores ahead.
+        constexpr int NSLOT = R::NST > KA ? R::NST : KA;
+        constexpr int PFD = kRestPrefetch < R::NST ? kRestPrefetch : R::NST;
+        uint4 sv[R::NST];
+        int srow[R::NST];
+        static_for<PFD>([&](auto kc) __attribute__((always_inline)) {
+          constexpr int k = decltype(kc)::value;
+          rest_load<OSZ, FBR>(k, stg, rows, sv[k], srow[k]);
+        });
+        static_for<NSLOT>([&](auto ic) __attribute__((always_inline)) {
+          constexpr int i = decltype(ic)::value;
+          __builtin_amdgcn_sched_barrier(0);
+          static_for<R::NST>([&](auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            if constexpr (k * KA / R::NST == i) {
+              if constexpr (k + PFD < R::NST) rest_load<OSZ, FBR>(k + PFD, stg, rows, sv[k + PFD], srow[k + PFD]);
+              bad |= rest_put<OSZ, FBR>(sv[k], srow[k], dst_w, a.sink, store_ok, F, rd * FBR, row_lim);
+              if constexpr (rd == 0 && (k == R::K1 || k == R::K2)) {
+                if (early == (k == R::K1)) {   // uniform
+                  __builtin_amdgcn_sched_barrier(0);
+                  fill();
+                  __builtin_amdgcn_sched_barrier(0);
+                }
+              }
+            }
+          });
+          if constexpr (rd == NRD - 1 && i < KS) mfma(ic);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        wave_lds_sync();   // the staging rows are free for the next round
+      });
+      if (p_real && __builtin_amdgcn_ballot_w64(bad) != 0) bad_jobs |= 1u << p_j;
     };
 
     // ---- prologue: the first units' loads and the first segment's loads
@@ -638,6 +744,10 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
     Src sq = src_of(cur.j);                 // the job of the unit last fetched
     u32x4 xv[NXV], xv2[NXV];
     int ent, in, ent2 = 0, in2 = 0;
+    // fragment buffers (0..2, rotating): of the pending unit, of this unit,
+    // of the next one
+    uint32_t fi_cur = 0, fi_nx = 1;
+    p_fi = 2;
     fetch(cur, sq, xv, ent, in);
     const Src sq2 = FUSED && nx.j >= 0 ? src_of(nx.j) : sq;
     if (FUSED) fetch(nx.j >= 0 ? nx : cur, sq2, xv2, ent2, in2);
@@ -646,13 +756,14 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
       commit(cur, sq, xv, ent, in, recb(u_lo), (int*)(recb(u_lo) + rec_rows_off));
       commit(nx.j >= 0 ? nx : cur, sq2, xv2, ent2, in2, recb(u_lo + 1), (int*)(recb(u_lo + 1) + rec_rows_off));
     } else {
-      commit(cur, sq, xv, ent, in, fragb(u_lo), (int*)(fragb(u_lo) + stg_block_bytes(KS)));
+      commit(cur, sq, xv, ent, in, fragb(fi_cur), (int*)(fragb(fi_cur) + stg_block_bytes(KS)));
     }
     seg_finish();
     __syncthreads();
+    BuildJob bjob = build_job(cur.j);
     if (FUSED) {
       sq = sq2;
-      build(cur, recb(u_lo), fragb(u_lo));
+      build(cur, bjob, recb(u_lo), fragb(fi_cur));
       __syncthreads();
     }
     // Every load of the prologue has completed, also in lanes that had no use
@@ -662,48 +773,74 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
 
     for (uint32_t u = u_lo; u < u_hi; ++u) {
       if (cur.j != seg_j || cur.slab != seg_slab) {   // uniform: a new segment
-        report_bad();
         seg_issue(cur);
         seg_finish();
         __syncthreads();
       }
+      const RUnit nx_old = nx;
+      // B fragments of this unit, K step s, from LDS into the MFMAs
+      const uint8_t* fr = fragb(fi_cur);
+      const bool act = active;
+      auto mfma = [&](auto sc) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        if (act) {
+          const f16x8 b = __builtin_bit_cast(f16x8, *(const uint4*)(fr + s * 1024 + lane * 16));
+#pragma unroll
+          for (int fb = 0; fb < NFB; ++fb)
+            acc[fb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, A[fb][s]), b, acc[fb], 0, 0, 0);
+        }
+      };
       // Every iteration issues the same loads and commits them (past the
       // range the current unit is loaded again into a buffer nothing reads),
-      // so the compiler can count this unit's stores between the loads and
-      // the wait for them.
+      // so the compiler can count the stores between the loads and the wait
+      // for them.
       if (FUSED) {
         const RUnit nx2 = rest_next(a, nx, n_slabs);
         const RUnit fu = nx2.j >= 0 ? nx2 : cur;
+        if (nx.j >= 0 && nx.j != bjob.j) bjob = build_job(nx.j);   // uniform
         if (fu.j != sq.j) sq = src_of(fu.j);
         fetch(fu, sq, xv, ent, in);
         __builtin_amdgcn_sched_barrier(0);
-        // unit u + 1 is dequantized while unit u's stores drain
-        compute(cur, fragb(u), [&] {
-          if (nx.j >= 0) build(nx, recb(u + 1), fragb(u + 1));
+        // the previous unit is stored while this one is multiplied and the
+        // next one dequantized
+        store_pending(mfma, [&] {
+          if (nx.j >= 0) build(nx, bjob, recb(u + 1), fragb(fi_nx));
         });
         __builtin_amdgcn_sched_barrier(0);
         commit(fu, sq, xv, ent, in, recb(u), (int*)(recb(u) + rec_rows_off));
-        // the loads of this iteration have completed (only its stores may be
-        // outstanding), on every path through commit
-        wait_vmcnt<NSTORES>();
-        __syncthreads();
-        cur = nx;
         nx = nx2;
       } else {
         const RUnit fu = nx.j >= 0 ? nx : cur;
         if (fu.j != sq.j) sq = src_of(fu.j);
         fetch(fu, sq, xv, ent, in);
         __builtin_amdgcn_sched_barrier(0);
-        compute(cur, fragb(u), [] {});
+        store_pending(mfma, [] {});
         __builtin_amdgcn_sched_barrier(0);
-        commit(fu, sq, xv, ent, in, fragb(u + 1), (int*)(fragb(u + 1) + stg_block_bytes(KS)));
-        wait_vmcnt<NSTORES>();
-        __syncthreads();
-        cur = nx;
+        commit(fu, sq, xv, ent, in, fragb(fi_nx), (int*)(fragb(fi_nx) + stg_block_bytes(KS)));
         nx = rest_next(a, nx, n_slabs);
       }
+      // the loads of this iteration have completed (only its stores may be
+      // outstanding), on every path through commit
+      wait_vmcnt<NSTORES>();
+      __syncthreads();
+      // this unit becomes the pending one
+      p_real = true;
+      p_ok = job_ok;
+      p_j = cur.j;
+      p_fw = f_w;
+      p_par = seg_par;
+      const uint32_t fi_free = p_fi;
+      p_fi = fi_cur;
+      fi_cur = fi_nx;
+      fi_nx = fi_free;
+      cur = nx_old;
     }
-    report_bad();
+    // the last unit
+    store_pending([](auto) {}, [] {});
+    // reported once every store is issued
+    if (tid % 64 == 0) {
+      for (uint32_t m = bad_jobs; m; m &= m - 1) set_status(a, a.jobs[__builtin_ctz(m)].status_idx, KVTC_E_INVALID);
+    }
   }
 
   if (FUSED) {

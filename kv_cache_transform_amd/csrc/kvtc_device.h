@@ -6,6 +6,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <utility>
 
 #include <algorithm>
 #include <cstdlib>
@@ -386,6 +387,18 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt is six bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// f(std::integral_constant<int, i>{}) for i = 0 .. N - 1, each call with its
+// index as a compile-time constant (unrolling that does not depend on the
+// optimizer's size limits: register arrays stay in registers).
+template <class Fn, int... I>
+__device__ __forceinline__ void static_for_impl(Fn&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // ------------------------------------------------------ launch helpers ---

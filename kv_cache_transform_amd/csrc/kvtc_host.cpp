@@ -620,14 +620,14 @@ size_t kvtc_staging_bytes(const kvtc_codec* c, const kvtc_job* jobs, int32_t n_j
 }
 
 size_t kvtc_decode_workspace_bytes(const kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs) {
-  // 0 flags jobs the codec cannot decode; the fused decode needs only the
-  // status words and the sink.
+  // 0 flags jobs the codec cannot decode; otherwise the status words and the
+  // sink, then the staging of the two-stage schedule.
   if (!c || !jobs || n_jobs <= 0) return 0;
   for (int i = 0; i < n_jobs; ++i) {
     int idx;
     if (!slot_index(c, jobs[i].layer, jobs[i].kind, &idx) || !c->slots[idx].calibrated) return 0;
   }
-  return kvtc_workspace_bytes(n_jobs);
+  return kvtc_workspace_bytes(n_jobs) + kvtc_staging_bytes(c, jobs, n_jobs);
 }
 
 }  // extern "C"
@@ -865,9 +865,18 @@ kvtc_status kvtc_decode(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, int
   if (!c || !jobs || n_jobs <= 0 || n_jobs > KVTC_MAX_JOBS) return fail(KVTC_E_INVALID, "bad codec, jobs or job count");
   const size_t need = kvtc_decode_workspace_bytes(c, jobs, n_jobs);
   if (need == 0) return fail(KVTC_E_INVALID, "job: bad layer or kind, or not calibrated");
-  if (!d_ws || ws_bytes < need) return fail(KVTC_E_CAPACITY, "workspace below kvtc_decode_workspace_bytes");
-  // One fused launch per batch: headers, passthrough rows, dequantization
-  // and the restore, with no staging buffer.
+  const size_t base = kvtc_workspace_bytes(n_jobs);
+  if (!d_ws || ws_bytes < base) return fail(KVTC_E_CAPACITY, "workspace below kvtc_workspace_bytes(n_jobs)");
+  if (ws_bytes >= need) {
+    // Two-stage schedule, the staging right after the status words and sink:
+    // stage 1 for every batch, then stage 2 for every batch.
+    uint8_t* stg = need > base ? (uint8_t*)d_ws + base : nullptr;
+    kvtc_status st = kvtc_decode_unpack(c, jobs, n_jobs, out_dtype, stg, need - base, d_ws, stream);
+    if (st != KVTC_OK) return st;
+    return kvtc_decode_restore(c, jobs, n_jobs, out_dtype, stg, need - base, d_ws, stream);
+  }
+  // Fused schedule: one launch per batch (headers, passthrough rows,
+  // dequantization and the restore), no staging.
   std::vector<LaunchArgs> b;
   std::vector<int> k;
   std::vector<size_t> l;

@@ -143,16 +143,18 @@ __host__ __device__ constexpr size_t stg_block_bytes(int ks) { return (size_t)ks
 // the slab with their V' fragments in registers; nfb = 4 needs ks <= 6 (the
 // fragments and four accumulators then fit in 256 VGPRs) and F a multiple of
 // 1024 (one slab covers 1024 features), else nfb = 2.
-// LDS (bytes): the passthrough row list, the slab's mu (fp32), the waves'
-// output staging rows (kRestStgRow each), two fragment buffers
-// (rest_frag_bytes: the B fragments and token scales of a block, then its 32
-// output rows as int32), and for the fused decode two record buffers of
-// rec_lds bytes (32 record rows of stride dec_rec_stride(rb), 16 bytes of
-// padding for 8-byte reads, then 32 int32 output rows).
+// LDS (bytes): the passthrough row list, the mu (fp32) of two slabs (the
+// current segment's and the one before), the waves' output staging rows
+// (kRestStgRow bytes each, 16-byte chunks XOR-swizzled by row), three
+// fragment buffers (rest_frag_bytes: the B
+// fragments and token scales of a block, then its 32 output rows as int32),
+// and for the fused decode two record buffers of rec_lds bytes (32 record
+// rows of stride dec_rec_stride(rb), 16 bytes of padding for 8-byte reads,
+// then 32 int32 output rows).
 constexpr int kRestWaves = 8;
 constexpr int kRestThreads = 64 * kRestWaves;
 constexpr int kRestPassRows = 8;
-constexpr int kRestStgRow = 256 + 16;
+constexpr int kRestStgRow = 256;
 __host__ __device__ constexpr int rest_nfb(int ks, int F) { return ks <= 6 && F % 1024 == 0 ? 4 : 2; }
 __host__ __device__ constexpr int rest_slab(int nfb) { return kRestWaves * 32 * nfb; }
 __host__ __device__ constexpr size_t rest_frag_bytes(int ks) { return stg_block_bytes(ks) + kDecTok * 4; }
@@ -163,10 +165,11 @@ __host__ __device__ constexpr size_t rest_rec_bytes(int rb_max) {
   return (rec_rows_bytes(rb_max) + 16 + 15) / 16 * 16 + kDecTok * 4;
 }
 constexpr size_t kRestMuOff = 64;
-constexpr size_t kRestStgOff = kRestMuOff + 4 * 1024;
+constexpr size_t kRestMuBytes = 4 * 1024;   // one slab's mu (rest_slab(4) floats)
+constexpr size_t kRestStgOff = kRestMuOff + 2 * kRestMuBytes;
 constexpr size_t kRestFragOff = kRestStgOff + (size_t)kRestWaves * kDecTok * kRestStgRow;
 __host__ __device__ constexpr size_t rest_lds_bytes(int ks, bool fused, size_t rec_lds) {
-  return kRestFragOff + 2 * rest_frag_bytes(ks) + (fused ? 2 * rec_lds : 0);
+  return kRestFragOff + 3 * rest_frag_bytes(ks) + (fused ? 2 * rec_lds : 0);
 }
 
 // Host-side launchers implemented in kvtc_encode.hip and kvtc_decode.hip (G = group size, lds =

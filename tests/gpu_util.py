@@ -79,9 +79,11 @@ class DevCodec:
         return torch.full((max(rows, 1), F), -7, dtype=dt, device=DEV) if dt == torch.int16 else \
             torch.full((max(rows, 1), F), -7.0, dtype=dt, device=DEV)
 
-    def decode(self, items, out_dtype, F, paging=None, two_stage=False, stg_fill=0):
+    def decode(self, items, out_dtype, F, paging=None, two_stage=False, stg_fill=0, schedule="fused"):
         """items: list of (layer, kind, T, stream bytes). paging: list of
         (block_table dev tensor, block_size, n_blocks) per item or None.
+        two_stage: the explicit kvtc_decode_unpack / kvtc_decode_restore calls,
+        else kvtc_decode with the workspace of `schedule` (see decode_jobs).
         stg_fill: byte the staging memory holds before the call (0xFF makes
         every float read from it that stage 1 did not write a NaN).
         Returns (outputs, status)."""
@@ -106,15 +108,19 @@ class DevCodec:
             self.codec.decode_restore(jobs, out_dtype, stg, stg.numel(), self.ws, s)
             st = self.status(len(jobs))
         else:
-            st = self.decode_jobs(jobs, out_dtype, stg_fill)
+            st = self.decode_jobs(jobs, out_dtype, stg_fill, schedule)
         torch.cuda.synchronize()
         return outs, st
 
-    def decode_jobs(self, jobs, out_dtype, stg_fill=0):
+    def decode_jobs(self, jobs, out_dtype, stg_fill=0, schedule="fused"):
         """kvtc_decode of prepared jobs with a workspace of its own (status words
-        zeroed, the staging part filled with stg_fill); returns the status."""
+        zeroed, any staging part filled with stg_fill): schedule "fused" gives it
+        kvtc_workspace_bytes(n) (the single-launch schedule), "staged"
+        kvtc_decode_workspace_bytes (the two-stage schedule). Returns the status."""
         s = torch.cuda.current_stream()
-        n = self.codec.decode_workspace_bytes(jobs)
+        full = self.codec.decode_workspace_bytes(jobs)
+        assert full > 0
+        n = K.kvtc_workspace_bytes(len(jobs)) if schedule == "fused" else full
         dws = torch.zeros((n + 3) // 4, dtype=torch.int32, device=DEV)
         dws.view(torch.uint8)[K.kvtc_workspace_bytes(len(jobs)):].fill_(stg_fill)
         self.codec.decode(jobs, out_dtype, dws, n, s)

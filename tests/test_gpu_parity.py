@@ -167,12 +167,14 @@ def test_decode_parity(case, out_dtype):
         worst = max(worst, _decode_check(w, op, art.slots[(l, k)], ref.stream, T, outs[i],
                                          out_dtype, l, k, rows))
     print(f"{case} out={out_dtype}: max rel err {worst:.3e}")
-    # the two-stage (unpack + restore) path computes exactly what the fused one does
-    outs2, st2 = dc.decode([(l, k, T, ref.stream) for l, k, _, ref in items], out_dtype, op.F,
-                           paging, two_stage=True)
-    assert np.all(st2 == 0), st2
-    for a, b in zip(outs, outs2):
-        assert torch.equal(a, b)
+    # the two-stage path computes exactly what the fused one does, through
+    # the explicit stage calls and through kvtc_decode given the staging
+    for kw in ({"two_stage": True}, {"schedule": "staged", "stg_fill": 0xFF}):
+        outs2, st2 = dc.decode([(l, k, T, ref.stream) for l, k, _, ref in items], out_dtype, op.F,
+                               paging, **kw)
+        assert np.all(st2 == 0), (kw, st2)
+        for a, b in zip(outs, outs2):
+            assert torch.equal(a, b), kw
 
 
 @pytest.mark.parametrize("case", list(CASES))

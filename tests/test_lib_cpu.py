@@ -176,10 +176,10 @@ def test_deflate_roundtrip():
 
 
 def test_decode_workspace_sizes():
-    """kvtc_decode_workspace_bytes: the status words and the sink (the fused
-    decode needs no staging; 0 is reserved for jobs naming an unknown or
-    uncalibrated (layer, kind)); the two-stage calls' staging is one block of
-    ks * 1024 + 128 bytes per 32 compressed tokens, 0 without compressed rows."""
+    """kvtc_decode_workspace_bytes: the status words and the sink, then the
+    two-stage schedule's staging (0 is reserved for jobs naming an unknown or
+    uncalibrated (layer, kind)); the staging is one block of ks * 1024 + 128
+    bytes per 32 compressed tokens, 0 without compressed rows."""
     w = synth.workload("tiny")
     _, kp = _params_pair(w)
     c = K.Codec(kp)
@@ -194,5 +194,5 @@ def test_decode_workspace_sizes():
     jobs = short + [K.make_job(0, 0, T, 16, 16, 1 << 20)]
     blocks = 256 * ((2 * (ks * 1024 + 128) + 255) // 256)
     assert c.staging_bytes(jobs) == blocks
-    assert c.decode_workspace_bytes(jobs) == K.kvtc_workspace_bytes(len(jobs))
+    assert c.decode_workspace_bytes(jobs) == K.kvtc_workspace_bytes(len(jobs)) + blocks
     assert c.decode_workspace_bytes([K.make_job(0, 1, T, 16, 16, 1 << 20)]) == 0   # V never calibrated
