@@ -219,6 +219,20 @@ size_t kvtc_decode_workspace_bytes(const kvtc_codec* codec, const kvtc_job* jobs
 kvtc_status kvtc_decode(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
                         int32_t out_dtype, void* d_ws, size_t ws_bytes, hipStream_t stream);
 
+/* kvtc_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops, harnesses that forbid hipMalloc): the fused
+ * schedule, with its status words and sink in a static device array of
+ * kvtc_workspace_bytes(KVTC_MAX_JOBS) bytes (33 KiB; one copy per GPU, kept
+ * until the process ends, its address looked up on the first call on each
+ * device) instead of a caller's workspace. The call allocates nothing: it
+ * clears this call's status words with a small kernel, decodes, and, if
+ * d_status is not NULL, writes each job's kvtc_status to d_status[i] (device
+ * memory, n_jobs int32) on `stream`. More than KVTC_MAX_JOBS jobs give
+ * KVTC_E_CAPACITY. Every call on one GPU uses the same array: calls that
+ * overlap on one GPU (other streams, other threads) race on it. */
+kvtc_status kvtc_decode_noalloc(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
+                                int32_t out_dtype, int32_t* d_status, hipStream_t stream);
+
 /* Two-stage decode for layer-by-layer pipelines (section 2C: decompression
  * can proceed layer by layer). Stage 1 validates headers, copies passthrough
  * rows to dst and turns every record into the operands of the

@@ -76,6 +76,7 @@ def lib():
         "kvtc_encode": (st, [vp, C.POINTER(kvtc_job), i32, vp, vp]),
         "kvtc_decode": (st, [vp, C.POINTER(kvtc_job), i32, i32, vp, sz, vp]),
         "kvtc_decode_workspace_bytes": (sz, [vp, C.POINTER(kvtc_job), i32]),
+        "kvtc_decode_noalloc": (st, [vp, C.POINTER(kvtc_job), i32, i32, vp, vp]),
         "kvtc_unpack": (st, [vp, C.POINTER(kvtc_job), vp, vp, vp, vp]),
         "kvtc_staging_bytes": (sz, [vp, C.POINTER(kvtc_job), i32]),
         "kvtc_decode_unpack": (st, [vp, C.POINTER(kvtc_job), i32, i32, vp, sz, vp, vp]),
@@ -201,6 +202,11 @@ def kvtc_decode_workspace_bytes(codec: int, jobs) -> int:
     return lib().kvtc_decode_workspace_bytes(codec, _jobs(jobs), len(jobs))
 
 
+def kvtc_decode_noalloc(codec: int, jobs, out_dtype: int, d_status=None, stream=None) -> None:
+    _check(lib().kvtc_decode_noalloc(codec, _jobs(jobs), len(jobs), out_dtype, _ptr(d_status),
+                                     _stream(stream)))
+
+
 def kvtc_staging_bytes(codec: int, jobs) -> int:
     return lib().kvtc_staging_bytes(codec, _jobs(jobs), len(jobs))
 
@@ -288,6 +294,9 @@ class Codec:
 
     def decode(self, jobs, out_dtype, d_ws, ws_bytes, stream=None):
         kvtc_decode(self.h, jobs, out_dtype, d_ws, ws_bytes, stream)
+
+    def decode_noalloc(self, jobs, out_dtype, d_status=None, stream=None):
+        kvtc_decode_noalloc(self.h, jobs, out_dtype, d_status, stream)
 
     def decode_workspace_bytes(self, jobs) -> int:
         return kvtc_decode_workspace_bytes(self.h, jobs)

@@ -14,6 +14,8 @@
 // D[feature][token] = sum_j V'[feature][j] * c_hat[token][j] on
 // v_mfma_f32_32x32x16_f16 per 128-feature slab (V' in LDS), written as
 // S_t * D + mu through LDS rows in coalesced row-piece stores.
+#include <mutex>
+
 #include "kvtc_device.h"
 
 namespace kvtc {
@@ -976,6 +978,63 @@ int launch_unpack(const LaunchArgs& a, int G, size_t lds, void* codes, void* ss,
   } else {
     return (int)hipErrorInvalidValue;
   }
+  return (int)hipGetLastError();
+}
+
+// ----------------------------------------------- decode without allocation ---
+//
+// Status words and sink of kvtc_decode_noalloc: a workspace of
+// kvtc_workspace_bytes(kMaxScratchJobs) bytes in a static device array (one
+// copy per GPU, held until the process ends). Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in): each device's
+// address comes from hipGetSymbolAddress, once, with that device current.
+constexpr int kMaxScratchJobs = KVTC_MAX_JOBS;
+constexpr size_t kScratchBytes = ((size_t)kMaxScratchJobs * 8 + 255) / 256 * 256 + kSinkBytes;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // per device, null until looked up
+}  // namespace
+
+int noalloc_scratch(void** ptr, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = kScratchBytes;
+  return (int)hipSuccess;
+}
+
+// Zero n status words (a fill kernel, not a memset node, so the call can sit
+// in a captured graph and be replayed).
+__global__ void clear_words_kernel(unsigned long long* w, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) w[i] = 0ull;
+}
+// Status words -> kvtc_status codes (the rank in the low byte).
+__global__ void status_codes_kernel(const unsigned long long* w, int32_t* out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = rank_status((int)(w[i] & 0xFFull));
+}
+
+int launch_clear_words(void* words, int n, hipStream_t s) {
+  hipLaunchKernelGGL(clear_words_kernel, dim3((n + 255) / 256), dim3(256), 0, s, (unsigned long long*)words, n);
+  return (int)hipGetLastError();
+}
+int launch_status_codes(const void* words, int32_t* out, int n, hipStream_t s) {
+  hipLaunchKernelGGL(status_codes_kernel, dim3((n + 255) / 256), dim3(256), 0, s,
+                     (const unsigned long long*)words, out, n);
   return (int)hipGetLastError();
 }
 

@@ -808,6 +808,24 @@ kvtc_status hip_status(int e, const char* what) {
   return fail(KVTC_E_HIP, std::string(what) + ": " + hipGetErrorString((hipError_t)e));
 }
 
+// Fused decode schedule: one launch per batch (headers, passthrough rows,
+// dequantization and the restore), the workspace holding only the status
+// words and the sink.
+kvtc_status decode_fused(kvtc_codec* c, const kvtc_job* jobs, int n_jobs, int out_dtype, void* d_ws,
+                         hipStream_t stream) {
+  std::vector<LaunchArgs> b;
+  std::vector<int> k;
+  std::vector<size_t> l;
+  kvtc_status st = plan(c, Mode::Decode, jobs, n_jobs, out_dtype, d_ws, nullptr, 0, b, k, l);
+  if (st != KVTC_OK) return st;
+  for (size_t i = 0; i < b.size(); ++i) {
+    if (b[i].total_tiles + b[i].total_cblks == 0) continue;   // every job has a header unit
+    st = hip_status(launch_restore(b[i], k[i], true, l[i], stream), "decode launch");
+    if (st != KVTC_OK) return st;
+  }
+  return KVTC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -875,19 +893,26 @@ kvtc_status kvtc_decode(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, int
     if (st != KVTC_OK) return st;
     return kvtc_decode_restore(c, jobs, n_jobs, out_dtype, stg, need - base, d_ws, stream);
   }
-  // Fused schedule: one launch per batch (headers, passthrough rows,
-  // dequantization and the restore), no staging.
-  std::vector<LaunchArgs> b;
-  std::vector<int> k;
-  std::vector<size_t> l;
-  kvtc_status st = plan(c, Mode::Decode, jobs, n_jobs, out_dtype, d_ws, nullptr, 0, b, k, l);
+  return decode_fused(c, jobs, n_jobs, out_dtype, d_ws, stream);
+}
+
+kvtc_status kvtc_decode_noalloc(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, int32_t out_dtype,
+                                int32_t* d_status, hipStream_t stream) {
+  if (!c || !jobs || n_jobs <= 0) return fail(KVTC_E_INVALID, "bad codec, jobs or job count");
+  void* ws = nullptr;
+  size_t ws_cap = 0;
+  kvtc_status st = hip_status(noalloc_scratch(&ws, &ws_cap), "static workspace lookup");
   if (st != KVTC_OK) return st;
-  for (size_t i = 0; i < b.size(); ++i) {
-    if (b[i].total_tiles + b[i].total_cblks == 0) continue;   // every job has a header unit
-    st = hip_status(launch_restore(b[i], k[i], true, l[i], stream), "decode launch");
-    if (st != KVTC_OK) return st;
-  }
-  return KVTC_OK;
+  if (kvtc_workspace_bytes(n_jobs) > ws_cap)
+    return fail(KVTC_E_CAPACITY, "more jobs than kvtc_decode_noalloc's static workspace holds (KVTC_MAX_JOBS)");
+  if (kvtc_decode_workspace_bytes(c, jobs, n_jobs) == 0)
+    return fail(KVTC_E_INVALID, "job: bad layer or kind, or not calibrated");
+  // the array keeps the last call's words: start this call's from zero
+  st = hip_status(launch_clear_words(ws, n_jobs, stream), "status clear launch");
+  if (st != KVTC_OK) return st;
+  st = decode_fused(c, jobs, n_jobs, out_dtype, ws, stream);
+  if (st != KVTC_OK || !d_status) return st;
+  return hip_status(launch_status_codes(ws, d_status, n_jobs, stream), "status launch");
 }
 
 kvtc_status kvtc_unpack(kvtc_codec* c, const kvtc_job* job, void* d_codes, void* d_shift_scale, void* d_ws,

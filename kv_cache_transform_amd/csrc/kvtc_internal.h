@@ -180,6 +180,11 @@ int launch_encode(const LaunchArgs& a, int nb, int G, size_t lds, hipStream_t s)
 int launch_prep(const LaunchArgs& a, int ks, size_t lds, hipStream_t s);
 int launch_restore(const LaunchArgs& a, int ks, bool fused, size_t lds, hipStream_t s);
 int launch_unpack(const LaunchArgs& a, int G, size_t lds, void* codes, void* ss, hipStream_t s);
+// kvtc_decode_noalloc's workspace: this device's copy of a static device
+// array (address looked up once per device), and its size.
+int noalloc_scratch(void** ptr, size_t* bytes);
+int launch_clear_words(void* words, int n, hipStream_t s);
+int launch_status_codes(const void* words, int32_t* out, int n, hipStream_t s);
 int launch_pack(const LaunchArgs& a, int G, size_t lds, const void* codes, const void* ss,
                 hipStream_t s);
 
