@@ -298,13 +298,12 @@ def main():
         ach = alg / n_launch / per_launch_t / 1e9
         r = {"kernel": name, "achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBPS, 4),
              "alg_bytes_per_launch": int(alg / n_launch), "us_per_launch": round(per_launch_t * 1e6, 2),
-             "launches_per_call": n_launch}
+             "launches_per_call": n_launch, "traffic": measured_traffic(name, args.workload)}
         if name in timed_in:
             r["timed_in"] = timed_in[name]
         return r
 
     flops = sum(2 * F * r_eff[(l, k)] * tc for l, k, _ in jobs)
-    traffic = measured_traffic(dominant, args.workload)
 
     # --- compression ratio (host zlib on a sample of streams; not timed)
     host_streams = sbuf.cpu().numpy()
@@ -338,7 +337,7 @@ def main():
         "decode_path": {"schedule": "two-stage pipeline" if pipe is not None else "two-stage",
                         "achieved": round(dec_alg / dec_t / 1e9, 1),
                         "frac": round(dec_alg / dec_t / 1e9 / HBM_PEAK_GBPS, 4)},
-        "roofline": dict(bound="hbm", peak=HBM_PEAK_GBPS, unit="GB/s", traffic=traffic, **roof(dominant)),
+        "roofline": dict(bound="hbm", peak=HBM_PEAK_GBPS, unit="GB/s", **roof(dominant)),
         "roofline_other": [roof(k) for k in kern if k != dominant],
         "mfma_flops_per_call": flops,
         "copy_GBps": round(copy_gbps, 1),

@@ -205,8 +205,8 @@ kvtc_status kvtc_encode(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
  * schedules that produce identical results, chosen by the workspace given:
  *  - ws_bytes >= kvtc_decode_workspace_bytes(jobs) (kvtc_workspace_bytes
  *    (n_jobs) followed by kvtc_staging_bytes(jobs)): the two-stage schedule
- *    below (kvtc_decode_unpack, then kvtc_decode_restore) with the staging
- *    inside d_ws; measured faster, at the cost of the staging memory;
+ *    below, stage 1 then stage 2 of each launch batch in turn, with the
+ *    staging inside d_ws;
  *  - kvtc_workspace_bytes(n_jobs) <= ws_bytes < that: the fused schedule, one
  *    launch per batch (at most 32 jobs of one K-step count) that dequantizes
  *    each block of 32 records into MFMA operands in LDS and restores it, with

@@ -886,12 +886,30 @@ kvtc_status kvtc_decode(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, int
   const size_t base = kvtc_workspace_bytes(n_jobs);
   if (!d_ws || ws_bytes < base) return fail(KVTC_E_CAPACITY, "workspace below kvtc_workspace_bytes(n_jobs)");
   if (ws_bytes >= need) {
-    // Two-stage schedule, the staging right after the status words and sink:
-    // stage 1 for every batch, then stage 2 for every batch.
+    // Two-stage schedule, the staging right after the status words and sink.
+    // Stage 2 of each batch follows its stage 1, so the batch's staging is
+    // still in the caches when it is read back. (Both plans group the jobs
+    // by K-step count the same way, so their batches correspond.)
     uint8_t* stg = need > base ? (uint8_t*)d_ws + base : nullptr;
-    kvtc_status st = kvtc_decode_unpack(c, jobs, n_jobs, out_dtype, stg, need - base, d_ws, stream);
+    std::vector<LaunchArgs> bu, br;
+    std::vector<int> ku, kr;
+    std::vector<size_t> lu, lr;
+    kvtc_status st = plan(c, Mode::Unpack, jobs, n_jobs, out_dtype, d_ws, stg, need - base, bu, ku, lu);
     if (st != KVTC_OK) return st;
-    return kvtc_decode_restore(c, jobs, n_jobs, out_dtype, stg, need - base, d_ws, stream);
+    st = plan(c, Mode::Restore, jobs, n_jobs, out_dtype, d_ws, stg, need - base, br, kr, lr);
+    if (st != KVTC_OK) return st;
+    if (bu.size() != br.size()) return fail(KVTC_E_INVALID, "internal: stage batches differ");
+    for (size_t i = 0; i < bu.size(); ++i) {
+      if (bu[i].total_tiles + bu[i].total_cblks > 0) {   // every job has a header unit
+        st = hip_status(launch_prep(bu[i], ku[i], lu[i], stream), "decode stage 1 launch");
+        if (st != KVTC_OK) return st;
+      }
+      if (br[i].total_tiles > 0) {
+        st = hip_status(launch_restore(br[i], kr[i], false, lr[i], stream), "decode stage 2 launch");
+        if (st != KVTC_OK) return st;
+      }
+    }
+    return KVTC_OK;
   }
   return decode_fused(c, jobs, n_jobs, out_dtype, d_ws, stream);
 }
