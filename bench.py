@@ -148,11 +148,13 @@ def main():
         out = torch.empty((len(slots), R * per_req * bs, F), dtype=torch.int16, device=dev)
         pool_of = {s: i for i, s in enumerate(slots)}
         dec_jobs = [K.make_job(l, k, T, sbuf.data_ptr() + int(offs[i]), out[pool_of[(l, k)]],
-                               out[pool_of[(l, k)]].numel() * 2, tables[i], bs, R * per_req)
+                               out[pool_of[(l, k)]].numel() * 2, tables[i], bs, R * per_req,
+                               src_capacity=sizes[i])
                     for i, (l, k, _) in enumerate(jobs)]
     else:
         out = torch.empty((n_jobs, T, F), dtype=torch.int16, device=dev)
-        dec_jobs = [K.make_job(l, k, T, sbuf.data_ptr() + int(offs[i]), out[i], out[i].numel() * 2)
+        dec_jobs = [K.make_job(l, k, T, sbuf.data_ptr() + int(offs[i]), out[i], out[i].numel() * 2,
+                               src_capacity=sizes[i])
                     for i, (l, k, _) in enumerate(jobs)]
     log(f"calibration {calib_s:.1f}s; state {n_state / 2**20:.1f} MiB; "
         f"streams {offs[-1] / 2**20:.1f} MiB; {n_jobs} tensors")

@@ -106,6 +106,10 @@ typedef struct kvtc_codec kvtc_codec;
 /* One tensor of work: the K or V cache of one layer, [n_tokens, F] rows.
  *   encode:  src = KV rows (device, params.dtype), dst = stream (device).
  *   decode:  src = stream (device), dst = KV rows (device, out dtype).
+ * src_capacity bounds what the kernels read at src: n_tokens rows for encode
+ * (and for kvtc_pack's passthrough rows), kvtc_encoded_bytes(n_tokens) for
+ * decode and kvtc_unpack; a smaller value is rejected with KVTC_E_CAPACITY
+ * before anything is launched.
  * block_table (device, int32, decode only): when non-NULL, token t is written
  * to physical row block_table[t / block_size] * block_size + t % block_size
  * of dst (a paged cache of [n_blocks, block_size, F]); dst_capacity bounds the
@@ -115,6 +119,7 @@ typedef struct {
   int32_t kind;
   int64_t n_tokens;
   const void* src;
+  size_t src_capacity;     /* bytes readable at src                          */
   void* dst;
   size_t dst_capacity;     /* bytes available at dst                         */
   const int32_t* block_table;

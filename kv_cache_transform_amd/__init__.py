@@ -32,7 +32,8 @@ class kvtc_params(C.Structure):
 
 class kvtc_job(C.Structure):
     _fields_ = [("layer", C.c_int32), ("kind", C.c_int32), ("n_tokens", C.c_int64),
-                ("src", C.c_void_p), ("dst", C.c_void_p), ("dst_capacity", C.c_size_t),
+                ("src", C.c_void_p), ("src_capacity", C.c_size_t), ("dst", C.c_void_p),
+                ("dst_capacity", C.c_size_t),
                 ("block_table", C.c_void_p), ("block_size", C.c_int32), ("n_blocks", C.c_int32)]
 
 
@@ -122,9 +123,15 @@ def _jobs(jobs):
 
 
 def make_job(layer, kind, n_tokens, src, dst, dst_capacity, block_table=None, block_size=0,
-             n_blocks=0) -> kvtc_job:
-    return kvtc_job(int(layer), int(kind), int(n_tokens), _ptr(src), _ptr(dst), int(dst_capacity),
-                    _ptr(block_table), int(block_size), int(n_blocks))
+             n_blocks=0, src_capacity=None) -> kvtc_job:
+    """src_capacity defaults to the byte size of src when src is a tensor; a
+    raw pointer needs it given."""
+    if src_capacity is None:
+        if not hasattr(src, "numel"):
+            raise ValueError("make_job: src_capacity is required when src is a raw pointer")
+        src_capacity = src.numel() * src.element_size()
+    return kvtc_job(int(layer), int(kind), int(n_tokens), _ptr(src), int(src_capacity), _ptr(dst),
+                    int(dst_capacity), _ptr(block_table), int(block_size), int(n_blocks))
 
 
 # ------------------------------------------------------------ C entry points ---

@@ -655,8 +655,6 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
                  std::vector<int>& shape, std::vector<size_t>& lds) {
   if (!c || !jobs || n <= 0 || n > KVTC_MAX_JOBS) return fail(KVTC_E_INVALID, "bad codec, jobs or job count");
   if (!d_ws || !aligned16(d_ws)) return fail(KVTC_E_INVALID, "workspace must be non-null and aligned");
-  if (!c->d_state || c->uploaded_version != c->calib_version)
-    return fail(KVTC_E_INVALID, "device state is missing or stale: call kvtc_upload");
   const bool dec = mode == Mode::Unpack || mode == Mode::Restore || mode == Mode::Decode;
   if (dec && out_dtype != KVTC_F32 && out_dtype != KVTC_BF16) return fail(KVTC_E_INVALID, "bad output dtype");
   const int F = c->F;
@@ -675,6 +673,12 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
     if (j.n_tokens < 0 || j.n_tokens > (int64_t)INT32_MAX) return fail(KVTC_E_INVALID, "job: bad n_tokens");
     if (!j.dst || !aligned16(j.dst)) return fail(KVTC_E_INVALID, "job: dst must be non-null and 16-byte aligned");
     if (!j.src || !aligned16(j.src)) return fail(KVTC_E_INVALID, "job: src must be non-null and 16-byte aligned");
+    // what the kernels read from src: the KV rows (encode, and the
+    // passthrough rows of the pack hook) or the whole stream
+    const bool reads_rows = mode == Mode::Encode || mode == Mode::Pack;
+    const size_t src_need = reads_rows ? (size_t)j.n_tokens * F * elem_bytes(c->p.dtype) : stream_bytes(c, s, j.n_tokens);
+    if (j.src_capacity < src_need)
+      return fail(KVTC_E_CAPACITY, reads_rows ? "job: src_capacity below n_tokens rows" : "job: src_capacity below kvtc_encoded_bytes");
     JobDesc& d = desc[i];
     std::memset(&d, 0, sizeof(d));
     d.src = j.src;
@@ -725,6 +729,9 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
       if (s.record_bytes > 24 * key[i]) return fail(KVTC_E_UNSUPPORTED, "record wider than the decode tiles");
     }
   }
+  // (checked after the jobs, so job errors are reported without a device)
+  if (!c->d_state || c->uploaded_version != c->calib_version)
+    return fail(KVTC_E_INVALID, "device state is missing or stale: call kvtc_upload");
   std::vector<int> order(n);
   for (int i = 0; i < n; ++i) order[i] = i;
   std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return key[x] < key[y]; });

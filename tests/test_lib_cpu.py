@@ -148,17 +148,40 @@ def test_calibrate_errors():
         c.calibrate(0, 2, np.zeros((100, 64), np.float32))      # bad kind
 
 
-def test_encode_requires_upload_and_calibration():
+def test_job_checks_precede_any_launch():
+    """Host validation (no device here): an uncalibrated slot, a src or dst
+    too small, or a missing workspace is rejected before the device state is
+    looked at, so nothing is launched; with valid jobs the missing upload is
+    the error."""
     w = synth.workload("tiny")
     op, kp = _params_pair(w)
     c = K.Codec(kp)
-    job = K.make_job(0, 0, 100, 4096, 8192, 1 << 20)
+    T, F = 100, w.features
+    rows = T * F * 4
+    job = K.make_job(0, 0, T, 4096, 8192, 1 << 20, src_capacity=rows)
     with pytest.raises(K.KvtcError) as e:
         c.encode([job], 256)
-    assert e.value.status == K.KVTC_E_INVALID           # never uploaded
+    assert e.value.status == K.KVTC_E_NOT_CALIBRATED
+    c.calibrate(0, 0, synth.storage(w, synth.gen_kv(w, 0, 0, 1, w.calib_tokens)), threads=2)
+    n = c.encoded_bytes(0, 0, T)
+    with pytest.raises(K.KvtcError) as e:                # encode reads n_tokens rows of src
+        c.encode([K.make_job(0, 0, T, 4096, 8192, n, src_capacity=rows - 16)], 256)
+    assert e.value.status == K.KVTC_E_CAPACITY and "src_capacity" in str(e.value)
+    with pytest.raises(K.KvtcError) as e:                # and writes the whole stream
+        c.encode([K.make_job(0, 0, T, 4096, 8192, n - 1, src_capacity=rows)], 256)
+    assert e.value.status == K.KVTC_E_CAPACITY
+    dec = lambda cap: [K.make_job(0, 0, T, 4096, 8192, rows, src_capacity=cap)]
+    with pytest.raises(K.KvtcError) as e:                # decode reads the whole stream
+        c.decode(dec(n - 1), K.KVTC_F32, 256, K.kvtc_workspace_bytes(1))
+    assert e.value.status == K.KVTC_E_CAPACITY and "src_capacity" in str(e.value)
+    with pytest.raises(K.KvtcError) as e:
+        c.encode([K.make_job(0, 0, T, 4096, 8192, n, src_capacity=rows)], 256)
+    assert e.value.status == K.KVTC_E_INVALID and "kvtc_upload" in str(e.value)   # never uploaded
     with pytest.raises(K.KvtcError) as e:
         c.encode([job], 0)
     assert e.value.status == K.KVTC_E_INVALID           # no workspace
+    with pytest.raises(ValueError):                      # a raw pointer needs its capacity
+        K.make_job(0, 0, T, 4096, 8192, rows)
 
 
 def test_zero_allocation_when_budget_too_small():
@@ -186,13 +209,13 @@ def test_decode_workspace_sizes():
     c.calibrate(0, 0, synth.storage(w, synth.gen_kv(w, 0, 0, 1, w.calib_tokens)), threads=2)
     info = c.slot(0, 0)
     ks = (info.r_eff + 15) // 16
-    short = [K.make_job(0, 0, T, 16, 16, 1 << 20) for T in (0, 1, w.sink + w.window)]
+    short = [K.make_job(0, 0, T, 16, 16, 1 << 20, src_capacity=1 << 20) for T in (0, 1, w.sink + w.window)]
     base = K.kvtc_workspace_bytes(len(short))
     assert c.staging_bytes(short) == 0
     assert c.decode_workspace_bytes(short) == base
     T = w.sink + w.window + 33                     # 33 compressed rows: two blocks
-    jobs = short + [K.make_job(0, 0, T, 16, 16, 1 << 20)]
+    jobs = short + [K.make_job(0, 0, T, 16, 16, 1 << 20, src_capacity=1 << 20)]
     blocks = 256 * ((2 * (ks * 1024 + 128) + 255) // 256)
     assert c.staging_bytes(jobs) == blocks
     assert c.decode_workspace_bytes(jobs) == K.kvtc_workspace_bytes(len(jobs)) + blocks
-    assert c.decode_workspace_bytes([K.make_job(0, 1, T, 16, 16, 1 << 20)]) == 0   # V never calibrated
+    assert c.decode_workspace_bytes([K.make_job(0, 1, T, 16, 16, 1 << 20, src_capacity=1 << 20)]) == 0   # V never calibrated
