@@ -16,6 +16,9 @@ encode and the decode inside the timed region. value = bf16 KV bytes per
 step / step time. After the timed steps the same two stages are timed with
 an event between them (the per-kernel breakdown), and kvtc_decode with only
 the status words (the single-launch fused schedule) is timed on its own.
+Then the online encode: layer l + 1's K and V are produced (a bf16 GEMM per
+tensor standing in for the model's projections) on one stream while layer l
+is encoded on another (`online_encode`).
 For a paged workload (qwen25_7b_paged) the decode is the layer-by-layer
 two-stream pipeline: stage 1 (unpack) of layer l+1 runs on one stream while
 stage 2 (restore into the paged cache) of layer l runs on another. The
@@ -350,6 +353,8 @@ def main():
     }
     if pipe is not None:
         result["pipeline"] = pipe.overlap(stream)
+    else:
+        result["online_encode"] = online_encode(K, codec, jobs, sizes, offs, T, F, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(codec, w, jobs[: args.cpu_sample], xs, K)
     print(json.dumps(result), flush=True)
@@ -430,6 +435,87 @@ class Pipeline:
         t_p = float(np.median(times))
         return {"unpack_ms": round(float(t_u), 4), "restore_ms": round(float(t_r), 4),
                 "pipelined_ms": round(t_p, 4), "overlap": round(float(t_u + t_r) / t_p, 3)}
+
+
+def online_encode(K, codec, jobs, sizes, offs, T, F, dev, stream, hidden=4096, reps=3, enc_wgs=32):
+    """Layer-by-layer encode overlapped with KV production: a producer (a bf16
+    GEMM of [T, hidden] states by a [hidden, F] projection per tensor, torch,
+    standing in for the model's K and V projections) writes layer l + 1 on
+    one stream while kvtc_encode compresses layer l on another. Reported: the
+    producer alone, the per-layer encodes alone and back to back, the two
+    streams together (the encode with its full persistent grid, and capped
+    at enc_wgs workgroups so that most of the chip stays with the producer),
+    and the share of the encode time the overlap hides."""
+    import torch
+    layers = sorted({l for l, _, _ in jobs})
+    idx = {l: [i for i, (jl, _, _) in enumerate(jobs) if jl == l] for l in layers}
+    g = torch.Generator(device=dev).manual_seed(3)
+    h = torch.randn((T, hidden), generator=g, device=dev).to(torch.bfloat16)
+    wts = (torch.randn((len(jobs), hidden, F), generator=g, device=dev) * hidden ** -0.5).to(torch.bfloat16)
+    kv = torch.empty((len(jobs), T, F), dtype=torch.bfloat16, device=dev)
+    sbuf = torch.empty(int(offs[-1]), dtype=torch.uint8, device=dev)
+    ljobs = {l: [K.make_job(jobs[i][0], jobs[i][1], T, kv[i], sbuf.data_ptr() + int(offs[i]), sizes[i])
+                 for i in idx[l]] for l in layers}
+    ws = {l: torch.zeros(K.kvtc_workspace_bytes(len(idx[l])) // 4, dtype=torch.int32, device=dev)
+          for l in layers}
+    sp, se = torch.cuda.Stream(), torch.cuda.Stream()
+    ev = {l: torch.cuda.Event() for l in layers}
+
+    def produce(l):
+        for i in idx[l]:
+            torch.matmul(h, wts[i], out=kv[i])
+
+    def timed(fn):
+        t = []
+        for _ in range(reps + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b))
+        return float(np.median(t[1:]))
+
+    def pipelined(p_s, e_s):
+        start = torch.cuda.Event()
+        start.record(stream)
+        p_s.wait_event(start)
+        e_s.wait_event(start)
+        for l in layers:
+            with torch.cuda.stream(p_s):
+                produce(l)
+                ev[l].record(p_s)
+            e_s.wait_event(ev[l])
+            codec.encode(ljobs[l], ws[l], e_s)
+        stream.wait_stream(e_s)
+        stream.wait_stream(p_s)
+
+    def capped(fn, cap):
+        old = os.environ.get("KVTC_MAX_WORKGROUPS")
+        os.environ["KVTC_MAX_WORKGROUPS"] = str(cap)
+        try:
+            return fn()
+        finally:
+            if old is None:
+                del os.environ["KVTC_MAX_WORKGROUPS"]
+            else:
+                os.environ["KVTC_MAX_WORKGROUPS"] = old
+
+    t_prod = timed(lambda: [produce(l) for l in layers])
+    t_enc = timed(lambda: [codec.encode(ljobs[l], ws[l], stream) for l in layers])
+    t_seq = timed(lambda: [(produce(l), codec.encode(ljobs[l], ws[l], stream)) for l in layers])
+    t_pipe = timed(lambda: pipelined(sp, se))
+    t_pipe_m = capped(lambda: timed(lambda: pipelined(sp, se)), enc_wgs)
+    for l in layers:
+        if np.any(K.kvtc_read_device_status(ws[l], len(idx[l]), stream) != 0):
+            raise SystemExit("device status errors in the online encode")
+    best = min(t_pipe, t_pipe_m)
+    return {"layers": len(layers), "producer": f"bf16 GEMM [{T} x {hidden}] x [{hidden} x {F}] per tensor",
+            "producer_ms": round(t_prod, 4), "encode_ms": round(t_enc, 4), "sequential_ms": round(t_seq, 4),
+            "pipelined_ms": round(t_pipe, 4),
+            f"pipelined_encode_{enc_wgs}_workgroups_ms": round(t_pipe_m, 4),
+            "overlap": round(t_seq / best, 3), "encode_hidden": round((t_seq - best) / t_enc, 3)}
 
 
 def measured_traffic(kernel, workload):
