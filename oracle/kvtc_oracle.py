@@ -47,6 +47,23 @@ choice below is marked READING and is the plainest one the text supports:
   Z0  a dropped (0-bit) component decodes to 0, so it adds nothing to the mean.
   Z1  DEFLATE is zlib level 6 over the whole stream, for the ratio only.
 
+Calibration of a set of tensors at once (calibrate_set), for the page's
+claims that one basis serves several layers and heads (section 3, second
+contribution) and that the DP places bits where they lower the error most
+(section 2A):
+  P1s shared basis: the tensors of one kind (K or V) in the set share one
+      basis V, the PCA of their pooled rows, each tensor's rows centred on its
+      own mean first; each tensor keeps its own mean, distortion table and
+      widths.
+  Q6g global budget: the widths of every tensor in the set are chosen
+      together, minimising the sum of their distortions subject to the sum of
+      their bits per token being at most (number of tensors) * B; every tensor
+      compresses the same tokens, so this is the same total size as B each.
+      A tensor may hold at most max_active active groups (the library's
+      records index at most 256 components).
+  Q7g ties of the global allocation: fewest total bits, then the most bits to
+      the tensor earliest in (layer, kind) order, then Q7 inside each tensor.
+
 Byte formats (all little-endian):
 
   artifact  = "KVTA" u32 version, i32 n_layers, kv_heads, head_dim, sink,
@@ -377,6 +394,142 @@ def dp_allocate(D: np.ndarray, G: int, budget: int) -> np.ndarray:
         else:
             raise OracleError("DP reconstruction failed")
     return widths
+
+
+def slot_dp_table(D: np.ndarray, G: int, max_bits_used: int, max_active: int) -> np.ndarray:
+    """f[g, u, r] = least distortion of groups g.. of one tensor spending
+    exactly u bits with at most r active groups (used by dp_allocate_global).
+
+    Same recurrence and nesting as dp_allocate, f[g][u][r] = min_b D[g, b] +
+    f[g+1][u - cost(b)][r - (b > 0)], evaluated for every u at once."""
+    n_g, nb = D.shape
+    U = max_bits_used
+    f = np.full((n_g + 1, U + 1, max_active + 1), np.inf)
+    f[n_g, 0, :] = 0.0
+    for g in range(n_g - 1, -1, -1):
+        for r in range(max_active + 1):
+            best = np.full(U + 1, np.inf)
+            for b in range(nb):
+                c, rr = group_cost(b, G), r - (1 if b > 0 else 0)
+                if rr < 0 or c > U:
+                    continue
+                cand = np.full(U + 1, np.inf)
+                cand[c:] = D[g, b] + f[g + 1, : U + 1 - c, rr]
+                best = np.minimum(best, cand)
+            f[g, :, r] = best
+    return f
+
+
+def dp_allocate_global(Ds, G: int, budget_per_tensor: int, max_active: int):
+    """Widths of several tensors chosen together (readings Q6g, Q7g).
+
+    Ds: the distortion tables D[g, b] of the tensors, in (layer, kind) order.
+    Minimises sum_s sum_g D_s[g, b_sg] subject to sum_s sum_g cost(b_sg) <=
+    len(Ds) * budget_per_tensor and at most max_active active groups per
+    tensor.  e_s[u] = f_s[0, u, max_active] is tensor s's least distortion at
+    exactly u bits; H[s][U] = min_u e_s[u] + H[s+1][U - u] combines them."""
+    S = len(Ds)
+    B = S * budget_per_tensor
+    if budget_per_tensor < 0 or max_active < 0:
+        raise OracleError("negative budget or cap")
+    tables, es = [], []
+    for D in Ds:
+        n_g, nb = D.shape
+        top = min(B, min(n_g, max_active) * group_cost(nb - 1, G))
+        f = slot_dp_table(D, G, top, max_active)
+        tables.append(f)
+        es.append(f[0, :, max_active])
+    H = np.full((S + 1, B + 1), np.inf)
+    H[S, 0] = 0.0
+    for s in range(S - 1, -1, -1):
+        for u, e in enumerate(es[s]):
+            if e < np.inf:
+                H[s, u:] = np.minimum(H[s, u:], e + H[s + 1, : B + 1 - u])
+    U = int(np.argmin(H[0]))                   # first minimum = fewest bits
+    out = []
+    for s in range(S):
+        e, f, D = es[s], tables[s], Ds[s]
+        for u in range(min(U, e.size - 1), -1, -1):      # most bits to the earlier tensor
+            if e[u] < np.inf and e[u] + H[s + 1, U - u] == H[s, U]:
+                break
+        else:
+            raise OracleError("global DP reconstruction failed (tensor level)")
+        U -= u
+        n_g, nb = D.shape
+        w = np.zeros(n_g, np.uint8)
+        r = max_active
+        for g in range(n_g):
+            for b in range(nb - 1, -1, -1):              # largest width first (Q7)
+                c, rr = group_cost(b, G), r - (1 if b > 0 else 0)
+                if c <= u and rr >= 0 and D[g, b] + f[g + 1, u - c, rr] == f[g, u, r]:
+                    w[g] = b
+                    u, r = u - c, rr
+                    break
+            else:
+                raise OracleError("global DP reconstruction failed (group level)")
+        out.append(w)
+    return out
+
+
+def shared_pca(rows_list):
+    """One basis for several tensors (reading P1s): every tensor's rows are
+    centred on that tensor's own mean, then pooled, then pca_basis."""
+    return pca_basis(np.vstack([r - r.mean(axis=0) for r in rows_list]))
+
+
+def _make_slot(layer, kind, params: Params, mu, V, lam, D, widths) -> Slot:
+    G = params.group
+    cols = np.concatenate([np.arange(g * G, (g + 1) * G) for g in np.nonzero(widths)[0]]
+                          ) if np.any(widths) else np.zeros(0, np.int64)
+    return Slot(layer, kind, params.F, G, np.asarray(widths, np.uint8), mu.astype(np.float32),
+                lam, V[:, cols].astype(np.float32), mu64=mu, V64=V, D=D)
+
+
+def calibrate_set(inputs, params: Params, shared_basis: bool = False,
+                  global_budget: bool = False, max_active: int | None = None) -> dict:
+    """Calibrate several tensors at once (readings P1s, Q6g, Q7g).
+
+    inputs: (layer, kind, x_cal [n, F]) triples, at most one per (layer, kind).
+    shared_basis: one PCA basis per kind over the pooled rows of its tensors,
+    each centred on its own mean.  global_budget: widths from
+    dp_allocate_global with at most max_active active groups per tensor (no cap
+    if None).  Without either flag every tensor is calibrate()'s result.
+    Returns {(layer, kind): Slot}."""
+    params.check()
+    prep = {}
+    for layer, kind, x_cal in inputs:
+        x = np.asarray(x_cal, np.float64)
+        n, F = x.shape
+        if F != params.F:
+            raise OracleError("feature count mismatch")
+        if (layer, kind) in prep:
+            raise OracleError("a (layer, kind) appears twice")
+        rows = x[params.sink: n - params.window]                 # R1
+        if rows.shape[0] < 1:
+            raise OracleError("no calibration rows after sink and window")
+        prep[(layer, kind)] = rows
+    keys = sorted(prep)
+    mus = {k: prep[k].mean(axis=0) for k in keys}
+    basis = {}
+    if shared_basis:
+        for kind in sorted({k for _, k in keys}):
+            same = [key for key in keys if key[1] == kind]
+            Vl = shared_pca([prep[key] for key in same])
+            for key in same:
+                basis[key] = Vl
+    else:
+        for key in keys:
+            basis[key] = pca_basis(prep[key] - mus[key])
+    D = {key: distortion_table((prep[key] - mus[key]) @ basis[key][0], params.group,
+                               params.max_bits) for key in keys}
+    if global_budget:
+        cap = params.n_groups if max_active is None else max_active
+        ws = dict(zip(keys, dp_allocate_global([D[k] for k in keys], params.group,
+                                               params.budget_bits, cap)))
+    else:
+        ws = {k: dp_allocate(D[k], params.group, params.budget_bits) for k in keys}
+    return {k: _make_slot(k[0], k[1], params, mus[k], basis[k][0], basis[k][1], D[k], ws[k])
+            for k in keys}
 
 
 def calibrate(x_cal: np.ndarray, params: Params, layer: int, kind: int) -> Slot:

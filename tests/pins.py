@@ -85,6 +85,33 @@ def brute_force_widths(D, G, budget):
     return ws[i].astype(np.uint8), obj[i]
 
 
+def brute_force_global(Ds, G, budget, cap):
+    """Every width vector of every tensor at once (equal group counts), kept
+    if each tensor has at most cap active groups and the bits sum to at most
+    len(Ds) * budget, ordered by (objective, total bits, most bits to earlier
+    tensors, lexicographically largest widths).  D values must be exact
+    binary fractions so no summation order matters."""
+    S, (n_g, nb) = len(Ds), Ds[0].shape
+    ws = np.array(list(itertools.product(range(nb), repeat=S * n_g)), np.int64).reshape(-1, S, n_g)
+    bits = np.sum(G * ws + 64 * (ws > 0), axis=2)                    # [N, S]
+    obj = sum(np.sum(Ds[s][np.arange(n_g), ws[:, s]], axis=1) for s in range(S))
+    ok = (np.sum(bits, axis=1) <= S * budget) & np.all(np.sum(ws > 0, axis=2) <= cap, axis=1)
+    ws, bits, obj = ws[ok], bits[ok], obj[ok]
+    flat = ws.reshape(len(ws), -1)
+    keys = ([-flat[:, i] for i in range(S * n_g - 1, -1, -1)]
+            + [-bits[:, s] for s in range(S - 1, -1, -1)] + [np.sum(bits, axis=1), obj])
+    i = np.lexsort(keys)[0]
+    return [ws[i, s].astype(np.uint8) for s in range(S)], obj[i]
+
+
+def three_scaled_tensors():
+    """Three family-B-like tensors of very different energy (scales 1, 4, 1/4)."""
+    x, _ = family_b_small(seed=12, n=1500)
+    y, _ = family_b_small(seed=13, n=1500)
+    z, _ = family_b_small(seed=14, n=1500)
+    return [(0, 0, x), (1, 0, 4 * y), (0, 1, z / 4)]
+
+
 # ------------------------------------------------------------------- pins ---
 
 def check_bf16_vs_torch():
@@ -245,6 +272,91 @@ def check_dp_bruteforce():
         assert obj <= prev + 1e-12
         assert sum(16 * int(b) + (64 if b else 0) for b in w) <= budget
         prev = obj
+
+
+def check_dp_global_bruteforce():
+    """The global allocation (several tensors, one budget, a cap on active
+    groups per tensor) against brute force, ties included."""
+    rng = np.random.default_rng(11)
+    for trial in range(24):
+        S = int(rng.integers(1, 4))
+        n_g = 1 if S == 3 else int(rng.integers(1, 3))
+        nb = int(rng.integers(2, 5))
+        G = int(rng.choice([8, 16]))
+        Ds = []
+        for _ in range(S):
+            e = np.sort(rng.uniform(0, 50, n_g))[::-1]
+            Ds.append(np.array([[np.round(e[g] * 4.0 ** -b * 64) / 64 for b in range(nb)]
+                                for g in range(n_g)]))
+        if trial % 4 == 1 and S > 1:
+            Ds[1] = Ds[0].copy()                # identical tensors: a tie between tensors
+        if trial % 6 == 2:
+            Ds[-1][:] = 0.0
+        for budget in (0, 60, 72, 100, 180):
+            for cap in (0, 1, 2):
+                ws = O.dp_allocate_global(Ds, G, budget, cap)
+                bw, _ = brute_force_global(Ds, G, budget, cap)
+                assert all(np.array_equal(a, b) for a, b in zip(ws, bw)), (trial, budget, cap, ws, bw)
+    # one tensor and no binding cap: the per-tensor DP
+    gd = golden("dp_examples.json")
+    D = np.array(gd["D"])
+    for case in gd["cases"]:
+        (w,) = O.dp_allocate_global([D], gd["G"], case["budget"], D.shape[0])
+        assert w.tolist() == case["widths"], (case, w)
+
+
+def check_global_budget_moves_bits():
+    """One budget over three tensors of very different energy: never worse
+    than a budget per tensor, strictly better here, within the total bits
+    and the cap."""
+    p = small_params(F=64, G=16, bpv=2.0)
+    ins = three_scaled_tensors()
+    per = O.calibrate_set(ins, p)
+    glob = O.calibrate_set(ins, p, global_budget=True, max_active=2)
+    obj = lambda sl: sum(sl.D[g, b] for g, b in enumerate(sl.widths))
+    bits = lambda sl: sum(16 * int(b) + (64 if b else 0) for b in sl.widths)
+    o_per = sum(obj(sl) for sl in per.values())
+    o_glob = sum(obj(sl) for sl in glob.values())
+    assert o_glob < 0.9 * o_per, (o_glob, o_per)
+    assert sum(bits(sl) for sl in glob.values()) <= 3 * p.budget_bits
+    assert all(sl.n_act <= 2 for sl in glob.values())
+    big = glob[(1, 0)]
+    assert bits(big) > p.budget_bits and bits(glob[(0, 1)]) < p.budget_bits
+    for k, sl in per.items():                 # without the flag: calibrate() per tensor
+        ref = O.calibrate(ins[[i[:2] for i in ins].index(k)][2], p, *k)
+        assert np.array_equal(sl.widths, ref.widths) and np.array_equal(sl.V32, ref.V32)
+
+
+def check_shared_basis():
+    """A basis shared by the tensors of one kind: a single tensor gives
+    calibrate()'s slot; a copy of a tensor shifted by a constant row gives
+    the same basis and its own mean; for different tensors the eigenvalues
+    are those of the summed scatter matrices (numpy eigh); K and V are never
+    pooled together."""
+    p = small_params(F=64, G=16, bpv=2.0)
+    x, _ = family_b_small(seed=4, n=1500)
+    one = O.calibrate_set([(0, 0, x)], p, shared_basis=True)[(0, 0)]
+    ref = O.calibrate(x, p, 0, 0)
+    assert np.array_equal(one.V32, ref.V32) and np.array_equal(one.mu32, ref.mu32)
+    off = np.round(np.random.default_rng(2).standard_normal(64) * 8) * 0.5
+    x2 = x.astype(np.float64) + off
+    pair = O.calibrate_set([(0, 0, x), (1, 0, x2)], p, shared_basis=True)
+    k = 12                                    # the planted rank; the gap after it is huge
+    for sl in pair.values():
+        Pa, Pb = sl.V64[:, :k] @ sl.V64[:, :k].T, ref.V64[:, :k] @ ref.V64[:, :k].T
+        assert np.abs(Pa - Pb).max() < 1e-8
+        assert np.allclose(sl.lam[:k], ref.lam[:k], rtol=1e-9)
+    assert np.array_equal(pair[(1, 0)].mu32, O.calibrate(x2, p, 1, 0).mu32)
+    y, _ = family_b_small(seed=9, n=1200)
+    z, _ = family_b_small(seed=10, n=1000)
+    mix = O.calibrate_set([(0, 0, x), (1, 0, y), (0, 1, z)], p, shared_basis=True)
+    rows = [r[p.sink: len(r) - p.window].astype(np.float64) for r in (x, y)]
+    scat = sum((r - r.mean(axis=0)).T @ (r - r.mean(axis=0)) for r in rows)
+    ev = np.linalg.eigvalsh(scat / sum(len(r) for r in rows))[::-1]
+    for key in ((0, 0), (1, 0)):
+        assert np.allclose(mix[key].lam[:24], ev[:24], rtol=1e-8, atol=1e-12 * ev[0])
+    assert np.array_equal(mix[(0, 0)].V32, mix[(1, 0)].V32)
+    assert np.array_equal(mix[(0, 1)].V32, O.calibrate(z, p, 0, 1).V32)
 
 
 def check_projection_exact():

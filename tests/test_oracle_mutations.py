@@ -147,7 +147,47 @@ def _deflate_ratios_swapped(stream, raw_bytes):
     return b, a, z
 
 
+def _global_latest_first(Ds, G, budget, max_active):
+    """Ties between tensors resolved toward the last tensor."""
+    return _orig["dp_allocate_global"](Ds[::-1], G, budget, max_active)[::-1]
+
+
+def _global_cap_ignored(Ds, G, budget, max_active):
+    return _orig["dp_allocate_global"](Ds, G, budget, max(D.shape[0] for D in Ds))
+
+
+def _global_per_tensor(Ds, G, budget, max_active):
+    return [O.dp_allocate(D, G, budget) for D in Ds]
+
+
+def _shared_pooled_mean(rows_list):
+    x = np.vstack(rows_list)
+    return O.pca_basis(x - x.mean(axis=0))
+
+
+def _shared_first_only(rows_list):
+    return O.pca_basis(rows_list[0] - rows_list[0].mean(axis=0))
+
+
+def _calibrate_set_kinds_pooled(inputs, params, shared_basis=False, global_budget=False,
+                                max_active=None):
+    """K and V pooled into one shared basis."""
+    out = _orig["calibrate_set"]([(2 * l + k, 0, x) for l, k, x in inputs], params,
+                                 shared_basis, global_budget, max_active)
+    res = {}
+    for (lk, _), sl in out.items():
+        sl.layer, sl.kind = lk // 2, lk % 2
+        res[(lk // 2, lk % 2)] = sl
+    return res
+
+
 MUTATIONS = {
+    "global_ties_to_last_tensor": ("dp_allocate_global", _global_latest_first),
+    "global_cap_ignored": ("dp_allocate_global", _global_cap_ignored),
+    "global_budget_per_tensor": ("dp_allocate_global", _global_per_tensor),
+    "shared_basis_pooled_mean": ("shared_pca", _shared_pooled_mean),
+    "shared_basis_first_tensor": ("shared_pca", _shared_first_only),
+    "shared_basis_kinds_pooled": ("calibrate_set", _calibrate_set_kinds_pooled),
     "deflate_level9": ("deflate_ratio", _deflate_level9),
     "deflate_ratios_swapped": ("deflate_ratio", _deflate_ratios_swapped),
     "no_centering": ("project", _project_no_centering),
