@@ -165,6 +165,43 @@ void kvtc_destroy(kvtc_codec* codec);
 kvtc_status kvtc_calibrate(kvtc_codec* codec, int32_t layer, int32_t kind,
                            const void* host_kv, int64_t n_tokens, int32_t threads);
 
+/* One tensor of a calibration set: [n_tokens, F] rows in params.dtype
+ * storage, host memory, read only. */
+typedef struct {
+  int32_t layer;
+  int32_t kind;
+  const void* host_kv;
+  int64_t n_tokens;
+} kvtc_calib_input;
+
+/* kvtc_calibrate_set flags. */
+#define KVTC_CAL_SHARED_BASIS 1u  /* one basis per kind across the set's layers */
+#define KVTC_CAL_GLOBAL_BUDGET 2u /* one bit budget across the whole set */
+
+/* Calibrate several (layer, kind) tensors in one call. The page on KV cache
+ * transform coding finds one PCA basis reusable across layers and heads
+ * (section 3, contributions) and places bits by a DP under a budget (section
+ * 2A); the two flags apply these across tensors:
+ *   KVTC_CAL_SHARED_BASIS: the tensors of one kind share one basis, the
+ *     eigenvectors of the sum of their scatter matrices over the total row
+ *     count, each tensor's rows [s, n - w) centred on its own mean first.
+ *     Every tensor keeps its own mean, distortion table and widths; each
+ *     slot stores its own copy of the basis, so streams, kernels and the
+ *     artifact format are unchanged.
+ *   KVTC_CAL_GLOBAL_BUDGET: the widths of all tensors are chosen together,
+ *     minimising the sum of their distortion tables subject to the sum of
+ *     their bits per token being at most n * floor(bits_per_value * F), with
+ *     at most KVTC_MAX_REFF / G active groups per tensor. Ties: fewest total
+ *     bits, then the most bits to the tensor earliest in (layer, kind) order,
+ *     then kvtc_calibrate's rule inside each tensor.
+ * With no flag each tensor gets exactly kvtc_calibrate's result. A (layer,
+ * kind) may appear at most once; the call is all or nothing (on error no slot
+ * changes). Errors: KVTC_E_INVALID (bad arguments, unknown flags, too few
+ * rows, duplicates), KVTC_E_UNSUPPORTED (without the global budget, a tensor
+ * needing more than KVTC_MAX_REFF components). */
+kvtc_status kvtc_calibrate_set(kvtc_codec* codec, const kvtc_calib_input* inputs, int32_t n,
+                               uint32_t flags, int32_t threads);
+
 kvtc_status kvtc_slot_info_get(const kvtc_codec* codec, int32_t layer, int32_t kind,
                                kvtc_slot_info* info);
 

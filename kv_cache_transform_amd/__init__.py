@@ -22,12 +22,18 @@ KVTC_F32, KVTC_BF16 = 0, 1
 KVTC_K, KVTC_V = 0, 1
 KVTC_MAX_REFF = 256
 KVTC_MAX_JOBS = 4096
+KVTC_CAL_SHARED_BASIS, KVTC_CAL_GLOBAL_BUDGET = 1, 2
 
 
 class kvtc_params(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("sink", C.c_int32), ("window", C.c_int32), ("group", C.c_int32),
                 ("max_bits", C.c_int32), ("bits_per_value", C.c_float), ("dtype", C.c_int32)]
+
+
+class kvtc_calib_input(C.Structure):
+    _fields_ = [("layer", C.c_int32), ("kind", C.c_int32), ("host_kv", C.c_void_p),
+                ("n_tokens", C.c_int64)]
 
 
 class kvtc_job(C.Structure):
@@ -67,6 +73,7 @@ def lib():
         "kvtc_create": (st, [C.POINTER(kvtc_params), C.POINTER(vp)]),
         "kvtc_destroy": (None, [vp]),
         "kvtc_calibrate": (st, [vp, i32, i32, vp, i64, i32]),
+        "kvtc_calibrate_set": (st, [vp, C.POINTER(kvtc_calib_input), i32, C.c_uint32, i32]),
         "kvtc_slot_info_get": (st, [vp, i32, i32, C.POINTER(kvtc_slot_info)]),
         "kvtc_save": (st, [vp, vp, sz, C.POINTER(sz)]),
         "kvtc_load": (st, [vp, sz, C.POINTER(vp)]),
@@ -157,6 +164,15 @@ def kvtc_destroy(codec: int) -> None:
 def kvtc_calibrate(codec: int, layer: int, kind: int, host_kv: np.ndarray, threads: int = 0) -> None:
     a = np.ascontiguousarray(host_kv)
     _check(lib().kvtc_calibrate(codec, layer, kind, a.ctypes.data, a.shape[0], threads))
+
+
+def kvtc_calibrate_set(codec: int, inputs, flags: int = 0, threads: int = 0) -> None:
+    """inputs: (layer, kind, host_kv [n, F]) triples."""
+    arrs = [np.ascontiguousarray(x) for _, _, x in inputs]
+    arr = (kvtc_calib_input * max(1, len(arrs)))()
+    for i, ((layer, kind, _), a) in enumerate(zip(inputs, arrs)):
+        arr[i] = kvtc_calib_input(layer, kind, a.ctypes.data, a.shape[0])
+    _check(lib().kvtc_calibrate_set(codec, arr, len(arrs), flags, threads))
 
 
 def kvtc_slot_info_get(codec: int, layer: int, kind: int) -> kvtc_slot_info:
@@ -280,6 +296,9 @@ class Codec:
 
     def calibrate(self, layer, kind, host_kv, threads=0):
         kvtc_calibrate(self.h, layer, kind, host_kv, threads)
+
+    def calibrate_set(self, inputs, flags=0, threads=0):
+        kvtc_calibrate_set(self.h, inputs, flags, threads)
 
     def slot(self, layer, kind) -> kvtc_slot_info:
         return kvtc_slot_info_get(self.h, layer, kind)

@@ -197,6 +197,240 @@ void finish_slot(const kvtc_params& p, int layer, int kind, Slot& s) {
   s.calibrated = true;
 }
 
+// Global allocation over several tensors sharing one budget: minimise the
+// sum of their distortions subject to sum of their bits <= n * budget and at
+// most max_active active groups per tensor. Costs are multiples of
+// unit = gcd(G, 64) bits, so the tables run in units. Per tensor,
+// f[g][u][r] = least distortion of groups g.. spending exactly u units with
+// at most r active groups (the per-tensor recurrence with a count of active
+// groups); e_s[u] = f_s[0][u][cap]; H[s][U] = min_u e_s[u] + H[s+1][U - u].
+// Ties: fewest total bits, then the most bits to the tensor earliest in the
+// list, then the per-tensor rule (largest b first).
+struct CapTable {
+  int n_g, top, cap;
+  std::vector<double> f;
+  double& at(int g, long u, int r) { return f[((size_t)g * (top + 1) + u) * (cap + 1) + r]; }
+};
+
+void cap_table(const std::vector<double>& D, int n_g, int nb, int G, int unit, int top, int cap,
+               CapTable& t) {
+  const double INF = std::numeric_limits<double>::infinity();
+  t.n_g = n_g;
+  t.top = top;
+  t.cap = cap;
+  t.f.assign((size_t)(n_g + 1) * (top + 1) * (cap + 1), INF);
+  for (int r = 0; r <= cap; ++r) t.at(n_g, 0, r) = 0.0;
+  for (int g = n_g - 1; g >= 0; --g)
+    for (int r = 0; r <= cap; ++r)
+      for (long u = 0; u <= top; ++u) {
+        double best = INF;
+        for (int b = 0; b < nb; ++b) {
+          const long c = group_cost(b, G) / unit;
+          const int rr = r - (b > 0 ? 1 : 0);
+          if (rr < 0 || c > u) continue;
+          const double v = D[(size_t)g * nb + b] + t.at(g + 1, u - c, rr);
+          if (v < best) best = v;
+        }
+        t.at(g, u, r) = best;
+      }
+}
+
+std::vector<std::vector<uint8_t>> dp_allocate_global(const std::vector<std::vector<double>>& Ds, int n_g,
+                                                     int nb, int G, long budget, int max_active) {
+  const double INF = std::numeric_limits<double>::infinity();
+  const int S = (int)Ds.size();
+  int unit = kScaleBits;
+  while (G % unit) unit /= 2;                  // gcd(G, 64); G is a multiple of 8
+  const long Bu = (long)S * budget / unit;
+  const int cap = std::min(max_active, n_g);
+  const int top = (int)std::min<long>(Bu, (long)cap * group_cost(nb - 1, G) / unit);
+  std::vector<std::vector<double>> e(S);
+  CapTable t;
+  for (int s = 0; s < S; ++s) {
+    cap_table(Ds[s], n_g, nb, G, unit, top, cap, t);
+    e[s].resize(top + 1);
+    for (int u = 0; u <= top; ++u) e[s][u] = t.at(0, u, cap);
+  }
+  std::vector<double> H((size_t)(S + 1) * (Bu + 1), INF);
+  auto h = [&](int s, long U) -> double& { return H[(size_t)s * (Bu + 1) + U]; };
+  h(S, 0) = 0.0;
+  for (int s = S - 1; s >= 0; --s)
+    for (int u = 0; u <= top; ++u) {
+      if (!(e[s][u] < INF)) continue;
+      for (long U = u; U <= Bu; ++U) {
+        const double v = e[s][u] + h(s + 1, U - u);
+        if (v < h(s, U)) h(s, U) = v;
+      }
+    }
+  long U = 0;
+  for (long v = 1; v <= Bu; ++v)
+    if (h(0, v) < h(0, U)) U = v;
+  std::vector<std::vector<uint8_t>> out(S, std::vector<uint8_t>(n_g, 0));
+  for (int s = 0; s < S; ++s) {
+    long u = std::min<long>(U, top);
+    for (; u >= 0; --u)
+      if (e[s][u] < INF && e[s][u] + h(s + 1, U - u) == h(s, U)) break;
+    if (u < 0) u = 0;                          // unreachable: H[s][U] came from some u
+    U -= u;
+    cap_table(Ds[s], n_g, nb, G, unit, top, cap, t);
+    int r = cap;
+    for (int g = 0; g < n_g; ++g)
+      for (int b = nb - 1; b >= 0; --b) {
+        const long c = group_cost(b, G) / unit;
+        const int rr = r - (b > 0 ? 1 : 0);
+        if (c <= u && rr >= 0 && Ds[s][(size_t)g * nb + b] + t.at(g + 1, u - c, rr) == t.at(g, u, r)) {
+          out[s][g] = (uint8_t)b;
+          u -= c;
+          r = rr;
+          break;
+        }
+      }
+  }
+  return out;
+}
+
+// Rows [s, n - w) of one calibration tensor in fp64, centred on their mean.
+struct CalRows {
+  long n_r = 0;
+  std::vector<double> X;    // [n_r][F], centred
+  std::vector<double> mu;   // [F]
+};
+
+kvtc_status load_centred(const kvtc_params& p, int F, const void* host_kv, int64_t n_tokens, int threads,
+                         CalRows& r) {
+  const long n_r = (long)n_tokens - p.sink - p.window;
+  if (n_tokens < 0 || n_r < 1) return fail(KVTC_E_INVALID, "need at least one row after sink and window");
+  r.n_r = n_r;
+  r.X.assign((size_t)n_r * F, 0.0);
+  parallel_for((int)std::min<long>(n_r, 1L << 30), threads, [&](int t) {
+    const size_t src_row = (size_t)(t + p.sink) * F;
+    double* xr = r.X.data() + (size_t)t * F;
+    if (p.dtype == KVTC_BF16) {
+      const uint16_t* s = (const uint16_t*)host_kv + src_row;
+      for (int f = 0; f < F; ++f) xr[f] = bf16_to_f32(s[f]);
+    } else {
+      const float* s = (const float*)host_kv + src_row;
+      for (int f = 0; f < F; ++f) xr[f] = s[f];
+    }
+  });
+  // Mean (section 2B subtracts it before the transform).
+  r.mu.assign(F, 0.0);
+  for (long t = 0; t < n_r; ++t) {
+    const double* xr = r.X.data() + (size_t)t * F;
+    for (int f = 0; f < F; ++f) r.mu[f] += xr[f];
+  }
+  for (int f = 0; f < F; ++f) r.mu[f] /= (double)n_r;
+  parallel_for((int)n_r, threads, [&](int t) {
+    double* xr = r.X.data() + (size_t)t * F;
+    for (int f = 0; f < F; ++f) xr[f] -= r.mu[f];
+  });
+  return KVTC_OK;
+}
+
+// cov += X^T X (upper triangle computed, then mirrored) of centred rows.
+void add_scatter(const CalRows& r, int F, int threads, std::vector<double>& cov) {
+  std::vector<double> sc((size_t)F * F);
+  gemm_f64(F, F, (int)r.n_r, r.X.data(), 1, F, r.X.data(), F, sc.data(), F, true, threads);
+  for (int i = 0; i < F; ++i)
+    for (int j = 0; j < i; ++j) sc[(size_t)i * F + j] = sc[(size_t)j * F + i];
+  for (size_t k = 0; k < sc.size(); ++k) cov[k] += sc[k];
+}
+
+// Eigenvectors of the scatter / n_rows: the right singular vectors of the
+// centred rows (the SVD of section 2A), eigenvalues sigma^2 / n, sorted by
+// descending eigenvalue (stable), largest-magnitude entry of each made
+// positive. V[f][j], column j = component j.
+kvtc_status eigen_basis(int F, std::vector<double>& cov, double n_rows, std::vector<double>& V,
+                        std::vector<double>& lam) {
+  for (auto& v : cov) v /= n_rows;
+  std::vector<double> evals, zt;
+  if (sym_eigen(F, cov, evals, zt) != 0) return fail(KVTC_E_INVALID, "eigensolver did not converge");
+  std::vector<int> order(F);
+  for (int j = 0; j < F; ++j) order[j] = j;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return evals[a] > evals[b]; });
+  V.assign((size_t)F * F, 0.0);
+  lam.assign(F, 0.0);
+  for (int j = 0; j < F; ++j) {
+    const double* z = zt.data() + (size_t)order[j] * F;
+    lam[j] = evals[order[j]];
+    int imax = 0;
+    for (int f = 1; f < F; ++f)
+      if (std::fabs(z[f]) > std::fabs(z[imax])) imax = f;
+    const double sgn = z[imax] < 0 ? -1.0 : 1.0;
+    for (int f = 0; f < F; ++f) V[(size_t)f * F + j] = sgn * z[f];
+  }
+  return KVTC_OK;
+}
+
+// Empirical distortion table D[g][b] of the quantizer on the calibration
+// coefficients C = X V (fp64).
+std::vector<double> distortion(const CalRows& r, int F, int G, int nb, const std::vector<double>& V,
+                               int threads) {
+  const long n_r = r.n_r;
+  const int n_g = F / G;
+  std::vector<double> C((size_t)n_r * F);
+  gemm_f64((int)n_r, F, F, r.X.data(), F, 1, V.data(), F, C.data(), F, false, threads);
+  std::vector<double> D((size_t)n_g * nb, 0.0);
+  parallel_for(n_g, threads, [&](int g) {
+    std::vector<double> acc(nb, 0.0);
+    for (long t = 0; t < n_r; ++t) {
+      const double* cg = C.data() + (size_t)t * F + (size_t)g * G;
+      double mn = cg[0], mx = cg[0], e0 = 0.0;
+      for (int i = 0; i < G; ++i) {
+        mn = std::min(mn, cg[i]);
+        mx = std::max(mx, cg[i]);
+        e0 += cg[i] * cg[i];
+      }
+      acc[0] += e0;
+      const double scale = mx - mn;
+      for (int b = 1; b < nb; ++b) {
+        if (!(scale > 0)) continue;  // every value equals the shift: no error
+        const double k = (double)((1 << b) - 1);
+        const double inv = k / scale, step = scale / k;
+        double e = 0.0;
+        for (int i = 0; i < G; ++i) {
+          double q = std::nearbyint((cg[i] - mn) * inv);
+          q = std::min(std::max(q, 0.0), k);
+          const double d = cg[i] - (mn + q * step);
+          e += d * d;
+        }
+        acc[b] += e;
+      }
+    }
+    for (int b = 0; b < nb; ++b) D[(size_t)g * nb + b] = acc[b] / (double)n_r;
+  });
+  return D;
+}
+
+std::vector<float> to_f32(const std::vector<double>& v) { return std::vector<float>(v.begin(), v.end()); }
+
+// A calibrated slot from its widths, mean, eigenvalues and full basis
+// (V[f][j] in fp32, F x F): the active groups' columns in component order.
+kvtc_status build_slot(const kvtc_params& p, int layer, int kind, const std::vector<uint8_t>& widths,
+                       const std::vector<double>& mu, const std::vector<double>& lam,
+                       const std::vector<float>& V, Slot& s) {
+  const int F = p.kv_heads * p.head_dim, G = p.group, n_g = F / G;
+  int n_act = 0;
+  for (int g = 0; g < n_g; ++g) n_act += widths[g] ? 1 : 0;
+  if (n_act * G > KVTC_MAX_REFF)
+    return fail(KVTC_E_UNSUPPORTED, "allocation needs more than KVTC_MAX_REFF active components");
+  s = Slot();
+  s.widths = widths;
+  s.mu32.resize(F);
+  for (int f = 0; f < F; ++f) s.mu32[f] = (float)mu[f];
+  s.lam = lam;
+  s.V32.resize((size_t)F * n_act * G);
+  int a = 0;
+  for (int g = 0; g < n_g; ++g) {
+    if (!widths[g]) continue;
+    for (int i = 0; i < G; ++i)
+      for (int f = 0; f < F; ++f) s.V32[(size_t)f * n_act * G + a * G + i] = V[(size_t)f * F + g * G + i];
+    ++a;
+  }
+  finish_slot(p, layer, kind, s);
+  return KVTC_OK;
+}
+
 bool slot_index(const kvtc_codec* c, int layer, int kind, int* idx) {
   if (!c || layer < 0 || layer >= c->p.n_layers || (kind != KVTC_K && kind != KVTC_V)) return false;
   *idx = layer * 2 + kind;
@@ -258,115 +492,119 @@ kvtc_status kvtc_calibrate(kvtc_codec* c, int32_t layer, int32_t kind, const voi
   int idx;
   if (!slot_index(c, layer, kind, &idx)) return fail(KVTC_E_INVALID, "bad codec, layer or kind");
   if (!host_kv) return fail(KVTC_E_INVALID, "null calibration data");
+  if (threads <= 0) threads = std::max(1u, std::thread::hardware_concurrency());
+  const kvtc_params& p = c->p;
+  const int F = c->F, nb = p.max_bits + 1;
+  CalRows r;
+  kvtc_status st = load_centred(p, F, host_kv, n_tokens, threads, r);
+  if (st != KVTC_OK) return st;
+  std::vector<double> cov((size_t)F * F, 0.0), V, lam;
+  add_scatter(r, F, threads, cov);
+  st = eigen_basis(F, cov, (double)r.n_r, V, lam);
+  if (st != KVTC_OK) return st;
+  const std::vector<double> D = distortion(r, F, p.group, nb, V, threads);
+  Slot s;
+  st = build_slot(p, layer, kind, dp_allocate(D, c->n_g, nb, p.group, budget_bits(p)), r.mu, lam,
+                  to_f32(V), s);
+  if (st != KVTC_OK) return st;
+  c->slots[idx] = std::move(s);
+  std::lock_guard<std::mutex> lk(c->mu);
+  ++c->calib_version;
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_calibrate_set(kvtc_codec* c, const kvtc_calib_input* in, int32_t n, uint32_t flags,
+                               int32_t threads) {
+  if (!c || !in || n < 1) return fail(KVTC_E_INVALID, "bad codec or inputs");
+  if (flags & ~(uint32_t)(KVTC_CAL_SHARED_BASIS | KVTC_CAL_GLOBAL_BUDGET))
+    return fail(KVTC_E_INVALID, "unknown calibration flags");
+  if (threads <= 0) threads = std::max(1u, std::thread::hardware_concurrency());
   const kvtc_params& p = c->p;
   const int F = c->F, G = p.group, n_g = c->n_g, nb = p.max_bits + 1;
-  const long n_r = (long)n_tokens - p.sink - p.window;
-  if (n_tokens < 0 || n_r < 1) return fail(KVTC_E_INVALID, "need at least one row after sink and window");
-  if (threads <= 0) threads = std::max(1u, std::thread::hardware_concurrency());
+  // Tensors in (layer, kind) order; each at most once.
+  std::vector<int> ord(n);
+  for (int i = 0; i < n; ++i) {
+    int idx;
+    if (!slot_index(c, in[i].layer, in[i].kind, &idx)) return fail(KVTC_E_INVALID, "bad layer or kind");
+    if (!in[i].host_kv) return fail(KVTC_E_INVALID, "null calibration data");
+    if (in[i].n_tokens - p.sink - p.window < 1)
+      return fail(KVTC_E_INVALID, "need at least one row after sink and window");
+    ord[i] = i;
+  }
+  auto key = [&](int i) { return in[i].layer * 2 + in[i].kind; };
+  std::sort(ord.begin(), ord.end(), [&](int a, int b) { return key(a) < key(b); });
+  for (int i = 1; i < n; ++i)
+    if (key(ord[i]) == key(ord[i - 1])) return fail(KVTC_E_INVALID, "a (layer, kind) appears twice");
 
-  // Rows [s, n - w) in fp64.
-  std::vector<double> X((size_t)n_r * F);
-  parallel_for((int)std::min<long>(n_r, 1L << 30), threads, [&](int t) {
-    const size_t src_row = (size_t)(t + p.sink) * F;
-    double* xr = X.data() + (size_t)t * F;
-    if (p.dtype == KVTC_BF16) {
-      const uint16_t* s = (const uint16_t*)host_kv + src_row;
-      for (int f = 0; f < F; ++f) xr[f] = bf16_to_f32(s[f]);
-    } else {
-      const float* s = (const float*)host_kv + src_row;
-      for (int f = 0; f < F; ++f) xr[f] = s[f];
-    }
-  });
-  // Mean (section 2B subtracts it before the transform).
-  std::vector<double> mu(F, 0.0);
-  for (long t = 0; t < n_r; ++t) {
-    const double* xr = X.data() + (size_t)t * F;
-    for (int f = 0; f < F; ++f) mu[f] += xr[f];
-  }
-  for (int f = 0; f < F; ++f) mu[f] /= (double)n_r;
-  parallel_for((int)n_r, threads, [&](int t) {
-    double* xr = X.data() + (size_t)t * F;
-    for (int f = 0; f < F; ++f) xr[f] -= mu[f];
-  });
-  // Covariance; its eigenvectors are the right singular vectors of the
-  // centred rows (the SVD of section 2A) and its eigenvalues are sigma^2/n.
-  std::vector<double> cov((size_t)F * F);
-  gemm_f64(F, F, (int)n_r, X.data(), 1, F, X.data(), F, cov.data(), F, true, threads);
-  for (int i = 0; i < F; ++i)
-    for (int j = 0; j < i; ++j) cov[(size_t)i * F + j] = cov[(size_t)j * F + i];
-  for (auto& v : cov) v /= (double)n_r;
-  std::vector<double> evals, zt;
-  if (sym_eigen(F, cov, evals, zt) != 0) return fail(KVTC_E_INVALID, "eigensolver did not converge");
-  std::vector<int> order(F);
-  for (int j = 0; j < F; ++j) order[j] = j;
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return evals[a] > evals[b]; });
-  std::vector<double> V((size_t)F * F);  // V[f][j], column j = component j
-  std::vector<double> lam(F);
-  for (int j = 0; j < F; ++j) {
-    const double* z = zt.data() + (size_t)order[j] * F;
-    lam[j] = evals[order[j]];
-    int imax = 0;
-    for (int f = 1; f < F; ++f)
-      if (std::fabs(z[f]) > std::fabs(z[imax])) imax = f;
-    const double sgn = z[imax] < 0 ? -1.0 : 1.0;
-    for (int f = 0; f < F; ++f) V[(size_t)f * F + j] = sgn * z[f];
-  }
-  // Calibration coefficients and the empirical distortion table.
-  std::vector<double> C((size_t)n_r * F);
-  gemm_f64((int)n_r, F, F, X.data(), F, 1, V.data(), F, C.data(), F, false, threads);
-  X.clear();
-  X.shrink_to_fit();
-  std::vector<double> D((size_t)n_g * nb, 0.0);
-  parallel_for(n_g, threads, [&](int g) {
-    std::vector<double> acc(nb, 0.0);
-    for (long t = 0; t < n_r; ++t) {
-      const double* cg = C.data() + (size_t)t * F + (size_t)g * G;
-      double mn = cg[0], mx = cg[0], e0 = 0.0;
-      for (int i = 0; i < G; ++i) {
-        mn = std::min(mn, cg[i]);
-        mx = std::max(mx, cg[i]);
-        e0 += cg[i] * cg[i];
+  // Means, bases and distortion tables.
+  std::vector<std::vector<double>> mus(n), lams(n), Ds(n);
+  std::vector<std::vector<float>> Vs(n);        // per tensor, or per kind when shared
+  std::vector<int> vref(n);                     // which entry of Vs / lams a tensor uses
+  if (flags & KVTC_CAL_SHARED_BASIS) {
+    for (int kind = 0; kind < 2; ++kind) {
+      std::vector<int> same;
+      for (int i : ord)
+        if (in[i].kind == kind) same.push_back(i);
+      if (same.empty()) continue;
+      // one basis over the pooled rows, each tensor centred on its own mean
+      std::vector<double> cov((size_t)F * F, 0.0), V, lam;
+      double n_rows = 0;
+      for (int i : same) {
+        CalRows r;
+        kvtc_status st = load_centred(p, F, in[i].host_kv, in[i].n_tokens, threads, r);
+        if (st != KVTC_OK) return st;
+        add_scatter(r, F, threads, cov);
+        n_rows += (double)r.n_r;
+        mus[i] = std::move(r.mu);
       }
-      acc[0] += e0;
-      const double scale = mx - mn;
-      for (int b = 1; b < nb; ++b) {
-        if (!(scale > 0)) continue;  // every value equals the shift: no error
-        const double k = (double)((1 << b) - 1);
-        const double inv = k / scale, step = scale / k;
-        double e = 0.0;
-        for (int i = 0; i < G; ++i) {
-          double q = std::nearbyint((cg[i] - mn) * inv);
-          q = std::min(std::max(q, 0.0), k);
-          const double d = cg[i] - (mn + q * step);
-          e += d * d;
-        }
-        acc[b] += e;
+      kvtc_status st = eigen_basis(F, cov, n_rows, V, lam);
+      if (st != KVTC_OK) return st;
+      for (int i : same) {
+        CalRows r;
+        st = load_centred(p, F, in[i].host_kv, in[i].n_tokens, threads, r);
+        if (st != KVTC_OK) return st;
+        Ds[i] = distortion(r, F, G, nb, V, threads);
+        vref[i] = same[0];
       }
+      Vs[same[0]] = to_f32(V);
+      lams[same[0]] = std::move(lam);
     }
-    for (int b = 0; b < nb; ++b) D[(size_t)g * nb + b] = acc[b] / (double)n_r;
-  });
-  C.clear();
-  C.shrink_to_fit();
-  Slot s;
-  s.widths = dp_allocate(D, n_g, nb, G, budget_bits(p));
-  int n_act = 0;
-  for (int g = 0; g < n_g; ++g) n_act += s.widths[g] ? 1 : 0;
-  if (n_act * G > KVTC_MAX_REFF)
-    return fail(KVTC_E_UNSUPPORTED, "allocation needs more than KVTC_MAX_REFF active components");
-  s.mu32.resize(F);
-  for (int f = 0; f < F; ++f) s.mu32[f] = (float)mu[f];
-  s.lam = lam;
-  s.V32.resize((size_t)F * n_act * G);
-  int a = 0;
-  for (int g = 0; g < n_g; ++g) {
-    if (!s.widths[g]) continue;
-    for (int i = 0; i < G; ++i)
-      for (int f = 0; f < F; ++f)
-        s.V32[(size_t)f * n_act * G + a * G + i] = (float)V[(size_t)f * F + g * G + i];
-    ++a;
+  } else {
+    for (int i : ord) {
+      CalRows r;
+      kvtc_status st = load_centred(p, F, in[i].host_kv, in[i].n_tokens, threads, r);
+      if (st != KVTC_OK) return st;
+      std::vector<double> cov((size_t)F * F, 0.0), V, lam;
+      add_scatter(r, F, threads, cov);
+      st = eigen_basis(F, cov, (double)r.n_r, V, lam);
+      if (st != KVTC_OK) return st;
+      Ds[i] = distortion(r, F, G, nb, V, threads);
+      mus[i] = std::move(r.mu);
+      Vs[i] = to_f32(V);
+      lams[i] = std::move(lam);
+      vref[i] = i;
+    }
   }
-  finish_slot(p, layer, kind, s);
-  c->slots[idx] = std::move(s);
+
+  // Widths: one DP per tensor, or one over the whole set.
+  std::vector<std::vector<uint8_t>> widths(n);
+  if (flags & KVTC_CAL_GLOBAL_BUDGET) {
+    std::vector<std::vector<double>> ds;
+    for (int i : ord) ds.push_back(Ds[i]);
+    const auto ws = dp_allocate_global(ds, n_g, nb, G, budget_bits(p), KVTC_MAX_REFF / G);
+    for (int k = 0; k < n; ++k) widths[ord[k]] = ws[k];
+  } else {
+    for (int i : ord) widths[i] = dp_allocate(Ds[i], n_g, nb, G, budget_bits(p));
+  }
+
+  // Build every slot first, so a failure leaves the codec unchanged.
+  std::vector<Slot> out(n);
+  for (int i : ord) {
+    kvtc_status st = build_slot(p, in[i].layer, in[i].kind, widths[i], mus[i], lams[vref[i]],
+                                Vs[vref[i]], out[i]);
+    if (st != KVTC_OK) return st;
+  }
+  for (int i : ord) c->slots[key(i)] = std::move(out[i]);
   std::lock_guard<std::mutex> lk(c->mu);
   ++c->calib_version;
   return KVTC_OK;

@@ -34,6 +34,19 @@ def oracle_artifact(wname: str, slots, calib_tokens=None) -> O.Artifact:
     return O.Artifact(oracle_params(w), {(l, k): oracle_slot(wname, l, k, n) for l, k in slots})
 
 
+@functools.lru_cache(maxsize=None)
+def oracle_artifact_set(wname: str, slots: tuple, calib_tokens: int, shared: bool,
+                        global_budget: bool) -> O.Artifact:
+    """An artifact from the oracle's calibration of a tensor set (shared basis
+    per kind and/or one bit budget over the set, at most 256 components per
+    tensor)."""
+    w = synth.workload(wname)
+    ins = [(l, k, synth.gen_kv(w, l, k, synth.ROLE_CALIB, calib_tokens)) for l, k in slots]
+    op = oracle_params(w)
+    return O.Artifact(op, O.calibrate_set(ins, op, shared_basis=shared, global_budget=global_budget,
+                                          max_active=256 // w.group))
+
+
 def to_dev_bytes(b: bytes, pad: int = 0) -> torch.Tensor:
     t = torch.zeros(len(b) + pad, dtype=torch.uint8)
     t[: len(b)] = torch.frombuffer(bytearray(b), dtype=torch.uint8)

@@ -20,7 +20,7 @@ import kv_cache_transform_amd as K
 import oracle.kvtc_oracle as O
 import synth
 from gpu_util import (DEV, DevCodec, bf16_out_to_f64, code_stats, oracle_artifact,
-                      oracle_params, storage_to_dev, to_dev_bytes)
+                      oracle_artifact_set, oracle_params, storage_to_dev, to_dev_bytes)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,13 +40,21 @@ CASES = {
     "odd1_f32": ("odd1_f32", [(0, 0)], 2100, 1, None),
     # per-feature mean offsets about 40 times the spread
     "offsets_bf16": ("offsets_bf16", [(0, 0), (0, 1)], 4096, 1, None),
+    # three layers x {K, V} calibrated as one set: a basis shared by the layers
+    # of each kind and one bit budget over the six tensors (record sizes and
+    # active groups differ per tensor)
+    "llama31_8b_set": ("llama31_8b", [(l, k) for l in range(3) for k in (0, 1)], 8192, 1, 4096),
 }
+SET_CASES = {"llama31_8b_set": (True, True)}
 
 
 def _setup(case):
     wname, slots, T, reqs, calib = CASES[case]
     w = synth.workload(wname)
-    art = oracle_artifact(wname, slots, calib)
+    if case in SET_CASES:
+        art = oracle_artifact_set(wname, tuple(slots), calib, *SET_CASES[case])
+    else:
+        art = oracle_artifact(wname, slots, calib)
     op = art.params
     items = []
     for (l, k) in slots:

@@ -219,3 +219,104 @@ def test_decode_workspace_sizes():
     assert c.staging_bytes(jobs) == blocks
     assert c.decode_workspace_bytes(jobs) == K.kvtc_workspace_bytes(len(jobs)) + blocks
     assert c.decode_workspace_bytes([K.make_job(0, 1, T, 16, 16, 1 << 20, src_capacity=1 << 20)]) == 0   # V never calibrated
+
+
+# ------------------------------------------------- calibration of a tensor set
+
+def _set_inputs(wname="llama31_8b", layers=(0, 1), n=3000):
+    w = synth.workload(wname)
+    return w, [(l, k, synth.gen_kv(w, l, k, 1, n)) for l in layers for k in (0, 1)]
+
+
+def _lib_set(kp, w, inputs, flags):
+    c = K.Codec(kp)
+    c.calibrate_set([(l, k, synth.storage(w, x)) for l, k, x in inputs], flags, threads=8)
+    return c, O.parse_artifact(c.save()).slots
+
+
+def _compare_set(lib_slots, orc_slots, G):
+    """Library vs oracle for a set: means bit for bit, eigenvalues, the
+    projector of each active group; the widths equal, or (a near tie in the
+    two D tables) the same total objective within 1e-9."""
+    keys = sorted(orc_slots)
+    assert sorted(lib_slots) == keys
+    same = all(np.array_equal(lib_slots[k].widths, orc_slots[k].widths) for k in keys)
+    if not same:
+        obj = lambda ws: sum(orc_slots[k].D[g, b] for k in keys for g, b in enumerate(ws[k]))
+        a = obj({k: lib_slots[k].widths for k in keys})
+        b = obj({k: orc_slots[k].widths for k in keys})
+        assert abs(a - b) <= 1e-9 * b, (a, b)
+    for k in keys:
+        sl, so = lib_slots[k], orc_slots[k]
+        assert np.array_equal(sl.mu32, so.mu32)
+        ok = so.lam > so.lam[0] * 1e-12
+        assert np.allclose(sl.lam[ok], so.lam[ok], rtol=1e-6)
+        if same:
+            for a, g in enumerate(so.active_groups):
+                Vl = sl.V32[:, a * G:(a + 1) * G].astype(np.float64)
+                Vo = so.V64[:, g * G:(g + 1) * G]
+                assert np.abs(Vl @ Vl.T - Vo @ Vo.T).max() <= 1e-5, (k, g)
+    return same
+
+
+def test_calibrate_set_without_flags_is_per_tensor():
+    w, ins = _set_inputs(n=2500)
+    op, kp = _params_pair(w)
+    c1, _ = _lib_set(kp, w, ins, 0)
+    c2 = K.Codec(kp)
+    for l, k, x in ins:
+        c2.calibrate(l, k, synth.storage(w, x), threads=8)
+    assert c1.save() == c2.save()
+
+
+@pytest.mark.parametrize("flags", [K.KVTC_CAL_SHARED_BASIS, K.KVTC_CAL_GLOBAL_BUDGET,
+                                   K.KVTC_CAL_SHARED_BASIS | K.KVTC_CAL_GLOBAL_BUDGET])
+def test_calibrate_set_matches_oracle_llama8b(flags):
+    w, ins = _set_inputs()
+    op, kp = _params_pair(w)
+    _, lib = _lib_set(kp, w, ins, flags)
+    orc = O.calibrate_set(ins, op, shared_basis=bool(flags & K.KVTC_CAL_SHARED_BASIS),
+                          global_budget=bool(flags & K.KVTC_CAL_GLOBAL_BUDGET),
+                          max_active=K.KVTC_MAX_REFF // w.group)
+    _compare_set(lib, orc, w.group)
+    bits = sum(16 * int(b) + (64 if b else 0) for sl in lib.values() for b in sl.widths)
+    assert bits <= len(ins) * op.budget_bits
+    if flags & K.KVTC_CAL_SHARED_BASIS:
+        for k in (0, 1):
+            assert np.array_equal(lib[(0, k)].lam, lib[(1, k)].lam)
+    if flags & K.KVTC_CAL_GLOBAL_BUDGET:   # never worse than a budget per tensor
+        per = O.calibrate_set(ins, op, shared_basis=bool(flags & K.KVTC_CAL_SHARED_BASIS))
+        obj = lambda sl_w, key: sum(orc[key].D[g, b] for g, b in enumerate(sl_w))
+        assert sum(obj(lib[k].widths, k) for k in orc) <= sum(obj(per[k].widths, k) for k in orc) * (1 + 1e-12)
+
+
+def test_calibrate_set_global_exact_small():
+    """Three small tensors of very different energy, group 16 and 32: the
+    library's global widths are the oracle's."""
+    for G in (16, 32):
+        ins = pins.three_scaled_tensors()
+        op = O.Params(2, 2, 32, 4, 8, G, 8, 2.0, O.DTYPE_F32)
+        kp = K.params(2, 2, 32, 4, 8, G, 8, 2.0, K.KVTC_F32)
+        c = K.Codec(kp)
+        c.calibrate_set(ins, K.KVTC_CAL_GLOBAL_BUDGET | K.KVTC_CAL_SHARED_BASIS, threads=2)
+        lib = O.parse_artifact(c.save()).slots
+        orc = O.calibrate_set(ins, op, shared_basis=True, global_budget=True, max_active=256 // G)
+        assert _compare_set(lib, orc, G)
+
+
+def test_calibrate_set_errors_leave_codec_unchanged():
+    w, ins = _set_inputs(wname="tiny", layers=(0,), n=600)
+    ins = ins[:1]
+    op, kp = _params_pair(w)
+    c = K.Codec(kp)
+    c.calibrate(0, 0, synth.storage(w, ins[0][2]), threads=2)
+    before = c.save()
+    x = synth.storage(w, ins[0][2])
+    for args, flags in (([(0, 0, x), (0, 0, x)], 0),            # duplicate
+                        ([(0, 0, x)], 4),                          # unknown flag
+                        ([(0, 0, x[: w.sink + w.window])], 0),     # no row after sink and window
+                        ([(0, 0, x), (5, 0, x)], 0)):              # bad layer
+        with pytest.raises(K.KvtcError) as e:
+            c.calibrate_set(args, flags)
+        assert e.value.status == K.KVTC_E_INVALID
+        assert c.save() == before
