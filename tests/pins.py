@@ -26,6 +26,7 @@ import struct
 
 import numpy as np
 
+import oracle.kvtc_lossless as LZ
 import oracle.kvtc_oracle as O
 import synth
 
@@ -357,6 +358,93 @@ def check_shared_basis():
         assert np.allclose(mix[key].lam[:24], ev[:24], rtol=1e-8, atol=1e-12 * ev[0])
     assert np.array_equal(mix[(0, 0)].V32, mix[(1, 0)].V32)
     assert np.array_equal(mix[(0, 1)].V32, O.calibrate(z, p, 0, 1).V32)
+
+
+def lossless_streams():
+    """KVTC streams of several shapes for the lossless stage: family-B data in
+    bf16 and f32 at G = 16 and 32, every width 1..8 on an injected slot, no
+    active group, and the short lengths (0, 1, all passthrough, one
+    compressed row, a ragged last chunk)."""
+    rng = np.random.default_rng(31)
+    out = []
+    x, _ = family_b_small(seed=17, n=2600)
+    for G, dt in ((16, O.DTYPE_BF16), (32, O.DTYPE_F32)):
+        p = small_params(F=64, G=G, bpv=3.0, dtype=dt)
+        sl = O.calibrate(x[:2000], p, 0, 0)
+        xs = O.f32_to_bf16_bits(x[2000:]) if dt == O.DTYPE_BF16 else x[2000:]
+        for T in (600, 0, 1, 12, 13):
+            out.append((p, sl, T, O.encode(xs[:T], p, sl, 0, 0).stream))
+    p = small_params(F=128, G=16, bpv=12.0, dtype=O.DTYPE_BF16)
+    sl = injected_slot(np.eye(128), [1, 2, 3, 4, 5, 6, 7, 8], np.zeros(128), 16)
+    xs = O.f32_to_bf16_bits(rng.standard_normal((1100, 128)).astype(np.float32))
+    out.append((p, sl, 1100, O.encode(xs, p, sl, 0, 0).stream))
+    sl0 = injected_slot(np.zeros((128, 0)), [0] * 8, np.zeros(128), 16)
+    out.append((p, sl0, 300, O.encode(xs[:300], p, sl0, 0, 0).stream))
+    return out
+
+
+def check_rans_golden():
+    gd = golden("rans_examples.json")
+    for case in gd["cases"]:
+        sym = np.array(case["symbols"], np.uint8)
+        (pay,) = LZ.rans_encode([sym], np.array(case["freq"]))
+        assert pay.tolist() == case["payload_words"], (case, pay)
+        (back,) = LZ.rans_decode([pay], [len(sym)], np.array(case["freq"]))
+        assert np.array_equal(back, sym)
+    for case in gd["normalize"]:
+        assert LZ.normalize(np.array(case["hist"])).tolist() == case["freq"], case
+
+
+def check_rans_roundtrip_and_bound():
+    """Random sources: the model sums to M with a slot for exactly the present
+    symbols; decoding gives the chunk back; a chunk's payload is at most its
+    static-model information plus the rANS slack (each step at most
+    log2(17/16) bits above log2(M/f), since the state is at least 16 f) plus
+    the 32-bit final state and one 16-bit word."""
+    rng = np.random.default_rng(8)
+    for A, n in ((2, 1), (4, 999), (16, 1024), (256, 3000), (256, 1025), (32, 2048)):
+        sym = rng.choice(A, size=n, p=rng.dirichlet(np.full(A, 0.3))).astype(np.uint8)
+        h = np.bincount(sym, minlength=A)
+        f = LZ.normalize(h)
+        assert f.sum() == LZ.M and np.array_equal(f > 0, h > 0)
+        assert np.all(np.abs(f - h * LZ.M / n) <= np.count_nonzero(h) + 1)
+        chunks = [sym[i:i + LZ.CHUNK] for i in range(0, n, LZ.CHUNK)]
+        pays = LZ.rans_encode(chunks, f)
+        for ch, pay, back in zip(chunks, pays, LZ.rans_decode(pays, [len(c) for c in chunks], f)):
+            assert np.array_equal(ch, back)
+            info = float(np.sum(np.log2(LZ.M / f[ch])))
+            assert 16 * len(pay) <= info + len(ch) * np.log2(17 / 16) + 48, (A, n)
+
+
+def check_lossless_fields():
+    """The fields against the record parser: passthrough byte planes give the
+    passthrough bytes, the shift and scale planes give the fp32 values, the
+    code fields give each group's codes; merging them rebuilds the stream."""
+    for p, sl, T, st in lossless_streams():
+        fields = LZ.stream_fields(st, p, sl, T)
+        esz = p.elem_bytes
+        assert len(fields) == esz + 8 + sl.n_act
+        s1, w1, tc = O.split_rows(T, p.sink, p.window)
+        pt = np.stack([f for f, _ in fields[:esz]], axis=1).reshape(-1)
+        assert pt.tobytes() == st[64:64 + (s1 + w1) * p.F * esz]
+        codes, shift, scale = O.read_records(st, p, sl, T)
+        sh = np.stack([f for f, _ in fields[esz:esz + 4]], axis=1).copy().view("<f4").reshape(tc, sl.n_act)
+        sc = np.stack([f for f, _ in fields[esz + 4:esz + 8]], axis=1).copy().view("<f4").reshape(tc, sl.n_act)
+        assert np.array_equal(sh.view(np.uint32), shift.view(np.uint32))
+        assert np.array_equal(sc.view(np.uint32), scale.view(np.uint32))
+        for a, g in enumerate(sl.active_groups):
+            q, A = fields[esz + 8 + a]
+            assert A == 1 << int(sl.widths[g])
+            assert np.array_equal(q.reshape(tc, sl.G), codes[:, a * sl.G:(a + 1) * sl.G])
+        assert LZ.merge_fields(st[:64], fields, p, sl, T) == st
+
+
+def check_lossless_roundtrip():
+    """Container round trip on every shape, within the stated bound."""
+    for p, sl, T, st in lossless_streams():
+        z = LZ.compress(st, p, sl, T)
+        assert z[:4] == b"KVTZ" and len(z) <= LZ.container_bound(p, sl, T)
+        assert LZ.decompress(z, p, sl, T) == st
 
 
 def check_projection_exact():

@@ -8,10 +8,12 @@ restatement of it.
 import numpy as np
 import pytest
 
+import oracle.kvtc_lossless as LZ
 import oracle.kvtc_oracle as O
 import pins
 
 _orig = {name: getattr(O, name) for name in dir(O) if callable(getattr(O, name))}
+_orig_lz = {name: getattr(LZ, name) for name in dir(LZ) if callable(getattr(LZ, name))}
 
 
 def _project_no_centering(x_vals, slot):
@@ -181,6 +183,75 @@ def _calibrate_set_kinds_pooled(inputs, params, shared_basis=False, global_budge
     return res
 
 
+def _normalize_remainder_to_first(hist):
+    f = _orig_lz["normalize"](hist)
+    h = np.asarray(hist)
+    if h.sum():
+        r = int(np.argmax(h))
+        first = int(np.argmax(h > 0))
+        extra = f[r] - (1 + (h[r] * (LZ.M - np.count_nonzero(h))) // h.sum())
+        f[r] -= extra
+        f[first] += extra
+    return f
+
+
+def _normalize_no_floor_one(hist):
+    h = np.asarray(hist, np.int64)
+    f = np.zeros(h.size, np.int64)
+    if h.sum():
+        f = (h * LZ.M) // h.sum()
+        f[int(np.argmax(h))] += LZ.M - int(f.sum())
+    return f
+
+
+def _rans_emit_late(chunks, f):
+    """Renormalise when x > f * 2^20 instead of >=."""
+    out = []
+    f = np.asarray(f, np.int64)
+    c = np.concatenate([[0], np.cumsum(f)[:-1]])
+    for ch in chunks:
+        x, em = LZ.RANS_L, []
+        for s in ch[::-1]:
+            if x > (int(f[s]) << 20):
+                em.append(x & 0xFFFF)
+                x >>= 16
+            x = (x // int(f[s])) * LZ.M + x % int(f[s]) + int(c[s])
+        out.append(np.array([x & 0xFFFF, x >> 16] + em[::-1], np.uint16))
+    return out
+
+
+def _rans_words_in_emission_order(chunks, f):
+    out = []
+    for p in _orig_lz["rans_encode"](chunks, f):
+        out.append(np.concatenate([p[:2], p[2:][::-1]]).astype(np.uint16))
+    return out
+
+
+def _fields_planes_big_endian(stream, params, slot, T):
+    fs = _orig_lz["stream_fields"](stream, params, slot, T)
+    esz = params.elem_bytes
+    return fs[:esz][::-1] + fs[esz:esz + 4][::-1] + fs[esz + 4:esz + 8][::-1] + fs[esz + 8:]
+
+
+def _fields_codes_component_major(stream, params, slot, T):
+    fs = _orig_lz["stream_fields"](stream, params, slot, T)
+    esz = params.elem_bytes
+    out = fs[:esz + 8]
+    for q, A in fs[esz + 8:]:
+        out.append((q.reshape(-1, slot.G).T.reshape(-1).copy(), A))
+    return out
+
+
+LZ_MUTATIONS = {
+    "lz_normalize_remainder_to_first": ("normalize", _normalize_remainder_to_first),
+    "lz_normalize_drops_rare": ("normalize", _normalize_no_floor_one),
+    "lz_rans_emit_late": ("rans_encode", _rans_emit_late),
+    "lz_rans_word_order": ("rans_encode", _rans_words_in_emission_order),
+    "lz_planes_big_endian": ("stream_fields", _fields_planes_big_endian),
+    "lz_codes_component_major": ("stream_fields", _fields_codes_component_major),
+}
+
+
 MUTATIONS = {
     "global_ties_to_last_tensor": ("dp_allocate_global", _global_latest_first),
     "global_cap_ignored": ("dp_allocate_global", _global_cap_ignored),
@@ -211,10 +282,14 @@ MUTATIONS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
+@pytest.mark.parametrize("name", sorted(MUTATIONS) + sorted(LZ_MUTATIONS))
 def test_mutation_is_caught(name, monkeypatch):
-    attr, fake = MUTATIONS[name]
-    monkeypatch.setattr(O, attr, fake)
+    if name in LZ_MUTATIONS:
+        attr, fake = LZ_MUTATIONS[name]
+        monkeypatch.setattr(LZ, attr, fake)
+    else:
+        attr, fake = MUTATIONS[name]
+        monkeypatch.setattr(O, attr, fake)
     failed = []
     for check in pins.ALL:
         try:
