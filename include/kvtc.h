@@ -323,6 +323,76 @@ kvtc_status kvtc_read_device_status(const void* d_ws, int32_t n_jobs, int32_t* s
 kvtc_status kvtc_deflate(const void* in, size_t n, void* out, size_t cap, size_t* out_len,
                          int32_t level);
 
+/* ------------------------------------------------------------------------
+ * Lossless stage on the GPU. The KVTC page (section 2B) ends compression
+ * with DEFLATE run on the GPU; this stage is a coder of our own in its
+ * place that knows the stream layout. A KVTC stream is split into fields:
+ *   P_j (j < esz, esz = 2 for bf16, 4 for f32): byte j of every passthrough
+ *       element (rows [0, s') then [T - w', T)), alphabet 256;
+ *   S_j, R_j (j < 4): byte j of every record's fp32 shifts, then scales,
+ *       token-major then group, alphabet 256;
+ *   Q_a (a < n_act): the codes of active group a, token-major then
+ *       component, alphabet 2^b_a.
+ * Each field has a static model: its histogram h over its alphabet, N = sum
+ * h, n_p present symbols, M = 4096, f_s = 0 if h_s = 0 else
+ * 1 + floor(h_s * (M - n_p) / N), the remainder M - sum f added to the most
+ * frequent symbol (lowest index on ties), c_s = sum of f below s. Each field
+ * is cut into chunks of 1024 symbols (the last one shorter), each coded by
+ * rANS (J. Duda's asymmetric numeral systems; 32-bit state, L = 2^16, 16-bit
+ * words): from the chunk's last symbol to its first, starting at x = L, if
+ * x >= f_s * 2^20 the low 16 bits of x are emitted and x >>= 16, then
+ * x = floor(x / f_s) * M + (x mod f_s) + c_s. A chunk's payload is the
+ * final x (low word, high word) and the emitted words, last emitted first.
+ * Decoding: slot = x mod M, s with c_s <= slot < c_s + f_s,
+ * x = f_s * floor(x / M) + slot - c_s, and if x < L, x = x * 2^16 + the next
+ * word.
+ *
+ * Container ("KVTZ", little-endian): u32 magic, u16 version = 1, u16
+ * n_fields, u32 chunk symbols = 1024, u32 n_chunks, u64 stream bytes, u64
+ * container bytes, u32 payload offset, zeros to byte 64; the stream's
+ * 64-byte header; per field u32 n_symbols, u16 alphabet A, u16 0, u16 f[A];
+ * u32 end[n_chunks] (each chunk's payload end relative to the payload
+ * offset, chunks in field order); zeros to the payload offset (a multiple of
+ * 16); the payloads; zeros to the container size (a multiple of 16).
+ * ---------------------------------------------------------------------- */
+
+/* Largest container of a (layer, kind) stream of n_tokens tokens (0 if
+ * uncalibrated). */
+size_t kvtc_lossless_bound(const kvtc_codec* codec, int32_t layer, int32_t kind, int64_t n_tokens);
+
+/* Workspace bytes for kvtc_lossless_encode (encode != 0) or _decode of these
+ * jobs (0 on a bad job): the status words, one u64 container size per job,
+ * then per job its field symbols, models and (encode) per-chunk scratch:
+ * about 3.4 times the stream for encode and 1.2 times for decode at 8192
+ * tokens of 1024 bf16 features. */
+size_t kvtc_lossless_workspace_bytes(const kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs,
+                                     int32_t encode);
+
+/* Stream -> container for each job: src is the KVTC stream (device,
+ * src_capacity >= kvtc_encoded_bytes), dst the container (device,
+ * dst_capacity >= kvtc_lossless_bound); both 16-byte aligned. The container
+ * size of job i is stored in the workspace (kvtc_lossless_sizes) and in the
+ * container's header. Host errors as for kvtc_encode (KVTC_E_CAPACITY for a
+ * workspace below kvtc_lossless_workspace_bytes); the stream is not checked
+ * (run kvtc_decode on it for that). Enqueued on `stream`, not synchronised. */
+kvtc_status kvtc_lossless_encode(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs, void* d_ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/* Container -> stream for each job: src is the container (device,
+ * src_capacity at least its container bytes, which the device checks, and
+ * at least its tables, which the host checks), dst the stream (device,
+ * dst_capacity >= kvtc_encoded_bytes). A container whose header, tables or
+ * directory do not match the job's shape (KVTC_E_MISMATCH) or are
+ * inconsistent, or whose payload does not decode exactly to its chunk
+ * (KVTC_E_CORRUPT), sets the job's status word and no byte of its dst is
+ * written. */
+kvtc_status kvtc_lossless_decode(kvtc_codec* codec, const kvtc_job* jobs, int32_t n_jobs, void* d_ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/* Copy the n_jobs container sizes of the last kvtc_lossless_encode on this
+ * workspace to host memory; synchronises `stream` first. */
+kvtc_status kvtc_lossless_sizes(const void* d_ws, int32_t n_jobs, uint64_t* sizes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -92,6 +92,11 @@ def lib():
         "kvtc_pack": (st, [vp, C.POINTER(kvtc_job), vp, vp, vp, vp]),
         "kvtc_read_device_status": (st, [vp, i32, C.POINTER(i32), vp]),
         "kvtc_deflate": (st, [vp, sz, vp, sz, C.POINTER(sz), i32]),
+        "kvtc_lossless_bound": (sz, [vp, i32, i32, i64]),
+        "kvtc_lossless_workspace_bytes": (sz, [vp, vp, i32, i32]),
+        "kvtc_lossless_encode": (st, [vp, vp, i32, vp, sz, vp]),
+        "kvtc_lossless_decode": (st, [vp, vp, i32, vp, sz, vp]),
+        "kvtc_lossless_sizes": (st, [vp, i32, C.POINTER(C.c_uint64), vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -263,6 +268,29 @@ def kvtc_read_device_status(d_ws, n_jobs: int, stream=None) -> np.ndarray:
     return out
 
 
+def kvtc_lossless_bound(codec: int, layer: int, kind: int, n_tokens: int) -> int:
+    return lib().kvtc_lossless_bound(codec, layer, kind, n_tokens)
+
+
+def kvtc_lossless_workspace_bytes(codec: int, jobs, encode: bool) -> int:
+    return lib().kvtc_lossless_workspace_bytes(codec, _jobs(jobs), len(jobs), int(bool(encode)))
+
+
+def kvtc_lossless_encode(codec: int, jobs, d_ws, ws_bytes: int, stream=None) -> None:
+    _check(lib().kvtc_lossless_encode(codec, _jobs(jobs), len(jobs), _ptr(d_ws), ws_bytes, _stream(stream)))
+
+
+def kvtc_lossless_decode(codec: int, jobs, d_ws, ws_bytes: int, stream=None) -> None:
+    _check(lib().kvtc_lossless_decode(codec, _jobs(jobs), len(jobs), _ptr(d_ws), ws_bytes, _stream(stream)))
+
+
+def kvtc_lossless_sizes(d_ws, n_jobs: int, stream=None) -> np.ndarray:
+    out = np.zeros(n_jobs, np.uint64)
+    _check(lib().kvtc_lossless_sizes(_ptr(d_ws), n_jobs, out.ctypes.data_as(C.POINTER(C.c_uint64)),
+                                     _stream(stream)))
+    return out
+
+
 def kvtc_deflate(data: bytes, level: int = 6) -> bytes:
     n = C.c_size_t()
     _check(lib().kvtc_deflate(data, len(data), None, 0, C.byref(n), level))
@@ -323,6 +351,18 @@ class Codec:
 
     def decode_noalloc(self, jobs, out_dtype, d_status=None, stream=None):
         kvtc_decode_noalloc(self.h, jobs, out_dtype, d_status, stream)
+
+    def lossless_bound(self, layer, kind, n_tokens) -> int:
+        return kvtc_lossless_bound(self.h, layer, kind, n_tokens)
+
+    def lossless_workspace_bytes(self, jobs, encode) -> int:
+        return kvtc_lossless_workspace_bytes(self.h, jobs, encode)
+
+    def lossless_encode(self, jobs, d_ws, ws_bytes, stream=None):
+        kvtc_lossless_encode(self.h, jobs, d_ws, ws_bytes, stream)
+
+    def lossless_decode(self, jobs, d_ws, ws_bytes, stream=None):
+        kvtc_lossless_decode(self.h, jobs, d_ws, ws_bytes, stream)
 
     def decode_workspace_bytes(self, jobs) -> int:
         return kvtc_decode_workspace_bytes(self.h, jobs)

@@ -34,7 +34,7 @@ def _run(cmd, verbose):
 
 
 # gfx950 kernel translation units (compiled in parallel)
-HIP_SOURCES = ["kvtc_encode.hip", "kvtc_decode.hip"]
+HIP_SOURCES = ["kvtc_encode.hip", "kvtc_decode.hip", "kvtc_lossless.hip"]
 
 
 def build(verbose: bool = False) -> str:

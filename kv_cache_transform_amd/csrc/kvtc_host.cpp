@@ -1071,6 +1071,111 @@ kvtc_status decode_fused(kvtc_codec* c, const kvtc_job* jobs, int n_jobs, int ou
   return KVTC_OK;
 }
 
+// ---- lossless stage
+
+// The lossless fields of a job: widths of the active groups in `act`.
+LzShape lz_host_shape(const kvtc_codec* c, const Slot& s, uint32_t s1, uint32_t w1, uint32_t tc,
+                      std::vector<uint8_t>& act) {
+  act.clear();
+  for (uint8_t b : s.widths)
+    if (b) act.push_back(b);
+  LzShape sh;
+  sh.esz = (int)elem_bytes(c->p.dtype);
+  sh.n_act = s.n_act;
+  sh.G = c->p.group;
+  sh.n_pt = (s1 + w1) * (uint32_t)c->F;
+  sh.tc = tc;
+  sh.width = act.data();
+  return sh;
+}
+
+// Workspace: status words and sink, one u64 container size per job, then
+// each job's region (lz_layout).
+size_t lz_ws_base(int n) { return kvtc_workspace_bytes(n) + align_up(8 * (size_t)std::max(n, 1), kAlign); }
+
+kvtc_status lz_plan(kvtc_codec* c, bool enc, const kvtc_job* jobs, int n, void* d_ws, size_t ws_bytes,
+                    std::vector<LzArgs>& batches, size_t* need) {
+  if (!c || !jobs || n <= 0 || n > KVTC_MAX_JOBS) return fail(KVTC_E_INVALID, "bad codec, jobs or job count");
+  std::vector<LzJob> desc(n);
+  std::vector<uint32_t> units(n), segs(n), nfs(n), chunks(n);
+  std::vector<int> rbs(n);
+  std::vector<uint8_t> act;
+  size_t off = lz_ws_base(n);
+  for (int i = 0; i < n; ++i) {
+    const kvtc_job& j = jobs[i];
+    int idx;
+    if (!slot_index(c, j.layer, j.kind, &idx)) return fail(KVTC_E_INVALID, "job: bad layer or kind");
+    const Slot& s = c->slots[idx];
+    if (!s.calibrated) return fail(KVTC_E_NOT_CALIBRATED, "job: (layer, kind) is not calibrated");
+    if (j.n_tokens < 0 || j.n_tokens > (int64_t)INT32_MAX) return fail(KVTC_E_INVALID, "job: bad n_tokens");
+    LzJob& d = desc[i];
+    std::memset(&d, 0, sizeof(d));
+    d.T = (uint32_t)j.n_tokens;
+    split_rows(j.n_tokens, c->p, &d.s1, &d.w1, &d.tc);
+    const LzShape sh = lz_host_shape(c, s, d.s1, d.w1, d.tc, act);
+    const LzLayout L = lz_layout(sh, enc);
+    const size_t sb = stream_bytes(c, s, j.n_tokens), bound = lz_bound(sh);
+    if (bound >= (1ull << 32) - 16) return fail(KVTC_E_UNSUPPORTED, "job: container could reach 4 GiB");
+    if (!need) {
+      if (!j.src || !aligned16(j.src) || !j.dst || !aligned16(j.dst))
+        return fail(KVTC_E_INVALID, "job: src and dst must be non-null and 16-byte aligned");
+      if (enc && j.src_capacity < sb) return fail(KVTC_E_CAPACITY, "job: src_capacity below kvtc_encoded_bytes");
+      if (enc && j.dst_capacity < bound) return fail(KVTC_E_CAPACITY, "job: dst_capacity below kvtc_lossless_bound");
+      if (!enc && j.src_capacity < L.pay_off) return fail(KVTC_E_CAPACITY, "job: src_capacity below the container's tables");
+      if (!enc && j.dst_capacity < sb) return fail(KVTC_E_CAPACITY, "job: dst_capacity below kvtc_encoded_bytes");
+    }
+    d.src = (const uint8_t*)j.src;
+    d.dst = (uint8_t*)j.dst;
+    d.ws = (uint8_t*)d_ws + off;
+    d.src_cap = j.src_capacity;
+    d.stream_bytes = sb;
+    d.slot = idx;
+    d.status_idx = i;
+    off += L.bytes;
+    units[i] = std::max<uint32_t>(1, (sh.n_pt + kLzPassBlk - 1) / kLzPassBlk + (d.tc + kLzRecBlk - 1) / kLzRecBlk);
+    segs[i] = L.n_segs;
+    nfs[i] = (uint32_t)lz_nf(sh);
+    chunks[i] = L.n_chunks;
+    rbs[i] = s.record_bytes;
+  }
+  if (need) {
+    *need = off;
+    return KVTC_OK;
+  }
+  if (!d_ws || !aligned16(d_ws)) return fail(KVTC_E_INVALID, "workspace must be non-null and aligned");
+  if (ws_bytes < off) return fail(KVTC_E_CAPACITY, "workspace below kvtc_lossless_workspace_bytes");
+  if (!c->d_state || c->uploaded_version != c->calib_version)
+    return fail(KVTC_E_INVALID, "device state is missing or stale: call kvtc_upload");
+  for (int p = 0; p < n; p += kMaxLaunchJobs) {
+    LzArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.n_jobs = std::min(n - p, kMaxLaunchJobs);
+    a.esz = (int)elem_bytes(c->p.dtype);
+    a.F = c->F;
+    a.state = c->d_state;
+    a.status = (unsigned long long*)d_ws;
+    a.sizes = (unsigned long long*)((uint8_t*)d_ws + kvtc_workspace_bytes(n));
+    a.epoch = next_epoch();
+    int rb_max = 0;
+    for (int b = 0; b < a.n_jobs; ++b) {
+      LzJob d = desc[p + b];
+      d.unit0 = a.units;
+      d.seg0 = a.segs;
+      d.field0 = a.fields;
+      d.chunk0 = a.chunks;
+      a.units += units[p + b];
+      a.segs += segs[p + b];
+      a.fields += nfs[p + b];
+      a.chunks += chunks[p + b];
+      rb_max = std::max(rb_max, rbs[p + b]);
+      a.jobs[b] = d;
+    }
+    a.rec_lds = (size_t)kLzRecBlk * rb_max + 16;
+    batches.push_back(a);
+  }
+  return KVTC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1216,6 +1321,56 @@ kvtc_status kvtc_read_device_status(const void* d_ws, int32_t n_jobs, int32_t* s
   if (e == hipSuccess) e = hipMemcpy(words.data(), d_ws, sizeof(uint64_t) * n_jobs, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(KVTC_E_HIP, std::string("status read: ") + hipGetErrorString(e));
   for (int i = 0; i < n_jobs; ++i) status[i] = rank_status((int)(words[i] & 0xFF));
+  return KVTC_OK;
+}
+
+size_t kvtc_lossless_bound(const kvtc_codec* c, int32_t layer, int32_t kind, int64_t n_tokens) {
+  int idx;
+  if (!slot_index(c, layer, kind, &idx) || n_tokens < 0 || !c->slots[idx].calibrated) return 0;
+  uint32_t s1, w1, tc;
+  split_rows(n_tokens, c->p, &s1, &w1, &tc);
+  std::vector<uint8_t> act;
+  return lz_bound(lz_host_shape(c, c->slots[idx], s1, w1, tc, act));
+}
+
+size_t kvtc_lossless_workspace_bytes(const kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, int32_t encode) {
+  std::vector<LzArgs> b;
+  size_t need = 0;
+  if (lz_plan(const_cast<kvtc_codec*>(c), encode != 0, jobs, n_jobs, nullptr, 0, b, &need) != KVTC_OK) return 0;
+  return need;
+}
+
+kvtc_status kvtc_lossless_encode(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, void* d_ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  std::vector<LzArgs> b;
+  kvtc_status st = lz_plan(c, true, jobs, n_jobs, d_ws, ws_bytes, b, nullptr);
+  if (st != KVTC_OK) return st;
+  for (const LzArgs& a : b) {
+    st = hip_status(launch_lz_encode(a, stream), "lossless encode launch");
+    if (st != KVTC_OK) return st;
+  }
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_lossless_decode(kvtc_codec* c, const kvtc_job* jobs, int32_t n_jobs, void* d_ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  std::vector<LzArgs> b;
+  kvtc_status st = lz_plan(c, false, jobs, n_jobs, d_ws, ws_bytes, b, nullptr);
+  if (st != KVTC_OK) return st;
+  for (const LzArgs& a : b) {
+    st = hip_status(launch_lz_decode(a, stream), "lossless decode launch");
+    if (st != KVTC_OK) return st;
+  }
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_lossless_sizes(const void* d_ws, int32_t n_jobs, uint64_t* sizes, hipStream_t stream) {
+  if (!d_ws || !sizes || n_jobs <= 0) return fail(KVTC_E_INVALID, "bad arguments");
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e == hipSuccess)
+    e = hipMemcpy(sizes, (const uint8_t*)d_ws + kvtc_workspace_bytes(n_jobs), sizeof(uint64_t) * n_jobs,
+                  hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(KVTC_E_HIP, std::string("container sizes read: ") + hipGetErrorString(e));
   return KVTC_OK;
 }
 

@@ -172,6 +172,123 @@ __host__ __device__ constexpr size_t rest_lds_bytes(int ks, bool fused, size_t r
   return kRestFragOff + 3 * rest_frag_bytes(ks) + (fused ? 2 * rec_lds : 0);
 }
 
+// ---------------------------------------------------------------------------
+// Lossless stage: a KVTC stream <-> a KVTZ container (layout in kvtc.h at
+// kvtc_lossless_encode). The stream is split into fields (passthrough byte
+// planes, shift and scale byte planes, one field of codes per active group),
+// each coded by static rANS in independent chunks of kLzChunk symbols.
+constexpr int kLzChunk = 1024;
+constexpr int kLzMBits = 12;
+constexpr uint32_t kLzM = 1u << kLzMBits;
+constexpr uint32_t kLzL = 1u << 16;
+constexpr int kLzHead = 64;                 // container header, then the stream header
+constexpr int kLzTables = kLzHead + kHeaderBytes;
+constexpr int kLzMaxFields = 4 + 8 + kMaxActGroups;
+constexpr int kLzPassBlk = 256;             // passthrough elements per split/merge unit
+constexpr int kLzRecBlk = 64;               // records per split/merge unit
+constexpr uint32_t kLzSeg = 16384;          // symbols per histogram unit
+
+// The fields of one stream: esz passthrough planes of n_pt symbols, 4 shift
+// and 4 scale planes of tc * n_act, then n_act code fields of tc * G.
+struct LzShape {
+  int esz, n_act, G;
+  uint32_t n_pt, tc;
+  const uint8_t* width;     // widths of the active groups, in order
+};
+__host__ __device__ inline int lz_nf(const LzShape& s) { return s.esz + 8 + s.n_act; }
+__host__ __device__ inline uint32_t lz_n(const LzShape& s, int f) {
+  return f < s.esz ? s.n_pt : f < s.esz + 8 ? s.tc * (uint32_t)s.n_act : s.tc * (uint32_t)s.G;
+}
+__host__ __device__ inline int lz_alpha(const LzShape& s, int f) {
+  return f < s.esz + 8 ? 256 : 1 << s.width[f - s.esz - 8];
+}
+__host__ __device__ inline uint32_t lz_chunks(uint32_t n) { return (n + kLzChunk - 1) / kLzChunk; }
+// a field's symbols in the workspace: 16-byte aligned, at least 16 bytes of
+// padding behind them (whole 16-byte reads and 4-byte writes of a tail)
+__host__ __device__ inline uint32_t lz_sym_region(uint32_t n) { return (n + 31) & ~15u; }
+
+// Positions in the container and in a job's workspace region.
+struct LzLayout {
+  uint32_t n_chunks, n_segs;
+  uint32_t dir_off, pay_off;        // container: chunk directory, payloads
+  size_t sym, hist, fc, aux, cnt, state, dsto, scratch, bytes;   // workspace
+};
+// Field f's first symbol (workspace), first chunk, table entry (container)
+// and first histogram unit, by prefix sums over the fields before it.
+struct LzField {
+  uint32_t sym_off, chunk0, tab_off, seg0;
+};
+__host__ __device__ inline LzField lz_field(const LzShape& s, int f) {
+  LzField r = {0, 0, (uint32_t)kLzTables, 0};
+  for (int g = 0; g < f; ++g) {
+    const uint32_t n = lz_n(s, g);
+    r.sym_off += lz_sym_region(n);
+    r.chunk0 += lz_chunks(n);
+    r.tab_off += 8 + 2 * (uint32_t)lz_alpha(s, g);
+    r.seg0 += (n + kLzSeg - 1) / kLzSeg;
+  }
+  return r;
+}
+// encode: symbols, histograms, models (f | c << 16, then 1/f in fp64),
+// per-chunk emitted-word counts, final states and payload offsets, and the
+// scratch words; decode: symbols, models (f | c << 16, then the
+// slot -> symbol tables of kLzM bytes).
+__host__ __device__ inline LzLayout lz_layout(const LzShape& s, bool enc) {
+  const int nf = lz_nf(s);
+  const LzField e = lz_field(s, nf);
+  LzLayout L;
+  L.n_chunks = e.chunk0;
+  L.n_segs = e.seg0;
+  L.dir_off = e.tab_off;
+  L.pay_off = (L.dir_off + 4 * L.n_chunks + 15) & ~15u;
+  L.sym = 0;
+  L.hist = align_up(e.sym_off, 256);
+  L.fc = L.hist + (enc ? (size_t)nf * 256 * 4 : 0);
+  L.aux = L.fc + (size_t)nf * 256 * 4;
+  L.cnt = align_up(L.aux + (size_t)nf * (enc ? 256 * 8 : kLzM), 256);
+  L.state = L.cnt + (size_t)L.n_chunks * 4;
+  L.dsto = L.state + (size_t)L.n_chunks * 4;
+  L.scratch = align_up(L.dsto + (size_t)L.n_chunks * 4, 256);
+  L.bytes = align_up(L.scratch + (enc ? (size_t)L.n_chunks * kLzChunk * 2 : 0), 256);
+  return L;
+}
+// Largest container a stream of this shape needs (every chunk one word per
+// symbol plus its two state words, and the 16-byte tail padding).
+__host__ __device__ inline size_t lz_bound(const LzShape& s) {
+  const LzLayout L = lz_layout(s, false);
+  size_t b = L.pay_off + 15;
+  for (int f = 0; f < lz_nf(s); ++f) b += 2 * (size_t)lz_n(s, f) + 4 * (size_t)lz_chunks(lz_n(s, f));
+  return b;
+}
+
+struct LzJob {
+  const uint8_t* src;
+  uint8_t* dst;
+  uint8_t* ws;              // this job's workspace region (lz_layout)
+  uint64_t src_cap;
+  uint64_t stream_bytes;
+  uint32_t T, s1, w1, tc;
+  uint32_t unit0;           // first split/merge unit of the job in the launch
+  uint32_t seg0;            // first histogram unit
+  uint32_t field0;          // first field
+  uint32_t chunk0;          // first chunk
+  int32_t slot;
+  int32_t status_idx;
+};
+
+struct LzArgs {
+  LzJob jobs[kMaxLaunchJobs];
+  int32_t n_jobs;
+  int32_t esz;
+  int32_t F;
+  uint32_t units, segs, fields, chunks;   // totals of the launch
+  uint32_t epoch;
+  size_t rec_lds;                         // LDS bytes of one record block
+  const uint8_t* state;
+  unsigned long long* status;
+  unsigned long long* sizes;              // container bytes per job (encode)
+};
+
 // Host-side launchers implemented in kvtc_encode.hip and kvtc_decode.hip (G = group size, lds =
 // dynamic LDS bytes). Every job of one launch has the same shape parameter:
 // nb = r_enc / 32 for encode, ks = r_dec / 16 for the decode stages. They
@@ -187,5 +304,8 @@ int launch_clear_words(void* words, int n, hipStream_t s);
 int launch_status_codes(const void* words, int32_t* out, int n, hipStream_t s);
 int launch_pack(const LaunchArgs& a, int G, size_t lds, const void* codes, const void* ss,
                 hipStream_t s);
+// kvtc_lossless.hip: the lossless stage's kernel sequences.
+int launch_lz_encode(const LzArgs& a, hipStream_t s);
+int launch_lz_decode(const LzArgs& a, hipStream_t s);
 
 }  // namespace kvtc

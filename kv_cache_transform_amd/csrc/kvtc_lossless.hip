@@ -1,0 +1,639 @@
+// Lossless stage of libkvtc for gfx950: a KVTC stream <-> a KVTZ container.
+//
+// The KVTC page (section 2B) finishes compression with DEFLATE on the GPU.
+// This stage is our own replacement that knows the stream's layout: the
+// stream is split into fields (passthrough byte planes, the byte planes of
+// the fp32 shifts and scales, one field of codes per active group), each
+// field gets a static model (its histogram normalised to kLzM), and each
+// field is coded by rANS (range asymmetric numeral systems, J. Duda) in
+// independent chunks of kLzChunk symbols, one chunk per lane. The container
+// layout is written out in kvtc.h at kvtc_lossless_encode.
+//
+// Encode: split (stream -> field symbols), histogram, model (normalise,
+// write the tables), code (one lane per chunk, words into scratch), layout
+// (per job: chunk directory by a prefix sum, container header), copy
+// (payloads in decoder order). Decode: check (container header, tables,
+// directory), model (slot -> symbol tables), decode (one lane per chunk),
+// merge (field symbols -> stream). Every kernel is memory- or latency-bound;
+// no matrix unit is involved.
+#include "kvtc_device.h"
+
+namespace kvtc {
+namespace {
+
+constexpr int kLzThreads = 256;
+
+template <uint32_t LzJob::*M>
+__device__ __forceinline__ int lz_job_at(const LzArgs& a, uint32_t x) {
+  int lo = 0, hi = a.n_jobs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.jobs[mid].*M <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ const DevSlot* lz_slot(const LzArgs& a, const LzJob& j) {
+  return (const DevSlot*)a.state + j.slot;
+}
+
+__device__ __forceinline__ LzShape lz_shape(const LzArgs& a, const LzJob& j) {
+  const DevSlot* sl = lz_slot(a, j);
+  LzShape s;
+  s.esz = a.esz;
+  s.n_act = sl->n_act;
+  s.G = sl->G;
+  s.n_pt = (j.s1 + j.w1) * (uint32_t)a.F;
+  s.tc = j.tc;
+  s.width = sl->width;
+  return s;
+}
+
+__device__ __forceinline__ void lz_set(const LzArgs& a, const LzJob& j, int st) {
+  atomicMax(&a.status[j.status_idx], ((unsigned long long)a.epoch << 32) | (unsigned long long)status_rank(st));
+}
+
+// True if an earlier kernel of this call found the job bad.
+__device__ __forceinline__ bool lz_failed(const LzArgs& a, const LzJob& j) {
+  const unsigned long long w = __atomic_load_n(&a.status[j.status_idx], __ATOMIC_RELAXED);
+  return (uint32_t)(w >> 32) == a.epoch && (w & 0xFFull) != 0;
+}
+
+// Where field f's symbols start, for the fields whose position is a
+// closed form: the planes (f < esz + 8) and the first code field.
+__device__ __forceinline__ uint32_t lz_plane_off(const LzShape& s, int f) {
+  const uint32_t rp = lz_sym_region(s.n_pt), rs = lz_sym_region(s.tc * (uint32_t)s.n_act);
+  return f < s.esz ? f * rp : s.esz * rp + (f - s.esz) * rs;
+}
+__device__ __forceinline__ uint32_t lz_code_off(const LzShape& s, int a) {
+  return lz_plane_off(s, s.esz + 8) + a * lz_sym_region(s.tc * (uint32_t)s.G);
+}
+
+// Wave-wide (64 lanes) reductions and an inclusive scan.
+__device__ __forceinline__ uint64_t wave_sum(uint64_t v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v, int lane) {
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t u = (uint32_t)__shfl_up((int)v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// ------------------------------------------------------------- encode ----
+
+// One unit: a block of kLzPassBlk passthrough elements, or of kLzRecBlk
+// records, written out as field symbols. Unit 0 of a job also marks the job
+// OK for this call and clears its histograms.
+__global__ void __launch_bounds__(kLzThreads) lz_split_kernel(const LzArgs a) {
+  extern __shared__ uint8_t lds[];
+  const int ji = lz_job_at<&LzJob::unit0>(a, blockIdx.x);
+  const LzJob& j = a.jobs[ji];
+  const LzShape s = lz_shape(a, j);
+  const uint32_t u = blockIdx.x - j.unit0;
+  const int tid = threadIdx.x;
+  if (u == 0) {
+    if (tid == 0) lz_set(a, j, KVTC_OK);
+    const LzLayout L = lz_layout(s, true);
+    uint32_t* h = (uint32_t*)(j.ws + L.hist);
+    for (int i = tid; i < lz_nf(s) * 256; i += kLzThreads) h[i] = 0;
+  }
+  const uint32_t n_pb = (s.n_pt + kLzPassBlk - 1) / kLzPassBlk;
+  uint8_t* sym = j.ws;
+  if (u < n_pb) {
+    const uint32_t e = u * kLzPassBlk + tid;
+    if (e >= s.n_pt) return;
+    const uint8_t* src = j.src + kHeaderBytes;
+    const uint32_t rp = lz_sym_region(s.n_pt);
+    if (s.esz == 2) {
+      const uint32_t v = ((const uint16_t*)src)[e];
+      sym[e] = (uint8_t)v;
+      sym[rp + e] = (uint8_t)(v >> 8);
+    } else {
+      const uint32_t v = ((const uint32_t*)src)[e];
+      for (int b = 0; b < 4; ++b) sym[b * rp + e] = (uint8_t)(v >> (8 * b));
+    }
+    return;
+  }
+  const uint32_t r0 = (u - n_pb) * kLzRecBlk;
+  if (r0 >= s.tc) return;
+  const DevSlot* sl = lz_slot(a, j);
+  const int rb = sl->record_bytes, na = s.n_act, G = s.G;
+  const int nr = (int)min((uint32_t)kLzRecBlk, s.tc - r0);
+  // the block's records into LDS (16-byte aligned: the records start at
+  // 64 + n_pt * esz, a multiple of 16, and a block at 64 * rb bytes)
+  const uint8_t* base = j.src + kHeaderBytes + (size_t)s.n_pt * s.esz + (size_t)r0 * rb;
+  const int nbytes = nr * rb;
+  for (int i = tid * 4; i + 4 <= nbytes; i += kLzThreads * 4) *(uint32_t*)(lds + i) = *(const uint32_t*)(base + i);
+  for (int i = (nbytes & ~3) + tid; i < nbytes; i += kLzThreads) lds[i] = base[i];
+  __syncthreads();
+  for (int k = 0; k < 8; ++k) {
+    uint8_t* out = sym + lz_plane_off(s, s.esz + k) + (size_t)r0 * na;
+    for (int i = tid; i < nr * na; i += kLzThreads) {
+      const int t = i / na, g = i - t * na;
+      out[i] = lds[t * rb + g * 8 + k];
+    }
+  }
+  for (int g = 0; g < na; ++g) {
+    const int b = s.width[g], co = sl->chunk_off[g];
+    const uint32_t mask = (1u << b) - 1u;
+    uint8_t* out = sym + lz_code_off(s, g) + (size_t)r0 * G;
+    for (int i = tid; i < nr * G; i += kLzThreads) {
+      const int t = i / G, c = i - t * G;
+      const int bit = c * b, p = t * rb + co + (bit >> 3);
+      const uint32_t v = ((uint32_t)lds[p] | ((uint32_t)lds[p + 1] << 8)) >> (bit & 7);
+      out[i] = (uint8_t)(v & mask);
+    }
+  }
+}
+
+// One unit: kLzSeg symbols of one field into the field's histogram (a
+// sub-histogram per wave in LDS, runs of equal symbols added at once).
+__global__ void __launch_bounds__(kLzThreads) lz_hist_kernel(const LzArgs a) {
+  __shared__ uint32_t h[kLzThreads / 64][256];
+  const int ji = lz_job_at<&LzJob::seg0>(a, blockIdx.x);
+  const LzJob& j = a.jobs[ji];
+  const LzShape s = lz_shape(a, j);
+  const uint32_t u = blockIdx.x - j.seg0;
+  uint32_t seg0 = 0, sym_off = 0;
+  int f = 0;
+  for (; f < lz_nf(s); ++f) {
+    const uint32_t nf = lz_n(s, f), ns = (nf + kLzSeg - 1) / kLzSeg;
+    if (u < seg0 + ns) break;
+    seg0 += ns;
+    sym_off += lz_sym_region(nf);
+  }
+  const int tid = threadIdx.x, w = tid >> 6;
+  for (int i = tid; i < 256 * (kLzThreads / 64); i += kLzThreads) (&h[0][0])[i] = 0;
+  __syncthreads();
+  const uint32_t n = lz_n(s, f);
+  const uint32_t b0 = (u - seg0) * kLzSeg, b1 = min(n, b0 + kLzSeg);
+  const uint8_t* sym = j.ws + sym_off;
+  for (uint32_t i = b0 + tid * 16; i < b1; i += kLzThreads * 16) {
+    const u32x4 v = *(const u32x4*)(sym + i);
+    const int m = (int)min(16u, b1 - i);
+    uint32_t cur = v[0] & 0xFFu, run = 0;
+    for (int k = 0; k < m; ++k) {
+      const uint32_t c = (v[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+      if (c != cur) {
+        atomicAdd(&h[w][cur], run);
+        cur = c;
+        run = 0;
+      }
+      ++run;
+    }
+    atomicAdd(&h[w][cur], run);
+  }
+  __syncthreads();
+  uint32_t t = 0;
+  for (int k = 0; k < kLzThreads / 64; ++k) t += h[k][tid];
+  if (t) {
+    const LzLayout L = lz_layout(s, true);
+    atomicAdd((uint32_t*)(j.ws + L.hist) + f * 256 + tid, t);
+  }
+}
+
+// One wave per field: normalise the histogram (every present symbol gets
+// 1 + floor(h * (M - n_present) / N), the remainder goes to the most
+// frequent symbol, lowest index on ties), write the container's table entry
+// and the coder's model (f | c << 16 and 1/f).
+__global__ void __launch_bounds__(64) lz_model_kernel(const LzArgs a) {
+  const int ji = lz_job_at<&LzJob::field0>(a, blockIdx.x);
+  const LzJob& j = a.jobs[ji];
+  const LzShape s = lz_shape(a, j);
+  const int f = blockIdx.x - j.field0, lane = threadIdx.x;
+  const uint32_t n = lz_n(s, f);
+  const int A = lz_alpha(s, f);
+  const LzField fd = lz_field(s, f);
+  const LzLayout L = lz_layout(s, true);
+  uint8_t* tab = j.dst + fd.tab_off;
+  if (lane == 0) {
+    *(uint32_t*)tab = n;
+    *(uint32_t*)(tab + 4) = (uint32_t)A;
+  }
+  const uint32_t* hist = (const uint32_t*)(j.ws + L.hist) + f * 256;
+  uint32_t* fc = (uint32_t*)(j.ws + L.fc) + f * 256;
+  double* rcp = (double*)(j.ws + L.aux) + f * 256;
+  uint32_t hv[4], fv[4];
+  uint64_t N = 0;
+  uint32_t np = 0, hmax = 0;
+  for (int q = 0; q < 4; ++q) {
+    const int sy = lane + 64 * q;
+    hv[q] = sy < A ? hist[sy] : 0;
+    N += hv[q];
+    np += hv[q] ? 1 : 0;
+    hmax = max(hmax, hv[q]);
+  }
+  N = wave_sum(N);
+  np = (uint32_t)wave_sum(np);
+  hmax = wave_max(hmax);
+  uint32_t first = 256;
+  for (int q = 3; q >= 0; --q)
+    if (hv[q] == hmax && hmax) first = lane + 64 * q;
+  first = wave_min(first);
+  uint32_t sum = 0;
+  for (int q = 0; q < 4; ++q) {
+    fv[q] = hv[q] ? 1u + (uint32_t)(((uint64_t)hv[q] * (kLzM - np)) / (N ? N : 1)) : 0u;
+    sum += fv[q];
+  }
+  sum = (uint32_t)wave_sum(sum);
+  if (N)
+    for (int q = 0; q < 4; ++q)
+      if ((uint32_t)(lane + 64 * q) == first) fv[q] += kLzM - sum;
+  uint32_t run = 0;
+  for (int q = 0; q < 4; ++q) {
+    const int sy = lane + 64 * q;
+    const uint32_t inc = wave_scan(fv[q], lane);
+    const uint32_t c = run + inc - fv[q];
+    run += (uint32_t)__shfl((int)inc, 63, 64);
+    if (sy < A) {
+      ((uint16_t*)(tab + 8))[sy] = (uint16_t)fv[q];
+      fc[sy] = fv[q] | (c << 16);
+      rcp[sy] = fv[q] ? 1.0 / (double)fv[q] : 0.0;
+    }
+  }
+}
+
+// One lane per chunk: rANS from the chunk's last symbol to its first; the
+// emitted words go to the chunk's scratch in emission order.
+__global__ void __launch_bounds__(kLzThreads) lz_code_kernel(const LzArgs a) {
+  const uint32_t g = blockIdx.x * kLzThreads + threadIdx.x;
+  if (g >= a.chunks) return;
+  const int ji = lz_job_at<&LzJob::chunk0>(a, g);
+  const LzJob& j = a.jobs[ji];
+  const LzShape s = lz_shape(a, j);
+  const uint32_t kj = g - j.chunk0;
+  uint32_t k = kj, sym_off = 0;
+  int f = 0;
+  for (; f < lz_nf(s); ++f) {
+    const uint32_t nc = lz_chunks(lz_n(s, f));
+    if (k < nc) break;
+    k -= nc;
+    sym_off += lz_sym_region(lz_n(s, f));
+  }
+  const LzLayout L = lz_layout(s, true);
+  const uint32_t n = lz_n(s, f);
+  const int len = (int)min((uint32_t)kLzChunk, n - k * kLzChunk);
+  const uint8_t* sym = j.ws + sym_off + (size_t)k * kLzChunk;
+  const uint32_t* fc = (const uint32_t*)(j.ws + L.fc) + f * 256;
+  const double* rcp = (const double*)(j.ws + L.aux) + f * 256;
+  uint16_t* out = (uint16_t*)(j.ws + L.scratch) + (size_t)kj * kLzChunk;
+  uint32_t x = kLzL, cnt = 0;
+  for (int blk = (len - 1) >> 4; blk >= 0; --blk) {
+    const u32x4 v = *(const u32x4*)(sym + blk * 16);
+    for (int i = min(15, len - 1 - blk * 16); i >= 0; --i) {
+      const uint32_t sy = (v[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      const uint32_t m = fc[sy], fs = m & 0xFFFFu, cs = m >> 16;
+      if ((uint64_t)x >= ((uint64_t)fs << 20)) {
+        out[cnt++] = (uint16_t)x;
+        x >>= 16;
+      }
+      // floor(x / fs) from the fp64 reciprocal, off by at most one
+      uint32_t q = (uint32_t)((double)x * rcp[sy]);
+      int64_t r = (int64_t)x - (int64_t)q * fs;
+      if (r < 0) {
+        --q;
+        r += fs;
+      } else if (r >= (int64_t)fs) {
+        ++q;
+        r -= fs;
+      }
+      x = (q << kLzMBits) + (uint32_t)r + cs;
+    }
+  }
+  ((uint32_t*)(j.ws + L.cnt))[kj] = cnt;
+  ((uint32_t*)(j.ws + L.state))[kj] = x;
+}
+
+// One workgroup per job: payload sizes -> chunk directory (prefix sum) and
+// payload offsets; the container header, the stream header, the padding.
+__global__ void __launch_bounds__(kLzThreads) lz_layout_kernel(const LzArgs a) {
+  __shared__ uint32_t part[kLzThreads / 64];
+  const LzJob& j = a.jobs[blockIdx.x];
+  const LzShape s = lz_shape(a, j);
+  const LzLayout L = lz_layout(s, true);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint32_t* cnt = (const uint32_t*)(j.ws + L.cnt);
+  uint32_t* dsto = (uint32_t*)(j.ws + L.dsto);
+  uint32_t* dir = (uint32_t*)(j.dst + L.dir_off);
+  uint32_t run = 0;
+  for (uint32_t k0 = 0; k0 < L.n_chunks; k0 += kLzThreads) {
+    const uint32_t k = k0 + tid;
+    const uint32_t bytes = k < L.n_chunks ? 4 + 2 * cnt[k] : 0;
+    const uint32_t inc = wave_scan(bytes, lane);
+    if (lane == 63) part[w] = inc;
+    __syncthreads();
+    uint32_t before = run;
+    for (int q = 0; q < w; ++q) before += part[q];
+    uint32_t tile = 0;
+    for (int q = 0; q < kLzThreads / 64; ++q) tile += part[q];
+    if (k < L.n_chunks) {
+      dir[k] = before + inc;
+      dsto[k] = before + inc - bytes;
+    }
+    run += tile;
+    __syncthreads();
+  }
+  const uint32_t end = L.pay_off + run;
+  const uint64_t total = (end + 15u) & ~15u;
+  if (tid < 16) {
+    uint32_t v = 0;
+    switch (tid) {
+      case 0: v = 0x5A54564Bu; break;                     // "KVTZ"
+      case 1: v = 1u | ((uint32_t)lz_nf(s) << 16); break;
+      case 2: v = (uint32_t)kLzChunk; break;
+      case 3: v = L.n_chunks; break;
+      case 4: v = (uint32_t)j.stream_bytes; break;
+      case 5: v = (uint32_t)(j.stream_bytes >> 32); break;
+      case 6: v = (uint32_t)total; break;
+      case 7: v = (uint32_t)(total >> 32); break;
+      case 8: v = L.pay_off; break;
+      default: v = 0;
+    }
+    ((uint32_t*)j.dst)[tid] = v;
+  } else if (tid < 32) {
+    ((uint32_t*)(j.dst + kLzHead))[tid - 16] = ((const uint32_t*)j.src)[tid - 16];
+  }
+  for (uint32_t i = L.dir_off + 4 * L.n_chunks + tid; i < L.pay_off; i += kLzThreads) j.dst[i] = 0;
+  for (uint32_t i = end + tid; i < total; i += kLzThreads) j.dst[i] = 0;
+  if (tid == 0) a.sizes[j.status_idx] = total;
+}
+
+// One wave per chunk: its payload in decoder order (final state, then the
+// emitted words, last emitted first).
+__global__ void __launch_bounds__(kLzThreads) lz_copy_kernel(const LzArgs a) {
+  const uint32_t g = blockIdx.x * (kLzThreads / 64) + (threadIdx.x >> 6);
+  if (g >= a.chunks) return;
+  const int lane = threadIdx.x & 63;
+  const int ji = lz_job_at<&LzJob::chunk0>(a, g);
+  const LzJob& j = a.jobs[ji];
+  const LzShape s = lz_shape(a, j);
+  const LzLayout L = lz_layout(s, true);
+  const uint32_t k = g - j.chunk0;
+  const uint32_t cnt = ((const uint32_t*)(j.ws + L.cnt))[k];
+  const uint32_t x = ((const uint32_t*)(j.ws + L.state))[k];
+  const uint32_t off = ((const uint32_t*)(j.ws + L.dsto))[k];
+  const uint16_t* sc = (const uint16_t*)(j.ws + L.scratch) + (size_t)k * kLzChunk;
+  uint16_t* out = (uint16_t*)(j.dst + L.pay_off + off);
+  for (uint32_t i = lane; i < cnt + 2; i += 64)
+    out[i] = i == 0 ? (uint16_t)x : i == 1 ? (uint16_t)(x >> 16) : sc[cnt - 1 - (i - 2)];
+}
+
+// ------------------------------------------------------------- decode ----
+
+// One workgroup per job: the container's header, field table entries and
+// chunk directory must be those of the job's shape and self-consistent.
+__global__ void __launch_bounds__(kLzThreads) lz_check_kernel(const LzArgs a) {
+  __shared__ int bad;
+  const LzJob& j = a.jobs[blockIdx.x];
+  const LzShape s = lz_shape(a, j);
+  const LzLayout L = lz_layout(s, false);
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    lz_set(a, j, KVTC_OK);
+    bad = KVTC_OK;
+  }
+  __syncthreads();
+  const uint32_t* h = (const uint32_t*)j.src;
+  const uint64_t total = (uint64_t)h[6] | ((uint64_t)h[7] << 32);
+  if (tid == 0) {
+    int st = KVTC_OK;
+    if (h[0] != 0x5A54564Bu || (h[1] & 0xFFFFu) != 1u || h[2] != (uint32_t)kLzChunk)
+      st = KVTC_E_CORRUPT;
+    else if ((h[1] >> 16) != (uint32_t)lz_nf(s) || h[3] != L.n_chunks ||
+             ((uint64_t)h[4] | ((uint64_t)h[5] << 32)) != j.stream_bytes || h[8] != L.pay_off)
+      st = KVTC_E_MISMATCH;
+    else if (total % 16 || total > j.src_cap || total < L.pay_off)
+      st = KVTC_E_CORRUPT;
+    if (st != KVTC_OK) bad = st;
+  }
+  __syncthreads();
+  if (bad != KVTC_OK) {
+    if (tid == 0) lz_set(a, j, bad);
+    return;
+  }
+  if (tid < lz_nf(s)) {
+    const LzField fd = lz_field(s, tid);
+    const uint32_t* e = (const uint32_t*)(j.src + fd.tab_off);
+    if (e[0] != lz_n(s, tid) || e[1] != (uint32_t)lz_alpha(s, tid)) atomicMax(&bad, (int)-KVTC_E_MISMATCH);
+  }
+  const uint32_t* dir = (const uint32_t*)(j.src + L.dir_off);
+  for (uint32_t k = tid; k < L.n_chunks; k += kLzThreads) {
+    const uint32_t e = dir[k], p = k ? dir[k - 1] : 0;
+    if ((e & 1u) || e < p + 4 || (uint64_t)L.pay_off + e > total) atomicMax(&bad, (int)-KVTC_E_CORRUPT);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t last = L.n_chunks ? dir[L.n_chunks - 1] : 0;
+    if (((L.pay_off + (uint64_t)last + 15) & ~15ull) != total) atomicMax(&bad, (int)-KVTC_E_CORRUPT);
+  }
+  __syncthreads();
+  if (tid == 0 && bad != KVTC_OK) lz_set(a, j, -bad);
+}
+
+// One wave per field: the model from the container's table (it must sum to
+// M): f | c << 16 per symbol, and the slot -> symbol table.
+__global__ void __launch_bounds__(64) lz_dmodel_kernel(const LzArgs a) {
+  __shared__ uint32_t cum[256];
+  const int ji = lz_job_at<&LzJob::field0>(a, blockIdx.x);
+  const LzJob& j = a.jobs[ji];
+  if (lz_failed(a, j)) return;
+  const LzShape s = lz_shape(a, j);
+  const int f = blockIdx.x - j.field0, lane = threadIdx.x;
+  if (lz_n(s, f) == 0) return;
+  const int A = lz_alpha(s, f);
+  const LzField fd = lz_field(s, f);
+  const LzLayout L = lz_layout(s, false);
+  const uint16_t* fr = (const uint16_t*)(j.src + fd.tab_off + 8);
+  uint32_t* fc = (uint32_t*)(j.ws + L.fc) + f * 256;
+  uint8_t* tbl = j.ws + L.aux + (size_t)f * kLzM;
+  uint32_t fv[4], run = 0;
+  for (int q = 0; q < 4; ++q) {
+    const int sy = lane + 64 * q;
+    fv[q] = sy < A ? fr[sy] : 0u;
+    const uint32_t inc = wave_scan(fv[q], lane);
+    const uint32_t c = run + inc - fv[q];
+    run += (uint32_t)__shfl((int)inc, 63, 64);
+    if (sy < A) fc[sy] = fv[q] | (c << 16);
+    cum[sy] = sy < A ? c : 0xFFFFFFFFu;
+  }
+  if (run != kLzM) {
+    if (lane == 0) lz_set(a, j, KVTC_E_CORRUPT);
+    return;
+  }
+  __syncthreads();
+  for (uint32_t slot = lane; slot < kLzM; slot += 64) {
+    int lo = 0, hi = A - 1;          // the last symbol whose range starts at or before slot
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cum[mid] <= slot) lo = mid;
+      else hi = mid - 1;
+    }
+    tbl[slot] = (uint8_t)lo;
+  }
+}
+
+// One lane per chunk: rANS decoding, the payload read through two 16-byte
+// blocks (the container is padded to 16 bytes), symbols stored four at a
+// time into the field.
+__global__ void __launch_bounds__(kLzThreads) lz_decode_kernel(const LzArgs a) {
+  const uint32_t g = blockIdx.x * kLzThreads + threadIdx.x;
+  if (g >= a.chunks) return;
+  const int ji = lz_job_at<&LzJob::chunk0>(a, g);
+  const LzJob& j = a.jobs[ji];
+  if (lz_failed(a, j)) return;
+  const LzShape s = lz_shape(a, j);
+  const uint32_t kj = g - j.chunk0;
+  uint32_t k = kj, sym_off = 0;
+  int f = 0;
+  for (; f < lz_nf(s); ++f) {
+    const uint32_t nc = lz_chunks(lz_n(s, f));
+    if (k < nc) break;
+    k -= nc;
+    sym_off += lz_sym_region(lz_n(s, f));
+  }
+  const LzLayout L = lz_layout(s, false);
+  const uint32_t n = lz_n(s, f);
+  const int len = (int)min((uint32_t)kLzChunk, n - k * kLzChunk);
+  const uint32_t* dir = (const uint32_t*)(j.src + L.dir_off);
+  const uint32_t total = ((const uint32_t*)j.src)[6];
+  uint32_t pos = L.pay_off + (kj ? dir[kj - 1] : 0u);
+  const uint32_t end = L.pay_off + dir[kj];
+  const uint32_t* fc = (const uint32_t*)(j.ws + L.fc) + f * 256;
+  const uint8_t* tbl = j.ws + L.aux + (size_t)f * kLzM;
+  uint32_t* out = (uint32_t*)(j.ws + sym_off + (size_t)k * kLzChunk);
+  uint32_t blk = pos >> 4;
+  u32x4 cur = *(const u32x4*)(j.src + (size_t)blk * 16);
+  u32x4 nxt = (blk + 1) * 16 < total ? *(const u32x4*)(j.src + (size_t)(blk + 1) * 16) : u32x4(0u);
+  auto word = [&]() -> uint32_t {
+    if ((pos >> 4) != blk) {
+      ++blk;
+      cur = nxt;
+      nxt = (blk + 1) * 16 < total ? *(const u32x4*)(j.src + (size_t)(blk + 1) * 16) : u32x4(0u);
+    }
+    const uint32_t wv = (cur[(pos >> 2) & 3] >> (8 * (pos & 2))) & 0xFFFFu;
+    pos += 2;
+    return wv;
+  };
+  uint32_t x = word();
+  x |= word() << 16;
+  uint32_t acc = 0;
+  bool ok = true;
+  for (int i = 0; i < len; ++i) {
+    const uint32_t slot = x & (kLzM - 1);
+    const uint32_t sy = tbl[slot];
+    const uint32_t m = fc[sy];
+    x = (m & 0xFFFFu) * (x >> kLzMBits) + slot - (m >> 16);
+    if (x < kLzL) {
+      if (pos >= end) {
+        ok = false;
+        break;
+      }
+      x = (x << 16) | word();
+    }
+    acc |= sy << (8 * (i & 3));
+    if ((i & 3) == 3 || i == len - 1) {
+      out[i >> 2] = acc;
+      acc = 0;
+    }
+  }
+  if (!ok || pos != end || x != kLzL) lz_set(a, j, KVTC_E_CORRUPT);
+}
+
+// One unit per block of passthrough elements or records: field symbols back
+// into the stream (nothing is written for a job found bad). Unit 0 of a job
+// also copies the stream header.
+__global__ void __launch_bounds__(kLzThreads) lz_merge_kernel(const LzArgs a) {
+  extern __shared__ uint8_t lds[];
+  const int ji = lz_job_at<&LzJob::unit0>(a, blockIdx.x);
+  const LzJob& j = a.jobs[ji];
+  if (lz_failed(a, j)) return;
+  const LzShape s = lz_shape(a, j);
+  const uint32_t u = blockIdx.x - j.unit0;
+  const int tid = threadIdx.x;
+  uint8_t* dst = j.dst;
+  if (u == 0 && tid < 16) ((uint32_t*)dst)[tid] = ((const uint32_t*)(j.src + kLzHead))[tid];
+  const uint32_t n_pb = (s.n_pt + kLzPassBlk - 1) / kLzPassBlk;
+  const uint8_t* sym = j.ws;
+  if (u < n_pb) {
+    const uint32_t e = u * kLzPassBlk + tid;
+    if (e >= s.n_pt) return;
+    const uint32_t rp = lz_sym_region(s.n_pt);
+    uint8_t* out = dst + kHeaderBytes;
+    if (s.esz == 2) {
+      ((uint16_t*)out)[e] = (uint16_t)(sym[e] | ((uint32_t)sym[rp + e] << 8));
+    } else {
+      uint32_t v = 0;
+      for (int b = 0; b < 4; ++b) v |= (uint32_t)sym[b * rp + e] << (8 * b);
+      ((uint32_t*)out)[e] = v;
+    }
+    return;
+  }
+  const uint32_t r0 = (u - n_pb) * kLzRecBlk;
+  if (r0 >= s.tc) return;
+  const DevSlot* sl = lz_slot(a, j);
+  const int rb = sl->record_bytes, na = s.n_act, G = s.G;
+  const int nr = (int)min((uint32_t)kLzRecBlk, s.tc - r0);
+  for (int k = 0; k < 8; ++k) {
+    const uint8_t* in = sym + lz_plane_off(s, s.esz + k) + (size_t)r0 * na;
+    for (int i = tid; i < nr * na; i += kLzThreads) {
+      const int t = i / na, g = i - t * na;
+      lds[t * rb + g * 8 + k] = in[i];
+    }
+  }
+  for (int g = 0; g < na; ++g) {
+    const int b = s.width[g], co = sl->chunk_off[g], nb = G * b / 8;
+    const uint8_t* in = sym + lz_code_off(s, g) + (size_t)r0 * G;
+    for (int i = tid; i < nr * nb; i += kLzThreads) {
+      const int t = i / nb, y = i - t * nb;
+      const int lo = 8 * y, c0 = lo / b, c1 = min(G - 1, (lo + 7) / b);
+      uint32_t v = 0;
+      for (int c = c0; c <= c1; ++c) {
+        const int sh = c * b - lo;
+        const uint32_t q = in[t * G + c];
+        v |= sh >= 0 ? q << sh : q >> -sh;
+      }
+      lds[t * rb + co + y] = (uint8_t)v;
+    }
+  }
+  __syncthreads();
+  uint8_t* base = dst + kHeaderBytes + (size_t)s.n_pt * s.esz + (size_t)r0 * rb;
+  const int nbytes = nr * rb;
+  for (int i = tid * 4; i + 4 <= nbytes; i += kLzThreads * 4) *(uint32_t*)(base + i) = *(const uint32_t*)(lds + i);
+  for (int i = (nbytes & ~3) + tid; i < nbytes; i += kLzThreads) base[i] = lds[i];
+}
+
+int grid_of(uint32_t n, uint32_t per) { return (int)((n + per - 1) / per); }
+
+}  // namespace
+
+int launch_lz_encode(const LzArgs& a, hipStream_t s) {
+  if (a.units) hipLaunchKernelGGL(lz_split_kernel, dim3(a.units), dim3(kLzThreads), a.rec_lds, s, a);
+  if (a.segs) hipLaunchKernelGGL(lz_hist_kernel, dim3(a.segs), dim3(kLzThreads), 0, s, a);
+  if (a.fields) hipLaunchKernelGGL(lz_model_kernel, dim3(a.fields), dim3(64), 0, s, a);
+  if (a.chunks) hipLaunchKernelGGL(lz_code_kernel, dim3(grid_of(a.chunks, kLzThreads)), dim3(kLzThreads), 0, s, a);
+  hipLaunchKernelGGL(lz_layout_kernel, dim3(a.n_jobs), dim3(kLzThreads), 0, s, a);
+  if (a.chunks) hipLaunchKernelGGL(lz_copy_kernel, dim3(grid_of(a.chunks, kLzThreads / 64)), dim3(kLzThreads), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+int launch_lz_decode(const LzArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(lz_check_kernel, dim3(a.n_jobs), dim3(kLzThreads), 0, s, a);
+  if (a.fields) hipLaunchKernelGGL(lz_dmodel_kernel, dim3(a.fields), dim3(64), 0, s, a);
+  if (a.chunks) hipLaunchKernelGGL(lz_decode_kernel, dim3(grid_of(a.chunks, kLzThreads)), dim3(kLzThreads), 0, s, a);
+  if (a.units) hipLaunchKernelGGL(lz_merge_kernel, dim3(a.units), dim3(kLzThreads), a.rec_lds, s, a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace kvtc

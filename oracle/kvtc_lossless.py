@@ -50,7 +50,9 @@ Container (little-endian):
   128  per field: u32 n_symbols, u16 alphabet A, u16 0, u16 f[A]
   then u32 end[n_chunks]: end of each chunk's payload relative to
        payload_offset (chunks in field order, then chunk order)
-  payload_offset = that position rounded up to 16; then the payloads.
+  payload_offset = that position rounded up to 16; then the payloads, then
+  zeros up to container_bytes, the end of the last payload rounded up to 16
+  (so a reader may fetch whole 16-byte blocks).
 """
 from __future__ import annotations
 
@@ -215,13 +217,14 @@ def compress(stream: bytes, params, slot, T: int) -> bytes:
     ends = np.cumsum([2 * len(p) for p in payloads]).astype("<u4")
     dir_off = CONTAINER_HEADER + HEADER_BYTES + sum(len(t) for t in tables)
     pay_off = (dir_off + 4 * n_chunks + 15) // 16 * 16
-    total = pay_off + (int(ends[-1]) if n_chunks else 0)
+    total = (pay_off + (int(ends[-1]) if n_chunks else 0) + 15) // 16 * 16
     head = (MAGIC + struct.pack("<HHIIQQI", VERSION, len(fields), CHUNK, n_chunks, len(stream),
                                 total, pay_off))
     body = (head + bytes(CONTAINER_HEADER - len(head)) + bytes(stream[:HEADER_BYTES])
             + b"".join(tables) + ends.tobytes())
     body += bytes(pay_off - len(body))
     body += b"".join(p.astype("<u2").tobytes() for p in payloads)
+    body += bytes(total - len(body))
     assert len(body) == total
     return body
 
@@ -272,4 +275,4 @@ def container_bound(params, slot, T: int) -> int:
     alph = [256] * (params.elem_bytes + 8) + [1 << int(slot.widths[g]) for g in slot.active_groups]
     n_chunks = sum((n + CHUNK - 1) // CHUNK for n in sizes)
     head = CONTAINER_HEADER + HEADER_BYTES + sum(8 + 2 * a for a in alph) + 4 * n_chunks
-    return (head + 15) // 16 * 16 + sum(2 * n for n in sizes) + 4 * n_chunks
+    return (head + 15) // 16 * 16 + sum(2 * n for n in sizes) + 4 * n_chunks + 15

@@ -320,3 +320,15 @@ def test_calibrate_set_errors_leave_codec_unchanged():
             c.calibrate_set(args, flags)
         assert e.value.status == K.KVTC_E_INVALID
         assert c.save() == before
+
+
+def test_lossless_bound_matches_oracle():
+    """The library's container bound and the oracle's agree on every shape of
+    the lossless pins (no device needed), and an uncalibrated slot has none."""
+    import oracle.kvtc_lossless as LZ
+    for p, sl, T, _ in pins.lossless_streams():
+        c = K.Codec.load(O.Artifact(p, {(0, 0): sl}).serialize())
+        assert c.lossless_bound(0, 0, T) == LZ.container_bound(p, sl, T), (p, T)
+        job = K.make_job(0, 0, T, 16, 16, 1 << 30, src_capacity=1 << 30)
+        assert c.lossless_workspace_bytes([job], True) > c.lossless_workspace_bytes([job], False) > 0
+    assert c.lossless_bound(0, 1, 100) == 0
