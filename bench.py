@@ -351,6 +351,8 @@ def main():
                         "r_eff": sorted(set(r_eff.values()))},
         "calibration_s": None if args.load_artifact else round(calib_s, 1),
     }
+    result["lossless"] = lossless_stage(K, codec, jobs, sizes, offs, sbuf, T, F, esz, dev, stream,
+                                        args.steps, raw_s / z_s)
     if pipe is not None:
         result["pipeline"] = pipe.overlap(stream)
     else:
@@ -435,6 +437,59 @@ class Pipeline:
         t_p = float(np.median(times))
         return {"unpack_ms": round(float(t_u), 4), "restore_ms": round(float(t_r), 4),
                 "pipelined_ms": round(t_p, 4), "overlap": round(float(t_u + t_r) / t_p, 3)}
+
+
+def lossless_stage(K, codec, jobs, sizes, offs, sbuf, T, F, esz, dev, stream, reps, deflate_ratio):
+    """The GPU lossless stage over every stream of the step: one
+    kvtc_lossless_encode call (streams -> containers) and one
+    kvtc_lossless_decode call (containers -> streams), timed with events;
+    the decoded streams must equal the originals byte for byte. Throughput is
+    stream bytes per second; the ratio is raw KV bytes over container bytes,
+    beside host zlib's on the sampled streams."""
+    import torch
+    n = len(jobs)
+    bounds = [codec.lossless_bound(l, k, T) for l, k, _ in jobs]
+    coff = np.cumsum([0] + [(b + 255) // 256 * 256 for b in bounds])
+    cbuf = torch.zeros(int(coff[-1]), dtype=torch.uint8, device=dev)
+    back = torch.zeros_like(sbuf)
+    ej = [K.make_job(l, k, T, sbuf.data_ptr() + int(offs[i]), cbuf.data_ptr() + int(coff[i]), bounds[i],
+                     src_capacity=sizes[i]) for i, (l, k, _) in enumerate(jobs)]
+    n_e = codec.lossless_workspace_bytes(ej, True)
+    wse = torch.zeros(n_e, dtype=torch.uint8, device=dev)
+    dj = [K.make_job(l, k, T, cbuf.data_ptr() + int(coff[i]), back.data_ptr() + int(offs[i]), sizes[i],
+                     src_capacity=bounds[i]) for i, (l, k, _) in enumerate(jobs)]
+    n_d = codec.lossless_workspace_bytes(dj, False)
+    wsd = torch.zeros(n_d, dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+
+    t_enc = timed(lambda: codec.lossless_encode(ej, wse, n_e, stream))
+    if np.any(K.kvtc_read_device_status(wse, n, stream) != 0):
+        raise SystemExit("device status errors in the lossless encode")
+    csizes = K.kvtc_lossless_sizes(wse, n, stream)
+    t_dec = timed(lambda: codec.lossless_decode(dj, wsd, n_d, stream))
+    if np.any(K.kvtc_read_device_status(wsd, n, stream) != 0):
+        raise SystemExit("device status errors in the lossless decode")
+    for i in range(n):
+        a, b = int(offs[i]), int(offs[i]) + sizes[i]
+        if not torch.equal(sbuf[a:b], back[a:b]):
+            raise SystemExit(f"lossless round trip differs on tensor {i}")
+    st_bytes, c_bytes = int(sum(sizes)), int(csizes.sum())
+    raw = n * T * F * esz
+    return {"encode_ms": round(t_enc * 1e3, 4), "decode_ms": round(t_dec * 1e3, 4),
+            "encode_stream_GBps": round(st_bytes / t_enc / 1e9, 2),
+            "decode_stream_GBps": round(st_bytes / t_dec / 1e9, 2),
+            "stream_bytes": st_bytes, "container_bytes": c_bytes,
+            "raw_over_stream": round(raw / st_bytes, 3), "raw_over_container": round(raw / c_bytes, 3),
+            "raw_over_deflate_sample": round(deflate_ratio, 3), "round_trip": "exact"}
 
 
 def online_encode(K, codec, jobs, sizes, offs, T, F, dev, stream, hidden=4096, reps=3, enc_wgs=32):
