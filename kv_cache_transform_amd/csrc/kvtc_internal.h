@@ -176,8 +176,10 @@ __host__ __device__ constexpr size_t rest_lds_bytes(int ks, bool fused, size_t r
 // Lossless stage: a KVTC stream <-> a KVTZ container (layout in kvtc.h at
 // kvtc_lossless_encode). The stream is split into fields (passthrough byte
 // planes, shift and scale byte planes, one field of codes per active group),
-// each coded by static rANS in independent chunks of kLzChunk symbols.
-constexpr int kLzChunk = 1024;
+// each coded by static rANS in independent chunks of kLzChunk symbols, each
+// chunk with kLzLanes interleaved states (one wavefront per chunk).
+constexpr int kLzLanes = 64;
+constexpr int kLzChunk = 256 * kLzLanes;
 constexpr int kLzMBits = 12;
 constexpr uint32_t kLzM = 1u << kLzMBits;
 constexpr uint32_t kLzL = 1u << 16;
@@ -230,9 +232,9 @@ __host__ __device__ inline LzField lz_field(const LzShape& s, int f) {
   return r;
 }
 // encode: symbols, histograms, models (f | c << 16, then 1/f in fp64),
-// per-chunk emitted-word counts, final states and payload offsets, and the
-// scratch words; decode: symbols, models (f | c << 16, then the
-// slot -> symbol tables of kLzM bytes).
+// per-chunk emitted-word counts, kLzLanes final states and payload offsets,
+// and the scratch words; decode: symbols, then per field the slot table of
+// kLzM words (symbol | (f - 1) << 8 | (slot - c) << 20).
 __host__ __device__ inline LzLayout lz_layout(const LzShape& s, bool enc) {
   const int nf = lz_nf(s);
   const LzField e = lz_field(s, nf);
@@ -244,20 +246,21 @@ __host__ __device__ inline LzLayout lz_layout(const LzShape& s, bool enc) {
   L.sym = 0;
   L.hist = align_up(e.sym_off, 256);
   L.fc = L.hist + (enc ? (size_t)nf * 256 * 4 : 0);
-  L.aux = L.fc + (size_t)nf * 256 * 4;
-  L.cnt = align_up(L.aux + (size_t)nf * (enc ? 256 * 8 : kLzM), 256);
+  L.aux = L.fc + (enc ? (size_t)nf * 256 * 4 : 0);
+  L.cnt = align_up(L.aux + (size_t)nf * (enc ? 256 * 8 : kLzM * 4), 256);
   L.state = L.cnt + (size_t)L.n_chunks * 4;
-  L.dsto = L.state + (size_t)L.n_chunks * 4;
+  L.dsto = L.state + (size_t)L.n_chunks * 4 * kLzLanes;
   L.scratch = align_up(L.dsto + (size_t)L.n_chunks * 4, 256);
   L.bytes = align_up(L.scratch + (enc ? (size_t)L.n_chunks * kLzChunk * 2 : 0), 256);
   return L;
 }
-// Largest container a stream of this shape needs (every chunk one word per
-// symbol plus its two state words, and the 16-byte tail padding).
+// Largest container a stream of this shape needs (one word per symbol, every
+// chunk's kLzLanes states, and the 16-byte tail padding).
 __host__ __device__ inline size_t lz_bound(const LzShape& s) {
   const LzLayout L = lz_layout(s, false);
   size_t b = L.pay_off + 15;
-  for (int f = 0; f < lz_nf(s); ++f) b += 2 * (size_t)lz_n(s, f) + 4 * (size_t)lz_chunks(lz_n(s, f));
+  for (int f = 0; f < lz_nf(s); ++f)
+    b += 2 * (size_t)lz_n(s, f) + 4 * kLzLanes * (size_t)lz_chunks(lz_n(s, f));
   return b;
 }
 

@@ -6,14 +6,17 @@
 // the fp32 shifts and scales, one field of codes per active group), each
 // field gets a static model (its histogram normalised to kLzM), and each
 // field is coded by rANS (range asymmetric numeral systems, J. Duda) in
-// independent chunks of kLzChunk symbols, one chunk per lane. The container
-// layout is written out in kvtc.h at kvtc_lossless_encode.
+// independent chunks of kLzChunk symbols. A chunk has 64 interleaved states
+// and is coded by one wavefront, one state per lane: each step codes 64
+// consecutive symbols, and the words the step emits or takes are placed by a
+// ballot and a prefix count. The container layout is written out in kvtc.h
+// at kvtc_lossless_encode.
 //
 // Encode: split (stream -> field symbols), histogram, model (normalise,
-// write the tables), code (one lane per chunk, words into scratch), layout
+// write the tables), code (one wavefront per chunk, words into scratch), layout
 // (per job: chunk directory by a prefix sum, container header), copy
 // (payloads in decoder order). Decode: check (container header, tables,
-// directory), model (slot -> symbol tables), decode (one lane per chunk),
+// directory), model (slot tables), decode (one wavefront per chunk),
 // merge (field symbols -> stream). Every kernel is memory- or latency-bound;
 // no matrix unit is involved.
 #include "kvtc_device.h"
@@ -265,11 +268,17 @@ __global__ void __launch_bounds__(64) lz_model_kernel(const LzArgs a) {
   }
 }
 
-// One lane per chunk: rANS from the chunk's last symbol to its first; the
-// emitted words go to the chunk's scratch in emission order.
-__global__ void __launch_bounds__(kLzThreads) lz_code_kernel(const LzArgs a) {
-  const uint32_t g = blockIdx.x * kLzThreads + threadIdx.x;
-  if (g >= a.chunks) return;
+__device__ __forceinline__ uint64_t lanes_below(int l) { return (1ull << l) - 1ull; }
+
+// One wavefront per chunk: the steps from the last to the first, lane l
+// coding symbol 64 t + l with its own state. A step's emitted words go to
+// the chunk's scratch in reverse decoder order (the copy kernel reverses
+// them): the k words of a step take the next k positions, the lane of rank
+// r among the emitting lanes position k - 1 - r. The next step's symbol and
+// model entries are loaded one step ahead.
+__global__ void __launch_bounds__(kLzLanes) lz_code_kernel(const LzArgs a) {
+  const uint32_t g = blockIdx.x;
+  const int l = threadIdx.x;
   const int ji = lz_job_at<&LzJob::chunk0>(a, g);
   const LzJob& j = a.jobs[ji];
   const LzShape s = lz_shape(a, j);
@@ -283,37 +292,56 @@ __global__ void __launch_bounds__(kLzThreads) lz_code_kernel(const LzArgs a) {
     sym_off += lz_sym_region(lz_n(s, f));
   }
   const LzLayout L = lz_layout(s, true);
-  const uint32_t n = lz_n(s, f);
-  const int len = (int)min((uint32_t)kLzChunk, n - k * kLzChunk);
+  const uint32_t len = min((uint32_t)kLzChunk, lz_n(s, f) - k * kLzChunk);
+  const int steps = (int)((len + kLzLanes - 1) / kLzLanes);
   const uint8_t* sym = j.ws + sym_off + (size_t)k * kLzChunk;
   const uint32_t* fc = (const uint32_t*)(j.ws + L.fc) + f * 256;
   const double* rcp = (const double*)(j.ws + L.aux) + f * 256;
-  uint16_t* out = (uint16_t*)(j.ws + L.scratch) + (size_t)kj * kLzChunk;
+  uint16_t* rev = (uint16_t*)(j.ws + L.scratch) + (size_t)kj * kLzChunk;
   uint32_t x = kLzL, cnt = 0;
-  for (int blk = (len - 1) >> 4; blk >= 0; --blk) {
-    const u32x4 v = *(const u32x4*)(sym + blk * 16);
-    for (int i = min(15, len - 1 - blk * 16); i >= 0; --i) {
-      const uint32_t sy = (v[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-      const uint32_t m = fc[sy], fs = m & 0xFFFFu, cs = m >> 16;
-      if ((uint64_t)x >= ((uint64_t)fs << 20)) {
-        out[cnt++] = (uint16_t)x;
-        x >>= 16;
-      }
-      // floor(x / fs) from the fp64 reciprocal, off by at most one
-      uint32_t q = (uint32_t)((double)x * rcp[sy]);
-      int64_t r = (int64_t)x - (int64_t)q * fs;
-      if (r < 0) {
-        --q;
-        r += fs;
-      } else if (r >= (int64_t)fs) {
-        ++q;
-        r -= fs;
-      }
-      x = (q << kLzMBits) + (uint32_t)r + cs;
+  int t = steps - 1;
+  uint32_t i = (uint32_t)t * kLzLanes + l;
+  bool act = i < len;
+  uint32_t sy = act ? sym[i] : 0u;
+  uint32_t m = fc[sy];
+  double r = rcp[sy];
+  for (; t >= 0; --t) {
+    uint32_t sy2 = 0, m2 = 0;
+    double r2 = 0.0;
+    if (t > 0) {                      // every step before the last is full
+      sy2 = sym[(uint32_t)(t - 1) * kLzLanes + l];
+      m2 = fc[sy2];
+      r2 = rcp[sy2];
     }
+    const uint32_t fs = m & 0xFFFFu, cs = m >> 16;
+    const bool emit = act && (uint64_t)x >= ((uint64_t)fs << 20);
+    const uint64_t mask = __ballot(emit);
+    const uint32_t ke = (uint32_t)__popcll(mask);
+    if (emit) {
+      rev[cnt + ke - 1 - (uint32_t)__popcll(mask & lanes_below(l))] = (uint16_t)x;
+      x >>= 16;
+    }
+    cnt += ke;
+    if (act) {
+      // floor(x / fs) from the fp64 reciprocal, off by at most one
+      uint32_t q = (uint32_t)((double)x * r);
+      int64_t rm = (int64_t)x - (int64_t)q * fs;
+      if (rm < 0) {
+        --q;
+        rm += fs;
+      } else if (rm >= (int64_t)fs) {
+        ++q;
+        rm -= fs;
+      }
+      x = (q << kLzMBits) + (uint32_t)rm + cs;
+    }
+    sy = sy2;
+    m = m2;
+    r = r2;
+    act = t > 0;
   }
-  ((uint32_t*)(j.ws + L.cnt))[kj] = cnt;
-  ((uint32_t*)(j.ws + L.state))[kj] = x;
+  ((uint32_t*)(j.ws + L.state))[(size_t)kj * kLzLanes + l] = x;
+  if (l == 0) ((uint32_t*)(j.ws + L.cnt))[kj] = cnt;
 }
 
 // One workgroup per job: payload sizes -> chunk directory (prefix sum) and
@@ -330,7 +358,7 @@ __global__ void __launch_bounds__(kLzThreads) lz_layout_kernel(const LzArgs a) {
   uint32_t run = 0;
   for (uint32_t k0 = 0; k0 < L.n_chunks; k0 += kLzThreads) {
     const uint32_t k = k0 + tid;
-    const uint32_t bytes = k < L.n_chunks ? 4 + 2 * cnt[k] : 0;
+    const uint32_t bytes = k < L.n_chunks ? 4 * kLzLanes + 2 * cnt[k] : 0;
     const uint32_t inc = wave_scan(bytes, lane);
     if (lane == 63) part[w] = inc;
     __syncthreads();
@@ -370,24 +398,23 @@ __global__ void __launch_bounds__(kLzThreads) lz_layout_kernel(const LzArgs a) {
   if (tid == 0) a.sizes[j.status_idx] = total;
 }
 
-// One wave per chunk: its payload in decoder order (final state, then the
-// emitted words, last emitted first).
+// One workgroup per chunk: its payload in decoder order (the 64 final
+// states, then the words, reversed from the scratch).
 __global__ void __launch_bounds__(kLzThreads) lz_copy_kernel(const LzArgs a) {
-  const uint32_t g = blockIdx.x * (kLzThreads / 64) + (threadIdx.x >> 6);
-  if (g >= a.chunks) return;
-  const int lane = threadIdx.x & 63;
+  const uint32_t g = blockIdx.x;
   const int ji = lz_job_at<&LzJob::chunk0>(a, g);
   const LzJob& j = a.jobs[ji];
   const LzShape s = lz_shape(a, j);
   const LzLayout L = lz_layout(s, true);
   const uint32_t k = g - j.chunk0;
   const uint32_t cnt = ((const uint32_t*)(j.ws + L.cnt))[k];
-  const uint32_t x = ((const uint32_t*)(j.ws + L.state))[k];
   const uint32_t off = ((const uint32_t*)(j.ws + L.dsto))[k];
+  const uint32_t* st = (const uint32_t*)(j.ws + L.state) + (size_t)k * kLzLanes;
   const uint16_t* sc = (const uint16_t*)(j.ws + L.scratch) + (size_t)k * kLzChunk;
   uint16_t* out = (uint16_t*)(j.dst + L.pay_off + off);
-  for (uint32_t i = lane; i < cnt + 2; i += 64)
-    out[i] = i == 0 ? (uint16_t)x : i == 1 ? (uint16_t)(x >> 16) : sc[cnt - 1 - (i - 2)];
+  constexpr uint32_t nst = 2 * kLzLanes;
+  for (uint32_t i = threadIdx.x; i < cnt + nst; i += kLzThreads)
+    out[i] = i < nst ? (uint16_t)(st[i >> 1] >> (16 * (i & 1))) : sc[cnt - 1 - (i - nst)];
 }
 
 // ------------------------------------------------------------- decode ----
@@ -431,7 +458,7 @@ __global__ void __launch_bounds__(kLzThreads) lz_check_kernel(const LzArgs a) {
   const uint32_t* dir = (const uint32_t*)(j.src + L.dir_off);
   for (uint32_t k = tid; k < L.n_chunks; k += kLzThreads) {
     const uint32_t e = dir[k], p = k ? dir[k - 1] : 0;
-    if ((e & 1u) || e < p + 4 || (uint64_t)L.pay_off + e > total) atomicMax(&bad, (int)-KVTC_E_CORRUPT);
+    if ((e & 1u) || e < p + 4 * kLzLanes || (uint64_t)L.pay_off + e > total) atomicMax(&bad, (int)-KVTC_E_CORRUPT);
   }
   __syncthreads();
   if (tid == 0) {
@@ -443,9 +470,11 @@ __global__ void __launch_bounds__(kLzThreads) lz_check_kernel(const LzArgs a) {
 }
 
 // One wave per field: the model from the container's table (it must sum to
-// M): f | c << 16 per symbol, and the slot -> symbol table.
+// M) as the slot table: per slot, its symbol s | (f_s - 1) << 8 |
+// (slot - c_s) << 20.
 __global__ void __launch_bounds__(64) lz_dmodel_kernel(const LzArgs a) {
   __shared__ uint32_t cum[256];
+  __shared__ uint32_t frq[256];
   const int ji = lz_job_at<&LzJob::field0>(a, blockIdx.x);
   const LzJob& j = a.jobs[ji];
   if (lz_failed(a, j)) return;
@@ -456,17 +485,15 @@ __global__ void __launch_bounds__(64) lz_dmodel_kernel(const LzArgs a) {
   const LzField fd = lz_field(s, f);
   const LzLayout L = lz_layout(s, false);
   const uint16_t* fr = (const uint16_t*)(j.src + fd.tab_off + 8);
-  uint32_t* fc = (uint32_t*)(j.ws + L.fc) + f * 256;
-  uint8_t* tbl = j.ws + L.aux + (size_t)f * kLzM;
-  uint32_t fv[4], run = 0;
+  uint32_t* tbl = (uint32_t*)(j.ws + L.aux) + (size_t)f * kLzM;
+  uint32_t run = 0;
   for (int q = 0; q < 4; ++q) {
     const int sy = lane + 64 * q;
-    fv[q] = sy < A ? fr[sy] : 0u;
-    const uint32_t inc = wave_scan(fv[q], lane);
-    const uint32_t c = run + inc - fv[q];
+    const uint32_t fv = sy < A ? fr[sy] : 0u;
+    const uint32_t inc = wave_scan(fv, lane);
+    cum[sy] = sy < A ? run + inc - fv : 0xFFFFFFFFu;
+    frq[sy] = fv;
     run += (uint32_t)__shfl((int)inc, 63, 64);
-    if (sy < A) fc[sy] = fv[q] | (c << 16);
-    cum[sy] = sy < A ? c : 0xFFFFFFFFu;
   }
   if (run != kLzM) {
     if (lane == 0) lz_set(a, j, KVTC_E_CORRUPT);
@@ -480,16 +507,20 @@ __global__ void __launch_bounds__(64) lz_dmodel_kernel(const LzArgs a) {
       if (cum[mid] <= slot) lo = mid;
       else hi = mid - 1;
     }
-    tbl[slot] = (uint8_t)lo;
+    tbl[slot] = (uint32_t)lo | ((frq[lo] - 1u) << 8) | ((slot - cum[lo]) << 20);
   }
 }
 
-// One lane per chunk: rANS decoding, the payload read through two 16-byte
-// blocks (the container is padded to 16 bytes), symbols stored four at a
-// time into the field.
-__global__ void __launch_bounds__(kLzThreads) lz_decode_kernel(const LzArgs a) {
-  const uint32_t g = blockIdx.x * kLzThreads + threadIdx.x;
-  if (g >= a.chunks) return;
+// One wavefront per chunk, lane l decoding symbols 64 t + l with its own
+// state: per step a slot-table lookup (LDS) and the state update; the lanes
+// whose state fell below L take the next words in lane order (ballot and
+// prefix count), read from three 64-word windows of the payload held in
+// registers (lane l holds word base + l of each) through lane permutes;
+// a window is loaded two windows ahead of its use.
+__global__ void __launch_bounds__(kLzLanes) lz_decode_kernel(const LzArgs a) {
+  __shared__ uint32_t tbl[kLzM];
+  const uint32_t g = blockIdx.x;
+  const int l = threadIdx.x;
   const int ji = lz_job_at<&LzJob::chunk0>(a, g);
   const LzJob& j = a.jobs[ji];
   if (lz_failed(a, j)) return;
@@ -504,51 +535,50 @@ __global__ void __launch_bounds__(kLzThreads) lz_decode_kernel(const LzArgs a) {
     sym_off += lz_sym_region(lz_n(s, f));
   }
   const LzLayout L = lz_layout(s, false);
-  const uint32_t n = lz_n(s, f);
-  const int len = (int)min((uint32_t)kLzChunk, n - k * kLzChunk);
+  const u32x4* gt = (const u32x4*)(j.ws + L.aux + (size_t)f * kLzM * 4);
+  for (int i = l; i < (int)kLzM / 4; i += kLzLanes) ((u32x4*)tbl)[i] = gt[i];
+  const uint32_t len = min((uint32_t)kLzChunk, lz_n(s, f) - k * kLzChunk);
+  const int steps = (int)((len + kLzLanes - 1) / kLzLanes);
   const uint32_t* dir = (const uint32_t*)(j.src + L.dir_off);
-  const uint32_t total = ((const uint32_t*)j.src)[6];
-  uint32_t pos = L.pay_off + (kj ? dir[kj - 1] : 0u);
-  const uint32_t end = L.pay_off + dir[kj];
-  const uint32_t* fc = (const uint32_t*)(j.ws + L.fc) + f * 256;
-  const uint8_t* tbl = j.ws + L.aux + (size_t)f * kLzM;
-  uint32_t* out = (uint32_t*)(j.ws + sym_off + (size_t)k * kLzChunk);
-  uint32_t blk = pos >> 4;
-  u32x4 cur = *(const u32x4*)(j.src + (size_t)blk * 16);
-  u32x4 nxt = (blk + 1) * 16 < total ? *(const u32x4*)(j.src + (size_t)(blk + 1) * 16) : u32x4(0u);
-  auto word = [&]() -> uint32_t {
-    if ((pos >> 4) != blk) {
-      ++blk;
-      cur = nxt;
-      nxt = (blk + 1) * 16 < total ? *(const u32x4*)(j.src + (size_t)(blk + 1) * 16) : u32x4(0u);
-    }
-    const uint32_t wv = (cur[(pos >> 2) & 3] >> (8 * (pos & 2))) & 0xFFFFu;
-    pos += 2;
-    return wv;
-  };
-  uint32_t x = word();
-  x |= word() << 16;
-  uint32_t acc = 0;
+  const uint32_t start = L.pay_off + (kj ? dir[kj - 1] : 0u);
+  const uint32_t nw = (L.pay_off + dir[kj] - start) / 2;     // >= 128, checked
+  const uint16_t* w = (const uint16_t*)(j.src + start);
+  uint8_t* out = j.ws + sym_off + (size_t)k * kLzChunk;
+  uint32_t x = (uint32_t)w[2 * l] | ((uint32_t)w[2 * l + 1] << 16);
+  uint32_t pos = 2 * kLzLanes, wb = pos;
+  auto load = [&](uint32_t b) -> uint32_t { return b + l < nw ? (uint32_t)w[b + l] : 0u; };
+  uint32_t w0 = load(wb), w1 = load(wb + kLzLanes), w2 = load(wb + 2 * kLzLanes);
+  __syncthreads();
   bool ok = true;
-  for (int i = 0; i < len; ++i) {
-    const uint32_t slot = x & (kLzM - 1);
-    const uint32_t sy = tbl[slot];
-    const uint32_t m = fc[sy];
-    x = (m & 0xFFFFu) * (x >> kLzMBits) + slot - (m >> 16);
-    if (x < kLzL) {
-      if (pos >= end) {
-        ok = false;
-        break;
-      }
-      x = (x << 16) | word();
+  for (int t = 0; t < steps; ++t) {
+    const uint32_t i = (uint32_t)t * kLzLanes + l;
+    const bool act = i < len;
+    const uint32_t e = tbl[x & (kLzM - 1)];
+    if (act) {
+      x = (((e >> 8) & 0xFFFu) + 1u) * (x >> kLzMBits) + (e >> 20);
+      out[i] = (uint8_t)e;
     }
-    acc |= sy << (8 * (i & 3));
-    if ((i & 3) == 3 || i == len - 1) {
-      out[i >> 2] = acc;
-      acc = 0;
+    const bool need = act && x < kLzL;
+    const uint64_t mask = __ballot(need);
+    const uint32_t kn = (uint32_t)__popcll(mask);
+    if (pos + kn > nw) {
+      ok = false;
+      break;
+    }
+    const uint32_t idx = pos - wb + (uint32_t)__popcll(mask & lanes_below(l));
+    const uint32_t v0 = (uint32_t)__shfl((int)w0, (int)(idx & 63u), 64);
+    const uint32_t v1 = (uint32_t)__shfl((int)w1, (int)(idx & 63u), 64);
+    if (need) x = (x << 16) | (idx < (uint32_t)kLzLanes ? v0 : v1);
+    pos += kn;
+    if (pos - wb >= (uint32_t)kLzLanes) {
+      wb += kLzLanes;
+      w0 = w1;
+      w1 = w2;
+      w2 = load(wb + 2 * kLzLanes);
     }
   }
-  if (!ok || pos != end || x != kLzL) lz_set(a, j, KVTC_E_CORRUPT);
+  const bool bad = !ok || pos != nw || __ballot(x != kLzL) != 0ull;
+  if (bad && l == 0) lz_set(a, j, KVTC_E_CORRUPT);
 }
 
 // One unit per block of passthrough elements or records: field symbols back
@@ -614,24 +644,22 @@ __global__ void __launch_bounds__(kLzThreads) lz_merge_kernel(const LzArgs a) {
   for (int i = (nbytes & ~3) + tid; i < nbytes; i += kLzThreads) base[i] = lds[i];
 }
 
-int grid_of(uint32_t n, uint32_t per) { return (int)((n + per - 1) / per); }
-
 }  // namespace
 
 int launch_lz_encode(const LzArgs& a, hipStream_t s) {
   if (a.units) hipLaunchKernelGGL(lz_split_kernel, dim3(a.units), dim3(kLzThreads), a.rec_lds, s, a);
   if (a.segs) hipLaunchKernelGGL(lz_hist_kernel, dim3(a.segs), dim3(kLzThreads), 0, s, a);
   if (a.fields) hipLaunchKernelGGL(lz_model_kernel, dim3(a.fields), dim3(64), 0, s, a);
-  if (a.chunks) hipLaunchKernelGGL(lz_code_kernel, dim3(grid_of(a.chunks, kLzThreads)), dim3(kLzThreads), 0, s, a);
+  if (a.chunks) hipLaunchKernelGGL(lz_code_kernel, dim3(a.chunks), dim3(kLzLanes), 0, s, a);
   hipLaunchKernelGGL(lz_layout_kernel, dim3(a.n_jobs), dim3(kLzThreads), 0, s, a);
-  if (a.chunks) hipLaunchKernelGGL(lz_copy_kernel, dim3(grid_of(a.chunks, kLzThreads / 64)), dim3(kLzThreads), 0, s, a);
+  if (a.chunks) hipLaunchKernelGGL(lz_copy_kernel, dim3(a.chunks), dim3(kLzThreads), 0, s, a);
   return (int)hipGetLastError();
 }
 
 int launch_lz_decode(const LzArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(lz_check_kernel, dim3(a.n_jobs), dim3(kLzThreads), 0, s, a);
   if (a.fields) hipLaunchKernelGGL(lz_dmodel_kernel, dim3(a.fields), dim3(64), 0, s, a);
-  if (a.chunks) hipLaunchKernelGGL(lz_decode_kernel, dim3(grid_of(a.chunks, kLzThreads)), dim3(kLzThreads), 0, s, a);
+  if (a.chunks) hipLaunchKernelGGL(lz_decode_kernel, dim3(a.chunks), dim3(kLzLanes), 0, s, a);
   if (a.units) hipLaunchKernelGGL(lz_merge_kernel, dim3(a.units), dim3(kLzThreads), a.rec_lds, s, a);
   return (int)hipGetLastError();
 }

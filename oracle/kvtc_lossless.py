@@ -17,8 +17,9 @@ our own that knows the stream's layout (READING L1):
       group (one symbol per code, alphabet 2^b).  Each field is coded on its
       own with a static model (its normalised histogram) by range asymmetric
       numeral systems (rANS: J. Duda, "Asymmetric numeral systems", 2009 and
-      2013), in independent chunks of CHUNK symbols so that chunks code in
-      parallel.  The 64-byte stream header is kept verbatim.
+      2013), in independent chunks of CHUNK symbols with 64 interleaved states each,
+      so that chunks code in parallel and the 64 lanes of a wavefront code
+      one chunk together.  The 64-byte stream header is kept verbatim.
 
 Fields, in order (esz = 2 for bf16, 4 for f32; n_act active groups):
   P_j, j < esz   byte j (little-endian) of every passthrough element: rows
@@ -34,14 +35,21 @@ of symbols present, M = 4096.  f_s = 0 if h_s = 0, else 1 + floor(h_s *
 (M - n_p) / N); the remainder M - sum f goes to the most frequent symbol
 (lowest index on ties).  c_s = sum of f over symbols below s.
 
-rANS (state x, L = 2^16, 16-bit words): a chunk s_0 .. s_{n-1} is encoded
-from its last symbol to its first, starting at x = L; for each symbol, if
-x >= f_s * 2^20 the low 16 bits of x are emitted and x >>= 16; then
-x = floor(x / f_s) * M + (x mod f_s) + c_s.  The chunk's payload is the
-final x as two words (low, high), then the emitted words, last emitted
-first.  Decoding reads x from the first two words; per symbol, slot =
-x mod M, s is the symbol with c_s <= slot < c_s + f_s, x = f_s * floor(x / M)
-+ slot - c_s, and if x < L the next word w gives x = x * 2^16 + w.
+rANS (32-bit states, L = 2^16, 16-bit words), 64 states per chunk: symbol i
+of a chunk of n <= CHUNK = 16384 symbols belongs to state (lane) i mod 64 and
+to step i div 64.  Encoding starts every state at L and runs the steps from
+the last to the first; in a step, every lane with a symbol s: if
+x >= f_s * 2^20 it emits the low 16 bits of x and x >>= 16, then
+x = floor(x / f_s) * M + (x mod f_s) + c_s.  The chunk's payload is the 64
+final states, each as (low word, high word), then the emitted words step by
+step from step 0 to the last, inside a step in ascending lane order.
+Decoding reads the 64 states and runs the steps from the first: every lane
+with a symbol takes slot = x mod M, s with c_s <= slot < c_s + f_s,
+x = f_s * floor(x / M) + slot - c_s; then the lanes with x < L, in ascending
+lane order, each take the next word w: x = x * 2^16 + w.  Every state ends at
+L and every word is used.  (Independent states let the 64 lanes of a GPU
+wavefront code one chunk together; the word order is what a wavefront
+produces with a ballot and a prefix count.)
 
 Container (little-endian):
   0    "KVTZ", u16 version = 1, u16 n_fields, u32 CHUNK, u32 n_chunks,
@@ -64,7 +72,8 @@ from .kvtc_oracle import HEADER_BYTES, OracleError, pack_codes, split_rows, unpa
 
 MAGIC = b"KVTZ"
 VERSION = 1
-CHUNK = 1024
+LANES = 64
+CHUNK = 16384
 M_BITS = 12
 M = 1 << M_BITS
 RANS_L = 1 << 16
@@ -138,35 +147,28 @@ def normalize(hist: np.ndarray) -> np.ndarray:
 
 def rans_encode(chunks, f: np.ndarray):
     """Encode each chunk (u8 symbol arrays) with frequencies f; returns the
-    payloads (u16 word arrays, decoder order).  The chunks are independent;
-    they are stepped together, each from its own last symbol to its first."""
-    n = len(chunks)
-    if n == 0:
-        return []
+    payloads (u16 word arrays, decoder order).  The 64 lanes of a step are
+    computed together."""
     f = np.asarray(f, np.uint64)
     c = np.concatenate([[0], np.cumsum(f)[:-1]]).astype(np.uint64)
-    lens = np.array([len(ch) for ch in chunks])
-    width = int(lens.max())
-    sym = np.zeros((n, width), np.int64)
-    for k, ch in enumerate(chunks):
-        sym[k, :len(ch)] = ch
-    x = np.full(n, RANS_L, np.uint64)
-    emitted = np.zeros((n, width), np.uint16)
-    cnt = np.zeros(n, np.int64)
-    for i in range(width - 1, -1, -1):
-        act = i < lens
-        s = sym[:, i]
-        fs, cs = np.where(act, f[s], 1).astype(np.uint64), c[s]     # chunks already done: any f
-        emit = act & (x >= (fs << np.uint64(20)))
-        emitted[emit, cnt[emit]] = (x[emit] & np.uint64(0xFFFF)).astype(np.uint16)
-        cnt[emit] += 1
-        x = np.where(emit, x >> np.uint64(16), x)
-        xn = (x // fs) * np.uint64(M) + (x % fs) + cs
-        x = np.where(act, xn, x)
     out = []
-    for k in range(n):
-        words = [int(x[k]) & 0xFFFF, int(x[k]) >> 16] + emitted[k, :cnt[k]][::-1].tolist()
-        out.append(np.array(words, np.uint16))
+    for ch in chunks:
+        n = len(ch)
+        steps = (n + LANES - 1) // LANES
+        sym = np.zeros(steps * LANES, np.int64)
+        sym[:n] = ch
+        x = np.full(LANES, RANS_L, np.uint64)
+        groups = []
+        for t in range(steps - 1, -1, -1):
+            act = np.arange(t * LANES, (t + 1) * LANES) < n
+            s = sym[t * LANES:(t + 1) * LANES]
+            fs = np.where(act, f[s], 1).astype(np.uint64)     # lanes without a symbol: any f
+            emit = act & (x >= (fs << np.uint64(20)))
+            groups.append((x[emit] & np.uint64(0xFFFF)).astype(np.uint16))
+            x = np.where(emit, x >> np.uint64(16), x)
+            x = np.where(act, (x // fs) * np.uint64(M) + (x % fs) + c[s], x)
+        states = np.stack([x & np.uint64(0xFFFF), x >> np.uint64(16)], axis=1).reshape(-1)
+        out.append(np.concatenate([states.astype(np.uint16)] + groups[::-1]).astype(np.uint16))
     return out
 
 
@@ -177,24 +179,25 @@ def rans_decode(payloads, lens, f: np.ndarray):
     slot_sym = np.repeat(np.arange(f.size), f)           # slot -> symbol
     out = []
     for words, n in zip(payloads, lens):
-        w = [int(v) for v in words]
-        if len(w) < 2:
-            raise OracleError("chunk payload shorter than its state")
-        x = w[0] | (w[1] << 16)
-        pos = 2
+        w = np.asarray(words, np.int64)
+        if len(w) < 2 * LANES:
+            raise OracleError("chunk payload shorter than its states")
+        x = w[0:2 * LANES:2] | (w[1:2 * LANES:2] << 16)
+        pos = 2 * LANES
         syms = np.zeros(n, np.uint8)
-        for i in range(n):
-            slot = x & (M - 1)
-            s = int(slot_sym[slot])
-            syms[i] = s
-            x = int(f[s]) * (x >> M_BITS) + slot - int(c[s])
-            if x < RANS_L:
-                if pos >= len(w):
-                    raise OracleError("chunk payload ends early")
-                x = (x << 16) | w[pos]
-                pos += 1
-        if pos != len(w) or x != RANS_L:
-            raise OracleError("chunk payload does not end at the initial state")
+        for t in range((n + LANES - 1) // LANES):
+            lanes = np.arange(min(LANES, n - t * LANES))
+            slot = x[lanes] & (M - 1)
+            s = slot_sym[slot]
+            syms[t * LANES + lanes] = s
+            x[lanes] = f[s] * (x[lanes] >> M_BITS) + slot - c[s]
+            need = lanes[x[lanes] < RANS_L]                    # ascending lanes
+            if pos + len(need) > len(w):
+                raise OracleError("chunk payload ends early")
+            x[need] = (x[need] << 16) | w[pos:pos + len(need)]
+            pos += len(need)
+        if pos != len(w) or np.any(x != RANS_L):
+            raise OracleError("chunk payload does not end at the initial states")
         out.append(syms)
     return out
 
@@ -267,12 +270,12 @@ def decompress(container: bytes, params, slot, T: int) -> bytes:
 
 
 def container_bound(params, slot, T: int) -> int:
-    """Largest container a stream of this shape can need: every chunk at one
-    word per symbol plus its state."""
+    """Largest container a stream of this shape can need: one word per symbol
+    plus every chunk's 64 states."""
     s1, w1, tc = split_rows(T, params.sink, params.window)
     n_pt = (s1 + w1) * params.F
     sizes = [n_pt] * params.elem_bytes + [tc * slot.n_act] * 8 + [tc * slot.G] * slot.n_act
     alph = [256] * (params.elem_bytes + 8) + [1 << int(slot.widths[g]) for g in slot.active_groups]
     n_chunks = sum((n + CHUNK - 1) // CHUNK for n in sizes)
     head = CONTAINER_HEADER + HEADER_BYTES + sum(8 + 2 * a for a in alph) + 4 * n_chunks
-    return (head + 15) // 16 * 16 + sum(2 * n for n in sizes) + 4 * n_chunks + 15
+    return (head + 15) // 16 * 16 + sum(2 * n for n in sizes) + 4 * LANES * n_chunks + 15

@@ -204,27 +204,39 @@ def _normalize_no_floor_one(hist):
     return f
 
 
-def _rans_emit_late(chunks, f):
-    """Renormalise when x > f * 2^20 instead of >=."""
-    out = []
+def _interleaved_encode(chunks, f, late=False, descending=False):
+    """The chunk coder with one planted change: renormalise when x > f * 2^20
+    instead of >= (late), or order a step's words by descending lane."""
     f = np.asarray(f, np.int64)
     c = np.concatenate([[0], np.cumsum(f)[:-1]])
-    for ch in chunks:
-        x, em = LZ.RANS_L, []
-        for s in ch[::-1]:
-            if x > (int(f[s]) << 20):
-                em.append(x & 0xFFFF)
-                x >>= 16
-            x = (x // int(f[s])) * LZ.M + x % int(f[s]) + int(c[s])
-        out.append(np.array([x & 0xFFFF, x >> 16] + em[::-1], np.uint16))
-    return out
-
-
-def _rans_words_in_emission_order(chunks, f):
     out = []
-    for p in _orig_lz["rans_encode"](chunks, f):
-        out.append(np.concatenate([p[:2], p[2:][::-1]]).astype(np.uint16))
+    for ch in chunks:
+        n = len(ch)
+        x = [LZ.RANS_L] * LZ.LANES
+        groups = []
+        for t in range((n + LZ.LANES - 1) // LZ.LANES - 1, -1, -1):
+            words = []
+            for l in range(LZ.LANES):
+                i = t * LZ.LANES + l
+                if i >= n:
+                    continue
+                fs, cs = int(f[ch[i]]), int(c[ch[i]])
+                if (x[l] > (fs << 20)) if late else (x[l] >= (fs << 20)):
+                    words.append(x[l] & 0xFFFF)
+                    x[l] >>= 16
+                x[l] = (x[l] // fs) * LZ.M + x[l] % fs + cs
+            groups.append(words[::-1] if descending else words)
+        states = [v for xl in x for v in (xl & 0xFFFF, xl >> 16)]
+        out.append(np.array(states + [w for g in groups[::-1] for w in g], np.uint64).astype(np.uint16))
     return out
+
+
+def _rans_emit_late(chunks, f):
+    return _interleaved_encode(chunks, f, late=True)
+
+
+def _rans_words_descending(chunks, f):
+    return _interleaved_encode(chunks, f, descending=True)
 
 
 def _fields_planes_big_endian(stream, params, slot, T):
@@ -246,7 +258,7 @@ LZ_MUTATIONS = {
     "lz_normalize_remainder_to_first": ("normalize", _normalize_remainder_to_first),
     "lz_normalize_drops_rare": ("normalize", _normalize_no_floor_one),
     "lz_rans_emit_late": ("rans_encode", _rans_emit_late),
-    "lz_rans_word_order": ("rans_encode", _rans_words_in_emission_order),
+    "lz_rans_word_order": ("rans_encode", _rans_words_descending),
     "lz_planes_big_endian": ("stream_fields", _fields_planes_big_endian),
     "lz_codes_component_major": ("stream_fields", _fields_codes_component_major),
 }
