@@ -337,18 +337,21 @@ kvtc_status kvtc_deflate(const void* in, size_t n, void* out, size_t cap, size_t
  * h, n_p present symbols, M = 4096, f_s = 0 if h_s = 0 else
  * 1 + floor(h_s * (M - n_p) / N), the remainder M - sum f added to the most
  * frequent symbol (lowest index on ties), c_s = sum of f below s. Each field
- * is cut into chunks of 1024 symbols (the last one shorter), each coded by
- * rANS (J. Duda's asymmetric numeral systems; 32-bit state, L = 2^16, 16-bit
- * words): from the chunk's last symbol to its first, starting at x = L, if
- * x >= f_s * 2^20 the low 16 bits of x are emitted and x >>= 16, then
- * x = floor(x / f_s) * M + (x mod f_s) + c_s. A chunk's payload is the
- * final x (low word, high word) and the emitted words, last emitted first.
- * Decoding: slot = x mod M, s with c_s <= slot < c_s + f_s,
- * x = f_s * floor(x / M) + slot - c_s, and if x < L, x = x * 2^16 + the next
- * word.
+ * is cut into chunks of 16384 symbols (the last one shorter), each coded by
+ * rANS (J. Duda's asymmetric numeral systems; 32-bit states, L = 2^16,
+ * 16-bit words) with 64 interleaved states: symbol i of a chunk belongs to
+ * state i mod 64 and step i div 64. Encoding starts every state at L and
+ * runs the steps from the last: each state with a symbol s emits its low 16
+ * bits and shifts right by 16 if x >= f_s * 2^20, then
+ * x = floor(x / f_s) * M + (x mod f_s) + c_s. A chunk's payload is the 64
+ * final states (low word, high word), then the emitted words of step 0,
+ * step 1, ..., inside a step by ascending state. Decoding runs the steps
+ * from the first: slot = x mod M, s with c_s <= slot < c_s + f_s,
+ * x = f_s * floor(x / M) + slot - c_s, then the states with x < L take the
+ * next words in ascending order (x = x * 2^16 + w); every state ends at L.
  *
  * Container ("KVTZ", little-endian): u32 magic, u16 version = 1, u16
- * n_fields, u32 chunk symbols = 1024, u32 n_chunks, u64 stream bytes, u64
+ * n_fields, u32 chunk symbols = 16384, u32 n_chunks, u64 stream bytes, u64
  * container bytes, u32 payload offset, zeros to byte 64; the stream's
  * 64-byte header; per field u32 n_symbols, u16 alphabet A, u16 0, u16 f[A];
  * u32 end[n_chunks] (each chunk's payload end relative to the payload
