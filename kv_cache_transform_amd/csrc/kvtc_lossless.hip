@@ -210,7 +210,7 @@ __global__ void __launch_bounds__(kLzThreads) lz_hist_kernel(const LzArgs a) {
 // One wave per field: normalise the histogram (every present symbol gets
 // 1 + floor(h * (M - n_present) / N), the remainder goes to the most
 // frequent symbol, lowest index on ties), write the container's table entry
-// and the coder's model (f | c << 16 and 1/f).
+// and the coder's model (f | c << 16 and a 32-bit reciprocal of f).
 __global__ void __launch_bounds__(64) lz_model_kernel(const LzArgs a) {
   const int ji = lz_job_at<&LzJob::field0>(a, blockIdx.x);
   const LzJob& j = a.jobs[ji];
@@ -227,7 +227,7 @@ __global__ void __launch_bounds__(64) lz_model_kernel(const LzArgs a) {
   }
   const uint32_t* hist = (const uint32_t*)(j.ws + L.hist) + f * 256;
   uint32_t* fc = (uint32_t*)(j.ws + L.fc) + f * 256;
-  double* rcp = (double*)(j.ws + L.aux) + f * 256;
+  uint32_t* rcp = (uint32_t*)(j.ws + L.aux) + f * 256;
   uint32_t hv[4], fv[4];
   uint64_t N = 0;
   uint32_t np = 0, hmax = 0;
@@ -263,7 +263,9 @@ __global__ void __launch_bounds__(64) lz_model_kernel(const LzArgs a) {
     if (sy < A) {
       ((uint16_t*)(tab + 8))[sy] = (uint16_t)fv[q];
       fc[sy] = fv[q] | (c << 16);
-      rcp[sy] = fv[q] ? 1.0 / (double)fv[q] : 0.0;
+      // floor(2^32 / f) (2^32 - 1 for f = 1): x * rcp >> 32 is floor(x / f)
+      // or one less, for every 32-bit x
+      rcp[sy] = fv[q] > 1 ? (uint32_t)(0x100000000ull / fv[q]) : 0xFFFFFFFFu;
     }
   }
 }
@@ -271,12 +273,18 @@ __global__ void __launch_bounds__(64) lz_model_kernel(const LzArgs a) {
 __device__ __forceinline__ uint64_t lanes_below(int l) { return (1ull << l) - 1ull; }
 
 // One wavefront per chunk: the steps from the last to the first, lane l
-// coding symbol 64 t + l with its own state. A step's emitted words go to
-// the chunk's scratch in reverse decoder order (the copy kernel reverses
-// them): the k words of a step take the next k positions, the lane of rank
-// r among the emitting lanes position k - 1 - r. The next step's symbol and
-// model entries are loaded one step ahead.
+// coding symbol 64 t + l with its own state. The chunk's symbols and the
+// field's model (f | c << 16 and the reciprocal of f, one 8-byte entry per
+// symbol) are staged in LDS first, and the next step's symbol and entry are
+// read one step ahead, so the loop's chain is the state arithmetic alone
+// and it issues no global load (only the stores of emitted words, which
+// nothing waits for). A step's emitted words go to the chunk's scratch in
+// reverse decoder order (the copy kernel reverses them): the k words of a
+// step take the next k positions, the lane of rank r among the emitting
+// lanes position k - 1 - r.
 __global__ void __launch_bounds__(kLzLanes) lz_code_kernel(const LzArgs a) {
+  __shared__ __align__(16) uint8_t syms[kLzChunk];
+  __shared__ uint64_t mdl[256];
   const uint32_t g = blockIdx.x;
   const int l = threadIdx.x;
   const int ji = lz_job_at<&LzJob::chunk0>(a, g);
@@ -294,50 +302,35 @@ __global__ void __launch_bounds__(kLzLanes) lz_code_kernel(const LzArgs a) {
   const LzLayout L = lz_layout(s, true);
   const uint32_t len = min((uint32_t)kLzChunk, lz_n(s, f) - k * kLzChunk);
   const int steps = (int)((len + kLzLanes - 1) / kLzLanes);
-  const uint8_t* sym = j.ws + sym_off + (size_t)k * kLzChunk;
+  // (the field's symbol region is padded: whole 16-byte reads stay inside)
+  const u32x4* src = (const u32x4*)(j.ws + sym_off + (size_t)k * kLzChunk);
+  for (uint32_t i = l; i < (len + 15) / 16; i += kLzLanes) ((u32x4*)syms)[i] = src[i];
   const uint32_t* fc = (const uint32_t*)(j.ws + L.fc) + f * 256;
-  const double* rcp = (const double*)(j.ws + L.aux) + f * 256;
+  const uint32_t* rcp = (const uint32_t*)(j.ws + L.aux) + f * 256;
+  for (int i = l; i < 256; i += kLzLanes) mdl[i] = fc[i] | ((uint64_t)rcp[i] << 32);
+  __syncthreads();
   uint16_t* rev = (uint16_t*)(j.ws + L.scratch) + (size_t)kj * kLzChunk;
   uint32_t x = kLzL, cnt = 0;
   int t = steps - 1;
-  uint32_t i = (uint32_t)t * kLzLanes + l;
-  bool act = i < len;
-  uint32_t sy = act ? sym[i] : 0u;
-  uint32_t m = fc[sy];
-  double r = rcp[sy];
+  bool act = (uint32_t)t * kLzLanes + l < len;
+  uint64_t m = mdl[act ? syms[(uint32_t)t * kLzLanes + l] : 0u];
   for (; t >= 0; --t) {
-    uint32_t sy2 = 0, m2 = 0;
-    double r2 = 0.0;
-    if (t > 0) {                      // every step before the last is full
-      sy2 = sym[(uint32_t)(t - 1) * kLzLanes + l];
-      m2 = fc[sy2];
-      r2 = rcp[sy2];
-    }
-    const uint32_t fs = m & 0xFFFFu, cs = m >> 16;
+    // every step before the last is full
+    const uint64_t mn = t > 0 ? mdl[syms[(uint32_t)(t - 1) * kLzLanes + l]] : 0ull;
+    const uint32_t fs = (uint32_t)m & 0xFFFFu, cs = ((uint32_t)m >> 16) & 0xFFFFu, rf = (uint32_t)(m >> 32);
     const bool emit = act && (uint64_t)x >= ((uint64_t)fs << 20);
     const uint64_t mask = __ballot(emit);
     const uint32_t ke = (uint32_t)__popcll(mask);
-    if (emit) {
-      rev[cnt + ke - 1 - (uint32_t)__popcll(mask & lanes_below(l))] = (uint16_t)x;
-      x >>= 16;
-    }
+    if (emit) rev[cnt + ke - 1 - (uint32_t)__popcll(mask & lanes_below(l))] = (uint16_t)x;
     cnt += ke;
-    if (act) {
-      // floor(x / fs) from the fp64 reciprocal, off by at most one
-      uint32_t q = (uint32_t)((double)x * r);
-      int64_t rm = (int64_t)x - (int64_t)q * fs;
-      if (rm < 0) {
-        --q;
-        rm += fs;
-      } else if (rm >= (int64_t)fs) {
-        ++q;
-        rm -= fs;
-      }
-      x = (q << kLzMBits) + (uint32_t)rm + cs;
-    }
-    sy = sy2;
-    m = m2;
-    r = r2;
+    const uint32_t xe = emit ? x >> 16 : x;
+    uint32_t q = __umulhi(xe, rf);
+    uint32_t rm = xe - q * fs;
+    const bool up = rm >= fs;
+    q += up ? 1u : 0u;
+    rm -= up ? fs : 0u;
+    x = act ? (q << kLzMBits) + rm + cs : x;
+    m = mn;
     act = t > 0;
   }
   ((uint32_t*)(j.ws + L.state))[(size_t)kj * kLzLanes + l] = x;
@@ -471,10 +464,12 @@ __global__ void __launch_bounds__(kLzThreads) lz_check_kernel(const LzArgs a) {
 
 // One wave per field: the model from the container's table (it must sum to
 // M) as the slot table: per slot, its symbol s | (f_s - 1) << 8 |
-// (slot - c_s) << 20.
+// (slot - c_s) << 20. Lane l fills slots [64 l, 64 l + 64) in LDS (one
+// search for its first slot, then a walk), then the table is copied out.
 __global__ void __launch_bounds__(64) lz_dmodel_kernel(const LzArgs a) {
-  __shared__ uint32_t cum[256];
+  __shared__ uint32_t cum[257];
   __shared__ uint32_t frq[256];
+  __shared__ __align__(16) uint32_t tb[kLzM];
   const int ji = lz_job_at<&LzJob::field0>(a, blockIdx.x);
   const LzJob& j = a.jobs[ji];
   if (lz_failed(a, j)) return;
@@ -485,7 +480,6 @@ __global__ void __launch_bounds__(64) lz_dmodel_kernel(const LzArgs a) {
   const LzField fd = lz_field(s, f);
   const LzLayout L = lz_layout(s, false);
   const uint16_t* fr = (const uint16_t*)(j.src + fd.tab_off + 8);
-  uint32_t* tbl = (uint32_t*)(j.ws + L.aux) + (size_t)f * kLzM;
   uint32_t run = 0;
   for (int q = 0; q < 4; ++q) {
     const int sy = lane + 64 * q;
@@ -495,30 +489,41 @@ __global__ void __launch_bounds__(64) lz_dmodel_kernel(const LzArgs a) {
     frq[sy] = fv;
     run += (uint32_t)__shfl((int)inc, 63, 64);
   }
+  if (lane == 0) cum[256] = 0xFFFFFFFFu;
   if (run != kLzM) {
     if (lane == 0) lz_set(a, j, KVTC_E_CORRUPT);
     return;
   }
   __syncthreads();
-  for (uint32_t slot = lane; slot < kLzM; slot += 64) {
-    int lo = 0, hi = A - 1;          // the last symbol whose range starts at or before slot
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (cum[mid] <= slot) lo = mid;
-      else hi = mid - 1;
-    }
-    tbl[slot] = (uint32_t)lo | ((frq[lo] - 1u) << 8) | ((slot - cum[lo]) << 20);
+  const uint32_t s0 = (uint32_t)lane * 64;
+  int lo = 0, hi = A - 1;            // the last symbol whose range starts at or before s0
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cum[mid] <= s0) lo = mid;
+    else hi = mid - 1;
   }
+  for (uint32_t slot = s0; slot < s0 + 64; ++slot) {
+    while (cum[lo + 1] <= slot) ++lo;  // symbols without slots share the next one's start
+    tb[slot] = (uint32_t)lo | ((frq[lo] - 1u) << 8) | ((slot - cum[lo]) << 20);
+  }
+  __syncthreads();
+  u32x4* out = (u32x4*)(j.ws + L.aux + (size_t)f * kLzM * 4);
+  for (int i = lane; i < (int)kLzM / 4; i += 64) out[i] = ((const u32x4*)tb)[i];
 }
 
 // One wavefront per chunk, lane l decoding symbols 64 t + l with its own
-// state: per step a slot-table lookup (LDS) and the state update; the lanes
+// state: per step a slot-table lookup and the state update, then the lanes
 // whose state fell below L take the next words in lane order (ballot and
-// prefix count), read from three 64-word windows of the payload held in
-// registers (lane l holds word base + l of each) through lane permutes;
-// a window is loaded two windows ahead of its use.
+// prefix count). Everything the loop reads is in LDS: the slot table, and
+// the payload in a ring of two 1 KiB blocks; the block after those is
+// already loaded into registers and enters the ring when the ring's older
+// block is used up, so each global load has about ten steps to arrive.
+// Symbols are staged in LDS and stored 16 steps (1 KiB) at a time.
+constexpr uint32_t kLzBlk = 1024;            // payload bytes per ring block (64 lanes x 16)
 __global__ void __launch_bounds__(kLzLanes) lz_decode_kernel(const LzArgs a) {
-  __shared__ uint32_t tbl[kLzM];
+  __shared__ __align__(16) uint32_t tbl[kLzM];
+  __shared__ __align__(16) uint8_t syms[16 * kLzLanes];
+  __shared__ __align__(16) uint8_t ring[2 * kLzBlk];
   const uint32_t g = blockIdx.x;
   const int l = threadIdx.x;
   const int ji = lz_job_at<&LzJob::chunk0>(a, g);
@@ -540,23 +545,36 @@ __global__ void __launch_bounds__(kLzLanes) lz_decode_kernel(const LzArgs a) {
   const uint32_t len = min((uint32_t)kLzChunk, lz_n(s, f) - k * kLzChunk);
   const int steps = (int)((len + kLzLanes - 1) / kLzLanes);
   const uint32_t* dir = (const uint32_t*)(j.src + L.dir_off);
+  const uint32_t total = ((const uint32_t*)j.src)[6];
   const uint32_t start = L.pay_off + (kj ? dir[kj - 1] : 0u);
   const uint32_t nw = (L.pay_off + dir[kj] - start) / 2;     // >= 128, checked
-  const uint16_t* w = (const uint16_t*)(j.src + start);
-  uint8_t* out = j.ws + sym_off + (size_t)k * kLzChunk;
-  uint32_t x = (uint32_t)w[2 * l] | ((uint32_t)w[2 * l + 1] << 16);
-  uint32_t pos = 2 * kLzLanes, wb = pos;
-  auto load = [&](uint32_t b) -> uint32_t { return b + l < nw ? (uint32_t)w[b + l] : 0u; };
-  uint32_t w0 = load(wb), w1 = load(wb + kLzLanes), w2 = load(wb + 2 * kLzLanes);
+  // blocks of the container from a0 = start rounded down to 16; byte
+  // off0 + 2 p of block space is payload word p
+  const uint32_t a0 = start & ~15u, off0 = start - a0;
+  auto blk = [&](uint32_t b) -> u32x4 {
+    const uint32_t at = a0 + b * kLzBlk + 16u * (uint32_t)l;
+    return at < total ? *(const u32x4*)(j.src + at) : u32x4(0u);
+  };
+  const u32x4 b0 = blk(0), b1 = blk(1);
+  u32x4 pend = blk(2);
+  ((u32x4*)ring)[l] = b0;
+  ((u32x4*)ring)[kLzLanes + l] = b1;
   __syncthreads();
+  const uint16_t* rw = (const uint16_t*)ring;
+  auto word = [&](uint32_t p) -> uint32_t { return rw[((off0 + 2 * p) & (2 * kLzBlk - 1)) >> 1]; };
+  uint32_t x = word(2 * l) | (word(2 * l + 1) << 16);
+  uint32_t pos = 2 * kLzLanes, cur = 0;
+  u32x4* out = (u32x4*)(j.ws + sym_off + (size_t)k * kLzChunk);
   bool ok = true;
   for (int t = 0; t < steps; ++t) {
     const uint32_t i = (uint32_t)t * kLzLanes + l;
     const bool act = i < len;
     const uint32_t e = tbl[x & (kLzM - 1)];
-    if (act) {
-      x = (((e >> 8) & 0xFFFu) + 1u) * (x >> kLzMBits) + (e >> 20);
-      out[i] = (uint8_t)e;
+    if (act) x = (((e >> 8) & 0xFFFu) + 1u) * (x >> kLzMBits) + (e >> 20);
+    syms[(t & 15) * kLzLanes + l] = (uint8_t)e;
+    if ((t & 15) == 15 || t == steps - 1) {   // 16 steps staged: 1 KiB out, 16 bytes a lane
+      const uint32_t q = (uint32_t)(t & ~15) * kLzLanes / 16 + l;
+      if (q * 16 < len) out[q] = ((const u32x4*)syms)[l];
     }
     const bool need = act && x < kLzL;
     const uint64_t mask = __ballot(need);
@@ -565,16 +583,13 @@ __global__ void __launch_bounds__(kLzLanes) lz_decode_kernel(const LzArgs a) {
       ok = false;
       break;
     }
-    const uint32_t idx = pos - wb + (uint32_t)__popcll(mask & lanes_below(l));
-    const uint32_t v0 = (uint32_t)__shfl((int)w0, (int)(idx & 63u), 64);
-    const uint32_t v1 = (uint32_t)__shfl((int)w1, (int)(idx & 63u), 64);
-    if (need) x = (x << 16) | (idx < (uint32_t)kLzLanes ? v0 : v1);
+    if (need) x = (x << 16) | word(pos + (uint32_t)__popcll(mask & lanes_below(l)));
     pos += kn;
-    if (pos - wb >= (uint32_t)kLzLanes) {
-      wb += kLzLanes;
-      w0 = w1;
-      w1 = w2;
-      w2 = load(wb + 2 * kLzLanes);
+    const uint32_t nb = (off0 + 2 * pos) / kLzBlk;
+    if (nb > cur) {                   // block cur used up: its ring half takes block cur + 2
+      ((u32x4*)ring)[(cur & 1) * kLzLanes + l] = pend;
+      cur = nb;
+      pend = blk(cur + 2);
     }
   }
   const bool bad = !ok || pos != nw || __ballot(x != kLzL) != 0ull;
