@@ -1170,7 +1170,11 @@ kvtc_status lz_plan(kvtc_codec* c, bool enc, const kvtc_job* jobs, int n, void* 
       rb_max = std::max(rb_max, rbs[p + b]);
       a.jobs[b] = d;
     }
-    a.rec_lds = (size_t)kLzRecBlk * rb_max + 16;
+    a.rec_lds = (size_t)kLzRecBlk * rb_max + 16;   // split: the block's records; merge: its symbols
+    for (int b = 0; b < a.n_jobs; ++b) {
+      const Slot& sl = c->slots[a.jobs[b].slot];
+      a.rec_lds = std::max(a.rec_lds, (size_t)kLzRecBlk * sl.n_act * (8 + c->p.group) + 16);
+    }
     batches.push_back(a);
   }
   return KVTC_OK;

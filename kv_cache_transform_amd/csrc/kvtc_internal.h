@@ -186,9 +186,11 @@ constexpr uint32_t kLzL = 1u << 16;
 constexpr int kLzHead = 64;                 // container header, then the stream header
 constexpr int kLzTables = kLzHead + kHeaderBytes;
 constexpr int kLzMaxFields = 4 + 8 + kMaxActGroups;
-constexpr int kLzPassBlk = 256;             // passthrough elements per split/merge unit
+constexpr int kLzPassBlk = 4096;            // passthrough elements per split/merge unit (16 a thread)
 constexpr int kLzRecBlk = 64;               // records per split/merge unit
 constexpr uint32_t kLzSeg = 16384;          // symbols per histogram unit
+// record bytes: 8 per active group plus at most one per active component
+constexpr int kLzMaxRec = 8 * kMaxActGroups + KVTC_MAX_REFF;
 
 // The fields of one stream: esz passthrough planes of n_pt symbols, 4 shift
 // and 4 scale planes of tc * n_act, then n_act code fields of tc * G.

@@ -115,17 +115,33 @@ __global__ void __launch_bounds__(kLzThreads) lz_split_kernel(const LzArgs a) {
   const uint32_t n_pb = (s.n_pt + kLzPassBlk - 1) / kLzPassBlk;
   uint8_t* sym = j.ws;
   if (u < n_pb) {
-    const uint32_t e = u * kLzPassBlk + tid;
-    if (e >= s.n_pt) return;
-    const uint8_t* src = j.src + kHeaderBytes;
+    // 16 consecutive elements a thread: 16-byte loads of the stream (its
+    // passthrough rows start at byte 64) and a 16-byte store per plane
+    const uint32_t e0 = u * kLzPassBlk + 16 * tid;
+    if (e0 >= s.n_pt) return;
+    const uint8_t* src = j.src + kHeaderBytes + (size_t)e0 * s.esz;
     const uint32_t rp = lz_sym_region(s.n_pt);
-    if (s.esz == 2) {
-      const uint32_t v = ((const uint16_t*)src)[e];
-      sym[e] = (uint8_t)v;
-      sym[rp + e] = (uint8_t)(v >> 8);
+    if (e0 + 16 <= s.n_pt) {
+      u32x4 pl[4] = {u32x4(0u), u32x4(0u), u32x4(0u), u32x4(0u)};
+      for (int v = 0; v < s.esz; ++v) {                 // 4 (bf16) or 8 (f32) elements per load
+        const u32x4 w = ((const u32x4*)src)[v];
+        for (int q = 0; q < 4; ++q) {
+          if (s.esz == 2) {
+            const int e = 8 * v + 2 * q;                // elements e, e + 1 of the 16
+            pl[0][e >> 2] |= ((w[q] & 0xFFu) | ((w[q] >> 8) & 0xFF00u)) << (8 * (e & 3));
+            pl[1][e >> 2] |= (((w[q] >> 8) & 0xFFu) | ((w[q] >> 16) & 0xFF00u)) << (8 * (e & 3));
+          } else {
+            const int e = 4 * v + q;
+            for (int b = 0; b < 4; ++b) pl[b][e >> 2] |= ((w[q] >> (8 * b)) & 0xFFu) << (8 * (e & 3));
+          }
+        }
+      }
+      for (int b = 0; b < s.esz; ++b) *(u32x4*)(sym + b * rp + e0) = pl[b];
     } else {
-      const uint32_t v = ((const uint32_t*)src)[e];
-      for (int b = 0; b < 4; ++b) sym[b * rp + e] = (uint8_t)(v >> (8 * b));
+      for (uint32_t e = e0; e < s.n_pt; ++e) {
+        const uint8_t* p = j.src + kHeaderBytes + (size_t)e * s.esz;
+        for (int b = 0; b < s.esz; ++b) sym[b * rp + e] = p[b];
+      }
     }
     return;
   }
@@ -141,22 +157,38 @@ __global__ void __launch_bounds__(kLzThreads) lz_split_kernel(const LzArgs a) {
   for (int i = tid * 4; i + 4 <= nbytes; i += kLzThreads * 4) *(uint32_t*)(lds + i) = *(const uint32_t*)(base + i);
   for (int i = (nbytes & ~3) + tid; i < nbytes; i += kLzThreads) lds[i] = base[i];
   __syncthreads();
+  // every field's run of this block starts at a multiple of 4 (r0 is a
+  // multiple of 64); a thread writes 4 consecutive symbols. A run only ends
+  // inside a word in the field's last block, where the zeros past its end
+  // land in the region's padding.
   for (int k = 0; k < 8; ++k) {
     uint8_t* out = sym + lz_plane_off(s, s.esz + k) + (size_t)r0 * na;
-    for (int i = tid; i < nr * na; i += kLzThreads) {
-      const int t = i / na, g = i - t * na;
-      out[i] = lds[t * rb + g * 8 + k];
+    for (int i = 4 * tid; i < nr * na; i += 4 * kLzThreads) {
+      uint32_t v = 0;
+      int t = i / na, g = i - t * na;
+      for (int q = 0; q < 4 && i + q < nr * na; ++q) {
+        v |= (uint32_t)lds[t * rb + g * 8 + k] << (8 * q);
+        if (++g == na) {
+          g = 0;
+          ++t;
+        }
+      }
+      *(uint32_t*)(out + i) = v;
     }
   }
   for (int g = 0; g < na; ++g) {
     const int b = s.width[g], co = sl->chunk_off[g];
     const uint32_t mask = (1u << b) - 1u;
     uint8_t* out = sym + lz_code_off(s, g) + (size_t)r0 * G;
-    for (int i = tid; i < nr * G; i += kLzThreads) {
-      const int t = i / G, c = i - t * G;
-      const int bit = c * b, p = t * rb + co + (bit >> 3);
-      const uint32_t v = ((uint32_t)lds[p] | ((uint32_t)lds[p + 1] << 8)) >> (bit & 7);
-      out[i] = (uint8_t)(v & mask);
+    for (int i = 4 * tid; i < nr * G; i += 4 * kLzThreads) {
+      const int t = i / G, c = i - t * G;      // G is a multiple of 8: one record
+      uint32_t v = 0;
+      for (int q = 0; q < 4; ++q) {
+        const int bit = (c + q) * b, p = t * rb + co + (bit >> 3);
+        const uint32_t w = ((uint32_t)lds[p] | ((uint32_t)lds[p + 1] << 8)) >> (bit & 7);
+        v |= (w & mask) << (8 * q);
+      }
+      *(uint32_t*)(out + i) = v;
     }
   }
 }
@@ -598,9 +630,13 @@ __global__ void __launch_bounds__(kLzLanes) lz_decode_kernel(const LzArgs a) {
 
 // One unit per block of passthrough elements or records: field symbols back
 // into the stream (nothing is written for a job found bad). Unit 0 of a job
-// also copies the stream header.
+// also copies the stream header. A record block stages its symbols in LDS
+// (8 planes of 64 n_act bytes, then n_act code runs of 64 G bytes) with a
+// map from record byte to (group, width, byte of the group's chunk), then
+// each thread assembles 4 consecutive stream bytes.
 __global__ void __launch_bounds__(kLzThreads) lz_merge_kernel(const LzArgs a) {
-  extern __shared__ uint8_t lds[];
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ uint32_t omap[kLzMaxRec];
   const int ji = lz_job_at<&LzJob::unit0>(a, blockIdx.x);
   const LzJob& j = a.jobs[ji];
   if (lz_failed(a, j)) return;
@@ -612,16 +648,34 @@ __global__ void __launch_bounds__(kLzThreads) lz_merge_kernel(const LzArgs a) {
   const uint32_t n_pb = (s.n_pt + kLzPassBlk - 1) / kLzPassBlk;
   const uint8_t* sym = j.ws;
   if (u < n_pb) {
-    const uint32_t e = u * kLzPassBlk + tid;
-    if (e >= s.n_pt) return;
+    // 16 consecutive elements a thread: a 16-byte load per plane (the
+    // regions are padded), 16-byte stores of the elements
+    const uint32_t e0 = u * kLzPassBlk + 16 * tid;
+    if (e0 >= s.n_pt) return;
     const uint32_t rp = lz_sym_region(s.n_pt);
-    uint8_t* out = dst + kHeaderBytes;
-    if (s.esz == 2) {
-      ((uint16_t*)out)[e] = (uint16_t)(sym[e] | ((uint32_t)sym[rp + e] << 8));
+    u32x4 pl[4];
+    for (int b = 0; b < s.esz; ++b) pl[b] = *(const u32x4*)(sym + b * rp + e0);
+    uint8_t* out = dst + kHeaderBytes + (size_t)e0 * s.esz;
+    if (e0 + 16 <= s.n_pt) {
+      for (int v = 0; v < s.esz; ++v) {
+        u32x4 w;
+        for (int q = 0; q < 4; ++q) {
+          uint32_t x = 0;
+          if (s.esz == 2) {
+            const int e = 8 * v + 2 * q;
+            const uint32_t lo = pl[0][e >> 2] >> (8 * (e & 3)), hi = pl[1][e >> 2] >> (8 * (e & 3));
+            x = (lo & 0xFFu) | ((hi & 0xFFu) << 8) | ((lo & 0xFF00u) << 8) | ((hi & 0xFF00u) << 16);
+          } else {
+            const int e = 4 * v + q;
+            for (int b = 0; b < 4; ++b) x |= ((pl[b][e >> 2] >> (8 * (e & 3))) & 0xFFu) << (8 * b);
+          }
+          w[q] = x;
+        }
+        ((u32x4*)out)[v] = w;
+      }
     } else {
-      uint32_t v = 0;
-      for (int b = 0; b < 4; ++b) v |= (uint32_t)sym[b * rp + e] << (8 * b);
-      ((uint32_t*)out)[e] = v;
+      for (uint32_t e = 0; e < s.n_pt - e0; ++e)
+        for (int b = 0; b < s.esz; ++b) out[e * s.esz + b] = (uint8_t)(pl[b][e >> 2] >> (8 * (e & 3)));
     }
     return;
   }
@@ -630,33 +684,58 @@ __global__ void __launch_bounds__(kLzThreads) lz_merge_kernel(const LzArgs a) {
   const DevSlot* sl = lz_slot(a, j);
   const int rb = sl->record_bytes, na = s.n_act, G = s.G;
   const int nr = (int)min((uint32_t)kLzRecBlk, s.tc - r0);
+  // stage: planes at k * 64 na, codes of group g at 8 * 64 na + g * 64 G
+  // (whole words; a word past a run's end reads padding or the next block)
+  const int pl_b = kLzRecBlk * na, cd_b = kLzRecBlk * G;
   for (int k = 0; k < 8; ++k) {
-    const uint8_t* in = sym + lz_plane_off(s, s.esz + k) + (size_t)r0 * na;
-    for (int i = tid; i < nr * na; i += kLzThreads) {
-      const int t = i / na, g = i - t * na;
-      lds[t * rb + g * 8 + k] = in[i];
-    }
+    const uint32_t* in = (const uint32_t*)(sym + lz_plane_off(s, s.esz + k) + (size_t)r0 * na);
+    for (int i = tid; i < (nr * na + 3) / 4; i += kLzThreads) ((uint32_t*)(lds + k * pl_b))[i] = in[i];
   }
   for (int g = 0; g < na; ++g) {
-    const int b = s.width[g], co = sl->chunk_off[g], nb = G * b / 8;
-    const uint8_t* in = sym + lz_code_off(s, g) + (size_t)r0 * G;
-    for (int i = tid; i < nr * nb; i += kLzThreads) {
-      const int t = i / nb, y = i - t * nb;
-      const int lo = 8 * y, c0 = lo / b, c1 = min(G - 1, (lo + 7) / b);
-      uint32_t v = 0;
-      for (int c = c0; c <= c1; ++c) {
-        const int sh = c * b - lo;
-        const uint32_t q = in[t * G + c];
-        v |= sh >= 0 ? q << sh : q >> -sh;
-      }
-      lds[t * rb + co + y] = (uint8_t)v;
+    const uint32_t* in = (const uint32_t*)(sym + lz_code_off(s, g) + (size_t)r0 * G);
+    for (int i = tid; i < nr * G / 4; i += kLzThreads) ((uint32_t*)(lds + 8 * pl_b + g * cd_b))[i] = in[i];
+  }
+  for (int o = tid; o < rb; o += kLzThreads) {
+    uint32_t m = 0;
+    if (o >= 8 * na) {
+      int g = 0;
+      while (g + 1 < na && sl->chunk_off[g + 1] <= o) ++g;
+      m = (uint32_t)g | ((uint32_t)s.width[g] << 8) | ((uint32_t)(o - sl->chunk_off[g]) << 16);
     }
+    omap[o] = m;
   }
   __syncthreads();
   uint8_t* base = dst + kHeaderBytes + (size_t)s.n_pt * s.esz + (size_t)r0 * rb;
   const int nbytes = nr * rb;
-  for (int i = tid * 4; i + 4 <= nbytes; i += kLzThreads * 4) *(uint32_t*)(base + i) = *(const uint32_t*)(lds + i);
-  for (int i = (nbytes & ~3) + tid; i < nbytes; i += kLzThreads) base[i] = lds[i];
+  for (int y0 = 4 * tid; y0 < nbytes; y0 += 4 * kLzThreads) {
+    uint32_t v = 0;
+    const int ny = min(4, nbytes - y0);
+    int t = y0 / rb, o = y0 - t * rb;
+    for (int q = 0; q < ny; ++q, ++o) {
+      if (o == rb) {
+        o = 0;
+        ++t;
+      }
+      uint32_t byte;
+      if (o < 8 * na) {
+        byte = lds[(o & 7) * pl_b + t * na + (o >> 3)];
+      } else {
+        const uint32_t m = omap[o];
+        const int g = (int)(m & 0xFFu), b = (int)((m >> 8) & 0xFFu), lo = 8 * (int)(m >> 16);
+        const uint8_t* cq = lds + 8 * pl_b + g * cd_b + t * G;
+        byte = 0;
+        for (int c = lo / b, c1 = min(G - 1, (lo + 7) / b); c <= c1; ++c) {
+          const int sh = c * b - lo;
+          const uint32_t qv = cq[c];
+          byte |= sh >= 0 ? qv << sh : qv >> -sh;
+        }
+      }
+      v |= (byte & 0xFFu) << (8 * q);
+    }
+    if (ny == 4) *(uint32_t*)(base + y0) = v;
+    else
+      for (int q = 0; q < ny; ++q) base[y0 + q] = (uint8_t)(v >> (8 * q));
+  }
 }
 
 }  // namespace
