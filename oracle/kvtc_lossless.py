@@ -84,6 +84,8 @@ CONTAINER_HEADER = 64
 
 def stream_fields(stream: bytes, params, slot, T: int):
     """Split a KVTC stream into its fields (reading L1): [(symbols u8, A)]."""
+    if getattr(slot, "cwidths", None) is not None:
+        raise OracleError("the lossless stage takes streams with a width per group")
     s1, w1, tc = split_rows(T, params.sink, params.window)
     esz, F = params.elem_bytes, params.F
     n_pt = (s1 + w1) * F

@@ -64,6 +64,24 @@ contribution) and that the DP places bits where they lower the error most
   Q7g ties of the global allocation: fewest total bits, then the most bits to
       the tensor earliest in (layer, kind) order, then Q7 inside each tensor.
 
+Per-component widths (the page's section 2A gives each principal component
+its own width; READING Q2c, an alternative to Q2 chosen at calibration):
+  Q2c every component j of a group has its own width b_j in 0..max_bits; the
+      group's (shift, scale) is the min and range of all G of its components
+      per token, as in Q4; component j is coded on 2^b_j - 1 levels of that
+      range (q = clamp(rint(fp32(c - shift) * fp32(k_j / scale)), 0, k_j)) and
+      decodes to shift + q * fp32(scale / k_j); b_j = 0 drops it (it decodes
+      to 0).  A group is active if any b_j > 0.  Its codes are packed in
+      component order, code j at bit sum_{i<j} b_i of the group's chunk, LSB
+      first; the chunk is ceil(sum_j b_j / 8) bytes (zero padded).  Cost of
+      an active group: 64 + 8 * ceil(sum_j b_j / 8) bits.  Distortion D_j(b):
+      the empirical error of that quantizer on component j with its group's
+      grid.  DP: per group, E_g(s) = least sum_j D_j(b_j) with sum_j b_j = s;
+      across groups, least sum_g E_g(s_g) within the budget.  Ties: fewest
+      bits, then the largest s for the earliest group, then the
+      lexicographically largest widths inside a group.  Slot format: the
+      seventh header int is 1 and the widths array holds F component widths.
+
 Byte formats (all little-endian):
 
   artifact  = "KVTA" u32 version, i32 n_layers, kv_heads, head_dim, sink,
@@ -188,6 +206,9 @@ class Slot:
     mu64: np.ndarray | None = None
     V64: np.ndarray | None = None
     D: np.ndarray | None = None
+    # Per-component widths (reading Q2c), u8 [F]; None for group widths.
+    # With them, widths[g] is the group's largest component width.
+    cwidths: np.ndarray | None = None
 
     @property
     def active_groups(self) -> np.ndarray:
@@ -203,18 +224,25 @@ class Slot:
 
     @property
     def record_bytes(self) -> int:
+        if self.cwidths is not None:
+            return 8 * self.n_act + sum(chunk_bytes_pc(self.group_cwidths(g)) for g in self.active_groups)
         return 8 * self.n_act + self.G * int(np.sum(self.widths.astype(np.int64))) // 8
+
+    def group_cwidths(self, g: int) -> np.ndarray:
+        """Component widths of group g (Q2c)."""
+        return self.cwidths[g * self.G:(g + 1) * self.G]
 
     def basis_bf16(self) -> np.ndarray:
         """Operational basis V' = bf16_rne(V32) over the active columns (N1)."""
         return bf16_rne(self.V32)
 
     def serialize(self) -> bytes:
-        n_g = self.F // self.G
+        pc = self.cwidths is not None
+        n_w = self.F if pc else self.F // self.G
         head = SLOT_MAGIC + struct.pack("<7i", self.layer, self.kind, self.F, self.G,
-                                        self.n_act, self.r_eff, 0)
-        w = np.zeros((n_g + 7) // 8 * 8, np.uint8)
-        w[:n_g] = self.widths
+                                        self.n_act, self.r_eff, 1 if pc else 0)
+        w = np.zeros((n_w + 7) // 8 * 8, np.uint8)
+        w[:n_w] = self.cwidths if pc else self.widths
         body = (head + w.tobytes() + np.asarray(self.mu32, "<f4").tobytes()
                 + np.asarray(self.lam, "<f8").tobytes()
                 + np.ascontiguousarray(self.V32, "<f4").tobytes())
@@ -256,11 +284,18 @@ def parse_artifact(buf: bytes) -> Artifact:
         start = off
         if buf[off:off + 4] != SLOT_MAGIC:
             raise OracleError("bad slot magic")
-        layer, kind, F, G, n_act, r_eff, _z = struct.unpack_from("<7i", buf, off + 4)
+        layer, kind, F, G, n_act, r_eff, pc = struct.unpack_from("<7i", buf, off + 4)
+        if pc not in (0, 1):
+            raise OracleError("bad slot mode")
         off += 32
         n_g = F // G
-        wpad = (n_g + 7) // 8 * 8
-        widths = np.frombuffer(buf, np.uint8, n_g, off).copy()
+        n_w = F if pc else n_g
+        wpad = (n_w + 7) // 8 * 8
+        widths = np.frombuffer(buf, np.uint8, n_w, off).copy()
+        cwidths = None
+        if pc:
+            cwidths = widths
+            widths = cwidths.reshape(n_g, G).max(axis=1).astype(np.uint8)
         off += wpad
         mu32 = np.frombuffer(buf, "<f4", F, off).copy()
         off += 4 * F
@@ -272,7 +307,7 @@ def parse_artifact(buf: bytes) -> Artifact:
         if fnv1a64(buf[start:off]) != sid:
             raise OracleError("slot id mismatch")
         off += 8
-        sl = Slot(layer, kind, F, G, widths, mu32, lam, V32)
+        sl = Slot(layer, kind, F, G, widths, mu32, lam, V32, cwidths=cwidths)
         if sl.n_act != n_act or sl.r_eff != r_eff:
             raise OracleError("inconsistent slot")
         slots[(layer, kind)] = sl
@@ -297,6 +332,51 @@ def quantize_fp32(c: np.ndarray, b: int):
     q = np.clip(np.rint(u), 0, k)
     q[~nz] = 0
     return q.astype(np.uint8), shift.astype(np.float32), scale
+
+
+def quantize_fp32_pc(c: np.ndarray, bs):
+    """The group quantizer with a width per component (reading Q2c): the
+    group's shift and scale over all its components, component j on
+    2^bs[j] - 1 levels; a zero width gives code 0."""
+    c = np.asarray(c, np.float32)
+    shift = c.min(axis=1)
+    scale = (c.max(axis=1) - shift).astype(np.float32)
+    nz = scale > 0
+    q = np.zeros(c.shape, np.uint8)
+    d = (c - shift[:, None]).astype(np.float32)
+    for j, b in enumerate(bs):
+        if b == 0:
+            continue
+        k = np.float32(2 ** int(b) - 1)
+        inv = np.zeros_like(scale)
+        inv[nz] = k / scale[nz]                              # IEEE fp32 division
+        u = (d[:, j] * inv).astype(np.float32)
+        qj = np.clip(np.rint(u), 0, k)
+        qj[~nz] = 0
+        q[:, j] = qj.astype(np.uint8)
+    return q, shift.astype(np.float32), scale
+
+
+def dequantize_pc(q, shift, scale, bs) -> np.ndarray:
+    """Inverse of quantize_fp32_pc in fp64; a zero width decodes to 0."""
+    out = np.zeros(q.shape)
+    for j, b in enumerate(bs):
+        if b:
+            out[:, j] = dequantize(q[:, j:j + 1], shift, scale, int(b))[:, 0]
+    return out
+
+
+def quant_dequant_fp64_pc(c: np.ndarray, b: int, j: int) -> np.ndarray:
+    """Component j of group rows c [n, G] through b levels of the group's
+    fp64 grid (for the distortion table of reading Q2c)."""
+    k = float(2 ** b - 1)
+    shift = c.min(axis=1)
+    scale = c.max(axis=1) - shift
+    out = c[:, j].copy()
+    nz = scale > 0
+    q = np.clip(np.rint((c[nz, j] - shift[nz]) * (k / scale[nz])), 0, k)
+    out[nz] = shift[nz] + q * (scale[nz] / k)
+    return out
 
 
 def dequantize(q: np.ndarray, shift: np.ndarray, scale: np.ndarray, b: int) -> np.ndarray:
@@ -420,6 +500,91 @@ def slot_dp_table(D: np.ndarray, G: int, max_bits_used: int, max_active: int) ->
     return f
 
 
+def distortion_table_pc(C: np.ndarray, G: int, max_bits: int) -> np.ndarray:
+    """Dc[j, b] = mean over rows of component j's squared error at b bits on
+    its group's grid (reading Q2c); b = 0 drops it (its energy)."""
+    n, F = C.shape
+    Dc = np.zeros((F, max_bits + 1))
+    for g in range(F // G):
+        cg = C[:, g * G:(g + 1) * G]
+        for j in range(G):
+            Dc[g * G + j, 0] = np.mean(cg[:, j] ** 2)
+            for b in range(1, max_bits + 1):
+                e = cg[:, j] - quant_dequant_fp64_pc(cg, b, j)
+                Dc[g * G + j, b] = np.mean(e * e)
+    return Dc
+
+
+def chunk_bytes_pc(bs) -> int:
+    return (int(np.sum(np.asarray(bs, np.int64))) + 7) // 8
+
+
+def group_cost_pc(s: int) -> int:
+    """Bits of a group whose component widths sum to s (reading Q2c)."""
+    return 0 if s == 0 else SCALE_BITS + 8 * ((s + 7) // 8)
+
+
+def dp_allocate_pc(Dc: np.ndarray, G: int, budget: int) -> np.ndarray:
+    """Component widths minimising sum_j Dc[j, b_j] within the budget, with
+    the cost of reading Q2c (ties in its order).
+
+    Per group, e[i][s] = least distortion of components i.. of the group
+    whose widths sum to s (nested from the last component); across groups,
+    f[g][u] = min_s E_g(s) + f[g+1][u - cost(s)] (nested from the last)."""
+    F, nb = Dc.shape
+    n_g = F // G
+    smax = (nb - 1) * G
+    INF = np.inf
+    inner = []
+    for g in range(n_g):
+        D = Dc[g * G:(g + 1) * G]
+        e = np.full((G + 1, smax + 1), INF)
+        e[G, 0] = 0.0
+        for i in range(G - 1, -1, -1):
+            for sm in range(smax + 1):
+                best = INF
+                for b in range(nb):
+                    if b <= sm and e[i + 1, sm - b] < INF:
+                        v = D[i, b] + e[i + 1, sm - b]
+                        if v < best:
+                            best = v
+                e[i, sm] = best
+        inner.append(e)
+    f = np.full((n_g + 1, budget + 1), INF)
+    f[n_g, 0] = 0.0
+    for g in range(n_g - 1, -1, -1):
+        for u in range(budget + 1):
+            best = INF
+            for sm in range(smax + 1):
+                c = group_cost_pc(sm)
+                if c <= u and inner[g][0, sm] < INF and f[g + 1, u - c] < INF:
+                    v = inner[g][0, sm] + f[g + 1, u - c]
+                    if v < best:
+                        best = v
+            f[g, u] = best
+    u = int(np.argmin(f[0]))                  # first minimum = fewest bits
+    out = np.zeros(F, np.uint8)
+    for g in range(n_g):
+        e = inner[g]
+        for sm in range(smax, -1, -1):        # largest sum first
+            c = group_cost_pc(sm)
+            if c <= u and e[0, sm] < INF and e[0, sm] + f[g + 1, u - c] == f[g, u]:
+                break
+        else:
+            raise OracleError("DP reconstruction failed (group)")
+        u -= c
+        D = Dc[g * G:(g + 1) * G]
+        for i in range(G):
+            for b in range(min(nb - 1, sm), -1, -1):   # largest width first
+                if e[i + 1, sm - b] < INF and D[i, b] + e[i + 1, sm - b] == e[i, sm]:
+                    out[g * G + i] = b
+                    sm -= b
+                    break
+            else:
+                raise OracleError("DP reconstruction failed (component)")
+    return out
+
+
 def dp_allocate_global(Ds, G: int, budget_per_tensor: int, max_active: int):
     """Widths of several tensors chosen together (readings Q6g, Q7g).
 
@@ -486,7 +651,8 @@ def _make_slot(layer, kind, params: Params, mu, V, lam, D, widths) -> Slot:
 
 
 def calibrate_set(inputs, params: Params, shared_basis: bool = False,
-                  global_budget: bool = False, max_active: int | None = None) -> dict:
+                  global_budget: bool = False, max_active: int | None = None,
+                  component_widths: bool = False) -> dict:
     """Calibrate several tensors at once (readings P1s, Q6g, Q7g).
 
     inputs: (layer, kind, x_cal [n, F]) triples, at most one per (layer, kind).
@@ -520,6 +686,19 @@ def calibrate_set(inputs, params: Params, shared_basis: bool = False,
     else:
         for key in keys:
             basis[key] = pca_basis(prep[key] - mus[key])
+    if component_widths:
+        if global_budget:
+            raise OracleError("component widths take a budget per tensor")
+        out = {}
+        for k in keys:
+            C = (prep[k] - mus[k]) @ basis[k][0]
+            Dc = distortion_table_pc(C, params.group, params.max_bits)
+            cw = dp_allocate_pc(Dc, params.group, params.budget_bits)
+            widths = cw.reshape(-1, params.group).max(axis=1).astype(np.uint8)
+            sl = _make_slot(k[0], k[1], params, mus[k], basis[k][0], basis[k][1], Dc, widths)
+            sl.cwidths = cw
+            out[k] = sl
+        return out
     D = {key: distortion_table((prep[key] - mus[key]) @ basis[key][0], params.group,
                                params.max_bits) for key in keys}
     if global_budget:
@@ -571,6 +750,33 @@ def pack_codes(q: np.ndarray, b: int) -> np.ndarray:
     return np.packbits(bits.astype(np.uint8).reshape(T, G * b), axis=1, bitorder="little")
 
 
+def pack_codes_pc(q: np.ndarray, bs) -> np.ndarray:
+    """Codes [T, G] with a width per component -> bytes [T, ceil(sum b / 8)]:
+    code j at bit sum_{i<j} b_i, LSB first, zero padded (reading Q2c)."""
+    T = q.shape[0]
+    cols = [((q[:, j].astype(np.uint16)[:, None] >> np.arange(int(b), dtype=np.uint16)) & 1)
+            for j, b in enumerate(bs) if b]
+    nbits = int(np.sum(np.asarray(bs, np.int64)))
+    bits = np.zeros((T, chunk_bytes_pc(bs) * 8), np.uint8)
+    if cols:
+        bits[:, :nbits] = np.concatenate(cols, axis=1)
+    return np.packbits(bits, axis=1, bitorder="little")
+
+
+def unpack_codes_pc(chunk: np.ndarray, bs) -> np.ndarray:
+    T = chunk.shape[0]
+    bits = np.unpackbits(chunk, axis=1, bitorder="little")
+    q = np.zeros((T, len(bs)), np.uint8)
+    pos = 0
+    for j, b in enumerate(bs):
+        b = int(b)
+        if b:
+            q[:, j] = np.sum(bits[:, pos:pos + b].astype(np.uint16) << np.arange(b, dtype=np.uint16),
+                             axis=1).astype(np.uint8)
+        pos += b
+    return q
+
+
 def unpack_codes(chunk: np.ndarray, G: int, b: int) -> np.ndarray:
     T = chunk.shape[0]
     bits = np.unpackbits(chunk, axis=1, bitorder="little").reshape(T, G, b)
@@ -617,8 +823,11 @@ def build_records(codes, shift, scale, slot: Slot) -> np.ndarray:
     ss[:, :, 1] = scale
     parts.append(ss.view(np.uint8).reshape(tc, 8 * slot.n_act))
     for a, g in enumerate(slot.active_groups):
-        b = int(slot.widths[g])
-        parts.append(pack_codes(codes[:, a * slot.G:(a + 1) * slot.G], b))
+        q = codes[:, a * slot.G:(a + 1) * slot.G]
+        if slot.cwidths is not None:
+            parts.append(pack_codes_pc(q, slot.group_cwidths(g)))
+        else:
+            parts.append(pack_codes(q, int(slot.widths[g])))
     if not parts or tc == 0:
         return np.zeros((tc, slot.record_bytes), np.uint8)
     return np.concatenate(parts, axis=1)
@@ -639,7 +848,10 @@ def encode(x_store: np.ndarray, params: Params, slot: Slot, layer: int, kind: in
     scale = np.zeros((tc, slot.n_act), np.float32)
     for a, g in enumerate(slot.active_groups):
         sl = slice(a * slot.G, (a + 1) * slot.G)
-        codes[:, sl], shift[:, a], scale[:, a] = quantize_fp32(c[:, sl], int(slot.widths[g]))
+        if slot.cwidths is not None:
+            codes[:, sl], shift[:, a], scale[:, a] = quantize_fp32_pc(c[:, sl], slot.group_cwidths(g))
+        else:
+            codes[:, sl], shift[:, a], scale[:, a] = quantize_fp32(c[:, sl], int(slot.widths[g]))
     rec = build_records(codes, shift, scale, slot)
     stream = (make_header(params, slot, layer, kind, T) + passthrough.tobytes()
               + rec.tobytes())
@@ -687,9 +899,14 @@ def read_records(stream: bytes, params: Params, slot: Slot, T: int):
     codes = np.zeros((tc, slot.r_eff), np.uint8)
     pos = 8 * slot.n_act
     for a, g in enumerate(slot.active_groups):
-        b = int(slot.widths[g])
-        nbytes = slot.G * b // 8
-        codes[:, a * slot.G:(a + 1) * slot.G] = unpack_codes(rec[:, pos:pos + nbytes], slot.G, b)
+        if slot.cwidths is not None:
+            bs = slot.group_cwidths(g)
+            nbytes = chunk_bytes_pc(bs)
+            codes[:, a * slot.G:(a + 1) * slot.G] = unpack_codes_pc(rec[:, pos:pos + nbytes], bs)
+        else:
+            b = int(slot.widths[g])
+            nbytes = slot.G * b // 8
+            codes[:, a * slot.G:(a + 1) * slot.G] = unpack_codes(rec[:, pos:pos + nbytes], slot.G, b)
         pos += nbytes
     return codes, ss[:, :, 0].astype(np.float32), ss[:, :, 1].astype(np.float32)
 
@@ -700,7 +917,10 @@ def reconstruct(codes, shift, scale, slot: Slot) -> np.ndarray:
     chat = np.zeros((tc, slot.r_eff))
     for a, g in enumerate(slot.active_groups):
         sl = slice(a * slot.G, (a + 1) * slot.G)
-        chat[:, sl] = dequantize(codes[:, sl], shift[:, a], scale[:, a], int(slot.widths[g]))
+        if slot.cwidths is not None:
+            chat[:, sl] = dequantize_pc(codes[:, sl], shift[:, a], scale[:, a], slot.group_cwidths(g))
+        else:
+            chat[:, sl] = dequantize(codes[:, sl], shift[:, a], scale[:, a], int(slot.widths[g]))
     return slot.mu32.astype(np.float64) + chat @ slot.basis_bf16().astype(np.float64).T
 
 

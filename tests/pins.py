@@ -449,6 +449,118 @@ def check_lossless_roundtrip():
         assert LZ.decompress(z, p, sl, T) == st
 
 
+_PC_ALLOCS = {}
+
+
+def brute_force_pc(Dc, G, budgets):
+    """Every component width vector, ordered by (objective, bits of reading
+    Q2c, largest component sum for the earliest group, lexicographically
+    largest widths); the best one within each budget. Dc must hold exact
+    binary fractions."""
+    F, nb = Dc.shape
+    n_g = F // G
+    if (F, nb) not in _PC_ALLOCS:
+        ws = np.array(list(itertools.product(range(nb), repeat=F)), np.int64)
+        sums = ws.reshape(len(ws), n_g, G).sum(axis=2)
+        cost = np.where(sums > 0, 64 + 8 * ((sums + 7) // 8), 0).sum(axis=1)
+        _PC_ALLOCS[(F, nb)] = (ws, sums, cost)
+    ws, sums, cost = _PC_ALLOCS[(F, nb)]
+    obj = np.sum(Dc[np.arange(F), ws], axis=1)
+    keys = ([-ws[:, j] for j in range(F - 1, -1, -1)] + [-sums[:, g] for g in range(n_g - 1, -1, -1)]
+            + [cost, obj])
+    order = np.lexsort(keys)
+    out = []
+    for budget in budgets:
+        i = order[np.argmax(cost[order] <= budget)]
+        out.append(ws[i].astype(np.uint8))
+    return out
+
+
+def check_pc_pack_golden():
+    gd = golden("pack_pc_examples.json")
+    for case in gd["cases"]:
+        q = np.array([case["codes"]], np.uint8)
+        got = O.pack_codes_pc(q, case["widths"])
+        assert got[0].tolist() == case["bytes"], (case["note"], got)
+        back = O.unpack_codes_pc(got, case["widths"])
+        want = [c if w else 0 for c, w in zip(case["codes"], case["widths"])]
+        assert back[0].tolist() == want
+
+
+def check_pc_quantizer_golden():
+    gd = golden("quantizer_pc_examples.json")
+    for case in gd["cases"]:
+        c = np.array([case["c"]], np.float32)
+        q, sh, sc = O.quantize_fp32_pc(c, case["widths"])
+        assert q[0].tolist() == case["codes"], (case["note"], q)
+        assert float(sh[0]) == case["shift"] and float(sc[0]) == case["scale"]
+        ch = O.dequantize_pc(q, sh, sc, case["widths"])
+        assert ch[0].tolist() == case["chat"], (case["note"], ch)
+
+
+def check_pc_dp_bruteforce():
+    """The per-component allocation of reading Q2c against brute force: one
+    group of 8 components with widths 0..3, and two groups of 8 with widths
+    0..1; exact dyadic tables, ties included."""
+    rng = np.random.default_rng(13)
+    for trial in range(3):
+        for n_g, nb in ((1, 4), (2, 2)):
+            F = 8 * n_g
+            e = np.sort(rng.uniform(0, 40, F))[::-1]
+            Dc = np.array([[np.round(e[j] * 4.0 ** -b * 16) / 16 for b in range(nb)] for j in range(F)])
+            if trial % 3 == 1:
+                Dc[F // 2:] = Dc[:F // 2] if n_g == 2 else Dc[F // 2:]
+            if trial % 3 == 2:
+                Dc[-3:] = 0.0
+            budgets = (0, 65, 72, 80, 90, 150, 170)
+            for budget, bw in zip(budgets, brute_force_pc(Dc, 8, budgets)):
+                w = O.dp_allocate_pc(Dc, 8, budget)
+                assert np.array_equal(w, bw), (trial, n_g, budget, w, bw)
+
+
+def check_pc_tables_and_reduction():
+    """The per-component distortion table sums, over a group at one width,
+    to the group table of reading Q2 (same grid, same quantizer); equal
+    widths inside every group reproduce the group-width records byte for
+    byte; per-component allocation is never worse than group widths; the
+    quantizer keeps every coded component within half its step."""
+    x, _ = family_b_small(seed=23, n=2400)
+    p = small_params(F=64, G=16, bpv=3.0)
+    sl = O.calibrate(x[:1600], p, 0, 0)
+    rows = x[p.sink:1600 - p.window].astype(np.float64)
+    C = (rows - sl.mu64) @ sl.V64
+    Dc = O.distortion_table_pc(C, 16, 8)
+    for g in range(4):
+        for b in range(9):
+            assert np.isclose(Dc[g * 16:(g + 1) * 16, b].sum(), sl.D[g, b], rtol=1e-12, atol=1e-300)
+    eq = O.Slot(0, 0, 64, 16, sl.widths, sl.mu32, sl.lam, sl.V32,
+                cwidths=np.repeat(sl.widths, 16).astype(np.uint8))
+    assert eq.record_bytes == sl.record_bytes
+    xe = x[1600:].astype(np.float32)
+    a_ = O.encode(xe, p, sl, 0, 0).stream
+    b_ = O.encode(xe, p, eq, 0, 0).stream
+    assert a_[O.HEADER_BYTES:] == b_[O.HEADER_BYTES:]
+    cw = O.dp_allocate_pc(Dc, 16, p.budget_bits)
+    obj_pc = sum(Dc[j, b] for j, b in enumerate(cw))
+    obj_g = sum(sl.D[g, b] for g, b in enumerate(sl.widths))
+    assert obj_pc <= obj_g * (1 + 1e-12)
+    pc = O.calibrate_set([(0, 0, x[:1600])], p, component_widths=True)[(0, 0)]
+    assert np.array_equal(pc.cwidths, cw)
+    er = O.encode(xe, p, pc, 0, 0)
+    for a, g in enumerate(pc.active_groups):
+        bs = pc.group_cwidths(g)
+        cg = er.coeffs[:, a * 16:(a + 1) * 16].astype(np.float64)
+        ch = O.dequantize_pc(er.codes[:, a * 16:(a + 1) * 16], er.shift[:, a], er.scale[:, a], bs)
+        for j, b in enumerate(bs):
+            if b:
+                step = er.scale[:, a].astype(np.float64) / (2 ** int(b) - 1)
+                assert np.all(np.abs(cg[:, j] - ch[:, j]) <= step / 2 * (1 + 1e-5) + 1e-6 * np.abs(cg[:, j]))
+            else:
+                assert np.all(ch[:, j] == 0)
+    art = O.parse_artifact(O.Artifact(p, {(0, 0): pc}).serialize()).slots[(0, 0)]
+    assert np.array_equal(art.cwidths, pc.cwidths) and art.record_bytes == pc.record_bytes
+
+
 def check_projection_exact():
     """c = fp32 of the exact sum of (x - mu32) times bf16 V' (section 2B)."""
     rng = np.random.default_rng(6)

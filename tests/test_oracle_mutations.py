@@ -254,6 +254,43 @@ def _fields_codes_component_major(stream, params, slot, T):
     return out
 
 
+def _pack_pc_msb_first(q, bs):
+    rev = q.copy()
+    for j, b in enumerate(bs):
+        if b:
+            v = q[:, j].astype(np.uint16)
+            rev[:, j] = sum(((v >> i) & 1) << (int(b) - 1 - i) for i in range(int(b))).astype(np.uint8)
+    return _orig["pack_codes_pc"](rev, bs)
+
+
+def _dequant_pc_group_width(q, shift, scale, bs):
+    m = int(np.max(bs))
+    return _orig["dequantize_pc"](q, shift, scale, [m if b else 0 for b in bs])
+
+
+def _quant_pc_active_range(c, bs):
+    """Shift and scale over the coded components only."""
+    c = np.asarray(c, np.float32)
+    act = np.asarray(bs) > 0
+    q, _, _ = _orig["quantize_fp32_pc"](c[:, act], np.asarray(bs)[act])
+    full = np.zeros(c.shape, np.uint8)
+    full[:, act] = q
+    shift = c[:, act].min(axis=1)
+    return full, shift, (c[:, act].max(axis=1) - shift).astype(np.float32)
+
+
+def _group_cost_pc_unpadded(s_):
+    return 0 if s_ == 0 else 64 + s_
+
+
+PC_MUTATIONS = {
+    "pc_pack_msb_first": ("pack_codes_pc", _pack_pc_msb_first),
+    "pc_dequant_group_width": ("dequantize_pc", _dequant_pc_group_width),
+    "pc_range_over_coded_only": ("quantize_fp32_pc", _quant_pc_active_range),
+    "pc_cost_without_padding": ("group_cost_pc", _group_cost_pc_unpadded),
+}
+
+
 LZ_MUTATIONS = {
     "lz_normalize_remainder_to_first": ("normalize", _normalize_remainder_to_first),
     "lz_normalize_drops_rare": ("normalize", _normalize_no_floor_one),
@@ -294,13 +331,13 @@ MUTATIONS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS) + sorted(LZ_MUTATIONS))
+@pytest.mark.parametrize("name", sorted(MUTATIONS) + sorted(PC_MUTATIONS) + sorted(LZ_MUTATIONS))
 def test_mutation_is_caught(name, monkeypatch):
     if name in LZ_MUTATIONS:
         attr, fake = LZ_MUTATIONS[name]
         monkeypatch.setattr(LZ, attr, fake)
     else:
-        attr, fake = MUTATIONS[name]
+        attr, fake = {**MUTATIONS, **PC_MUTATIONS}[name]
         monkeypatch.setattr(O, attr, fake)
     failed = []
     for check in pins.ALL:
