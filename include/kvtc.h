@@ -134,7 +134,9 @@ typedef struct {
   int32_t r_eff;           /* n_act * G active components                    */
   int32_t record_bytes;    /* bytes per compressed token                     */
   uint64_t slot_id;        /* FNV-1a 64 of the slot's serialized bytes       */
-  uint8_t widths[512];     /* width per group (F/G entries)                  */
+  uint8_t widths[512];     /* width per group (F/G entries); with a width
+                              per component, each group's largest            */
+  int32_t per_component;   /* 1: a width per component (see kvtc_calibrate_set) */
 } kvtc_slot_info;
 
 /* Largest active component count the kernels accept. */
@@ -177,6 +179,7 @@ typedef struct {
 /* kvtc_calibrate_set flags. */
 #define KVTC_CAL_SHARED_BASIS 1u  /* one basis per kind across the set's layers */
 #define KVTC_CAL_GLOBAL_BUDGET 2u /* one bit budget across the whole set */
+#define KVTC_CAL_COMPONENT_WIDTHS 4u /* a width per component inside each group */
 
 /* Calibrate several (layer, kind) tensors in one call. The page on KV cache
  * transform coding finds one PCA basis reusable across layers and heads
@@ -194,6 +197,24 @@ typedef struct {
  *     at most KVTC_MAX_REFF / G active groups per tensor. Ties: fewest total
  *     bits, then the most bits to the tensor earliest in (layer, kind) order,
  *     then kvtc_calibrate's rule inside each tensor.
+ *   KVTC_CAL_COMPONENT_WIDTHS (not with the global budget): section 2A gives
+ *     each principal component its own width; with this flag every
+ *     component j of a group gets a width b_j in 0..max_bits while the group
+ *     keeps one (shift, scale) per token, the min and range of all its G
+ *     components. Component j is coded on k_j = 2^b_j - 1 levels,
+ *     q = clamp(rint(fp32(c - shift) * fp32(k_j / scale)), 0, k_j), and
+ *     decodes to shift + q * fp32(scale / k_j); b_j = 0 drops it (0). A
+ *     group is active if any b_j > 0; its codes are packed in component
+ *     order, code j at bit sum_{i<j} b_i of the group's chunk, which is
+ *     ceil(sum_j b_j / 8) bytes; an active group costs 64 + 8 ceil(sum_j
+ *     b_j / 8) bits. The widths minimise the sum of the components'
+ *     empirical distortions within the budget (ties: fewest bits, then the
+ *     largest width sum for the earliest group, then the largest widths
+ *     first). Such slots serialize with mode 1 (see kvtc_save) and decode
+ *     only through the two-stage schedule (kvtc_decode with its full
+ *     workspace, or kvtc_decode_unpack + kvtc_decode_restore): the fused
+ *     schedule, kvtc_decode_noalloc, the pack/unpack hooks and the lossless
+ *     stage return KVTC_E_UNSUPPORTED for them.
  * With no flag each tensor gets exactly kvtc_calibrate's result. A (layer,
  * kind) may appear at most once; the call is all or nothing (on error no slot
  * changes). Errors: KVTC_E_INVALID (bad arguments, unknown flags, too few
@@ -209,9 +230,11 @@ kvtc_status kvtc_slot_info_get(const kvtc_codec* codec, int32_t layer, int32_t k
  * needed) is set. Format (little-endian): "KVTA", u32 version=1, i32 n_layers,
  * kv_heads, head_dim, sink, window, group, max_bits, f32 bits_per_value,
  * i32 dtype, i32 n_slots, then per slot in (layer, kind) order: "KVTS",
- * i32 layer, kind, F, G, n_act, r_eff, 0, u8 widths[F/G] zero-padded to a
- * multiple of 8, f32 mu32[F], f64 lambda[F], f32 V32[F][r_eff] (active columns
- * in component order), u64 slot_id = FNV-1a 64 of the slot's preceding bytes. */
+ * i32 layer, kind, F, G, n_act, r_eff, mode (0: a width per group, 1: a
+ * width per component), u8 widths[F/G] (mode 0) or widths[F] (mode 1)
+ * zero-padded to a multiple of 8, f32 mu32[F], f64 lambda[F], f32
+ * V32[F][r_eff] (active groups' columns in component order), u64 slot_id =
+ * FNV-1a 64 of the slot's preceding bytes. */
 kvtc_status kvtc_save(const kvtc_codec* codec, void* buf, size_t cap, size_t* written);
 /* Create a codec from artifact bytes (host memory); checks every slot id. */
 kvtc_status kvtc_load(const void* buf, size_t n, kvtc_codec** out);

@@ -22,7 +22,7 @@ KVTC_F32, KVTC_BF16 = 0, 1
 KVTC_K, KVTC_V = 0, 1
 KVTC_MAX_REFF = 256
 KVTC_MAX_JOBS = 4096
-KVTC_CAL_SHARED_BASIS, KVTC_CAL_GLOBAL_BUDGET = 1, 2
+KVTC_CAL_SHARED_BASIS, KVTC_CAL_GLOBAL_BUDGET, KVTC_CAL_COMPONENT_WIDTHS = 1, 2, 4
 
 
 class kvtc_params(C.Structure):
@@ -46,7 +46,7 @@ class kvtc_job(C.Structure):
 class kvtc_slot_info(C.Structure):
     _fields_ = [("calibrated", C.c_int32), ("n_act", C.c_int32), ("r_eff", C.c_int32),
                 ("record_bytes", C.c_int32), ("slot_id", C.c_uint64),
-                ("widths", C.c_uint8 * 512)]
+                ("widths", C.c_uint8 * 512), ("per_component", C.c_int32)]
 
 
 class KvtcError(RuntimeError):

@@ -30,7 +30,8 @@ kvtc_status fail(kvtc_status s, const std::string& msg) {
 
 struct Slot {
   bool calibrated = false;
-  std::vector<uint8_t> widths;   // [F/G]
+  std::vector<uint8_t> widths;   // [F/G]; with cwidths, each group's largest component width
+  std::vector<uint8_t> cwidths;  // [F] a width per component, or empty (a width per group)
   std::vector<float> mu32;       // [F]
   std::vector<double> lam;       // [F]
   std::vector<float> V32;        // [F][r_eff]
@@ -171,23 +172,33 @@ std::vector<uint8_t> dp_allocate(const std::vector<double>& D, int n_g, int nb, 
   return w;
 }
 
+// Bytes of a group's code chunk with a width per component: the widths'
+// sum rounded up to whole bytes.
+int chunk_bytes_pc(const uint8_t* cw, int G) {
+  int sum = 0;
+  for (int i = 0; i < G; ++i) sum += cw[i];
+  return (sum + 7) / 8;
+}
+
 void finish_slot(const kvtc_params& p, int layer, int kind, Slot& s) {
   const int F = p.kv_heads * p.head_dim, G = p.group, n_g = F / G;
+  const bool pc = !s.cwidths.empty();
   s.n_act = 0;
-  int sum_b = 0;
+  int code_bytes = 0;
   for (int g = 0; g < n_g; ++g)
     if (s.widths[g]) {
       ++s.n_act;
-      sum_b += s.widths[g];
+      code_bytes += pc ? chunk_bytes_pc(s.cwidths.data() + (size_t)g * G, G) : G * s.widths[g] / 8;
     }
   s.r_eff = s.n_act * G;
-  s.record_bytes = 8 * s.n_act + G * sum_b / 8;
+  s.record_bytes = 8 * s.n_act + code_bytes;
   std::vector<uint8_t> b;
   b.insert(b.end(), {'K', 'V', 'T', 'S'});
-  const int32_t hdr[7] = {layer, kind, F, G, s.n_act, s.r_eff, 0};
+  const int32_t hdr[7] = {layer, kind, F, G, s.n_act, s.r_eff, pc ? 1 : 0};
   for (int32_t v : hdr) put(b, v);
-  const size_t wpad = (size_t)(n_g + 7) / 8 * 8;
-  for (size_t i = 0; i < wpad; ++i) b.push_back(i < (size_t)n_g ? s.widths[i] : 0);
+  const std::vector<uint8_t>& wv = pc ? s.cwidths : s.widths;
+  const size_t nw = wv.size(), wpad = (nw + 7) / 8 * 8;
+  for (size_t i = 0; i < wpad; ++i) b.push_back(i < nw ? wv[i] : 0);
   for (float v : s.mu32) put(b, v);
   for (double v : s.lam) put(b, v);
   for (float v : s.V32) put(b, v);
@@ -402,13 +413,126 @@ std::vector<double> distortion(const CalRows& r, int F, int G, int nb, const std
   return D;
 }
 
+// Per-component distortion Dc[j][b] (a width per component): component j
+// on b levels of its group's grid (the min and range of all G components),
+// b = 0 its energy.
+std::vector<double> distortion_pc(const CalRows& r, int F, int G, int nb, const std::vector<double>& V,
+                                  int threads) {
+  const long n_r = r.n_r;
+  const int n_g = F / G;
+  std::vector<double> C((size_t)n_r * F);
+  gemm_f64((int)n_r, F, F, r.X.data(), F, 1, V.data(), F, C.data(), F, false, threads);
+  std::vector<double> D((size_t)F * nb, 0.0);
+  parallel_for(n_g, threads, [&](int g) {
+    std::vector<double> acc((size_t)G * nb, 0.0);
+    for (long t = 0; t < n_r; ++t) {
+      const double* cg = C.data() + (size_t)t * F + (size_t)g * G;
+      double mn = cg[0], mx = cg[0];
+      for (int i = 1; i < G; ++i) {
+        mn = std::min(mn, cg[i]);
+        mx = std::max(mx, cg[i]);
+      }
+      const double scale = mx - mn;
+      for (int i = 0; i < G; ++i) {
+        acc[(size_t)i * nb] += cg[i] * cg[i];
+        if (!(scale > 0)) continue;  // every value equals the shift: no error
+        for (int b = 1; b < nb; ++b) {
+          const double k = (double)((1 << b) - 1);
+          double q = std::nearbyint((cg[i] - mn) * (k / scale));
+          q = std::min(std::max(q, 0.0), k);
+          const double d = cg[i] - (mn + q * (scale / k));
+          acc[(size_t)i * nb + b] += d * d;
+        }
+      }
+    }
+    for (int i = 0; i < G; ++i)
+      for (int b = 0; b < nb; ++b) D[((size_t)g * G + i) * nb + b] = acc[(size_t)i * nb + b] / (double)n_r;
+  });
+  return D;
+}
+
+int group_cost_pc(int sum) { return sum == 0 ? 0 : kScaleBits + 8 * ((sum + 7) / 8); }
+
+// Widths per component minimising sum_j Dc[j][b_j] within the budget, a
+// group costing 64 + 8 ceil(sum_j b_j / 8) bits when any b_j > 0. Per group,
+// e[i][s] = least distortion of components i.. of the group with widths
+// summing to s (nested from the last component); across groups,
+// f[g][u] = min_s e_g[0][s] + f[g+1][u - cost(s)] (nested from the last
+// group). Ties: fewest bits, then the largest s for the earliest group,
+// then the largest widths first inside a group.
+std::vector<uint8_t> dp_allocate_pc(const std::vector<double>& Dc, int F, int nb, int G, long budget) {
+  const double INF = std::numeric_limits<double>::infinity();
+  const int n_g = F / G, smax = (nb - 1) * G;
+  const long U = budget + 1;
+  std::vector<double> E((size_t)n_g * (G + 1) * (smax + 1), INF);
+  auto e = [&](int g, int i, int sm) -> double& { return E[((size_t)g * (G + 1) + i) * (smax + 1) + sm]; };
+  for (int g = 0; g < n_g; ++g) {
+    const double* D = Dc.data() + (size_t)g * G * nb;
+    e(g, G, 0) = 0.0;
+    for (int i = G - 1; i >= 0; --i)
+      for (int sm = 0; sm <= smax; ++sm) {
+        double best = INF;
+        for (int b = 0; b < nb && b <= sm; ++b) {
+          const double nx = e(g, i + 1, sm - b);
+          if (nx < INF) {
+            const double v = D[(size_t)i * nb + b] + nx;
+            if (v < best) best = v;
+          }
+        }
+        e(g, i, sm) = best;
+      }
+  }
+  std::vector<double> f((size_t)(n_g + 1) * U, INF);
+  f[(size_t)n_g * U] = 0.0;
+  for (int g = n_g - 1; g >= 0; --g)
+    for (long u = 0; u < U; ++u) {
+      double best = INF;
+      for (int sm = 0; sm <= smax; ++sm) {
+        const long c = group_cost_pc(sm);
+        if (c > u || !(e(g, 0, sm) < INF)) continue;
+        const double nx = f[(size_t)(g + 1) * U + u - c];
+        if (nx < INF) {
+          const double v = e(g, 0, sm) + nx;
+          if (v < best) best = v;
+        }
+      }
+      f[(size_t)g * U + u] = best;
+    }
+  long u = 0;
+  for (long v = 1; v < U; ++v)
+    if (f[v] < f[u]) u = v;
+  std::vector<uint8_t> w(F, 0);
+  for (int g = 0; g < n_g; ++g) {
+    int sm = smax;
+    for (; sm >= 0; --sm) {
+      const long c = group_cost_pc(sm);
+      if (c <= u && e(g, 0, sm) < INF && e(g, 0, sm) + f[(size_t)(g + 1) * U + u - c] == f[(size_t)g * U + u])
+        break;
+    }
+    if (sm < 0) sm = 0;   // unreachable: f[g][u] came from some s
+    u -= group_cost_pc(sm);
+    const double* D = Dc.data() + (size_t)g * G * nb;
+    for (int i = 0; i < G; ++i)
+      for (int b = std::min(nb - 1, sm); b >= 0; --b) {
+        const double nx = e(g, i + 1, sm - b);
+        if (nx < INF && D[(size_t)i * nb + b] + nx == e(g, i, sm)) {
+          w[(size_t)g * G + i] = (uint8_t)b;
+          sm -= b;
+          break;
+        }
+      }
+  }
+  return w;
+}
+
 std::vector<float> to_f32(const std::vector<double>& v) { return std::vector<float>(v.begin(), v.end()); }
 
 // A calibrated slot from its widths, mean, eigenvalues and full basis
 // (V[f][j] in fp32, F x F): the active groups' columns in component order.
 kvtc_status build_slot(const kvtc_params& p, int layer, int kind, const std::vector<uint8_t>& widths,
                        const std::vector<double>& mu, const std::vector<double>& lam,
-                       const std::vector<float>& V, Slot& s) {
+                       const std::vector<float>& V, Slot& s,
+                       const std::vector<uint8_t>& cwidths = std::vector<uint8_t>()) {
   const int F = p.kv_heads * p.head_dim, G = p.group, n_g = F / G;
   int n_act = 0;
   for (int g = 0; g < n_g; ++g) n_act += widths[g] ? 1 : 0;
@@ -427,6 +551,7 @@ kvtc_status build_slot(const kvtc_params& p, int layer, int kind, const std::vec
       for (int f = 0; f < F; ++f) s.V32[(size_t)f * n_act * G + a * G + i] = V[(size_t)f * F + g * G + i];
     ++a;
   }
+  s.cwidths = cwidths;
   finish_slot(p, layer, kind, s);
   return KVTC_OK;
 }
@@ -516,8 +641,11 @@ kvtc_status kvtc_calibrate(kvtc_codec* c, int32_t layer, int32_t kind, const voi
 kvtc_status kvtc_calibrate_set(kvtc_codec* c, const kvtc_calib_input* in, int32_t n, uint32_t flags,
                                int32_t threads) {
   if (!c || !in || n < 1) return fail(KVTC_E_INVALID, "bad codec or inputs");
-  if (flags & ~(uint32_t)(KVTC_CAL_SHARED_BASIS | KVTC_CAL_GLOBAL_BUDGET))
+  if (flags & ~(uint32_t)(KVTC_CAL_SHARED_BASIS | KVTC_CAL_GLOBAL_BUDGET | KVTC_CAL_COMPONENT_WIDTHS))
     return fail(KVTC_E_INVALID, "unknown calibration flags");
+  const bool pcw = (flags & KVTC_CAL_COMPONENT_WIDTHS) != 0;
+  if (pcw && (flags & KVTC_CAL_GLOBAL_BUDGET))
+    return fail(KVTC_E_INVALID, "component widths take a budget per tensor");
   if (threads <= 0) threads = std::max(1u, std::thread::hardware_concurrency());
   const kvtc_params& p = c->p;
   const int F = c->F, G = p.group, n_g = c->n_g, nb = p.max_bits + 1;
@@ -563,7 +691,7 @@ kvtc_status kvtc_calibrate_set(kvtc_codec* c, const kvtc_calib_input* in, int32_
         CalRows r;
         st = load_centred(p, F, in[i].host_kv, in[i].n_tokens, threads, r);
         if (st != KVTC_OK) return st;
-        Ds[i] = distortion(r, F, G, nb, V, threads);
+        Ds[i] = pcw ? distortion_pc(r, F, G, nb, V, threads) : distortion(r, F, G, nb, V, threads);
         vref[i] = same[0];
       }
       Vs[same[0]] = to_f32(V);
@@ -578,7 +706,7 @@ kvtc_status kvtc_calibrate_set(kvtc_codec* c, const kvtc_calib_input* in, int32_
       add_scatter(r, F, threads, cov);
       st = eigen_basis(F, cov, (double)r.n_r, V, lam);
       if (st != KVTC_OK) return st;
-      Ds[i] = distortion(r, F, G, nb, V, threads);
+      Ds[i] = pcw ? distortion_pc(r, F, G, nb, V, threads) : distortion(r, F, G, nb, V, threads);
       mus[i] = std::move(r.mu);
       Vs[i] = to_f32(V);
       lams[i] = std::move(lam);
@@ -593,6 +721,8 @@ kvtc_status kvtc_calibrate_set(kvtc_codec* c, const kvtc_calib_input* in, int32_
     for (int i : ord) ds.push_back(Ds[i]);
     const auto ws = dp_allocate_global(ds, n_g, nb, G, budget_bits(p), KVTC_MAX_REFF / G);
     for (int k = 0; k < n; ++k) widths[ord[k]] = ws[k];
+  } else if (pcw) {
+    for (int i : ord) widths[i] = dp_allocate_pc(Ds[i], F, nb, G, budget_bits(p));   // per component
   } else {
     for (int i : ord) widths[i] = dp_allocate(Ds[i], n_g, nb, G, budget_bits(p));
   }
@@ -600,8 +730,15 @@ kvtc_status kvtc_calibrate_set(kvtc_codec* c, const kvtc_calib_input* in, int32_
   // Build every slot first, so a failure leaves the codec unchanged.
   std::vector<Slot> out(n);
   for (int i : ord) {
-    kvtc_status st = build_slot(p, in[i].layer, in[i].kind, widths[i], mus[i], lams[vref[i]],
-                                Vs[vref[i]], out[i]);
+    std::vector<uint8_t> gw = widths[i], cw;
+    if (pcw) {   // a group's width: its largest component's (nonzero: active)
+      cw.swap(gw);
+      gw.assign(n_g, 0);
+      for (int g = 0; g < n_g; ++g)
+        for (int k = 0; k < G; ++k) gw[g] = std::max(gw[g], cw[(size_t)g * G + k]);
+    }
+    kvtc_status st = build_slot(p, in[i].layer, in[i].kind, gw, mus[i], lams[vref[i]], Vs[vref[i]],
+                                out[i], cw);
     if (st != KVTC_OK) return st;
   }
   for (int i : ord) c->slots[key(i)] = std::move(out[i]);
@@ -621,6 +758,7 @@ kvtc_status kvtc_slot_info_get(const kvtc_codec* c, int32_t layer, int32_t kind,
   info->r_eff = s.r_eff;
   info->record_bytes = s.record_bytes;
   info->slot_id = s.slot_id;
+  info->per_component = s.cwidths.empty() ? 0 : 1;
   for (int g = 0; g < c->n_g && g < 512; ++g) info->widths[g] = s.widths[g];
   return KVTC_OK;
 }
@@ -684,24 +822,31 @@ kvtc_status kvtc_load(const void* buf, size_t n, kvtc_codec** out) {
     const size_t start = off;
     if (!need(32) || std::memcmp(b + off, "KVTS", 4) != 0) return fail(KVTC_E_CORRUPT, "bad slot magic");
     off += 4;
-    int32_t layer, kind, sF, sG, n_act, r_eff, zero;
+    int32_t layer, kind, sF, sG, n_act, r_eff, mode;
     rd32(&layer);
     rd32(&kind);
     rd32(&sF);
     rd32(&sG);
     rd32(&n_act);
     rd32(&r_eff);
-    rd32(&zero);
+    rd32(&mode);
     int idx;
     if (!slot_index(c, layer, kind, &idx) || sF != F || sG != G || r_eff != n_act * G ||
-        n_act < 0 || n_act > n_g)
+        n_act < 0 || n_act > n_g || (mode != 0 && mode != 1))
       return fail(KVTC_E_CORRUPT, "inconsistent slot header");
     if (r_eff > KVTC_MAX_REFF) return fail(KVTC_E_UNSUPPORTED, "slot exceeds KVTC_MAX_REFF");
-    const size_t wpad = (size_t)(n_g + 7) / 8 * 8;
+    const size_t nw = mode ? (size_t)F : (size_t)n_g, wpad = (nw + 7) / 8 * 8;
     const size_t body = wpad + 4 * (size_t)F + 8 * (size_t)F + 4 * (size_t)F * r_eff + 8;
     if (!need(body)) return fail(KVTC_E_CORRUPT, "truncated slot");
     Slot s;
-    s.widths.assign(b + off, b + off + n_g);
+    if (mode) {
+      s.cwidths.assign(b + off, b + off + F);
+      s.widths.assign(n_g, 0);
+      for (int g = 0; g < n_g; ++g)
+        for (int i = 0; i < G; ++i) s.widths[g] = std::max(s.widths[g], s.cwidths[(size_t)g * G + i]);
+    } else {
+      s.widths.assign(b + off, b + off + n_g);
+    }
     off += wpad;
     int cnt = 0;
     for (uint8_t w : s.widths) {
@@ -738,6 +883,7 @@ size_t kvtc_device_state_bytes(const kvtc_codec* c) {
     const size_t r_enc = align_up((size_t)s.r_eff, 32), r_dec = align_up((size_t)s.r_eff, 16);
     n += 2 * align_up(4 * (size_t)c->F, kAlign) + align_up(2 * r_enc * c->F, kAlign) +
          align_up(2 * (size_t)c->F * r_dec, kAlign) + align_up(4 * r_enc, kAlign);
+    if (!s.cwidths.empty()) n += align_up(4 * (size_t)s.r_eff, kAlign);
   }
   return n;
 }
@@ -771,12 +917,14 @@ kvtc_status kvtc_upload(kvtc_codec* c, void* d_state, size_t bytes, hipStream_t 
     d.G = G;
     d.F = F;
     d.slot_id = s.slot_id;
+    const bool pc = !s.cwidths.empty();
+    d.pc = pc ? 1 : 0;
     int a = 0, chunk = 8 * s.n_act;
     for (int g = 0; g < c->n_g; ++g) {
       if (!s.widths[g]) continue;
       d.width[a] = s.widths[g];
       d.chunk_off[a] = (uint16_t)chunk;
-      chunk += G * s.widths[g] / 8;
+      chunk += pc ? chunk_bytes_pc(s.cwidths.data() + (size_t)g * G, G) : G * s.widths[g] / 8;
       ++a;
     }
     d.mu_off = off;
@@ -823,6 +971,23 @@ kvtc_status kvtc_upload(kvtc_codec* c, void* d_state, size_t bytes, hipStream_t 
       cmu[j] = (float)acc;
     }
     off += align_up(4 * (size_t)r_enc, kAlign);
+    if (pc) {
+      // per active component: (bit position in the record << 8) | width
+      d.pcw_off = off;
+      uint32_t* pcw = (uint32_t*)(h.data() + off);
+      int aa = 0;
+      for (int g = 0; g < c->n_g; ++g) {
+        if (!s.widths[g]) continue;
+        uint32_t bit = 8u * d.chunk_off[aa];
+        for (int i = 0; i < G; ++i) {
+          const uint32_t w = s.cwidths[(size_t)g * G + i];
+          pcw[aa * G + i] = (bit << 8) | w;
+          bit += w;
+        }
+        ++aa;
+      }
+      off += align_up(4 * (size_t)r, kAlign);
+    }
   }
   std::memcpy(h.data(), table.data(), table.size() * sizeof(DevSlot));
   hipError_t e = hipMemcpyAsync(d_state, h.data(), need, hipMemcpyHostToDevice, stream);
@@ -928,6 +1093,10 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
     d.kind = j.kind;
     d.status_idx = i;
     d.bs_shift = -1;
+    if (!s.cwidths.empty() && (mode == Mode::Decode || mode == Mode::Pack || mode == Mode::UnpackCodes))
+      return fail(KVTC_E_UNSUPPORTED,
+                  "a width per component needs the two-stage decode (kvtc_decode with its full workspace, "
+                  "or the stage calls); the pack and unpack hooks take group widths");
     if (mode == Mode::Encode || mode == Mode::Pack) {
       if (j.dst_capacity < stream_bytes(c, s, j.n_tokens))
         return fail(KVTC_E_CAPACITY, "job: dst_capacity below kvtc_encoded_bytes");
@@ -1107,6 +1276,7 @@ kvtc_status lz_plan(kvtc_codec* c, bool enc, const kvtc_job* jobs, int n, void* 
     if (!slot_index(c, j.layer, j.kind, &idx)) return fail(KVTC_E_INVALID, "job: bad layer or kind");
     const Slot& s = c->slots[idx];
     if (!s.calibrated) return fail(KVTC_E_NOT_CALIBRATED, "job: (layer, kind) is not calibrated");
+    if (!s.cwidths.empty()) return fail(KVTC_E_UNSUPPORTED, "the lossless stage takes group widths");
     if (j.n_tokens < 0 || j.n_tokens > (int64_t)INT32_MAX) return fail(KVTC_E_INVALID, "job: bad n_tokens");
     LzJob& d = desc[i];
     std::memset(&d, 0, sizeof(d));

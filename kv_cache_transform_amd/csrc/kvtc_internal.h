@@ -30,6 +30,8 @@ struct alignas(16) DevSlot {
   uint64_t vdec_off;      // f16  V'   F x r_dec in MFMA A-operand order (cols >= r_eff are zero)
   uint64_t mhi_off;       // f32  mu_hi[F] = bf16_rne(mu32), the encode's centring vector
   uint64_t cmu_off;       // f32  V'^T (mu32 - mu_hi) [r_enc]  (rows >= r_eff are zero)
+  uint64_t pcw_off;       // with a width per component: u32 [r_eff], per active component
+                          // (bit position in the record << 8) | width
   uint64_t slot_id;
   int32_t calibrated;
   int32_t n_act;
@@ -39,7 +41,9 @@ struct alignas(16) DevSlot {
   int32_t r_dec;          // r_eff rounded up to 16 (decode MFMA K steps)
   int32_t G;
   int32_t F;
-  uint8_t width[kMaxActGroups];        // width of active group a
+  int32_t pc;             // 1: a width per component (pcw_off), 0: a width per group
+  int32_t pad_;
+  uint8_t width[kMaxActGroups];        // width of active group a (its largest component's, pc)
   uint16_t chunk_off[kMaxActGroups];   // byte offset of its chunk in a record
 };
 

@@ -332,3 +332,41 @@ def test_lossless_bound_matches_oracle():
         job = K.make_job(0, 0, T, 16, 16, 1 << 30, src_capacity=1 << 30)
         assert c.lossless_workspace_bytes([job], True) > 0 and c.lossless_workspace_bytes([job], False) > 0
     assert c.lossless_bound(0, 1, 100) == 0
+
+
+def test_component_widths_match_oracle():
+    """KVTC_CAL_COMPONENT_WIDTHS against the oracle's reading Q2c: small
+    family-B tensors at G = 16 and 32 (widths exact), a llama31_8b tensor
+    (widths, or the objective on a near tie); the artifact bytes go both
+    ways; with the global budget the call is refused."""
+    for G, bpv in ((16, 3.0), (32, 2.0)):
+        x, _ = pins.family_b_small(seed=29, n=2200)
+        op = O.Params(2, 2, 32, 4, 8, G, 8, bpv, O.DTYPE_F32)
+        kp = K.params(2, 2, 32, 4, 8, G, 8, bpv, K.KVTC_F32)
+        c = K.Codec(kp)
+        c.calibrate_set([(1, 0, x)], K.KVTC_CAL_COMPONENT_WIDTHS, threads=2)
+        so = O.calibrate_set([(1, 0, x)], op, component_widths=True)[(1, 0)]
+        sl = O.parse_artifact(c.save()).slots[(1, 0)]
+        assert np.array_equal(sl.cwidths, so.cwidths), (G, sl.cwidths, so.cwidths)
+        assert sl.record_bytes == so.record_bytes == c.slot(1, 0).record_bytes
+        assert c.slot(1, 0).per_component == 1
+        art = O.Artifact(op, {(1, 0): so}).serialize()
+        assert K.Codec.load(art).save() == art
+    w, ins = _set_inputs(layers=(0,), n=3000)
+    op, kp = _params_pair(w)
+    c = K.Codec(kp)
+    c.calibrate_set([(l, k, synth.storage(w, x)) for l, k, x in ins], K.KVTC_CAL_COMPONENT_WIDTHS, threads=8)
+    lib = O.parse_artifact(c.save()).slots
+    orc = O.calibrate_set(ins, op, component_widths=True)
+    for k in orc:
+        a, b = lib[k], orc[k]
+        if not np.array_equal(a.cwidths, b.cwidths):
+            obj = lambda cw: sum(b.D[j, v] for j, v in enumerate(cw))
+            assert abs(obj(a.cwidths) - obj(b.cwidths)) <= 1e-9 * obj(b.cwidths)
+        assert np.array_equal(a.mu32, b.mu32)
+        assert sum(64 + 8 * ((int(s) + 7) // 8) for s in a.cwidths.reshape(-1, w.group).sum(axis=1) if s) \
+            <= op.budget_bits
+    with pytest.raises(K.KvtcError) as e:
+        c.calibrate_set([(0, 0, synth.storage(w, ins[0][2]))],
+                        K.KVTC_CAL_COMPONENT_WIDTHS | K.KVTC_CAL_GLOBAL_BUDGET)
+    assert e.value.status == K.KVTC_E_INVALID
