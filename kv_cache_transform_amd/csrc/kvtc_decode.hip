@@ -100,6 +100,29 @@ __device__ __forceinline__ uint4 frag_from_bits(uint64_t bits, float shift, floa
   }
 }
 
+// B fragment of 8 components with a width each (a width per component):
+// entry = (bit position in the record << 8) | width; c_hat = shift + q *
+// fp32(scale / k) times the power of two Sinv as in frag_from_bits, and 0
+// for a zero width. A code spans at most two bytes of the record row.
+__device__ __forceinline__ uint4 frag_pc(const uint8_t* rec, const uint32_t* ent, float shift, float scale,
+                                         float Sinv) {
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t e = ent[i], pos = e >> 8;
+    const int w = (int)(e & 0xFFu);
+    x[i] = 0.f;
+    if (w) {
+      const uint32_t b2 = (uint32_t)rec[pos >> 3] | ((uint32_t)rec[(pos >> 3) + 1] << 8);
+      const uint32_t q = (b2 >> (pos & 7u)) & ((1u << w) - 1u);
+      const float kf = (float)((1 << w) - 1);
+      x[i] = __builtin_fmaf((float)q, div_by_levels(scale, kf, 1.0f / kf) * Sinv, shift * Sinv);
+    }
+  }
+  return make_uint4(pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]), pack_f16x2(x[4], x[5]),
+                    pack_f16x2(x[6], x[7]));
+}
+
 // Stage 1, one launch over a batch of jobs. First the header and
 // passthrough units (kPrepPassRows rows each; job j owns max(1, units) of
 // them from cblk_begin, and its first one records the header check in the
@@ -193,14 +216,20 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
   float S, Sinv;
   token_scale(m, S, Sinv);
   uint8_t* blk = (uint8_t*)jd.staging + (size_t)c * stg_block_bytes(KS);
+  const uint32_t* pcw = sl.pc ? (const uint32_t*)(a.state + sl.pcw_off) : nullptr;
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const int ag = 16 * s / G;
-    const int w = slot_width(sl, ag);
-    const float kf = (float)((1 << w) - 1);
-    const uint4 f = tok_ok ? frag_from_bits(code_bits8(r, sl, ag, 16 * s + 8 * h - ag * G, w), ps[s].x,
-                                            ps[s].y, w, kf, 1.0f / kf, Sinv)
-                           : make_uint4(0u, 0u, 0u, 0u);
+    uint4 f = make_uint4(0u, 0u, 0u, 0u);
+    if (pcw) {   // a width per component (uniform)
+      if (tok_ok) f = frag_pc(r, pcw + 16 * s + 8 * h, ps[s].x, ps[s].y, Sinv);
+    } else {
+      const int w = slot_width(sl, ag);
+      const float kf = (float)((1 << w) - 1);
+      if (tok_ok)
+        f = frag_from_bits(code_bits8(r, sl, ag, 16 * s + 8 * h - ag * G, w), ps[s].x, ps[s].y, w, kf,
+                           1.0f / kf, Sinv);
+    }
     *(uint4*)(blk + s * 1024 + lane * 16) = f;
   }
   if (h == 0) *(float*)(blk + KS * 1024 + t * 4) = tok_ok ? S : 1.f;

@@ -284,6 +284,14 @@ __device__ __forceinline__ void or_code_run(uint32_t* rw, uint32_t pos, uint32_t
   if (sh + 4u * (uint32_t)w > 32u) atomicOr(rw + (pos >> 5) + 1, run >> (32u - sh));
 }
 
+// One code of width w at record bit pos (a width per component): LDS words,
+// atomics since neighbouring codes can share a word.
+__device__ __forceinline__ void or_code(uint32_t* rw, uint32_t pos, uint32_t q, int w) {
+  const uint32_t sh = pos & 31u;
+  atomicOr(rw + (pos >> 5), q << sh);
+  if (sh + (uint32_t)w > 32u) atomicOr(rw + (pos >> 5) + 1, q >> (32u - sh));
+}
+
 // Bit position in the record of component o of active group a (width w).
 __device__ __forceinline__ uint32_t code_bit(CSlot& sl, int a, int o, int w) {
   return 8u * (uint32_t)slot_chunk(sl, a) + (uint32_t)(o * w);

@@ -50,9 +50,13 @@ __device__ __forceinline__ float xor32(float x, int h) {
 // [(8m + 4h) w, (8m + 4h + 4) w) of the group's chunk and are merged into
 // the record with at most two 32-bit ORs per run (runs of the two lanes can
 // share a word).
+//
+// With a width per component (sl.pc), component o of active group a is
+// coded on its own 2^w - 1 levels of the group's range and ORed in at its
+// own bit position; both come from the slot's table (pcw_off in state).
 template <int NB, int G>
-__device__ __forceinline__ void quantize_tile(const f32x16 (&acc)[NB], CSlot& sl, uint8_t* rec,
-                                              int h, bool tok_ok) {
+__device__ __forceinline__ void quantize_tile(const f32x16 (&acc)[NB], CSlot& sl, const uint8_t* state,
+                                              uint8_t* rec, int h, bool tok_ok) {
   // A group of G components is the item range [(G/2) * sg, (G/2) * (sg + 1))
   // of block b with sg = a % (32/G).
   constexpr int SUB = 32 / G;
@@ -74,21 +78,39 @@ __device__ __forceinline__ void quantize_tile(const f32x16 (&acc)[NB], CSlot& sl
         }
         mn = fminf(mn, xor32(mn, h));
         mx = fmaxf(mx, xor32(mx, h));
-        const int w = slot_width(sl, ag);
-        const float k = (float)((1 << w) - 1);
         const float scale = mx - mn;
-        const float inv = scale > 0.f ? k / scale : 0.f;
+        if (sl.pc) {
+          const uint32_t* pcw = (const uint32_t*)(state + sl.pcw_off) + ag * G;
 #pragma unroll
-        for (int m = 0; m < G / 8; ++m) {
-          uint32_t run = 0;
+          for (int m = 0; m < G / 8; ++m)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float d = v[4 * m + e] - mn;
-            const float u = d * inv;
-            const float r = fminf(fmaxf(__builtin_rintf(u), 0.f), k);
-            run |= (uint32_t)r << (e * w);
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t ent = pcw[8 * m + 4 * h + e];
+              const int wc = (int)(ent & 0xFFu);
+              if (wc) {
+                const float kc = (float)((1 << wc) - 1);
+                const float invc = scale > 0.f ? kc / scale : 0.f;
+                const float u = (v[4 * m + e] - mn) * invc;
+                const float r = fminf(fmaxf(__builtin_rintf(u), 0.f), kc);
+                if (tok_ok) or_code(rw, ent >> 8, (uint32_t)r, wc);
+              }
+            }
+        } else {
+          const int w = slot_width(sl, ag);
+          const float k = (float)((1 << w) - 1);
+          const float inv = scale > 0.f ? k / scale : 0.f;
+#pragma unroll
+          for (int m = 0; m < G / 8; ++m) {
+            uint32_t run = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float d = v[4 * m + e] - mn;
+              const float u = d * inv;
+              const float r = fminf(fmaxf(__builtin_rintf(u), 0.f), k);
+              run |= (uint32_t)r << (e * w);
+            }
+            if (tok_ok) or_code_run(rw, code_bit(sl, ag, 8 * m + 4 * h, w), run, w);
           }
-          if (tok_ok) or_code_run(rw, code_bit(sl, ag, 8 * m + 4 * h, w), run, w);
         }
         if (tok_ok && h == 0) put_scales(rw, ag, mn, scale);
       }
@@ -396,7 +418,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!F32IN
       for (int i = lane; i < nz; i += 64) z[i] = (u32x4){0u, 0u, 0u, 0u};
       wave_lds_sync();
     }
-    quantize_tile<NB, G>(acc, sl, smem + (size_t)tl * rbp, h, (uint32_t)tl < n);
+    quantize_tile<NB, G>(acc, sl, a.state, smem + (size_t)tl * rbp, h, (uint32_t)tl < n);
     if (te < b_end) init_acc(next_cblk_job(a, cj, te));
     __syncthreads();
     records_to_global((uint8_t*)jd.dst + record_base(jd, F, esz) + (size_t)t0 * rb, smem, n, rb, rbp);
