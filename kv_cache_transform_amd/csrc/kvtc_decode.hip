@@ -135,7 +135,8 @@ __device__ __forceinline__ uint4 frag_pc(const uint8_t* rec, const uint32_t* ent
 // otherwise), and builds the B operands and token scales of its 32 tokens,
 // stg_block_bytes(KS) bytes of staging per block. No workgroup barrier
 // follows the passthrough units: the waves run on their own.
-template <int KS>
+// PC: every job of the launch has a width per component (frag_pc).
+template <int KS, bool PC>
 __global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int flag;
@@ -216,12 +217,12 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const LaunchArgs a) {
   float S, Sinv;
   token_scale(m, S, Sinv);
   uint8_t* blk = (uint8_t*)jd.staging + (size_t)c * stg_block_bytes(KS);
-  const uint32_t* pcw = sl.pc ? (const uint32_t*)(a.state + sl.pcw_off) : nullptr;
+  const uint32_t* pcw = PC ? (const uint32_t*)(a.state + sl.pcw_off) : nullptr;
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const int ag = 16 * s / G;
     uint4 f = make_uint4(0u, 0u, 0u, 0u);
-    if (pcw) {   // a width per component (uniform)
+    if (PC) {
       if (tok_ok) f = frag_pc(r, pcw + 16 * s + 8 * h, ps[s].x, ps[s].y, Sinv);
     } else {
       const int w = slot_width(sl, ag);
@@ -951,10 +952,15 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const LaunchArgs a, ui
 int launch_prep(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
   // one wave per compressed block; any grid covers the passthrough units
   const dim3 g = grid_for(std::max(8u, (a.total_tiles + kWaves - 1) / kWaves));
-#define KVTC_PREP(KV)                                                       \
-  case KV:                                                                  \
-    allow_lds(prep_kernel<KV>, lds);                                        \
-    hipLaunchKernelGGL((prep_kernel<KV>), g, dim3(kThreads), lds, s, a);    \
+#define KVTC_PREP(KV)                                                             \
+  case KV:                                                                        \
+    if (a.pc) {                                                                   \
+      allow_lds(prep_kernel<KV, true>, lds);                                      \
+      hipLaunchKernelGGL((prep_kernel<KV, true>), g, dim3(kThreads), lds, s, a);  \
+    } else {                                                                      \
+      allow_lds(prep_kernel<KV, false>, lds);                                     \
+      hipLaunchKernelGGL((prep_kernel<KV, false>), g, dim3(kThreads), lds, s, a); \
+    }                                                                             \
     break;
   switch (ks) {
     KVTC_KS_CASES(KVTC_PREP)

@@ -1064,7 +1064,7 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
   const size_t out_esz = elem_bytes(out_dtype);
   // Per-job validation and the fields that do not depend on the batch.
   std::vector<JobDesc> desc(n);
-  std::vector<int> key(n);
+  std::vector<int> key(n), pcj(n, 0);
   std::vector<size_t> st_off(n, 0);
   size_t st_total = 0;
   for (int i = 0; i < n; ++i) {
@@ -1133,6 +1133,7 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
         d.staging = d_staging + st_off[i];
       }
       key[i] = (int)(align_up((size_t)s.r_eff, 16) / 16);
+      pcj[i] = s.cwidths.empty() ? 0 : 1;   // stage 1 takes such jobs in launches of their own
       if (s.record_bytes > 24 * key[i]) return fail(KVTC_E_UNSUPPORTED, "record wider than the decode tiles");
     }
   }
@@ -1141,10 +1142,11 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
     return fail(KVTC_E_INVALID, "device state is missing or stale: call kvtc_upload");
   std::vector<int> order(n);
   for (int i = 0; i < n; ++i) order[i] = i;
-  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return key[x] < key[y]; });
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int x, int y) { return key[x] != key[y] ? key[x] < key[y] : pcj[x] < pcj[y]; });
   for (int p = 0; p < n;) {
     int q = p;
-    while (q < n && q - p < kMaxLaunchJobs && key[order[q]] == key[order[p]]) ++q;
+    while (q < n && q - p < kMaxLaunchJobs && key[order[q]] == key[order[p]] && pcj[order[q]] == pcj[order[p]]) ++q;
     LaunchArgs a;
     std::memset(&a, 0, sizeof(a));
     a.n_jobs = q - p;
@@ -1155,6 +1157,7 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
     a.status = (unsigned long long*)d_ws;
     a.sink = (uint8_t*)d_ws + sink_offset(n);
     a.epoch = next_epoch();
+    a.pc = pcj[order[p]];
     uint32_t tiles = 0, cblks = 0;
     size_t rb_max = 0;
     for (int b = 0; b < a.n_jobs; ++b) {

@@ -83,6 +83,7 @@ struct LaunchArgs {
   unsigned long long* status;  // per-launch slice of the workspace status words
   uint8_t* sink;           // kSinkBytes of workspace that absorb stores without a row
   uint32_t epoch;          // stamp of this launch (see status_word)
+  int32_t pc;              // decode stage 1: every job's slot has a width per component
   uint32_t wave_lds;       // decode stage 1: LDS bytes of each wave's record rows;
                            // fused decode: LDS bytes of each record buffer
 };

@@ -313,7 +313,7 @@ def test_calibrate_set_errors_leave_codec_unchanged():
     before = c.save()
     x = synth.storage(w, ins[0][2])
     for args, flags in (([(0, 0, x), (0, 0, x)], 0),            # duplicate
-                        ([(0, 0, x)], 4),                          # unknown flag
+                        ([(0, 0, x)], 8),                          # unknown flag
                         ([(0, 0, x[: w.sink + w.window])], 0),     # no row after sink and window
                         ([(0, 0, x), (5, 0, x)], 0)):              # bad layer
         with pytest.raises(K.KvtcError) as e:
