@@ -61,6 +61,10 @@ def main():
     ap.add_argument("--calib-tokens", type=int, default=0, help="override (0 = workload's)")
     ap.add_argument("--distinct-requests", type=int, default=2,
                     help="distinct synthetic requests per (layer, kind); the rest are copies")
+    ap.add_argument("--core-only", action="store_true",
+                    help="only the step and its per-kernel loops (no lossless stage or online "
+                         "encode sections): for profiler runs whose per-kernel averages must "
+                         "cover the step's launches alone")
     ap.add_argument("--save-artifact", default="", help="write the calibrated artifact here")
     ap.add_argument("--load-artifact", default="",
                     help="use this artifact (written by --save-artifact for the same workload) "
@@ -351,11 +355,12 @@ def main():
                         "r_eff": sorted(set(r_eff.values()))},
         "calibration_s": None if args.load_artifact else round(calib_s, 1),
     }
-    result["lossless"] = lossless_stage(K, codec, jobs, sizes, offs, sbuf, T, F, esz, dev, stream,
-                                        args.steps, raw_s / z_s)
+    if not args.core_only:
+        result["lossless"] = lossless_stage(K, codec, jobs, sizes, offs, sbuf, T, F, esz, dev, stream,
+                                            args.steps, raw_s / z_s)
     if pipe is not None:
         result["pipeline"] = pipe.overlap(stream)
-    else:
+    elif not args.core_only:
         result["online_encode"] = online_encode(K, codec, jobs, sizes, offs, T, F, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(codec, w, jobs[: args.cpu_sample], xs, K)
