@@ -162,8 +162,10 @@ void kvtc_destroy(kvtc_codec* codec);
  * descending eigenvalue with the largest-magnitude entry of each made
  * positive, the empirical distortion D_g(b) of the quantizer on the
  * calibration coefficients, and the DP widths. n_tokens - s - w must be >= 1.
- * Returns KVTC_E_UNSUPPORTED if the widths need more than KVTC_MAX_REFF active
- * components. Uses up to `threads` host threads (0 = hardware concurrency). */
+ * The widths keep at most KVTC_MAX_REFF / G active groups (the kernels'
+ * limit): when the DP's optimum needs more, they minimise the distortion
+ * under both the budget and that cap. Uses up to `threads` host threads
+ * (0 = hardware concurrency). */
 kvtc_status kvtc_calibrate(kvtc_codec* codec, int32_t layer, int32_t kind,
                            const void* host_kv, int64_t n_tokens, int32_t threads);
 
@@ -218,8 +220,9 @@ typedef struct {
  * With no flag each tensor gets exactly kvtc_calibrate's result. A (layer,
  * kind) may appear at most once; the call is all or nothing (on error no slot
  * changes). Errors: KVTC_E_INVALID (bad arguments, unknown flags, too few
- * rows, duplicates), KVTC_E_UNSUPPORTED (without the global budget, a tensor
- * needing more than KVTC_MAX_REFF components). */
+ * rows, duplicates), KVTC_E_UNSUPPORTED (with a width per component, a
+ * tensor needing more than KVTC_MAX_REFF components; group widths keep to
+ * the cap as in kvtc_calibrate). */
 kvtc_status kvtc_calibrate_set(kvtc_codec* codec, const kvtc_calib_input* inputs, int32_t n,
                                uint32_t flags, int32_t threads);
 

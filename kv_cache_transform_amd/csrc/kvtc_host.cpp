@@ -300,6 +300,18 @@ std::vector<std::vector<uint8_t>> dp_allocate_global(const std::vector<std::vect
   return out;
 }
 
+// The DP widths with at most KVTC_MAX_REFF / G active groups (the kernels'
+// limit): dp_allocate's, or, when they need more, the allocation minimising
+// the distortion under both the budget and the cap (dp_allocate_global of
+// the one tensor, which equals dp_allocate whenever the cap does not bind).
+std::vector<uint8_t> dp_allocate_capped(const std::vector<double>& D, int n_g, int nb, int G, long budget) {
+  std::vector<uint8_t> w = dp_allocate(D, n_g, nb, G, budget);
+  int n_act = 0;
+  for (uint8_t b : w) n_act += b ? 1 : 0;
+  if (n_act * G <= KVTC_MAX_REFF) return w;
+  return dp_allocate_global({D}, n_g, nb, G, budget, KVTC_MAX_REFF / G)[0];
+}
+
 // Rows [s, n - w) of one calibration tensor in fp64, centred on their mean.
 struct CalRows {
   long n_r = 0;
@@ -629,7 +641,7 @@ kvtc_status kvtc_calibrate(kvtc_codec* c, int32_t layer, int32_t kind, const voi
   if (st != KVTC_OK) return st;
   const std::vector<double> D = distortion(r, F, p.group, nb, V, threads);
   Slot s;
-  st = build_slot(p, layer, kind, dp_allocate(D, c->n_g, nb, p.group, budget_bits(p)), r.mu, lam,
+  st = build_slot(p, layer, kind, dp_allocate_capped(D, c->n_g, nb, p.group, budget_bits(p)), r.mu, lam,
                   to_f32(V), s);
   if (st != KVTC_OK) return st;
   c->slots[idx] = std::move(s);
@@ -724,7 +736,7 @@ kvtc_status kvtc_calibrate_set(kvtc_codec* c, const kvtc_calib_input* in, int32_
   } else if (pcw) {
     for (int i : ord) widths[i] = dp_allocate_pc(Ds[i], F, nb, G, budget_bits(p));   // per component
   } else {
-    for (int i : ord) widths[i] = dp_allocate(Ds[i], n_g, nb, G, budget_bits(p));
+    for (int i : ord) widths[i] = dp_allocate_capped(Ds[i], n_g, nb, G, budget_bits(p));
   }
 
   // Build every slot first, so a failure leaves the codec unchanged.

@@ -705,14 +705,22 @@ def calibrate_set(inputs, params: Params, shared_basis: bool = False,
         cap = params.n_groups if max_active is None else max_active
         ws = dict(zip(keys, dp_allocate_global([D[k] for k in keys], params.group,
                                                params.budget_bits, cap)))
-    else:
+    elif max_active is None:
         ws = {k: dp_allocate(D[k], params.group, params.budget_bits) for k in keys}
+    else:
+        ws = {k: dp_allocate_global([D[k]], params.group, params.budget_bits, max_active)[0]
+              for k in keys}
     return {k: _make_slot(k[0], k[1], params, mus[k], basis[k][0], basis[k][1], D[k], ws[k])
             for k in keys}
 
 
-def calibrate(x_cal: np.ndarray, params: Params, layer: int, kind: int) -> Slot:
-    """Calibrate one (layer, kind) from calibration rows x_cal [n, F] (values)."""
+def calibrate(x_cal: np.ndarray, params: Params, layer: int, kind: int,
+              max_active: int | None = None) -> Slot:
+    """Calibrate one (layer, kind) from calibration rows x_cal [n, F] (values).
+
+    max_active: at most this many active groups (the widths then minimise the
+    distortion under both the budget and the cap: dp_allocate_global of the
+    one tensor, which is dp_allocate whenever the cap does not bind)."""
     params.check()
     x = np.asarray(x_cal, np.float64)
     n, F = x.shape
@@ -726,7 +734,10 @@ def calibrate(x_cal: np.ndarray, params: Params, layer: int, kind: int) -> Slot:
     V, lam = pca_basis(xc)
     C = xc @ V
     D = distortion_table(C, params.group, params.max_bits)
-    widths = dp_allocate(D, params.group, params.budget_bits)
+    if max_active is None:
+        widths = dp_allocate(D, params.group, params.budget_bits)
+    else:
+        (widths,) = dp_allocate_global([D], params.group, params.budget_bits, max_active)
     G = params.group
     cols = np.concatenate([np.arange(g * G, (g + 1) * G) for g in np.nonzero(widths)[0]]
                           ) if np.any(widths) else np.zeros(0, np.int64)

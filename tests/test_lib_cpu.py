@@ -370,3 +370,22 @@ def test_component_widths_match_oracle():
         c.calibrate_set([(0, 0, synth.storage(w, ins[0][2]))],
                         K.KVTC_CAL_COMPONENT_WIDTHS | K.KVTC_CAL_GLOBAL_BUDGET)
     assert e.value.status == K.KVTC_E_INVALID
+
+
+def test_allocation_keeps_to_the_kernels_cap():
+    """At 8 bits per value the DP's optimum on a llama31_8b tensor wants more
+    than KVTC_MAX_REFF components; the library keeps to the cap with the
+    allocation that is optimal under both limits, the oracle's capped one."""
+    w = synth.workload("llama31_8b")
+    x = synth.gen_kv(w, 0, 0, 1, 2000)
+    op = O.Params(w.n_layers, w.kv_heads, w.head_dim, w.sink, w.window, w.group, 8, 8.0, O.DTYPE_BF16)
+    kp = K.params(w.n_layers, w.kv_heads, w.head_dim, w.sink, w.window, w.group, 8, 8.0, K.KVTC_BF16)
+    cap = K.KVTC_MAX_REFF // w.group
+    free = O.calibrate(x, op, 0, 0)
+    assert free.n_act > cap                     # the uncapped optimum needs more
+    so = O.calibrate(x, op, 0, 0, max_active=cap)
+    c = K.Codec(kp)
+    c.calibrate(0, 0, synth.storage(w, x), threads=8)
+    sl = O.parse_artifact(c.save()).slots[(0, 0)]
+    assert sl.n_act <= cap and so.n_act <= cap
+    _compare_slots(sl, so)
