@@ -61,6 +61,8 @@ def main():
     ap.add_argument("--calib-tokens", type=int, default=0, help="override (0 = workload's)")
     ap.add_argument("--distinct-requests", type=int, default=2,
                     help="distinct synthetic requests per (layer, kind); the rest are copies")
+    ap.add_argument("--pipeline-buffers", type=int, default=2,
+                    help="paged workloads: staging buffers of the two-stream layer pipeline")
     ap.add_argument("--core-only", action="store_true",
                     help="only the step and its per-kernel loops (no lossless stage or online "
                          "encode sections): for profiler runs whose per-kernel averages must "
@@ -169,7 +171,7 @@ def main():
     def encode():
         codec.encode(enc_jobs, ws, stream)
 
-    pipe = Pipeline(K, codec, w, jobs, dec_jobs, dev) if w.paged else None
+    pipe = Pipeline(K, codec, w, jobs, dec_jobs, dev, args.pipeline_buffers) if w.paged else None
 
     # kvtc_decode's full workspace (status words, sink, staging) selects the
     # two-stage schedule; the status words alone, the fused one
@@ -369,20 +371,22 @@ def main():
 
 class Pipeline:
     """Layer-by-layer decode on two streams: stage 1 (unpack, stream U) of
-    layer l+1 overlaps stage 2 (restore, stream R) of layer l; two staging
-    buffers and workspaces alternate between layers."""
+    later layers overlaps stage 2 (restore, stream R) of layer l; nbuf staging
+    buffers and workspaces rotate between layers, so stage 1 runs up to
+    nbuf - 1 layers ahead of stage 2."""
 
-    def __init__(self, K, codec, w, jobs, dec_jobs, dev):
+    def __init__(self, K, codec, w, jobs, dec_jobs, dev, nbuf=2):
         import torch
         self.K, self.codec, self.torch = K, codec, torch
         self.layers = []
         for l in range(w.n_layers):
             self.layers.append([dj for (jl, _, _), dj in zip(jobs, dec_jobs) if jl == l])
         self.nst = max(codec.staging_bytes(js) for js in self.layers)
-        self.staging = [torch.empty(self.nst, dtype=torch.uint8, device=dev) for _ in range(2)]
+        self.nbuf = max(2, min(nbuf, len(self.layers)))
+        self.staging = [torch.empty(self.nst, dtype=torch.uint8, device=dev) for _ in range(self.nbuf)]
         self.nj = max(len(js) for js in self.layers)
         self.ws = [torch.zeros(K.kvtc_workspace_bytes(self.nj) // 4, dtype=torch.int32, device=dev)
-                   for _ in range(2)]
+                   for _ in range(self.nbuf)]
         self.su, self.sr = torch.cuda.Stream(), torch.cuda.Stream()
         L = len(self.layers)
         self.ev_u = [torch.cuda.Event() for _ in range(L)]
@@ -395,9 +399,9 @@ class Pipeline:
         self.su.wait_event(start)
         self.sr.wait_event(start)
         for l, js in enumerate(self.layers):
-            b = l % 2
-            if l >= 2:
-                self.su.wait_event(self.ev_r[l - 2])        # staging buffer b is free again
+            b = l % self.nbuf
+            if l >= self.nbuf:
+                self.su.wait_event(self.ev_r[l - self.nbuf])   # staging buffer b is free again
             self.codec.decode_unpack(js, K.KVTC_BF16, self.staging[b], self.nst, self.ws[b], self.su)
             self.ev_u[l].record(self.su)
             self.sr.wait_event(self.ev_u[l])
@@ -407,7 +411,7 @@ class Pipeline:
         stream.wait_stream(self.su)
 
     def check(self):
-        for b in range(2):
+        for b in range(self.nbuf):
             st = self.K.kvtc_read_device_status(self.ws[b], self.nj, None)
             if np.any(st != 0):
                 raise SystemExit(f"pipeline status errors: {st}")
@@ -440,8 +444,9 @@ class Pipeline:
             torch.cuda.synchronize()
             times.append(p0.elapsed_time(p1))
         t_p = float(np.median(times))
-        return {"unpack_ms": round(float(t_u), 4), "restore_ms": round(float(t_r), 4),
-                "pipelined_ms": round(t_p, 4), "overlap": round(float(t_u + t_r) / t_p, 3)}
+        return {"staging_buffers": self.nbuf, "unpack_ms": round(float(t_u), 4),
+                "restore_ms": round(float(t_r), 4), "pipelined_ms": round(t_p, 4),
+                "overlap": round(float(t_u + t_r) / t_p, 3)}
 
 
 def lossless_stage(K, codec, jobs, sizes, offs, sbuf, T, F, esz, dev, stream, reps, deflate_ratio):
