@@ -32,7 +32,13 @@
  *                on bf16 MFMA with fp32 accumulation started at
  *                -(mu32 - mu_hi) V'; the rounding error scales with |x - mu|,
  *                so a code may differ by one step from the exact sum near a
- *                rounding boundary whatever the size of the mean.
+ *                rounding boundary whatever the size of the mean. A bf16 slot
+ *                whose mean is no larger than its spread (|mu32|^2 <= sum of
+ *                the calibration's covariance eigenvalues) folds the mean
+ *                instead: the stored token is one exact bf16 operand and the
+ *                accumulation starts at -mu32 V' (fp64, rounded once); its
+ *                rounding error scales with |x|, within a factor of about
+ *                sqrt(2) of |x - mu| there (kvtc_slot_info.folded_mean).
  *   dequantize   c_hat = shift + q * fp32(scale / k); dropped groups give 0;
  *                x_hat = mu32 + sum_j c_hat_j V'_j.
  *   stream       64-byte header ("KVTC", u16 version=1, u8 dtype, u8 kind,
@@ -137,6 +143,10 @@ typedef struct {
   uint8_t widths[512];     /* width per group (F/G entries); with a width
                               per component, each group's largest            */
   int32_t per_component;   /* 1: a width per component (see kvtc_calibrate_set) */
+  int32_t folded_mean;     /* 1: the encode multiplies the token as stored and
+                              subtracts mu32 V' (bf16 codecs whose |mu32|^2 is
+                              at most the sum of the covariance eigenvalues);
+                              0: it centres each token first (see projection) */
 } kvtc_slot_info;
 
 /* Largest active component count the kernels accept. */

@@ -46,7 +46,7 @@ class kvtc_job(C.Structure):
 class kvtc_slot_info(C.Structure):
     _fields_ = [("calibrated", C.c_int32), ("n_act", C.c_int32), ("r_eff", C.c_int32),
                 ("record_bytes", C.c_int32), ("slot_id", C.c_uint64),
-                ("widths", C.c_uint8 * 512), ("per_component", C.c_int32)]
+                ("widths", C.c_uint8 * 512), ("per_component", C.c_int32), ("folded_mean", C.c_int32)]
 
 
 class KvtcError(RuntimeError):

@@ -129,8 +129,9 @@ __device__ __forceinline__ void quantize_tile(const f32x16 (&acc)[NB], CSlot& sl
 // ahead of the computation moves on into the next tile of the range, so the
 // loads of a tile's first slices are in flight during the previous tile's
 // quantization, and the pipeline fills once per workgroup.
-template <int NB, int G, bool F32IN, bool ODD>
+template <int NB, int G, bool F32IN, bool ODD, bool FOLD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!F32IN && NB <= 3 ? 2 : 1))) void encode_kernel(const LaunchArgs a) {
+  static_assert(!(FOLD && F32IN), "only a bf16 token is an exact single MFMA operand");
   extern __shared__ __align__(16) uint8_t smem[];
   const uint32_t g = logical_tile();
   const int F = a.F;
@@ -187,7 +188,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!F32IN
   // three terms hold it exactly. The product's rounding error therefore
   // scales with |x - mu| (the centred token), not with |x|: a mean large
   // against the spread costs no precision.
-  constexpr int NT = enc_terms(F32IN);
+  //
+  // Folded mean (FOLD, bf16 slots whose mean is no larger than their
+  // spread): the stored bf16 token is the B fragment as it is (one term, no
+  // centring arithmetic, no mean in LDS) and the accumulators start at
+  // -mu32 V'. The error then scales with |x|, which such a mean keeps within
+  // a factor of about sqrt(2) of |x - mu|.
+  constexpr int NT = FOLD ? 1 : enc_terms(F32IN);
   constexpr int slice_elems = 32 * NB * kEncRowPad;
   constexpr int XROW = enc_xrow_bytes(F32IN);   // bytes per token tile row
   uint16_t* const vbase = (uint16_t*)smem;
@@ -271,7 +278,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!F32IN
   const float* mu_staged = nullptr;
   auto stage_first = [&](const float* mu, const u32x4 (&xr)[NI], const vregs_t& v)
       __attribute__((always_inline)) {
-    if (mu != mu_staged) {   // uniform
+    if (!FOLD && mu != mu_staged) {   // uniform
       for (int i = threadIdx.x; i < F / 4; i += kThreads) ((float4*)mu_l)[i] = ((const float4*)mu)[i];
       __syncthreads();
       mu_staged = mu;
@@ -317,39 +324,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!F32IN
     for (int s = 0; s < kEncKS / 16; ++s) {
       // B fragment: features f .. f + 8 of the slice for token lane % 32.
       const int f = 16 * s + 8 * h;
-      const float4 m0 = *(const float4*)(mu_l + it * kEncKS + f);
-      const float4 m1 = *(const float4*)(mu_l + it * kEncKS + f + 4);
-      const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-      float d[8];
-      if (F32IN) {
-        const u32x4 x0 = *(const u32x4*)(xrow + 4 * f);
-        const u32x4 x1 = *(const u32x4*)(xrow + 4 * f + 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          d[e] = __uint_as_float(x0[e]) - mv[e];
-          d[e + 4] = __uint_as_float(x1[e]) - mv[e + 4];
-        }
-      } else {   // two bf16 per dword, low half first
-        const u32x4 x0 = *(const u32x4*)(xrow + 2 * f);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          d[2 * e] = __uint_as_float(x0[e] << 16) - mv[2 * e];
-          d[2 * e + 1] = __uint_as_float(x0[e] & 0xFFFF0000u) - mv[2 * e + 1];
-        }
-      }
       bf16x8 bx[NT];
+      if constexpr (FOLD) {
+        bx[0] = __builtin_bit_cast(bf16x8, *(const u32x4*)(xrow + 2 * f));
+      } else {
+        const float4 m0 = *(const float4*)(mu_l + it * kEncKS + f);
+        const float4 m1 = *(const float4*)(mu_l + it * kEncKS + f + 4);
+        const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        float d[8];
+        if (F32IN) {
+          const u32x4 x0 = *(const u32x4*)(xrow + 4 * f);
+          const u32x4 x1 = *(const u32x4*)(xrow + 4 * f + 16);
 #pragma unroll
-      for (int p = 0; p < NT; ++p) {
-        uint32_t t[4];
+          for (int e = 0; e < 4; ++e) {
+            d[e] = __uint_as_float(x0[e]) - mv[e];
+            d[e + 4] = __uint_as_float(x1[e]) - mv[e + 4];
+          }
+        } else {   // two bf16 per dword, low half first
+          const u32x4 x0 = *(const u32x4*)(xrow + 2 * f);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          t[e] = pack_bf16x2(d[2 * e], d[2 * e + 1]);
-          if (p + 1 < NT) {   // the remainder is exact in fp32
-            d[2 * e] -= bf16_to_f32(t[e] & 0xFFFFu);
-            d[2 * e + 1] -= bf16_to_f32(t[e] >> 16);
+          for (int e = 0; e < 4; ++e) {
+            d[2 * e] = __uint_as_float(x0[e] << 16) - mv[2 * e];
+            d[2 * e + 1] = __uint_as_float(x0[e] & 0xFFFF0000u) - mv[2 * e + 1];
           }
         }
-        bx[p] = __builtin_bit_cast(bf16x8, (u32x4){t[0], t[1], t[2], t[3]});
+#pragma unroll
+        for (int p = 0; p < NT; ++p) {
+          uint32_t t[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            t[e] = pack_bf16x2(d[2 * e], d[2 * e + 1]);
+            if (p + 1 < NT) {   // the remainder is exact in fp32
+              d[2 * e] -= bf16_to_f32(t[e] & 0xFFFFu);
+              d[2 * e + 1] -= bf16_to_f32(t[e] >> 16);
+            }
+          }
+          bx[p] = __builtin_bit_cast(bf16x8, (u32x4){t[0], t[1], t[2], t[3]});
+        }
       }
       bf16x8 av[NB];
 #pragma unroll
@@ -513,19 +524,19 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const LaunchArgs a, cons
 // 143 at two, 150 at three).
 constexpr int kEncMaxPerCU = 2;
 
-template <int G, bool F32IN, bool ODD>
+template <int G, bool F32IN, bool ODD, bool FOLD>
 static int launch_encode_g(const LaunchArgs& a, int nb, size_t lds, hipStream_t s) {
   // Persistent: the resident workgroups (at most kEncMaxPerCU per CU), or
   // fewer when there are fewer compressed blocks (any grid covers the
   // headers and passthrough units).
 #define KVTC_ENC(NBV)                                                                      \
   case NBV: {                                                                              \
-    allow_lds(encode_kernel<NBV, G, F32IN, ODD>, lds);                                     \
+    allow_lds(encode_kernel<NBV, G, F32IN, ODD, FOLD>, lds);                                     \
     const dim3 g(std::min({grid_for(std::max(1u, (a.total_cblks + kEncWaves - 1) / kEncWaves)).x, \
-                           resident_grid(encode_kernel<NBV, G, F32IN, ODD>, kThreads, lds,  \
+                           resident_grid(encode_kernel<NBV, G, F32IN, ODD, FOLD>, kThreads, lds,  \
                                          kEncMaxPerCU),                                    \
                            persistent_grid_cap()}));                                           \
-    hipLaunchKernelGGL((encode_kernel<NBV, G, F32IN, ODD>), g, dim3(kThreads), lds, s, a); \
+    hipLaunchKernelGGL((encode_kernel<NBV, G, F32IN, ODD, FOLD>), g, dim3(kThreads), lds, s, a); \
     break;                                                                                 \
   }
   switch (nb) {
@@ -540,12 +551,15 @@ static int launch_encode_g(const LaunchArgs& a, int nb, size_t lds, hipStream_t 
 int launch_encode(const LaunchArgs& a, int nb, int G, size_t lds, hipStream_t s) {
   const bool f32 = a.dtype == KVTC_F32;
   const bool odd = (a.F / kEncKS) & 1;
+  if (f32 && a.fold) return (int)hipErrorInvalidValue;
 #define KVTC_ENC_G(GV)                                                                   \
   if (G == GV)                                                                           \
-    return f32 ? (odd ? launch_encode_g<GV, true, true>(a, nb, lds, s)                   \
-                      : launch_encode_g<GV, true, false>(a, nb, lds, s))                 \
-               : (odd ? launch_encode_g<GV, false, true>(a, nb, lds, s)                  \
-                      : launch_encode_g<GV, false, false>(a, nb, lds, s));
+    return f32 ? (odd ? launch_encode_g<GV, true, true, false>(a, nb, lds, s)            \
+                      : launch_encode_g<GV, true, false, false>(a, nb, lds, s))          \
+               : a.fold ? (odd ? launch_encode_g<GV, false, true, true>(a, nb, lds, s)   \
+                               : launch_encode_g<GV, false, false, true>(a, nb, lds, s)) \
+                        : (odd ? launch_encode_g<GV, false, true, false>(a, nb, lds, s)  \
+                               : launch_encode_g<GV, false, false, false>(a, nb, lds, s));
   KVTC_ENC_G(16)
   KVTC_ENC_G(32)
 #undef KVTC_ENC_G

@@ -590,6 +590,21 @@ size_t stream_bytes(const kvtc_codec* c, const Slot& s, long T) {
   return kHeaderBytes + (size_t)(s1 + w1) * c->F * elem_bytes(c->p.dtype) + (size_t)tc * s.record_bytes;
 }
 
+// Whether the encode folds the mean into the product for this slot (bf16
+// input only): c = V'^T x - V'^T mu32 with the token multiplied as stored
+// (an exact bf16 operand, one MFMA term), instead of centring each token
+// first (two terms). The fp32 rounding error of the folded product scales
+// with |x| rather than |x - mu|; when the calibration's mean is no larger
+// than its spread (|mu32|^2 <= sum of the covariance eigenvalues = E|x - mu|^2)
+// |x| is within a factor of about sqrt(2) of |x - mu|, and so is the error.
+bool folds_mean(const kvtc_codec* c, const Slot& s) {
+  if (c->p.dtype != KVTC_BF16 || !s.calibrated || s.r_eff == 0) return false;
+  double m2 = 0.0, tr = 0.0;
+  for (float v : s.mu32) m2 += (double)v * v;
+  for (double v : s.lam) tr += v;
+  return m2 <= tr;
+}
+
 // Decode staging of one job: stg_block_bytes(ks) per block of kDecTok
 // compressed tokens.
 size_t job_staging_bytes(const Slot& s, uint32_t tc) {
@@ -771,6 +786,7 @@ kvtc_status kvtc_slot_info_get(const kvtc_codec* c, int32_t layer, int32_t kind,
   info->record_bytes = s.record_bytes;
   info->slot_id = s.slot_id;
   info->per_component = s.cwidths.empty() ? 0 : 1;
+  info->folded_mean = folds_mean(c, s) ? 1 : 0;
   for (int g = 0; g < c->n_g && g < 512; ++g) info->widths[g] = s.widths[g];
   return KVTC_OK;
 }
@@ -931,6 +947,8 @@ kvtc_status kvtc_upload(kvtc_codec* c, void* d_state, size_t bytes, hipStream_t 
     d.slot_id = s.slot_id;
     const bool pc = !s.cwidths.empty();
     d.pc = pc ? 1 : 0;
+    const bool fold = folds_mean(c, s);
+    d.fold = fold ? 1 : 0;
     int a = 0, chunk = 8 * s.n_act;
     for (int g = 0; g < c->n_g; ++g) {
       if (!s.widths[g]) continue;
@@ -968,7 +986,8 @@ kvtc_status kvtc_upload(kvtc_codec* c, void* d_state, size_t bytes, hipStream_t 
     // for bf16 tokens whenever token and mean lie within a factor 2^8 of each
     // other, so the error scales with |x - mu| and not with |x|) and starts
     // its accumulators at -V'^T (mu32 - mu_hi), this small remainder's
-    // projection in fp64 rounded once.
+    // projection in fp64 rounded once. A slot that folds the mean (see
+    // folds_mean) multiplies the raw token and starts at -V'^T mu32.
     d.mhi_off = off;
     float* mhi = (float*)(h.data() + off);
     for (int f = 0; f < F; ++f) mhi[f] = bf16_to_f32(f32_to_bf16(s.mu32[f]));
@@ -978,7 +997,7 @@ kvtc_status kvtc_upload(kvtc_codec* c, void* d_state, size_t bytes, hipStream_t 
     for (int j = 0; j < r; ++j) {
       double acc = 0.0;
       for (int f = 0; f < F; ++f)
-        acc += ((double)s.mu32[f] - (double)mhi[f]) *
+        acc += ((double)s.mu32[f] - (fold ? 0.0 : (double)mhi[f])) *
                (double)bf16_to_f32(f32_to_bf16(s.V32[(size_t)f * r + j]));
       cmu[j] = (float)acc;
     }
@@ -1076,7 +1095,7 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
   const size_t out_esz = elem_bytes(out_dtype);
   // Per-job validation and the fields that do not depend on the batch.
   std::vector<JobDesc> desc(n);
-  std::vector<int> key(n), pcj(n, 0);
+  std::vector<int> key(n), pcj(n, 0);   // pcj: launch class (decode: pc slots; encode: folded mean)
   std::vector<size_t> st_off(n, 0);
   size_t st_total = 0;
   for (int i = 0; i < n; ++i) {
@@ -1113,6 +1132,7 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
       if (j.dst_capacity < stream_bytes(c, s, j.n_tokens))
         return fail(KVTC_E_CAPACITY, "job: dst_capacity below kvtc_encoded_bytes");
       key[i] = std::max<int>(1, (int)(align_up((size_t)s.r_eff, 32) / 32));
+      if (mode == Mode::Encode) pcj[i] = folds_mean(c, s) ? 1 : 0;   // one product form per launch
     } else if (mode == Mode::UnpackCodes) {
       key[i] = 0;
     } else {
@@ -1169,7 +1189,8 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
     a.status = (unsigned long long*)d_ws;
     a.sink = (uint8_t*)d_ws + sink_offset(n);
     a.epoch = next_epoch();
-    a.pc = pcj[order[p]];
+    a.pc = mode == Mode::Encode ? 0 : pcj[order[p]];
+    a.fold = mode == Mode::Encode ? pcj[order[p]] : 0;
     uint32_t tiles = 0, cblks = 0;
     size_t rb_max = 0;
     for (int b = 0; b < a.n_jobs; ++b) {

@@ -29,7 +29,8 @@ struct alignas(16) DevSlot {
   uint64_t venc_off;      // bf16 V'^T [r_enc][F]   (rows >= r_eff are zero)
   uint64_t vdec_off;      // f16  V'   F x r_dec in MFMA A-operand order (cols >= r_eff are zero)
   uint64_t mhi_off;       // f32  mu_hi[F] = bf16_rne(mu32), the encode's centring vector
-  uint64_t cmu_off;       // f32  V'^T (mu32 - mu_hi) [r_enc]  (rows >= r_eff are zero)
+  uint64_t cmu_off;       // f32  V'^T (mu32 - mu_hi) [r_enc], or V'^T mu32 when fold
+                          // (rows >= r_eff are zero)
   uint64_t pcw_off;       // with a width per component: u32 [r_eff], per active component
                           // (bit position in the record << 8) | width
   uint64_t slot_id;
@@ -42,7 +43,7 @@ struct alignas(16) DevSlot {
   int32_t G;
   int32_t F;
   int32_t pc;             // 1: a width per component (pcw_off), 0: a width per group
-  int32_t pad_;
+  int32_t fold;           // 1: the encode folds the mean into the product (cmu_off = V'^T mu32)
   uint8_t width[kMaxActGroups];        // width of active group a (its largest component's, pc)
   uint16_t chunk_off[kMaxActGroups];   // byte offset of its chunk in a record
 };
@@ -84,6 +85,7 @@ struct LaunchArgs {
   uint8_t* sink;           // kSinkBytes of workspace that absorb stores without a row
   uint32_t epoch;          // stamp of this launch (see status_word)
   int32_t pc;              // decode stage 1: every job's slot has a width per component
+  int32_t fold;            // encode: every job's slot folds the mean into the product
   uint32_t wave_lds;       // decode stage 1: LDS bytes of each wave's record rows;
                            // fused decode: LDS bytes of each record buffer
 };

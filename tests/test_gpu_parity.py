@@ -276,32 +276,36 @@ def test_edge_lengths_in_one_launch():
         _decode_check(w, op, slot, refs[i].stream, lens[i], out, K.KVTC_F32, 0, 0)
 
 
-def _injected(F, G, widths, dtype, seed, s=4, w=16, mu_scale=1.0):
+def _injected(F, G, widths, dtype, seed, s=4, w=16, mu_scale=1.0, lam=0.0):
     rng = np.random.default_rng(seed)
     widths = np.asarray(widths, np.uint8)
     r = int(np.count_nonzero(widths)) * G
     V = np.linalg.qr(rng.standard_normal((F, F)))[0][:, :r] if r else np.zeros((F, 0))
     p = O.Params(1, 1, F, s, w, G, 8, 16.0, dtype)
     sl = O.Slot(0, 0, F, G, widths, (mu_scale * rng.standard_normal(F)).astype(np.float32),
-                np.zeros(F), V.astype(np.float32))
+                np.full(F, lam), V.astype(np.float32))
     return p, sl
 
 
 # Tokens x = mu + 3 z (z ~ N(0, 1)) around a mean of mu_ratio * 3 * N(0, 1)
-# per feature, i.e. |mu| / spread = mu_ratio: the projection is of the
-# centred token, so the code mismatches must stay within the bar however
-# large the mean is.
-MEAN_RATIOS = {"mean10": 10.0, "mean100": 100.0}
+# per feature, i.e. |mu| / spread = mu_ratio. With the slot's eigenvalues at
+# the tokens' variance (9 per feature), mean09 sits just under the bound
+# below which the encode folds the mean into the product (|mu|^2 <= sum of
+# the eigenvalues); mean10 and mean100 are centred (their eigenvalues are
+# given as zero, as are those of the other injected slots). Either way the
+# code mismatches must stay within the bar.
+MEAN_RATIOS = {"mean09": 0.9, "mean10": 10.0, "mean100": 100.0}
 
 
 @pytest.mark.parametrize("variant", ["zero_bits", "reff256_g16", "reff256_g32", "odd_groups",
-                                     "mean10", "mean100"])
+                                     "mean09", "mean10", "mean100"])
 def test_injected_artifacts(variant):
     F = 1024
     if variant in MEAN_RATIOS:
         wd = np.zeros(64, np.uint8)
         wd[:6] = [8, 8, 7, 7, 6, 4]
-        p, sl = _injected(F, 16, wd, O.DTYPE_BF16, 5, mu_scale=3.0 * MEAN_RATIOS[variant])
+        p, sl = _injected(F, 16, wd, O.DTYPE_BF16, 5, mu_scale=3.0 * MEAN_RATIOS[variant],
+                          lam=9.0 if variant == "mean09" else 0.0)
     elif variant == "zero_bits":
         p, sl = _injected(F, 16, np.zeros(64), O.DTYPE_BF16, 1)
     elif variant == "reff256_g16":
@@ -318,6 +322,7 @@ def test_injected_artifacts(variant):
         p, sl = _injected(F, 16, wd, O.DTYPE_BF16, 4)
     art = O.Artifact(p, {(0, 0): sl})
     dc = DevCodec(art.serialize())
+    assert dc.codec.slot(0, 0).folded_mean == (1 if variant == "mean09" else 0)
     rng = np.random.default_rng(9)
     T = 777
     x = (rng.standard_normal((T, F)) * 3).astype(np.float32)

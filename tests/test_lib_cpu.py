@@ -389,3 +389,25 @@ def test_allocation_keeps_to_the_kernels_cap():
     sl = O.parse_artifact(c.save()).slots[(0, 0)]
     assert sl.n_act <= cap and so.n_act <= cap
     _compare_slots(sl, so)
+
+
+@pytest.mark.parametrize("name", ["llama31_8b", "offsets_bf16", "odd1_f32"])
+def test_folded_mean_follows_the_documented_bound(name):
+    """The encode folds the mean into the product exactly for bf16 slots with
+    |mu32|^2 <= sum of the covariance eigenvalues (kvtc_slot_info.folded_mean);
+    checked on oracle-calibrated slots: a Llama-shaped layer (mean about half
+    the spread: folded), one with offsets far above the spread and an f32
+    tensor (both centred)."""
+    w = synth.workload(name)
+    op, _ = _params_pair(w)
+    n = min(w.calib_tokens, 4096)
+    slots = {(0, k): O.calibrate(synth.gen_kv(w, 0, k, 1, n), op, 0, k) for k in range(len(w.kinds))}
+    c = K.Codec.load(O.Artifact(op, slots).serialize())
+    for (l, k), so in slots.items():
+        expect = (op.dtype == O.DTYPE_BF16 and so.r_eff > 0
+                  and float(np.sum(so.mu32.astype(np.float64) ** 2)) <= float(np.sum(so.lam)))
+        assert c.slot(l, k).folded_mean == int(expect)
+        if name == "llama31_8b":
+            assert expect
+        else:
+            assert not expect
