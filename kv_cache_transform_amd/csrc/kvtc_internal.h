@@ -242,8 +242,8 @@ __host__ __device__ inline LzField lz_field(const LzShape& s, int f) {
 }
 // encode: symbols, histograms, models (f | c << 16, then 1/f in fp64),
 // per-chunk emitted-word counts, kLzLanes final states and payload offsets,
-// and the scratch words; decode: symbols, then per field the slot table of
-// kLzM words (symbol | (f - 1) << 8 | (slot - c) << 20).
+// and the scratch words; decode: symbols, then per field (kLzM words each)
+// the symbol of every slot (kLzM bytes) and per symbol (f - 1) | c << 16.
 __host__ __device__ inline LzLayout lz_layout(const LzShape& s, bool enc) {
   const int nf = lz_nf(s);
   const LzField e = lz_field(s, nf);

@@ -305,17 +305,20 @@ __global__ void __launch_bounds__(64) lz_model_kernel(const LzArgs a) {
 __device__ __forceinline__ uint64_t lanes_below(int l) { return (1ull << l) - 1ull; }
 
 // One wavefront per chunk: the steps from the last to the first, lane l
-// coding symbol 64 t + l with its own state. The chunk's symbols and the
-// field's model (f | c << 16 and the reciprocal of f, one 8-byte entry per
-// symbol) are staged in LDS first, and the next step's symbol and entry are
+// coding symbol 64 t + l with its own state. The field's model (f | c << 16
+// and the reciprocal of f, one 8-byte entry per symbol) is staged in LDS,
+// and the chunk's symbols half a chunk at a time (the upper half first), so
+// a workgroup holds 10 KiB of LDS and every chunk of a launch can be
+// resident at once. Within a half the next step's symbol and entry are
 // read one step ahead, so the loop's chain is the state arithmetic alone
 // and it issues no global load (only the stores of emitted words, which
 // nothing waits for). A step's emitted words go to the chunk's scratch in
 // reverse decoder order (the copy kernel reverses them): the k words of a
 // step take the next k positions, the lane of rank r among the emitting
 // lanes position k - 1 - r.
+constexpr uint32_t kLzHalf = kLzChunk / 2;   // symbols staged at a time
 __global__ void __launch_bounds__(kLzLanes) lz_code_kernel(const LzArgs a) {
-  __shared__ __align__(16) uint8_t syms[kLzChunk];
+  __shared__ __align__(16) uint8_t syms[kLzHalf];
   __shared__ uint64_t mdl[256];
   const uint32_t g = blockIdx.x;
   const int l = threadIdx.x;
@@ -333,37 +336,43 @@ __global__ void __launch_bounds__(kLzLanes) lz_code_kernel(const LzArgs a) {
   }
   const LzLayout L = lz_layout(s, true);
   const uint32_t len = min((uint32_t)kLzChunk, lz_n(s, f) - k * kLzChunk);
-  const int steps = (int)((len + kLzLanes - 1) / kLzLanes);
   // (the field's symbol region is padded: whole 16-byte reads stay inside)
   const u32x4* src = (const u32x4*)(j.ws + sym_off + (size_t)k * kLzChunk);
-  for (uint32_t i = l; i < (len + 15) / 16; i += kLzLanes) ((u32x4*)syms)[i] = src[i];
   const uint32_t* fc = (const uint32_t*)(j.ws + L.fc) + f * 256;
   const uint32_t* rcp = (const uint32_t*)(j.ws + L.aux) + f * 256;
   for (int i = l; i < 256; i += kLzLanes) mdl[i] = fc[i] | ((uint64_t)rcp[i] << 32);
-  __syncthreads();
   uint16_t* rev = (uint16_t*)(j.ws + L.scratch) + (size_t)kj * kLzChunk;
   uint32_t x = kLzL, cnt = 0;
-  int t = steps - 1;
-  bool act = (uint32_t)t * kLzLanes + l < len;
-  uint64_t m = mdl[act ? syms[(uint32_t)t * kLzLanes + l] : 0u];
-  for (; t >= 0; --t) {
-    // every step before the last is full
-    const uint64_t mn = t > 0 ? mdl[syms[(uint32_t)(t - 1) * kLzLanes + l]] : 0ull;
-    const uint32_t fs = (uint32_t)m & 0xFFFFu, cs = ((uint32_t)m >> 16) & 0xFFFFu, rf = (uint32_t)(m >> 32);
-    const bool emit = act && (uint64_t)x >= ((uint64_t)fs << 20);
-    const uint64_t mask = __ballot(emit);
-    const uint32_t ke = (uint32_t)__popcll(mask);
-    if (emit) rev[cnt + ke - 1 - (uint32_t)__popcll(mask & lanes_below(l))] = (uint16_t)x;
-    cnt += ke;
-    const uint32_t xe = emit ? x >> 16 : x;
-    uint32_t q = __umulhi(xe, rf);
-    uint32_t rm = xe - q * fs;
-    const bool up = rm >= fs;
-    q += up ? 1u : 0u;
-    rm -= up ? fs : 0u;
-    x = act ? (q << kLzMBits) + rm + cs : x;
-    m = mn;
-    act = t > 0;
+  constexpr int kHalfSteps = (int)(kLzHalf / kLzLanes);
+  const int steps = (int)((len + kLzLanes - 1) / kLzLanes);
+  for (int hf = (steps - 1) / kHalfSteps; hf >= 0; --hf) {
+    const int t0 = hf * kHalfSteps;
+    const uint32_t n16 = (min(len - (uint32_t)t0 * kLzLanes, kLzHalf) + 15) / 16;
+    __syncthreads();   // the previous half's reads are done
+    for (uint32_t i = l; i < n16; i += kLzLanes) ((u32x4*)syms)[i] = src[(uint32_t)t0 * kLzLanes / 16 + i];
+    __syncthreads();
+    int t = min(steps, t0 + kHalfSteps) - 1;
+    // only the chunk's last step can be partial
+    bool act = (uint32_t)t * kLzLanes + l < len;
+    uint64_t m = mdl[act ? syms[(uint32_t)(t - t0) * kLzLanes + l] : 0u];
+    for (; t >= t0; --t) {
+      const uint64_t mn = t > t0 ? mdl[syms[(uint32_t)(t - 1 - t0) * kLzLanes + l]] : 0ull;
+      const uint32_t fs = (uint32_t)m & 0xFFFFu, cs = ((uint32_t)m >> 16) & 0xFFFFu, rf = (uint32_t)(m >> 32);
+      const bool emit = act && (uint64_t)x >= ((uint64_t)fs << 20);
+      const uint64_t mask = __ballot(emit);
+      const uint32_t ke = (uint32_t)__popcll(mask);
+      if (emit) rev[cnt + ke - 1 - (uint32_t)__popcll(mask & lanes_below(l))] = (uint16_t)x;
+      cnt += ke;
+      const uint32_t xe = emit ? x >> 16 : x;
+      uint32_t q = __umulhi(xe, rf);
+      uint32_t rm = xe - q * fs;
+      const bool up = rm >= fs;
+      q += up ? 1u : 0u;
+      rm -= up ? fs : 0u;
+      x = act ? (q << kLzMBits) + rm + cs : x;
+      m = mn;
+      act = true;
+    }
   }
   ((uint32_t*)(j.ws + L.state))[(size_t)kj * kLzLanes + l] = x;
   if (l == 0) ((uint32_t*)(j.ws + L.cnt))[kj] = cnt;
@@ -494,66 +503,85 @@ __global__ void __launch_bounds__(kLzThreads) lz_check_kernel(const LzArgs a) {
   if (tid == 0 && bad != KVTC_OK) lz_set(a, j, -bad);
 }
 
-// One wave per field: the model from the container's table (it must sum to
-// M) as the slot table: per slot, its symbol s | (f_s - 1) << 8 |
-// (slot - c_s) << 20. Lane l fills slots [64 l, 64 l + 64) in LDS (one
-// search for its first slot, then a walk), then the table is copied out.
-__global__ void __launch_bounds__(64) lz_dmodel_kernel(const LzArgs a) {
+// One workgroup per field: the model from the container's table (it must
+// sum to M) as the decoder's two tables: per slot its symbol (one byte, kLzM
+// bytes), then per symbol (f_s - 1) | c_s << 16 (256 words). Wave 0 forms
+// the cumulative counts; then thread i fills slots [16 i, 16 i + 16) in LDS
+// (one search for its first slot, then a walk), and the tables are copied
+// out.
+constexpr int kLzSlotsPer = (int)kLzM / kLzThreads;
+__global__ void __launch_bounds__(kLzThreads) lz_dmodel_kernel(const LzArgs a) {
   __shared__ uint32_t cum[257];
   __shared__ uint32_t frq[256];
-  __shared__ __align__(16) uint32_t tb[kLzM];
+  __shared__ uint32_t total;
+  __shared__ __align__(16) uint8_t tb[kLzM];
   const int ji = lz_job_at<&LzJob::field0>(a, blockIdx.x);
   const LzJob& j = a.jobs[ji];
   if (lz_failed(a, j)) return;
   const LzShape s = lz_shape(a, j);
-  const int f = blockIdx.x - j.field0, lane = threadIdx.x;
+  const int f = blockIdx.x - j.field0, tid = threadIdx.x;
   if (lz_n(s, f) == 0) return;
   const int A = lz_alpha(s, f);
   const LzField fd = lz_field(s, f);
   const LzLayout L = lz_layout(s, false);
-  const uint16_t* fr = (const uint16_t*)(j.src + fd.tab_off + 8);
-  uint32_t run = 0;
-  for (int q = 0; q < 4; ++q) {
-    const int sy = lane + 64 * q;
-    const uint32_t fv = sy < A ? fr[sy] : 0u;
-    const uint32_t inc = wave_scan(fv, lane);
-    cum[sy] = sy < A ? run + inc - fv : 0xFFFFFFFFu;
-    frq[sy] = fv;
-    run += (uint32_t)__shfl((int)inc, 63, 64);
-  }
-  if (lane == 0) cum[256] = 0xFFFFFFFFu;
-  if (run != kLzM) {
-    if (lane == 0) lz_set(a, j, KVTC_E_CORRUPT);
-    return;
+  if (tid < 64) {
+    const int lane = tid;
+    const uint16_t* fr = (const uint16_t*)(j.src + fd.tab_off + 8);
+    uint32_t run = 0;
+    for (int q = 0; q < 4; ++q) {
+      const int sy = lane + 64 * q;
+      const uint32_t fv = sy < A ? fr[sy] : 0u;
+      const uint32_t inc = wave_scan(fv, lane);
+      cum[sy] = sy < A ? run + inc - fv : 0xFFFFFFFFu;
+      frq[sy] = fv;
+      run += (uint32_t)__shfl((int)inc, 63, 64);
+    }
+    if (lane == 0) {
+      cum[256] = 0xFFFFFFFFu;
+      total = run;
+    }
   }
   __syncthreads();
-  const uint32_t s0 = (uint32_t)lane * 64;
+  if (total != kLzM) {   // uniform
+    if (tid == 0) lz_set(a, j, KVTC_E_CORRUPT);
+    return;
+  }
+  const uint32_t s0 = (uint32_t)tid * kLzSlotsPer;
   int lo = 0, hi = A - 1;            // the last symbol whose range starts at or before s0
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (cum[mid] <= s0) lo = mid;
     else hi = mid - 1;
   }
-  for (uint32_t slot = s0; slot < s0 + 64; ++slot) {
-    while (cum[lo + 1] <= slot) ++lo;  // symbols without slots share the next one's start
-    tb[slot] = (uint32_t)lo | ((frq[lo] - 1u) << 8) | ((slot - cum[lo]) << 20);
+  uint32_t w[kLzSlotsPer / 4] = {};
+#pragma unroll
+  for (int i = 0; i < kLzSlotsPer; ++i) {
+    while (cum[lo + 1] <= s0 + (uint32_t)i) ++lo;  // symbols without slots share the next one's start
+    w[i / 4] |= (uint32_t)lo << (8 * (i % 4));
   }
+  static_assert(kLzSlotsPer == 16, "one 16-byte store of slot symbols per thread");
+  ((u32x4*)tb)[tid] = (u32x4){w[0], w[1], w[2], w[3]};
   __syncthreads();
-  u32x4* out = (u32x4*)(j.ws + L.aux + (size_t)f * kLzM * 4);
-  for (int i = lane; i < (int)kLzM / 4; i += 64) out[i] = ((const u32x4*)tb)[i];
+  uint8_t* out = j.ws + L.aux + (size_t)f * kLzM * 4;
+  for (int i = tid; i < (int)kLzM / 16; i += kLzThreads) ((u32x4*)out)[i] = ((const u32x4*)tb)[i];
+  // symbols without slots (past the alphabet, or of count 0) get 0: no
+  // slot names them
+  ((uint32_t*)(out + kLzM))[tid] = tid < A && frq[tid] ? (frq[tid] - 1u) | (cum[tid] << 16) : 0u;
 }
 
 // One wavefront per chunk, lane l decoding symbols 64 t + l with its own
-// state: per step a slot-table lookup and the state update, then the lanes
+// state: per step the slot's symbol, its (f, c) and the state update, then the lanes
 // whose state fell below L take the next words in lane order (ballot and
-// prefix count). Everything the loop reads is in LDS: the slot table, and
+// prefix count). Everything the loop reads is in LDS: the two tables (5 KiB,
+// so a workgroup holds 9 KiB and every chunk of a launch can be resident), and
 // the payload in a ring of two 1 KiB blocks; the block after those is
 // already loaded into registers and enters the ring when the ring's older
 // block is used up, so each global load has about ten steps to arrive.
 // Symbols are staged in LDS and stored 16 steps (1 KiB) at a time.
 constexpr uint32_t kLzBlk = 1024;            // payload bytes per ring block (64 lanes x 16)
 __global__ void __launch_bounds__(kLzLanes) lz_decode_kernel(const LzArgs a) {
-  __shared__ __align__(16) uint32_t tbl[kLzM];
+  __shared__ __align__(16) uint8_t tsym[kLzM];
+  __shared__ __align__(16) uint32_t tfc[256];
   __shared__ __align__(16) uint8_t syms[16 * kLzLanes];
   __shared__ __align__(16) uint8_t ring[2 * kLzBlk];
   const uint32_t g = blockIdx.x;
@@ -573,7 +601,11 @@ __global__ void __launch_bounds__(kLzLanes) lz_decode_kernel(const LzArgs a) {
   }
   const LzLayout L = lz_layout(s, false);
   const u32x4* gt = (const u32x4*)(j.ws + L.aux + (size_t)f * kLzM * 4);
-  for (int i = l; i < (int)kLzM / 4; i += kLzLanes) ((u32x4*)tbl)[i] = gt[i];
+  for (int i = l; i < (int)(kLzM + 1024) / 16; i += kLzLanes) {
+    const u32x4 v = gt[i];
+    if (i < (int)kLzM / 16) ((u32x4*)tsym)[i] = v;
+    else ((u32x4*)tfc)[i - kLzM / 16] = v;
+  }
   const uint32_t len = min((uint32_t)kLzChunk, lz_n(s, f) - k * kLzChunk);
   const int steps = (int)((len + kLzLanes - 1) / kLzLanes);
   const uint32_t* dir = (const uint32_t*)(j.src + L.dir_off);
@@ -601,9 +633,11 @@ __global__ void __launch_bounds__(kLzLanes) lz_decode_kernel(const LzArgs a) {
   for (int t = 0; t < steps; ++t) {
     const uint32_t i = (uint32_t)t * kLzLanes + l;
     const bool act = i < len;
-    const uint32_t e = tbl[x & (kLzM - 1)];
-    if (act) x = (((e >> 8) & 0xFFFu) + 1u) * (x >> kLzMBits) + (e >> 20);
-    syms[(t & 15) * kLzLanes + l] = (uint8_t)e;
+    const uint32_t slot = x & (kLzM - 1);
+    const uint32_t sy = tsym[slot];
+    const uint32_t e = tfc[sy];
+    if (act) x = ((e & 0xFFFFu) + 1u) * (x >> kLzMBits) + slot - (e >> 16);
+    syms[(t & 15) * kLzLanes + l] = (uint8_t)sy;
     if ((t & 15) == 15 || t == steps - 1) {   // 16 steps staged: 1 KiB out, 16 bytes a lane
       const uint32_t q = (uint32_t)(t & ~15) * kLzLanes / 16 + l;
       if (q * 16 < len) out[q] = ((const u32x4*)syms)[l];
@@ -752,7 +786,7 @@ int launch_lz_encode(const LzArgs& a, hipStream_t s) {
 
 int launch_lz_decode(const LzArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(lz_check_kernel, dim3(a.n_jobs), dim3(kLzThreads), 0, s, a);
-  if (a.fields) hipLaunchKernelGGL(lz_dmodel_kernel, dim3(a.fields), dim3(64), 0, s, a);
+  if (a.fields) hipLaunchKernelGGL(lz_dmodel_kernel, dim3(a.fields), dim3(kLzThreads), 0, s, a);
   if (a.chunks) hipLaunchKernelGGL(lz_decode_kernel, dim3(a.chunks), dim3(kLzLanes), 0, s, a);
   if (a.units) hipLaunchKernelGGL(lz_merge_kernel, dim3(a.units), dim3(kLzThreads), a.rec_lds, s, a);
   return (int)hipGetLastError();

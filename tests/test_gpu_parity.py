@@ -409,6 +409,35 @@ def test_mixed_record_sizes_in_one_launch():
             _decode_check(None, p, slots[(0, kind)], ref.stream, T, out, K.KVTC_F32, 0, kind)
 
 
+def test_folded_and_centred_slots_in_one_call():
+    """One kvtc_encode call over jobs of a slot that folds the mean (mean just
+    under its spread) and of one that centres it (mean ten spreads), in
+    alternation: the host puts each product form in launches of its own,
+    and every stream must match the oracle's header, passthrough rows and
+    codes."""
+    F = 1024
+    wd = np.zeros(64, np.uint8)
+    wd[:6] = [8, 8, 7, 7, 6, 4]
+    p, sf = _injected(F, 16, wd, O.DTYPE_BF16, 5, mu_scale=3.0 * 0.9, lam=9.0)
+    _, s0 = _injected(F, 16, wd, O.DTYPE_BF16, 6, mu_scale=3.0 * 10.0)
+    sc = O.Slot(0, 1, F, 16, s0.widths, s0.mu32, s0.lam, s0.V32)
+    dc = DevCodec(O.Artifact(p, {(0, 0): sf, (0, 1): sc}).serialize())
+    assert dc.codec.slot(0, 0).folded_mean == 1 and dc.codec.slot(0, 1).folded_mean == 0
+    rng = np.random.default_rng(13)
+    items, refs = [], []
+    for kind, sl, T in ((0, sf, 777), (1, sc, 1300), (0, sf, 64), (1, sc, 2049), (0, sf, 3000)):
+        x = (rng.standard_normal((T, F)) * 3 + sl.mu32).astype(np.float32)
+        store = O.f32_to_bf16_bits(x)
+        refs.append((O.encode(store, p, sl, 0, kind), sl, T))
+        items.append((0, kind, storage_to_dev(store)))
+    for sb, (ref, sl, T) in zip(dc.encode(items), refs):
+        s1, w1, _ = O.split_rows(T, p.sink, p.window)
+        rec0 = 64 + (s1 + w1) * F * 2
+        assert sb[:rec0] == ref.stream[:rec0]
+        nbad, ntot, mx, _, _ = code_stats(sb, ref, p, sl, T)
+        assert mx <= 1 and nbad <= max(2, ntot * CODE_RATE), (T, nbad, ntot)
+
+
 @pytest.mark.parametrize("dtype", [O.DTYPE_BF16, O.DTYPE_F32])
 @pytest.mark.parametrize("case", list(IDENTITY_CASES))
 def test_identity_basis_is_exact(case, dtype):
