@@ -36,6 +36,7 @@ struct Slot {
   std::vector<double> lam;       // [F]
   std::vector<float> V32;        // [F][r_eff]
   int n_act = 0, r_eff = 0, record_bytes = 0;
+  bool fold = false;             // the encode folds the mean into the product (see folds_mean)
   uint64_t slot_id = 0;
   std::vector<uint8_t> bytes;    // serialized slot (including the id)
 };
@@ -192,6 +193,19 @@ void finish_slot(const kvtc_params& p, int layer, int kind, Slot& s) {
     }
   s.r_eff = s.n_act * G;
   s.record_bytes = 8 * s.n_act + code_bytes;
+  // Whether the encode folds the mean into the product (bf16 input only):
+  // c = V'^T x - V'^T mu32 with the token multiplied as stored (an exact bf16
+  // operand, one MFMA term), instead of centring each token first (two
+  // terms). The fp32 rounding error of the folded product scales with |x|
+  // rather than |x - mu|; when the calibration's mean is no larger than its
+  // spread (|mu32|^2 <= sum of the covariance eigenvalues = E|x - mu|^2) |x|
+  // is within a factor of about sqrt(2) of |x - mu|, and so is the error.
+  {
+    double m2 = 0.0, tr = 0.0;
+    for (float v : s.mu32) m2 += (double)v * v;
+    for (double v : s.lam) tr += v;
+    s.fold = p.dtype == KVTC_BF16 && s.r_eff > 0 && m2 <= tr;
+  }
   std::vector<uint8_t> b;
   b.insert(b.end(), {'K', 'V', 'T', 'S'});
   const int32_t hdr[7] = {layer, kind, F, G, s.n_act, s.r_eff, pc ? 1 : 0};
@@ -590,20 +604,9 @@ size_t stream_bytes(const kvtc_codec* c, const Slot& s, long T) {
   return kHeaderBytes + (size_t)(s1 + w1) * c->F * elem_bytes(c->p.dtype) + (size_t)tc * s.record_bytes;
 }
 
-// Whether the encode folds the mean into the product for this slot (bf16
-// input only): c = V'^T x - V'^T mu32 with the token multiplied as stored
-// (an exact bf16 operand, one MFMA term), instead of centring each token
-// first (two terms). The fp32 rounding error of the folded product scales
-// with |x| rather than |x - mu|; when the calibration's mean is no larger
-// than its spread (|mu32|^2 <= sum of the covariance eigenvalues = E|x - mu|^2)
-// |x| is within a factor of about sqrt(2) of |x - mu|, and so is the error.
-bool folds_mean(const kvtc_codec* c, const Slot& s) {
-  if (c->p.dtype != KVTC_BF16 || !s.calibrated || s.r_eff == 0) return false;
-  double m2 = 0.0, tr = 0.0;
-  for (float v : s.mu32) m2 += (double)v * v;
-  for (double v : s.lam) tr += v;
-  return m2 <= tr;
-}
+// Whether the encode folds the mean into the product for this slot (decided
+// when the slot is finished, see finish_slot).
+bool folds_mean(const kvtc_codec*, const Slot& s) { return s.calibrated && s.fold; }
 
 // Decode staging of one job: stg_block_bytes(ks) per block of kDecTok
 // compressed tokens.
