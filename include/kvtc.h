@@ -225,8 +225,8 @@ typedef struct {
  *     first). Such slots serialize with mode 1 (see kvtc_save) and decode
  *     only through the two-stage schedule (kvtc_decode with its full
  *     workspace, or kvtc_decode_unpack + kvtc_decode_restore): the fused
- *     schedule, kvtc_decode_noalloc, the pack/unpack hooks and the lossless
- *     stage return KVTC_E_UNSUPPORTED for them.
+ *     schedule, kvtc_decode_noalloc and the pack/unpack hooks return
+ *     KVTC_E_UNSUPPORTED for them (the lossless stage takes them).
  * With no flag each tensor gets exactly kvtc_calibrate's result. A (layer,
  * kind) may appear at most once; the call is all or nothing (on error no slot
  * changes). Errors: KVTC_E_INVALID (bad arguments, unknown flags, too few
@@ -368,7 +368,10 @@ kvtc_status kvtc_deflate(const void* in, size_t n, void* out, size_t cap, size_t
  *   S_j, R_j (j < 4): byte j of every record's fp32 shifts, then scales,
  *       token-major then group, alphabet 256;
  *   Q_a (a < n_act): the codes of active group a, token-major then
- *       component, alphabet 2^b_a.
+ *       component, alphabet 2^b_a. With a width per component each code is
+ *       read from its own b_j bits (a width-0 component gives 0) and b_a is
+ *       the group's largest width; the decode packs each back into its own
+ *       bits, the chunk's padding bits zero.
  * Each field has a static model: its histogram h over its alphabet, N = sum
  * h, n_p present symbols, M = 4096, f_s = 0 if h_s = 0 else
  * 1 + floor(h_s * (M - n_p) / N), the remainder M - sum f added to the most

@@ -1315,7 +1315,6 @@ kvtc_status lz_plan(kvtc_codec* c, bool enc, const kvtc_job* jobs, int n, void* 
     if (!slot_index(c, j.layer, j.kind, &idx)) return fail(KVTC_E_INVALID, "job: bad layer or kind");
     const Slot& s = c->slots[idx];
     if (!s.calibrated) return fail(KVTC_E_NOT_CALIBRATED, "job: (layer, kind) is not calibrated");
-    if (!s.cwidths.empty()) return fail(KVTC_E_UNSUPPORTED, "the lossless stage takes group widths");
     if (j.n_tokens < 0 || j.n_tokens > (int64_t)INT32_MAX) return fail(KVTC_E_INVALID, "job: bad n_tokens");
     LzJob& d = desc[i];
     std::memset(&d, 0, sizeof(d));

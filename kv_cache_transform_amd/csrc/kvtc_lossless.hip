@@ -176,6 +176,9 @@ __global__ void __launch_bounds__(kLzThreads) lz_split_kernel(const LzArgs a) {
       *(uint32_t*)(out + i) = v;
     }
   }
+  // With a width per component, code j of active group g sits at the record
+  // bit and width of the slot's table entry g * G + j ((bit << 8) | width).
+  const uint32_t* pcw = sl->pc ? (const uint32_t*)(a.state + sl->pcw_off) : nullptr;
   for (int g = 0; g < na; ++g) {
     const int b = s.width[g], co = sl->chunk_off[g];
     const uint32_t mask = (1u << b) - 1u;
@@ -184,9 +187,16 @@ __global__ void __launch_bounds__(kLzThreads) lz_split_kernel(const LzArgs a) {
       const int t = i / G, c = i - t * G;      // G is a multiple of 8: one record
       uint32_t v = 0;
       for (int q = 0; q < 4; ++q) {
-        const int bit = (c + q) * b, p = t * rb + co + (bit >> 3);
+        int bit = 8 * co + (c + q) * b;
+        uint32_t m = mask;
+        if (pcw) {
+          const uint32_t e = pcw[g * G + c + q];
+          bit = (int)(e >> 8);
+          m = (1u << (e & 0xFFu)) - 1u;
+        }
+        const int p = t * rb + (bit >> 3);
         const uint32_t w = ((uint32_t)lds[p] | ((uint32_t)lds[p + 1] << 8)) >> (bit & 7);
-        v |= (w & mask) << (8 * q);
+        v |= (w & m) << (8 * q);
       }
       *(uint32_t*)(out + i) = v;
     }
@@ -671,6 +681,7 @@ __global__ void __launch_bounds__(kLzLanes) lz_decode_kernel(const LzArgs a) {
 __global__ void __launch_bounds__(kLzThreads) lz_merge_kernel(const LzArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ uint32_t omap[kLzMaxRec];
+  __shared__ uint32_t pcw_l[KVTC_MAX_REFF];
   const int ji = lz_job_at<&LzJob::unit0>(a, blockIdx.x);
   const LzJob& j = a.jobs[ji];
   if (lz_failed(a, j)) return;
@@ -729,12 +740,35 @@ __global__ void __launch_bounds__(kLzThreads) lz_merge_kernel(const LzArgs a) {
     const uint32_t* in = (const uint32_t*)(sym + lz_code_off(s, g) + (size_t)r0 * G);
     for (int i = tid; i < nr * G / 4; i += kLzThreads) ((uint32_t*)(lds + 8 * pl_b + g * cd_b))[i] = in[i];
   }
+  // With a width per component, the slot's table ((record bit << 8) | width
+  // per component of each active group) in LDS, and per record byte of a
+  // chunk the range [c0, c1] of the group's components that have bits in it
+  // (c0 > c1: padding only).
+  const bool pc = sl->pc != 0;
+  if (pc) {
+    const uint32_t* pcw = (const uint32_t*)(a.state + sl->pcw_off);
+    for (int i = tid; i < na * G; i += kLzThreads) pcw_l[i] = pcw[i];
+    __syncthreads();
+  }
   for (int o = tid; o < rb; o += kLzThreads) {
     uint32_t m = 0;
     if (o >= 8 * na) {
       int g = 0;
       while (g + 1 < na && sl->chunk_off[g + 1] <= o) ++g;
-      m = (uint32_t)g | ((uint32_t)s.width[g] << 8) | ((uint32_t)(o - sl->chunk_off[g]) << 16);
+      if (pc) {
+        int c0 = G, c1 = -1;
+        for (int c = 0; c < G; ++c) {
+          const uint32_t e = pcw_l[g * G + c];
+          const int lo = (int)(e >> 8), hi = lo + (int)(e & 0xFFu);
+          if (hi > lo && lo < 8 * o + 8 && hi > 8 * o) {
+            c0 = min(c0, c);
+            c1 = c;
+          }
+        }
+        m = (uint32_t)g | ((uint32_t)c0 << 8) | ((uint32_t)(c1 & 0xFF) << 16);
+      } else {
+        m = (uint32_t)g | ((uint32_t)s.width[g] << 8) | ((uint32_t)(o - sl->chunk_off[g]) << 16);
+      }
     }
     omap[o] = m;
   }
@@ -755,13 +789,24 @@ __global__ void __launch_bounds__(kLzThreads) lz_merge_kernel(const LzArgs a) {
         byte = lds[(o & 7) * pl_b + t * na + (o >> 3)];
       } else {
         const uint32_t m = omap[o];
-        const int g = (int)(m & 0xFFu), b = (int)((m >> 8) & 0xFFu), lo = 8 * (int)(m >> 16);
+        const int g = (int)(m & 0xFFu);
         const uint8_t* cq = lds + 8 * pl_b + g * cd_b + t * G;
         byte = 0;
-        for (int c = lo / b, c1 = min(G - 1, (lo + 7) / b); c <= c1; ++c) {
-          const int sh = c * b - lo;
-          const uint32_t qv = cq[c];
-          byte |= sh >= 0 ? qv << sh : qv >> -sh;
+        if (pc) {
+          const int c1 = (int)((m >> 16) & 0xFFu);
+          for (int c = (int)((m >> 8) & 0xFFu); c <= c1 && c < G; ++c) {
+            const uint32_t e = pcw_l[g * G + c];
+            const int sh = (int)(e >> 8) - 8 * o;
+            const uint32_t qv = cq[c] & ((1u << (e & 0xFFu)) - 1u);
+            byte |= sh >= 0 ? qv << sh : qv >> -sh;
+          }
+        } else {
+          const int b = (int)((m >> 8) & 0xFFu), lo = 8 * (int)(m >> 16);
+          for (int c = lo / b, c1 = min(G - 1, (lo + 7) / b); c <= c1; ++c) {
+            const int sh = c * b - lo;
+            const uint32_t qv = cq[c];
+            byte |= sh >= 0 ? qv << sh : qv >> -sh;
+          }
         }
       }
       v |= (byte & 0xFFu) << (8 * q);

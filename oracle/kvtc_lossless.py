@@ -30,6 +30,13 @@ Fields, in order (esz = 2 for bf16, 4 for f32; n_act active groups):
                  2^b_a
 A field with no symbols has no chunks and an all-zero table.
 
+With a width per component (reading Q2c of the oracle) the fields are the
+same (READING L1c): Q_a still holds all G codes of each record's group a,
+component j's code read from its own b_j bits of the group's chunk (a
+component of width 0 gives the symbol 0), and its alphabet is 2^b_a with b_a
+the group's largest component width; the merge packs each code back into
+its own b_j bits, the chunk's padding bits zero.
+
 Model: h = the field's histogram over its alphabet, N = sum h, n_p = number
 of symbols present, M = 4096.  f_s = 0 if h_s = 0, else 1 + floor(h_s *
 (M - n_p) / N); the remainder M - sum f goes to the most frequent symbol
@@ -68,7 +75,8 @@ import struct
 
 import numpy as np
 
-from .kvtc_oracle import HEADER_BYTES, OracleError, pack_codes, split_rows, unpack_codes
+from .kvtc_oracle import (HEADER_BYTES, OracleError, chunk_bytes_pc, pack_codes, pack_codes_pc, split_rows,
+                          unpack_codes, unpack_codes_pc)
 
 MAGIC = b"KVTZ"
 VERSION = 1
@@ -83,9 +91,8 @@ CONTAINER_HEADER = 64
 # ------------------------------------------------------------------ fields ---
 
 def stream_fields(stream: bytes, params, slot, T: int):
-    """Split a KVTC stream into its fields (reading L1): [(symbols u8, A)]."""
-    if getattr(slot, "cwidths", None) is not None:
-        raise OracleError("the lossless stage takes streams with a width per group")
+    """Split a KVTC stream into its fields (readings L1, L1c): [(symbols u8, A)]."""
+    pc = getattr(slot, "cwidths", None) is not None
     s1, w1, tc = split_rows(T, params.sink, params.window)
     esz, F = params.elem_bytes, params.F
     n_pt = (s1 + w1) * F
@@ -101,8 +108,13 @@ def stream_fields(stream: bytes, params, slot, T: int):
     pos = 8 * na
     for g in slot.active_groups:
         b = int(slot.widths[g])
-        nbytes = slot.G * b // 8
-        q = unpack_codes(rec[:, pos:pos + nbytes], slot.G, b)
+        if pc:
+            bs = slot.group_cwidths(g)
+            nbytes = chunk_bytes_pc(bs)
+            q = unpack_codes_pc(rec[:, pos:pos + nbytes], bs)
+        else:
+            nbytes = slot.G * b // 8
+            q = unpack_codes(rec[:, pos:pos + nbytes], slot.G, b)
         fields.append((q.reshape(-1).copy(), 1 << b))
         pos += nbytes
     return fields
@@ -122,9 +134,13 @@ def merge_fields(header: bytes, fields, params, slot, T: int) -> bytes:
         ss[:, :, 0, j] = fields[esz + j][0].reshape(tc, na)
         ss[:, :, 1, j] = fields[esz + 4 + j][0].reshape(tc, na)
     parts = [ss.reshape(tc, 8 * na)]
+    pc = getattr(slot, "cwidths", None) is not None
     for a, g in enumerate(slot.active_groups):
-        b = int(slot.widths[g])
-        parts.append(pack_codes(fields[esz + 8 + a][0].reshape(tc, slot.G), b))
+        q = fields[esz + 8 + a][0].reshape(tc, slot.G)
+        if pc:
+            parts.append(pack_codes_pc(q, slot.group_cwidths(g)))
+        else:
+            parts.append(pack_codes(q, int(slot.widths[g])))
     rec = np.concatenate(parts, axis=1) if parts else np.zeros((tc, 0), np.uint8)
     return bytes(header) + pt.tobytes() + rec.tobytes()
 

@@ -380,6 +380,19 @@ def lossless_streams():
     out.append((p, sl, 1100, O.encode(xs, p, sl, 0, 0).stream))
     sl0 = injected_slot(np.zeros((128, 0)), [0] * 8, np.zeros(128), 16)
     out.append((p, sl0, 300, O.encode(xs[:300], p, sl0, 0, 0).stream))
+    # a width per component (reading L1c): widths 0..8 mixed inside every
+    # active group, so chunks end in padding bits and some codes are empty
+    p = small_params(F=64, G=16, bpv=3.0, dtype=O.DTYPE_BF16)
+    pc = O.calibrate_set([(0, 0, x[:2000])], p, component_widths=True)[(0, 0)]
+    cw = pc.cwidths.copy()
+    for a, g in enumerate(pc.active_groups):
+        cw[g * 16:(g + 1) * 16] = [(3 * a + 5 * i + 1) % 9 for i in range(16)]
+        cw[g * 16] = max(cw[g * 16], 1)
+    pc.cwidths = cw
+    pc.widths = cw.reshape(-1, 16).max(axis=1).astype(np.uint8)
+    xs = O.f32_to_bf16_bits(x[2000:])
+    for T in (600, 13):
+        out.append((p, pc, T, O.encode(xs[:T], p, pc, 0, 0).stream))
     return out
 
 

@@ -16,7 +16,7 @@ import oracle.kvtc_lossless as LZ
 import oracle.kvtc_oracle as O
 import pins
 import synth
-from gpu_util import DEV, DevCodec, oracle_artifact, to_dev_bytes
+from gpu_util import DEV, DevCodec, oracle_artifact, oracle_params, to_dev_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -95,6 +95,49 @@ def test_lossless_matches_oracle(case):
     print(f"{case}: raw/stream {raw / tot_s:.3f} raw/container {raw / tot_z:.3f} raw/zlib {raw / tot_d:.3f}")
 
 
+def _pc_streams(wname, slots, T, calib, mixed):
+    """Streams of slots with a width per component (the oracle's reading
+    Q2c); with mixed, every width 0..8 inside each active group."""
+    w = synth.workload(wname)
+    op = oracle_params(w)
+    ins = [(l, k, synth.gen_kv(w, l, k, synth.ROLE_CALIB, calib or w.calib_tokens)) for l, k in slots]
+    sls = O.calibrate_set(ins, op, component_widths=True)
+    if mixed:
+        for sl in sls.values():
+            cw = sl.cwidths.copy()
+            for a, g in enumerate(sl.active_groups):
+                cw[g * sl.G:(g + 1) * sl.G] = [(3 * a + 5 * i + 1) % 9 for i in range(sl.G)]
+                cw[g * sl.G] = max(cw[g * sl.G], 1)
+            sl.cwidths = cw
+            sl.widths = cw.reshape(-1, sl.G).max(axis=1).astype(np.uint8)
+    art = O.Artifact(op, sls)
+    items = []
+    for l, k in slots:
+        store = synth.storage(w, synth.gen_kv(w, l, k, synth.ROLE_EVAL, T))
+        items.append((l, k, T, O.encode(store, op, art.slots[(l, k)], l, k).stream))
+    return art, items
+
+
+PC_CASES = {
+    "llama31_8b_mixed": ("llama31_8b", [(0, 0), (0, 1)], 8192, 4096, True),
+    "nemo12b_g32_mixed": ("nemo12b", [(0, 0)], 6000, 4096, True),
+    "odd3_bf16": ("odd3_bf16", [(0, 0), (0, 1)], 1100, None, False),
+    "odd1_f32_mixed": ("odd1_f32", [(0, 0)], 2100, None, True),
+}
+
+
+@pytest.mark.parametrize("case", list(PC_CASES))
+def test_lossless_per_component_widths(case):
+    """Streams with a width per component: the container equals the oracle's
+    (reading L1c) byte for byte and decodes back to the stream."""
+    art, items = _pc_streams(*PC_CASES[case])
+    conts, (st, back) = _run(art, items)
+    assert np.all(st == 0), st
+    for (l, k, T, stb), z, b in zip(items, conts, back):
+        assert z == LZ.compress(stb, art.params, art.slots[(l, k)], T), "container differs from the oracle's"
+        assert b == stb, "decoded stream differs"
+
+
 def test_lossless_edge_shapes():
     """Lengths 0, 1, all passthrough, one compressed row and a ragged last
     chunk; every width 1..8 on one injected slot; no active group; f32 and
@@ -102,7 +145,8 @@ def test_lossless_edge_shapes():
     streams = pins.lossless_streams()
     by_art = {}
     for p, sl, T, st in streams:
-        key = (p.F, p.group, p.dtype, tuple(sl.widths.tolist()), float(np.sum(sl.V32)))
+        cw = None if sl.cwidths is None else tuple(sl.cwidths.tolist())
+        key = (p.F, p.group, p.dtype, tuple(sl.widths.tolist()), cw, float(np.sum(sl.V32)))
         by_art.setdefault(key, (p, sl, []))[2].append((T, st))
     for p, sl, lst in by_art.values():
         art = O.Artifact(p, {(0, 0): sl})

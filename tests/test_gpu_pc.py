@@ -110,8 +110,9 @@ def test_pc_decode_parity(case, out_dtype):
 
 
 def test_pc_refused_where_unsupported():
-    """The fused schedule, kvtc_decode_noalloc and the lossless stage refuse
-    slots with a width per component before any launch."""
+    """The fused schedule and kvtc_decode_noalloc refuse slots with a width
+    per component before any launch (the lossless stage takes them: see
+    test_gpu_lossless.py)."""
     w, art, op, items = _setup("odd3_bf16")
     dc = DevCodec(art.serialize())
     T = items[0][2].shape[0]
@@ -124,7 +125,4 @@ def test_pc_refused_where_unsupported():
     job = K.make_job(l, k, T, src, out, out.numel() * 2, src_capacity=len(ref.stream))
     with pytest.raises(K.KvtcError) as e:
         dc.codec.decode_noalloc([job], K.KVTC_BF16)
-    assert e.value.status == K.KVTC_E_UNSUPPORTED
-    with pytest.raises(K.KvtcError) as e:
-        dc.codec.lossless_encode([job], src, 1 << 20)
     assert e.value.status == K.KVTC_E_UNSUPPORTED

@@ -254,6 +254,17 @@ def _fields_codes_component_major(stream, params, slot, T):
     return out
 
 
+def _fields_pc_alphabet_first_width(stream, params, slot, T):
+    fs = _orig_lz["stream_fields"](stream, params, slot, T)
+    if getattr(slot, "cwidths", None) is None:
+        return fs
+    esz = params.elem_bytes
+    out = fs[:esz + 8]
+    for (q, _), g in zip(fs[esz + 8:], slot.active_groups):
+        out.append((q, 1 << int(slot.group_cwidths(g)[0])))
+    return out
+
+
 def _pack_pc_msb_first(q, bs):
     rev = q.copy()
     for j, b in enumerate(bs):
@@ -298,6 +309,7 @@ LZ_MUTATIONS = {
     "lz_rans_word_order": ("rans_encode", _rans_words_descending),
     "lz_planes_big_endian": ("stream_fields", _fields_planes_big_endian),
     "lz_codes_component_major": ("stream_fields", _fields_codes_component_major),
+    "lz_pc_alphabet_first_width": ("stream_fields", _fields_pc_alphabet_first_width),
 }
 
 
