@@ -222,11 +222,10 @@ typedef struct {
  *     b_j / 8) bits. The widths minimise the sum of the components'
  *     empirical distortions within the budget (ties: fewest bits, then the
  *     largest width sum for the earliest group, then the largest widths
- *     first). Such slots serialize with mode 1 (see kvtc_save) and decode
- *     only through the two-stage schedule (kvtc_decode with its full
- *     workspace, or kvtc_decode_unpack + kvtc_decode_restore): the fused
- *     schedule, kvtc_decode_noalloc and the pack/unpack hooks return
- *     KVTC_E_UNSUPPORTED for them (the lossless stage takes them).
+ *     first). Such slots serialize with mode 1 (see kvtc_save); every
+ *     decode schedule, kvtc_decode_noalloc and the lossless stage take them
+ *     (in launches of their own); the pack/unpack hooks return
+ *     KVTC_E_UNSUPPORTED for them.
  * With no flag each tensor gets exactly kvtc_calibrate's result. A (layer,
  * kind) may appear at most once; the call is all or nothing (on error no slot
  * changes). Errors: KVTC_E_INVALID (bad arguments, unknown flags, too few

@@ -450,8 +450,9 @@ __device__ __forceinline__ bool rest_put(const uint4& v, int row, uint8_t* dst_w
 // Stores whose LDS reads are in flight ahead of the store being issued.
 constexpr int kRestPrefetch = 8;
 
-template <int KS, int NFB, bool FUSED, bool OUT32>
+template <int KS, int NFB, bool FUSED, bool OUT32, bool PC>
 __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2))) void restore_kernel(const LaunchArgs a) {
+  static_assert(FUSED || !PC, "stage 2 reads the staging, whatever the record layout");
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int pflag;
   constexpr int FPW = 32 * NFB;                 // features per wave
@@ -580,6 +581,7 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
     struct BuildJob {
       int j, rbp, G, n_g;
       int w[NSW > 0 ? NSW : 1], chunk[NSW > 0 ? NSW : 1];
+      const uint32_t* pcw;   // PC: the slot's (record bit << 8) | width per component
     };
     auto build_job = [&](int j) __attribute__((always_inline)) {
       BuildJob bj;
@@ -589,6 +591,7 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
       bj.rbp = dec_rec_stride(sl.record_bytes);
       bj.G = sl.G;
       bj.n_g = 16 * KS / bj.G;
+      bj.pcw = PC ? (const uint32_t*)(a.state + sl.pcw_off) : nullptr;
 #pragma unroll
       for (int i = 0; i < NSW; ++i) {
         const int s = wave + kRestWaves * i;
@@ -622,12 +625,16 @@ __global__ __launch_bounds__(kRestThreads) __attribute__((amdgpu_waves_per_eu(2)
           float S, Sinv;
           token_scale(m, S, Sinv);
           const int ag = 16 * s / bj.G;
-          const int w = bj.w[i];
-          const float kf = (float)((1 << w) - 1);
           const float2 ps = get_scales(rr, ag);
-          const uint64_t bits = lds_u64(rr + bj.chunk[i] + ((16 * s + 8 * h - ag * bj.G) * w) / 8);
-          const uint4 f = tok_ok ? frag_from_bits(bits, ps.x, ps.y, w, kf, 1.0f / kf, Sinv)
-                                 : make_uint4(0u, 0u, 0u, 0u);
+          uint4 f = make_uint4(0u, 0u, 0u, 0u);
+          if constexpr (PC) {
+            if (tok_ok) f = frag_pc(rr, bj.pcw + 16 * s + 8 * h, ps.x, ps.y, Sinv);
+          } else {
+            const int w = bj.w[i];
+            const float kf = (float)((1 << w) - 1);
+            const uint64_t bits = lds_u64(rr + bj.chunk[i] + ((16 * s + 8 * h - ag * bj.G) * w) / 8);
+            if (tok_ok) f = frag_from_bits(bits, ps.x, ps.y, w, kf, 1.0f / kf, Sinv);
+          }
           *(uint4*)(fr + s * 1024 + lane * 16) = f;
           if (s == 0 && h == 0) *(float*)(fr + KS * 1024 + t * 4) = tok_ok ? S : 1.f;
         }
@@ -973,17 +980,17 @@ int launch_prep(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
 
 // Restore launch: nfb from the K-step count and F; at most 8 / kRestWaves
 // workgroups per CU (the occupancy query), fewer when there are few units.
-template <bool FU, bool O32>
+template <bool FU, bool O32, bool PC>
 static int launch_restore_t(const LaunchArgs& a, int ks, size_t lds, hipStream_t s) {
   const int nfb = rest_nfb(ks, a.F);
 #define KVTC_REST(KV, NFBV)                                                                      \
   if (ks == KV && nfb == NFBV) {                                                                 \
-    allow_lds(restore_kernel<KV, NFBV, FU, O32>, lds);                                           \
+    allow_lds(restore_kernel<KV, NFBV, FU, O32, PC>, lds);                                           \
     const dim3 g(std::min({std::max(8u, (a.total_tiles + 7u) / 8u * 8u),                         \
-                           resident_grid(restore_kernel<KV, NFBV, FU, O32>, kRestThreads, lds,  \
+                           resident_grid(restore_kernel<KV, NFBV, FU, O32, PC>, kRestThreads, lds,  \
                                          8 / kRestWaves),                                        \
                            persistent_grid_cap()}));                                             \
-    hipLaunchKernelGGL((restore_kernel<KV, NFBV, FU, O32>), g, dim3(kRestThreads), lds, s, a);  \
+    hipLaunchKernelGGL((restore_kernel<KV, NFBV, FU, O32, PC>), g, dim3(kRestThreads), lds, s, a);  \
     return (int)hipGetLastError();                                                               \
   }
 #define KVTC_REST4(KV) KVTC_REST(KV, 4)
@@ -998,8 +1005,12 @@ static int launch_restore_t(const LaunchArgs& a, int ks, size_t lds, hipStream_t
 
 int launch_restore(const LaunchArgs& a, int ks, bool fused, size_t lds, hipStream_t s) {
   const bool o32 = a.out_dtype == KVTC_F32;
-  return fused ? (o32 ? launch_restore_t<true, true>(a, ks, lds, s) : launch_restore_t<true, false>(a, ks, lds, s))
-               : (o32 ? launch_restore_t<false, true>(a, ks, lds, s) : launch_restore_t<false, false>(a, ks, lds, s));
+  if (fused && a.pc)   // the fused build reads each code at its own bit and width
+    return o32 ? launch_restore_t<true, true, true>(a, ks, lds, s) : launch_restore_t<true, false, true>(a, ks, lds, s);
+  return fused ? (o32 ? launch_restore_t<true, true, false>(a, ks, lds, s)
+                      : launch_restore_t<true, false, false>(a, ks, lds, s))
+               : (o32 ? launch_restore_t<false, true, false>(a, ks, lds, s)
+                      : launch_restore_t<false, false, false>(a, ks, lds, s));
 }
 
 int launch_unpack(const LaunchArgs& a, int G, size_t lds, void* codes, void* ss, hipStream_t s) {

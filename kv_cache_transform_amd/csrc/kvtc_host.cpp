@@ -1127,10 +1127,8 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
     d.kind = j.kind;
     d.status_idx = i;
     d.bs_shift = -1;
-    if (!s.cwidths.empty() && (mode == Mode::Decode || mode == Mode::Pack || mode == Mode::UnpackCodes))
-      return fail(KVTC_E_UNSUPPORTED,
-                  "a width per component needs the two-stage decode (kvtc_decode with its full workspace, "
-                  "or the stage calls); the pack and unpack hooks take group widths");
+    if (!s.cwidths.empty() && (mode == Mode::Pack || mode == Mode::UnpackCodes))
+      return fail(KVTC_E_UNSUPPORTED, "the pack and unpack hooks take group widths");
     if (mode == Mode::Encode || mode == Mode::Pack) {
       if (j.dst_capacity < stream_bytes(c, s, j.n_tokens))
         return fail(KVTC_E_CAPACITY, "job: dst_capacity below kvtc_encoded_bytes");
@@ -1168,7 +1166,7 @@ kvtc_status plan(kvtc_codec* c, Mode mode, const kvtc_job* jobs, int n, int out_
         d.staging = d_staging + st_off[i];
       }
       key[i] = (int)(align_up((size_t)s.r_eff, 16) / 16);
-      pcj[i] = s.cwidths.empty() ? 0 : 1;   // stage 1 takes such jobs in launches of their own
+      pcj[i] = s.cwidths.empty() ? 0 : 1;   // stage 1 and the fused decode take such jobs in launches of their own
       if (s.record_bytes > 24 * key[i]) return fail(KVTC_E_UNSUPPORTED, "record wider than the decode tiles");
     }
   }

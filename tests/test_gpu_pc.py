@@ -2,7 +2,7 @@
 C ABI), against the oracle's reading Q2c: artifacts calibrated by the oracle
 with component_widths, streams encoded by the library, codes and records
 compared with the oracle's, and the oracle's streams decoded by the
-two-stage schedule (the only one that takes such slots)."""
+two-stage and fused schedules and by kvtc_decode_noalloc."""
 import functools
 
 import numpy as np
@@ -12,7 +12,7 @@ import torch
 import kv_cache_transform_amd as K
 import oracle.kvtc_oracle as O
 import synth
-from gpu_util import DEV, DevCodec, bf16_out_to_f64, code_stats, oracle_params, storage_to_dev
+from gpu_util import DEV, DevCodec, bf16_out_to_f64, code_stats, oracle_params, storage_to_dev, to_dev_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -107,22 +107,37 @@ def test_pc_decode_parity(case, out_dtype):
     assert np.all(st2 == 0)
     for a, b in zip(outs, outs2):
         assert torch.equal(a, b)
+    # the fused schedule builds the same operands from the records in LDS
+    outs3, st3 = dc.decode(jobs, out_dtype, op.F, schedule="fused")
+    assert np.all(st3 == 0), st3
+    for a, b in zip(outs, outs3):
+        assert torch.equal(a, b)
 
 
-def test_pc_refused_where_unsupported():
-    """The fused schedule and kvtc_decode_noalloc refuse slots with a width
-    per component before any launch (the lossless stage takes them: see
-    test_gpu_lossless.py)."""
+def test_pc_noalloc_decodes_and_hooks_refuse():
+    """kvtc_decode_noalloc (the fused schedule without a workspace) decodes
+    slots with a width per component exactly as kvtc_decode does; the pack
+    test hook, which takes group widths, refuses them before any launch."""
     w, art, op, items = _setup("odd3_bf16")
     dc = DevCodec(art.serialize())
     T = items[0][2].shape[0]
+    ref_outs, st = dc.decode([(l, k, T, ref.stream) for l, k, _, ref in items], K.KVTC_BF16, op.F)
+    assert np.all(st == 0), st
+    srcs = [to_dev_bytes(ref.stream, 16) for _, _, _, ref in items]
+    outs = [torch.zeros((T, op.F), dtype=torch.int16, device=DEV) for _ in items]
+    jobs = [K.make_job(l, k, T, src, out, out.numel() * 2, src_capacity=len(ref.stream))
+            for (l, k, _, ref), src, out in zip(items, srcs, outs)]
+    d_st = torch.full((len(jobs),), -99, dtype=torch.int32, device=DEV)
+    dc.codec.decode_noalloc(jobs, K.KVTC_BF16, d_st)
+    torch.cuda.synchronize()
+    assert d_st.cpu().tolist() == [0] * len(jobs)
+    for a, b in zip(ref_outs, outs):
+        assert torch.equal(a[:T], b)
+    l, k, store, ref = items[0]
+    x = storage_to_dev(store)
+    buf = torch.zeros(len(ref.stream), dtype=torch.uint8, device=DEV)
+    codes = torch.zeros(T * op.F, dtype=torch.uint8, device=DEV)
+    ss = torch.zeros(T * op.F * 2, dtype=torch.float32, device=DEV)
     with pytest.raises(K.KvtcError) as e:
-        dc.decode([(l, k, T, ref.stream) for l, k, _, ref in items], K.KVTC_BF16, op.F, schedule="fused")
-    assert e.value.status == K.KVTC_E_UNSUPPORTED
-    l, k, _, ref = items[0]
-    src = torch.zeros(len(ref.stream) + 16, dtype=torch.uint8, device=DEV)
-    out = torch.zeros((T, op.F), dtype=torch.int16, device=DEV)
-    job = K.make_job(l, k, T, src, out, out.numel() * 2, src_capacity=len(ref.stream))
-    with pytest.raises(K.KvtcError) as e:
-        dc.codec.decode_noalloc([job], K.KVTC_BF16)
+        dc.codec.pack(K.make_job(l, k, T, x, buf, len(ref.stream)), codes, ss, dc.ws)
     assert e.value.status == K.KVTC_E_UNSUPPORTED
