@@ -482,9 +482,22 @@ class Pipeline:
             torch.cuda.synchronize()
             times.append(p0.elapsed_time(p1))
         t_p = float(np.median(times))
+        # the same layers each decoded by one fused-schedule call (status
+        # words only: no staging), back to back on one stream
+        nw = K.kvtc_workspace_bytes(self.nj)
+        tf = []
+        for _ in range(reps):
+            p0.record(stream)
+            for js in self.layers:
+                self.codec.decode(js, K.KVTC_BF16, self.ws[0], nw, stream)
+            p1.record(stream)
+            torch.cuda.synchronize()
+            tf.append(p0.elapsed_time(p1))
+        self.check()
         return {"staging_buffers": self.nbuf, "unpack_ms": round(float(t_u), 4),
                 "restore_ms": round(float(t_r), 4), "pipelined_ms": round(t_p, 4),
-                "overlap": round(float(t_u + t_r) / t_p, 3)}
+                "overlap": round(float(t_u + t_r) / t_p, 3),
+                "layer_fused_ms": round(float(np.median(tf)), 4)}
 
 
 def lossless_stage(K, codec, jobs, sizes, offs, sbuf, T, F, esz, dev, stream, reps, deflate_ratio):
