@@ -228,10 +228,12 @@ typedef struct {
  *     KVTC_E_UNSUPPORTED for them.
  * With no flag each tensor gets exactly kvtc_calibrate's result. A (layer,
  * kind) may appear at most once; the call is all or nothing (on error no slot
- * changes). Errors: KVTC_E_INVALID (bad arguments, unknown flags, too few
- * rows, duplicates), KVTC_E_UNSUPPORTED (with a width per component, a
- * tensor needing more than KVTC_MAX_REFF components; group widths keep to
- * the cap as in kvtc_calibrate). */
+ * changes). Every tensor keeps to the kernels' cap of KVTC_MAX_REFF active
+ * components as in kvtc_calibrate: with a width per component, when the
+ * plain allocation has more than KVTC_MAX_REFF / G active groups, the widths
+ * minimise the distortion under both the budget and that cap (same tie
+ * order). Errors: KVTC_E_INVALID (bad arguments, unknown flags, too few
+ * rows, duplicates). */
 kvtc_status kvtc_calibrate_set(kvtc_codec* codec, const kvtc_calib_input* inputs, int32_t n,
                                uint32_t flags, int32_t threads);
 

@@ -486,28 +486,108 @@ int group_cost_pc(int sum) { return sum == 0 ? 0 : kScaleBits + 8 * ((sum + 7) /
 // f[g][u] = min_s e_g[0][s] + f[g+1][u - cost(s)] (nested from the last
 // group). Ties: fewest bits, then the largest s for the earliest group,
 // then the largest widths first inside a group.
-std::vector<uint8_t> dp_allocate_pc(const std::vector<double>& Dc, int F, int nb, int G, long budget) {
+// Per-component allocation (a width per component, cost 64 + 8 ceil(sum/8)
+// bits per active group). PcInner: per group g, e(g, i, s) = least
+// distortion of components i.. of the group whose widths sum to s.
+struct PcInner {
+  int n_g, G, nb, smax;
+  std::vector<double> E;
+  double& e(int g, int i, int sm) { return E[((size_t)g * (G + 1) + i) * (smax + 1) + sm]; }
+};
+PcInner pc_inner(const std::vector<double>& Dc, int F, int nb, int G) {
   const double INF = std::numeric_limits<double>::infinity();
-  const int n_g = F / G, smax = (nb - 1) * G;
-  const long U = budget + 1;
-  std::vector<double> E((size_t)n_g * (G + 1) * (smax + 1), INF);
-  auto e = [&](int g, int i, int sm) -> double& { return E[((size_t)g * (G + 1) + i) * (smax + 1) + sm]; };
-  for (int g = 0; g < n_g; ++g) {
+  PcInner P{F / G, G, nb, (nb - 1) * G, {}};
+  P.E.assign((size_t)P.n_g * (G + 1) * (P.smax + 1), INF);
+  for (int g = 0; g < P.n_g; ++g) {
     const double* D = Dc.data() + (size_t)g * G * nb;
-    e(g, G, 0) = 0.0;
+    P.e(g, G, 0) = 0.0;
     for (int i = G - 1; i >= 0; --i)
-      for (int sm = 0; sm <= smax; ++sm) {
+      for (int sm = 0; sm <= P.smax; ++sm) {
         double best = INF;
         for (int b = 0; b < nb && b <= sm; ++b) {
-          const double nx = e(g, i + 1, sm - b);
+          const double nx = P.e(g, i + 1, sm - b);
           if (nx < INF) {
             const double v = D[(size_t)i * nb + b] + nx;
             if (v < best) best = v;
           }
         }
-        e(g, i, sm) = best;
+        P.e(g, i, sm) = best;
       }
   }
+  return P;
+}
+// Group g's component widths summing to sm, largest width first.
+void pc_components(PcInner& P, const std::vector<double>& Dc, int g, int sm, std::vector<uint8_t>& w) {
+  const double INF = std::numeric_limits<double>::infinity();
+  const int G = P.G, nb = P.nb;
+  const double* D = Dc.data() + (size_t)g * G * nb;
+  for (int i = 0; i < G; ++i)
+    for (int b = std::min(nb - 1, sm); b >= 0; --b) {
+      const double nx = P.e(g, i + 1, sm - b);
+      if (nx < INF && D[(size_t)i * nb + b] + nx == P.e(g, i, sm)) {
+        w[(size_t)g * G + i] = (uint8_t)b;
+        sm -= b;
+        break;
+      }
+    }
+}
+
+// At most R active groups: f(g, u, r) = least distortion of groups g.. at
+// exactly u bits with at most r of them active; the same tie order as the
+// plain allocation (fewest bits, largest sum for the earliest group, largest
+// widths first).
+std::vector<uint8_t> dp_allocate_pc_capped(PcInner& P, const std::vector<double>& Dc, long budget, int R) {
+  const double INF = std::numeric_limits<double>::infinity();
+  const int n_g = P.n_g, smax = P.smax;
+  const long U = budget + 1;
+  std::vector<double> f((size_t)(n_g + 1) * U * (R + 1), INF);
+  auto F_ = [&](int g, long u, int r) -> double& { return f[((size_t)g * U + u) * (R + 1) + r]; };
+  for (int r = 0; r <= R; ++r) F_(n_g, 0, r) = 0.0;
+  for (int g = n_g - 1; g >= 0; --g)
+    for (long u = 0; u < U; ++u)
+      for (int r = 0; r <= R; ++r) {
+        double best = INF;
+        for (int sm = 0; sm <= smax; ++sm) {
+          const long c = group_cost_pc(sm);
+          const int rr = r - (sm > 0 ? 1 : 0);
+          if (c > u || rr < 0 || !(P.e(g, 0, sm) < INF)) continue;
+          const double nx = F_(g + 1, u - c, rr);
+          if (nx < INF) {
+            const double v = P.e(g, 0, sm) + nx;
+            if (v < best) best = v;
+          }
+        }
+        F_(g, u, r) = best;
+      }
+  long u = 0;
+  for (long v = 1; v < U; ++v)
+    if (F_(0, v, R) < F_(0, u, R)) u = v;
+  std::vector<uint8_t> w((size_t)n_g * P.G, 0);
+  int r = R;
+  for (int g = 0; g < n_g; ++g) {
+    int sm = smax;
+    for (; sm > 0; --sm) {
+      const long c = group_cost_pc(sm);
+      if (c <= u && r >= 1 && P.e(g, 0, sm) < INF &&
+          P.e(g, 0, sm) + F_(g + 1, u - c, r - 1) == F_(g, u, r))
+        break;
+    }
+    u -= group_cost_pc(sm);   // sm == 0: the group stays inactive
+    if (sm > 0) --r;
+    pc_components(P, Dc, g, sm, w);
+  }
+  return w;
+}
+
+// The plain allocation: f(g, u) = min_s E_g(s) + f(g + 1, u - cost(s)); with
+// max_active, the capped one whenever the plain result has more active
+// groups than that (reading Q3c).
+std::vector<uint8_t> dp_allocate_pc(const std::vector<double>& Dc, int F, int nb, int G, long budget,
+                                    int max_active) {
+  const double INF = std::numeric_limits<double>::infinity();
+  PcInner P = pc_inner(Dc, F, nb, G);
+  const int n_g = P.n_g, smax = P.smax;
+  const long U = budget + 1;
   std::vector<double> f((size_t)(n_g + 1) * U, INF);
   f[(size_t)n_g * U] = 0.0;
   for (int g = n_g - 1; g >= 0; --g)
@@ -515,10 +595,10 @@ std::vector<uint8_t> dp_allocate_pc(const std::vector<double>& Dc, int F, int nb
       double best = INF;
       for (int sm = 0; sm <= smax; ++sm) {
         const long c = group_cost_pc(sm);
-        if (c > u || !(e(g, 0, sm) < INF)) continue;
+        if (c > u || !(P.e(g, 0, sm) < INF)) continue;
         const double nx = f[(size_t)(g + 1) * U + u - c];
         if (nx < INF) {
-          const double v = e(g, 0, sm) + nx;
+          const double v = P.e(g, 0, sm) + nx;
           if (v < best) best = v;
         }
       }
@@ -528,26 +608,20 @@ std::vector<uint8_t> dp_allocate_pc(const std::vector<double>& Dc, int F, int nb
   for (long v = 1; v < U; ++v)
     if (f[v] < f[u]) u = v;
   std::vector<uint8_t> w(F, 0);
+  int n_act = 0;
   for (int g = 0; g < n_g; ++g) {
     int sm = smax;
     for (; sm >= 0; --sm) {
       const long c = group_cost_pc(sm);
-      if (c <= u && e(g, 0, sm) < INF && e(g, 0, sm) + f[(size_t)(g + 1) * U + u - c] == f[(size_t)g * U + u])
+      if (c <= u && P.e(g, 0, sm) < INF && P.e(g, 0, sm) + f[(size_t)(g + 1) * U + u - c] == f[(size_t)g * U + u])
         break;
     }
     if (sm < 0) sm = 0;   // unreachable: f[g][u] came from some s
     u -= group_cost_pc(sm);
-    const double* D = Dc.data() + (size_t)g * G * nb;
-    for (int i = 0; i < G; ++i)
-      for (int b = std::min(nb - 1, sm); b >= 0; --b) {
-        const double nx = e(g, i + 1, sm - b);
-        if (nx < INF && D[(size_t)i * nb + b] + nx == e(g, i, sm)) {
-          w[(size_t)g * G + i] = (uint8_t)b;
-          sm -= b;
-          break;
-        }
-      }
+    if (sm > 0) ++n_act;
+    pc_components(P, Dc, g, sm, w);
   }
+  if (n_act > max_active) return dp_allocate_pc_capped(P, Dc, budget, max_active);
   return w;
 }
 
@@ -752,7 +826,7 @@ kvtc_status kvtc_calibrate_set(kvtc_codec* c, const kvtc_calib_input* in, int32_
     const auto ws = dp_allocate_global(ds, n_g, nb, G, budget_bits(p), KVTC_MAX_REFF / G);
     for (int k = 0; k < n; ++k) widths[ord[k]] = ws[k];
   } else if (pcw) {
-    for (int i : ord) widths[i] = dp_allocate_pc(Ds[i], F, nb, G, budget_bits(p));   // per component
+    for (int i : ord) widths[i] = dp_allocate_pc(Ds[i], F, nb, G, budget_bits(p), KVTC_MAX_REFF / G);
   } else {
     for (int i : ord) widths[i] = dp_allocate_capped(Ds[i], n_g, nb, G, budget_bits(p));
   }

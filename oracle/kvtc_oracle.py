@@ -81,6 +81,10 @@ its own width; READING Q2c, an alternative to Q2 chosen at calibration):
       bits, then the largest s for the earliest group, then the
       lexicographically largest widths inside a group.  Slot format: the
       seventh header int is 1 and the widths array holds F component widths.
+  Q3c with a cap of max_active active groups (the library's 256 components),
+      used only when the plain allocation breaks it: the across-group DP also
+      counts the active groups, f[g][u][r] = least distortion of groups g.. at
+      exactly u bits with at most r active; the same tie order.
 
 Byte formats (all little-endian):
 
@@ -524,13 +528,9 @@ def group_cost_pc(s: int) -> int:
     return 0 if s == 0 else SCALE_BITS + 8 * ((s + 7) // 8)
 
 
-def dp_allocate_pc(Dc: np.ndarray, G: int, budget: int) -> np.ndarray:
-    """Component widths minimising sum_j Dc[j, b_j] within the budget, with
-    the cost of reading Q2c (ties in its order).
-
-    Per group, e[i][s] = least distortion of components i.. of the group
-    whose widths sum to s (nested from the last component); across groups,
-    f[g][u] = min_s E_g(s) + f[g+1][u - cost(s)] (nested from the last)."""
+def _pc_inner(Dc: np.ndarray, G: int):
+    """Per group g, e[i][s] = least distortion of components i.. of the group
+    whose widths sum to s (nested from the last component)."""
     F, nb = Dc.shape
     n_g = F // G
     smax = (nb - 1) * G
@@ -550,6 +550,84 @@ def dp_allocate_pc(Dc: np.ndarray, G: int, budget: int) -> np.ndarray:
                             best = v
                 e[i, sm] = best
         inner.append(e)
+    return inner
+
+
+def _pc_components(Dc: np.ndarray, G: int, g: int, e: np.ndarray, sm: int, out: np.ndarray):
+    """Group g's component widths summing to sm, largest width first."""
+    nb = Dc.shape[1]
+    D = Dc[g * G:(g + 1) * G]
+    for i in range(G):
+        for b in range(min(nb - 1, sm), -1, -1):
+            if e[i + 1, sm - b] < np.inf and D[i, b] + e[i + 1, sm - b] == e[i, sm]:
+                out[g * G + i] = b
+                sm -= b
+                break
+        else:
+            raise OracleError("DP reconstruction failed (component)")
+
+
+def dp_allocate_pc(Dc: np.ndarray, G: int, budget: int, max_active: int | None = None) -> np.ndarray:
+    """Component widths minimising sum_j Dc[j, b_j] within the budget, with
+    the cost of reading Q2c (ties in its order); with max_active, at most
+    that many active groups (reading Q3c: the plain result whenever it keeps
+    to the cap, else _dp_allocate_pc_capped's).
+
+    Per group, e[i][s] (see _pc_inner); across groups,
+    f[g][u] = min_s E_g(s) + f[g+1][u - cost(s)] (nested from the last)."""
+    out = _dp_allocate_pc_plain(Dc, G, budget)
+    if max_active is not None and np.count_nonzero(out.reshape(-1, G).sum(axis=1)) > max_active:
+        out = _dp_allocate_pc_capped(Dc, G, budget, max_active)
+    return out
+
+
+def _dp_allocate_pc_capped(Dc: np.ndarray, G: int, budget: int, max_active: int) -> np.ndarray:
+    """The allocation of dp_allocate_pc with at most max_active active groups:
+    f[g][u][r] = least distortion of groups g.. at exactly u bits with at
+    most r of them active, f[g][u][r] = min(f[g+1][u][r], min_{s>0} E_g(s) +
+    f[g+1][u - cost(s)][r - 1]); the same tie order (fewest bits, then the
+    largest sum for the earliest group, then the largest widths first)."""
+    F, nb = Dc.shape
+    n_g = F // G
+    smax = (nb - 1) * G
+    INF = np.inf
+    inner = _pc_inner(Dc, G)
+    R = max_active
+    f = np.full((n_g + 1, budget + 1, R + 1), INF)
+    f[n_g, 0, :] = 0.0
+    for g in range(n_g - 1, -1, -1):
+        for r in range(R + 1):
+            best = np.full(budget + 1, INF)       # over u at once
+            for sm in range(smax + 1):
+                c = group_cost_pc(sm)
+                rr = r - (1 if sm > 0 else 0)
+                if c <= budget and rr >= 0 and inner[g][0, sm] < INF:
+                    best[c:] = np.minimum(best[c:], inner[g][0, sm] + f[g + 1, :budget + 1 - c, rr])
+            f[g, :, r] = best
+    u = int(np.argmin(f[0, :, R]))               # first minimum = fewest bits
+    r = R
+    out = np.zeros(F, np.uint8)
+    for g in range(n_g):
+        e = inner[g]
+        for sm in range(smax, -1, -1):            # largest sum first
+            c = group_cost_pc(sm)
+            rr = r - (1 if sm > 0 else 0)
+            if c <= u and rr >= 0 and e[0, sm] < INF and e[0, sm] + f[g + 1, u - c, rr] == f[g, u, r]:
+                break
+        else:
+            raise OracleError("DP reconstruction failed (group)")
+        u -= c
+        r = rr
+        _pc_components(Dc, G, g, e, sm, out)
+    return out
+
+
+def _dp_allocate_pc_plain(Dc: np.ndarray, G: int, budget: int) -> np.ndarray:
+    F, nb = Dc.shape
+    n_g = F // G
+    smax = (nb - 1) * G
+    INF = np.inf
+    inner = _pc_inner(Dc, G)
     f = np.full((n_g + 1, budget + 1), INF)
     f[n_g, 0] = 0.0
     for g in range(n_g - 1, -1, -1):
@@ -573,15 +651,7 @@ def dp_allocate_pc(Dc: np.ndarray, G: int, budget: int) -> np.ndarray:
         else:
             raise OracleError("DP reconstruction failed (group)")
         u -= c
-        D = Dc[g * G:(g + 1) * G]
-        for i in range(G):
-            for b in range(min(nb - 1, sm), -1, -1):   # largest width first
-                if e[i + 1, sm - b] < INF and D[i, b] + e[i + 1, sm - b] == e[i, sm]:
-                    out[g * G + i] = b
-                    sm -= b
-                    break
-            else:
-                raise OracleError("DP reconstruction failed (component)")
+        _pc_components(Dc, G, g, e, sm, out)
     return out
 
 
@@ -659,7 +729,9 @@ def calibrate_set(inputs, params: Params, shared_basis: bool = False,
     shared_basis: one PCA basis per kind over the pooled rows of its tensors,
     each centred on its own mean.  global_budget: widths from
     dp_allocate_global with at most max_active active groups per tensor (no cap
-    if None).  Without either flag every tensor is calibrate()'s result.
+    if None).  component_widths: a width per component (reading Q2c), with at
+    most max_active active groups when given (reading Q3c).  Without a flag
+    every tensor is calibrate()'s result.
     Returns {(layer, kind): Slot}."""
     params.check()
     prep = {}
@@ -693,7 +765,7 @@ def calibrate_set(inputs, params: Params, shared_basis: bool = False,
         for k in keys:
             C = (prep[k] - mus[k]) @ basis[k][0]
             Dc = distortion_table_pc(C, params.group, params.max_bits)
-            cw = dp_allocate_pc(Dc, params.group, params.budget_bits)
+            cw = dp_allocate_pc(Dc, params.group, params.budget_bits, max_active)
             widths = cw.reshape(-1, params.group).max(axis=1).astype(np.uint8)
             sl = _make_slot(k[0], k[1], params, mus[k], basis[k][0], basis[k][1], Dc, widths)
             sl.cwidths = cw

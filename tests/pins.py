@@ -465,7 +465,7 @@ def check_lossless_roundtrip():
 _PC_ALLOCS = {}
 
 
-def brute_force_pc(Dc, G, budgets):
+def brute_force_pc(Dc, G, budgets, cap=None):
     """Every component width vector, ordered by (objective, bits of reading
     Q2c, largest component sum for the earliest group, lexicographically
     largest widths); the best one within each budget. Dc must hold exact
@@ -478,6 +478,9 @@ def brute_force_pc(Dc, G, budgets):
         cost = np.where(sums > 0, 64 + 8 * ((sums + 7) // 8), 0).sum(axis=1)
         _PC_ALLOCS[(F, nb)] = (ws, sums, cost)
     ws, sums, cost = _PC_ALLOCS[(F, nb)]
+    if cap is not None:   # at most cap active groups
+        keep = np.count_nonzero(sums, axis=1) <= cap
+        ws, sums, cost = ws[keep], sums[keep], cost[keep]
     obj = np.sum(Dc[np.arange(F), ws], axis=1)
     keys = ([-ws[:, j] for j in range(F - 1, -1, -1)] + [-sums[:, g] for g in range(n_g - 1, -1, -1)]
             + [cost, obj])
@@ -514,7 +517,8 @@ def check_pc_quantizer_golden():
 def check_pc_dp_bruteforce():
     """The per-component allocation of reading Q2c against brute force: one
     group of 8 components with widths 0..3, and two groups of 8 with widths
-    0..1; exact dyadic tables, ties included."""
+    0..1, also capped at one active group (reading Q3c); exact dyadic tables,
+    ties included."""
     rng = np.random.default_rng(13)
     for trial in range(3):
         for n_g, nb in ((1, 4), (2, 2)):
@@ -529,6 +533,11 @@ def check_pc_dp_bruteforce():
             for budget, bw in zip(budgets, brute_force_pc(Dc, 8, budgets)):
                 w = O.dp_allocate_pc(Dc, 8, budget)
                 assert np.array_equal(w, bw), (trial, n_g, budget, w, bw)
+            if n_g == 2:   # reading Q3c: at most one active group
+                for budget, bw in zip(budgets, brute_force_pc(Dc, 8, budgets, cap=1)):
+                    w = O.dp_allocate_pc(Dc, 8, budget, max_active=1)
+                    assert np.array_equal(w, bw), (trial, "cap 1", budget, w, bw)
+                    assert np.array_equal(O._dp_allocate_pc_capped(Dc, 8, budget, 1), bw)
 
 
 def check_pc_tables_and_reduction():

@@ -411,3 +411,28 @@ def test_folded_mean_follows_the_documented_bound(name):
             assert expect
         else:
             assert not expect
+
+
+def test_component_widths_keep_to_the_kernels_cap():
+    """A width per component at 8 bits per value on 10 groups of 32: the plain
+    allocation wants more than KVTC_MAX_REFF / 32 = 8 active groups; the
+    library keeps to the cap with the oracle's capped allocation (reading
+    Q3c), equal widths or an equal objective on a near tie."""
+    rng = np.random.default_rng(41)
+    F, G, n = 320, 32, 2000
+    Q = np.linalg.qr(rng.standard_normal((F, F)))[0]
+    x = ((rng.standard_normal((n, F)) * np.linspace(3.0, 0.5, F)) @ Q.T).astype(np.float32)
+    op = O.Params(1, 5, 64, 4, 8, G, 8, 8.0, O.DTYPE_F32)
+    kp = K.params(1, 5, 64, 4, 8, G, 8, 8.0, K.KVTC_F32)
+    cap = K.KVTC_MAX_REFF // G
+    free = O.calibrate_set([(0, 0, x)], op, component_widths=True)[(0, 0)]
+    assert free.n_act > cap                     # the plain optimum needs more
+    so = O.calibrate_set([(0, 0, x)], op, component_widths=True, max_active=cap)[(0, 0)]
+    assert so.n_act <= cap
+    c = K.Codec(kp)
+    c.calibrate_set([(0, 0, x)], K.KVTC_CAL_COMPONENT_WIDTHS, threads=8)
+    sl = O.parse_artifact(c.save()).slots[(0, 0)]
+    assert sl.n_act <= cap
+    if not np.array_equal(sl.cwidths, so.cwidths):   # a near tie may flip
+        obj = lambda cw: sum(so.D[j, b] for j, b in enumerate(cw))
+        assert abs(obj(sl.cwidths) - obj(so.cwidths)) <= 1e-9 * obj(so.cwidths)

@@ -294,7 +294,18 @@ def _group_cost_pc_unpadded(s_):
     return 0 if s_ == 0 else 64 + s_
 
 
+def _dp_pc_cap_ignored(Dc, G, budget, max_active=None):
+    return _orig["dp_allocate_pc"](Dc, G, budget)
+
+
+def _dp_pc_capped_counts_all_groups(Dc, G, budget, max_active):
+    """The cap charged for every group, active or not."""
+    return _orig["_dp_allocate_pc_capped"](Dc, G, budget, max(0, max_active - Dc.shape[0] // G + 1))
+
+
 PC_MUTATIONS = {
+    "pc_cap_ignored": ("dp_allocate_pc", _dp_pc_cap_ignored),
+    "pc_cap_counts_all_groups": ("_dp_allocate_pc_capped", _dp_pc_capped_counts_all_groups),
     "pc_pack_msb_first": ("pack_codes_pc", _pack_pc_msb_first),
     "pc_dequant_group_width": ("dequantize_pc", _dequant_pc_group_width),
     "pc_range_over_coded_only": ("quantize_fp32_pc", _quant_pc_active_range),
