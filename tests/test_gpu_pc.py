@@ -141,3 +141,53 @@ def test_pc_noalloc_decodes_and_hooks_refuse():
     with pytest.raises(K.KvtcError) as e:
         dc.codec.pack(K.make_job(l, k, T, x, buf, len(ref.stream)), codes, ss, dc.ws)
     assert e.value.status == K.KVTC_E_UNSUPPORTED
+
+
+def test_pc_and_group_slots_in_one_call():
+    """One call over jobs of a slot with a width per component and of a slot
+    with group widths, alternating: encode, both decode schedules (the host
+    gives each kind launches of its own) and the lossless round trip all
+    match the oracle."""
+    import oracle.kvtc_lossless as LZ
+    w = synth.workload("odd3_bf16")
+    op = oracle_params(w)
+    x0 = synth.gen_kv(w, 0, 0, synth.ROLE_CALIB, w.calib_tokens)
+    x1 = synth.gen_kv(w, 0, 1, synth.ROLE_CALIB, w.calib_tokens)
+    slots = {(0, 0): O.calibrate_set([(0, 0, x0)], op, component_widths=True)[(0, 0)],
+             (0, 1): O.calibrate(x1, op, 0, 1)}
+    art = O.Artifact(op, slots)
+    dc = DevCodec(art.serialize())
+    assert dc.codec.slot(0, 0).per_component == 1 and dc.codec.slot(0, 1).per_component == 0
+    items = []
+    for i, T in enumerate((700, 1100, 33, 900)):
+        k = i % 2
+        store = synth.storage(w, synth.gen_kv(w, 0, k, synth.ROLE_EVAL, T))
+        items.append((k, T, store, O.encode(store, op, slots[(0, k)], 0, k)))
+    streams = dc.encode([(0, k, storage_to_dev(store)) for k, _, store, _ in items])
+    for (k, T, _, ref), sb in zip(items, streams):
+        nb, nt, mx, _, _ = code_stats(sb, ref, op, slots[(0, k)], T)
+        assert mx <= 1 and nb <= max(2, nt * CODE_RATE), (k, T, nb, nt)
+    jobs = [(0, k, T, ref.stream) for k, T, _, ref in items]
+    outs, st = dc.decode(jobs, K.KVTC_F32, op.F, schedule="staged")
+    assert np.all(st == 0), st
+    outs2, st2 = dc.decode(jobs, K.KVTC_F32, op.F, schedule="fused")
+    assert np.all(st2 == 0), st2
+    for (k, T, _, ref), a, b in zip(items, outs, outs2):
+        assert torch.equal(a, b)
+        full, _ = O.decode(ref.stream, op, slots[(0, k)], 0, k, T, K.KVTC_F32)
+        g = a[:T].cpu().numpy().astype(np.float64)
+        assert np.abs(g - full).max() / max(np.abs(full).max(), 1e-30) <= DEC_TOL
+    # lossless: containers equal the oracle's and decode back
+    srcs = [to_dev_bytes(ref.stream, 16) for *_, ref in items]
+    bounds = [dc.codec.lossless_bound(0, k, T) for k, T, _, _ in items]
+    dsts = [torch.zeros(b + 16, dtype=torch.uint8, device=DEV) for b in bounds]
+    ljobs = [K.make_job(0, k, T, s, d, b, src_capacity=len(ref.stream))
+             for (k, T, _, ref), s, d, b in zip(items, srcs, dsts, bounds)]
+    n = dc.codec.lossless_workspace_bytes(ljobs, True)
+    lws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    dc.codec.lossless_encode(ljobs, lws, n)
+    torch.cuda.synchronize()
+    assert np.all(K.kvtc_read_device_status(lws, len(ljobs), None) == 0)
+    sizes = K.kvtc_lossless_sizes(lws, len(ljobs), None)
+    for (k, T, _, ref), d, z in zip(items, dsts, sizes):
+        assert bytes(d[:int(z)].cpu().numpy().tobytes()) == LZ.compress(ref.stream, op, slots[(0, k)], T)
