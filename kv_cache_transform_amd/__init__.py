@@ -64,7 +64,7 @@ def lib():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        raise ImportError(f"{LIB_PATH} is missing: build it with kv_cache_transform_amd.build.build()")
     L = C.CDLL(LIB_PATH)
     vp, st, i32, i64, sz = C.c_void_p, C.c_int, C.c_int32, C.c_int64, C.c_size_t
     sig = {
