@@ -265,8 +265,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!F32IN
     *(uint4*)((BUF) + (idx / (kEncKS / 8)) * kEncRowPad + (idx % (kEncKS / 8)) * 8) = \
         make_uint4(V[4 * q], V[4 * q + 1], V[4 * q + 2], V[4 * q + 3]);              \
   }
+  // Token rows are read once: non-temporal loads keep them from displacing
+  // the basis and the decode's lines in the caches.
 #define KVTC_LOAD_X(DST) \
-  _Pragma("unroll") for (int i = 0; i < NI; ++i) DST[i] = *(const u32x4*)(l_x + xoff[i] + (size_t)lk * kEncKS * esz);
+  _Pragma("unroll") for (int i = 0; i < NI; ++i) DST[i] = __builtin_nontemporal_load((const u32x4*)(l_x + xoff[i] + (size_t)lk * kEncKS * esz));
   // Rows of one slice into the wave's token tile as loaded: row
   // i * RPI + lane / CH, features cx * EPC .. + EPC.
   auto stage_x = [&](const u32x4 (&xr)[NI]) __attribute__((always_inline)) {
