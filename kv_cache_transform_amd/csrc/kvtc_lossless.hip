@@ -675,12 +675,12 @@ __global__ void __launch_bounds__(kLzLanes) lz_decode_kernel(const LzArgs a) {
 // One unit per block of passthrough elements or records: field symbols back
 // into the stream (nothing is written for a job found bad). Unit 0 of a job
 // also copies the stream header. A record block stages its symbols in LDS
-// (8 planes of 64 n_act bytes, then n_act code runs of 64 G bytes) with a
-// map from record byte to (group, width, byte of the group's chunk), then
-// each thread assembles 4 consecutive stream bytes.
+// (8 planes of 64 n_act bytes, then n_act code runs of 64 G bytes); each
+// thread assembles whole (record, group) items in registers, writes them
+// into the packed records over the staged symbols, and the block leaves in
+// 16-byte stores.
 __global__ void __launch_bounds__(kLzThreads) lz_merge_kernel(const LzArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ uint32_t omap[kLzMaxRec];
   __shared__ uint32_t pcw_l[KVTC_MAX_REFF];
   const int ji = lz_job_at<&LzJob::unit0>(a, blockIdx.x);
   const LzJob& j = a.jobs[ji];
@@ -741,80 +741,78 @@ __global__ void __launch_bounds__(kLzThreads) lz_merge_kernel(const LzArgs a) {
     for (int i = tid; i < nr * G / 4; i += kLzThreads) ((uint32_t*)(lds + 8 * pl_b + g * cd_b))[i] = in[i];
   }
   // With a width per component, the slot's table ((record bit << 8) | width
-  // per component of each active group) in LDS, and per record byte of a
-  // chunk the range [c0, c1] of the group's components that have bits in it
-  // (c0 > c1: padding only).
+  // per component of each active group) in LDS.
   const bool pc = sl->pc != 0;
   if (pc) {
     const uint32_t* pcw = (const uint32_t*)(a.state + sl->pcw_off);
     for (int i = tid; i < na * G; i += kLzThreads) pcw_l[i] = pcw[i];
-    __syncthreads();
   }
-  for (int o = tid; o < rb; o += kLzThreads) {
-    uint32_t m = 0;
-    if (o >= 8 * na) {
-      int g = 0;
-      while (g + 1 < na && sl->chunk_off[g + 1] <= o) ++g;
+  __syncthreads();
+  // Each thread assembles whole (record, group) items in registers: the 8
+  // bytes of the group's (shift, scale) and its code chunk (each code at its
+  // bit offset in the chunk, LSB first). At most 64 * 16 items per block
+  // (KVTC_MAX_REFF components), so at most kLzItems per thread.
+  constexpr int kLzItems = kLzRecBlk * (KVTC_MAX_REFF / 16) / kLzThreads;
+  const int n_it = nr * na;
+  uint32_t ssw[kLzItems][2];
+  uint64_t acc[kLzItems][4];
+#pragma unroll
+  for (int k = 0; k < kLzItems; ++k) {
+    const int it = tid + kLzThreads * k;
+    ssw[k][0] = ssw[k][1] = 0u;
+    acc[k][0] = acc[k][1] = acc[k][2] = acc[k][3] = 0ull;
+    if (it >= n_it) continue;
+    const int t = it / na, g = it - t * na;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ssw[k][q >> 2] |= (uint32_t)lds[q * pl_b + t * na + g] << (8 * (q & 3));
+    const uint8_t* cq = lds + 8 * pl_b + g * cd_b + t * G;
+    const int b = s.width[g];
+    for (int c = 0; c < G; ++c) {
+      int rel = c * b, w = b;
       if (pc) {
-        int c0 = G, c1 = -1;
-        for (int c = 0; c < G; ++c) {
-          const uint32_t e = pcw_l[g * G + c];
-          const int lo = (int)(e >> 8), hi = lo + (int)(e & 0xFFu);
-          if (hi > lo && lo < 8 * o + 8 && hi > 8 * o) {
-            c0 = min(c0, c);
-            c1 = c;
-          }
-        }
-        m = (uint32_t)g | ((uint32_t)c0 << 8) | ((uint32_t)(c1 & 0xFF) << 16);
-      } else {
-        m = (uint32_t)g | ((uint32_t)s.width[g] << 8) | ((uint32_t)(o - sl->chunk_off[g]) << 16);
+        const uint32_t e = pcw_l[g * G + c];
+        rel = (int)(e >> 8) - 8 * sl->chunk_off[g];
+        w = (int)(e & 0xFFu);
+      }
+      const uint64_t qv = (uint64_t)(cq[c] & ((1u << w) - 1u));
+      const int wi = rel >> 6, sh = rel & 63;
+      // a code never crosses two words' boundary by more than its 8 bits
+      uint64_t lo = qv << sh, hi = sh ? qv >> (64 - sh) : 0ull;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        if (x == wi) acc[k][x] |= lo;
+        if (x == wi + 1) acc[k][x] |= hi;
       }
     }
-    omap[o] = m;
+  }
+  __syncthreads();   // every staged symbol is read
+  // The block's records, packed, over the staged symbols (they take at most
+  // the same bytes: rb <= na * (8 + G)).
+#pragma unroll
+  for (int k = 0; k < kLzItems; ++k) {
+    const int it = tid + kLzThreads * k;
+    if (it >= n_it) continue;
+    const int t = it / na, g = it - t * na;
+    uint8_t* rw = lds + t * rb;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) rw[8 * g + q] = (uint8_t)(ssw[k][q >> 2] >> (8 * (q & 3)));
+    const int co = sl->chunk_off[g];
+    const int cb = (g + 1 < na ? sl->chunk_off[g + 1] : rb) - co;   // the chunk's bytes
+    for (int y = 0; y < cb; ++y) {
+      uint64_t wv = 0;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        if (x == (y >> 3)) wv = acc[k][x];
+      rw[co + y] = (uint8_t)(wv >> (8 * (y & 7)));
+    }
   }
   __syncthreads();
   uint8_t* base = dst + kHeaderBytes + (size_t)s.n_pt * s.esz + (size_t)r0 * rb;
   const int nbytes = nr * rb;
-  for (int y0 = 4 * tid; y0 < nbytes; y0 += 4 * kLzThreads) {
-    uint32_t v = 0;
-    const int ny = min(4, nbytes - y0);
-    int t = y0 / rb, o = y0 - t * rb;
-    for (int q = 0; q < ny; ++q, ++o) {
-      if (o == rb) {
-        o = 0;
-        ++t;
-      }
-      uint32_t byte;
-      if (o < 8 * na) {
-        byte = lds[(o & 7) * pl_b + t * na + (o >> 3)];
-      } else {
-        const uint32_t m = omap[o];
-        const int g = (int)(m & 0xFFu);
-        const uint8_t* cq = lds + 8 * pl_b + g * cd_b + t * G;
-        byte = 0;
-        if (pc) {
-          const int c1 = (int)((m >> 16) & 0xFFu);
-          for (int c = (int)((m >> 8) & 0xFFu); c <= c1 && c < G; ++c) {
-            const uint32_t e = pcw_l[g * G + c];
-            const int sh = (int)(e >> 8) - 8 * o;
-            const uint32_t qv = cq[c] & ((1u << (e & 0xFFu)) - 1u);
-            byte |= sh >= 0 ? qv << sh : qv >> -sh;
-          }
-        } else {
-          const int b = (int)((m >> 8) & 0xFFu), lo = 8 * (int)(m >> 16);
-          for (int c = lo / b, c1 = min(G - 1, (lo + 7) / b); c <= c1; ++c) {
-            const int sh = c * b - lo;
-            const uint32_t qv = cq[c];
-            byte |= sh >= 0 ? qv << sh : qv >> -sh;
-          }
-        }
-      }
-      v |= (byte & 0xFFu) << (8 * q);
-    }
-    if (ny == 4) *(uint32_t*)(base + y0) = v;
-    else
-      for (int q = 0; q < ny; ++q) base[y0 + q] = (uint8_t)(v >> (8 * q));
-  }
+  // 16-byte copies (base is 16-byte aligned: the header, n_pt * esz and
+  // 64 * rb are multiples of 16), then the tail
+  for (int v = tid; v < nbytes / 16; v += kLzThreads) ((u32x4*)base)[v] = ((const u32x4*)lds)[v];
+  for (int y = (nbytes & ~15) + tid; y < nbytes; y += kLzThreads) base[y] = lds[y];
 }
 
 }  // namespace
