@@ -38,7 +38,9 @@
  *                instead: the stored token is one exact bf16 operand and the
  *                accumulation starts at -mu32 V' (fp64, rounded once); its
  *                rounding error scales with |x|, within a factor of about
- *                sqrt(2) of |x - mu| there (kvtc_slot_info.folded_mean).
+ *                sqrt(2) of |x - mu| there (kvtc_slot_info.folded_mean). A
+ *                slot finished (calibrated or loaded) while the environment
+ *                variable KVTC_ENCODE_CENTRED is "1" stays centred.
  *   dequantize   c_hat = shift + q * fp32(scale / k); dropped groups give 0;
  *                x_hat = mu32 + sum_j c_hat_j V'_j.
  *   stream       64-byte header ("KVTC", u16 version=1, u8 dtype, u8 kind,

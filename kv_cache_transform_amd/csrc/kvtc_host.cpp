@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <limits>
 #include <memory>
@@ -200,11 +201,15 @@ void finish_slot(const kvtc_params& p, int layer, int kind, Slot& s) {
   // rather than |x - mu|; when the calibration's mean is no larger than its
   // spread (|mu32|^2 <= sum of the covariance eigenvalues = E|x - mu|^2) |x|
   // is within a factor of about sqrt(2) of |x - mu|, and so is the error.
+  // KVTC_ENCODE_CENTRED=1 in the environment when the slot is finished keeps
+  // it on the centred product (for comparisons).
   {
     double m2 = 0.0, tr = 0.0;
     for (float v : s.mu32) m2 += (double)v * v;
     for (double v : s.lam) tr += v;
-    s.fold = p.dtype == KVTC_BF16 && s.r_eff > 0 && m2 <= tr;
+    const char* env = std::getenv("KVTC_ENCODE_CENTRED");
+    const bool centred = env && env[0] == '1';
+    s.fold = p.dtype == KVTC_BF16 && s.r_eff > 0 && m2 <= tr && !centred;
   }
   std::vector<uint8_t> b;
   b.insert(b.end(), {'K', 'V', 'T', 'S'});
