@@ -79,7 +79,7 @@ def main():
                          "instead of calibrating")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU: the path is not sharded here (--gpus must be 1)"}))
         sys.exit(2)
 
     import torch
