@@ -89,7 +89,7 @@ typedef enum {
   KVTC_E_MISMATCH = -4,        /* stream does not belong to this job/codec    */
   KVTC_E_NOT_CALIBRATED = -5,  /* (layer, kind) has no calibration            */
   KVTC_E_HIP = -6,             /* a HIP runtime call failed                   */
-  KVTC_E_UNSUPPORTED = -7      /* valid but outside this build's limits       */
+  KVTC_E_UNSUPPORTED = -7      /* valid but outside the library's limits      */
 } kvtc_status;
 
 typedef enum { KVTC_F32 = 0, KVTC_BF16 = 1 } kvtc_dtype;
